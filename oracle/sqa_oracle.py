@@ -1,0 +1,235 @@
+"""Plain, slow, float64 CPU oracle for Sparse Query Attention (SQA).
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import, call or execute anything in
+this package. The HIP path never imports it, and it imports nothing from the
+HIP path: the two share no code, tables or helpers. Seeded inputs come from
+the separate ``synth`` module, which holds no attention arithmetic.
+
+What is computed, and where it comes from
+-----------------------------------------
+* SQA keeps the per-head width d = d_model / H of the baseline and reduces the
+  number of *query* heads H_q below H, instead of reducing key/value heads
+  further ("SQAT-m: Sparse Query Attention Transformer mini", introduction and
+  "Architecture details"; SQA paper abstract, chatpaper page). The attention
+  FLOPs drop in proportion to H_q / H.
+* Query heads are split into H_kv contiguous groups, each sharing one key head
+  and one value head; one group is MQA and H groups is MHA ("GQA: Training
+  Generalized Multi-Query Transformer Models", nlp-lineage page, section
+  "The idea"). Query head i reads K/V head floor(i * H_kv / H_q).
+* The pages name multi-head attention and the attention-score computation but
+  never write the formula. The oracle uses the textbook per-head
+  scaled-dot-product softmax attention:
+      s_tu = scale * <Q[b,i,t,:], K[b,j,u,:]>,   u in U_t
+      O[b,i,t,:] = sum_u softmax_u(s_tu) V[b,j,u,:]
+  with U_t = all keys (encoder-style) or {u <= t} (causal, the SQAT-m text
+  generation model), and optionally LSE[b,i,t] = log sum_u exp(s_tu).
+* The layer (SQAT-m, "Architecture details" and "Model size difference"):
+  Q = X W_Q (H_q*d wide), K = X W_K and V = X W_V (H_kv*d wide), RoPE on Q and
+  K, SQA, then Y = O_flat W_O with W_O of H_q*d rows. Weights are [in, out].
+  The pages say "RoPE" only; the oracle uses rotate-half pairs (c, c + d/2)
+  with theta_c = base^(-2c/d) and angle t * theta_c. Which pairing RxLM uses
+  is parity unpinned (an interleaved pairing gives the same layer output up to
+  a fixed permutation of the W_Q / W_K columns).
+
+Every function upcasts its inputs to float64 (bf16 and fp32 upcasts are
+exact) and follows the definition directly: two-pass max-subtracted softmax,
+BLAS matrix products, no tiling beyond chunking query rows to bound memory.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "kv_head_index",
+    "attention",
+    "rope",
+    "layer",
+    "layer_weight_shapes",
+    "attention_param_count",
+]
+
+
+def kv_head_index(i: int, H_q: int, H_kv: int) -> int:
+    """K/V head read by query head i: floor(i * H_kv / H_q).
+
+    Contiguous grouping of query heads ("GQA ..." page, "The idea"): with H_kv
+    groups of g = H_q / H_kv heads this is i // g; H_kv = 1 is MQA and
+    H_kv = H_q is MHA.
+    """
+    if not (1 <= H_kv <= H_q):
+        raise ValueError("need 1 <= H_kv <= H_q")
+    if not (0 <= i < H_q):
+        raise ValueError("query head index out of range")
+    return (i * H_kv) // H_q
+
+
+def _attend_rows(q_rows: np.ndarray, t_rows: np.ndarray, kj: np.ndarray,
+                 vj: np.ndarray, scale: float, causal: bool):
+    """Softmax attention of a block of query rows against one K/V head (fp64).
+
+    q_rows [R, d] at positions t_rows [R]; kj, vj [N, d]. Returns O [R, d] and
+    LSE [R]. Two passes: row max, then exp / sum / weighted sum of V.
+    """
+    s = (q_rows @ kj.T) * scale                       # [R, N]
+    if causal:
+        u = np.arange(kj.shape[0])
+        s = np.where(u[None, :] <= t_rows[:, None], s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    o = (e @ vj) / l
+    lse = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: Optional[float] = None,
+              causal: bool = False, rows: Optional[Sequence[int]] = None,
+              return_lse: bool = False, threads: int = 1, chunk_elems: int = 1 << 23):
+    """SQA forward in float64.
+
+    q: [B, H_q, N, d]; k, v: [B, H_kv, N, d]; H_kv must be in [1, H_q]. The
+    general mapping floor(i*H_kv/H_q) is used, so H_kv need not divide H_q.
+    ``scale`` defaults to 1/sqrt(d). ``rows`` selects query positions (the
+    same positions for every (b, head)); the result then has len(rows) rows.
+    ``threads`` > 1 spreads (b, head, row-chunk) tasks over threads (numpy
+    releases the GIL in BLAS and ufuncs); results do not depend on it.
+    Returns O [B, H_q, R, d] float64 (and LSE [B, H_q, R] if return_lse).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("expected 4-D [B, H, N, d] arrays")
+    B, H_q, N, d = q.shape
+    Bk, H_kv, Nk, dk = k.shape
+    if (Bk, Nk, dk) != (B, N, d) or v.shape != k.shape:
+        raise ValueError("q/k/v shapes disagree")
+    if not (1 <= H_kv <= H_q):
+        raise ValueError("need 1 <= H_kv <= H_q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    t_all = np.arange(N, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = t_all.shape[0]
+    out = np.empty((B, H_q, R, d), dtype=np.float64)
+    lse = np.empty((B, H_q, R), dtype=np.float64)
+    if R == 0 or B == 0:
+        return (out, lse) if return_lse else out
+
+    chunk = max(1, min(R, chunk_elems // max(N, 1)))
+    kv64 = {}
+
+    def kv_of(b: int, j: int):
+        key = (b, j)
+        if key not in kv64:
+            kv64[key] = (k[b, j].astype(np.float64), v[b, j].astype(np.float64))
+        return kv64[key]
+
+    tasks = []
+    for b in range(B):
+        for i in range(H_q):
+            j = kv_head_index(i, H_q, H_kv)
+            kv_of(b, j)
+            for r0 in range(0, R, chunk):
+                tasks.append((b, i, j, r0, min(R, r0 + chunk)))
+
+    def run(task):
+        b, i, j, r0, r1 = task
+        kj, vj = kv64[(b, j)]
+        t_rows = t_all[r0:r1]
+        q_rows = q[b, i, t_rows].astype(np.float64)
+        o, ls = _attend_rows(q_rows, t_rows, kj, vj, float(scale), causal)
+        out[b, i, r0:r1] = o
+        lse[b, i, r0:r1] = ls
+
+    if threads <= 1:
+        for t in tasks:
+            run(t)
+    else:
+        try:
+            from threadpoolctl import threadpool_limits
+        except ImportError:  # pragma: no cover - threadpoolctl is installed
+            threadpool_limits = None
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                with ThreadPoolExecutor(max_workers=threads) as ex:
+                    list(ex.map(run, tasks))
+        else:
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                list(ex.map(run, tasks))
+    return (out, lse) if return_lse else out
+
+
+def rope(x: np.ndarray, base: float, positions: Optional[np.ndarray] = None) -> np.ndarray:
+    """Rotary position embedding, rotate-half convention, float64.
+
+    x: [..., N, d] with d even; position of row n is positions[n] (default n).
+    For c < d/2 the pair (x_c, x_{c+d/2}) is rotated by angle t * theta_c,
+    theta_c = base^(-2c/d):
+        y_c       = x_c cos - x_{c+d/2} sin
+        y_{c+d/2} = x_c sin + x_{c+d/2} cos
+    """
+    x = np.asarray(x, dtype=np.float64)
+    N, d = x.shape[-2], x.shape[-1]
+    if d % 2:
+        raise ValueError("RoPE needs an even head dimension")
+    h = d // 2
+    t = np.arange(N, dtype=np.float64) if positions is None else np.asarray(positions, np.float64)
+    theta = base ** (-2.0 * np.arange(h, dtype=np.float64) / d)
+    ang = t[:, None] * theta[None, :]                  # [N, h]
+    cos, sin = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * cos - x2 * sin, x1 * sin + x2 * cos], axis=-1)
+
+
+def layer_weight_shapes(D: int, H: int, H_q: int, H_kv: int):
+    """Projection shapes of one SQA layer ([in, out] layout).
+
+    d = D / H is kept from the baseline head split; the query and output
+    projections are H_q*d wide and the key/value projections H_kv*d wide
+    (SQAT-m model card, "Architecture details" and "Model size difference").
+    """
+    if D % H:
+        raise ValueError("D must be a multiple of H")
+    d = D // H
+    return {"W_Q": (D, H_q * d), "W_K": (D, H_kv * d), "W_V": (D, H_kv * d),
+            "W_O": (H_q * d, D)}
+
+
+def attention_param_count(D: int, H: int, H_q: int, H_kv: int) -> int:
+    """Number of projection weights in one attention layer (no biases)."""
+    return sum(a * b for a, b in layer_weight_shapes(D, H, H_q, H_kv).values())
+
+
+def layer(x: np.ndarray, wq: np.ndarray, wk: np.ndarray, wv: np.ndarray, wo: np.ndarray,
+          H: int, H_q: int, H_kv: int, rope_base: float = 10000.0,
+          scale: Optional[float] = None, causal: bool = True,
+          threads: int = 1) -> np.ndarray:
+    """One SQA attention layer forward in float64.
+
+    x [B, N, D]; weights in [in, out] layout with the shapes of
+    ``layer_weight_shapes``. Head h owns projection columns [h*d, (h+1)*d).
+    No biases, norms or residual. Returns Y [B, N, D].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, N, D = x.shape
+    shapes = layer_weight_shapes(D, H, H_q, H_kv)
+    for name, w in (("W_Q", wq), ("W_K", wk), ("W_V", wv), ("W_O", wo)):
+        if tuple(np.shape(w)) != shapes[name]:
+            raise ValueError(f"{name} has shape {np.shape(w)}, expected {shapes[name]}")
+    d = D // H
+
+    def heads(y: np.ndarray, nh: int) -> np.ndarray:       # [B,N,nh*d] -> [B,nh,N,d]
+        return y.reshape(B, N, nh, d).transpose(0, 2, 1, 3)
+
+    qh = rope(heads(x @ np.asarray(wq, np.float64), H_q), rope_base)
+    kh = rope(heads(x @ np.asarray(wk, np.float64), H_kv), rope_base)
+    vh = heads(x @ np.asarray(wv, np.float64), H_kv)
+    o = attention(qh, kh, vh, scale=scale, causal=causal, threads=threads)
+    o_flat = o.transpose(0, 2, 1, 3).reshape(B, N, H_q * d)
+    return o_flat @ np.asarray(wo, np.float64)
