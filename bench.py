@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Throughput of the SQA attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--variant HQ,HKV] [--causal 0|1] [--no-cpu-baseline]
+                    [--no-compare]
+
+A step is one sqa_attn_fwd call over the whole workload (default: B=1,
+N=32768, d=64, SQA H_q=8 / H_kv=4, bf16, encoder-style), with inputs already
+resident in HBM. FLOPs are counted as 4*B*N^2*H_q*d, halved for causal.
+Prints ONE JSON line. The line also carries:
+  * roofline: the attention kernel's achieved TFLOP/s against the MI355X
+    dense bf16 MFMA peak (2516.6 TFLOP/s = 256 CU x 4096 FLOP/clk x 2.4 GHz),
+    timed with HIP events on the stream the kernel runs on;
+  * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
+    sample of the same workload (sampled query rows, every head);
+  * comparison: MHA / GQA-4 / MQA at the same shape (H_q = 16) and the
+    measured speedup of the SQA variant over MHA.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # dense MFMA, published MI355X figure
+PEAK_F32_TFLOPS = 157.3
+METRIC = "SQA fwd TFLOP/s + tokens/s at N=32k-200k; % of MI355X bf16 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.json")
+
+
+def counted_flops(B, Hq, N, d, causal):
+    f = 4.0 * B * N * N * Hq * d
+    return f / 2 if causal else f
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "sparse_query_attention_sqa_amd", "csrc", "attn_fwd_bf16.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload: str, variant, causal: int):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, only if
+    it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    key = f"{workload}:{variant[0]},{variant[1]}:c{causal}"
+    e = t.get("entries", {}).get(key)
+    if not e or t.get("kernel_sha256_16") != kernel_source_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def time_variant(sqa, torch, q, k, v, scale, causal, steps, warmup):
+    stream = torch.cuda.current_stream()
+    out = torch.empty_like(q)
+    for _ in range(warmup):
+        sqa.sqa_attn_fwd(q, k, v, scale=scale, causal=causal, out=out)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        sqa.sqa_attn_fwd(q, k, v, scale=scale, causal=causal, out=out)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return start.elapsed_time(end) / steps, wall, out
+
+
+def cpu_baseline(w, variant, causal, rows_count):
+    import numpy as np
+
+    from oracle import attention as oracle_attention
+    from synth import draw_qkv, sample_rows, select_variant
+    Hq, Hkv = variant
+    q, k, v = select_variant(*draw_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=0, peaky=w.peaky),
+                             Hq, Hkv)
+    rows = sample_rows(w.N, rows_count)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    threads = max(1, min(16, cores))
+    t0 = time.perf_counter()
+    oracle_attention(q, k, v, scale=w.scale, causal=bool(causal), rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    if causal:
+        flops = float(np.sum(4.0 * (rows + 1) * w.d)) * w.B * Hq
+    else:
+        flops = 4.0 * len(rows) * w.N * w.d * w.B * Hq
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} seeded query rows x {w.B * Hq} heads of {w.name} "
+                      f"({Hq},{Hkv}) causal={causal}, full key range; fp64 numpy, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long32k_bf16")
+    ap.add_argument("--variant", default=None, help="H_q,H_kv (default: the workload's first)")
+    ap.add_argument("--causal", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=16384)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward needs no collective; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_query_attention_sqa_amd as sqa
+    from synth import WORKLOADS, draw_qkv, select_variant
+
+    if not os.path.exists(sqa.lib_path()):
+        from sparse_query_attention_sqa_amd import _build
+        _build.build()
+    sqa.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    w = WORKLOADS[args.workload]
+    if w.layer or w.dtype != "bf16":
+        print("bench.py times the bf16 attention workloads", file=sys.stderr)
+        sys.exit(2)
+    variant = tuple(int(x) for x in args.variant.split(",")) if args.variant else w.variants[0]
+    causal = w.causal[0] if args.causal is None else args.causal
+    Hq, Hkv = variant
+
+    q_all, k_all, v_all = draw_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=0, peaky=w.peaky)
+
+    def dev(a):
+        return torch.from_numpy(a).to("cuda").to(torch.bfloat16).contiguous()
+
+    def run(var):
+        q, k, v = (dev(a) for a in select_variant(q_all, k_all, v_all, *var))
+        ms, wall, _ = time_variant(sqa, torch, q, k, v, w.scale, bool(causal), args.steps, args.warmup)
+        del q, k, v
+        torch.cuda.empty_cache()
+        return ms, wall
+
+    ms, wall = run(variant)
+    flops = counted_flops(w.B, Hq, w.N, w.d, causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+    tokens = w.B * w.N / (ms * 1e-3)
+
+    comparison = None
+    if not args.no_compare:
+        comparison = {}
+        for var in [(16, 16), (16, 4), (16, 1)] + [v for v in w.variants if v != variant]:
+            key = f"{var[0]},{var[1]}"
+            if key in comparison or var == variant or var[0] > w.H:
+                continue
+            cms, _ = run(var)
+            comparison[key] = {"ms": round(cms, 4),
+                               "tflops": round(counted_flops(w.B, var[0], w.N, w.d, causal) / (cms * 1e-3) / 1e12, 2)}
+        if "16,16" in comparison:
+            comparison["speedup_vs_mha"] = round(comparison["16,16"]["ms"] / ms, 3)
+            comparison["expected_H_over_Hq"] = w.H / Hq
+
+    traffic = stored_traffic(w.name, variant, causal)
+    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic,
+                "kernel": "attn_fwd_bf16_kernel<64>" if w.d == 64 else "attn_fwd_bf16_kernel<16>",
+                "per_launch_flop": flops}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, variant, causal, args.cpu_rows)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "tokens_per_s": round(tokens, 1),
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "H_q": Hq, "H_kv": Hkv,
+                   "d": w.d, "causal": int(causal), "scale": w.scale, "peaky_keys": w.peaky,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "comparison": comparison,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,132 @@
+/*
+ * libsqa -- Sparse Query Attention (SQA) forward on AMD Instinct MI355X (gfx950).
+ *
+ * SQA is full-sequence softmax attention in which the number of query heads
+ * H_q is cut below the baseline head count H while the head width d stays
+ * d_model / H, so the attention-score FLOPs fall in proportion to H_q / H
+ * (SQA paper abstract, chatpaper page; SQAT-m model card, "Architecture
+ * details"). Query heads form H_kv contiguous groups that each share one key
+ * head and one value head, as in grouped-query attention ("GQA: Training
+ * Generalized Multi-Query Transformer Models", nlp-lineage page, "The idea"):
+ * query head i reads K/V head floor(i * H_kv / H_q).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers to tensors are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors), 16-byte aligned, contiguous row-major, with the shapes given.
+ *     The caller owns every buffer; the library never allocates, frees or
+ *     synchronises, and keeps no state across calls except a thread-local
+ *     error string.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream. Work is enqueued asynchronously; results are visible after the
+ *     caller synchronises the stream.
+ *   - Every argument is checked before anything is launched. On any error
+ *     nothing is launched and the outputs are left untouched. Launch failures
+ *     return SQA_ERR_HIP (detail in sqa_last_error()). Faults during execution
+ *     surface at the caller's next synchronisation.
+ *   - Zero-sized problems (B == 0 or N == 0) return SQA_OK and launch nothing.
+ *   - No exceptions or output cross this interface.
+ */
+#ifndef SQA_H_
+#define SQA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SQA_OK = 0,
+  SQA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  SQA_ERR_SHAPE = 2,       /* negative size, H_kv not in [1, H_q], H_q % H_kv != 0 */
+  SQA_ERR_UNSUPPORTED = 3, /* valid but not implemented: d, dtype, ...            */
+  SQA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                     */
+  SQA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required              */
+  SQA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed           */
+  SQA_ERR_ARG = 7          /* other invalid argument (non-finite scale, aliasing) */
+} sqa_status;
+
+typedef enum { SQA_F32 = 0, SQA_BF16 = 1 } sqa_dtype;
+
+/*
+ * sqa_attn_fwd -- SQA attention forward.
+ *
+ * For every b < B, query head i < H_q, position t < N, with j = i / (H_q/H_kv):
+ *   s_tu      = scale * sum_c q[b,i,t,c] * k[b,j,u,c]          for u in U_t
+ *   o[b,i,t,:] = sum_{u in U_t} softmax_u(s_tu) * v[b,j,u,:]
+ *   lse[b,i,t] = log sum_{u in U_t} exp(s_tu)                   (natural log)
+ * U_t = {0..N-1} if causal == 0 (encoder-style, full sequence) and {0..t} if
+ * causal == 1 (decoder). The pages name the attention but do not write the
+ * formula; this is the textbook scaled-dot-product form.
+ *
+ *   q    [B, H_q,  N, d]  input,  dtype
+ *   k, v [B, H_kv, N, d]  input,  dtype
+ *   o    [B, H_q,  N, d]  output, dtype; must not overlap q, k or v
+ *   lse  [B, H_q,  N]     optional output, fp32; NULL to skip
+ *   d     16 or 64.  H_q % H_kv == 0 and 1 <= H_kv <= H_q.
+ *   dtype SQA_BF16: bf16 in/out; scores, softmax state and the output
+ *         accumulator are fp32, the probabilities are rounded to bf16 for the
+ *         P.V product, the output is rounded to nearest-even bf16.
+ *         SQA_F32: fp32 in/out with fp32 arithmetic throughout.
+ *   scale any finite float (1/sqrt(d) is the usual choice).
+ * Errors: SQA_ERR_NULL, SQA_ERR_SHAPE, SQA_ERR_UNSUPPORTED (d, dtype),
+ * SQA_ERR_ALIGN, SQA_ERR_ARG (scale not finite, causal not 0/1, o overlaps an
+ * input), SQA_ERR_HIP.
+ */
+sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                        int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d,
+                        int dtype, float scale, int causal, float* lse, void* stream);
+
+/*
+ * sqa_layer_workspace_bytes -- bytes of device workspace sqa_layer_fwd needs
+ * for these sizes: bf16 Q [B,H_q,N,d], K and V [B,H_kv,N,d] and the attention
+ * output [B,H_q,N,d], each rounded up to 256 bytes. Returns 0 for invalid or
+ * zero sizes.
+ */
+size_t sqa_layer_workspace_bytes(int64_t B, int64_t N, int64_t D, int64_t H,
+                                 int64_t H_q, int64_t H_kv, int dtype);
+
+/*
+ * sqa_layer_fwd -- one SQA attention layer forward (SQAT-m model card,
+ * "Architecture details" and "Model size difference"):
+ *   Q = x W_q, K = x W_k, V = x W_v        (weights in [in, out] layout)
+ *   Q, K <- RoPE (rotate-half pairs (c, c+d/2), angle t * rope_base^(-2c/d),
+ *                 position t = 0..N-1 of each sequence)
+ *   O = sqa_attn_fwd(Q, K, V, scale, causal)
+ *   y = O_flat W_o,   O_flat[b, t, i*d + c] = O[b, i, t, c]
+ * with d = D / H; head h owns projection columns [h*d, (h+1)*d). No biases,
+ * norms or residual.
+ *
+ *   x   [B, N, D]        bf16 input
+ *   w_q [D, H_q*d]       bf16      w_k, w_v [D, H_kv*d] bf16
+ *   w_o [H_q*d, D]       bf16
+ *   y   [B, N, D]        bf16 output; must not overlap x
+ *   workspace            device buffer of at least
+ *                        sqa_layer_workspace_bytes(...) bytes, owned by the
+ *                        caller; its contents on return are unspecified.
+ *   D = 256 with d = 16 (the SQAT-m split) or D % 64 == 0 with d = 64;
+ *   dtype must be SQA_BF16.
+ * Errors: as sqa_attn_fwd, plus SQA_ERR_WORKSPACE.
+ */
+sqa_status sqa_layer_fwd(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                         const void* w_o, void* y, int64_t B, int64_t N, int64_t D,
+                         int64_t H, int64_t H_q, int64_t H_kv, float rope_base, float scale,
+                         int causal, int dtype, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* sqa_status_str(int status);
+
+/* Detail of the last error raised on the calling thread ("" if none).
+ * The pointer stays valid until the next libsqa call on that thread. */
+const char* sqa_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int sqa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQA_H_ */

@@ -1,0 +1,188 @@
+"""Python binding for libsqa: Sparse Query Attention forward on MI355X.
+
+Argument marshalling only. Every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/sqa.h``; torch is used for
+device memory and the current HIP stream. There is no fallback path: if the
+library is not built, importing the functions raises.
+
+    sqa_attn_fwd(q, k, v, *, scale=None, causal=False, out=None, return_lse=False)
+    sqa_layer_fwd(x, w_q, w_k, w_v, w_o, *, H, H_q, H_kv, rope_base=10000.0,
+                  scale=None, causal=True, out=None, workspace=None)
+    sqa_layer_workspace_bytes(B, N, D, H, H_q, H_kv, dtype="bf16")
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = ["SQAError", "lib_path", "load_library", "sqa_attn_fwd", "sqa_layer_fwd",
+           "sqa_layer_workspace_bytes", "sqa_status_str", "sqa_version",
+           "SQA_F32", "SQA_BF16"]
+
+SQA_F32 = 0
+SQA_BF16 = 1
+
+_STATUS = {0: "SQA_OK", 1: "SQA_ERR_NULL", 2: "SQA_ERR_SHAPE", 3: "SQA_ERR_UNSUPPORTED",
+           4: "SQA_ERR_ALIGN", 5: "SQA_ERR_WORKSPACE", 6: "SQA_ERR_HIP", 7: "SQA_ERR_ARG"}
+
+_LIB = None
+
+
+def lib_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsqa.so")
+
+
+class SQAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libsqa.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"libsqa.so is not built ({path}); run __graft_entry__.build() "
+                          "or python -m sparse_query_attention_sqa_amd._build")
+    lib = ctypes.CDLL(path)
+    i64, vp, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    lib.sqa_attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, f32,
+                                 ctypes.c_int, vp, vp]
+    lib.sqa_attn_fwd.restype = ctypes.c_int
+    lib.sqa_layer_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
+    lib.sqa_layer_workspace_bytes.restype = ctypes.c_size_t
+    lib.sqa_layer_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32,
+                                  ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.sqa_layer_fwd.restype = ctypes.c_int
+    lib.sqa_status_str.argtypes = [ctypes.c_int]
+    lib.sqa_status_str.restype = ctypes.c_char_p
+    lib.sqa_last_error.argtypes = []
+    lib.sqa_last_error.restype = ctypes.c_char_p
+    lib.sqa_version.argtypes = []
+    lib.sqa_version.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load_library().sqa_last_error().decode(errors="replace")
+        raise SQAError(status, msg)
+
+
+def sqa_status_str(status: int) -> str:
+    return load_library().sqa_status_str(status).decode()
+
+
+def sqa_version() -> int:
+    return load_library().sqa_version()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SQA_BF16
+    if t.dtype == torch.float32:
+        return SQA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_device(*ts) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("libsqa takes GPU tensors only (no CPU fallback)")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def sqa_attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, out=None,
+                 return_lse: bool = False):
+    """SQA attention forward on the GPU.
+
+    q [B, H_q, N, d]; k, v [B, H_kv, N, d]; bf16 or fp32, contiguous, on the
+    same GPU. Query head i reads K/V head i // (H_q // H_kv). Returns
+    o [B, H_q, N, d] (and lse [B, H_q, N] fp32 if ``return_lse``).
+    """
+    torch = _torch()
+    lib = load_library()
+    _require_device(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected 4-D [B, H, N, d] tensors")
+    if k.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("k and v must match; q, k, v must share a dtype")
+    B, H_q, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError("q and k/v shapes disagree")
+    H_kv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require_device(out)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    lse = torch.empty((B, H_q, N), dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib.sqa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H_q, H_kv,
+                          N, d, _dtype_code(q), float(scale), int(bool(causal)),
+                          lse.data_ptr() if lse is not None else None, _stream_handle(q.device))
+    _check(st)
+    return (out, lse) if return_lse else out
+
+
+def sqa_layer_workspace_bytes(B: int, N: int, D: int, H: int, H_q: int, H_kv: int,
+                              dtype: str = "bf16") -> int:
+    code = SQA_BF16 if dtype == "bf16" else SQA_F32
+    return int(load_library().sqa_layer_workspace_bytes(B, N, D, H, H_q, H_kv, code))
+
+
+def sqa_layer_fwd(x, w_q, w_k, w_v, w_o, *, H: int, H_q: int, H_kv: int,
+                  rope_base: float = 10000.0, scale: Optional[float] = None,
+                  causal: bool = True, out=None, workspace=None):
+    """One SQA attention layer forward: projections, RoPE, SQA, output projection.
+
+    x [B, N, D] bf16; w_q [D, H_q*d], w_k/w_v [D, H_kv*d], w_o [H_q*d, D]
+    bf16 in [in, out] layout, d = D // H. Returns y [B, N, D] bf16.
+    ``workspace`` is an optional uint8 GPU tensor of at least
+    ``sqa_layer_workspace_bytes`` bytes (allocated here if omitted).
+    """
+    torch = _torch()
+    lib = load_library()
+    _require_device(x, w_q, w_k, w_v, w_o)
+    if x.dim() != 3:
+        raise ValueError("x must be [B, N, D]")
+    B, N, D = x.shape
+    d = D // H if H else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d) if d > 0 else 1.0
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _require_device(out)
+    need = int(lib.sqa_layer_workspace_bytes(B, N, D, H, H_q, H_kv, _dtype_code(x)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    else:
+        _require_device(workspace)
+    st = lib.sqa_layer_fwd(x.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(),
+                           w_o.data_ptr(), out.data_ptr(), B, N, D, H, H_q, H_kv,
+                           float(rope_base), float(scale), int(bool(causal)), _dtype_code(x),
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           _stream_handle(x.device))
+    _check(st)
+    return out

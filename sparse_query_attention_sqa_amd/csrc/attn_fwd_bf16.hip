@@ -1,0 +1,442 @@
+// SQA attention forward, bf16 in/out, fp32 softmax state, for gfx950.
+//
+// What is computed: per query head i and position t, softmax attention over
+// the keys of K/V head floor(i*H_kv/H_q) (contiguous query-head groups as in
+// grouped-query attention, "GQA ..." page, "The idea"), with H_q below the
+// baseline head count (SQA paper abstract). Encoder-style (all keys) or
+// causal (keys u <= t).
+//
+// Work decomposition (MI355X-first design, not taken from the pages):
+//   * A workgroup is 4 waves that share one (batch, K/V head). Each wave owns
+//     a "slot": 64 consecutive query positions of one query head of the
+//     group. Slots are ordered (position block, head-in-group), so the 4
+//     waves of a workgroup read the same K/V head -- for g = H_q/H_kv >= 2
+//     they are different query heads at the same positions, which is the
+//     reuse SQA/GQA grouping offers.
+//   * K/V are streamed in 64-key tiles, HBM -> registers -> LDS, double
+//     buffered with one barrier per tile; each tile is read from HBM once per
+//     workgroup and consumed by 4 x 64 = 256 query rows.
+//   * Scores are computed transposed, S^T = K Q^T, with
+//     v_mfma_f32_32x32x16_bf16 (A = K tile from LDS, B = Q held in
+//     registers). The accumulator layout then already is the B operand of
+//     O^T = V^T P^T, so probabilities never leave registers. K rows are
+//     stored in LDS under the permutation pi (below) so that each lane's 16
+//     accumulator entries are 16 consecutive keys; V^T is stored transposed
+//     (built in registers with a 4x4 transpose) so the A operand of the P.V
+//     product is one 16-byte LDS read.
+//   * Online softmax in fp32 with base-2 exponentials (v_exp_f32) of
+//     s*c - m, c = |scale|*log2(e). The running maximum m is only raised when
+//     a tile's maximum exceeds it by more than kRescaleSlack (log2 units); the
+//     probabilities are then bounded by 2^kRescaleSlack, well inside the
+//     bf16/fp32 range, and the O rescale is skipped on most tiles.
+//   * Probabilities are rounded to bf16 (round to nearest even) for the P.V
+//     MFMA; the row sum l adds the same rounded values, so the weights that
+//     multiply V sum exactly to l.
+//   * Causal: tiles above a wave's diagonal are skipped; only the diagonal
+//     tile and a ragged tail tile are masked. Workgroups are issued
+//     longest-first. Encoder-style: blockIdx is remapped so consecutive
+//     workgroups (same K/V head) land on the same XCD and share its L2.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace sqa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;      // 4 waves of 64
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 64;   // query rows per wave: two 32-row MFMA tiles
+constexpr int kTileKeys = 64;      // keys per K/V tile
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kXcds = 8;
+
+template <int D>
+struct Cfg {
+  static_assert(D == 16 || D == 64, "head dim");
+  static constexpr int DSTEPS = D / 16;            // MFMA k-steps over d for S^T
+  static constexpr int DSUB = (D + 31) / 32;       // 32-row O^T tiles over d
+  static constexpr int KROW = D + 8;               // LDS pitch of a K row (bf16)
+  static constexpr int VROWS = DSUB * 32;          // rows of V^T in LDS
+  static constexpr int VROW = kTileKeys + 8;       // LDS pitch of a V^T row (bf16)
+  static constexpr int KBUF = kTileKeys * KROW;    // bf16 elements per K buffer
+  static constexpr int VBUF = VROWS * VROW;        // bf16 elements per V^T buffer
+  static constexpr int BUF = KBUF + VBUF;
+  static constexpr int KCHUNKS = kTileKeys * D / 8;          // 16-byte chunks per K tile
+  static constexpr int KLOADS = (KCHUNKS + kThreads - 1) / kThreads;
+  static constexpr int VBLOCKS = (kTileKeys / 4) * (D / 4);  // 4x4 blocks per V tile
+};
+
+struct Args {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int N, Hq, Hkv, g;
+  int TB;          // ceil(N / 64): query position blocks per head
+  int wg_per_bkv;  // workgroups per (batch, K/V head)
+  int n_bkv;       // B * Hkv
+  int nwg;
+  float c;         // |scale| * log2(e)
+  uint32_t qsign;  // 0x80008000 flips both bf16 halves when scale < 0
+  int causal;
+};
+
+// MFMA row r of a 32-key sub-tile holds key pi(r); the accumulator entry i
+// of lane-half lg then is key lg*16 + i. pi_inv places a key in LDS.
+__device__ __forceinline__ int pi_inv(int p) {
+  return ((p & 15) >> 2) * 8 + (p >> 4) * 4 + (p & 3);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2_t f = {a, b};
+  bf16x2_t h = __builtin_convertvector(f, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+template <int D>
+struct TileRegs {
+  u32x4_t k[Cfg<D>::KLOADS];
+  u32x2_t v[4];
+};
+
+// HBM -> registers for K/V tile kt (key rows clamped into [0, N)).
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* kbase,
+                                          const uint16_t* vbase, int kt, int N, int tid) {
+  using C = Cfg<D>;
+  const int key0 = kt * kTileKeys;
+#pragma unroll
+  for (int it = 0; it < C::KLOADS; ++it) {
+    const int c = tid + it * kThreads;
+    if (c < C::KCHUNKS) {
+      const int key = c / (D / 8), dc = c % (D / 8);
+      const int row = min(key0 + key, N - 1);
+      r.k[it] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)row * D + dc * 8);
+    }
+  }
+  if (tid < C::VBLOCKS) {
+    const int kg = tid / (D / 4), dg = tid % (D / 4);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = min(key0 + kg * 4 + rr, N - 1);
+      r.v[rr] = *reinterpret_cast<const u32x2_t*>(vbase + (size_t)row * D + dg * 4);
+    }
+  }
+}
+
+// registers -> LDS: K rows under pi_inv, V transposed (4x4 blocks).
+template <int D>
+__device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* buf, int tid) {
+  using C = Cfg<D>;
+  uint16_t* ks = buf;
+  uint16_t* vs = buf + C::KBUF;
+#pragma unroll
+  for (int it = 0; it < C::KLOADS; ++it) {
+    const int c = tid + it * kThreads;
+    if (c < C::KCHUNKS) {
+      const int key = c / (D / 8), dc = c % (D / 8);
+      const int lrow = (key & ~31) + pi_inv(key & 31);
+      *reinterpret_cast<u32x4_t*>(ks + lrow * C::KROW + dc * 8) = r.k[it];
+    }
+  }
+  if (tid < C::VBLOCKS) {
+    const int kg = tid / (D / 4), dg = tid % (D / 4);
+    // r.v[rr] = {V[key rr][d0], V[rr][d0+1]} , {V[rr][d0+2], V[rr][d0+3]}
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int word = cc >> 1;
+      const bool hi = cc & 1;
+      uint32_t e[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) e[rr] = hi ? (r.v[rr][word] >> 16) : (r.v[rr][word] & 0xffffu);
+      u32x2_t out;
+      out[0] = e[0] | (e[1] << 16);
+      out[1] = e[2] | (e[3] << 16);
+      const int d = dg * 4 + cc;
+      const int lrow = (d & ~31) + pi_inv(d & 31);
+      *reinterpret_cast<u32x2_t*>(vs + lrow * C::VROW + kg * 4) = out;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(Args a) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, lg = lane >> 5;
+
+  // ---- workgroup -> (batch*Hkv, slot range)
+  int L;
+  if (!a.causal) {
+    // consecutive logical workgroups on one XCD (hardware deals blockIdx
+    // round-robin over the XCDs)
+    const int bid = blockIdx.x;
+    const int per = a.nwg / kXcds, rem = a.nwg % kXcds;
+    const int x = bid % kXcds, i = bid / kXcds;
+    L = x * per + min(x, rem) + i;
+  } else {
+    L = blockIdx.x;
+  }
+  int bkv, w_in;
+  if (!a.causal) {
+    bkv = L / a.wg_per_bkv;
+    w_in = L % a.wg_per_bkv;
+  } else {  // longest (largest position block) first
+    const int wr = L / a.n_bkv;
+    bkv = L % a.n_bkv;
+    w_in = a.wg_per_bkv - 1 - wr;
+  }
+  const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
+  const int slot = w_in * kWaves + wave;
+  const int tb = slot / a.g, jh = slot % a.g;
+  const bool wave_valid = tb < a.TB;
+  const int h = kvh * a.g + jh;
+  const int N = a.N;
+
+  int nt;
+  if (a.causal) {
+    const int maxtb = min((w_in * kWaves + kWaves - 1) / a.g, a.TB - 1);
+    nt = maxtb + 1;
+  } else {
+    nt = a.TB;
+  }
+  const int wave_last = a.causal ? tb : nt - 1;
+
+  const uint16_t* kbase = a.k + (size_t)bkv * N * D;
+  const uint16_t* vbase = a.v + (size_t)bkv * N * D;
+  const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)N * D;
+
+  // ---- Q fragments (B operand): query l32 of each 32-row tile, d chunk ds*2+lg
+  u32x4_t qf[2][C::DSTEPS];
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const int t = min(tb * kRowsPerWave + qs * 32 + l32, N - 1);
+#pragma unroll
+    for (int ds = 0; ds < C::DSTEPS; ++ds) {
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (wave_valid) x = *reinterpret_cast<const u32x4_t*>(a.q + qoff + (size_t)t * D + (ds * 2 + lg) * 8);
+      x ^= a.qsign;
+      qf[qs][ds] = x;
+    }
+  }
+
+  // V^T rows that hold no head dimension (D < 32) must read as finite zeros.
+  if (C::VROWS > D) {
+    for (int e = tid; e < 2 * C::VBUF; e += kThreads) {
+      const int bsel = e / C::VBUF, off = e % C::VBUF;
+      smem[bsel * C::BUF + C::KBUF + off] = 0;
+    }
+  }
+
+  f32x16_t acc_o[C::DSUB][2];
+#pragma unroll
+  for (int x = 0; x < C::DSUB; ++x)
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc_o[x][qs][i] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+
+  TileRegs<D> regs;
+  load_tile<D>(regs, kbase, vbase, 0, N, tid);
+  __syncthreads();  // zero-fill above is complete before tile stores
+  store_tile<D>(regs, smem, tid);
+  __syncthreads();
+
+  const float c = a.c;
+  for (int kt = 0; kt < nt; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nt) load_tile<D>(regs, kbase, vbase, kt + 1, N, tid);
+
+    if (wave_valid && kt <= wave_last) {
+      const uint16_t* ks = smem + cur * C::BUF;
+      const uint16_t* vs = ks + C::KBUF;
+
+      // S^T[key][query] for 2 key sub-tiles x 2 query sub-tiles
+      f32x16_t s[2][2];
+#pragma unroll
+      for (int kx = 0; kx < 2; ++kx) {
+        bf16x8_t kf[C::DSTEPS];
+#pragma unroll
+        for (int ds = 0; ds < C::DSTEPS; ++ds)
+          kf[ds] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
+              ks + (kx * 32 + l32) * C::KROW + (ds * 2 + lg) * 8));
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          f32x16_t accs;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) accs[i] = 0.f;
+#pragma unroll
+          for (int ds = 0; ds < C::DSTEPS; ++ds)
+            accs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], as_bf16x8(qf[qs][ds]), accs, 0, 0, 0);
+          s[kx][qs] = accs;
+        }
+      }
+
+      const int key0 = kt * kTileKeys;
+      const bool masked = (a.causal && kt == tb) || (key0 + kTileKeys > N);
+      if (masked) {
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          const int t = tb * kRowsPerWave + qs * 32 + l32;
+#pragma unroll
+          for (int kx = 0; kx < 2; ++kx)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = key0 + kx * 32 + lg * 16 + i;
+              const bool ok = key < N && (!a.causal || key <= t);
+              if (!ok) s[kx][qs][i] = -INFINITY;
+            }
+        }
+      }
+
+      // online softmax (fp32), lazily raised running maximum
+      uint32_t pk[2][2][2][4];  // [kx][qs][half][word] bf16 pairs
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        float mx = s[0][qs][0];
+#pragma unroll
+        for (int kx = 0; kx < 2; ++kx)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kx][qs][i]);
+        const float cand = (mx == -INFINITY) ? -INFINITY : mx * c;
+        const bool need = cand > m_run[qs] + kRescaleSlack;
+        if (__ballot(need)) {
+          const float other = __shfl_xor(cand, 32);
+          const float mnew = fmaxf(m_run[qs], fmaxf(cand, other));
+          const float alpha = (m_run[qs] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[qs] - mnew);
+          m_run[qs] = mnew;
+          l_run[qs] *= alpha;
+#pragma unroll
+          for (int x = 0; x < C::DSUB; ++x)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc_o[x][qs][i] *= alpha;
+        }
+        const float mneg = -m_run[qs];
+        float lsum = 0.f;
+#pragma unroll
+        for (int kx = 0; kx < 2; ++kx)
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kx][qs][2 * w], c, mneg));
+            float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kx][qs][2 * w + 1], c, mneg));
+            if (masked) {
+              if (s[kx][qs][2 * w] == -INFINITY) p0 = 0.f;
+              if (s[kx][qs][2 * w + 1] == -INFINITY) p1 = 0.f;
+            }
+            const uint32_t pp = pack_bf16x2(p0, p1);
+            pk[kx][qs][w >> 2][w & 3] = pp;
+            lsum += bf16lo(pp) + bf16hi(pp);
+          }
+        l_run[qs] += lsum;
+      }
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int x = 0; x < C::DSUB; ++x)
+#pragma unroll
+        for (int kx = 0; kx < 2; ++kx)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
+                vs + (x * 32 + l32) * C::VROW + kx * 32 + lg * 16 + hh * 8));
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs) {
+              u32x4_t pw = {pk[kx][qs][hh][0], pk[kx][qs][hh][1], pk[kx][qs][hh][2], pk[kx][qs][hh][3]};
+              acc_o[x][qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pw), acc_o[x][qs], 0, 0, 0);
+            }
+          }
+    }
+
+    if (kt + 1 < nt) store_tile<D>(regs, smem + (cur ^ 1) * C::BUF, tid);
+    __syncthreads();
+  }
+
+  if (!wave_valid) return;
+
+  // ---- epilogue: O = O^T / l (bf16, nearest even), LSE = m ln2 + ln l
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const float ltot = l_run[qs] + __shfl_xor(l_run[qs], 32);
+    const float inv = 1.0f / ltot;
+    const int t = tb * kRowsPerWave + qs * 32 + l32;
+    if (t < N) {
+#pragma unroll
+      for (int x = 0; x < C::DSUB; ++x) {
+        const int d0 = x * 32 + lg * 16;
+        if (d0 < D) {
+          u32x4_t w0, w1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w0[e] = pack_bf16x2(acc_o[x][qs][2 * e] * inv, acc_o[x][qs][2 * e + 1] * inv);
+            w1[e] = pack_bf16x2(acc_o[x][qs][8 + 2 * e] * inv, acc_o[x][qs][8 + 2 * e + 1] * inv);
+          }
+          uint16_t* dst = a.o + qoff + (size_t)t * D + d0;
+          *reinterpret_cast<u32x4_t*>(dst) = w0;
+          *reinterpret_cast<u32x4_t*>(dst + 8) = w1;
+        }
+      }
+      if (a.lse != nullptr && lg == 0) {
+        a.lse[((size_t)b * a.Hq + h) * (size_t)N + t] =
+            (m_run[qs] + log2f(ltot)) * 0.69314718055994531f;
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
+  Args a;
+  a.q = static_cast<const uint16_t*>(p.q);
+  a.k = static_cast<const uint16_t*>(p.k);
+  a.v = static_cast<const uint16_t*>(p.v);
+  a.o = static_cast<uint16_t*>(p.o);
+  a.lse = p.lse;
+  a.N = (int)p.N;
+  a.Hq = (int)p.Hq;
+  a.Hkv = (int)p.Hkv;
+  a.g = (int)(p.Hq / p.Hkv);
+  a.TB = (int)((p.N + kRowsPerWave - 1) / kRowsPerWave);
+  const int64_t slots = (int64_t)a.TB * a.g;
+  a.wg_per_bkv = (int)((slots + kWaves - 1) / kWaves);
+  a.n_bkv = (int)(p.B * p.Hkv);
+  const int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;
+  if (nwg > 0x7fffffff) return hipErrorInvalidValue;
+  a.nwg = (int)nwg;
+  a.c = fabsf(p.scale) * 1.4426950408889634f;
+  a.qsign = (p.scale < 0.f) ? 0x80008000u : 0u;
+  a.causal = p.causal;
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3(a.nwg), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream) {
+  if (p.D == 64) return launch_d<64>(p, stream);
+  if (p.D == 16) return launch_d<16>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sqa

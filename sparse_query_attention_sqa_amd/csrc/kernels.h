@@ -1,0 +1,52 @@
+// Internal launch interface between the C-ABI layer (sqa_api.cpp) and the
+// HIP kernels. Not part of the public ABI; see include/sqa.h for that.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace sqa {
+
+// SQA attention forward: q [B,Hq,N,D], k/v [B,Hkv,N,D], o [B,Hq,N,D],
+// optional lse [B,Hq,N] fp32. Hq % Hkv == 0. Sizes already validated.
+struct AttnProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t B, Hq, Hkv, N, D;
+  float scale;
+  int causal;
+};
+
+hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const AttnProblem& p, hipStream_t stream);
+
+// Projection + RoPE: x [M=B*N, Dm] bf16 times w_q [Dm,Hq*d] | w_k [Dm,Hkv*d] |
+// w_v [Dm,Hkv*d]; writes q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16 with RoPE applied
+// to q and k.
+struct QkvProblem {
+  const void* x;
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  void* q;
+  void* k;
+  void* v;
+  int64_t B, N, Dm, Hq, Hkv, d;
+  float rope_base;
+};
+hipError_t launch_qkv_rope(const QkvProblem& p, hipStream_t stream);
+
+// Output projection: y [B,N,Dm] = O_flat [B*N, Hq*d] times w_o [Hq*d, Dm],
+// reading O from its [B,Hq,N,d] layout.
+struct OprojProblem {
+  const void* o;
+  const void* wo;
+  void* y;
+  int64_t B, N, Dm, Hq, d;
+};
+hipError_t launch_out_proj(const OprojProblem& p, hipStream_t stream);
+
+}  // namespace sqa

@@ -1,0 +1,192 @@
+// C-ABI entry points of libsqa (declared and documented in include/sqa.h).
+//
+// Every argument is checked before anything is launched; on error nothing is
+// enqueued and the outputs are untouched. The library holds no state besides
+// a thread-local error string, never allocates device memory and never
+// synchronises: all work goes onto the caller's stream.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+#include "sqa.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+sqa_status fail(sqa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+sqa_status hip_fail(hipError_t e, const char* what) {
+  return fail(SQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+constexpr int64_t kMaxN = (int64_t(1) << 30);          // positions per sequence
+constexpr int64_t kMaxElems = (int64_t(1) << 40);      // elements per tensor
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Shape rules shared by the attention and layer entry points.
+sqa_status check_heads(int64_t H_q, int64_t H_kv) {
+  if (H_q < 1) return fail(SQA_ERR_SHAPE, "H_q must be >= 1 (got %lld)", (long long)H_q);
+  if (H_kv < 1 || H_kv > H_q)
+    return fail(SQA_ERR_SHAPE, "H_kv must be in [1, H_q] (got H_kv=%lld, H_q=%lld)", (long long)H_kv,
+                (long long)H_q);
+  if (H_q % H_kv != 0)
+    return fail(SQA_ERR_SHAPE, "H_q must be a multiple of H_kv (got %lld, %lld)", (long long)H_q,
+                (long long)H_kv);
+  if (H_q > 4096) return fail(SQA_ERR_SHAPE, "H_q too large (%lld)", (long long)H_q);
+  return SQA_OK;
+}
+
+sqa_status check_attn(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
+                      float scale, int causal) {
+  if (B < 0 || N < 0 || d < 0) return fail(SQA_ERR_SHAPE, "negative size");
+  sqa_status s = check_heads(H_q, H_kv);
+  if (s != SQA_OK) return s;
+  if (dtype != SQA_F32 && dtype != SQA_BF16) return fail(SQA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (d != 16 && d != 64) return fail(SQA_ERR_UNSUPPORTED, "head dim d=%lld not supported (16 or 64)", (long long)d);
+  if (!std::isfinite(scale)) return fail(SQA_ERR_ARG, "scale must be finite");
+  if (causal != 0 && causal != 1) return fail(SQA_ERR_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (N > kMaxN) return fail(SQA_ERR_SHAPE, "N=%lld exceeds the supported maximum", (long long)N);
+  if (B > 0 && N > 0 && B * H_q * N * d > kMaxElems)
+    return fail(SQA_ERR_SHAPE, "tensor too large");
+  return SQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H_q,
+                        int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal,
+                        float* lse, void* stream) {
+  g_err.clear();
+  sqa_status s = check_attn(B, H_q, H_kv, N, d, dtype, scale, causal);
+  if (s != SQA_OK) return s;
+  if (B == 0 || N == 0) return SQA_OK;
+  if (!q || !k || !v || !o) return fail(SQA_ERR_NULL, "q, k, v and o must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(SQA_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(SQA_ERR_ALIGN, "lse must be 4-byte aligned");
+  const size_t esz = dtype == SQA_BF16 ? 2 : 4;
+  const size_t nq = (size_t)(B * H_q * N * d) * esz, nkv = (size_t)(B * H_kv * N * d) * esz;
+  const size_t nl = lse ? (size_t)(B * H_q * N) * 4 : 0;
+  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
+    return fail(SQA_ERR_ARG, "o overlaps an input");
+  if (lse && (overlaps(lse, nl, o, nq) || overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) ||
+              overlaps(lse, nl, v, nkv)))
+    return fail(SQA_ERR_ARG, "lse overlaps another tensor");
+
+  sqa::AttnProblem p{q, k, v, o, lse, B, H_q, H_kv, N, d, scale, causal};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = (dtype == SQA_BF16) ? sqa::launch_attn_fwd_bf16(p, st) : sqa::launch_attn_fwd_f32(p, st);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return SQA_OK;
+}
+
+size_t sqa_layer_workspace_bytes(int64_t B, int64_t N, int64_t D, int64_t H, int64_t H_q, int64_t H_kv,
+                                 int dtype) {
+  if (B <= 0 || N <= 0 || D <= 0 || H <= 0 || H_q <= 0 || H_kv <= 0) return 0;
+  if (dtype != SQA_BF16 || D % H != 0) return 0;
+  const int64_t d = D / H;
+  if (B * N * (H_q > H_kv ? H_q : H_kv) * d > kMaxElems) return 0;
+  const size_t esz = 2;
+  const size_t nq = (size_t)(B * H_q * N * d) * esz, nkv = (size_t)(B * H_kv * N * d) * esz;
+  return 2 * round256(nq) + 2 * round256(nkv);
+}
+
+sqa_status sqa_layer_fwd(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                         const void* w_o, void* y, int64_t B, int64_t N, int64_t D, int64_t H,
+                         int64_t H_q, int64_t H_kv, float rope_base, float scale, int causal,
+                         int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (B < 0 || N < 0 || D < 0 || H < 0) return fail(SQA_ERR_SHAPE, "negative size");
+  if (H < 1 || D < 1 || D % H != 0)
+    return fail(SQA_ERR_SHAPE, "D must be a positive multiple of H (got D=%lld, H=%lld)", (long long)D,
+                (long long)H);
+  const int64_t d = D / H;
+  if (dtype != SQA_BF16) return fail(SQA_ERR_UNSUPPORTED, "the layer supports bf16 only");
+  sqa_status s = check_attn(B, H_q, H_kv, N, d, dtype, scale, causal);
+  if (s != SQA_OK) return s;
+  if (!std::isfinite(rope_base) || rope_base <= 0.f) return fail(SQA_ERR_ARG, "rope_base must be finite and > 0");
+  if (D % 16 != 0) return fail(SQA_ERR_UNSUPPORTED, "D must be a multiple of 16");
+  if (B == 0 || N == 0) return SQA_OK;
+  if (B * N * D > kMaxElems) return fail(SQA_ERR_SHAPE, "tensor too large");
+  if (!x || !w_q || !w_k || !w_v || !w_o || !y) return fail(SQA_ERR_NULL, "inputs and y must be non-NULL");
+  if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) || !aligned(w_o, 16) ||
+      !aligned(y, 16))
+    return fail(SQA_ERR_ALIGN, "x, weights and y must be 16-byte aligned");
+  const size_t need = sqa_layer_workspace_bytes(B, N, D, H, H_q, H_kv, dtype);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SQA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!aligned(workspace, 256)) return fail(SQA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const size_t nx = (size_t)(B * N * D) * 2;
+  const size_t nwq = (size_t)(D * H_q * d) * 2, nwk = (size_t)(D * H_kv * d) * 2;
+  if (overlaps(y, nx, x, nx) || overlaps(y, nx, w_q, nwq) || overlaps(y, nx, w_k, nwk) ||
+      overlaps(y, nx, w_v, nwk) || overlaps(y, nx, w_o, nwq))
+    return fail(SQA_ERR_ARG, "y overlaps an input");
+  if (overlaps(workspace, need, x, nx) || overlaps(workspace, need, y, nx) || overlaps(workspace, need, w_q, nwq) ||
+      overlaps(workspace, need, w_k, nwk) || overlaps(workspace, need, w_v, nwk) || overlaps(workspace, need, w_o, nwq))
+    return fail(SQA_ERR_ARG, "workspace overlaps an input or y");
+
+  const size_t nq = round256((size_t)(B * H_q * N * d) * 2), nkv = round256((size_t)(B * H_kv * N * d) * 2);
+  char* ws = static_cast<char*>(workspace);
+  void* qb = ws;
+  void* kb = ws + nq;
+  void* vb = ws + nq + nkv;
+  void* ob = ws + nq + 2 * nkv;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  sqa::QkvProblem qp{x, w_q, w_k, w_v, qb, kb, vb, B, N, D, H_q, H_kv, d, rope_base};
+  hipError_t e = sqa::launch_qkv_rope(qp, st);
+  if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
+  sqa::AttnProblem ap{qb, kb, vb, ob, nullptr, B, H_q, H_kv, N, d, scale, causal};
+  e = sqa::launch_attn_fwd_bf16(ap, st);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  sqa::OprojProblem op{ob, w_o, y, B, N, D, H_q, d};
+  e = sqa::launch_out_proj(op, st);
+  if (e != hipSuccess) return hip_fail(e, "output projection launch");
+  return SQA_OK;
+}
+
+const char* sqa_status_str(int status) {
+  switch (status) {
+    case SQA_OK: return "SQA_OK";
+    case SQA_ERR_NULL: return "SQA_ERR_NULL";
+    case SQA_ERR_SHAPE: return "SQA_ERR_SHAPE";
+    case SQA_ERR_UNSUPPORTED: return "SQA_ERR_UNSUPPORTED";
+    case SQA_ERR_ALIGN: return "SQA_ERR_ALIGN";
+    case SQA_ERR_WORKSPACE: return "SQA_ERR_WORKSPACE";
+    case SQA_ERR_HIP: return "SQA_ERR_HIP";
+    case SQA_ERR_ARG: return "SQA_ERR_ARG";
+    default: return "SQA_ERR_UNKNOWN";
+  }
+}
+
+const char* sqa_last_error(void) { return g_err.c_str(); }
+
+int sqa_version(void) { return 100; }
+
+}  // extern "C"

@@ -51,11 +51,15 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     GPU side can convert them to bf16 losslessly and the oracle can upcast them
     to float64 losslessly. NaN/Inf are not produced by the generators.
     """
-    a = np.ascontiguousarray(x, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    u = (u + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)
-    return u.astype(np.uint32).view(np.float32).reshape(a.shape)
+    a = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = a.view(np.uint32)
+    if np.any((u & np.uint32(0x7F800000)) == np.uint32(0x7F800000)):
+        raise ValueError("bf16_round expects finite values")
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    u += np.uint32(0x7FFF)          # finite inputs: no uint32 wrap-around
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return a
 
 
 @dataclass(frozen=True)

@@ -1,0 +1,130 @@
+"""Host-side checks of the C-ABI library: it loads without a GPU, exports every
+symbol include/sqa.h declares, and rejects invalid arguments before any HIP
+call (no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_query_attention_sqa_amd as sqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sqa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(sqa_[a-z0-9_]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sqa.lib_path()):
+        pytest.fail("libsqa.so is not built; run __graft_entry__.build()")
+    return sqa.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ["sqa_attn_fwd", "sqa_layer_fwd", "sqa_layer_workspace_bytes", "sqa_status_str",
+              "sqa_last_error", "sqa_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(sqa.lib_path())
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sqa_version() >= 100
+    for code, name in [(0, "SQA_OK"), (1, "SQA_ERR_NULL"), (2, "SQA_ERR_SHAPE"),
+                       (3, "SQA_ERR_UNSUPPORTED"), (4, "SQA_ERR_ALIGN"),
+                       (5, "SQA_ERR_WORKSPACE"), (6, "SQA_ERR_HIP"), (7, "SQA_ERR_ARG")]:
+        assert sqa.sqa_status_str(code) == name
+    assert sqa.sqa_status_str(99) == "SQA_ERR_UNKNOWN"
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def _no_gpu_present():
+    """Fake-pointer calls run only where no GPU exists, so that a validation
+    bug can never turn into a launch on real hardware (device_count does not
+    initialise the HIP runtime)."""
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+cpu_only = pytest.mark.skipif(not _no_gpu_present(),
+                              reason="fake-pointer validation tests run on GPU-less hosts only")
+
+
+def _attn(lib, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, B=1, Hq=8,
+          Hkv=4, N=1024, d=64, dtype=1, scale=0.125, causal=0, lse=None):
+    return lib.sqa_attn_fwd(q, k, v, o, B, Hq, Hkv, N, d, dtype, scale, causal, lse, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(o=None), 1),
+    (dict(Hkv=3), 2), (dict(Hkv=0), 2), (dict(Hkv=16), 2), (dict(Hq=0), 2), (dict(N=-1), 2),
+    (dict(B=-2), 2), (dict(N=1 << 31), 2),
+    (dict(d=32), 3), (dict(d=128), 3), (dict(dtype=5), 3),
+    (dict(q=FAKE + 2), 4), (dict(o=FAKE + 0x300008), 4),
+    (dict(scale=float("inf")), 7), (dict(scale=float("nan")), 7), (dict(causal=2), 7),
+    (dict(o=FAKE), 7),                               # o aliases q
+    (dict(lse=FAKE + 0x200000 + 64), 7),             # lse inside v
+    (dict(lse=FAKE + 0x400001), 4),
+])
+@cpu_only
+def test_attn_rejects_invalid_arguments(lib, kw, code):
+    assert _attn(lib, **kw) == code
+    assert lib.sqa_last_error().decode() != ""
+
+
+@cpu_only
+def test_zero_size_is_a_noop(lib):
+    assert _attn(lib, q=None, k=None, v=None, o=None, B=0) == 0
+    assert _attn(lib, q=None, k=None, v=None, o=None, N=0) == 0
+    assert lib.sqa_last_error().decode() == ""
+
+
+def test_layer_workspace_bytes(lib):
+    # SQAT-m layer: B=16 N=1024 D=256 H=16 (8,4): Q and O 4 MiB each, K and V 2 MiB each
+    assert sqa.sqa_layer_workspace_bytes(16, 1024, 256, 16, 8, 4) == 2 * 4194304 + 2 * 2097152
+    # B=1 N=3: Q 768 B, K 384 B -> rounded to 768 and 512
+    assert sqa.sqa_layer_workspace_bytes(1, 3, 256, 16, 8, 4) == 2 * 768 + 2 * 512
+    assert sqa.sqa_layer_workspace_bytes(0, 1024, 256, 16, 8, 4) == 0
+    assert sqa.sqa_layer_workspace_bytes(1, 1024, 256, 16, 8, 4, dtype="f32") == 0
+
+
+def _layer(lib, x=FAKE, ws=FAKE + 0x1000000, ws_bytes=1 << 26, B=16, N=1024, D=256, H=16, Hq=8,
+           Hkv=4, dtype=1, base=10000.0, causal=1):
+    return lib.sqa_layer_fwd(x, FAKE + 0x100000, FAKE + 0x110000, FAKE + 0x120000,
+                             FAKE + 0x130000, FAKE + 0x200000 if x else FAKE + 0x200000,
+                             B, N, D, H, Hq, Hkv, base, 0.25, causal, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(ws=None), 5), (dict(ws_bytes=100), 5), (dict(dtype=0), 3),
+    (dict(D=250), 2), (dict(H=0), 2), (dict(Hkv=3), 2), (dict(D=512, H=16), 3),
+    (dict(base=0.0), 7), (dict(base=float("nan")), 7), (dict(ws=FAKE + 0x1000010), 4),
+])
+@cpu_only
+def test_layer_rejects_invalid_arguments(lib, kw, code):
+    assert _layer(lib, **kw) == code
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 2, 8, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sqa.sqa_attn_fwd(q, q[:, :1].contiguous(), q[:, :1].contiguous())
