@@ -81,14 +81,13 @@ def time_variant(sqa, torch, q, k, v, scale, causal, steps, warmup):
     return start.elapsed_time(end) / steps, wall, out
 
 
-def cpu_baseline(w, variant, causal, rows_count):
+def cpu_baseline(w, variant, causal, rows_count, arrays):
     import numpy as np
 
     from oracle import attention as oracle_attention
-    from synth import draw_qkv, sample_rows, select_variant
+    from synth import sample_rows, select_variant
     Hq, Hkv = variant
-    q, k, v = select_variant(*draw_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=0, peaky=w.peaky),
-                             Hq, Hkv)
+    q, k, v = select_variant(*arrays, Hq, Hkv)
     rows = sample_rows(w.N, rows_count)
     try:
         cores = len(os.sched_getaffinity(0))
@@ -118,7 +117,10 @@ def main():
     ap.add_argument("--causal", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=16384)
+    ap.add_argument("--cpu-rows", type=int, default=65536)
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
+                         "used to scale rocprofv3 FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -139,6 +141,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_calib:
+        n = args.copy_calib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_per_launch": n}), flush=True)
+        return
 
     w = WORKLOADS[args.workload]
     if w.layer or w.dtype != "bf16":
@@ -188,7 +200,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, variant, causal, args.cpu_rows)
+        cpu = cpu_baseline(w, variant, causal, args.cpu_rows, (q_all, k_all, v_all))
 
     line = {
         "metric": METRIC,

@@ -107,8 +107,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
 template <int D>
 struct TileRegs {
@@ -176,8 +174,113 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* buf, 
   }
 }
 
+// One K/V tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// MASKED adds the causal (key <= t) and tail (key < N) masks; it is used only
+// for a wave's diagonal tile and for the ragged last tile.
+template <int D, bool MASKED>
+__device__ __forceinline__ void process_tile(const uint16_t* ks, const u32x4_t (&qf)[2][Cfg<D>::DSTEPS],
+                                             f32x16_t (&acc_o)[Cfg<D>::DSUB][2], float (&m_run)[2],
+                                             float (&l_run)[2], float c, int key0, int N, int causal,
+                                             int trow0, int l32, int lg) {
+  using C = Cfg<D>;
+  const uint16_t* vs = ks + C::KBUF;
+
+  // S^T[key][query] for 2 key sub-tiles x 2 query sub-tiles
+  f32x16_t s[2][2];
+#pragma unroll
+  for (int kx = 0; kx < 2; ++kx) {
+    bf16x8_t kf[C::DSTEPS];
+#pragma unroll
+    for (int ds = 0; ds < C::DSTEPS; ++ds)
+      kf[ds] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(ks + (kx * 32 + l32) * C::KROW + (ds * 2 + lg) * 8));
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      f32x16_t accs;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) accs[i] = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < C::DSTEPS; ++ds)
+        accs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], as_bf16x8(qf[qs][ds]), accs, 0, 0, 0);
+      s[kx][qs] = accs;
+    }
+  }
+
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int t = trow0 + qs * 32 + l32;
+#pragma unroll
+      for (int kx = 0; kx < 2; ++kx)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + kx * 32 + lg * 16 + i;
+          const bool ok = key < N && (!causal || key <= t);
+          if (!ok) s[kx][qs][i] = -INFINITY;
+        }
+    }
+  }
+
+  // online softmax (fp32), lazily raised running maximum
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  uint32_t pk[2][2][2][4];  // [kx][qs][half][word] bf16 pairs
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    float mx = s[0][qs][0];
+#pragma unroll
+    for (int kx = 0; kx < 2; ++kx)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kx][qs][i]);
+    const float cand = (MASKED && mx == -INFINITY) ? -INFINITY : mx * c;
+    const bool need = cand > m_run[qs] + kRescaleSlack;
+    if (__ballot(need)) {
+      const float other = __shfl_xor(cand, 32);
+      const float mnew = fmaxf(m_run[qs], fmaxf(cand, other));
+      const float alpha = (m_run[qs] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[qs] - mnew);
+      m_run[qs] = mnew;
+      l_run[qs] *= alpha;
+#pragma unroll
+      for (int x = 0; x < C::DSUB; ++x)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc_o[x][qs][i] *= alpha;
+    }
+    const float mneg = -m_run[qs];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kx = 0; kx < 2; ++kx)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kx][qs][2 * w], c, mneg));
+        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kx][qs][2 * w + 1], c, mneg));
+        if constexpr (MASKED) {
+          if (s[kx][qs][2 * w] == -INFINITY) p0 = 0.f;
+          if (s[kx][qs][2 * w + 1] == -INFINITY) p1 = 0.f;
+        }
+        const uint32_t pp = pack_bf16x2(p0, p1);
+        pk[kx][qs][w >> 2][w & 3] = pp;
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, lsum, false);
+      }
+    l_run[qs] += lsum;
+  }
+
+  // O^T += V^T P^T
+#pragma unroll
+  for (int x = 0; x < C::DSUB; ++x)
+#pragma unroll
+    for (int kx = 0; kx < 2; ++kx)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
+            vs + (x * 32 + l32) * C::VROW + kx * 32 + lg * 16 + hh * 8));
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          u32x4_t pw = {pk[kx][qs][hh][0], pk[kx][qs][hh][1], pk[kx][qs][hh][2], pk[kx][qs][hh][3]};
+          acc_o[x][qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pw), acc_o[x][qs], 0, 0, 0);
+        }
+      }
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(Args a) {
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Args a) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
 
@@ -271,102 +374,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(Args a) {
 
     if (wave_valid && kt <= wave_last) {
       const uint16_t* ks = smem + cur * C::BUF;
-      const uint16_t* vs = ks + C::KBUF;
-
-      // S^T[key][query] for 2 key sub-tiles x 2 query sub-tiles
-      f32x16_t s[2][2];
-#pragma unroll
-      for (int kx = 0; kx < 2; ++kx) {
-        bf16x8_t kf[C::DSTEPS];
-#pragma unroll
-        for (int ds = 0; ds < C::DSTEPS; ++ds)
-          kf[ds] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
-              ks + (kx * 32 + l32) * C::KROW + (ds * 2 + lg) * 8));
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-          f32x16_t accs;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) accs[i] = 0.f;
-#pragma unroll
-          for (int ds = 0; ds < C::DSTEPS; ++ds)
-            accs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], as_bf16x8(qf[qs][ds]), accs, 0, 0, 0);
-          s[kx][qs] = accs;
-        }
-      }
-
       const int key0 = kt * kTileKeys;
       const bool masked = (a.causal && kt == tb) || (key0 + kTileKeys > N);
-      if (masked) {
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-          const int t = tb * kRowsPerWave + qs * 32 + l32;
-#pragma unroll
-          for (int kx = 0; kx < 2; ++kx)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = key0 + kx * 32 + lg * 16 + i;
-              const bool ok = key < N && (!a.causal || key <= t);
-              if (!ok) s[kx][qs][i] = -INFINITY;
-            }
-        }
-      }
-
-      // online softmax (fp32), lazily raised running maximum
-      uint32_t pk[2][2][2][4];  // [kx][qs][half][word] bf16 pairs
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        float mx = s[0][qs][0];
-#pragma unroll
-        for (int kx = 0; kx < 2; ++kx)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kx][qs][i]);
-        const float cand = (mx == -INFINITY) ? -INFINITY : mx * c;
-        const bool need = cand > m_run[qs] + kRescaleSlack;
-        if (__ballot(need)) {
-          const float other = __shfl_xor(cand, 32);
-          const float mnew = fmaxf(m_run[qs], fmaxf(cand, other));
-          const float alpha = (m_run[qs] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[qs] - mnew);
-          m_run[qs] = mnew;
-          l_run[qs] *= alpha;
-#pragma unroll
-          for (int x = 0; x < C::DSUB; ++x)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc_o[x][qs][i] *= alpha;
-        }
-        const float mneg = -m_run[qs];
-        float lsum = 0.f;
-#pragma unroll
-        for (int kx = 0; kx < 2; ++kx)
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kx][qs][2 * w], c, mneg));
-            float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kx][qs][2 * w + 1], c, mneg));
-            if (masked) {
-              if (s[kx][qs][2 * w] == -INFINITY) p0 = 0.f;
-              if (s[kx][qs][2 * w + 1] == -INFINITY) p1 = 0.f;
-            }
-            const uint32_t pp = pack_bf16x2(p0, p1);
-            pk[kx][qs][w >> 2][w & 3] = pp;
-            lsum += bf16lo(pp) + bf16hi(pp);
-          }
-        l_run[qs] += lsum;
-      }
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int x = 0; x < C::DSUB; ++x)
-#pragma unroll
-        for (int kx = 0; kx < 2; ++kx)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
-                vs + (x * 32 + l32) * C::VROW + kx * 32 + lg * 16 + hh * 8));
-#pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
-              u32x4_t pw = {pk[kx][qs][hh][0], pk[kx][qs][hh][1], pk[kx][qs][hh][2], pk[kx][qs][hh][3]};
-              acc_o[x][qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pw), acc_o[x][qs], 0, 0, 0);
-            }
-          }
+      if (masked)
+        process_tile<D, true>(ks, qf, acc_o, m_run, l_run, c, key0, N, a.causal,
+                              tb * kRowsPerWave, l32, lg);
+      else
+        process_tile<D, false>(ks, qf, acc_o, m_run, l_run, c, key0, N, a.causal,
+                               tb * kRowsPerWave, l32, lg);
     }
 
     if (kt + 1 < nt) store_tile<D>(regs, smem + (cur ^ 1) * C::BUF, tid);
