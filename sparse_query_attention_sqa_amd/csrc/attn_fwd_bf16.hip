@@ -285,7 +285,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, lg = lane >> 5;
 
   // ---- workgroup -> (batch*Hkv, slot range)
@@ -449,7 +450,7 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream) {
-  if (p.D == 64) return launch_d<64>(p, stream);
+  if (p.D == 64) return launch_attn_fwd_bf16_d64(p, stream);
   if (p.D == 16) return launch_d<16>(p, stream);
   return hipErrorInvalidValue;
 }

@@ -21,6 +21,8 @@ struct AttnProblem {
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream);
+// head dim 64, software-pipelined (attn_fwd_bf16_d64.hip)
+hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnProblem& p, hipStream_t stream);
 
 // Projection + RoPE: x [M=B*N, Dm] bf16 times w_q [Dm,Hq*d] | w_k [Dm,Hkv*d] |
