@@ -1,37 +1,57 @@
 // SQA attention forward for head dim 64, bf16 in/out, gfx950: the
 // software-pipelined kernel used for the long-sequence workloads.
 //
-// Same operation as attn_fwd_bf16.hip (query head i attends K/V head
-// floor(i*H_kv/H_q), "GQA ..." page "The idea"; fewer query heads than the
-// baseline, SQA paper abstract), same workgroup/slot decomposition and the
-// same transposed MFMA formulation (S^T = K Q^T, O^T += V^T P^T with
-// v_mfma_f32_32x32x16_bf16, K rows permuted in LDS, V stored transposed).
+// Operation: query head i attends K/V head floor(i*H_kv/H_q) (contiguous
+// query-head groups, "GQA ..." page, "The idea"), with fewer query heads than
+// the baseline (SQA paper abstract); encoder-style or causal.
 //
-// What differs is the schedule. On gfx950 the softmax VALU work (one
-// v_exp_f32 plus ~3 VALU ops per score) costs about as much issue time as the
-// MFMA work per score at d = 64, and the two only overlap when independent
-// VALU and MFMA instructions are interleaved in one instruction stream. Each
-// wave's 64 query rows are therefore two 32-row halves h0/h1 in a two-phase
-// pipeline over K/V tiles j:
+// Decomposition: a workgroup is 4 waves that share one (batch, K/V head);
+// each wave owns 64 query positions of one query head of the group (slots
+// ordered by position block, then head-in-group), so one K/V tile in LDS
+// feeds 256 query rows, and for g = H_q/H_kv >= 2 those rows come from
+// different query heads -- the reuse the grouping offers.
 //
-//   phase A(j): MFMA  P(j-1,h1).V(j-1)   and  S(j,h1) = K(j).Q(h1)
-//               VALU  softmax of S(j,h0)                 -> P(j,h0)
-//   phase B(j): MFMA  P(j,h0).V(j)       and  S(j+1,h0) = K(j+1).Q(h0)
-//               VALU  softmax of S(j,h1)                 -> P(j,h1)
+// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
+// (A = K tile from LDS, B = Q in registers), so the score accumulator already
+// is the B operand of O^T += V^T P^T and probabilities never leave registers.
+// K rows sit in LDS under the permutation pi, making each lane's 16 scores 16
+// consecutive keys.
 //
-// with 32-key tiles, so each phase has 8 MFMAs and the softmax of 32x32
-// scores that do not depend on them. K/V tiles go HBM -> registers -> a
-// 3-deep LDS ring with one barrier per tile; K(j) and V(j) fragments are read
-// from LDS once per tile and kept in registers for both halves. The live set
-// (~230 VGPRs) allows two waves per SIMD.
+// Schedule. At d = 64 the softmax VALU work per score (one v_exp_f32 at half
+// rate plus ~2.5 other VALU ops) costs about as much issue time as the MFMA
+// work per score, and the two overlap only when independent MFMA and VALU
+// instructions are interleaved. Each wave's 64 rows are two 32-row halves in
+// a two-phase pipeline over 32-key tiles j:
 //
-// The running maximum is raised lazily: probabilities are computed against
-// the current maximum m, and only if a lane's sum of its 16 probabilities
-// exceeds 2^20 (or is not finite -- always the case on the first tile, where
-// m = -inf) is the exact row maximum taken, O and l rescaled and the tile's
-// probabilities recomputed. Between refreshes every probability is <= 2^20,
-// far inside the bf16/fp32 range, and the result equals the max-subtracted
-// softmax up to rounding.
+//   phase A(j): MFMA  P(j-1,h1).V(j-1)  and  S(j,h1) = K(j).Q(h1)
+//               VALU  softmax of S(j,h0)                -> P(j,h0)
+//   phase B(j): MFMA  P(j,h0).V(j)      and  S(j+1,h0) = K(j+1).Q(h0)
+//               VALU  softmax of S(j,h1)                -> P(j,h1)
+//
+// with sched_group_barrier hints alternating one MFMA with six VALU ops.
+//
+// Data movement. K and V tiles go straight from HBM to LDS with
+// buffer_load ... lds (no register staging), into a 4-slot ring with three
+// tiles of lookahead and one barrier per tile; the buffer descriptor's range
+// check zero-fills keys past N. Both tiles are stored row-major (128 B rows)
+// with an XOR swizzle of their 16-byte chunks; K fragments are 16-byte
+// ds_read_b128, and V^T fragments come from ds_read_b64_tr_b16, whose
+// 16-lane transpose hands each lane 4 consecutive keys of one head-dim
+// column. With the loop unrolled over the ring slots every LDS address is a
+// per-lane register plus an immediate, so the per-tile barrier block has no
+// VALU work.
+//
+// Softmax. fp32, base-2 exponentials of s*c - m with c = |scale|*log2(e);
+// probabilities are rounded to bf16 (nearest even) for the P.V MFMA and the
+// row sum adds the same rounded values (v_dot2c_f32_bf16). The running
+// maximum m is raised lazily: probabilities are computed against the current
+// m and only if a lane's sum of its 16 probabilities exceeds 2^20 (or is not
+// finite, as on the first tile where m = -inf) is the exact row maximum
+// taken, O and l rescaled and the tile recomputed; between refreshes every
+// probability is <= 2^20, far inside the bf16/fp32 range. Masked scores
+// (causal key > t, tail key >= N) are replaced by a large negative value,
+// only on diagonal and tail tiles, so one branch-free phase body serves all
+// tiles.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -47,22 +67,24 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int D = 64;
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 64;
-constexpr int kTileKeys = 32;         // keys per K/V tile (one 32-row MFMA block)
-constexpr int KROW = D + 8;            // bf16 elements per LDS row of K (144 B)
-constexpr int VROW = kTileKeys + 8;    // bf16 elements per LDS row of V^T (80 B)
-constexpr int KBUF = kTileKeys * KROW;
-constexpr int VBUF = D * VROW;
-constexpr int BUF = KBUF + VBUF;
-constexpr int NBUF = 3;
+constexpr int kTileKeys = 32;                      // keys per K/V tile
+constexpr int kRowBytes = D * 2;                   // 128 B per key row
+constexpr int kTileBytes = kTileKeys * kRowBytes;  // 4 KB (K or V)
+constexpr int kSlotBytes = 2 * kTileBytes;         // K then V
+constexpr int NBUF = 4;                            // ring slots
 constexpr int kXcds = 8;
-constexpr float kSumLimit = 1048576.0f;  // 2^20
+constexpr float kSumLimit = 1048576.0f;            // 2^20
 constexpr float kMaskedScore = -3.0e38f;
-constexpr float kMinC = 1e-30f;          // |scale|*log2(e) is clamped up to this
+constexpr float kMinC = 1e-30f;                    // |scale|*log2(e) is clamped up to this
+constexpr int kBufferWord3 = 0x00020000;           // raw buffer descriptor flags (gfx9)
 
 struct Args {
   const uint16_t* q;
@@ -71,79 +93,98 @@ struct Args {
   uint16_t* o;
   float* lse;
   int N, Hq, Hkv, g;
-  int TB;          // ceil(N / 64): 64-row query blocks per head
-  int NT;          // ceil(N / 32): 32-key tiles
+  int TB;   // ceil(N / 64): 64-row query blocks per head
+  int NT;   // ceil(N / 32): 32-key tiles
   int wg_per_bkv, n_bkv, nwg;
   float c;
   uint32_t qsign;
   int causal;
 };
 
-__device__ __forceinline__ int pi_inv(int p) { return ((p & 15) >> 2) * 8 + (p >> 4) * 4 + (p & 3); }
+// MFMA row r of a K tile holds key pi(r), so that S^T entry i of lane-half lg
+// is key lg*16 + i.
+__device__ __forceinline__ int pi_row(int r) { return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3); }
+// 16-byte chunk swizzles of the K and V tiles (bank-conflict-free reads)
+__device__ __forceinline__ int swz_k(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_v(int r) { return 2 * (r & 3); }
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2_t f = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-struct Staged {
-  u32x4_t k;     // 8 d of one key
-  u32x2_t v[2];  // 4 d of two consecutive keys
+// Wait for this wave's LDS reads and for all but the newest tile's DMA (or
+// for every DMA), then synchronise the workgroup.
+__device__ __forceinline__ void wait_vm_then_barrier(bool keep_one_tile) {
+  asm volatile("" ::: "memory");
+  if (keep_one_tile)
+    __builtin_amdgcn_s_waitcnt(0x0072);  // vmcnt(2) lgkmcnt(0)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The ring slots are separate __shared__ objects so that the compiler can
+// tell an LDS read of one slot from the DMA still in flight into another.
+struct Ring {
+  uint8_t* p[NBUF];
 };
 
-// HBM -> registers for tile kt (key rows clamped into [0, N)).
-__device__ __forceinline__ void load_tile(Staged& r, const uint16_t* kbase, const uint16_t* vbase, int kt,
-                                          int N, int tid) {
+struct Lane {
+  int l32, lg;
+  uint32_t voff_k, voff_v;  // DMA source offsets within a tile (bytes)
+  uint32_t koff[4];         // K fragment LDS offsets within a slot
+  uint32_t voffr[2];        // V^T transposed-read LDS offsets within a slot (x = 0, 1)
+};
+
+struct WaveState {
+  u32x4_t qf[2][4];
+  f32x16_t acc_o[2][2];  // [half][x]
+  float m_run[2], l_run[2];
+  u32x4_t kf[4];
+  u32x4_t vf[2][2];
+  f32x16_t sA, sB;
+  u32x4_t pk0[2], pk1[2];
+};
+
+// DMA K/V tile kt into ring slot SLOT: one 16-byte chunk per lane of each.
+template <int SLOT>
+__device__ __forceinline__ void issue_tile(const Ring& ring, const uint16_t* kbase, const uint16_t* vbase, int kt,
+                                           int N, int wave, const Lane& ln) {
   const int key0 = kt * kTileKeys;
-  {
-    const int key = tid >> 3, dc = tid & 7;
-    const int row = min(key0 + key, N - 1);
-    r.k = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)row * D + dc * 8);
-  }
-  const int kp = tid >> 4, dg = tid & 15;
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int row = min(key0 + 2 * kp + rr, N - 1);
-    r.v[rr] = *reinterpret_cast<const u32x2_t*>(vbase + (size_t)row * D + dg * 4);
-  }
+  const int rem = (N - key0) * kRowBytes;  // bytes of this head from key0 on
+  __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (size_t)key0 * D), (short)0, rem, kBufferWord3);
+  __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (size_t)key0 * D), (short)0, rem, kBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(ring.p[SLOT] + wave * 1024), 16, ln.voff_k, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(ring.p[SLOT] + kTileBytes + wave * 1024), 16,
+                                           ln.voff_v, 0, 0, 0);
 }
 
-// registers -> LDS: K rows under pi_inv; V transposed (2 keys x 4 d blocks).
-__device__ __forceinline__ void store_tile(const Staged& r, uint16_t* buf, int tid) {
-  uint16_t* ks = buf;
-  uint16_t* vs = buf + KBUF;
-  {
-    const int key = tid >> 3, dc = tid & 7;
-    *reinterpret_cast<u32x4_t*>(ks + pi_inv(key) * KROW + dc * 8) = r.k;
-  }
-  const int kp = tid >> 4, dg = tid & 15;
+template <int SLOT>
+__device__ __forceinline__ void read_k(const Ring& ring, const Lane& ln, u32x4_t (&kf)[4]) {
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
-    const int word = cc >> 1;
-    const bool hi = cc & 1;
-    const uint32_t e0 = hi ? (r.v[0][word] >> 16) : (r.v[0][word] & 0xffffu);
-    const uint32_t e1 = hi ? (r.v[1][word] >> 16) : (r.v[1][word] & 0xffffu);
-    const int d = dg * 4 + cc;
-    const int lrow = (d & ~31) + pi_inv(d & 31);
-    *reinterpret_cast<uint32_t*>(vs + lrow * VROW + 2 * kp) = e0 | (e1 << 16);
-  }
+  for (int ds = 0; ds < 4; ++ds) kf[ds] = *reinterpret_cast<const u32x4_t*>(ring.p[SLOT] + ln.koff[ds]);
 }
 
-// K(j) fragments (A operand of S^T): [ds]
-__device__ __forceinline__ void read_k(const uint16_t* buf, u32x4_t (&kf)[4], int l32, int lg) {
-#pragma unroll
-  for (int ds = 0; ds < 4; ++ds)
-    kf[ds] = *reinterpret_cast<const u32x4_t*>(buf + l32 * KROW + (ds * 2 + lg) * 8);
-}
-
-// V(j)^T fragments (A operand of O^T): [x][hh]
-__device__ __forceinline__ void read_v(const uint16_t* buf, u32x4_t (&vf)[2][2], int l32, int lg) {
-  const uint16_t* vs = buf + KBUF;
+// V^T fragments [x][hh]: the 8 keys lg*16 + hh*8 + 0..7 of head-dim row
+// x*32 + l32, as two transposed 4-key reads.
+template <int SLOT>
+__device__ __forceinline__ void read_v(const Ring& ring, const Lane& ln, u32x4_t (&vf)[2][2]) {
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      vf[x][hh] = *reinterpret_cast<const u32x4_t*>(vs + (x * 32 + l32) * VROW + lg * 16 + hh * 8);
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint8_t* p = ring.p[SLOT] + kTileBytes + ln.voffr[x] + hh * 8 * kRowBytes;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * kRowBytes));
+      const u32x2_t a = __builtin_bit_cast(u32x2_t, lo);
+      const u32x2_t b = __builtin_bit_cast(u32x2_t, hi);
+      vf[x][hh] = u32x4_t{a[0], a[1], b[0], b[1]};
+    }
 }
 
 __device__ __forceinline__ void mfma_s(const u32x4_t (&kf)[4], const u32x4_t (&q)[4], f32x16_t& s) {
@@ -164,9 +205,9 @@ __device__ __forceinline__ void mfma_pv(const u32x4_t (&vf)[2][2], const u32x4_t
       o[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[x][hh]), as_bf16x8(pk[hh]), o[x], 0, 0, 0);
 }
 
-// Scores of keys a query may not see (causal: key > t; ragged tail:
-// key >= N) become kMaskedScore, whose probability underflows to exactly 0
-// for any c >= kMinC. Only diagonal and tail tiles need this.
+// Scores of keys a query may not see (causal: key > t; tail: key >= N)
+// become kMaskedScore, whose probability underflows to exactly 0 for any
+// c >= kMinC. Only diagonal and tail tiles need this.
 __device__ __forceinline__ void mask_scores(f32x16_t& s, int key0, int N, int causal, int t, int lg) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -176,8 +217,8 @@ __device__ __forceinline__ void mask_scores(f32x16_t& s, int key0, int N, int ca
 }
 
 // probabilities of one 32-row half against the current maximum m, rounded to
-// bf16 (nearest even) and packed as the B operand of O^T += V^T P^T; returns
-// the lane's sum of its 16 rounded probabilities.
+// bf16 and packed as the B operand of O^T += V^T P^T; returns the lane's sum
+// of its 16 rounded probabilities.
 __device__ __forceinline__ float exp_half(const f32x16_t& s, u32x4_t (&pk)[2], float c, float m) {
   const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
   const float mneg = -m;
@@ -194,8 +235,8 @@ __device__ __forceinline__ float exp_half(const f32x16_t& s, u32x4_t (&pk)[2], f
 }
 
 // Finish the softmax of one half: if a lane's probabilities grew too large
-// (or the running maximum was still -inf), take the exact row maximum,
-// rescale O and l, and recompute the tile's probabilities.
+// (or m was still -inf), take the exact row maximum, rescale O and l and
+// recompute the tile's probabilities.
 __device__ __forceinline__ void finish_half(float lsum, const f32x16_t& s, u32x4_t (&pk)[2], float& m, float& l,
                                             f32x16_t (&o)[2], float c) {
   if (__ballot(!(lsum <= kSumLimit))) {
@@ -227,16 +268,71 @@ __device__ __forceinline__ void interleave_phase() {
   }
 }
 
+struct Ctx {
+  Ring ring;
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  int N, nt, last, tb, causal, wave;
+  int t0, t1;
+  float c;
+};
+
+// One pipeline step over tile j, whose K/V sit in ring slot SLOT = j % NBUF.
+template <int SLOT>
+__device__ __forceinline__ void step(const Ctx& cx, const Lane& ln, WaveState& w, int j) {
+  constexpr int NEXT = (SLOT + 1) % NBUF;
+  constexpr int AHEAD = (SLOT + 3) % NBUF;
+  const int key0 = j * kTileKeys;
+  const bool active = j <= cx.last;
+  const bool masked = (cx.causal && j >= 2 * cx.tb) || (key0 + kTileKeys > cx.N);
+
+  // ---------------- phase A(j)
+  if (active) {
+    if (masked) mask_scores(w.sB, key0, cx.N, cx.causal, cx.t0, ln.lg);
+    mfma_pv(w.vf, w.pk1, w.acc_o[1]);  // P(j-1,h1) V(j-1)
+    read_v<SLOT>(cx.ring, ln, w.vf);   // V(j), used from phase B on
+    mfma_s(w.kf, w.qf[1], w.sA);       // S(j,h1); K(j) is in kf
+    const float ls = exp_half(w.sB, w.pk0, cx.c, w.m_run[0]);
+    interleave_phase();
+    finish_half(ls, w.sB, w.pk0, w.m_run[0], w.l_run[0], w.acc_o[0], cx.c);
+  }
+
+  // tile j+1 must have landed (tile j+2 may still be in flight); every wave
+  // is done with tile j-1, whose slot receives tile j+3.
+  wait_vm_then_barrier(j + 2 < cx.nt);
+  if (j + 3 < cx.nt) issue_tile<AHEAD>(cx.ring, cx.kbase, cx.vbase, j + 3, cx.N, cx.wave, ln);
+
+  // ---------------- phase B(j); S(j+1,h0) is computed even past the wave's
+  // last tile (then unused) so the phase stays branch-free.
+  if (active) {
+    if (masked) mask_scores(w.sA, key0, cx.N, cx.causal, cx.t1, ln.lg);
+    read_k<NEXT>(cx.ring, ln, w.kf);   // K(j+1)
+    mfma_pv(w.vf, w.pk0, w.acc_o[0]);  // P(j,h0) V(j)
+    mfma_s(w.kf, w.qf[0], w.sB);       // S(j+1,h0)
+    const float ls = exp_half(w.sA, w.pk1, cx.c, w.m_run[1]);
+    interleave_phase();
+    finish_half(ls, w.sA, w.pk1, w.m_run[1], w.l_run[1], w.acc_o[1], cx.c);
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring3[kSlotBytes];
+  Ring ring;
+  ring.p[0] = ring0;
+  ring.p[1] = ring1;
+  ring.p[2] = ring2;
+  ring.p[3] = ring3;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, lg = lane >> 5;
 
+  // ---- workgroup -> (batch*Hkv, slot range)
   int L;
-  if (!a.causal) {
+  if (!a.causal) {  // consecutive logical workgroups on one XCD (shared L2)
     const int bid = blockIdx.x;
     const int per = a.nwg / kXcds, rem = a.nwg % kXcds;
     const int x = bid % kXcds, i = bid / kXcds;
@@ -248,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   if (!a.causal) {
     bkv = L / a.wg_per_bkv;
     w_in = L % a.wg_per_bkv;
-  } else {
+  } else {  // longest (largest position block) first
     const int wr = L / a.n_bkv;
     bkv = L % a.n_bkv;
     w_in = a.wg_per_bkv - 1 - wr;
@@ -266,120 +362,116 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   const int last = !wave_valid ? -1 : (a.causal ? min(2 * tb + 1, a.NT - 1) : a.NT - 1);
   const int trow0 = tb * kRowsPerWave;
 
+  Lane ln;
+  ln.l32 = lane & 31;
+  ln.lg = lane >> 5;
+  {
+    const int r = wave * 8 + (lane >> 3), s = lane & 7;
+    ln.voff_k = (uint32_t)(pi_row(r) * kRowBytes + ((s ^ swz_k(r)) * 16));
+    ln.voff_v = (uint32_t)(r * kRowBytes + ((s ^ swz_v(r)) * 16));
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+      ln.koff[ds] = (uint32_t)(ln.l32 * kRowBytes + (((ds * 2 + ln.lg) ^ swz_k(ln.l32)) * 16));
+    const int j16 = lane & 15, g1 = (lane >> 4) & 1;
+    const int row = ln.lg * 16 + (j16 >> 2);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int c16 = x * 4 + 2 * g1 + ((j16 & 3) >> 1);
+      ln.voffr[x] = (uint32_t)(row * kRowBytes + ((c16 ^ swz_v(row)) * 16) + (j16 & 1) * 8);
+    }
+  }
+
   const uint16_t* kbase = a.k + (size_t)bkv * N * D;
   const uint16_t* vbase = a.v + (size_t)bkv * N * D;
   const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)N * D;
 
-  u32x4_t qf[2][4];
+  WaveState w;
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
-    const int t = min(trow0 + qs * 32 + l32, N - 1);
+    const int t = min(trow0 + qs * 32 + ln.l32, N - 1);
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
       u32x4_t x = {0u, 0u, 0u, 0u};
-      if (wave_valid) x = *reinterpret_cast<const u32x4_t*>(a.q + qoff + (size_t)t * D + (ds * 2 + lg) * 8);
+      if (wave_valid) x = *reinterpret_cast<const u32x4_t*>(a.q + qoff + (size_t)t * D + (ds * 2 + ln.lg) * 8);
       x ^= a.qsign;
-      qf[qs][ds] = x;
+      w.qf[qs][ds] = x;
     }
   }
-
-  f32x16_t acc_o[2][2];  // [half][x]
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc_o[hh][x][i] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  const float c = a.c;
-  const int t0 = trow0 + l32, t1 = trow0 + 32 + l32;
-
-  // prologue: tiles 0 and 1 resident, tile 2 in flight, S(0,h0) issued
-  Staged st;
-  load_tile(st, kbase, vbase, 0, N, tid);
-  store_tile(st, smem, tid);
-  if (nt > 1) {
-    load_tile(st, kbase, vbase, 1, N, tid);
-    store_tile(st, smem + BUF, tid);
-  }
-  if (nt > 2) load_tile(st, kbase, vbase, 2, N, tid);
-  __syncthreads();
-
-  u32x4_t kf[4];
-  u32x4_t vf[2][2];
-  f32x16_t sA, sB;
-  u32x4_t pk0[2], pk1[2];
+      for (int i = 0; i < 16; ++i) w.acc_o[hh][x][i] = 0.f;
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    pk1[x] = u32x4_t{0u, 0u, 0u, 0u};  // P(-1,h1) = 0: the first phase A's P.V is a no-op
-    vf[x][0] = u32x4_t{0u, 0u, 0u, 0u};
-    vf[x][1] = u32x4_t{0u, 0u, 0u, 0u};
+    w.pk1[x] = u32x4_t{0u, 0u, 0u, 0u};  // P(-1,h1) = 0: the first phase A's P.V is a no-op
+    w.vf[x][0] = u32x4_t{0u, 0u, 0u, 0u};
+    w.vf[x][1] = u32x4_t{0u, 0u, 0u, 0u};
   }
-  read_k(smem, kf, l32, lg);
-  mfma_s(kf, qf[0], sB);
+  w.m_run[0] = w.m_run[1] = -INFINITY;
+  w.l_run[0] = w.l_run[1] = 0.f;
 
-  for (int j = 0; j < nt; ++j) {
-    const uint16_t* bj = smem + (j % NBUF) * BUF;
-    const uint16_t* bn = smem + ((j + 1) % NBUF) * BUF;
-    const int key0 = j * kTileKeys;
-    const bool active = j <= last;
-    const bool masked = (a.causal && j >= 2 * tb) || (key0 + kTileKeys > N);
+  // zero the ring once so that no LDS byte is ever uninitialised
+#pragma unroll
+  for (int sl = 0; sl < NBUF; ++sl)
+    for (int e = tid; e < kSlotBytes / 16; e += kThreads)
+      reinterpret_cast<u32x4_t*>(ring.p[sl])[e] = u32x4_t{0u, 0u, 0u, 0u};
+  wait_vm_then_barrier(false);
 
-    // ---------------- phase A(j)
-    if (active) {
-      if (masked) mask_scores(sB, key0, N, a.causal, t0, lg);
-      mfma_pv(vf, pk1, acc_o[1]);    // P(j-1,h1) V(j-1)
-      read_v(bj, vf, l32, lg);       // V(j), used from phase B on
-      mfma_s(kf, qf[1], sA);         // S(j,h1); K(j) is in kf
-      const float ls = exp_half(sB, pk0, c, m_run[0]);
-      interleave_phase();
-      finish_half(ls, sB, pk0, m_run[0], l_run[0], acc_o[0], c);
-    }
+  // prologue: tiles 0..2 in flight, wait for tiles 0 and 1, S(0,h0)
+  issue_tile<0>(ring, kbase, vbase, 0, N, wave, ln);
+  if (nt > 1) issue_tile<1>(ring, kbase, vbase, 1, N, wave, ln);
+  if (nt > 2) issue_tile<2>(ring, kbase, vbase, 2, N, wave, ln);
+  wait_vm_then_barrier(nt > 2);
 
-    __syncthreads();  // every wave is done with tile j-1's buffer
-    if (j + 2 < nt) {
-      store_tile(st, smem + ((j + 2) % NBUF) * BUF, tid);
-      if (j + 3 < nt) load_tile(st, kbase, vbase, j + 3, N, tid);
-    }
+  Ctx cx;
+  cx.ring = ring;
+  cx.kbase = kbase;
+  cx.vbase = vbase;
+  cx.N = N;
+  cx.nt = nt;
+  cx.last = last;
+  cx.tb = tb;
+  cx.causal = a.causal;
+  cx.wave = wave;
+  cx.t0 = trow0 + ln.l32;
+  cx.t1 = trow0 + 32 + ln.l32;
+  cx.c = a.c;
 
-    // ---------------- phase B(j); S(j+1,h0) is computed even past the
-    // wave's last tile (then unused), so the phase stays branch-free.
-    if (active) {
-      if (masked) mask_scores(sA, key0, N, a.causal, t1, lg);
-      read_k(bn, kf, l32, lg);       // K(j+1)
-      mfma_pv(vf, pk0, acc_o[0]);    // P(j,h0) V(j)
-      mfma_s(kf, qf[0], sB);         // S(j+1,h0)
-      const float ls = exp_half(sA, pk1, c, m_run[1]);
-      interleave_phase();
-      finish_half(ls, sA, pk1, m_run[1], l_run[1], acc_o[1], c);
-    }
+  read_k<0>(ring, ln, w.kf);
+  mfma_s(w.kf, w.qf[0], w.sB);
+
+  for (int j = 0; j < nt; j += NBUF) {
+    step<0>(cx, ln, w, j);
+    if (j + 1 < nt) step<1>(cx, ln, w, j + 1);
+    if (j + 2 < nt) step<2>(cx, ln, w, j + 2);
+    if (j + 3 < nt) step<3>(cx, ln, w, j + 3);
   }
-  if (last >= 0) mfma_pv(vf, pk1, acc_o[1]);  // drain P(last,h1) V(last)
+  if (last >= 0) mfma_pv(w.vf, w.pk1, w.acc_o[1]);  // drain P(last,h1) V(last)
 
   if (!wave_valid) return;
 
+  // ---- epilogue: O = O^T / l (bf16, nearest even); LSE = m ln2 + ln l
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
-    const float ltot = l_run[qs] + __shfl_xor(l_run[qs], 32);
+    const float ltot = w.l_run[qs] + __shfl_xor(w.l_run[qs], 32);
     const float inv = 1.0f / ltot;
-    const int t = trow0 + qs * 32 + l32;
+    const int t = trow0 + qs * 32 + ln.l32;
     if (t < N) {
+      uint16_t* orow = a.o + qoff + (size_t)t * D;
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int d0 = x * 32 + lg * 16;
-        u32x4_t w0, w1;
+      for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w0[e] = pack_bf16x2(acc_o[qs][x][2 * e] * inv, acc_o[qs][x][2 * e + 1] * inv);
-          w1[e] = pack_bf16x2(acc_o[qs][x][8 + 2 * e] * inv, acc_o[qs][x][8 + 2 * e + 1] * inv);
+        for (int ab = 0; ab < 4; ++ab) {
+          // accumulator entries 4ab..4ab+3 are head dims x*32 + 8ab + 4lg + 0..3
+          u32x2_t wv;
+          wv[0] = pack_bf16x2(w.acc_o[qs][x][4 * ab] * inv, w.acc_o[qs][x][4 * ab + 1] * inv);
+          wv[1] = pack_bf16x2(w.acc_o[qs][x][4 * ab + 2] * inv, w.acc_o[qs][x][4 * ab + 3] * inv);
+          *reinterpret_cast<u32x2_t*>(orow + x * 32 + 8 * ab + 4 * ln.lg) = wv;
         }
-        uint16_t* dst = a.o + qoff + (size_t)t * D + d0;
-        *reinterpret_cast<u32x4_t*>(dst) = w0;
-        *reinterpret_cast<u32x4_t*>(dst + 8) = w1;
-      }
-      if (a.lse != nullptr && lg == 0)
-        a.lse[((size_t)b * a.Hq + h) * (size_t)N + t] = (m_run[qs] + log2f(ltot)) * 0.69314718055994531f;
+      if (a.lse != nullptr && ln.lg == 0)
+        a.lse[((size_t)b * a.Hq + h) * (size_t)N + t] = (w.m_run[qs] + log2f(ltot)) * 0.69314718055994531f;
     }
   }
 }
@@ -388,6 +480,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
 
 hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream) {
   if (p.D != D) return hipErrorInvalidValue;
+  if (p.N * kRowBytes > 0x7fffffffLL) return hipErrorInvalidValue;  // buffer descriptor range
   Args a;
   a.q = static_cast<const uint16_t*>(p.q);
   a.k = static_cast<const uint16_t*>(p.k);
