@@ -42,13 +42,17 @@ def counted_flops(B, Hq, N, d, causal):
     return f / 2 if causal else f
 
 
-def kernel_source_hash() -> str:
-    p = os.path.join(ROOT, "sparse_query_attention_sqa_amd", "csrc", "attn_fwd_bf16.hip")
-    with open(p, "rb") as f:
+def kernel_source(d: int) -> str:
+    name = "attn_fwd_bf16_d64.hip" if d == 64 else "attn_fwd_bf16.hip"
+    return os.path.join(ROOT, "sparse_query_attention_sqa_amd", "csrc", name)
+
+
+def kernel_source_hash(d: int = 64) -> str:
+    with open(kernel_source(d), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic(workload: str, variant, causal: int):
+def stored_traffic(workload: str, variant, causal: int, d: int):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, only if
     it was taken on the current kernel source."""
     try:
@@ -58,7 +62,7 @@ def stored_traffic(workload: str, variant, causal: int):
         return None
     key = f"{workload}:{variant[0]},{variant[1]}:c{causal}"
     e = t.get("entries", {}).get(key)
-    if not e or t.get("kernel_sha256_16") != kernel_source_hash():
+    if not e or e.get("kernel_sha256_16") != kernel_source_hash(d):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -111,7 +115,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long32k_bf16")
     ap.add_argument("--variant", default=None, help="H_q,H_kv (default: the workload's first)")
     ap.add_argument("--causal", type=int, default=None)
@@ -191,11 +195,11 @@ def main():
             comparison["speedup_vs_mha"] = round(comparison["16,16"]["ms"] / ms, 3)
             comparison["expected_H_over_Hq"] = w.H / Hq
 
-    traffic = stored_traffic(w.name, variant, causal)
+    traffic = stored_traffic(w.name, variant, causal, w.d)
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic,
-                "kernel": "attn_fwd_bf16_kernel<64>" if w.d == 64 else "attn_fwd_bf16_kernel<16>",
+                "kernel": "attn_fwd_bf16_d64_kernel" if w.d == 64 else "attn_fwd_bf16_kernel<16>",
                 "per_launch_flop": flops}
 
     cpu = None

@@ -31,19 +31,21 @@
 // with sched_group_barrier hints alternating one MFMA with six VALU ops.
 //
 // Data movement. K and V tiles go straight from HBM to LDS with
-// buffer_load ... lds (no register staging), into a 4-slot ring with three
+// buffer_load ... lds (no register staging), into a 5-slot ring with four
 // tiles of lookahead and one barrier per tile; the buffer descriptor's range
 // check zero-fills keys past N. Both tiles are stored row-major (128 B rows)
 // with an XOR swizzle of their 16-byte chunks; K fragments are 16-byte
 // ds_read_b128, and V^T fragments come from ds_read_b64_tr_b16, whose
 // 16-lane transpose hands each lane 4 consecutive keys of one head-dim
-// column. With the loop unrolled over the ring slots every LDS address is a
-// per-lane register plus an immediate, so the per-tile barrier block has no
-// VALU work.
+// column. K(j+1) is already resident during phase A(j), so its fragments are
+// read there, ahead of the MFMAs of phase B(j) that use them. With the loop
+// unrolled over the ring slots every LDS address is a per-lane register plus
+// an immediate, so the per-tile barrier block has no VALU work.
 //
 // Softmax. fp32, base-2 exponentials of s*c - m with c = |scale|*log2(e);
 // probabilities are rounded to bf16 (nearest even) for the P.V MFMA and the
-// row sum adds the same rounded values (v_dot2c_f32_bf16). The running
+// row sum adds the same rounded values (v_dot2c_f32_bf16, two partial sums).
+// The running
 // maximum m is raised lazily: probabilities are computed against the current
 // m and only if a lane's sum of its 16 probabilities exceeds 2^20 (or is not
 // finite, as on the first tile where m = -inf) is the exact row maximum
@@ -79,7 +81,7 @@ constexpr int kTileKeys = 32;                      // keys per K/V tile
 constexpr int kRowBytes = D * 2;                   // 128 B per key row
 constexpr int kTileBytes = kTileKeys * kRowBytes;  // 4 KB (K or V)
 constexpr int kSlotBytes = 2 * kTileBytes;         // K then V
-constexpr int NBUF = 4;                            // ring slots
+constexpr int NBUF = 5;                            // ring slots
 constexpr int kXcds = 8;
 constexpr float kSumLimit = 1048576.0f;            // 2^20
 constexpr float kMaskedScore = -3.0e38f;
@@ -222,16 +224,17 @@ __device__ __forceinline__ void mask_scores(f32x16_t& s, int key0, int N, int ca
 __device__ __forceinline__ float exp_half(const f32x16_t& s, u32x4_t (&pk)[2], float c, float m) {
   const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
   const float mneg = -m;
-  float lsum = 0.f;
+  float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * w], c, mneg));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * w + 1], c, mneg));
     const uint32_t pp = pack_bf16x2(p0, p1);
     pk[w >> 2][w & 3] = pp;
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, lsum, false);
+    if (w & 1) ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, ls1, false);
+    else ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, ls0, false);
   }
-  return lsum;
+  return ls0 + ls1;
 }
 
 // Finish the softmax of one half: if a lane's probabilities grew too large
@@ -281,7 +284,7 @@ struct Ctx {
 template <int SLOT>
 __device__ __forceinline__ void step(const Ctx& cx, const Lane& ln, WaveState& w, int j) {
   constexpr int NEXT = (SLOT + 1) % NBUF;
-  constexpr int AHEAD = (SLOT + 3) % NBUF;
+  constexpr int AHEAD = (SLOT + 4) % NBUF;
   const int key0 = j * kTileKeys;
   const bool active = j <= cx.last;
   const bool masked = (cx.causal && j >= 2 * cx.tb) || (key0 + kTileKeys > cx.N);
@@ -292,21 +295,20 @@ __device__ __forceinline__ void step(const Ctx& cx, const Lane& ln, WaveState& w
     mfma_pv(w.vf, w.pk1, w.acc_o[1]);  // P(j-1,h1) V(j-1)
     read_v<SLOT>(cx.ring, ln, w.vf);   // V(j), used from phase B on
     mfma_s(w.kf, w.qf[1], w.sA);       // S(j,h1); K(j) is in kf
+    read_k<NEXT>(cx.ring, ln, w.kf);   // K(j+1), resident since the last barrier
     const float ls = exp_half(w.sB, w.pk0, cx.c, w.m_run[0]);
     interleave_phase();
     finish_half(ls, w.sB, w.pk0, w.m_run[0], w.l_run[0], w.acc_o[0], cx.c);
   }
 
-  // tile j+1 must have landed (tile j+2 may still be in flight); every wave
-  // is done with tile j-1, whose slot receives tile j+3.
-  wait_vm_then_barrier(j + 2 < cx.nt);
-  if (j + 3 < cx.nt) issue_tile<AHEAD>(cx.ring, cx.kbase, cx.vbase, j + 3, cx.N, cx.wave, ln);
+  // tiles j+1 and j+2 must have landed (tile j+3 may still be in flight);
+  // every wave is done with tile j-1, whose slot receives tile j+4.
+  wait_vm_then_barrier(j + 3 < cx.nt);
+  if (j + 4 < cx.nt) issue_tile<AHEAD>(cx.ring, cx.kbase, cx.vbase, j + 4, cx.N, cx.wave, ln);
 
-  // ---------------- phase B(j); S(j+1,h0) is computed even past the wave's
-  // last tile (then unused) so the phase stays branch-free.
+  // ---------------- phase B(j)
   if (active) {
     if (masked) mask_scores(w.sA, key0, cx.N, cx.causal, cx.t1, ln.lg);
-    read_k<NEXT>(cx.ring, ln, w.kf);   // K(j+1)
     mfma_pv(w.vf, w.pk0, w.acc_o[0]);  // P(j,h0) V(j)
     mfma_s(w.kf, w.qf[0], w.sB);       // S(j+1,h0)
     const float ls = exp_half(w.sA, w.pk1, cx.c, w.m_run[1]);
@@ -320,11 +322,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   __shared__ __attribute__((aligned(16))) uint8_t ring1[kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ring2[kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ring3[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring4[kSlotBytes];
   Ring ring;
   ring.p[0] = ring0;
   ring.p[1] = ring1;
   ring.p[2] = ring2;
   ring.p[3] = ring3;
+  ring.p[4] = ring4;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -419,11 +423,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
       reinterpret_cast<u32x4_t*>(ring.p[sl])[e] = u32x4_t{0u, 0u, 0u, 0u};
   wait_vm_then_barrier(false);
 
-  // prologue: tiles 0..2 in flight, wait for tiles 0 and 1, S(0,h0)
+  // prologue: tiles 0..3 in flight, wait for tiles 0..2, S(0,h0)
   issue_tile<0>(ring, kbase, vbase, 0, N, wave, ln);
   if (nt > 1) issue_tile<1>(ring, kbase, vbase, 1, N, wave, ln);
   if (nt > 2) issue_tile<2>(ring, kbase, vbase, 2, N, wave, ln);
-  wait_vm_then_barrier(nt > 2);
+  if (nt > 3) issue_tile<3>(ring, kbase, vbase, 3, N, wave, ln);
+  wait_vm_then_barrier(nt > 3);
 
   Ctx cx;
   cx.ring = ring;
@@ -447,6 +452,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
     if (j + 1 < nt) step<1>(cx, ln, w, j + 1);
     if (j + 2 < nt) step<2>(cx, ln, w, j + 2);
     if (j + 3 < nt) step<3>(cx, ln, w, j + 3);
+    if (j + 4 < nt) step<4>(cx, ln, w, j + 4);
   }
   if (last >= 0) mfma_pv(w.vf, w.pk1, w.acc_o[1]);  // drain P(last,h1) V(last)
 
