@@ -111,6 +111,88 @@ def cpu_baseline(w, variant, causal, rows_count, arrays):
                       f"{dt:.2f} s wall"}
 
 
+# v_exp_f32 issues at half rate: 64 lanes / 8 cycles per SIMD, 1024 SIMDs, 2.4 GHz
+PEAK_EXP_PER_S = 1024 * 8 * 2.4e9
+
+
+def _timed(torch, fn, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _common(args, ms, w, extra):
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "data": "synthetic"}
+    line.update(extra)
+    return line
+
+
+def bench_layer(sqa, torch, w, args):
+    """SQAT-m attention layer: projections + RoPE + causal SQA + output projection."""
+    from synth import draw_layer
+    Hq, Hkv = w.variants[0]
+    d = w.d_model // w.H
+    x, wq, wk, wv, wo = draw_layer(w.B, w.N, w.d_model, w.H, Hq, Hkv, seed=0)
+    dev = lambda a: torch.from_numpy(a).to("cuda").to(torch.bfloat16).contiguous()
+    tx, tq, tk, tv, to = (dev(a) for a in (x, wq, wk, wv, wo))
+    out = torch.empty_like(tx)
+    ws = torch.empty(sqa.sqa_layer_workspace_bytes(w.B, w.N, w.d_model, w.H, Hq, Hkv),
+                     dtype=torch.uint8, device="cuda")
+    fn = lambda: sqa.sqa_layer_fwd(tx, tq, tk, tv, to, H=w.H, H_q=Hq, H_kv=Hkv, rope_base=w.rope_base,
+                                   scale=w.scale, causal=True, out=out, workspace=ws)
+    ms = _timed(torch, fn, args.steps, args.warmup)
+    attn = counted_flops(w.B, Hq, w.N, d, True)
+    gemm = 2.0 * w.B * w.N * w.d_model * (Hq + 2 * Hkv) * d + 2.0 * w.B * w.N * Hq * d * w.d_model
+    exps = w.B * Hq * w.N * (w.N + 1) / 2.0
+    tflops = (attn + gemm) / (ms * 1e-3) / 1e12
+    achieved = exps / (ms * 1e-3) / 1e12
+    return _common(args, ms, w, {
+        "value": round(tflops, 3), "unit": "TFLOP/s", "dtype": "bf16",
+        "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1),
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.d_model, "H": w.H, "H_q": Hq,
+                   "H_kv": Hkv, "d": d, "causal": 1, "flop_attention": attn, "flop_gemm": gemm},
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3),
+                     "peak": round(PEAK_EXP_PER_S / 1e12, 3), "unit": "Texp/s",
+                     "frac": round(achieved * 1e12 / PEAK_EXP_PER_S, 4), "traffic": None,
+                     "kernel": "whole layer (attention at d=16 is v_exp-bound)"},
+        "cpu_baseline": None, "comparison": None})
+
+
+def bench_f32(sqa, torch, w, args):
+    """SQAT-m attention core in fp32 (VALU-bound correctness workload)."""
+    from synth import draw_qkv, select_variant
+    Hq, Hkv = w.variants[0]
+    causal = w.causal[0] if args.causal is None else args.causal
+    q, k, v = select_variant(*draw_qkv(w.B, w.H, w.N, w.d, "f32", seed=0), Hq, Hkv)
+    dev = lambda a: torch.from_numpy(a).to("cuda").contiguous()
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    out = torch.empty_like(tq)
+    fn = lambda: sqa.sqa_attn_fwd(tq, tk, tv, scale=w.scale, causal=bool(causal), out=out)
+    ms = _timed(torch, fn, args.steps, args.warmup)
+    flops = counted_flops(w.B, Hq, w.N, w.d, causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return _common(args, ms, w, {
+        "value": round(tflops, 4), "unit": "TFLOP/s", "dtype": "f32",
+        "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1),
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "H_q": Hq, "H_kv": Hkv,
+                   "d": w.d, "causal": int(causal), "scale": w.scale},
+        "roofline": {"bound": "alu", "achieved": round(tflops, 4), "peak": PEAK_F32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_F32_TFLOPS, 5), "traffic": None,
+                     "kernel": "attn_fwd_f32_kernel<16>"},
+        "cpu_baseline": None, "comparison": None})
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,9 +239,12 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
-    if w.layer or w.dtype != "bf16":
-        print("bench.py times the bf16 attention workloads", file=sys.stderr)
-        sys.exit(2)
+    if w.layer:
+        print(json.dumps(bench_layer(sqa, torch, w, args)), flush=True)
+        return
+    if w.dtype != "bf16":
+        print(json.dumps(bench_f32(sqa, torch, w, args)), flush=True)
+        return
     variant = tuple(int(x) for x in args.variant.split(",")) if args.variant else w.variants[0]
     causal = w.causal[0] if args.causal is None else args.causal
     Hq, Hkv = variant
