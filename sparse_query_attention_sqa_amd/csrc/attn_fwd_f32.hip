@@ -1,14 +1,17 @@
 // SQA attention forward with fp32 inputs, outputs and arithmetic throughout
-// (no reduced-precision step). Same operation as the bf16 kernel: query head
+// (no reduced-precision step). Same operation as the bf16 kernels: query head
 // i attends K/V head floor(i*H_kv/H_q) ("GQA ..." page, "The idea"; SQA paper
 // abstract), encoder-style or causal.
 //
-// One thread owns one query row; a workgroup is 256 consecutive positions of
-// one (batch, query head). K/V are staged through LDS in 64-key tiles. For
-// each tile a thread computes its 64 scores, raises its running maximum once,
-// rescales its output accumulator, then accumulates exp(s - m) * v. This path
-// serves the small fp32 configurations (d = 16 at N = 1024); it is VALU-bound
-// by design and uses IEEE expf.
+// This path serves small fp32 workloads (the SQAT-m attention core: d = 16,
+// N = 1024, 8 query heads), where one thread per query row would leave most
+// of the GPU idle. A workgroup therefore takes RB query rows of one
+// (batch, head) and splits each row's key range over S threads: thread
+// (row r, split s) runs an exact fp32 streaming softmax over its keys
+// (16-key tiles: scores, tile maximum, rescale, accumulate, IEEE expf), then
+// the S partial (max, sum, output) triples of a row are merged through LDS.
+// K/V rows are read straight from global memory; all threads of a split read
+// the same key at the same time, so those reads are broadcasts from cache.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -19,7 +22,7 @@ namespace sqa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 64;
+constexpr int kKeyTile = 16;
 
 struct Args32 {
   const float* q;
@@ -33,17 +36,19 @@ struct Args32 {
   int causal;
 };
 
-template <int D>
+template <int D, int S>
 __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(Args32 a) {
-  __shared__ float ks[kTile][D];
-  __shared__ float vs[kTile][D];
+  constexpr int RB = kThreads / S;  // query rows per workgroup
+  __shared__ float part[S][RB][D + 2];
+
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x / a.blocks_per_head;       // b * Hq + h
+  const int r = tid % RB, sp = tid / RB;
+  const int bh = blockIdx.x / a.blocks_per_head;  // b * Hq + h
   const int blk = blockIdx.x % a.blocks_per_head;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int kvh = h / a.g;
   const int N = a.N;
-  const int t = blk * kThreads + tid;
+  const int t = blk * RB + r;
   const bool valid = t < N;
   const int tq = min(t, N - 1);
 
@@ -59,31 +64,22 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(Args32 a) {
   }
   float m = -INFINITY, l = 0.f;
 
-  const int last_row = min(N - 1, blk * kThreads + kThreads - 1);
-  const int nkeys = a.causal ? last_row + 1 : N;
-  const int ntiles = (nkeys + kTile - 1) / kTile;
-  const int my_end = a.causal ? tq + 1 : N;  // keys [0, my_end) are visible
+  // this thread's keys: [lo, hi)
+  const int chunk = (N + S - 1) / S;
+  const int kend = a.causal ? tq + 1 : N;
+  const int lo = sp * chunk;
+  const int hi = min(lo + chunk, kend);
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int key0 = kt * kTile;
-    __syncthreads();
-    for (int e = tid; e < kTile * D; e += kThreads) {
-      const int r = e / D, c = e % D;
-      const int row = min(key0 + r, N - 1);
-      ks[r][c] = kbase[(size_t)row * D + c];
-      vs[r][c] = vbase[(size_t)row * D + c];
-    }
-    __syncthreads();
-    if (key0 >= my_end) continue;
-    const int cnt = min(kTile, my_end - key0);
-
-    float s[kTile];
+  for (int key0 = lo; key0 < hi; key0 += kKeyTile) {
+    const int cnt = min(kKeyTile, hi - key0);
+    float s[kKeyTile];
     float mt = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
+    for (int j = 0; j < kKeyTile; ++j) {
+      const float* kr = kbase + (size_t)min(key0 + j, N - 1) * D;
       float dot = 0.f;
 #pragma unroll
-      for (int c = 0; c < D; ++c) dot = fmaf(qv[c], ks[j][c], dot);
+      for (int c = 0; c < D; ++c) dot = fmaf(qv[c], kr[c], dot);
       s[j] = dot * a.scale;
       if (j < cnt) mt = fmaxf(mt, s[j]);
     }
@@ -94,24 +90,50 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(Args32 a) {
 #pragma unroll
     for (int c = 0; c < D; ++c) acc[c] *= alpha;
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
-      const float p = (j < cnt) ? expf(s[j] - m) : 0.f;
-      l += p;
+    for (int j = 0; j < kKeyTile; ++j) {
+      if (j < cnt) {
+        const float p = expf(s[j] - m);
+        const float* vr = vbase + (size_t)(key0 + j) * D;
+        l += p;
 #pragma unroll
-      for (int c = 0; c < D; ++c) acc[c] = fmaf(p, vs[j][c], acc[c]);
+        for (int c = 0; c < D; ++c) acc[c] = fmaf(p, vr[c], acc[c]);
+      }
     }
   }
 
-  if (!valid) return;
-  const float inv = 1.0f / l;
+  // merge the S partial softmax states of each row
+#pragma unroll
+  for (int c = 0; c < D; ++c) part[sp][r][c] = acc[c];
+  part[sp][r][D] = m;
+  part[sp][r][D + 1] = l;
+  __syncthreads();
+  if (sp != 0 || !valid) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int x = 0; x < S; ++x) M = fmaxf(M, part[x][r][D]);
+  float L = 0.f;
+  float out[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) out[c] = 0.f;
+#pragma unroll
+  for (int x = 0; x < S; ++x) {
+    const float mx = part[x][r][D];
+    if (mx == -INFINITY) continue;  // empty split
+    const float w = expf(mx - M);
+    L = fmaf(part[x][r][D + 1], w, L);
+#pragma unroll
+    for (int c = 0; c < D; ++c) out[c] = fmaf(part[x][r][c], w, out[c]);
+  }
+  const float inv = 1.0f / L;
   float* orow = a.o + ((size_t)bh * N + t) * D;
 #pragma unroll
-  for (int c = 0; c < D; ++c) orow[c] = acc[c] * inv;
-  if (a.lse != nullptr) a.lse[(size_t)bh * N + t] = m + logf(l);
+  for (int c = 0; c < D; ++c) orow[c] = out[c] * inv;
+  if (a.lse != nullptr) a.lse[(size_t)bh * N + t] = M + logf(L);
 }
 
-template <int D>
+template <int D, int S>
 hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
+  constexpr int RB = kThreads / S;
   Args32 a;
   a.q = static_cast<const float*>(p.q);
   a.k = static_cast<const float*>(p.k);
@@ -122,20 +144,20 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
   a.Hq = (int)p.Hq;
   a.Hkv = (int)p.Hkv;
   a.g = (int)(p.Hq / p.Hkv);
-  a.blocks_per_head = (int)((p.N + kThreads - 1) / kThreads);
+  a.blocks_per_head = (int)((p.N + RB - 1) / RB);
   a.scale = p.scale;
   a.causal = p.causal;
   const int64_t nblk = (int64_t)a.blocks_per_head * p.B * p.Hq;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_fwd_f32_kernel<D>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, S>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd_f32(const AttnProblem& p, hipStream_t stream) {
-  if (p.D == 16) return launch_d<16>(p, stream);
-  if (p.D == 64) return launch_d<64>(p, stream);
+  if (p.D == 16) return launch_d<16, 8>(p, stream);
+  if (p.D == 64) return launch_d<64, 4>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -2,9 +2,11 @@
 // details" and "Model size difference"): the query and output projections are
 // H_q*d wide, the key/value projections H_kv*d wide, with d = d_model / H.
 //
+//   rope_table : (cos, sin) of t*base^(-2c/d) for every position t and pair c,
+//              the angle formed and reduced modulo 2*pi in fp64.
 //   qkv_rope : [B*N, Dm] x [W_q | W_k | W_v] -> Q [B,Hq,N,d], K/V [B,Hkv,N,d]
 //              with rotary position embedding applied to Q and K in the
-//              epilogue (rotate-half pairs (c, c+d/2), angle t*base^(-2c/d)).
+//              epilogue (rotate-half pairs (c, c+d/2)), reading the table.
 //   out_proj : O_flat [B*N, Hq*d] x W_o -> Y [B, N, Dm], reading O in its
 //              [B, Hq, N, d] attention layout (no separate transpose pass).
 //
@@ -43,7 +45,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 struct Theta {
-  float v[kMaxHalf];
+  double v[kMaxHalf];
 };
 
 // Source of the A operand rows: either a row-major [M, K] matrix, or the
@@ -153,11 +155,11 @@ __device__ __forceinline__ void spill_acc(const f32x16_t& acc, float* cs) {
 }
 
 struct QkvArgs {
+  const float* cs;  // [N, d/2] (cos, sin)
   ASrc A;
   WSrc W;
   uint16_t* out[3];
   int64_t M, Ncols, K, N, Hq, Hkv, d;
-  Theta theta;
   int nblk_n;
 };
 
@@ -196,9 +198,8 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(QkvArgs a) {
       y[e] = x;
     } else {
       const int kpair = c % (int)half;
-      const float ang = (float)t * a.theta.v[kpair];
-      float sn, cn;
-      sincosf(ang, &sn, &cn);
+      const float2 csv = *reinterpret_cast<const float2*>(a.cs + 2 * (t * half + kpair));
+      const float cn = csv.x, sn = csv.y;
       if (c < half) {
         const float xp = cs[r * CPITCH + lbase + c + (int)half];
         y[e] = x * cn - xp * sn;
@@ -252,7 +253,41 @@ __global__ __launch_bounds__(kThreads) void out_proj_kernel(OprojArgs a) {
   *reinterpret_cast<u32x4_t*>(dst + 8) = w1;
 }
 
+struct RopeArgs {
+  float* cs;
+  int64_t N, half;
+  Theta theta;
+};
+
+__global__ __launch_bounds__(kThreads) void rope_table_kernel(RopeArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= a.N * a.half) return;
+  const int64_t t = i / a.half, c = i % a.half;
+  const double twopi = 6.283185307179586476925286766559;
+  double ang = (double)t * a.theta.v[c];
+  ang -= twopi * floor(ang / twopi);  // reduce to [0, 2*pi) in fp64
+  float sn, cn;
+  sincosf((float)ang, &sn, &cn);
+  a.cs[2 * i] = cn;
+  a.cs[2 * i + 1] = sn;
+}
+
 }  // namespace
+
+hipError_t launch_rope_table(float* cs, int64_t N, int64_t d, float rope_base, hipStream_t stream) {
+  if (d % 2 != 0 || d / 2 > kMaxHalf) return hipErrorInvalidValue;
+  RopeArgs a;
+  a.cs = cs;
+  a.N = N;
+  a.half = d / 2;
+  for (int i = 0; i < kMaxHalf; ++i)
+    a.theta.v[i] = (i < d / 2) ? pow((double)rope_base, -2.0 * i / (double)d) : 0.0;
+  const int64_t n = N * a.half;
+  const int64_t nblk = (n + kThreads - 1) / kThreads;
+  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_qkv_rope(const QkvProblem& p, hipStream_t stream) {
   if (p.d / 2 > kMaxHalf || p.d % 16 != 0 || p.Dm % 16 != 0) return hipErrorInvalidValue;
@@ -279,9 +314,7 @@ hipError_t launch_qkv_rope(const QkvProblem& p, hipStream_t stream) {
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.d = p.d;
-  for (int i = 0; i < kMaxHalf; ++i) {
-    a.theta.v[i] = (i < p.d / 2) ? (float)pow((double)p.rope_base, -2.0 * i / (double)p.d) : 0.f;
-  }
+  a.cs = p.rope_cs;
   a.nblk_n = (int)((a.Ncols + BN - 1) / BN);
   const int64_t nblk = ((a.M + BM - 1) / BM) * a.nblk_n;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
