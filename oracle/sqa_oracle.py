@@ -24,6 +24,13 @@ What is computed, and where it comes from
       O[b,i,t,:] = sum_u softmax_u(s_tu) V[b,j,u,:]
   with U_t = all keys (encoder-style) or {u <= t} (causal, the SQAT-m text
   generation model), and optionally LSE[b,i,t] = log sum_u exp(s_tu).
+* The backward pass (the pages place SQA's gains in training: pre-training and
+  fine-tuning in the SQA abstract, training time per batch on the SQAT-m
+  card's results) is the exact derivative of that forward for an upstream
+  gradient dO, written out with the chain rule through the softmax:
+      P = softmax(S),  dP = dO V^T,  dS = P * (dP - rowsum(P * dP)),
+      dQ = scale dS K,  dK_j = scale sum_{i in group j} dS^T Q_i,
+      dV_j = sum_{i in group j} P^T dO_i.
 * The layer (SQAT-m, "Architecture details" and "Model size difference"):
   Q = X W_Q (H_q*d wide), K = X W_K and V = X W_V (H_kv*d wide), RoPE on Q and
   K, SQA, then Y = O_flat W_O with W_O of H_q*d rows. Weights are [in, out].
@@ -48,6 +55,7 @@ import numpy as np
 __all__ = [
     "kv_head_index",
     "attention",
+    "attention_bwd",
     "rope",
     "layer",
     "layer_weight_shapes",
@@ -163,6 +171,120 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: Optional[float
             with ThreadPoolExecutor(max_workers=threads) as ex:
                 list(ex.map(run, tasks))
     return (out, lse) if return_lse else out
+
+
+def _attend_rows_bwd(q_rows: np.ndarray, t_rows: np.ndarray, kj: np.ndarray, vj: np.ndarray,
+                     do_rows: np.ndarray, scale: float, causal: bool):
+    """Gradients of one block of query rows against one K/V head (fp64).
+
+    Returns dQ [R, d] for these rows and their contributions dK_part, dV_part
+    [N, d] to the head's key and value gradients. The softmax is recomputed
+    exactly (two passes); nothing saved by a forward is used.
+    """
+    s = (q_rows @ kj.T) * scale                       # [R, N]
+    if causal:
+        u = np.arange(kj.shape[0])
+        s = np.where(u[None, :] <= t_rows[:, None], s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    p = e / e.sum(axis=1, keepdims=True)              # masked entries are exactly 0
+    dp = do_rows @ vj.T                               # dL/dP        [R, N]
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))   # dL/dS (softmax Jacobian)
+    dq = (ds @ kj) * scale
+    dk_part = (ds.T @ q_rows) * scale
+    dv_part = p.T @ do_rows
+    return dq, dk_part, dv_part
+
+
+def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                  scale: Optional[float] = None, causal: bool = False,
+                  rows: Optional[Sequence[int]] = None, threads: int = 1,
+                  chunk_elems: int = 1 << 22):
+    """Backward of ``attention`` in float64: returns (dQ, dK, dV).
+
+    dout is the upstream gradient dL/dO, shaped like O [B, H_q, N, d]. dK and
+    dV [B, H_kv, N, d] sum the contributions of every query head of a K/V
+    head's group. With ``rows`` only dQ is computed, for those query positions
+    ([B, H_q, R, d]); dK and dV need every row and are returned as None.
+    ``threads`` > 1 splits each (b, K/V head)'s rows into slices whose partial
+    sums are added in slice order, so results do not depend on it.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    dout = np.asarray(dout)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4 or dout.shape != q.shape:
+        raise ValueError("expected 4-D [B, H, N, d] arrays, dout shaped like q")
+    B, H_q, N, d = q.shape
+    Bk, H_kv, Nk, dk_ = k.shape
+    if (Bk, Nk, dk_) != (B, N, d) or v.shape != k.shape:
+        raise ValueError("q/k/v shapes disagree")
+    if not (1 <= H_kv <= H_q):
+        raise ValueError("need 1 <= H_kv <= H_q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    scale = float(scale)
+    want_kv = rows is None
+    t_all = np.arange(N, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = t_all.shape[0]
+    dq = np.zeros((B, H_q, R, d), dtype=np.float64)
+    dk = np.zeros((B, H_kv, N, d), dtype=np.float64) if want_kv else None
+    dv = np.zeros((B, H_kv, N, d), dtype=np.float64) if want_kv else None
+    if R == 0 or B == 0 or N == 0:
+        return dq, dk, dv
+
+    chunk = max(1, min(R, chunk_elems // max(N, 1)))
+    # work items of one (b, j): (query head i, row chunk) in a fixed order
+    groups = {}
+    for b in range(B):
+        for i in range(H_q):
+            j = kv_head_index(i, H_q, H_kv)
+            for r0 in range(0, R, chunk):
+                groups.setdefault((b, j), []).append((i, r0, min(R, r0 + chunk)))
+    nslice = max(1, min(threads, 8))
+    tasks = []
+    for (b, j), items in groups.items():
+        per = -(-len(items) // nslice)
+        for sl in range(nslice):
+            part = items[sl * per:(sl + 1) * per]
+            if part:
+                tasks.append((b, j, sl, part))
+
+    def run(task):
+        b, j, sl, part = task
+        kj = k[b, j].astype(np.float64)
+        vj = v[b, j].astype(np.float64)
+        dk_acc = np.zeros((N, d), dtype=np.float64) if want_kv else None
+        dv_acc = np.zeros((N, d), dtype=np.float64) if want_kv else None
+        for (i, r0, r1) in part:
+            t_rows = t_all[r0:r1]
+            gq, gk, gv = _attend_rows_bwd(q[b, i, t_rows].astype(np.float64), t_rows, kj, vj,
+                                          dout[b, i, t_rows].astype(np.float64), scale, causal)
+            dq[b, i, r0:r1] = gq
+            if want_kv:
+                dk_acc += gk
+                dv_acc += gv
+        return (b, j, sl, dk_acc, dv_acc)
+
+    if threads <= 1:
+        results = [run(t) for t in tasks]
+    else:
+        try:
+            from threadpoolctl import threadpool_limits
+        except ImportError:  # pragma: no cover - threadpoolctl is installed
+            threadpool_limits = None
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                with ThreadPoolExecutor(max_workers=threads) as ex:
+                    results = list(ex.map(run, tasks))
+        else:
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                results = list(ex.map(run, tasks))
+    if want_kv:
+        for (b, j, sl, gk, gv) in sorted(results, key=lambda r: (r[0], r[1], r[2])):
+            dk[b, j] += gk
+            dv[b, j] += gv
+    return dq, dk, dv
 
 
 def rope(x: np.ndarray, base: float, positions: Optional[np.ndarray] = None) -> np.ndarray:
