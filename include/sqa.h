@@ -79,6 +79,48 @@ sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* o,
                         int dtype, float scale, int causal, float* lse, void* stream);
 
 /*
+ * sqa_attn_bwd_workspace_bytes -- bytes of device workspace sqa_attn_bwd
+ * needs for these sizes: one fp32 pair (lse * log2(e), D_t) per query row,
+ * with each (batch, query head)'s rows padded up to a multiple of 32, i.e.
+ * 8 * B * H_q * ceil(N / 32) * 32 bytes. Returns 0 for invalid or zero
+ * sizes, or when d / dtype are not supported by sqa_attn_bwd.
+ */
+size_t sqa_attn_bwd_workspace_bytes(int64_t B, int64_t H_q, int64_t N, int64_t d, int dtype);
+
+/*
+ * sqa_attn_bwd -- gradients of sqa_attn_fwd for an upstream gradient dout
+ * (the backward pass of training, where the SQA abstract places SQA's gains:
+ * pre-training and fine-tuning). With P the forward's attention
+ * probabilities (same scale and causal mask) and j = i / (H_q/H_kv):
+ *   D_t        = sum_c dout[b,i,t,c] * o[b,i,t,c]
+ *   dS_tu      = P_tu * (sum_c dout[b,i,t,c] * v[b,j,u,c] - D_t)
+ *   dq[b,i,t]  = scale * sum_u dS_tu * k[b,j,u]
+ *   dk[b,j,u]  = scale * sum_{i in group j} sum_t dS_tu * q[b,i,t]
+ *   dv[b,j,u]  = sum_{i in group j} sum_t P_tu * dout[b,i,t]
+ * the exact derivative of the forward's definition (a textbook chain rule
+ * through the softmax; the pages do not write it out).
+ *
+ *   q, o, dout [B, H_q, N, d]  inputs, bf16; o and lse as written by
+ *                              sqa_attn_fwd on the same q, k, v, scale, causal
+ *   k, v       [B, H_kv, N, d] inputs, bf16
+ *   lse        [B, H_q, N]     input, fp32, natural log (sqa_attn_fwd's lse)
+ *   dq         [B, H_q, N, d]  output, bf16, overwritten
+ *   dk, dv     [B, H_kv, N, d] outputs, bf16, overwritten (group sums)
+ *   workspace  device buffer of at least sqa_attn_bwd_workspace_bytes(...)
+ *              bytes, owned by the caller; contents on return unspecified.
+ *   d = 64 and dtype SQA_BF16 only (others: SQA_ERR_UNSUPPORTED).
+ *   Arithmetic: P is recomputed from lse; scores and all sums are fp32, P and
+ *   dS are rounded to bf16 (nearest even) for the matrix products, outputs
+ *   are rounded to nearest-even bf16. Deterministic: no atomics.
+ * Outputs must not overlap each other, an input or the workspace.
+ * Errors: as sqa_attn_fwd, plus SQA_ERR_WORKSPACE.
+ */
+sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q,
+                        int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * sqa_layer_workspace_bytes -- bytes of device workspace sqa_layer_fwd needs
  * for these sizes: bf16 Q [B,H_q,N,d], K and V [B,H_kv,N,d], the attention
  * output [B,H_q,N,d] and an fp32 RoPE (cos, sin) table [N, d/2, 2], each

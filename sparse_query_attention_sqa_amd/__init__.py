@@ -1,4 +1,4 @@
-"""Python binding for libsqa: Sparse Query Attention forward on MI355X.
+"""Python binding for libsqa: Sparse Query Attention on MI355X.
 
 Argument marshalling only. Every step of the computation runs in the HIP
 kernels behind the C ABI declared in ``include/sqa.h``; torch is used for
@@ -6,6 +6,9 @@ device memory and the current HIP stream. There is no fallback path: if the
 library is not built, importing the functions raises.
 
     sqa_attn_fwd(q, k, v, *, scale=None, causal=False, out=None, return_lse=False)
+    sqa_attn_bwd(q, k, v, o, dout, lse, *, scale=None, causal=False, dq=None, dk=None,
+                 dv=None, workspace=None)
+    sqa_attn_bwd_workspace_bytes(B, H_q, N, d, dtype="bf16")
     sqa_layer_fwd(x, w_q, w_k, w_v, w_o, *, H, H_q, H_kv, rope_base=10000.0,
                   scale=None, causal=True, out=None, workspace=None)
     sqa_layer_workspace_bytes(B, N, D, H, H_q, H_kv, dtype="bf16")
@@ -17,7 +20,8 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["SQAError", "lib_path", "load_library", "sqa_attn_fwd", "sqa_layer_fwd",
+__all__ = ["SQAError", "lib_path", "load_library", "sqa_attn_fwd", "sqa_attn_bwd",
+           "sqa_attn_bwd_workspace_bytes", "sqa_layer_fwd",
            "sqa_layer_workspace_bytes", "sqa_status_str", "sqa_version",
            "SQA_F32", "SQA_BF16"]
 
@@ -54,6 +58,11 @@ def load_library() -> ctypes.CDLL:
     lib.sqa_attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, f32,
                                  ctypes.c_int, vp, vp]
     lib.sqa_attn_fwd.restype = ctypes.c_int
+    lib.sqa_attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.sqa_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.sqa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                 ctypes.c_int, f32, ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.sqa_attn_bwd.restype = ctypes.c_int
     lib.sqa_layer_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
     lib.sqa_layer_workspace_bytes.restype = ctypes.c_size_t
     lib.sqa_layer_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32,
@@ -143,6 +152,62 @@ def sqa_attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False
                           lse.data_ptr() if lse is not None else None, _stream_handle(q.device))
     _check(st)
     return (out, lse) if return_lse else out
+
+
+def sqa_attn_bwd_workspace_bytes(B: int, H_q: int, N: int, d: int, dtype: str = "bf16") -> int:
+    code = SQA_BF16 if dtype == "bf16" else SQA_F32
+    return int(load_library().sqa_attn_bwd_workspace_bytes(B, H_q, N, d, code))
+
+
+def sqa_attn_bwd(q, k, v, o, dout, lse, *, scale: Optional[float] = None, causal: bool = False,
+                 dq=None, dk=None, dv=None, workspace=None):
+    """Gradients of ``sqa_attn_fwd`` for the upstream gradient ``dout``.
+
+    q, o, dout [B, H_q, N, d]; k, v [B, H_kv, N, d] bf16 (d = 64); lse
+    [B, H_q, N] fp32 from ``sqa_attn_fwd(..., return_lse=True)`` with the same
+    scale and causal flag. Returns (dq, dk, dv); dk and dv sum over the query
+    heads of each K/V head's group. ``workspace`` is an optional uint8 GPU
+    tensor of at least ``sqa_attn_bwd_workspace_bytes`` bytes.
+    """
+    torch = _torch()
+    lib = load_library()
+    _require_device(q, k, v, o, dout, lse)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected 4-D [B, H, N, d] tensors")
+    if k.shape != v.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("k/v and q/o/dout shapes must match")
+    if len({q.dtype, k.dtype, v.dtype, o.dtype, dout.dtype}) != 1:
+        raise ValueError("q, k, v, o and dout must share a dtype")
+    if lse.dtype != torch.float32:
+        raise ValueError("lse must be float32")
+    B, H_q, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d or tuple(lse.shape) != (B, H_q, N):
+        raise ValueError("q, k/v and lse shapes disagree")
+    H_kv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    outs = []
+    for t, like in ((dq, q), (dk, k), (dv, v)):
+        if t is None:
+            t = torch.empty_like(like)
+        else:
+            _require_device(t)
+            if t.shape != like.shape or t.dtype != like.dtype:
+                raise ValueError("gradient outputs must match their inputs in shape and dtype")
+        outs.append(t)
+    code = _dtype_code(q)
+    need = int(lib.sqa_attn_bwd_workspace_bytes(B, H_q, N, d, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _require_device(workspace)
+    st = lib.sqa_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                          lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                          B, H_q, H_kv, N, d, code, float(scale), int(bool(causal)),
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _stream_handle(q.device))
+    _check(st)
+    return outs[0], outs[1], outs[2]
 
 
 def sqa_layer_workspace_bytes(B: int, N: int, D: int, H: int, H_q: int, H_kv: int,

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsqa.so")
 
-SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_bf16_d64.hip", "attn_fwd_f32.hip", "layer_gemm.hip", "sqa_api.cpp"]
+SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_bf16_d64.hip", "attn_fwd_f32.hip", "attn_bwd_bf16_d64.hip",
+           "layer_gemm.hip", "sqa_api.cpp"]
 
 
 def hipcc() -> str:

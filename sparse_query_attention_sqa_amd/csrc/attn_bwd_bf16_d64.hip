@@ -1,0 +1,579 @@
+// SQA attention backward for head dim 64, bf16 in/out, gfx950.
+//
+// Operation: the exact derivative of the forward (query head i attends K/V
+// head floor(i*H_kv/H_q), "GQA ..." page, "The idea"; fewer query heads than
+// the baseline, SQA paper abstract, whose gains are quoted for training).
+// With P = softmax(S), S = scale Q K^T (masked), upstream gradient dO:
+//   D_t  = sum_c dO[t,c] O[t,c]          (equals rowsum(P * dP))
+//   dP   = dO V^T,   dS = P * (dP - D)
+//   dQ   = scale dS K,   dK_j = scale sum_{i in group j} dS_i^T Q_i,
+//   dV_j = sum_{i in group j} P_i^T dO_i.
+// P is recomputed from the forward's log-sum-exp: P = 2^(s*c - lse*log2 e)
+// with c = scale*log2 e.
+//
+// Three kernels, all on the caller's stream:
+//   1. bwd_rowterms_kernel: (lse*log2 e, D) per query row into the workspace.
+//   2. bwd_dkdv_kernel (K/V-stationary): a wave holds 32 keys of one K/V head
+//      (K and V as MFMA B operands in registers) and streams every query tile
+//      of every query head of the group through LDS: S = Q K^T and
+//      dP = dO V^T (A = Q / dO rows), then dV^T += dO^T P and
+//      dK^T += Q^T dS (A = transposed reads of Q / dO). Because the wave sees
+//      the whole group, the group sum needs no atomics.
+//   3. bwd_dq_kernel (Q-stationary, like the forward): a wave holds 32 query
+//      rows (Q, dO in registers) and streams K/V tiles: S^T = K Q^T,
+//      dP^T = V dO^T, dQ^T += K^T dS^T.
+// Both streamed operands are DMA'd HBM -> LDS (buffer_load ... lds) into a
+// ring, each tile in the two layouts of bf16_tiles.h (row layout for row
+// fragments, transposed layout for ds_read_b64_tr_b16), with one barrier per
+// tile. Every DMA is issued unconditionally -- tiles past the last one needed
+// get an empty descriptor range and cost no memory traffic -- so the explicit
+// vmcnt waits are exact. P and dS are rounded to bf16 (nearest even) for the
+// MFMA products; everything else accumulates in fp32.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "bf16_tiles.h"
+#include "kernels.h"
+
+namespace sqa {
+namespace {
+
+using namespace tiles;
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kXcds = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt vm, expcnt 7, lgkmcnt lgkm.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+// Wait until at most VM of this wave's DMAs are in flight and its LDS reads
+// are done, then synchronise the workgroup.
+template <int VM>
+__device__ __forceinline__ void barrier_vm() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ------------------------------------------------------------------ row terms
+struct RowArgs {
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  float2* rt;   // [B*H_q, Np]: every head's rows padded to Np, a multiple of 32
+  int64_t nrows;  // B*H_q*Np
+  int N, Np;
+};
+
+// Eight lanes per query row: each forms the products of 8 bf16 pairs exactly
+// (v_dot2_f32_bf16) and the eight partial sums are added with lane shuffles.
+// Padding rows (t >= N) get (0, 0), so row-term tiles are always whole.
+__global__ __launch_bounds__(256) void bwd_rowterms_kernel(RowArgs a) {
+  const int64_t prow = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int part = threadIdx.x & 7;
+  const int64_t bh = prow / a.Np;
+  const int t = (int)(prow - bh * a.Np);
+  const bool valid = prow < a.nrows && t < a.N;
+  const int64_t row = bh * a.N + t;
+  float acc = 0.f;
+  if (valid) {
+    const u32x4_t ov = *reinterpret_cast<const u32x4_t*>(a.o + row * kD + part * 8);
+    const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(a.dout + row * kD + part * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // copy the elements out first: a bit cast of a vector-element
+      // expression reads element 0
+      const uint32_t ow = ov[w], dw = dv[w];
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ow), __builtin_bit_cast(bf16x2_t, dw), acc,
+                                            false);
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (prow < a.nrows && part == 0) a.rt[prow] = valid ? make_float2(a.lse[row] * kLog2e, acc) : make_float2(0.f, 0.f);
+}
+
+// Workgroup -> (b*H_kv + K/V head, index w_in within that head).
+// Encoder-style: consecutive logical workgroups on one XCD (they share the
+// streamed operand in L2). Causal: workgroups launch largest-work first,
+// which is ascending w_in, or descending with `reverse`.
+__device__ __forceinline__ void wg_coords(int causal, bool reverse, int nwg, int wg_per_bkv, int n_bkv,
+                                          int& bkv, int& w_in) {
+  if (!causal) {
+    const int bid = blockIdx.x;
+    const int per = nwg / kXcds, rem = nwg % kXcds;
+    const int x = bid % kXcds, i = bid / kXcds;
+    const int L = x * per + min(x, rem) + i;
+    bkv = L / wg_per_bkv;
+    w_in = L % wg_per_bkv;
+  } else {
+    const int L = blockIdx.x;
+    const int wr = L / n_bkv;
+    bkv = L % n_bkv;
+    w_in = reverse ? wg_per_bkv - 1 - wr : wr;
+  }
+}
+
+// ------------------------------------------------------------------ dK, dV
+constexpr int kKvBuf = 4;                           // ring slots
+constexpr int kKvRt = 4 * kTileBytes;               // row-term area offset
+constexpr int kKvSlot = 4 * kTileBytes + 1024;      // Q rows | dO rows | Q tr | dO tr | row terms
+constexpr int kKvDma = 5;                           // DMA instructions per wave per step
+
+struct KvArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float2* rt;  // row terms, [B*H_q, Np]
+  uint16_t* dk;
+  uint16_t* dv;
+  int N, Np, Hq, Hkv, g, KB, NQT, wg_per_bkv, n_bkv, nwg;
+  float c, scale;
+  int causal;
+};
+
+struct KvRing {
+  uint8_t* p[kKvBuf];
+};
+
+struct KvCtx {
+  KvRing ring;
+  const uint16_t* q;     // Q of batch b, head 0
+  const uint16_t* dout;  // dO of batch b, head 0
+  const float2* rt;      // row terms of batch b, head 0 (rows padded to Np)
+  int N, Np, g, h0, qt0, kb, causal, wave;
+  bool wave_valid;
+  float c;
+  uint32_t off_rows, off_tr;
+  ReadOffsets ro;
+};
+
+struct KvState {
+  u32x4_t kb_f[4], vb_f[4];  // K and V rows of this wave's 32 keys as B operands
+  f32x16_t acc_k[2], acc_v[2];
+};
+
+// DMA step s (query tile qt of query head h0 + i) into ring slot SLOT.
+template <int SLOT>
+__device__ __forceinline__ void kv_issue(const KvCtx& cx, int s) {
+  const int qt = cx.qt0 + s / cx.g, i = s % cx.g;
+  const size_t head = (size_t)(cx.h0 + i) * cx.N;
+  const int row0 = qt * kTileRows;
+  uint8_t* slot = cx.ring.p[SLOT];
+  const uint16_t* qb = cx.q + head * kD;
+  const uint16_t* db = cx.dout + head * kD;
+  const float2* rb = cx.rt + (size_t)(cx.h0 + i) * cx.Np;
+  dma_tile_part(qb, row0, cx.N, slot + cx.wave * 1024, cx.off_rows);
+  dma_tile_part(db, row0, cx.N, slot + kTileBytes + cx.wave * 1024, cx.off_rows);
+  dma_tile_part(qb, row0, cx.N, slot + 2 * kTileBytes + cx.wave * 1024, cx.off_tr);
+  dma_tile_part(db, row0, cx.N, slot + 3 * kTileBytes + cx.wave * 1024, cx.off_tr);
+  // row terms of the 32 rows (8 B each, whole tiles thanks to the padding)
+  // land in the first 256 B of the area; every wave writes the same bytes
+  // (lanes past 16 write zeros beyond them)
+  const int rem = row0 < cx.Np ? kTileRows * 8 : 0;
+  __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(rb + row0), (short)0, rem, kBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + kKvRt), 16, (uint32_t)(threadIdx.x & 63) * 16,
+                                           0, 0, 0);
+}
+
+template <int SLOT>
+__device__ __forceinline__ void kv_step(const KvCtx& cx, KvState& w, int s, int nsteps) {
+  constexpr int AHEAD = (SLOT + kKvBuf - 1) % kKvBuf;
+  // this wave's DMA of step s has landed; every wave is done with step s-1
+  barrier_vm<(kKvBuf - 2) * kKvDma>();
+  kv_issue<AHEAD>(cx, s + kKvBuf - 1);
+  const int qt = cx.qt0 + s / cx.g;
+  const bool active = cx.wave_valid && (!cx.causal || qt >= cx.kb);
+  if (!active) return;
+  const uint8_t* slot = cx.ring.p[SLOT];
+  const int lane = threadIdx.x & 63, lg = lane >> 5, l32 = lane & 31;
+
+  u32x4_t a[4];
+  read_rows(slot, cx.ro, a);
+  const f32x16_t sc = mfma_k64(a, w.kb_f);  // entry e: query qt*32 + lg*16 + e, key kb*32 + l32
+  read_rows(slot + kTileBytes, cx.ro, a);
+  const f32x16_t dp = mfma_k64(a, w.vb_f);
+
+  float2 rt[16];
+  const float4* rtp = reinterpret_cast<const float4*>(slot + kKvRt + lg * 128);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float4 x = rtp[e];
+    rt[2 * e] = make_float2(x.x, x.y);
+    rt[2 * e + 1] = make_float2(x.z, x.w);
+  }
+  const bool masked = cx.causal && qt == cx.kb;
+  f32x16_t p, ds;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float x = __builtin_fmaf(sc[e], cx.c, -rt[e].x);
+    if (masked && lg * 16 + e < l32) x = -INFINITY;  // query row before the key
+    p[e] = __builtin_amdgcn_exp2f(x);
+    ds[e] = p[e] * (dp[e] - rt[e].y);
+  }
+  u32x4_t pk[2], dsk[2];
+  pack_pairs(p, pk);
+  pack_pairs(ds, dsk);
+  u32x4_t t[2][2];
+  read_tr(slot + 3 * kTileBytes, cx.ro, t);
+  mfma_tr(t, pk, w.acc_v);
+  read_tr(slot + 2 * kTileBytes, cx.ro, t);
+  mfma_tr(t, dsk, w.acc_k);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[kKvSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[kKvSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[kKvSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring3[kKvSlot];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lg = lane >> 5, l32 = lane & 31;
+  int bkv, w_in;
+  wg_coords(a.causal, false, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
+  const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
+  const int N = a.N;
+
+  KvCtx cx;
+  cx.ring.p[0] = ring0;
+  cx.ring.p[1] = ring1;
+  cx.ring.p[2] = ring2;
+  cx.ring.p[3] = ring3;
+  cx.q = a.q + (size_t)b * a.Hq * N * kD;
+  cx.dout = a.dout + (size_t)b * a.Hq * N * kD;
+  cx.rt = a.rt + (size_t)b * a.Hq * a.Np;
+  cx.N = N;
+  cx.Np = a.Np;
+  cx.g = a.g;
+  cx.h0 = kvh * a.g;
+  cx.qt0 = a.causal ? w_in * kWaves : 0;  // the first query tile any key of this workgroup sees
+  cx.kb = w_in * kWaves + wave;
+  cx.causal = a.causal;
+  cx.wave = wave;
+  cx.wave_valid = cx.kb < a.KB;
+  cx.c = a.c;
+  cx.off_rows = dma_off_rows(wave, lane);
+  cx.off_tr = dma_off_tr(wave, lane);
+  cx.ro = read_offsets(lane);
+  const int nsteps = max(a.NQT - cx.qt0, 0) * a.g;
+
+  KvState w;
+  {
+    const int u = min(cx.kb * kTileRows + l32, N - 1);
+    const size_t kv_row = ((size_t)bkv * N + u) * kD;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      w.kb_f[ds] = u32x4_t{0u, 0u, 0u, 0u};
+      w.vb_f[ds] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if (cx.wave_valid) {
+      load_row_frags(a.k + kv_row, lg, w.kb_f);
+      load_row_frags(a.v + kv_row, lg, w.vb_f);
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      w.acc_k[x] = zero16();
+      w.acc_v[x] = zero16();
+    }
+  }
+
+  // zero the ring once so that no LDS byte is ever uninitialised
+  for (int e = tid; e < kKvSlot / 16; e += kThreads) {
+    reinterpret_cast<u32x4_t*>(ring0)[e] = u32x4_t{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4_t*>(ring1)[e] = u32x4_t{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4_t*>(ring2)[e] = u32x4_t{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4_t*>(ring3)[e] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+  barrier_vm<63>();
+
+  // prologue: steps 0 .. kKvBuf-2 in flight
+  kv_issue<0>(cx, 0);
+  kv_issue<1>(cx, 1);
+  kv_issue<2>(cx, 2);
+
+  // whole ring rounds first, so that every path to the loop back-edge has
+  // issued the same DMAs and the compiler's wait bookkeeping stays exact
+  int s = 0;
+  for (; s + kKvBuf <= nsteps; s += kKvBuf) {
+    kv_step<0>(cx, w, s, nsteps);
+    kv_step<1>(cx, w, s + 1, nsteps);
+    kv_step<2>(cx, w, s + 2, nsteps);
+    kv_step<3>(cx, w, s + 3, nsteps);
+  }
+  if (s < nsteps) kv_step<0>(cx, w, s, nsteps);
+  if (s + 1 < nsteps) kv_step<1>(cx, w, s + 1, nsteps);
+  if (s + 2 < nsteps) kv_step<2>(cx, w, s + 2, nsteps);
+  // drain the DMAs still in flight before the wave ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+
+  const int u = cx.kb * kTileRows + l32;
+  if (!cx.wave_valid || u >= N) return;
+  const size_t kv_row = ((size_t)bkv * N + u) * kD;
+  store_tr_row(a.dk + kv_row, w.acc_k, a.scale, lg);
+  store_tr_row(a.dv + kv_row, w.acc_v, 1.0f, lg);
+}
+
+// ------------------------------------------------------------------ dQ
+constexpr int kDqBuf = 4;
+constexpr int kDqSlot = 3 * kTileBytes;  // K rows | V rows | K tr
+constexpr int kDqDma = 3;
+
+struct DqArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float2* rt;  // row terms, [B*H_q, Np]
+  uint16_t* dq;
+  int N, Np, Hq, Hkv, g, TB, NT, wg_per_bkv, n_bkv, nwg;
+  float c, scale;
+  int causal;
+};
+
+struct DqRing {
+  uint8_t* p[kDqBuf];
+};
+
+struct DqCtx {
+  DqRing ring;
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  int N, nlim, last, tb, causal, wave, t;
+  float c;
+  uint32_t off_rows, off_tr;
+  ReadOffsets ro;
+};
+
+struct DqState {
+  u32x4_t qf[4], df[4];  // Q and dO of this wave's 32 rows as B operands
+  f32x16_t acc[2];
+  float lse2, dd;
+};
+
+template <int SLOT>
+__device__ __forceinline__ void dq_issue(const DqCtx& cx, int kt) {
+  const int row0 = kt * kTileRows;
+  uint8_t* slot = cx.ring.p[SLOT];
+  dma_tile_part(cx.kbase, row0, cx.nlim, slot + cx.wave * 1024, cx.off_rows);
+  dma_tile_part(cx.vbase, row0, cx.nlim, slot + kTileBytes + cx.wave * 1024, cx.off_rows);
+  dma_tile_part(cx.kbase, row0, cx.nlim, slot + 2 * kTileBytes + cx.wave * 1024, cx.off_tr);
+}
+
+template <int SLOT>
+__device__ __forceinline__ void dq_step(const DqCtx& cx, DqState& w, int j) {
+  constexpr int AHEAD = (SLOT + kDqBuf - 1) % kDqBuf;
+  // this wave's DMA of tile j has landed; every wave is done with tile j-1
+  barrier_vm<(kDqBuf - 2) * kDqDma>();
+  dq_issue<AHEAD>(cx, j + kDqBuf - 1);
+  if (j > cx.last) return;
+  const uint8_t* slot = cx.ring.p[SLOT];
+  const int lane = threadIdx.x & 63, lg = lane >> 5;
+
+  u32x4_t a[4];
+  read_rows(slot, cx.ro, a);
+  const f32x16_t sc = mfma_k64(a, w.qf);  // entry e: key j*32 + lg*16 + e, query t
+  read_rows(slot + kTileBytes, cx.ro, a);
+  const f32x16_t dp = mfma_k64(a, w.df);
+  u32x4_t kt[2][2];
+  read_tr(slot + 2 * kTileBytes, cx.ro, kt);
+
+  const int key0 = j * kTileRows + lg * 16;
+  const bool masked = (cx.causal && j == cx.tb) || (j * kTileRows + kTileRows > cx.N);
+  f32x16_t ds;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float x = __builtin_fmaf(sc[e], cx.c, -w.lse2);
+    if (masked) {
+      const int key = key0 + e;
+      if (!(key < cx.N && (!cx.causal || key <= cx.t))) x = -INFINITY;
+    }
+    ds[e] = __builtin_amdgcn_exp2f(x) * (dp[e] - w.dd);
+  }
+  u32x4_t dsk[2];
+  pack_pairs(ds, dsk);
+  mfma_tr(kt, dsk, w.acc);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[kDqSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[kDqSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[kDqSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring3[kDqSlot];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lg = lane >> 5, l32 = lane & 31;
+  int bkv, w_in;
+  wg_coords(a.causal, true, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
+  const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
+  const int slot = w_in * kWaves + wave;
+  const int tb = slot / a.g, jh = slot % a.g;
+  const bool wave_valid = tb < a.TB;
+  const int h = kvh * a.g + jh;
+  const int N = a.N;
+  // key tiles the workgroup streams, and the last one this wave uses
+  const int maxtb = min((w_in * kWaves + kWaves - 1) / a.g, a.TB - 1);
+  const int nt = a.causal ? maxtb + 1 : a.NT;
+
+  DqCtx cx;
+  cx.ring.p[0] = ring0;
+  cx.ring.p[1] = ring1;
+  cx.ring.p[2] = ring2;
+  cx.ring.p[3] = ring3;
+  cx.kbase = a.k + (size_t)bkv * N * kD;
+  cx.vbase = a.v + (size_t)bkv * N * kD;
+  cx.N = N;
+  cx.nlim = min(N, nt * kTileRows);
+  cx.last = !wave_valid ? -1 : (a.causal ? tb : a.NT - 1);
+  cx.tb = tb;
+  cx.causal = a.causal;
+  cx.wave = wave;
+  cx.t = tb * kTileRows + l32;
+  cx.c = a.c;
+  cx.off_rows = dma_off_rows(wave, lane);
+  cx.off_tr = dma_off_tr(wave, lane);
+  cx.ro = read_offsets(lane);
+
+  const size_t row_q = ((size_t)b * a.Hq + h) * N + min(cx.t, N - 1);
+  DqState w;
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) {
+    w.qf[ds] = u32x4_t{0u, 0u, 0u, 0u};
+    w.df[ds] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+  w.lse2 = 0.f;
+  w.dd = 0.f;
+  if (wave_valid) {
+    load_row_frags(a.q + row_q * kD, lg, w.qf);
+    load_row_frags(a.dout + row_q * kD, lg, w.df);
+    const float2 r = a.rt[((size_t)b * a.Hq + h) * a.Np + min(cx.t, N - 1)];
+    w.lse2 = r.x;
+    w.dd = r.y;
+  }
+  w.acc[0] = zero16();
+  w.acc[1] = zero16();
+
+  for (int e = tid; e < kDqSlot / 16; e += kThreads) {
+    reinterpret_cast<u32x4_t*>(ring0)[e] = u32x4_t{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4_t*>(ring1)[e] = u32x4_t{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4_t*>(ring2)[e] = u32x4_t{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4_t*>(ring3)[e] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+  barrier_vm<63>();
+
+  dq_issue<0>(cx, 0);
+  dq_issue<1>(cx, 1);
+  dq_issue<2>(cx, 2);
+
+  int j = 0;
+  for (; j + kDqBuf <= nt; j += kDqBuf) {
+    dq_step<0>(cx, w, j);
+    dq_step<1>(cx, w, j + 1);
+    dq_step<2>(cx, w, j + 2);
+    dq_step<3>(cx, w, j + 3);
+  }
+  if (j < nt) dq_step<0>(cx, w, j);
+  if (j + 1 < nt) dq_step<1>(cx, w, j + 1);
+  if (j + 2 < nt) dq_step<2>(cx, w, j + 2);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+
+  if (!wave_valid || cx.t >= N) return;
+  store_tr_row(a.dq + (((size_t)b * a.Hq + h) * N + cx.t) * kD, w.acc, a.scale, lg);
+}
+
+}  // namespace
+
+size_t attn_bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N) {
+  const int64_t Np = (N + kTileRows - 1) / kTileRows * kTileRows;
+  return (size_t)(B * Hq * Np) * sizeof(float2);
+}
+
+hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream) {
+  if (p.D != kD) return hipErrorInvalidValue;
+  if (p.N * kRowBytes > 0x7fffffffLL) return hipErrorInvalidValue;  // buffer descriptor range
+  const int N = (int)p.N;
+  const int Np = (N + kTileRows - 1) / kTileRows * kTileRows;
+  const float c = p.scale * kLog2e;
+  float2* rt = static_cast<float2*>(p.rowterms);
+
+  {
+    RowArgs a;
+    a.o = static_cast<const uint16_t*>(p.o);
+    a.dout = static_cast<const uint16_t*>(p.dout);
+    a.lse = p.lse;
+    a.rt = rt;
+    a.nrows = p.B * p.Hq * Np;
+    a.N = N;
+    a.Np = Np;
+    const int64_t nblk = (a.nrows + 31) / 32;
+    if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bwd_rowterms_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    KvArgs a;
+    a.q = static_cast<const uint16_t*>(p.q);
+    a.k = static_cast<const uint16_t*>(p.k);
+    a.v = static_cast<const uint16_t*>(p.v);
+    a.dout = static_cast<const uint16_t*>(p.dout);
+    a.rt = rt;
+    a.dk = static_cast<uint16_t*>(p.dk);
+    a.dv = static_cast<uint16_t*>(p.dv);
+    a.N = N;
+    a.Np = Np;
+    a.Hq = (int)p.Hq;
+    a.Hkv = (int)p.Hkv;
+    a.g = (int)(p.Hq / p.Hkv);
+    a.KB = (N + kTileRows - 1) / kTileRows;
+    a.NQT = a.KB;
+    a.wg_per_bkv = (a.KB + kWaves - 1) / kWaves;
+    a.n_bkv = (int)(p.B * p.Hkv);
+    const int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;
+    if (nwg > 0x7fffffff) return hipErrorInvalidValue;
+    a.nwg = (int)nwg;
+    a.c = c;
+    a.scale = p.scale;
+    a.causal = p.causal;
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(a.nwg), dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    DqArgs a;
+    a.q = static_cast<const uint16_t*>(p.q);
+    a.k = static_cast<const uint16_t*>(p.k);
+    a.v = static_cast<const uint16_t*>(p.v);
+    a.dout = static_cast<const uint16_t*>(p.dout);
+    a.rt = rt;
+    a.dq = static_cast<uint16_t*>(p.dq);
+    a.N = N;
+    a.Np = Np;
+    a.Hq = (int)p.Hq;
+    a.Hkv = (int)p.Hkv;
+    a.g = (int)(p.Hq / p.Hkv);
+    a.TB = (N + kTileRows - 1) / kTileRows;
+    a.NT = a.TB;
+    const int64_t slots = (int64_t)a.TB * a.g;
+    a.wg_per_bkv = (int)((slots + kWaves - 1) / kWaves);
+    a.n_bkv = (int)(p.B * p.Hkv);
+    const int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;
+    if (nwg > 0x7fffffff) return hipErrorInvalidValue;
+    a.nwg = (int)nwg;
+    a.c = c;
+    a.scale = p.scale;
+    a.causal = p.causal;
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(a.nwg), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+}
+
+}  // namespace sqa

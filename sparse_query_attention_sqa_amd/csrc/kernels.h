@@ -25,6 +25,27 @@ hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnProblem& p, hipStream_t stream);
 
+// SQA attention backward (bf16, head dim 64): dq [B,Hq,N,D], dk/dv
+// [B,Hkv,N,D] from q, k, v, the forward's o and lse, and dout. `rowterms`
+// is device scratch of attn_bwd_rowterm_bytes(B, Hq, N) bytes.
+struct BwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* rowterms;
+  int64_t B, Hq, Hkv, N, D;
+  float scale;
+  int causal;
+};
+size_t attn_bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N);
+hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream);
+
 // Projection + RoPE: x [M=B*N, Dm] bf16 times w_q [Dm,Hq*d] | w_k [Dm,Hkv*d] |
 // w_v [Dm,Hkv*d]; writes q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16 with RoPE applied
 // to q and k.

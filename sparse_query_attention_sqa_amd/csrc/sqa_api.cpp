@@ -105,6 +105,54 @@ sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* o, in
   return SQA_OK;
 }
 
+size_t sqa_attn_bwd_workspace_bytes(int64_t B, int64_t H_q, int64_t N, int64_t d, int dtype) {
+  if (B <= 0 || H_q <= 0 || N <= 0 || d != 64 || dtype != SQA_BF16) return 0;
+  if (N > kMaxN || B * H_q * N * d > kMaxElems) return 0;
+  return round256(sqa::attn_bwd_rowterm_bytes(B, H_q, N));
+}
+
+sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q,
+                        int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  sqa_status s = check_attn(B, H_q, H_kv, N, d, dtype, scale, causal);
+  if (s != SQA_OK) return s;
+  if (dtype != SQA_BF16 || d != 64)
+    return fail(SQA_ERR_UNSUPPORTED, "backward supports bf16 with d=64 only (got dtype %d, d=%lld)", dtype,
+                (long long)d);
+  if (B == 0 || N == 0) return SQA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return fail(SQA_ERR_NULL, "q, k, v, o, dout, lse, dq, dk and dv must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(SQA_ERR_ALIGN, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(SQA_ERR_ALIGN, "lse must be 4-byte aligned");
+  const size_t need = sqa_attn_bwd_workspace_bytes(B, H_q, N, d, dtype);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SQA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(SQA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  const size_t nq = (size_t)(B * H_q * N * d) * 2, nkv = (size_t)(B * H_kv * N * d) * 2;
+  const size_t nl = (size_t)(B * H_q * N) * 4;
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const size_t in_n[6] = {nq, nkv, nkv, nq, nq, nl};
+  const void* outs[4] = {dq, dk, dv, workspace};
+  const size_t out_n[4] = {nq, nkv, nkv, need};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (overlaps(outs[a], out_n[a], ins[b], in_n[b]))
+        return fail(SQA_ERR_ARG, "an output or the workspace overlaps an input");
+    for (int b = a + 1; b < 4; ++b)
+      if (overlaps(outs[a], out_n[a], outs[b], out_n[b]))
+        return fail(SQA_ERR_ARG, "outputs and workspace must not overlap each other");
+  }
+  sqa::BwdProblem p{q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H_q, H_kv, N, d, scale, causal};
+  hipError_t e = sqa::launch_attn_bwd_bf16_d64(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
+  return SQA_OK;
+}
+
 size_t sqa_layer_workspace_bytes(int64_t B, int64_t N, int64_t D, int64_t H, int64_t H_q, int64_t H_kv,
                                  int dtype) {
   if (B <= 0 || N <= 0 || D <= 0 || H <= 0 || H_q <= 0 || H_kv <= 0) return 0;

@@ -141,6 +141,13 @@ def draw_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,
     return q, k, v
 
 
+def draw_upstream(shape, dtype: str = "bf16", seed: int = 100) -> np.ndarray:
+    """Upstream gradient dL/dO for backward tests: N(0, 1) of the given shape
+    as float32 (bf16-representable for "bf16"), from its own seeded stream."""
+    rng = np.random.default_rng(seed)
+    return _normal(rng, tuple(shape), dtype)
+
+
 def select_variant(q: np.ndarray, k: np.ndarray, v: np.ndarray, H_q: int, H_kv: int):
     """Nested variant: query heads [0, H_q), K/V heads [0, H_kv), contiguous."""
     return (np.ascontiguousarray(q[:, :H_q]), np.ascontiguousarray(k[:, :H_kv]),

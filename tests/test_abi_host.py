@@ -129,3 +129,52 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 2, 8, 16, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         sqa.sqa_attn_fwd(q, q[:, :1].contiguous(), q[:, :1].contiguous())
+
+
+# ------------------------------------------------------------------ backward
+def test_header_declares_the_backward():
+    names = _declared_functions()
+    assert "sqa_attn_bwd" in names and "sqa_attn_bwd_workspace_bytes" in names
+
+
+def test_bwd_workspace_bytes(lib):
+    # one (lse*log2 e, D) fp32 pair per query row, rows padded to a multiple of 32
+    assert sqa.sqa_attn_bwd_workspace_bytes(1, 8, 32768, 64) == 8 * 32768 * 8
+    # N = 33 pads to 64 rows: 2*3*64*8 = 3072 B
+    assert sqa.sqa_attn_bwd_workspace_bytes(2, 3, 33, 64) == 3072
+    # N = 1 pads to 32 rows: 32*8 = 256 B
+    assert sqa.sqa_attn_bwd_workspace_bytes(1, 1, 1, 64) == 256
+    assert sqa.sqa_attn_bwd_workspace_bytes(0, 8, 1024, 64) == 0
+    assert sqa.sqa_attn_bwd_workspace_bytes(1, 8, 1024, 16) == 0
+    assert sqa.sqa_attn_bwd_workspace_bytes(1, 8, 1024, 64, dtype="f32") == 0
+
+
+def _bwd(lib, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000,
+         do=FAKE + 0x400000, lse=FAKE + 0x500000, dq=FAKE + 0x600000, dk=FAKE + 0x700000,
+         dv=FAKE + 0x800000, B=1, Hq=8, Hkv=4, N=1024, d=64, dtype=1, scale=0.125, causal=0,
+         ws=FAKE + 0x900000, ws_bytes=1 << 20):
+    return lib.sqa_attn_bwd(q, k, v, o, do, lse, dq, dk, dv, B, Hq, Hkv, N, d, dtype, scale,
+                            causal, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(lse=None), 1), (dict(dv=None), 1),
+    (dict(Hkv=3), 2), (dict(N=-1), 2),
+    (dict(d=16), 3), (dict(dtype=0), 3), (dict(d=128), 3),
+    (dict(do=FAKE + 0x400008), 4), (dict(lse=FAKE + 0x500002), 4), (dict(ws=FAKE + 0x900008), 4),
+    (dict(ws=None), 5), (dict(ws_bytes=65535), 5),
+    (dict(scale=float("nan")), 7), (dict(causal=-1), 7),
+    (dict(dq=FAKE + 0x300000), 7),                   # dq aliases o
+    (dict(dk=FAKE + 0x600000 + 4096), 7),            # dk inside dq
+    (dict(ws=FAKE + 0x800000), 7),                   # workspace aliases dv
+])
+@cpu_only
+def test_bwd_rejects_invalid_arguments(lib, kw, code):
+    assert _bwd(lib, **kw) == code
+    assert lib.sqa_last_error().decode() != ""
+
+
+@cpu_only
+def test_bwd_zero_size_is_a_noop(lib):
+    assert _bwd(lib, q=None, B=0, ws=None) == 0
+    assert _bwd(lib, N=0, ws=None) == 0
