@@ -15,7 +15,12 @@ Prints ONE JSON line. The line also carries:
   * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
     sample of the same workload (sampled query rows, every head);
   * comparison: MHA / GQA-4 / MQA at the same shape (H_q = 16) and the
-    measured speedup of the SQA variant over MHA.
+    measured speedup of the SQA variant over MHA;
+  * backward: one sqa_attn_bwd call per step on the same workload (the
+    forward's o and lse, a seeded N(0,1) upstream gradient), with FLOPs
+    counted as 2.5x the forward's (the five matrix products of the textbook
+    backward) and, separately, the FLOPs the kernels execute (3.5x: the dK/dV
+    and dQ kernels both recompute S and dP).
 """
 from __future__ import annotations
 
@@ -111,6 +116,31 @@ def cpu_baseline(w, variant, causal, rows_count, arrays):
                       f"{dt:.2f} s wall"}
 
 
+def bench_backward(sqa, torch, q, k, v, w, causal, steps, warmup):
+    """Time sqa_attn_bwd; inputs, o, lse and the upstream gradient are resident."""
+    from synth import draw_upstream
+    o, lse = sqa.sqa_attn_fwd(q, k, v, scale=w.scale, causal=bool(causal), return_lse=True)
+    do = torch.from_numpy(draw_upstream(tuple(q.shape), "bf16", seed=55)).to("cuda").to(torch.bfloat16)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    B, Hq, N, d = q.shape
+    ws = torch.empty(max(1, sqa.sqa_attn_bwd_workspace_bytes(B, Hq, N, d)), dtype=torch.uint8, device="cuda")
+
+    def fn():
+        sqa.sqa_attn_bwd(q, k, v, o, do, lse, scale=w.scale, causal=bool(causal), dq=dq, dk=dk, dv=dv,
+                         workspace=ws)
+
+    ms = _timed(torch, fn, steps, warmup)
+    fwd = counted_flops(B, Hq, N, d, causal)
+    counted = 2.5 * fwd
+    tflops = counted / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "counted_flop": counted, "tflops_counted": round(tflops, 2),
+            "frac_of_peak_counted": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "executed_flop": 3.5 * fwd,
+            "tflops_executed": round(3.5 * fwd / (ms * 1e-3) / 1e12, 2),
+            "kernels": ["bwd_rowterms_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"],
+            "tokens_per_s": round(B * N / (ms * 1e-3), 1)}
+
+
 # v_exp_f32 issues at half rate: 64 lanes / 8 cycles per SIMD, 1024 SIMDs, 2.4 GHz
 PEAK_EXP_PER_S = 1024 * 8 * 2.4e9
 
@@ -203,6 +233,9 @@ def main():
     ap.add_argument("--causal", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only sqa_attn_bwd (for profiling) and print its object")
     ap.add_argument("--cpu-rows", type=int, default=65536)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
@@ -261,6 +294,12 @@ def main():
         torch.cuda.empty_cache()
         return ms, wall
 
+    if args.backward_only:
+        q, k, v = (dev(a) for a in select_variant(q_all, k_all, v_all, *variant))
+        print(json.dumps({"backward": bench_backward(sqa, torch, q, k, v, w, causal, args.steps,
+                                                     args.warmup)}), flush=True)
+        return
+
     ms, wall = run(variant)
     flops = counted_flops(w.B, Hq, w.N, w.d, causal)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -279,6 +318,13 @@ def main():
         if "16,16" in comparison:
             comparison["speedup_vs_mha"] = round(comparison["16,16"]["ms"] / ms, 3)
             comparison["expected_H_over_Hq"] = w.H / Hq
+
+    backward = None
+    if not args.no_backward and w.d == 64:
+        q, k, v = (dev(a) for a in select_variant(q_all, k_all, v_all, *variant))
+        backward = bench_backward(sqa, torch, q, k, v, w, causal, args.steps, args.warmup)
+        del q, k, v
+        torch.cuda.empty_cache()
 
     traffic = stored_traffic(w.name, variant, causal, w.d)
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
@@ -311,6 +357,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "comparison": comparison,
+        "backward": backward,
         "wall_s_timed_region": round(wall, 4),
     }
     print(json.dumps(line), flush=True)
