@@ -31,6 +31,12 @@ What is computed, and where it comes from
       P = softmax(S),  dP = dO V^T,  dS = P * (dP - rowsum(P * dP)),
       dQ = scale dS K,  dK_j = scale sum_{i in group j} dS^T Q_i,
       dV_j = sum_{i in group j} P^T dO_i.
+* The block (SQAT-m card, "Architecture details": dim 256, RMS Norm, SwiGLU
+  feed forward with 768 dim, RoPE). The card does not give the order; the
+  oracle uses the pre-norm residual block
+      h = x + layer(rms_norm(x, g1)),  y = h + swiglu(rms_norm(h, g2))
+  with rms_norm(x, g) = x / sqrt(mean_c x_c^2 + eps) * g and
+  swiglu(z) = (silu(z W_gate) * (z W_up)) W_down, silu(u) = u / (1 + e^-u).
 * The layer (SQAT-m, "Architecture details" and "Model size difference"):
   Q = X W_Q (H_q*d wide), K = X W_K and V = X W_V (H_kv*d wide), RoPE on Q and
   K, SQA, then Y = O_flat W_O with W_O of H_q*d rows. Weights are [in, out].
@@ -59,6 +65,9 @@ __all__ = [
     "rope",
     "layer",
     "layer_weight_shapes",
+    "rms_norm",
+    "swiglu",
+    "block",
     "attention_param_count",
 ]
 
@@ -355,3 +364,43 @@ def layer(x: np.ndarray, wq: np.ndarray, wk: np.ndarray, wv: np.ndarray, wo: np.
     o = attention(qh, kh, vh, scale=scale, causal=causal, threads=threads)
     o_flat = o.transpose(0, 2, 1, 3).reshape(B, N, H_q * d)
     return o_flat @ np.asarray(wo, np.float64)
+
+
+def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """RMS normalisation over the last axis in float64 (SQAT-m card,
+    "Architecture details": RMS Norm): x / sqrt(mean(x^2) + eps) * weight."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    if w.shape != x.shape[-1:]:
+        raise ValueError("weight must match the last axis of x")
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * w
+
+
+def swiglu(z: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """SwiGLU feed forward in float64 (SQAT-m card, "Architecture details":
+    SwiGLU feed forward with 768 dim): (silu(z W_gate) * (z W_up)) W_down with
+    silu(u) = u * sigmoid(u); weights [in, out]."""
+    z = np.asarray(z, dtype=np.float64)
+    g = z @ np.asarray(w_gate, dtype=np.float64)
+    u = z @ np.asarray(w_up, dtype=np.float64)
+    silu = g / (1.0 + np.exp(-g))
+    return (silu * u) @ np.asarray(w_down, dtype=np.float64)
+
+
+def block(x: np.ndarray, norm1: np.ndarray, wq: np.ndarray, wk: np.ndarray, wv: np.ndarray,
+          wo: np.ndarray, norm2: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
+          w_down: np.ndarray, H: int, H_q: int, H_kv: int, rope_base: float = 10000.0,
+          scale: Optional[float] = None, causal: bool = True, eps: float = 1e-6,
+          threads: int = 1) -> np.ndarray:
+    """One SQAT-m transformer block forward in float64 (pre-norm residual):
+    h = x + layer(rms_norm(x, norm1)); y = h + swiglu(rms_norm(h, norm2)).
+    x [B, N, D]; attention weights as ``layer``; w_gate, w_up [D, F];
+    w_down [F, D]. Returns y [B, N, D]."""
+    x = np.asarray(x, dtype=np.float64)
+    F = np.shape(w_gate)[1]
+    D = x.shape[-1]
+    if np.shape(w_gate) != (D, F) or np.shape(w_up) != (D, F) or np.shape(w_down) != (F, D):
+        raise ValueError("feed-forward weights must be [D, F], [D, F], [F, D]")
+    h = x + layer(rms_norm(x, norm1, eps), wq, wk, wv, wo, H, H_q, H_kv, rope_base=rope_base,
+                  scale=scale, causal=causal, threads=threads)
+    return h + swiglu(rms_norm(h, norm2, eps), w_gate, w_up, w_down)

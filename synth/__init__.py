@@ -183,6 +183,32 @@ def draw_layer(B: int, N: int, D: int, H: int, H_q: int, H_kv: int,
     return x, wq, wk, wv, wo
 
 
+def draw_block(B: int, N: int, D: int, H: int, H_q: int, H_kv: int, F: int, seed: int = 0,
+               wstd: Optional[float] = None):
+    """Inputs of one transformer block: x ~ N(0, 1) [B, N, D]; RMSNorm gains
+    1 + N(0, 0.1) [D] (two); W_Q, W_K, W_V, W_O as in ``draw_layer``'s shapes
+    and W_gate, W_up [D, F], W_down [F, D], all ~ N(0, wstd) with wstd
+    defaulting to 1/sqrt(fan_in) per matrix. bf16-representable float32.
+    Draw order: x, norm1, W_Q, W_K, W_V, W_O, norm2, W_gate, W_up, W_down."""
+    d = D // H
+    rng = np.random.default_rng(seed)
+    x = _normal(rng, (B, N, D), "bf16")
+
+    def gain():
+        g = _normal(rng, (D,), "f32", std=0.1) + np.float32(1.0)
+        return bf16_round(g)
+
+    def mat(fan_in, fan_out):
+        std = wstd if wstd is not None else 1.0 / np.sqrt(fan_in)
+        return _normal(rng, (fan_in, fan_out), "bf16", std=std)
+
+    n1 = gain()
+    wq, wk, wv, wo = mat(D, H_q * d), mat(D, H_kv * d), mat(D, H_kv * d), mat(H_q * d, D)
+    n2 = gain()
+    wg, wu, wd = mat(D, F), mat(D, F), mat(F, D)
+    return x, n1, wq, wk, wv, wo, n2, wg, wu, wd
+
+
 def draw_attn_case(B: int, H_q: int, H_kv: int, N: int, d: int, dtype: str = "bf16",
                    seed: int = 0, peaky: bool = False):
     """Q [B,H_q,N,d], K/V [B,H_kv,N,d] drawn directly at the variant's head counts."""
