@@ -199,6 +199,59 @@ def bench_layer(sqa, torch, w, args):
         "cpu_baseline": None, "comparison": None})
 
 
+def bench_block(sqa, torch, w, args):
+    """SQAT-m block: RMSNorm, SQA layer, residual, RMSNorm, SwiGLU, residual.
+    One block call per step for the selected variant; the other variants of
+    the workload (MHA / GQA / MQA) go in `comparison`."""
+    from synth import draw_block
+    variant = tuple(int(x) for x in args.variant.split(",")) if args.variant else w.variants[0]
+    d = w.d_model // w.H
+    dev = lambda a: torch.from_numpy(a).to("cuda").to(torch.bfloat16).contiguous()
+
+    def flops(hq, hkv):
+        attn = counted_flops(w.B, hq, w.N, d, True)
+        proj = 2.0 * w.B * w.N * w.d_model * (hq + 2 * hkv) * d + 2.0 * w.B * w.N * hq * d * w.d_model
+        ffn = 3 * 2.0 * w.B * w.N * w.d_model * w.d_ff
+        return attn, proj, ffn
+
+    def run(var):
+        hq, hkv = var
+        arrs = [dev(a) for a in draw_block(w.B, w.N, w.d_model, w.H, hq, hkv, w.d_ff, seed=0)]
+        out = torch.empty_like(arrs[0])
+        ws = torch.empty(sqa.sqa_block_workspace_bytes(w.B, w.N, w.d_model, w.H, hq, hkv, w.d_ff),
+                         dtype=torch.uint8, device="cuda")
+        fn = lambda: sqa.sqa_block_fwd(*arrs, H=w.H, H_q=hq, H_kv=hkv, rope_base=w.rope_base,
+                                       scale=w.scale, causal=True, out=out, workspace=ws)
+        ms = _timed(torch, fn, args.steps, args.warmup)
+        del arrs, out, ws
+        torch.cuda.empty_cache()
+        return ms
+
+    ms = run(variant)
+    attn, proj, ffn = flops(*variant)
+    tflops = (attn + proj + ffn) / (ms * 1e-3) / 1e12
+    comparison = None
+    if not args.no_compare:
+        comparison = {}
+        for var in w.variants:
+            if var == variant:
+                continue
+            cms = run(var)
+            comparison[f"{var[0]},{var[1]}"] = {"ms": round(cms, 4)}
+        if "16,16" in comparison:
+            comparison["time_ratio_vs_mha"] = round(ms / comparison["16,16"]["ms"], 4)
+    return _common(args, ms, w, {
+        "value": round(tflops, 3), "unit": "TFLOP/s", "dtype": "bf16",
+        "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1),
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.d_model, "H": w.H,
+                   "H_q": variant[0], "H_kv": variant[1], "d": d, "F": w.d_ff, "causal": 1,
+                   "flop_attention": attn, "flop_projections": proj, "flop_ffn": ffn},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "whole block (small GEMMs, d=16 attention)"},
+        "cpu_baseline": None, "comparison": comparison})
+
+
 def bench_f32(sqa, torch, w, args):
     """SQAT-m attention core in fp32 (VALU-bound correctness workload)."""
     from synth import draw_qkv, select_variant
@@ -272,6 +325,9 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
+    if w.block:
+        print(json.dumps(bench_block(sqa, torch, w, args)), flush=True)
+        return
     if w.layer:
         print(json.dumps(bench_layer(sqa, torch, w, args)), flush=True)
         return

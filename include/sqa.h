@@ -157,6 +157,44 @@ sqa_status sqa_layer_fwd(const void* x, const void* w_q, const void* w_k, const 
                          int causal, int dtype, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * sqa_block_workspace_bytes -- bytes of device workspace sqa_block_fwd needs:
+ * sqa_layer_workspace_bytes(...) plus bf16 buffers for the normalised input
+ * [B, N, D], the residual stream after attention [B, N, D] and the SwiGLU
+ * activations [B, N, F], each rounded up to 256 bytes. 0 for invalid sizes.
+ */
+size_t sqa_block_workspace_bytes(int64_t B, int64_t N, int64_t D, int64_t H, int64_t H_q,
+                                 int64_t H_kv, int64_t F, int dtype);
+
+/*
+ * sqa_block_fwd -- one SQAT-m transformer block forward (SQAT-m model card,
+ * "Architecture details": dim 256, RMS Norm, SwiGLU feed forward with 768
+ * dim, RoPE; the card does not state the order, this is the pre-norm
+ * residual block):
+ *   h = x + layer(rms_norm(x, norm1))          (layer as sqa_layer_fwd)
+ *   y = h + (silu(z W_gate) * (z W_up)) W_down,  z = rms_norm(h, norm2)
+ *   rms_norm(x, g) = x / sqrt(mean_c x_c^2 + eps) * g,  silu(u) = u / (1 + e^-u)
+ *
+ *   x                [B, N, D]   bf16 input
+ *   norm1, norm2     [D]         bf16 RMSNorm gains
+ *   w_q, w_k, w_v, w_o           bf16, shapes as in sqa_layer_fwd
+ *   w_gate, w_up     [D, F]      bf16      w_down [F, D] bf16
+ *   y                [B, N, D]   bf16 output; must not overlap an input
+ *   eps              RMSNorm epsilon, finite and >= 0
+ *   workspace        at least sqa_block_workspace_bytes(...) bytes,
+ *                    256-byte aligned, owned by the caller.
+ *   Precision: norms, products and SwiGLU in fp32; the normalised input, the
+ *   residual stream h, the activations and Q/K/V/O are stored as bf16.
+ *   Layer constraints as sqa_layer_fwd; F a positive multiple of 16.
+ * Errors: as sqa_layer_fwd.
+ */
+sqa_status sqa_block_fwd(const void* x, const void* norm1, const void* w_q, const void* w_k,
+                         const void* w_v, const void* w_o, const void* norm2, const void* w_gate,
+                         const void* w_up, const void* w_down, void* y, int64_t B, int64_t N,
+                         int64_t D, int64_t H, int64_t H_q, int64_t H_kv, int64_t F,
+                         float rope_base, float scale, float eps, int causal, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code. Never NULL. */
 const char* sqa_status_str(int status);
 

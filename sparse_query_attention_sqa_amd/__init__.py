@@ -12,6 +12,9 @@ library is not built, importing the functions raises.
     sqa_layer_fwd(x, w_q, w_k, w_v, w_o, *, H, H_q, H_kv, rope_base=10000.0,
                   scale=None, causal=True, out=None, workspace=None)
     sqa_layer_workspace_bytes(B, N, D, H, H_q, H_kv, dtype="bf16")
+    sqa_block_fwd(x, norm1, w_q, w_k, w_v, w_o, norm2, w_gate, w_up, w_down, *, H, H_q, H_kv,
+                  rope_base=10000.0, scale=None, eps=1e-6, causal=True, out=None, workspace=None)
+    sqa_block_workspace_bytes(B, N, D, H, H_q, H_kv, F, dtype="bf16")
 """
 from __future__ import annotations
 
@@ -21,7 +24,8 @@ import os
 from typing import Optional
 
 __all__ = ["SQAError", "lib_path", "load_library", "sqa_attn_fwd", "sqa_attn_bwd",
-           "sqa_attn_bwd_workspace_bytes", "sqa_layer_fwd",
+           "sqa_attn_bwd_workspace_bytes", "sqa_layer_fwd", "sqa_block_fwd",
+           "sqa_block_workspace_bytes",
            "sqa_layer_workspace_bytes", "sqa_status_str", "sqa_version",
            "SQA_F32", "SQA_BF16"]
 
@@ -68,6 +72,11 @@ def load_library() -> ctypes.CDLL:
     lib.sqa_layer_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32,
                                   ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.sqa_layer_fwd.restype = ctypes.c_int
+    lib.sqa_block_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.c_int]
+    lib.sqa_block_workspace_bytes.restype = ctypes.c_size_t
+    lib.sqa_block_fwd.argtypes = [vp] * 11 + [i64] * 7 + [f32, f32, f32, ctypes.c_int, ctypes.c_int,
+                                                          vp, ctypes.c_size_t, vp]
+    lib.sqa_block_fwd.restype = ctypes.c_int
     lib.sqa_status_str.argtypes = [ctypes.c_int]
     lib.sqa_status_str.restype = ctypes.c_char_p
     lib.sqa_last_error.argtypes = []
@@ -247,6 +256,50 @@ def sqa_layer_fwd(x, w_q, w_k, w_v, w_o, *, H: int, H_q: int, H_kv: int,
     st = lib.sqa_layer_fwd(x.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(),
                            w_o.data_ptr(), out.data_ptr(), B, N, D, H, H_q, H_kv,
                            float(rope_base), float(scale), int(bool(causal)), _dtype_code(x),
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           _stream_handle(x.device))
+    _check(st)
+    return out
+
+
+def sqa_block_workspace_bytes(B: int, N: int, D: int, H: int, H_q: int, H_kv: int, F: int,
+                              dtype: str = "bf16") -> int:
+    code = SQA_BF16 if dtype == "bf16" else SQA_F32
+    return int(load_library().sqa_block_workspace_bytes(B, N, D, H, H_q, H_kv, F, code))
+
+
+def sqa_block_fwd(x, norm1, w_q, w_k, w_v, w_o, norm2, w_gate, w_up, w_down, *, H: int, H_q: int,
+                  H_kv: int, rope_base: float = 10000.0, scale: Optional[float] = None,
+                  eps: float = 1e-6, causal: bool = True, out=None, workspace=None):
+    """One pre-norm transformer block: h = x + layer(rms_norm(x)); y = h + SwiGLU(rms_norm(h)).
+
+    x [B, N, D] bf16; norm1/norm2 [D]; attention weights as ``sqa_layer_fwd``;
+    w_gate, w_up [D, F], w_down [F, D]; all bf16. Returns y [B, N, D].
+    """
+    torch = _torch()
+    lib = load_library()
+    _require_device(x, norm1, w_q, w_k, w_v, w_o, norm2, w_gate, w_up, w_down)
+    if x.dim() != 3 or w_gate.dim() != 2:
+        raise ValueError("x must be [B, N, D] and w_gate [D, F]")
+    B, N, D = x.shape
+    F = w_gate.shape[1]
+    d = D // H if H else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d) if d > 0 else 1.0
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _require_device(out)
+    code = _dtype_code(x)
+    need = int(lib.sqa_block_workspace_bytes(B, N, D, H, H_q, H_kv, F, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    else:
+        _require_device(workspace)
+    st = lib.sqa_block_fwd(x.data_ptr(), norm1.data_ptr(), w_q.data_ptr(), w_k.data_ptr(),
+                           w_v.data_ptr(), w_o.data_ptr(), norm2.data_ptr(), w_gate.data_ptr(),
+                           w_up.data_ptr(), w_down.data_ptr(), out.data_ptr(), B, N, D, H, H_q, H_kv,
+                           F, float(rope_base), float(scale), float(eps), int(bool(causal)), code,
                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                            _stream_handle(x.device))
     _check(st)

@@ -73,7 +73,32 @@ struct OprojProblem {
   const void* wo;
   void* y;
   int64_t B, N, Dm, Hq, d;
+  const void* resid;  // optional [B*N, Dm] added in the epilogue (nullptr: none)
 };
 hipError_t launch_out_proj(const OprojProblem& p, hipStream_t stream);
+
+// y [M, Ncols] = a [M, K] (row-major) times w [K, Ncols] (+ resid [M, Ncols]).
+struct DenseProblem {
+  const void* a;
+  const void* w;
+  const void* resid;  // nullable
+  void* y;
+  int64_t M, K, Ncols;
+};
+hipError_t launch_dense_residual(const DenseProblem& p, hipStream_t stream);
+
+// y = x / sqrt(mean(x^2) + eps) * g over rows of D (bf16 in/out).
+hipError_t launch_rms_norm(const void* x, const void* g, void* y, int64_t M, int64_t D, float eps,
+                           hipStream_t stream);
+
+// h [M, F] = silu(z w_gate) * (z w_up); z [M, K], w_gate / w_up [K, F].
+struct GateUpProblem {
+  const void* z;
+  const void* w_gate;
+  const void* w_up;
+  void* h;
+  int64_t M, K, F;
+};
+hipError_t launch_gate_up(const GateUpProblem& p, hipStream_t stream);
 
 }  // namespace sqa

@@ -8,7 +8,15 @@
 //              with rotary position embedding applied to Q and K in the
 //              epilogue (rotate-half pairs (c, c+d/2)), reading the table.
 //   out_proj : O_flat [B*N, Hq*d] x W_o -> Y [B, N, Dm], reading O in its
-//              [B, Hq, N, d] attention layout (no separate transpose pass).
+//              [B, Hq, N, d] attention layout (no separate transpose pass);
+//              also a plain row-major A (the feed-forward down projection),
+//              with an optional residual added in the epilogue.
+//
+// Block extras (SQAT-m card, "Architecture details": RMS Norm, SwiGLU feed
+// forward with 768 dim):
+//   rms_norm  : y = x / sqrt(mean(x^2) + eps) * g per row, fp32 math.
+//   gate_up   : h = silu(z W_gate) * (z W_up), both products from one A tile
+//               row block, the SwiGLU combination fused in the epilogue.
 //
 // Both are bf16 MFMA GEMMs (v_mfma_f32_32x32x16_bf16, fp32 accumulate) with a
 // 64x64 output tile per 4-wave workgroup (2x2 waves of 32x32). The reduction
@@ -223,6 +231,7 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(QkvArgs a) {
 struct OprojArgs {
   ASrc A;
   WSrc W;
+  const uint16_t* resid;  // [M, Ncols] added before rounding, or nullptr
   uint16_t* y;
   int64_t M, Ncols, K;
   int nblk_n;
@@ -242,13 +251,119 @@ __global__ __launch_bounds__(kThreads) void out_proj_kernel(OprojArgs a) {
   const int64_t m = m0 + r;
   const int64_t n = n0 + cq * 16;
   if (m >= a.M || n >= a.Ncols) return;
+  float yv[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) yv[e] = cs[r * CPITCH + cq * 16 + e];
+  if (a.resid != nullptr) {
+    const u32x4_t* rp = reinterpret_cast<const u32x4_t*>(a.resid + m * a.Ncols + n);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4_t rv = rp[h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t pr = rv[e];
+        yv[8 * h + 2 * e] += __builtin_bit_cast(float, pr << 16);
+        yv[8 * h + 2 * e + 1] += __builtin_bit_cast(float, pr & 0xffff0000u);
+      }
+    }
+  }
   u32x4_t w0, w1;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    w0[e] = pack_bf16x2(cs[r * CPITCH + cq * 16 + 2 * e], cs[r * CPITCH + cq * 16 + 2 * e + 1]);
-    w1[e] = pack_bf16x2(cs[r * CPITCH + cq * 16 + 8 + 2 * e], cs[r * CPITCH + cq * 16 + 8 + 2 * e + 1]);
+    w0[e] = pack_bf16x2(yv[2 * e], yv[2 * e + 1]);
+    w1[e] = pack_bf16x2(yv[8 + 2 * e], yv[8 + 2 * e + 1]);
   }
   uint16_t* dst = a.y + m * a.Ncols + n;
+  *reinterpret_cast<u32x4_t*>(dst) = w0;
+  *reinterpret_cast<u32x4_t*>(dst + 8) = w1;
+}
+
+// ---------------------------------------------------------------- RMSNorm
+struct NormArgs {
+  const uint16_t* x;
+  const uint16_t* g;
+  uint16_t* y;
+  int64_t M;
+  int D;
+  float eps;
+};
+
+// 32 lanes per row (8 rows per workgroup), 8 bf16 per lane per pass; the
+// sum of squares is reduced with lane shuffles inside the 32-lane half.
+__global__ __launch_bounds__(kThreads) void rms_norm_kernel(NormArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int l = threadIdx.x & 31;
+  if (row >= a.M) return;  // whole 32-lane halves leave together
+  const uint16_t* xr = a.x + row * a.D;
+  float ss = 0.f;
+  for (int c = l * 8; c < a.D; c += 256) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t pr = v[e];
+      const float lo = __builtin_bit_cast(float, pr << 16), hi = __builtin_bit_cast(float, pr & 0xffff0000u);
+      ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) ss += __shfl_xor(ss, off);
+  const float r = 1.0f / sqrtf(ss / (float)a.D + a.eps);
+  uint16_t* yr = a.y + row * a.D;
+  for (int c = l * 8; c < a.D; c += 256) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr + c);
+    const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(a.g + c);
+    u32x4_t o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t pr = v[e], gr = gv[e];
+      const float x0 = __builtin_bit_cast(float, pr << 16), x1 = __builtin_bit_cast(float, pr & 0xffff0000u);
+      const float g0 = __builtin_bit_cast(float, gr << 16), g1 = __builtin_bit_cast(float, gr & 0xffff0000u);
+      o[e] = pack_bf16x2(x0 * r * g0, x1 * r * g1);
+    }
+    *reinterpret_cast<u32x4_t*>(yr + c) = o;
+  }
+}
+
+// ---------------------------------------------------------------- SwiGLU
+struct GateUpArgs {
+  ASrc A;
+  WSrc Wg, Wu;
+  uint16_t* h;
+  int64_t M, F, K;
+  int nblk_n;
+};
+
+__global__ __launch_bounds__(kThreads) void gate_up_kernel(GateUpArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t as_[BM * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t ws_[BN * PITCH];
+  __shared__ __attribute__((aligned(16))) float cg[BM * CPITCH];
+  __shared__ __attribute__((aligned(16))) float cu[BM * CPITCH];
+  const int64_t m0 = (int64_t)(blockIdx.x / a.nblk_n) * BM;
+  const int64_t n0 = (int64_t)(blockIdx.x % a.nblk_n) * BN;
+  f32x16_t acc;
+  gemm_tile(a.A, a.Wg, a.M, a.F, a.K, m0, n0, as_, ws_, acc);
+  spill_acc(acc, cg);
+  gemm_tile(a.A, a.Wu, a.M, a.F, a.K, m0, n0, as_, ws_, acc);
+  spill_acc(acc, cu);
+  const int tid = threadIdx.x;
+  const int r = tid >> 2, cq = tid & 3;
+  const int64_t m = m0 + r;
+  const int64_t n = n0 + cq * 16;
+  if (m >= a.M || n >= a.F) return;
+  float hv[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float g = cg[r * CPITCH + cq * 16 + e];
+    const float u = cu[r * CPITCH + cq * 16 + e];
+    hv[e] = g / (1.0f + expf(-g)) * u;  // silu(g) * u
+  }
+  u32x4_t w0, w1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    w0[e] = pack_bf16x2(hv[2 * e], hv[2 * e + 1]);
+    w1[e] = pack_bf16x2(hv[8 + 2 * e], hv[8 + 2 * e + 1]);
+  }
+  uint16_t* dst = a.h + m * a.F + n;
   *reinterpret_cast<u32x4_t*>(dst) = w0;
   *reinterpret_cast<u32x4_t*>(dst + 8) = w1;
 }
@@ -337,6 +452,7 @@ hipError_t launch_out_proj(const OprojProblem& p, hipStream_t stream) {
   a.W.ncol[0] = p.Dm;
   a.W.ncol[1] = 0;
   a.W.ncol[2] = 0;
+  a.resid = static_cast<const uint16_t*>(p.resid);
   a.y = static_cast<uint16_t*>(p.y);
   a.M = p.B * p.N;
   a.Ncols = p.Dm;
@@ -345,6 +461,79 @@ hipError_t launch_out_proj(const OprojProblem& p, hipStream_t stream) {
   const int64_t nblk = ((a.M + BM - 1) / BM) * a.nblk_n;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(out_proj_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_residual(const DenseProblem& p, hipStream_t stream) {
+  if (p.K % 16 != 0 || p.Ncols % 16 != 0) return hipErrorInvalidValue;
+  OprojArgs a;
+  a.A.p = static_cast<const uint16_t*>(p.a);
+  a.A.K = p.K;
+  a.A.gather = 0;
+  a.A.N = 1;
+  a.A.Hq = 1;
+  a.A.d = 1;
+  a.W.w[0] = static_cast<const uint16_t*>(p.w);
+  a.W.w[1] = a.W.w[0];
+  a.W.w[2] = a.W.w[0];
+  a.W.ncol[0] = p.Ncols;
+  a.W.ncol[1] = 0;
+  a.W.ncol[2] = 0;
+  a.resid = static_cast<const uint16_t*>(p.resid);
+  a.y = static_cast<uint16_t*>(p.y);
+  a.M = p.M;
+  a.Ncols = p.Ncols;
+  a.K = p.K;
+  a.nblk_n = (int)((a.Ncols + BN - 1) / BN);
+  const int64_t nblk = ((a.M + BM - 1) / BM) * a.nblk_n;
+  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(out_proj_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_norm(const void* x, const void* g, void* y, int64_t M, int64_t D, float eps,
+                           hipStream_t stream) {
+  if (D % 8 != 0 || D > (int64_t(1) << 20)) return hipErrorInvalidValue;
+  NormArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.g = static_cast<const uint16_t*>(g);
+  a.y = static_cast<uint16_t*>(y);
+  a.M = M;
+  a.D = (int)D;
+  a.eps = eps;
+  const int64_t nblk = (M + 7) / 8;
+  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rms_norm_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up(const GateUpProblem& p, hipStream_t stream) {
+  if (p.K % 16 != 0 || p.F % 16 != 0) return hipErrorInvalidValue;
+  GateUpArgs a;
+  a.A.p = static_cast<const uint16_t*>(p.z);
+  a.A.K = p.K;
+  a.A.gather = 0;
+  a.A.N = 1;
+  a.A.Hq = 1;
+  a.A.d = 1;
+  for (int i = 0; i < 3; ++i) {
+    a.Wg.w[i] = static_cast<const uint16_t*>(p.w_gate);
+    a.Wu.w[i] = static_cast<const uint16_t*>(p.w_up);
+  }
+  a.Wg.ncol[0] = p.F;
+  a.Wg.ncol[1] = 0;
+  a.Wg.ncol[2] = 0;
+  a.Wu.ncol[0] = p.F;
+  a.Wu.ncol[1] = 0;
+  a.Wu.ncol[2] = 0;
+  a.h = static_cast<uint16_t*>(p.h);
+  a.M = p.M;
+  a.F = p.F;
+  a.K = p.K;
+  a.nblk_n = (int)((a.F + BN - 1) / BN);
+  const int64_t nblk = ((a.M + BM - 1) / BM) * a.nblk_n;
+  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gate_up_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

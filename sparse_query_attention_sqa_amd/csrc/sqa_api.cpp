@@ -165,11 +165,11 @@ size_t sqa_layer_workspace_bytes(int64_t B, int64_t N, int64_t D, int64_t H, int
   return 2 * round256(nq) + 2 * round256(nkv) + round256(ncs);
 }
 
-sqa_status sqa_layer_fwd(const void* x, const void* w_q, const void* w_k, const void* w_v,
-                         const void* w_o, void* y, int64_t B, int64_t N, int64_t D, int64_t H,
-                         int64_t H_q, int64_t H_kv, float rope_base, float scale, int causal,
-                         int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  g_err.clear();
+namespace {
+
+// Shape and argument rules of the layer (shared with the block).
+sqa_status check_layer(int64_t B, int64_t N, int64_t D, int64_t H, int64_t H_q, int64_t H_kv, float rope_base,
+                       float scale, int causal, int dtype, int64_t* d_out) {
   if (B < 0 || N < 0 || D < 0 || H < 0) return fail(SQA_ERR_SHAPE, "negative size");
   if (H < 1 || D < 1 || D % H != 0)
     return fail(SQA_ERR_SHAPE, "D must be a positive multiple of H (got D=%lld, H=%lld)", (long long)D,
@@ -180,8 +180,47 @@ sqa_status sqa_layer_fwd(const void* x, const void* w_q, const void* w_k, const 
   if (s != SQA_OK) return s;
   if (!std::isfinite(rope_base) || rope_base <= 0.f) return fail(SQA_ERR_ARG, "rope_base must be finite and > 0");
   if (D % 16 != 0) return fail(SQA_ERR_UNSUPPORTED, "D must be a multiple of 16");
-  if (B == 0 || N == 0) return SQA_OK;
   if (B * N * D > kMaxElems) return fail(SQA_ERR_SHAPE, "tensor too large");
+  *d_out = d;
+  return SQA_OK;
+}
+
+// Launch the layer on already validated arguments; `resid` (nullable) is
+// added to the output projection.
+sqa_status run_layer(const void* x, const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                     const void* resid, void* y, int64_t B, int64_t N, int64_t D, int64_t d, int64_t H_q,
+                     int64_t H_kv, float rope_base, float scale, int causal, char* ws, hipStream_t st) {
+  const size_t nq = round256((size_t)(B * H_q * N * d) * 2), nkv = round256((size_t)(B * H_kv * N * d) * 2);
+  void* qb = ws;
+  void* kb = ws + nq;
+  void* vb = ws + nq + nkv;
+  void* ob = ws + nq + 2 * nkv;
+  float* cs = reinterpret_cast<float*>(ws + 2 * nq + 2 * nkv);
+  hipError_t e = sqa::launch_rope_table(cs, N, d, rope_base, st);
+  if (e != hipSuccess) return hip_fail(e, "RoPE table launch");
+  sqa::QkvProblem qp{cs, x, w_q, w_k, w_v, qb, kb, vb, B, N, D, H_q, H_kv, d, rope_base};
+  e = sqa::launch_qkv_rope(qp, st);
+  if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
+  sqa::AttnProblem ap{qb, kb, vb, ob, nullptr, B, H_q, H_kv, N, d, scale, causal};
+  e = sqa::launch_attn_fwd_bf16(ap, st);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  sqa::OprojProblem op{ob, w_o, y, B, N, D, H_q, d, resid};
+  e = sqa::launch_out_proj(op, st);
+  if (e != hipSuccess) return hip_fail(e, "output projection launch");
+  return SQA_OK;
+}
+
+}  // namespace
+
+sqa_status sqa_layer_fwd(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                         const void* w_o, void* y, int64_t B, int64_t N, int64_t D, int64_t H,
+                         int64_t H_q, int64_t H_kv, float rope_base, float scale, int causal,
+                         int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int64_t d = 0;
+  sqa_status s = check_layer(B, N, D, H, H_q, H_kv, rope_base, scale, causal, dtype, &d);
+  if (s != SQA_OK) return s;
+  if (B == 0 || N == 0) return SQA_OK;
   if (!x || !w_q || !w_k || !w_v || !w_o || !y) return fail(SQA_ERR_NULL, "inputs and y must be non-NULL");
   if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) || !aligned(w_o, 16) ||
       !aligned(y, 16))
@@ -199,27 +238,71 @@ sqa_status sqa_layer_fwd(const void* x, const void* w_q, const void* w_k, const 
   if (overlaps(workspace, need, x, nx) || overlaps(workspace, need, y, nx) || overlaps(workspace, need, w_q, nwq) ||
       overlaps(workspace, need, w_k, nwk) || overlaps(workspace, need, w_v, nwk) || overlaps(workspace, need, w_o, nwq))
     return fail(SQA_ERR_ARG, "workspace overlaps an input or y");
+  return run_layer(x, w_q, w_k, w_v, w_o, nullptr, y, B, N, D, d, H_q, H_kv, rope_base, scale, causal,
+                   static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
 
-  const size_t nq = round256((size_t)(B * H_q * N * d) * 2), nkv = round256((size_t)(B * H_kv * N * d) * 2);
+size_t sqa_block_workspace_bytes(int64_t B, int64_t N, int64_t D, int64_t H, int64_t H_q, int64_t H_kv,
+                                 int64_t F, int dtype) {
+  const size_t lw = sqa_layer_workspace_bytes(B, N, D, H, H_q, H_kv, dtype);
+  if (lw == 0 || F <= 0 || B * N * F > kMaxElems) return 0;
+  return lw + 2 * round256((size_t)(B * N * D) * 2) + round256((size_t)(B * N * F) * 2);
+}
+
+sqa_status sqa_block_fwd(const void* x, const void* norm1, const void* w_q, const void* w_k, const void* w_v,
+                         const void* w_o, const void* norm2, const void* w_gate, const void* w_up,
+                         const void* w_down, void* y, int64_t B, int64_t N, int64_t D, int64_t H, int64_t H_q,
+                         int64_t H_kv, int64_t F, float rope_base, float scale, float eps, int causal, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int64_t d = 0;
+  sqa_status s = check_layer(B, N, D, H, H_q, H_kv, rope_base, scale, causal, dtype, &d);
+  if (s != SQA_OK) return s;
+  if (F < 1 || F % 16 != 0) return fail(SQA_ERR_UNSUPPORTED, "F must be a positive multiple of 16 (got %lld)",
+                                        (long long)F);
+  if (!std::isfinite(eps) || eps < 0.f) return fail(SQA_ERR_ARG, "eps must be finite and >= 0");
+  if (B == 0 || N == 0) return SQA_OK;
+  if (B * N * F > kMaxElems) return fail(SQA_ERR_SHAPE, "tensor too large");
+  const void* ins[10] = {x, norm1, w_q, w_k, w_v, w_o, norm2, w_gate, w_up, w_down};
+  for (const void* p : ins)
+    if (!p) return fail(SQA_ERR_NULL, "inputs must be non-NULL");
+  if (!y) return fail(SQA_ERR_NULL, "y must be non-NULL");
+  for (const void* p : ins)
+    if (!aligned(p, 16)) return fail(SQA_ERR_ALIGN, "inputs must be 16-byte aligned");
+  if (!aligned(y, 16)) return fail(SQA_ERR_ALIGN, "y must be 16-byte aligned");
+  const size_t need = sqa_block_workspace_bytes(B, N, D, H, H_q, H_kv, F, dtype);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SQA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!aligned(workspace, 256)) return fail(SQA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const size_t nx = (size_t)(B * N * D) * 2;
+  const size_t nwq = (size_t)(D * H_q * d) * 2, nwk = (size_t)(D * H_kv * d) * 2, nf = (size_t)(D * F) * 2;
+  const size_t in_n[10] = {nx, (size_t)D * 2, nwq, nwk, nwk, nwq, (size_t)D * 2, nf, nf, nf};
+  for (int i = 0; i < 10; ++i) {
+    if (overlaps(y, nx, ins[i], in_n[i])) return fail(SQA_ERR_ARG, "y overlaps an input");
+    if (overlaps(workspace, need, ins[i], in_n[i])) return fail(SQA_ERR_ARG, "workspace overlaps an input");
+  }
+  if (overlaps(workspace, need, y, nx)) return fail(SQA_ERR_ARG, "workspace overlaps y");
+
   char* ws = static_cast<char*>(workspace);
-  void* qb = ws;
-  void* kb = ws + nq;
-  void* vb = ws + nq + nkv;
-  void* ob = ws + nq + 2 * nkv;
-  float* cs = reinterpret_cast<float*>(ws + 2 * nq + 2 * nkv);
+  const size_t lw = sqa_layer_workspace_bytes(B, N, D, H, H_q, H_kv, dtype);
+  void* xn = ws + lw;                            // normalised input of a sub-layer
+  void* hb = ws + lw + round256(nx);             // residual stream after attention
+  void* gb = ws + lw + 2 * round256(nx);         // SwiGLU activations [M, F]
   hipStream_t st = static_cast<hipStream_t>(stream);
-
-  hipError_t e = sqa::launch_rope_table(cs, N, d, rope_base, st);
-  if (e != hipSuccess) return hip_fail(e, "RoPE table launch");
-  sqa::QkvProblem qp{cs, x, w_q, w_k, w_v, qb, kb, vb, B, N, D, H_q, H_kv, d, rope_base};
-  e = sqa::launch_qkv_rope(qp, st);
-  if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
-  sqa::AttnProblem ap{qb, kb, vb, ob, nullptr, B, H_q, H_kv, N, d, scale, causal};
-  e = sqa::launch_attn_fwd_bf16(ap, st);
-  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-  sqa::OprojProblem op{ob, w_o, y, B, N, D, H_q, d};
-  e = sqa::launch_out_proj(op, st);
-  if (e != hipSuccess) return hip_fail(e, "output projection launch");
+  const int64_t M = B * N;
+  hipError_t e = sqa::launch_rms_norm(x, norm1, xn, M, D, eps, st);
+  if (e != hipSuccess) return hip_fail(e, "RMSNorm launch");
+  s = run_layer(xn, w_q, w_k, w_v, w_o, x, hb, B, N, D, d, H_q, H_kv, rope_base, scale, causal, ws, st);
+  if (s != SQA_OK) return s;
+  e = sqa::launch_rms_norm(hb, norm2, xn, M, D, eps, st);
+  if (e != hipSuccess) return hip_fail(e, "RMSNorm launch");
+  sqa::GateUpProblem gp{xn, w_gate, w_up, gb, M, D, F};
+  e = sqa::launch_gate_up(gp, st);
+  if (e != hipSuccess) return hip_fail(e, "SwiGLU gate/up launch");
+  sqa::DenseProblem dp{gb, w_down, hb, y, M, F, D};
+  e = sqa::launch_dense_residual(dp, st);
+  if (e != hipSuccess) return hip_fail(e, "down projection launch");
   return SQA_OK;
 }
 

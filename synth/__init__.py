@@ -76,6 +76,8 @@ class Workload:
     sampled_rows: Optional[int] = None      # None: every row is checked
     peaky: bool = False
     layer: bool = False
+    block: bool = False         # whole transformer block (RMSNorm, layer, SwiGLU)
+    d_ff: int = 0               # SwiGLU width of a block workload
     d_model: int = 0
     rope_base: float = 10000.0
     description: str = ""
@@ -93,6 +95,14 @@ WORKLOADS = {
         dtype="bf16", causal=(1,), scale=0.25, layer=True, d_model=256,
         rope_base=10000.0,
         description="SQAT-m layer B=16 N=1024 D=256 (8,4) d=16 bf16 causal"),
+    # SQAT-m transformer block forward (RMSNorm, SQA layer, SwiGLU 768,
+    # residuals), bf16, causal; MHA / GQA / MQA variants for the
+    # time-per-batch comparison of the SQAT-m card.
+    "sqatm_block_bf16": Workload(
+        name="sqatm_block_bf16", B=16, N=1024, H=16, d=16,
+        variants=((8, 4), (16, 16), (16, 4), (16, 1)), dtype="bf16", causal=(1,),
+        scale=0.25, block=True, d_model=256, d_ff=768, rope_base=10000.0,
+        description="SQAT-m block B=16 N=1024 D=256 F=768 SQA(8,4) vs MHA/GQA/MQA bf16 causal"),
     # Long-context encoder-style attention at 32k.
     "long32k_bf16": Workload(
         name="long32k_bf16", B=1, N=32768, H=16, d=64,

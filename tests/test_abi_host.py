@@ -178,3 +178,33 @@ def test_bwd_rejects_invalid_arguments(lib, kw, code):
 def test_bwd_zero_size_is_a_noop(lib):
     assert _bwd(lib, q=None, B=0, ws=None) == 0
     assert _bwd(lib, N=0, ws=None) == 0
+
+
+# ------------------------------------------------------------------ block
+def test_block_workspace_bytes(lib):
+    # SQAT-m block B=16 N=1024 D=256 (8,4) F=768: the layer's workspace plus the
+    # normalised input and residual stream (8 MiB each) and the SwiGLU
+    # activations (24 MiB)
+    layer = 2 * 4194304 + 2 * 2097152 + 65536
+    assert sqa.sqa_block_workspace_bytes(16, 1024, 256, 16, 8, 4, 768) == layer + 2 * 8388608 + 25165824
+    assert sqa.sqa_block_workspace_bytes(16, 1024, 256, 16, 8, 4, 0) == 0
+    assert sqa.sqa_block_workspace_bytes(0, 1024, 256, 16, 8, 4, 768) == 0
+
+
+def _block(lib, x=FAKE, ws=FAKE + 0x4000000, ws_bytes=1 << 27, B=16, N=1024, D=256, H=16, Hq=8,
+           Hkv=4, F=768, eps=1e-6, dtype=1, g2=FAKE + 0x150000):
+    return lib.sqa_block_fwd(x, FAKE + 0x140000, FAKE + 0x100000, FAKE + 0x110000,
+                             FAKE + 0x120000, FAKE + 0x130000, g2, FAKE + 0x160000,
+                             FAKE + 0x1a0000, FAKE + 0x1e0000, FAKE + 0x2000000, B, N, D, H, Hq,
+                             Hkv, F, 10000.0, 0.25, eps, 1, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(g2=None), 1), (dict(ws=None), 5), (dict(ws_bytes=1 << 20), 5),
+    (dict(F=0), 3), (dict(F=100), 3), (dict(dtype=0), 3), (dict(D=250), 2),
+    (dict(eps=-1.0), 7), (dict(eps=float("nan")), 7), (dict(g2=FAKE + 0x150002), 4),
+    (dict(ws=FAKE + 0x4000010), 4), (dict(ws=FAKE + 0x1e0000), 7),
+])
+@cpu_only
+def test_block_rejects_invalid_arguments(lib, kw, code):
+    assert _block(lib, **kw) == code
