@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsqa.so")
 
 SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_bf16_d64.hip", "attn_fwd_f32.hip", "attn_bwd_bf16_d64.hip",
-           "layer_gemm.hip", "sqa_api.cpp"]
+           "gemm_bf16.hip", "norm_rope.hip", "sqa_api.cpp"]
 
 
 def hipcc() -> str:

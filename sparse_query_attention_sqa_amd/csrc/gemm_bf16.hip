@@ -1,0 +1,463 @@
+// bf16 GEMMs of the SQA layer and the SQAT-m block on gfx950, with fused
+// epilogues (SQAT-m model card, "Architecture details": RoPE, RMS Norm,
+// SwiGLU feed forward; "Model size difference": H_q*d-wide query and output
+// projections, H_kv*d-wide key and value projections).
+//
+//   C [M, n-range] = A [M, K] . W [K, n-range],  A row-major (or the
+//   attention output O [B, Hq, N, d] read as O_flat [B*N, Hq*d]), W [K, Ncols]
+//   row-major, fp32 accumulation (v_mfma_f32_32x32x16_bf16).
+//
+// Formulation: C^T = W^T A^T, so that W^T is the MFMA A operand read with
+// ds_read_b64_tr_b16 from W stored row-major in LDS, and A^T the B operand
+// read as 16-byte row chunks -- the layouts of bf16_tiles.h. Each lane then
+// owns one output row and runs of 4 consecutive columns, so RoPE partners
+// (c and c +- d/2), SwiGLU's gate and up, and the residual all meet in
+// registers.
+//
+// Tiling: the output columns are cut into 64-wide segments of the weight
+// parts (W_q | W_k | W_v for the QKV projection, one matrix otherwise); a
+// 4-wave workgroup computes 128 rows x two segments (SwiGLU: one segment of
+// both gate and up), and wave (wm, wn) owns 64 rows of segment wn as four
+// 32x32 accumulators. The reduction runs in 64-wide chunks, DMA'd HBM -> LDS
+// with buffer_load ... lds into two alternating stages; rows past M, columns
+// past the part's width and reduction indices past K are zero-filled by the
+// descriptor's range check (their lanes get an out-of-range offset).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "bf16_tiles.h"
+#include "kernels.h"
+
+namespace sqa {
+namespace {
+
+using namespace tiles;
+
+constexpr int kThreads = 256;
+constexpr int TM = 128;                      // rows per workgroup
+constexpr int TK = 64;                       // reduction chunk
+constexpr int kATiles = TM / kTileRows;      // 4 row tiles of [32 m][64 k]
+constexpr int kStageBytes = 8 * kTileBytes;  // A 16 KB | W 16 KB (4 tiles of [32 k][64 n])
+constexpr uint32_t kOOB = 0x80000000u;       // an offset past every descriptor range
+
+enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_QKV = 2 };
+
+// Where the reduction operand rows come from.
+struct ARows {
+  const uint16_t* p;
+  int64_t M, K;
+  int gather;      // 1: O [B, Hq, N, d] read as O_flat
+  int64_t N, Hq, d;
+};
+
+// One weight part: a [K, ncols] row-major matrix.
+struct WPart {
+  const uint16_t* w;
+  int64_t ncols;
+};
+
+struct GemmArgs {
+  ARows A;
+  WPart part[3];      // QKV: W_q, W_k, W_v; SwiGLU: gate, up; store: one
+  int nparts;
+  int segs[3];        // 64-column segments of each part
+  int segs_total;     // sum of segs
+  int tiles_total;    // column tiles: ceil(segs_total / 2) (SwiGLU: segs[0])
+  int epi;
+  // store epilogue
+  const uint16_t* resid;  // [M, ncols] or nullptr
+  uint16_t* y;            // [M, ncols] (SwiGLU: h [M, F])
+  // QKV epilogue
+  uint16_t* qkv[3];       // Q [B,Hq,N,d], K/V [B,Hkv,N,d]
+  const float* rope_cs;   // [N, d/2] (cos, sin)
+  int64_t Nseq, Hq, Hkv, d;
+};
+
+// Byte offset of A[m][k .. k+8) for a DMA lane (kOOB when outside).
+__device__ __forceinline__ uint32_t a_offset(const ARows& A, int64_t m, int64_t k) {
+  if (m >= A.M || k >= A.K) return kOOB;
+  if (!A.gather) return (uint32_t)((m * A.K + k) * 2);
+  const int64_t b = m / A.N, t = m % A.N;
+  const int64_t h = k / A.d, c = k % A.d;
+  return (uint32_t)((((b * A.Hq + h) * A.N + t) * A.d + c) * 2);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int nrec = (int)min(bytes, (int64_t)0x7fffffff);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kBufferWord3);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lg = lane >> 5, l32 = lane & 31;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // workgroup -> (row tile, column tile); W tile c (c = 0, 1) holds segment
+  // 2*ct + c: (part, first column). SwiGLU: gate and up at column ct*64.
+  const int mt = blockIdx.x / a.tiles_total;
+  const int ct = blockIdx.x % a.tiles_total;
+  const int64_t m0 = (int64_t)mt * TM;
+  const ARows& A = a.A;
+  const int64_t K = A.K;
+  int sp0, sp1;          // part of W tile 0 / 1
+  int64_t wc0, wc1;      // first column of W tile 0 / 1 within its part
+  if (EPI == EPI_SWIGLU) {
+    sp0 = 0;
+    sp1 = 1;
+    wc0 = wc1 = (int64_t)ct * 64;
+  } else {
+    auto seg = [&](int g, int& pt, int64_t& col) {
+      pt = 0;
+      while (pt < a.nparts - 1 && g >= a.segs[pt]) g -= a.segs[pt++];
+      col = (int64_t)g * 64;  // past the part's width when g >= segs[pt]: all masked
+    };
+    seg(2 * ct, sp0, wc0);
+    seg(2 * ct + 1, sp1, wc1);
+  }
+
+  // descriptors: A (whole operand; gathered offsets may go anywhere in O) and
+  // the parts that feed the two W tiles
+  const __amdgpu_buffer_rsrc_t ra = rsrc(A.p, A.M * A.K * 2);  // O has the size of O_flat
+  const WPart wp0 = a.part[sp0];
+  const WPart wp1 = a.part[sp1];
+  const __amdgpu_buffer_rsrc_t rw0 = rsrc(wp0.w, K * wp0.ncols * 2);
+  const __amdgpu_buffer_rsrc_t rw1 = rsrc(wp1.w, K * wp1.ncols * 2);
+
+  // This wave DMAs 8 row-parts of 8 rows: parts 2*wave, 2*wave+1 of the A
+  // tiles (16 parts) and of the W tiles (16 parts).
+  const int r8 = lane >> 3, s = lane & 7;
+
+  auto issue = [&](uint8_t* stage, int64_t k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // A: tile t = (4*wave + j) / 4 ... parts p = 4*wave + j (0..15)
+      const int p = wave * 4 + j;
+      const int t = p >> 2, q = p & 3;
+      const int r = q * 8 + r8;                       // row within the 32-row tile
+      const int64_t m = m0 + t * kTileRows + r;
+      const int64_t k = k0 + 8 * (s ^ swz_k(r));
+      const uint32_t off = a_offset(A, m, k);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(stage + t * kTileBytes + q * 1024), 16, off, 0,
+                                               0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // W: tile (kh, c) = parts p = 4*wave + j; tile index wt = p >> 2 = 2*kh + c
+      const int p = wave * 4 + j;
+      const int wt = p >> 2, q = p & 3;
+      const int kh = wt >> 1, c = wt & 1;
+      const int r = q * 8 + r8;                       // k row within the 32-row tile
+      const int64_t k = k0 + kh * kTileRows + r;
+      const WPart& w = c ? wp1 : wp0;
+      const int64_t col = (c ? wc1 : wc0) + 8 * (s ^ swz_v(r));
+      const uint32_t off = (k < K && col < w.ncols) ? (uint32_t)((k * w.ncols + col) * 2) : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c ? rw1 : rw0,
+                                               (lds_void_t*)(stage + (kATiles + wt) * kTileBytes + q * 1024), 16,
+                                               off, 0, 0, 0);
+    }
+  };
+
+  // read offsets: A^T fragments (B operand) for k step (kh, hh): row l32,
+  // logical chunk kh*4 + lg*2 + hh
+  uint32_t boff[2][2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      boff[kh][hh] = (uint32_t)(l32 * kRowBytes + (((kh * 4 + lg * 2 + hh) ^ swz_k(l32)) * 16));
+  const ReadOffsets ro = read_offsets(lane);
+  // W tile and transposed-read offset feeding accumulator slot x of this
+  // wave: SwiGLU -- gate (tile 0) and up (tile 1) at columns ct*64 + wn*32;
+  // otherwise both 32-column halves of W tile wn
+  const int wtile0 = (EPI == EPI_SWIGLU) ? 0 : wn;
+  const int wtile1 = (EPI == EPI_SWIGLU) ? 1 : wn;
+  const uint32_t toff0 = (EPI == EPI_SWIGLU) ? (wn ? ro.tr[1] : ro.tr[0]) : ro.tr[0];
+  const uint32_t toff1 = (EPI == EPI_SWIGLU) ? (wn ? ro.tr[1] : ro.tr[0]) : ro.tr[1];
+
+  f32x16_t acc[2][2];  // [slot x][row block mb]
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) acc[x][mb] = zero16();
+
+  // One reduction chunk from stage CUR while chunk kc+1 streams into NXT.
+  // The stages are separate LDS objects and the loop is unrolled by two, so
+  // the compiler can tell the reads of one from the DMA into the other.
+  auto chunk = [&](const uint8_t* cur, uint8_t* nxt, int kc, int nk) {
+    // chunk kc landed; every wave is done with chunk kc-1 (the other stage)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kc + 1 < nk) issue(nxt, (int64_t)(kc + 1) * TK);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      u32x4_t wf[2][2];  // [slot][hh]
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const uint8_t* tile = cur + (kATiles + kh * 2 + (x ? wtile1 : wtile0)) * kTileBytes;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint8_t* p = tile + (x ? toff1 : toff0) + hh * 8 * kRowBytes;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * kRowBytes));
+          const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+          wf[x][hh] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const uint8_t* at = cur + (wm * 2 + mb) * kTileBytes;
+          const u32x4_t af = *reinterpret_cast<const u32x4_t*>(at + boff[kh][hh]);
+#pragma unroll
+          for (int x = 0; x < 2; ++x) acc[x][mb] = mfma(wf[x][hh], af, acc[x][mb]);
+        }
+      }
+    }
+  };
+
+  const int nk = (int)((K + TK - 1) / TK);
+  issue(st0, 0);
+  for (int kc = 0; kc < nk; kc += 2) {
+    chunk(st0, st1, kc, nk);
+    if (kc + 1 < nk) chunk(st1, st0, kc + 1, nk);
+  }
+
+  // ---------------- epilogues. Entry i of acc[x][mb] (lane l): row
+  // m0 + wm*64 + mb*32 + l32; column (within the slot's 32) 8*(i/4) + 4*lg + i%4.
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int64_t m = m0 + wm * 64 + mb * 32 + l32;
+    if (m >= A.M) continue;
+    if (EPI == EPI_SWIGLU) {
+      const int64_t F = a.part[0].ncols;
+#pragma unroll
+      for (int ab = 0; ab < 4; ++ab) {
+        const int64_t n = wc0 + wn * 32 + 8 * ab + 4 * lg;
+        if (n >= F) continue;
+        float h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float g = acc[0][mb][4 * ab + e], u = acc[1][mb][4 * ab + e];
+          h[e] = g / (1.0f + expf(-g)) * u;
+        }
+        u32x2_t wv;
+        wv[0] = pack_bf16x2(h[0], h[1]);
+        wv[1] = pack_bf16x2(h[2], h[3]);
+        *reinterpret_cast<u32x2_t*>(a.y + m * F + n) = wv;
+      }
+    } else if (EPI == EPI_STORE) {
+      const int64_t ncols = a.part[0].ncols;
+      const int64_t nb = wn ? wc1 : wc0;
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int ab = 0; ab < 4; ++ab) {
+          const int64_t n = nb + x * 32 + 8 * ab + 4 * lg;
+          if (n >= ncols) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[x][mb][4 * ab + e];
+          if (a.resid != nullptr) {
+            const u32x2_t rv = *reinterpret_cast<const u32x2_t*>(a.resid + m * ncols + n);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const uint32_t pr = rv[e];
+              v[2 * e] += __builtin_bit_cast(float, pr << 16);
+              v[2 * e + 1] += __builtin_bit_cast(float, pr & 0xffff0000u);
+            }
+          }
+          u32x2_t wv;
+          wv[0] = pack_bf16x2(v[0], v[1]);
+          wv[1] = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<u32x2_t*>(a.y + m * ncols + n) = wv;
+        }
+    } else {  // EPI_QKV: RoPE on Q and K (rotate-half pairs (c, c + d/2)), scatter to [B, H, N, d]
+      const int part = wn ? sp1 : sp0;
+      const int64_t nb = wn ? wc1 : wc0;
+      const int64_t ncols = a.part[part].ncols;
+      const int64_t d = a.d, half = d / 2;
+      const int64_t b = m / a.Nseq, t = m % a.Nseq;
+      const int64_t nheads = (part == 0) ? a.Hq : a.Hkv;
+      const bool rope = part < 2;
+      // (cos, sin) of pair indices kp = 8*ab + 4*lg + e (mod half) of row t:
+      // four consecutive pairs (32 bytes) per ab; for d = 16 one group serves all
+      float2 cs[4][4];
+      if (rope) {
+        const float* row = a.rope_cs + 2 * (t * half);
+#pragma unroll
+        for (int ab = 0; ab < 4; ++ab) {
+          if (d == 16 && ab > 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cs[ab][e] = cs[0][e];
+            continue;
+          }
+          const int64_t kb = (8 * ab + 4 * lg) % half;
+          const float4* p4 = reinterpret_cast<const float4*>(row + 2 * kb);
+          const float4 u = p4[0], w = p4[1];
+          cs[ab][0] = make_float2(u.x, u.y);
+          cs[ab][1] = make_float2(u.z, u.w);
+          cs[ab][2] = make_float2(w.x, w.y);
+          cs[ab][3] = make_float2(w.z, w.w);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int ab = 0; ab < 4; ++ab) {
+          const int64_t n = nb + x * 32 + 8 * ab + 4 * lg;
+          if (n >= ncols) continue;
+          const int64_t head = n / d, c0 = n % d;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float xv = acc[x][mb][4 * ab + e];
+            if (!rope) {
+              v[e] = xv;
+              continue;
+            }
+            // the partner column c0 + e -+ d/2 of the same head sits in this
+            // lane: d = 16 -> entry 4*(ab^1) + e of the same slot; d = 64 ->
+            // the same entry of the other slot
+            const float xp = (d == 16) ? acc[x][mb][4 * (ab ^ 1) + e] : acc[x ^ 1][mb][4 * ab + e];
+            const float2 c2 = cs[ab][e];
+            v[e] = (c0 + e < half) ? xv * c2.x - xp * c2.y : xp * c2.y + xv * c2.x;
+          }
+          u32x2_t wv;
+          wv[0] = pack_bf16x2(v[0], v[1]);
+          wv[1] = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<u32x2_t*>(a.qkv[part] + (((b * nheads + head) * a.Nseq + t) * d + c0)) = wv;
+        }
+    }
+  }
+}
+
+hipError_t launch(const GemmArgs& a, int epi, hipStream_t stream) {
+  const int64_t mtiles = (a.A.M + TM - 1) / TM;
+  const int64_t nblk = mtiles * a.tiles_total;
+  if (nblk > 0x7fffffff || nblk <= 0) return hipErrorInvalidValue;
+  if (epi == EPI_STORE)
+    hipLaunchKernelGGL(gemm_kernel<EPI_STORE>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
+  else if (epi == EPI_SWIGLU)
+    hipLaunchKernelGGL(gemm_kernel<EPI_SWIGLU>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(gemm_kernel<EPI_QKV>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+GemmArgs base_args() {
+  GemmArgs a{};
+  a.A.gather = 0;
+  a.A.N = 1;
+  a.A.Hq = 1;
+  a.A.d = 1;
+  return a;
+}
+
+// 32-bit DMA offsets: every byte a lane may address must fit in 2^31.
+bool fits(int64_t bytes) { return bytes > 0 && bytes < 0x7fffffffLL; }
+
+}  // namespace
+
+hipError_t launch_qkv_rope(const QkvProblem& p, hipStream_t stream) {
+  if (p.d != 16 && p.d != 64) return hipErrorInvalidValue;
+  if (p.Dm % 8 != 0) return hipErrorInvalidValue;
+  GemmArgs a = base_args();
+  a.A.p = static_cast<const uint16_t*>(p.x);
+  a.A.M = p.B * p.N;
+  a.A.K = p.Dm;
+  if (!fits(a.A.M * a.A.K * 2)) return hipErrorInvalidValue;
+  const void* w[3] = {p.wq, p.wk, p.wv};
+  const int64_t nc[3] = {p.Hq * p.d, p.Hkv * p.d, p.Hkv * p.d};
+  a.nparts = 3;
+  a.segs_total = 0;
+  for (int i = 0; i < 3; ++i) {
+    a.part[i].w = static_cast<const uint16_t*>(w[i]);
+    a.part[i].ncols = nc[i];
+    a.segs[i] = (int)((nc[i] + 63) / 64);
+    a.segs_total += a.segs[i];
+  }
+  a.tiles_total = (a.segs_total + 1) / 2;
+  a.epi = EPI_QKV;
+  a.qkv[0] = static_cast<uint16_t*>(p.q);
+  a.qkv[1] = static_cast<uint16_t*>(p.k);
+  a.qkv[2] = static_cast<uint16_t*>(p.v);
+  a.rope_cs = p.rope_cs;
+  a.Nseq = p.N;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.d = p.d;
+  return launch(a, EPI_QKV, stream);
+}
+
+hipError_t launch_out_proj(const OprojProblem& p, hipStream_t stream) {
+  if (p.d % 8 != 0 || p.Dm % 8 != 0) return hipErrorInvalidValue;
+  GemmArgs a = base_args();
+  a.A.p = static_cast<const uint16_t*>(p.o);
+  a.A.M = p.B * p.N;
+  a.A.K = p.Hq * p.d;
+  a.A.gather = 1;
+  a.A.N = p.N;
+  a.A.Hq = p.Hq;
+  a.A.d = p.d;
+  if (!fits(a.A.M * a.A.K * 2)) return hipErrorInvalidValue;
+  a.nparts = 1;
+  a.part[0].w = static_cast<const uint16_t*>(p.wo);
+  a.part[0].ncols = p.Dm;
+  a.segs[0] = (int)((p.Dm + 63) / 64);
+  a.segs_total = a.segs[0];
+  a.tiles_total = (a.segs_total + 1) / 2;
+  a.epi = EPI_STORE;
+  a.resid = static_cast<const uint16_t*>(p.resid);
+  a.y = static_cast<uint16_t*>(p.y);
+  return launch(a, EPI_STORE, stream);
+}
+
+hipError_t launch_dense_residual(const DenseProblem& p, hipStream_t stream) {
+  if (p.K % 8 != 0 || p.Ncols % 8 != 0) return hipErrorInvalidValue;
+  GemmArgs a = base_args();
+  a.A.p = static_cast<const uint16_t*>(p.a);
+  a.A.M = p.M;
+  a.A.K = p.K;
+  if (!fits(a.A.M * a.A.K * 2)) return hipErrorInvalidValue;
+  a.nparts = 1;
+  a.part[0].w = static_cast<const uint16_t*>(p.w);
+  a.part[0].ncols = p.Ncols;
+  a.segs[0] = (int)((p.Ncols + 63) / 64);
+  a.segs_total = a.segs[0];
+  a.tiles_total = (a.segs_total + 1) / 2;
+  a.epi = EPI_STORE;
+  a.resid = static_cast<const uint16_t*>(p.resid);
+  a.y = static_cast<uint16_t*>(p.y);
+  return launch(a, EPI_STORE, stream);
+}
+
+hipError_t launch_gate_up(const GateUpProblem& p, hipStream_t stream) {
+  if (p.K % 8 != 0 || p.F % 8 != 0) return hipErrorInvalidValue;
+  GemmArgs a = base_args();
+  a.A.p = static_cast<const uint16_t*>(p.z);
+  a.A.M = p.M;
+  a.A.K = p.K;
+  if (!fits(a.A.M * a.A.K * 2)) return hipErrorInvalidValue;
+  a.nparts = 2;
+  a.part[0].w = static_cast<const uint16_t*>(p.w_gate);
+  a.part[0].ncols = p.F;
+  a.part[1].w = static_cast<const uint16_t*>(p.w_up);
+  a.part[1].ncols = p.F;
+  a.segs[0] = a.segs[1] = (int)((p.F + 63) / 64);
+  a.segs_total = a.segs[0];
+  a.tiles_total = a.segs[0];
+  a.epi = EPI_SWIGLU;
+  a.y = static_cast<uint16_t*>(p.h);
+  return launch(a, EPI_SWIGLU, stream);
+}
+
+}  // namespace sqa
