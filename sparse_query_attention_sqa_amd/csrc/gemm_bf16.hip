@@ -19,9 +19,13 @@
 // 4-wave workgroup computes 128 rows x two segments (SwiGLU: one segment of
 // both gate and up), and wave (wm, wn) owns 64 rows of segment wn as four
 // 32x32 accumulators. The reduction runs in 64-wide chunks, DMA'd HBM -> LDS
-// with buffer_load ... lds into two alternating stages; rows past M, columns
-// past the part's width and reduction indices past K are zero-filled by the
-// descriptor's range check (their lanes get an out-of-range offset).
+// with buffer_load ... lds into a ring of S stages with S-1 chunks in
+// flight (S = 4 for small grids, where one workgroup per CU would otherwise
+// wait out one HBM round trip per chunk; S = 2 otherwise); rows past M,
+// columns past the part's width and reduction indices past K -- including
+// whole chunks past the end, so every step issues the same DMAs and the
+// waits are exact -- are zero-filled by the descriptor's range check (their
+// lanes get an out-of-range offset).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -74,13 +78,37 @@ struct GemmArgs {
   int64_t Nseq, Hq, Hkv, d;
 };
 
-// Byte offset of A[m][k .. k+8) for a DMA lane (kOOB when outside).
-__device__ __forceinline__ uint32_t a_offset(const ARows& A, int64_t m, int64_t k) {
-  if (m >= A.M || k >= A.K) return kOOB;
-  if (!A.gather) return (uint32_t)((m * A.K + k) * 2);
-  const int64_t b = m / A.N, t = m % A.N;
-  const int64_t h = k / A.d, c = k % A.d;
-  return (uint32_t)((((b * A.Hq + h) * A.N + t) * A.d + c) * 2);
+// Row part of the byte offset of A[m][k] for a DMA lane, fixed across the
+// reduction (element units): row-major m*K, gathered ((b*Hq)*N + t)*d. All
+// offsets fit in 32 bits (checked at launch); d is a power of two.
+template <bool GATHER>
+__device__ __forceinline__ uint32_t a_row_base(const ARows& A, uint32_t m) {
+  if (!GATHER) return m * (uint32_t)A.K;
+  const uint32_t n = (uint32_t)A.N;
+  const uint32_t b = m / n, t = m - b * n;
+  return ((b * (uint32_t)A.Hq) * n + t) * (uint32_t)A.d;
+}
+
+// Byte offset of A[m][k .. k+8) given the row base (kOOB when outside);
+// branch-free so that the per-lane conditions become selects.
+template <bool GATHER>
+__device__ __forceinline__ uint32_t a_offset(const ARows& A, uint32_t base, bool row_ok, uint32_t k,
+                                             uint32_t dshift) {
+  uint32_t e;
+  if constexpr (GATHER) {
+    const uint32_t h = k >> dshift, c = k & ((1u << dshift) - 1u);
+    e = base + ((h * (uint32_t)A.N) << dshift) + c;
+  } else {
+    e = base + k;
+  }
+  return (row_ok && k < (uint32_t)A.K) ? e * 2u : kOOB;
+}
+
+// silu(g) * u with the hardware exp2 and reciprocal (about 1 ulp each):
+// g / (1 + e^-g) = g * rcp(1 + 2^(-g log2 e)); saturates to 0 and to g.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * g);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
@@ -88,10 +116,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kBufferWord3);
 }
 
-template <int EPI>
+constexpr int kDmaPerChunk = 8;  // DMA instructions per wave per chunk
+
+template <int EPI, int S, bool GATHER>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
+  static_assert(S >= 2 && S <= 4, "2 to 4 stages");
   __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[S > 2 ? kStageBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[S > 3 ? kStageBytes : 16];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -129,36 +162,49 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t rw0 = rsrc(wp0.w, K * wp0.ncols * 2);
   const __amdgpu_buffer_rsrc_t rw1 = rsrc(wp1.w, K * wp1.ncols * 2);
 
-  // This wave DMAs 8 row-parts of 8 rows: parts 2*wave, 2*wave+1 of the A
-  // tiles (16 parts) and of the W tiles (16 parts).
+  // This wave DMAs A tile `wave` (4 parts of 8 rows) and W tile `wave`
+  // (kh = wave / 2, c = wave % 2; 4 parts of 8 k-rows). Per-lane row terms
+  // are fixed across the reduction and computed once here.
   const int r8 = lane >> 3, s = lane & 7;
+  const uint32_t dshift = GATHER ? (uint32_t)__builtin_ctzll((unsigned long long)A.d) : 0u;
+  uint32_t a_base[4], a_k[4];
+  bool a_ok[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = q * 8 + r8;                         // row within the 32-row tile
+    const int64_t m = m0 + wave * kTileRows + r;
+    a_ok[q] = m < A.M;
+    a_base[q] = a_ok[q] ? a_row_base<GATHER>(A, (uint32_t)m) : 0u;
+    a_k[q] = 8u * (uint32_t)(s ^ swz_k(r));
+  }
+  const int wkh = wave >> 1, wc = wave & 1;
+  const WPart wq = wc ? wp1 : wp0;
+  const uint32_t wncols = (uint32_t)wq.ncols;
+  uint32_t w_col[4], w_r[4];
+  bool w_ok[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = q * 8 + r8;                         // k row within the 32-row tile
+    const int64_t col = (wc ? wc1 : wc0) + 8 * (s ^ swz_v(r));
+    w_ok[q] = col < wq.ncols;
+    w_col[q] = (uint32_t)col;
+    w_r[q] = (uint32_t)(wkh * kTileRows + r);
+  }
 
   auto issue = [&](uint8_t* stage, int64_t k0) {
+    const uint32_t k32 = (uint32_t)k0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // A: tile t = (4*wave + j) / 4 ... parts p = 4*wave + j (0..15)
-      const int p = wave * 4 + j;
-      const int t = p >> 2, q = p & 3;
-      const int r = q * 8 + r8;                       // row within the 32-row tile
-      const int64_t m = m0 + t * kTileRows + r;
-      const int64_t k = k0 + 8 * (s ^ swz_k(r));
-      const uint32_t off = a_offset(A, m, k);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(stage + t * kTileBytes + q * 1024), 16, off, 0,
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t off = a_offset<GATHER>(A, a_base[q], a_ok[q], k32 + a_k[q], dshift);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(stage + wave * kTileBytes + q * 1024), 16, off, 0,
                                                0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // W: tile (kh, c) = parts p = 4*wave + j; tile index wt = p >> 2 = 2*kh + c
-      const int p = wave * 4 + j;
-      const int wt = p >> 2, q = p & 3;
-      const int kh = wt >> 1, c = wt & 1;
-      const int r = q * 8 + r8;                       // k row within the 32-row tile
-      const int64_t k = k0 + kh * kTileRows + r;
-      const WPart& w = c ? wp1 : wp0;
-      const int64_t col = (c ? wc1 : wc0) + 8 * (s ^ swz_v(r));
-      const uint32_t off = (k < K && col < w.ncols) ? (uint32_t)((k * w.ncols + col) * 2) : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(c ? rw1 : rw0,
-                                               (lds_void_t*)(stage + (kATiles + wt) * kTileBytes + q * 1024), 16,
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t k = k32 + w_r[q];
+      const uint32_t off = (w_ok[q] && k < (uint32_t)K) ? (k * wncols + w_col[q]) * 2u : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wc ? rw1 : rw0,
+                                               (lds_void_t*)(stage + (kATiles + wave) * kTileBytes + q * 1024), 16,
                                                off, 0, 0, 0);
     }
   };
@@ -186,16 +232,20 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) acc[x][mb] = zero16();
 
-  // One reduction chunk from stage CUR while chunk kc+1 streams into NXT.
-  // The stages are separate LDS objects and the loop is unrolled by two, so
-  // the compiler can tell the reads of one from the DMA into the other.
-  auto chunk = [&](const uint8_t* cur, uint8_t* nxt, int kc, int nk) {
-    // chunk kc landed; every wave is done with chunk kc-1 (the other stage)
+  // One reduction chunk from stage CUR while chunk kc+S-1 streams into the
+  // stage freed by chunk kc-1. The stages are separate LDS objects and the
+  // loop is unrolled by S, so the compiler can tell the reads of one stage
+  // from the DMA into another.
+  auto chunk = [&](const uint8_t* cur, uint8_t* ahead, int kc) {
+    // chunk kc landed (later ones may not have); every wave is done with
+    // chunk kc-1, whose stage receives chunk kc+S-1
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    if constexpr (S == 2) __builtin_amdgcn_s_waitcnt(0x0070);           // vmcnt(0) lgkmcnt(0)
+    else if constexpr (S == 3) __builtin_amdgcn_s_waitcnt(0x0078);      // vmcnt(8) lgkmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0x4070);                            // vmcnt(16) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kc + 1 < nk) issue(nxt, (int64_t)(kc + 1) * TK);
+    issue(ahead, (int64_t)(kc + S - 1) * TK);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       u32x4_t wf[2][2];  // [slot][hh]
@@ -224,12 +274,20 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
     }
   };
 
+  uint8_t* stg[4] = {st0, st1, st2, st3};
   const int nk = (int)((K + TK - 1) / TK);
-  issue(st0, 0);
-  for (int kc = 0; kc < nk; kc += 2) {
-    chunk(st0, st1, kc, nk);
-    if (kc + 1 < nk) chunk(st1, st0, kc + 1, nk);
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j) issue(stg[j], (int64_t)j * TK);
+  int kc = 0;
+  for (; kc + S <= nk; kc += S) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) chunk(stg[j], stg[(j + S - 1) % S], kc + j);
   }
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j)
+    if (kc + j < nk) chunk(stg[j], stg[(j + S - 1) % S], kc + j);
+  // drain the zero-filling DMAs still in flight before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0x0070);
 
   // ---------------- epilogues. Entry i of acc[x][mb] (lane l): row
   // m0 + wm*64 + mb*32 + l32; column (within the slot's 32) 8*(i/4) + 4*lg + i%4.
@@ -245,10 +303,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
         if (n >= F) continue;
         float h[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float g = acc[0][mb][4 * ab + e], u = acc[1][mb][4 * ab + e];
-          h[e] = g / (1.0f + expf(-g)) * u;
-        }
+        for (int e = 0; e < 4; ++e) h[e] = silu_mul(acc[0][mb][4 * ab + e], acc[1][mb][4 * ab + e]);
         u32x2_t wv;
         wv[0] = pack_bf16x2(h[0], h[1]);
         wv[1] = pack_bf16x2(h[2], h[3]);
@@ -285,8 +340,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
       const int64_t nb = wn ? wc1 : wc0;
       const int64_t ncols = a.part[part].ncols;
       const int64_t d = a.d, half = d / 2;
-      const int64_t b = m / a.Nseq, t = m % a.Nseq;
+      const uint32_t dsh = (d == 16) ? 4u : 6u;
+      const uint32_t ns = (uint32_t)a.Nseq;
+      const uint32_t b = (uint32_t)m / ns, t = (uint32_t)m - b * ns;
       const int64_t nheads = (part == 0) ? a.Hq : a.Hkv;
+      // element offset of (b, head 0, t, 0); a head adds N*d
+      uint16_t* dst_bt = a.qkv[part] + ((int64_t)b * nheads * ns + t) * d;
+      const uint32_t head_stride = ns * (uint32_t)d;
       const bool rope = part < 2;
       // (cos, sin) of pair indices kp = 8*ab + 4*lg + e (mod half) of row t:
       // four consecutive pairs (32 bytes) per ab; for d = 16 one group serves all
@@ -315,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
         for (int ab = 0; ab < 4; ++ab) {
           const int64_t n = nb + x * 32 + 8 * ab + 4 * lg;
           if (n >= ncols) continue;
-          const int64_t head = n / d, c0 = n % d;
+          const int64_t head = n >> dsh, c0 = n & (d - 1);
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -334,10 +394,21 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
           u32x2_t wv;
           wv[0] = pack_bf16x2(v[0], v[1]);
           wv[1] = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2_t*>(a.qkv[part] + (((b * nheads + head) * a.Nseq + t) * d + c0)) = wv;
+          *reinterpret_cast<u32x2_t*>(dst_bt + (uint32_t)head * head_stride + (uint32_t)c0) = wv;
         }
     }
   }
+}
+
+template <int EPI, bool GATHER>
+hipError_t launch_stages(const GemmArgs& a, int64_t nblk, hipStream_t stream) {
+  // few workgroups (about one per CU or less): keep every chunk of a short
+  // reduction in flight at once; otherwise two stages and two workgroups/CU
+  if (nblk <= 384)
+    hipLaunchKernelGGL((gemm_kernel<EPI, 4, GATHER>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<EPI, 2, GATHER>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch(const GemmArgs& a, int epi, hipStream_t stream) {
@@ -345,12 +416,10 @@ hipError_t launch(const GemmArgs& a, int epi, hipStream_t stream) {
   const int64_t nblk = mtiles * a.tiles_total;
   if (nblk > 0x7fffffff || nblk <= 0) return hipErrorInvalidValue;
   if (epi == EPI_STORE)
-    hipLaunchKernelGGL(gemm_kernel<EPI_STORE>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
-  else if (epi == EPI_SWIGLU)
-    hipLaunchKernelGGL(gemm_kernel<EPI_SWIGLU>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(gemm_kernel<EPI_QKV>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+    return a.A.gather ? launch_stages<EPI_STORE, true>(a, nblk, stream)
+                      : launch_stages<EPI_STORE, false>(a, nblk, stream);
+  if (epi == EPI_SWIGLU) return launch_stages<EPI_SWIGLU, false>(a, nblk, stream);
+  return launch_stages<EPI_QKV, false>(a, nblk, stream);
 }
 
 GemmArgs base_args() {
@@ -399,7 +468,7 @@ hipError_t launch_qkv_rope(const QkvProblem& p, hipStream_t stream) {
 }
 
 hipError_t launch_out_proj(const OprojProblem& p, hipStream_t stream) {
-  if (p.d % 8 != 0 || p.Dm % 8 != 0) return hipErrorInvalidValue;
+  if (p.d < 8 || (p.d & (p.d - 1)) != 0 || p.Dm % 8 != 0) return hipErrorInvalidValue;  // d a power of two
   GemmArgs a = base_args();
   a.A.p = static_cast<const uint16_t*>(p.o);
   a.A.M = p.B * p.N;
