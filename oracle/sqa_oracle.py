@@ -37,6 +37,11 @@ What is computed, and where it comes from
       h = x + layer(rms_norm(x, g1)),  y = h + swiglu(rms_norm(h, g2))
   with rms_norm(x, g) = x / sqrt(mean_c x_c^2 + eps) * g and
   swiglu(z) = (silu(z W_gate) * (z W_up)) W_down, silu(u) = u / (1 + e^-u).
+* Packed variable-length batches (not on the pages; the plainest reading of
+  a batch of sequences of different lengths): sequences b = 0..B-1 are
+  concatenated along the token axis, sequence b owning tokens
+  cu[b] .. cu[b+1]-1; each attends only within itself, with positions
+  restarting at 0 for the causal mask. Layout [heads, T, d].
 * The layer (SQAT-m, "Architecture details" and "Model size difference"):
   Q = X W_Q (H_q*d wide), K = X W_K and V = X W_V (H_kv*d wide), RoPE on Q and
   K, SQA, then Y = O_flat W_O with W_O of H_q*d rows. Weights are [in, out].
@@ -62,6 +67,7 @@ __all__ = [
     "kv_head_index",
     "attention",
     "attention_bwd",
+    "attention_varlen",
     "rope",
     "layer",
     "layer_weight_shapes",
@@ -179,6 +185,40 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: Optional[float
         else:
             with ThreadPoolExecutor(max_workers=threads) as ex:
                 list(ex.map(run, tasks))
+    return (out, lse) if return_lse else out
+
+
+def attention_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens: Sequence[int],
+                     scale: Optional[float] = None, causal: bool = False, return_lse: bool = False,
+                     threads: int = 1):
+    """SQA forward over packed variable-length sequences, float64.
+
+    q: [H_q, T, d]; k, v: [H_kv, T, d]; cu_seqlens: B+1 non-decreasing token
+    offsets with cu[0] = 0 and cu[B] = T. Sequence b is tokens
+    cu[b] .. cu[b+1]-1 of every head; it attends only to its own keys, and its
+    causal positions count from 0. Each sequence is the dense ``attention``
+    above on its slice. Returns O [H_q, T, d] (and LSE [H_q, T]).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    if q.ndim != 3 or k.ndim != 3 or v.ndim != 3:
+        raise ValueError("expected 3-D [heads, T, d] arrays")
+    H_q, T, d = q.shape
+    if k.shape[1:] != (T, d) or v.shape != k.shape:
+        raise ValueError("q/k/v shapes disagree")
+    cu = [int(x) for x in cu_seqlens]
+    if len(cu) < 1 or cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must rise from 0 to T")
+    out = np.zeros((H_q, T, d), dtype=np.float64)
+    lse = np.zeros((H_q, T), dtype=np.float64)
+    for a, b in zip(cu, cu[1:]):
+        if b == a:
+            continue
+        o, ls = attention(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], scale=scale, causal=causal,
+                          return_lse=True, threads=threads)
+        out[:, a:b] = o[0]
+        lse[:, a:b] = ls[0]
     return (out, lse) if return_lse else out
 
 

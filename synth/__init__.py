@@ -41,6 +41,8 @@ __all__ = [
     "boundary_rows",
     "draw_layer",
     "draw_attn_case",
+    "draw_varlen",
+    "varlen_lengths",
 ]
 
 
@@ -217,6 +219,34 @@ def draw_block(B: int, N: int, D: int, H: int, H_q: int, H_kv: int, F: int, seed
     n2 = gain()
     wg, wu, wd = mat(D, F), mat(D, F), mat(F, D)
     return x, n1, wq, wk, wv, wo, n2, wg, wu, wd
+
+
+def varlen_lengths(total: int, count: int, seed: int = 3, min_len: int = 1) -> np.ndarray:
+    """A length mix of ``count`` sequences summing to ``total`` tokens: cut
+    points drawn uniformly without replacement (``default_rng(seed)``), so
+    lengths range from a few tokens to several times the mean."""
+    if count < 1 or total < count * min_len:
+        raise ValueError("need total >= count * min_len")
+    rng = np.random.default_rng(seed)
+    spare = total - count * min_len
+    cuts = np.sort(rng.choice(spare + count - 1, size=count - 1, replace=False))
+    parts = np.diff(np.concatenate([[-1], cuts, [spare + count - 1]])) - 1
+    return (parts + min_len).astype(np.int64)
+
+
+def draw_varlen(lens, H_q: int, H_kv: int, d: int, dtype: str = "bf16", seed: int = 0):
+    """Packed variable-length batch: the sequences of lengths ``lens`` are
+    concatenated along the token axis. Returns Q [H_q, T, d], K/V [H_kv, T, d]
+    ~ N(0, 1) (bf16-representable for "bf16"; draw order Q, K, V) and the
+    offsets cu_seqlens [B+1] (int32, cu[0] = 0, cu[B] = T)."""
+    lens = [int(x) for x in lens]
+    T = int(sum(lens))
+    rng = np.random.default_rng(seed)
+    q = _normal(rng, (H_q, T, d), dtype)
+    k = _normal(rng, (H_kv, T, d), dtype)
+    v = _normal(rng, (H_kv, T, d), dtype)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return q, k, v, cu
 
 
 def draw_attn_case(B: int, H_q: int, H_kv: int, N: int, d: int, dtype: str = "bf16",
