@@ -276,6 +276,58 @@ def bench_f32(sqa, torch, w, args):
         "cpu_baseline": None, "comparison": None})
 
 
+def bench_varlen(sqa, torch, w, args):
+    """Packed batch of sequences of mixed lengths (sqa_attn_fwd_varlen); FLOPs
+    are the sum over sequences of 4*len^2*H_q*d (halved for causal)."""
+    import numpy as np
+
+    from synth import draw_varlen, varlen_lengths
+    variant = tuple(int(x) for x in args.variant.split(",")) if args.variant else w.variants[0]
+    causal = w.causal[0] if args.causal is None else args.causal
+    lens = varlen_lengths(w.N, w.varlen)
+    q_all, k_all, v_all, cu = draw_varlen(lens, w.H, w.H, w.d, "bf16", seed=0)
+    tcu = torch.from_numpy(cu).to("cuda")
+    maxlen = int(lens.max())
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch.bfloat16).contiguous()
+
+    def flops(hq):
+        f = float(np.sum(4.0 * lens.astype(np.float64) ** 2)) * hq * w.d
+        return f / 2 if causal else f
+
+    def run(var):
+        hq, hkv = var
+        q, k, v = dev(q_all[:hq]), dev(k_all[:hkv]), dev(v_all[:hkv])
+        out = torch.empty_like(q)
+        fn = lambda: sqa.sqa_attn_fwd_varlen(q, k, v, tcu, maxlen, scale=w.scale, causal=bool(causal), out=out)
+        ms = _timed(torch, fn, args.steps, args.warmup)
+        del q, k, v, out
+        torch.cuda.empty_cache()
+        return ms
+
+    ms = run(variant)
+    tflops = flops(variant[0]) / (ms * 1e-3) / 1e12
+    comparison = None
+    if not args.no_compare:
+        comparison = {}
+        for var in w.variants:
+            if var != variant:
+                cms = run(var)
+                comparison[f"{var[0]},{var[1]}"] = {"ms": round(cms, 4),
+                                                    "tflops": round(flops(var[0]) / (cms * 1e-3) / 1e12, 2)}
+        if "16,16" in comparison:
+            comparison["speedup_vs_mha"] = round(comparison["16,16"]["ms"] / ms, 3)
+    kernel = "attn_fwd_bf16_d64_kernel" if w.d == 64 else f"attn_fwd_bf16_kernel<{w.d}>"
+    return _common(args, ms, w, {
+        "value": round(tflops, 3), "unit": "TFLOP/s", "dtype": "bf16",
+        "tokens_per_s": round(w.N / (ms * 1e-3), 1),
+        "config": {"workload": w.name, "T": w.N, "sequences": lens.tolist(), "H": w.H,
+                   "H_q": variant[0], "H_kv": variant[1], "d": w.d, "causal": int(causal)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": kernel, "per_launch_flop": flops(variant[0])},
+        "cpu_baseline": None, "comparison": comparison})
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -334,6 +386,9 @@ def main():
     if w.dtype != "bf16":
         print(json.dumps(bench_f32(sqa, torch, w, args)), flush=True)
         return
+    if w.varlen:
+        print(json.dumps(bench_varlen(sqa, torch, w, args)), flush=True)
+        return
     variant = tuple(int(x) for x in args.variant.split(",")) if args.variant else w.variants[0]
     causal = w.causal[0] if args.causal is None else args.causal
     Hq, Hkv = variant
@@ -386,7 +441,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic,
-                "kernel": "attn_fwd_bf16_d64_kernel" if w.d == 64 else "attn_fwd_bf16_kernel<16>",
+                "kernel": "attn_fwd_bf16_d64_kernel" if w.d == 64 else f"attn_fwd_bf16_kernel<{w.d}>",
                 "per_launch_flop": flops}
 
     cpu = None

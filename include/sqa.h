@@ -39,7 +39,7 @@ extern "C" {
 typedef enum {
   SQA_OK = 0,
   SQA_ERR_NULL = 1,        /* a required pointer is NULL                         */
-  SQA_ERR_SHAPE = 2,       /* negative size, H_kv not in [1, H_q], H_q % H_kv != 0 */
+  SQA_ERR_SHAPE = 2,       /* negative size, H_kv not in [1, H_q], too large      */
   SQA_ERR_UNSUPPORTED = 3, /* valid but not implemented: d, dtype, ...            */
   SQA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                     */
   SQA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required              */
@@ -52,7 +52,10 @@ typedef enum { SQA_F32 = 0, SQA_BF16 = 1 } sqa_dtype;
 /*
  * sqa_attn_fwd -- SQA attention forward.
  *
- * For every b < B, query head i < H_q, position t < N, with j = i / (H_q/H_kv):
+ * For every b < B, query head i < H_q, position t < N, with
+ * j = floor(i * H_kv / H_q) (contiguous query-head groups, "GQA ..." page,
+ * "The idea"; groups differ in size by at most one head when H_kv does not
+ * divide H_q):
  *   s_tu      = scale * sum_c q[b,i,t,c] * k[b,j,u,c]          for u in U_t
  *   o[b,i,t,:] = sum_{u in U_t} softmax_u(s_tu) * v[b,j,u,:]
  *   lse[b,i,t] = log sum_{u in U_t} exp(s_tu)                   (natural log)
@@ -64,7 +67,7 @@ typedef enum { SQA_F32 = 0, SQA_BF16 = 1 } sqa_dtype;
  *   k, v [B, H_kv, N, d]  input,  dtype
  *   o    [B, H_q,  N, d]  output, dtype; must not overlap q, k or v
  *   lse  [B, H_q,  N]     optional output, fp32; NULL to skip
- *   d     16 or 64.  H_q % H_kv == 0 and 1 <= H_kv <= H_q.
+ *   d     16, 32, 64 or 128.  1 <= H_kv <= H_q.
  *   dtype SQA_BF16: bf16 in/out; scores, softmax state and the output
  *         accumulator are fp32, the probabilities are rounded to bf16 for the
  *         P.V product, the output is rounded to nearest-even bf16.
@@ -79,6 +82,33 @@ sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* o,
                         int dtype, float scale, int causal, float* lse, void* stream);
 
 /*
+ * sqa_attn_fwd_varlen -- sqa_attn_fwd over a packed batch of sequences of
+ * different lengths. The B sequences are concatenated along the token axis:
+ * sequence b owns tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head,
+ * attends only to its own keys, and its causal positions count from 0 (a
+ * batch of different-length sequences; the pages do not describe one, this
+ * is the plain reading). Per sequence the result equals sqa_attn_fwd with
+ * B = 1 on that sequence's rows.
+ *
+ *   q, o       [H_q,  T, d]  input / output, dtype; o must not overlap an input
+ *   k, v       [H_kv, T, d]  inputs, dtype
+ *   cu_seqlens [B + 1]       input, DEVICE int32 array: cu[0] = 0,
+ *                            non-decreasing, cu[B] = T, every length
+ *                            cu[b+1] - cu[b] <= max_seqlen. Not read by the
+ *                            host; offsets outside this contract give
+ *                            unspecified (but in-bounds) results.
+ *   lse        [H_q, T]      optional output, fp32 natural log; NULL to skip
+ *   max_seqlen the longest sequence (sizes the launch), <= T
+ *   d, dtype, scale, causal, head counts: as sqa_attn_fwd. Empty sequences
+ *   are allowed.
+ * Errors: as sqa_attn_fwd; cu_seqlens must be 4-byte aligned.
+ */
+sqa_status sqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                               const int32_t* cu_seqlens, int64_t B, int64_t H_q, int64_t H_kv,
+                               int64_t T, int64_t max_seqlen, int64_t d, int dtype, float scale,
+                               int causal, float* lse, void* stream);
+
+/*
  * sqa_attn_bwd_workspace_bytes -- bytes of device workspace sqa_attn_bwd
  * needs for these sizes: one fp32 pair (lse * log2(e), D_t) per query row,
  * with each (batch, query head)'s rows padded up to a multiple of 32, i.e.
@@ -91,7 +121,7 @@ size_t sqa_attn_bwd_workspace_bytes(int64_t B, int64_t H_q, int64_t N, int64_t d
  * sqa_attn_bwd -- gradients of sqa_attn_fwd for an upstream gradient dout
  * (the backward pass of training, where the SQA abstract places SQA's gains:
  * pre-training and fine-tuning). With P the forward's attention
- * probabilities (same scale and causal mask) and j = i / (H_q/H_kv):
+ * probabilities (same scale and causal mask) and j = floor(i * H_kv / H_q):
  *   D_t        = sum_c dout[b,i,t,c] * o[b,i,t,c]
  *   dS_tu      = P_tu * (sum_c dout[b,i,t,c] * v[b,j,u,c] - D_t)
  *   dq[b,i,t]  = scale * sum_u dS_tu * k[b,j,u]
@@ -147,8 +177,8 @@ size_t sqa_layer_workspace_bytes(int64_t B, int64_t N, int64_t D, int64_t H,
  *   workspace            device buffer of at least
  *                        sqa_layer_workspace_bytes(...) bytes, owned by the
  *                        caller; its contents on return are unspecified.
- *   D = 256 with d = 16 (the SQAT-m split) or D % 64 == 0 with d = 64;
- *   dtype must be SQA_BF16.
+ *   d = D / H must be 16 (the SQAT-m split) or 64, D a multiple of 16
+ *   (other head dims: SQA_ERR_UNSUPPORTED); dtype must be SQA_BF16.
  * Errors: as sqa_attn_fwd, plus SQA_ERR_WORKSPACE.
  */
 sqa_status sqa_layer_fwd(const void* x, const void* w_q, const void* w_k, const void* w_v,

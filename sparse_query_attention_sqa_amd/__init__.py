@@ -6,6 +6,8 @@ device memory and the current HIP stream. There is no fallback path: if the
 library is not built, importing the functions raises.
 
     sqa_attn_fwd(q, k, v, *, scale=None, causal=False, out=None, return_lse=False)
+    sqa_attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen=None, *, scale=None, causal=False,
+                        out=None, return_lse=False)
     sqa_attn_bwd(q, k, v, o, dout, lse, *, scale=None, causal=False, dq=None, dk=None,
                  dv=None, workspace=None)
     sqa_attn_bwd_workspace_bytes(B, H_q, N, d, dtype="bf16")
@@ -23,7 +25,7 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["SQAError", "lib_path", "load_library", "sqa_attn_fwd", "sqa_attn_bwd",
+__all__ = ["SQAError", "lib_path", "load_library", "sqa_attn_fwd", "sqa_attn_fwd_varlen", "sqa_attn_bwd",
            "sqa_attn_bwd_workspace_bytes", "sqa_layer_fwd", "sqa_block_fwd",
            "sqa_block_workspace_bytes",
            "sqa_layer_workspace_bytes", "sqa_status_str", "sqa_version",
@@ -62,6 +64,9 @@ def load_library() -> ctypes.CDLL:
     lib.sqa_attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, f32,
                                  ctypes.c_int, vp, vp]
     lib.sqa_attn_fwd.restype = ctypes.c_int
+    lib.sqa_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                        f32, ctypes.c_int, vp, vp]
+    lib.sqa_attn_fwd_varlen.restype = ctypes.c_int
     lib.sqa_attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.sqa_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.sqa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
@@ -133,8 +138,9 @@ def sqa_attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False
     """SQA attention forward on the GPU.
 
     q [B, H_q, N, d]; k, v [B, H_kv, N, d]; bf16 or fp32, contiguous, on the
-    same GPU. Query head i reads K/V head i // (H_q // H_kv). Returns
-    o [B, H_q, N, d] (and lse [B, H_q, N] fp32 if ``return_lse``).
+    same GPU; d in {16, 32, 64, 128}. Query head i reads K/V head
+    floor(i * H_kv / H_q). Returns o [B, H_q, N, d] (and lse [B, H_q, N] fp32
+    if ``return_lse``).
     """
     torch = _torch()
     lib = load_library()
@@ -159,6 +165,50 @@ def sqa_attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False
     st = lib.sqa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H_q, H_kv,
                           N, d, _dtype_code(q), float(scale), int(bool(causal)),
                           lse.data_ptr() if lse is not None else None, _stream_handle(q.device))
+    _check(st)
+    return (out, lse) if return_lse else out
+
+
+def sqa_attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: Optional[int] = None, *,
+                        scale: Optional[float] = None, causal: bool = False, out=None,
+                        return_lse: bool = False):
+    """SQA attention forward over a packed batch of variable-length sequences.
+
+    q [H_q, T, d]; k, v [H_kv, T, d] (bf16 or fp32); cu_seqlens: int32 GPU
+    tensor [B + 1] of token offsets (0, ..., T). Sequence b is tokens
+    cu[b] .. cu[b+1]-1 and attends only within itself. ``max_seqlen`` (the
+    longest sequence) sizes the launch; if None it is read from cu_seqlens,
+    which synchronises with the device. Returns o [H_q, T, d] (and lse
+    [H_q, T] fp32 if ``return_lse``).
+    """
+    torch = _torch()
+    lib = load_library()
+    _require_device(q, k, v, cu_seqlens)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("expected 3-D [H, T, d] tensors")
+    if k.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("k and v must match; q, k, v must share a dtype")
+    H_q, T, d = q.shape
+    if k.shape[1] != T or k.shape[2] != d:
+        raise ValueError("q and k/v shapes disagree")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of B + 1 offsets")
+    B = cu_seqlens.numel() - 1
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if B > 0 else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require_device(out)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    lse = torch.empty((H_q, T), dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib.sqa_attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 cu_seqlens.data_ptr(), B, H_q, k.shape[0], T, int(max_seqlen), d,
+                                 _dtype_code(q), float(scale), int(bool(causal)),
+                                 lse.data_ptr() if lse is not None else None, _stream_handle(q.device))
     _check(st)
     return (out, lse) if return_lse else out
 

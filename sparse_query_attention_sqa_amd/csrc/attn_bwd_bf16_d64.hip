@@ -35,6 +35,7 @@
 
 #include "bf16_tiles.h"
 #include "kernels.h"
+#include "seq_groups.h"
 
 namespace sqa {
 namespace {
@@ -101,10 +102,13 @@ __global__ __launch_bounds__(256) void bwd_rowterms_kernel(RowArgs a) {
 // Workgroup -> (b*H_kv + K/V head, index w_in within that head).
 // Encoder-style: consecutive logical workgroups on one XCD (they share the
 // streamed operand in L2). Causal: workgroups launch largest-work first,
-// which is ascending w_in, or descending with `reverse`.
-__device__ __forceinline__ void wg_coords(int causal, bool reverse, int nwg, int wg_per_bkv, int n_bkv,
-                                          int& bkv, int& w_in) {
-  if (!causal) {
+// which is ascending w_in, or descending with `reverse`. Uneven head groups
+// (`spread`): the spread_coords order, which deals every group over all XCDs.
+__device__ __forceinline__ void wg_coords(int spread, int causal, bool reverse, int nwg, int wg_per_bkv,
+                                          int n_bkv, int& bkv, int& w_in) {
+  if (spread) {
+    spread_coords(blockIdx.x, n_bkv, wg_per_bkv, causal && reverse, bkv, w_in);
+  } else if (!causal) {
     const int bid = blockIdx.x;
     const int per = nwg / kXcds, rem = nwg % kXcds;
     const int x = bid % kXcds, i = bid / kXcds;
@@ -133,7 +137,8 @@ struct KvArgs {
   const float2* rt;  // row terms, [B*H_q, Np]
   uint16_t* dk;
   uint16_t* dv;
-  int N, Np, Hq, Hkv, g, KB, NQT, wg_per_bkv, n_bkv, nwg;
+  int N, Np, Hq, Hkv, KB, NQT, wg_per_bkv, n_bkv, nwg;
+  int spread;  // uneven head groups: spread_coords order
   float c, scale;
   int causal;
 };
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lg = lane >> 5, l32 = lane & 31;
   int bkv, w_in;
-  wg_coords(a.causal, false, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
+  wg_coords(a.spread, a.causal, false, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
   const int N = a.N;
 
@@ -252,8 +257,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
   cx.rt = a.rt + (size_t)b * a.Hq * a.Np;
   cx.N = N;
   cx.Np = a.Np;
-  cx.g = a.g;
-  cx.h0 = kvh * a.g;
+  const HeadGroup hg = head_group(kvh, a.Hq, a.Hkv);
+  cx.g = hg.count;
+  cx.h0 = hg.first;
   cx.qt0 = a.causal ? w_in * kWaves : 0;  // the first query tile any key of this workgroup sees
   cx.kb = w_in * kWaves + wave;
   cx.causal = a.causal;
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
   cx.off_rows = dma_off_rows(wave, lane);
   cx.off_tr = dma_off_tr(wave, lane);
   cx.ro = read_offsets(lane);
-  const int nsteps = max(a.NQT - cx.qt0, 0) * a.g;
+  const int nsteps = max(a.NQT - cx.qt0, 0) * cx.g;
 
   KvState w;
   {
@@ -333,7 +339,8 @@ struct DqArgs {
   const uint16_t* dout;
   const float2* rt;  // row terms, [B*H_q, Np]
   uint16_t* dq;
-  int N, Np, Hq, Hkv, g, TB, NT, wg_per_bkv, n_bkv, nwg;
+  int N, Np, Hq, Hkv, TB, NT, wg_per_bkv, n_bkv, nwg;  // wg_per_bkv: for the largest group
+  int spread;  // uneven head groups: spread_coords order
   float c, scale;
   int causal;
 };
@@ -412,15 +419,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lg = lane >> 5, l32 = lane & 31;
   int bkv, w_in;
-  wg_coords(a.causal, true, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
+  wg_coords(a.spread, a.causal, true, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
   const int slot = w_in * kWaves + wave;
-  const int tb = slot / a.g, jh = slot % a.g;
+  const HeadGroup hg = head_group(kvh, a.Hq, a.Hkv);
+  const int g = hg.count;
+  if (w_in * kWaves >= a.TB * g) return;  // past this group's rows (whole workgroup)
+  const int tb = slot / g, jh = slot % g;
   const bool wave_valid = tb < a.TB;
-  const int h = kvh * a.g + jh;
+  const int h = hg.first + jh;
   const int N = a.N;
   // key tiles the workgroup streams, and the last one this wave uses
-  const int maxtb = min((w_in * kWaves + kWaves - 1) / a.g, a.TB - 1);
+  const int maxtb = min((w_in * kWaves + kWaves - 1) / g, a.TB - 1);
   const int nt = a.causal ? maxtb + 1 : a.NT;
 
   DqCtx cx;
@@ -532,7 +542,7 @@ hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream) {
     a.Np = Np;
     a.Hq = (int)p.Hq;
     a.Hkv = (int)p.Hkv;
-    a.g = (int)(p.Hq / p.Hkv);
+    a.spread = p.Hq % p.Hkv != 0 ? 1 : 0;
     a.KB = (N + kTileRows - 1) / kTileRows;
     a.NQT = a.KB;
     a.wg_per_bkv = (a.KB + kWaves - 1) / kWaves;
@@ -559,10 +569,10 @@ hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream) {
     a.Np = Np;
     a.Hq = (int)p.Hq;
     a.Hkv = (int)p.Hkv;
-    a.g = (int)(p.Hq / p.Hkv);
+    a.spread = p.Hq % p.Hkv != 0 ? 1 : 0;
     a.TB = (N + kTileRows - 1) / kTileRows;
     a.NT = a.TB;
-    const int64_t slots = (int64_t)a.TB * a.g;
+    const int64_t slots = (int64_t)a.TB * max_group(a.Hq, a.Hkv);
     a.wg_per_bkv = (int)((slots + kWaves - 1) / kWaves);
     a.n_bkv = (int)(p.B * p.Hkv);
     const int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;

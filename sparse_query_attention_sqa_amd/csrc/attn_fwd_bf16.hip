@@ -1,4 +1,5 @@
-// SQA attention forward, bf16 in/out, fp32 softmax state, for gfx950.
+// SQA attention forward, bf16 in/out, fp32 softmax state, for gfx950: the
+// kernel for head dims 16, 32 and 128 (64 has its own pipelined kernel).
 //
 // What is computed: per query head i and position t, softmax attention over
 // the keys of K/V head floor(i*H_kv/H_q) (contiguous query-head groups as in
@@ -10,9 +11,11 @@
 //   * A workgroup is 4 waves that share one (batch, K/V head). Each wave owns
 //     a "slot": 64 consecutive query positions of one query head of the
 //     group. Slots are ordered (position block, head-in-group), so the 4
-//     waves of a workgroup read the same K/V head -- for g = H_q/H_kv >= 2
-//     they are different query heads at the same positions, which is the
-//     reuse SQA/GQA grouping offers.
+//     waves of a workgroup read the same K/V head -- for groups of g >= 2
+//     heads they are different query heads at the same positions, which is
+//     the reuse SQA/GQA grouping offers. Group sizes may differ by one head
+//     and packed sequences by length; the grid covers the largest group and
+//     the longest sequence, and workgroups with no rows leave at once.
 //   * K/V are streamed in 64-key tiles, HBM -> registers -> LDS, double
 //     buffered with one barrier per tile; each tile is read from HBM once per
 //     workgroup and consumed by 4 x 64 = 256 query rows.
@@ -41,6 +44,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "seq_groups.h"
 
 namespace sqa {
 namespace {
@@ -61,7 +65,8 @@ constexpr int kXcds = 8;
 
 template <int D>
 struct Cfg {
-  static_assert(D == 16 || D == 64, "head dim");
+  static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head dim");
+  static constexpr int MINB = D >= 128 ? 1 : 2;    // workgroups per CU the registers allow
   static constexpr int DSTEPS = D / 16;            // MFMA k-steps over d for S^T
   static constexpr int DSUB = (D + 31) / 32;       // 32-row O^T tiles over d
   static constexpr int KROW = D + 8;               // LDS pitch of a K row (bf16)
@@ -73,6 +78,7 @@ struct Cfg {
   static constexpr int KCHUNKS = kTileKeys * D / 8;          // 16-byte chunks per K tile
   static constexpr int KLOADS = (KCHUNKS + kThreads - 1) / kThreads;
   static constexpr int VBLOCKS = (kTileKeys / 4) * (D / 4);  // 4x4 blocks per V tile
+  static constexpr int VLOADS = (VBLOCKS + kThreads - 1) / kThreads;
 };
 
 struct Args {
@@ -81,11 +87,14 @@ struct Args {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
-  int N, Hq, Hkv, g;
-  int TB;          // ceil(N / 64): query position blocks per head
-  int wg_per_bkv;  // workgroups per (batch, K/V head)
+  const int* cu;   // packed sequence offsets (nullptr: dense)
+  int64_t T;       // packed: total tokens
+  int N, Hq, Hkv;  // N: the (longest) sequence length
+  int wg_per_bkv;  // workgroups per (batch, K/V head), for the largest group
   int n_bkv;       // B * Hkv
   int nwg;
+  int spread;      // 1: spread_coords order (packed sequences, causal uneven groups)
+  int exact_per_batch;  // > 0: exact_coords order with this many workgroups per batch
   float c;         // |scale| * log2(e)
   uint32_t qsign;  // 0x80008000 flips both bf16 halves when scale < 0
   int causal;
@@ -111,7 +120,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 template <int D>
 struct TileRegs {
   u32x4_t k[Cfg<D>::KLOADS];
-  u32x2_t v[4];
+  u32x2_t v[Cfg<D>::VLOADS][4];
 };
 
 // HBM -> registers for K/V tile kt (key rows clamped into [0, N)).
@@ -129,12 +138,16 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* kbase,
       r.k[it] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)row * D + dc * 8);
     }
   }
-  if (tid < C::VBLOCKS) {
-    const int kg = tid / (D / 4), dg = tid % (D / 4);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = min(key0 + kg * 4 + rr, N - 1);
-      r.v[rr] = *reinterpret_cast<const u32x2_t*>(vbase + (size_t)row * D + dg * 4);
+  for (int it = 0; it < C::VLOADS; ++it) {
+    const int blk = tid + it * kThreads;
+    if (blk < C::VBLOCKS) {
+      const int kg = blk / (D / 4), dg = blk % (D / 4);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = min(key0 + kg * 4 + rr, N - 1);
+        r.v[it][rr] = *reinterpret_cast<const u32x2_t*>(vbase + (size_t)row * D + dg * 4);
+      }
     }
   }
 }
@@ -154,22 +167,29 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* buf, 
       *reinterpret_cast<u32x4_t*>(ks + lrow * C::KROW + dc * 8) = r.k[it];
     }
   }
-  if (tid < C::VBLOCKS) {
-    const int kg = tid / (D / 4), dg = tid % (D / 4);
-    // r.v[rr] = {V[key rr][d0], V[rr][d0+1]} , {V[rr][d0+2], V[rr][d0+3]}
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const int word = cc >> 1;
-      const bool hi = cc & 1;
-      uint32_t e[4];
+  for (int it = 0; it < C::VLOADS; ++it) {
+    const int blk = tid + it * kThreads;
+    if (blk < C::VBLOCKS) {
+      const int kg = blk / (D / 4), dg = blk % (D / 4);
+      // r.v[it][rr] = {V[key rr][d0], V[rr][d0+1]} , {V[rr][d0+2], V[rr][d0+3]}
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) e[rr] = hi ? (r.v[rr][word] >> 16) : (r.v[rr][word] & 0xffffu);
-      u32x2_t out;
-      out[0] = e[0] | (e[1] << 16);
-      out[1] = e[2] | (e[3] << 16);
-      const int d = dg * 4 + cc;
-      const int lrow = (d & ~31) + pi_inv(d & 31);
-      *reinterpret_cast<u32x2_t*>(vs + lrow * C::VROW + kg * 4) = out;
+      for (int cc = 0; cc < 4; ++cc) {
+        const int word = cc >> 1;
+        const bool hi = cc & 1;
+        uint32_t e[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const uint32_t x = r.v[it][rr][word];  // scalar copy of the vector element
+          e[rr] = hi ? (x >> 16) : (x & 0xffffu);
+        }
+        u32x2_t out;
+        out[0] = e[0] | (e[1] << 16);
+        out[1] = e[2] | (e[3] << 16);
+        const int d = dg * 4 + cc;
+        const int lrow = (d & ~31) + pi_inv(d & 31);
+        *reinterpret_cast<u32x2_t*>(vs + lrow * C::VROW + kg * 4) = out;
+      }
     }
   }
 }
@@ -280,7 +300,7 @@ __device__ __forceinline__ void process_tile(const uint16_t* ks, const u32x4_t (
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Args a) {
+__global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_fwd_bf16_kernel(Args a) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
 
@@ -290,45 +310,56 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Args a) {
   const int l32 = lane & 31, lg = lane >> 5;
 
   // ---- workgroup -> (batch*Hkv, slot range)
-  int L;
-  if (!a.causal) {
+  int bkv, w_in;
+  if (a.spread) {  // packed sequences, or uneven groups under a causal mask
+    spread_coords(blockIdx.x, a.n_bkv, a.wg_per_bkv, a.causal != 0, bkv, w_in);
+  } else if (a.exact_per_batch > 0) {  // uneven groups, encoder-style: XCD-contiguous, exact counts
+    const int bid = blockIdx.x;
+    const int per = a.nwg / kXcds, rem = a.nwg % kXcds;
+    const int x = bid % kXcds, i = bid / kXcds;
+    exact_coords(x * per + min(x, rem) + i, a.exact_per_batch, a.Hq, a.Hkv,
+                 (a.N + kRowsPerWave - 1) / kRowsPerWave, kWaves, bkv, w_in);
+  } else if (!a.causal) {
     // consecutive logical workgroups on one XCD (hardware deals blockIdx
     // round-robin over the XCDs)
     const int bid = blockIdx.x;
     const int per = a.nwg / kXcds, rem = a.nwg % kXcds;
     const int x = bid % kXcds, i = bid / kXcds;
-    L = x * per + min(x, rem) + i;
-  } else {
-    L = blockIdx.x;
-  }
-  int bkv, w_in;
-  if (!a.causal) {
+    const int L = x * per + min(x, rem) + i;
     bkv = L / a.wg_per_bkv;
     w_in = L % a.wg_per_bkv;
   } else {  // longest (largest position block) first
+    const int L = blockIdx.x;
     const int wr = L / a.n_bkv;
     bkv = L % a.n_bkv;
     w_in = a.wg_per_bkv - 1 - wr;
   }
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
+  const HeadGroup hg = head_group(kvh, a.Hq, a.Hkv);
+  const SeqGeom sg = seq_geom(a.cu, a.T, a.N, b, a.Hq, a.Hkv);
+  const int N = sg.n, g = hg.count;
+  const int TB = (N + kRowsPerWave - 1) / kRowsPerWave;
+  // workgroups past this group's (or this sequence's) rows leave at once
+  if (w_in * kWaves >= TB * g) return;
   const int slot = w_in * kWaves + wave;
-  const int tb = slot / a.g, jh = slot % a.g;
-  const bool wave_valid = tb < a.TB;
-  const int h = kvh * a.g + jh;
-  const int N = a.N;
+  const int tb = slot / g, jh = slot % g;
+  const bool wave_valid = tb < TB;
+  const int h = hg.first + jh;
 
   int nt;
   if (a.causal) {
-    const int maxtb = min((w_in * kWaves + kWaves - 1) / a.g, a.TB - 1);
+    const int maxtb = min((w_in * kWaves + kWaves - 1) / g, TB - 1);
     nt = maxtb + 1;
   } else {
-    nt = a.TB;
+    nt = TB;
   }
   const int wave_last = a.causal ? tb : nt - 1;
 
-  const uint16_t* kbase = a.k + (size_t)bkv * N * D;
-  const uint16_t* vbase = a.v + (size_t)bkv * N * D;
-  const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)N * D;
+  const int64_t kvrow0 = sg.kv_base + (int64_t)kvh * sg.stride;
+  const int64_t qrow0 = sg.q_base + (int64_t)h * sg.stride;
+  const uint16_t* kbase = a.k + (size_t)kvrow0 * D;
+  const uint16_t* vbase = a.v + (size_t)kvrow0 * D;
+  const size_t qoff = (size_t)qrow0 * D;
 
   // ---- Q fragments (B operand): query l32 of each 32-row tile, d chunk ds*2+lg
   u32x4_t qf[2][C::DSTEPS];
@@ -414,8 +445,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Args a) {
         }
       }
       if (a.lse != nullptr && lg == 0) {
-        a.lse[((size_t)b * a.Hq + h) * (size_t)N + t] =
-            (m_run[qs] + log2f(ltot)) * 0.69314718055994531f;
+        a.lse[(size_t)qrow0 + t] = (m_run[qs] + log2f(ltot)) * 0.69314718055994531f;
       }
     }
   }
@@ -429,15 +459,26 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
   a.v = static_cast<const uint16_t*>(p.v);
   a.o = static_cast<uint16_t*>(p.o);
   a.lse = p.lse;
+  a.cu = p.cu_seqlens;
+  a.T = p.T;
   a.N = (int)p.N;
   a.Hq = (int)p.Hq;
   a.Hkv = (int)p.Hkv;
-  a.g = (int)(p.Hq / p.Hkv);
-  a.TB = (int)((p.N + kRowsPerWave - 1) / kRowsPerWave);
-  const int64_t slots = (int64_t)a.TB * a.g;
+  const bool uneven = p.Hq % p.Hkv != 0;
+  a.spread = (p.cu_seqlens != nullptr || (uneven && p.causal)) ? 1 : 0;
+  const int TB = (int)((p.N + kRowsPerWave - 1) / kRowsPerWave);
+  const int64_t slots = (int64_t)TB * max_group(a.Hq, a.Hkv);
   a.wg_per_bkv = (int)((slots + kWaves - 1) / kWaves);
   a.n_bkv = (int)(p.B * p.Hkv);
-  const int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;
+  int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;
+  a.exact_per_batch = 0;
+  if (uneven && !a.spread) {
+    int64_t per = 0;
+    for (int j = 0; j < a.Hkv; ++j) per += group_wgs(j, a.Hq, a.Hkv, TB, kWaves);
+    if (per > 0x7fffffff) return hipErrorInvalidValue;
+    a.exact_per_batch = (int)per;
+    nwg = per * p.B;
+  }
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
   a.nwg = (int)nwg;
   a.c = fabsf(p.scale) * 1.4426950408889634f;
@@ -452,6 +493,8 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream) {
   if (p.D == 64) return launch_attn_fwd_bf16_d64(p, stream);
   if (p.D == 16) return launch_d<16>(p, stream);
+  if (p.D == 32) return launch_d<32>(p, stream);
+  if (p.D == 128) return launch_d<128>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -8,8 +8,11 @@
 // Decomposition: a workgroup is 4 waves that share one (batch, K/V head);
 // each wave owns 64 query positions of one query head of the group (slots
 // ordered by position block, then head-in-group), so one K/V tile in LDS
-// feeds 256 query rows, and for g = H_q/H_kv >= 2 those rows come from
-// different query heads -- the reuse the grouping offers.
+// feeds 256 query rows, and for groups of g >= 2 heads those rows come from
+// different query heads -- the reuse the grouping offers. Groups may differ
+// in size by one head (H_kv need not divide H_q) and packed batches have
+// sequences of different lengths: the grid is sized for the largest group
+// and the longest sequence, and workgroups with no rows leave at once.
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 // (A = K tile from LDS, B = Q in registers), so the score accumulator already
@@ -59,6 +62,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "seq_groups.h"
 
 namespace sqa {
 namespace {
@@ -94,10 +98,12 @@ struct Args {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
-  int N, Hq, Hkv, g;
-  int TB;   // ceil(N / 64): 64-row query blocks per head
-  int NT;   // ceil(N / 32): 32-key tiles
-  int wg_per_bkv, n_bkv, nwg;
+  const int* cu;  // packed sequence offsets (nullptr: dense)
+  int64_t T;      // packed: total tokens
+  int N, Hq, Hkv;
+  int wg_per_bkv, n_bkv, nwg;  // sized for the longest sequence and the largest head group
+  int spread;                  // 1: spread_coords order (packed sequences, causal uneven groups)
+  int exact_per_batch;         // > 0: exact_coords order with this many workgroups per batch
   float c;
   uint32_t qsign;
   int causal;
@@ -335,35 +341,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- workgroup -> (batch*Hkv, slot range)
-  int L;
-  if (!a.causal) {  // consecutive logical workgroups on one XCD (shared L2)
+  int bkv, w_in;
+  if (a.spread) {  // packed sequences, or uneven groups under a causal mask
+    spread_coords(blockIdx.x, a.n_bkv, a.wg_per_bkv, a.causal != 0, bkv, w_in);
+  } else if (a.exact_per_batch > 0) {  // uneven groups, encoder-style: XCD-contiguous, exact counts
     const int bid = blockIdx.x;
     const int per = a.nwg / kXcds, rem = a.nwg % kXcds;
     const int x = bid % kXcds, i = bid / kXcds;
-    L = x * per + min(x, rem) + i;
-  } else {
-    L = blockIdx.x;
-  }
-  int bkv, w_in;
-  if (!a.causal) {
+    exact_coords(x * per + min(x, rem) + i, a.exact_per_batch, a.Hq, a.Hkv,
+                 (a.N + kRowsPerWave - 1) / kRowsPerWave, kWaves, bkv, w_in);
+  } else if (!a.causal) {  // consecutive logical workgroups on one XCD (shared L2)
+    const int bid = blockIdx.x;
+    const int per = a.nwg / kXcds, rem = a.nwg % kXcds;
+    const int x = bid % kXcds, i = bid / kXcds;
+    const int L = x * per + min(x, rem) + i;
     bkv = L / a.wg_per_bkv;
     w_in = L % a.wg_per_bkv;
   } else {  // longest (largest position block) first
+    const int L = blockIdx.x;
     const int wr = L / a.n_bkv;
     bkv = L % a.n_bkv;
     w_in = a.wg_per_bkv - 1 - wr;
   }
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
+  const HeadGroup hg = head_group(kvh, a.Hq, a.Hkv);
+  const SeqGeom sg = seq_geom(a.cu, a.T, a.N, b, a.Hq, a.Hkv);
+  const int N = sg.n, g = hg.count;
+  const int TB = (N + kRowsPerWave - 1) / kRowsPerWave;  // 64-row query blocks
+  const int NT = (N + kTileKeys - 1) / kTileKeys;        // 32-key tiles
+  // workgroups past this group's (or this sequence's) rows leave at once
+  if (w_in * kWaves >= TB * g) return;
   const int slot = w_in * kWaves + wave;
-  const int tb = slot / a.g, jh = slot % a.g;
-  const bool wave_valid = tb < a.TB;
-  const int h = kvh * a.g + jh;
-  const int N = a.N;
+  const int tb = slot / g, jh = slot % g;
+  const bool wave_valid = tb < TB;
+  const int h = hg.first + jh;
   // key tiles the workgroup streams, and the last one this wave computes
   // (-1: none). A causal wave's rows end at key tile 2*tb+1.
-  const int maxtb = min((w_in * kWaves + kWaves - 1) / a.g, a.TB - 1);
-  const int nt = a.causal ? min(2 * maxtb + 2, a.NT) : a.NT;
-  const int last = !wave_valid ? -1 : (a.causal ? min(2 * tb + 1, a.NT - 1) : a.NT - 1);
+  const int maxtb = min((w_in * kWaves + kWaves - 1) / g, TB - 1);
+  const int nt = a.causal ? min(2 * maxtb + 2, NT) : NT;
+  const int last = !wave_valid ? -1 : (a.causal ? min(2 * tb + 1, NT - 1) : NT - 1);
   const int trow0 = tb * kRowsPerWave;
 
   Lane ln;
@@ -385,9 +401,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
     }
   }
 
-  const uint16_t* kbase = a.k + (size_t)bkv * N * D;
-  const uint16_t* vbase = a.v + (size_t)bkv * N * D;
-  const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)N * D;
+  const int64_t kvrow0 = sg.kv_base + (int64_t)kvh * sg.stride;
+  const int64_t qrow0 = sg.q_base + (int64_t)h * sg.stride;
+  const uint16_t* kbase = a.k + (size_t)kvrow0 * D;
+  const uint16_t* vbase = a.v + (size_t)kvrow0 * D;
+  const size_t qoff = (size_t)qrow0 * D;
 
   WaveState w;
 #pragma unroll
@@ -477,7 +495,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
           *reinterpret_cast<u32x2_t*>(orow + x * 32 + 8 * ab + 4 * ln.lg) = wv;
         }
       if (a.lse != nullptr && ln.lg == 0)
-        a.lse[((size_t)b * a.Hq + h) * (size_t)N + t] = (w.m_run[qs] + log2f(ltot)) * 0.69314718055994531f;
+        a.lse[(size_t)qrow0 + t] = (w.m_run[qs] + log2f(ltot)) * 0.69314718055994531f;
     }
   }
 }
@@ -493,16 +511,26 @@ hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream) {
   a.v = static_cast<const uint16_t*>(p.v);
   a.o = static_cast<uint16_t*>(p.o);
   a.lse = p.lse;
+  a.cu = p.cu_seqlens;
+  a.T = p.T;
   a.N = (int)p.N;
   a.Hq = (int)p.Hq;
   a.Hkv = (int)p.Hkv;
-  a.g = (int)(p.Hq / p.Hkv);
-  a.TB = (int)((p.N + kRowsPerWave - 1) / kRowsPerWave);
-  a.NT = (int)((p.N + kTileKeys - 1) / kTileKeys);
-  const int64_t slots = (int64_t)a.TB * a.g;
+  const bool uneven = p.Hq % p.Hkv != 0;
+  a.spread = (p.cu_seqlens != nullptr || (uneven && p.causal)) ? 1 : 0;
+  const int TB = (int)((p.N + kRowsPerWave - 1) / kRowsPerWave);
+  const int64_t slots = (int64_t)TB * max_group(a.Hq, a.Hkv);
   a.wg_per_bkv = (int)((slots + kWaves - 1) / kWaves);
   a.n_bkv = (int)(p.B * p.Hkv);
-  const int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;
+  int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;
+  a.exact_per_batch = 0;
+  if (uneven && !a.spread) {
+    int64_t per = 0;
+    for (int j = 0; j < a.Hkv; ++j) per += group_wgs(j, a.Hq, a.Hkv, TB, kWaves);
+    if (per > 0x7fffffff) return hipErrorInvalidValue;
+    a.exact_per_batch = (int)per;
+    nwg = per * p.B;
+  }
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
   a.nwg = (int)nwg;
   a.c = fmaxf(fabsf(p.scale) * 1.4426950408889634f, kMinC);

@@ -17,6 +17,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "seq_groups.h"
 
 namespace sqa {
 namespace {
@@ -30,8 +31,10 @@ struct Args32 {
   const float* v;
   float* o;
   float* lse;
-  int N, Hq, Hkv, g;
-  int blocks_per_head;
+  const int* cu;  // packed sequence offsets (nullptr: dense)
+  int64_t T;      // packed: total tokens
+  int N, Hq, Hkv;
+  int blocks_per_head;  // for the longest sequence
   float scale;
   int causal;
 };
@@ -46,15 +49,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(Args32 a) {
   const int bh = blockIdx.x / a.blocks_per_head;  // b * Hq + h
   const int blk = blockIdx.x % a.blocks_per_head;
   const int b = bh / a.Hq, h = bh % a.Hq;
-  const int kvh = h / a.g;
-  const int N = a.N;
+  const int kvh = (h * a.Hkv) / a.Hq;
+  const SeqGeom sg = seq_geom(a.cu, a.T, a.N, b, a.Hq, a.Hkv);
+  const int N = sg.n;
+  if (blk * RB >= N) return;  // past this sequence's rows (whole workgroup)
   const int t = blk * RB + r;
   const bool valid = t < N;
   const int tq = min(t, N - 1);
 
-  const float* qrow = a.q + ((size_t)bh * N + tq) * D;
-  const float* kbase = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)N * D;
-  const float* vbase = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)N * D;
+  const int64_t qrow0 = sg.q_base + (int64_t)h * sg.stride;
+  const int64_t kvrow0 = sg.kv_base + (int64_t)kvh * sg.stride;
+  const float* qrow = a.q + ((size_t)qrow0 + tq) * D;
+  const float* kbase = a.k + (size_t)kvrow0 * D;
+  const float* vbase = a.v + (size_t)kvrow0 * D;
 
   float qv[D], acc[D];
 #pragma unroll
@@ -125,10 +132,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(Args32 a) {
     for (int c = 0; c < D; ++c) out[c] = fmaf(part[x][r][c], w, out[c]);
   }
   const float inv = 1.0f / L;
-  float* orow = a.o + ((size_t)bh * N + t) * D;
+  float* orow = a.o + ((size_t)qrow0 + t) * D;
 #pragma unroll
   for (int c = 0; c < D; ++c) orow[c] = out[c] * inv;
-  if (a.lse != nullptr) a.lse[(size_t)bh * N + t] = M + logf(L);
+  if (a.lse != nullptr) a.lse[(size_t)qrow0 + t] = M + logf(L);
 }
 
 template <int D, int S>
@@ -140,10 +147,11 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
   a.v = static_cast<const float*>(p.v);
   a.o = static_cast<float*>(p.o);
   a.lse = p.lse;
+  a.cu = p.cu_seqlens;
+  a.T = p.T;
   a.N = (int)p.N;
   a.Hq = (int)p.Hq;
   a.Hkv = (int)p.Hkv;
-  a.g = (int)(p.Hq / p.Hkv);
   a.blocks_per_head = (int)((p.N + RB - 1) / RB);
   a.scale = p.scale;
   a.causal = p.causal;
@@ -157,7 +165,9 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
 
 hipError_t launch_attn_fwd_f32(const AttnProblem& p, hipStream_t stream) {
   if (p.D == 16) return launch_d<16, 8>(p, stream);
+  if (p.D == 32) return launch_d<32, 8>(p, stream);
   if (p.D == 64) return launch_d<64, 4>(p, stream);
+  if (p.D == 128) return launch_d<128, 4>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -8,7 +8,11 @@
 namespace sqa {
 
 // SQA attention forward: q [B,Hq,N,D], k/v [B,Hkv,N,D], o [B,Hq,N,D],
-// optional lse [B,Hq,N] fp32. Hq % Hkv == 0. Sizes already validated.
+// optional lse [B,Hq,N] fp32; 1 <= Hkv <= Hq (query head i reads K/V head
+// floor(i*Hkv/Hq)). With cu_seqlens (device, B+1 int32 offsets) the tensors
+// are packed instead: q/o [Hq,T,D], k/v [Hkv,T,D], lse [Hq,T], sequence b
+// owning tokens cu[b] .. cu[b+1]-1, and N is the longest sequence. Sizes
+// already validated.
 struct AttnProblem {
   const void* q;
   const void* k;
@@ -18,6 +22,8 @@ struct AttnProblem {
   int64_t B, Hq, Hkv, N, D;
   float scale;
   int causal;
+  const int* cu_seqlens;  // nullptr: dense
+  int64_t T;              // packed: total tokens
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream);

@@ -1,0 +1,101 @@
+// Head groups and sequence geometry shared by the attention kernels.
+//
+// Head groups: query head i reads K/V head floor(i*H_kv/H_q) (contiguous
+// query-head groups, "GQA ..." page, "The idea"). The query heads of K/V head
+// j are then i in [first, first + count) with first = ceil(j*H_q/H_kv); group
+// sizes differ by at most one and are >= 1 when H_kv <= H_q, and equal
+// H_q/H_kv when H_kv divides H_q.
+//
+// Sequences: dense tensors are [B, H, N, d]; packed variable-length tensors
+// are [H, T, d] with sequence b owning tokens cu[b] .. cu[b+1]-1 of every
+// head. In both, row t of sequence b, head h is row base + h*stride + t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sqa {
+
+struct HeadGroup {
+  int first, count;
+};
+
+__host__ __device__ __forceinline__ HeadGroup head_group(int j, int Hq, int Hkv) {
+  const int first = (j * Hq + Hkv - 1) / Hkv;
+  const int next = ((j + 1) * Hq + Hkv - 1) / Hkv;
+  return HeadGroup{first, next - first};
+}
+
+// largest group: ceil(H_q / H_kv)
+__host__ __device__ __forceinline__ int max_group(int Hq, int Hkv) { return (Hq + Hkv - 1) / Hkv; }
+
+struct SeqGeom {
+  int64_t q_base;   // row of (sequence b, query head 0, t = 0)
+  int64_t kv_base;  // row of (sequence b, K/V head 0, t = 0)
+  int64_t stride;   // rows between consecutive heads
+  int n;            // rows of the sequence
+};
+
+// cu == nullptr: dense, every sequence has N rows. Otherwise packed with
+// offsets cu[0..B] into T tokens; the offsets are clamped into [0, T] and the
+// length to at most N (the longest sequence the launch was sized for), so a
+// bad offset array cannot move any access outside the tensors.
+__device__ __forceinline__ SeqGeom seq_geom(const int* cu, int64_t T, int N, int b, int Hq, int Hkv) {
+  SeqGeom g;
+  if (cu == nullptr) {
+    g.q_base = (int64_t)b * Hq * N;
+    g.kv_base = (int64_t)b * Hkv * N;
+    g.stride = N;
+    g.n = N;
+  } else {
+    int64_t s = cu[b], e = cu[b + 1];
+    s = s < 0 ? 0 : (s > T ? T : s);
+    e = e < s ? s : (e > T ? T : e);
+    g.q_base = s;
+    g.kv_base = s;
+    g.stride = T;
+    g.n = (int)(e - s < (int64_t)N ? e - s : (int64_t)N);
+  }
+  return g;
+}
+
+// Workgroup -> (b*H_kv + K/V head, workgroup index within it) for launches
+// whose workgroups differ in work beyond the causal triangle: uneven head
+// groups or packed sequences of different lengths. Workgroup indices are
+// outermost (descending if `descending`, so that under a causal mask the
+// longest rows start first) and the (batch, K/V head) pairs are rotated by
+// one per index, so that the workgroups of any one pair -- one long
+// sequence, or one large group -- are dealt over all XCDs instead of landing
+// on one.
+__device__ __forceinline__ void spread_coords(int bid, int n_bkv, int wg_per_bkv, bool descending, int& bkv,
+                                              int& w_in) {
+  const int wr = bid / n_bkv, r = bid % n_bkv;
+  bkv = (r + wr) % n_bkv;
+  w_in = descending ? wg_per_bkv - 1 - wr : wr;
+}
+
+// Workgroups of K/V head j when each takes W slots of (position block,
+// query head) and a head has TB position blocks.
+__host__ __device__ __forceinline__ int group_wgs(int j, int Hq, int Hkv, int TB, int W) {
+  return (TB * head_group(j, Hq, Hkv).count + W - 1) / W;
+}
+
+// Logical workgroup L -> (b*H_kv + K/V head, index within it) for a grid of
+// exactly B * per_batch workgroups, per_batch = sum_j group_wgs(j): groups
+// of different sizes get their own counts, so consecutive L stay on one
+// K/V head (shared L2 under an XCD-contiguous order) with no idle
+// workgroups. A scalar walk over the H_kv groups.
+__device__ __forceinline__ void exact_coords(int L, int per_batch, int Hq, int Hkv, int TB, int W, int& bkv,
+                                             int& w_in) {
+  const int b = L / per_batch;
+  int r = L % per_batch, j = 0;
+  for (; j < Hkv - 1; ++j) {
+    const int n = group_wgs(j, Hq, Hkv, TB, W);
+    if (r < n) break;
+    r -= n;
+  }
+  bkv = b * Hkv + j;
+  w_in = r;
+}
+
+}  // namespace sqa

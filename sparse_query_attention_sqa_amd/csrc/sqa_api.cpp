@@ -52,9 +52,6 @@ sqa_status check_heads(int64_t H_q, int64_t H_kv) {
   if (H_kv < 1 || H_kv > H_q)
     return fail(SQA_ERR_SHAPE, "H_kv must be in [1, H_q] (got H_kv=%lld, H_q=%lld)", (long long)H_kv,
                 (long long)H_q);
-  if (H_q % H_kv != 0)
-    return fail(SQA_ERR_SHAPE, "H_q must be a multiple of H_kv (got %lld, %lld)", (long long)H_q,
-                (long long)H_kv);
   if (H_q > 4096) return fail(SQA_ERR_SHAPE, "H_q too large (%lld)", (long long)H_q);
   return SQA_OK;
 }
@@ -65,7 +62,8 @@ sqa_status check_attn(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d
   sqa_status s = check_heads(H_q, H_kv);
   if (s != SQA_OK) return s;
   if (dtype != SQA_F32 && dtype != SQA_BF16) return fail(SQA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
-  if (d != 16 && d != 64) return fail(SQA_ERR_UNSUPPORTED, "head dim d=%lld not supported (16 or 64)", (long long)d);
+  if (d != 16 && d != 32 && d != 64 && d != 128)
+    return fail(SQA_ERR_UNSUPPORTED, "head dim d=%lld not supported (16, 32, 64 or 128)", (long long)d);
   if (!std::isfinite(scale)) return fail(SQA_ERR_ARG, "scale must be finite");
   if (causal != 0 && causal != 1) return fail(SQA_ERR_ARG, "causal must be 0 or 1 (got %d)", causal);
   if (N > kMaxN) return fail(SQA_ERR_SHAPE, "N=%lld exceeds the supported maximum", (long long)N);
@@ -99,6 +97,39 @@ sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* o, in
     return fail(SQA_ERR_ARG, "lse overlaps another tensor");
 
   sqa::AttnProblem p{q, k, v, o, lse, B, H_q, H_kv, N, d, scale, causal};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = (dtype == SQA_BF16) ? sqa::launch_attn_fwd_bf16(p, st) : sqa::launch_attn_fwd_f32(p, st);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return SQA_OK;
+}
+
+sqa_status sqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
+                               int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t max_seqlen, int64_t d,
+                               int dtype, float scale, int causal, float* lse, void* stream) {
+  g_err.clear();
+  if (B < 0 || T < 0 || max_seqlen < 0) return fail(SQA_ERR_SHAPE, "negative size");
+  // shape rules of one sequence of the longest length; the total is checked below
+  sqa_status s = check_attn(B > 0 ? 1 : 0, H_q, H_kv, max_seqlen, d, dtype, scale, causal);
+  if (s != SQA_OK) return s;
+  if (max_seqlen > T) return fail(SQA_ERR_SHAPE, "max_seqlen=%lld exceeds T=%lld", (long long)max_seqlen,
+                                  (long long)T);
+  if (T * H_q * d > kMaxElems) return fail(SQA_ERR_SHAPE, "tensor too large");
+  if (B == 0 || T == 0 || max_seqlen == 0) return SQA_OK;
+  if (!q || !k || !v || !o || !cu_seqlens) return fail(SQA_ERR_NULL, "q, k, v, o and cu_seqlens must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(SQA_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  if (!aligned(cu_seqlens, 4) || (lse && !aligned(lse, 4)))
+    return fail(SQA_ERR_ALIGN, "cu_seqlens and lse must be 4-byte aligned");
+  const size_t esz = dtype == SQA_BF16 ? 2 : 4;
+  const size_t nq = (size_t)(H_q * T * d) * esz, nkv = (size_t)(H_kv * T * d) * esz;
+  const size_t nl = lse ? (size_t)(H_q * T) * 4 : 0, ncu = (size_t)(B + 1) * 4;
+  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv) || overlaps(o, nq, cu_seqlens, ncu))
+    return fail(SQA_ERR_ARG, "o overlaps an input");
+  if (lse && (overlaps(lse, nl, o, nq) || overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) ||
+              overlaps(lse, nl, v, nkv) || overlaps(lse, nl, cu_seqlens, ncu)))
+    return fail(SQA_ERR_ARG, "lse overlaps another tensor");
+
+  sqa::AttnProblem p{q, k, v, o, lse, B, H_q, H_kv, max_seqlen, d, scale, causal, cu_seqlens, T};
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = (dtype == SQA_BF16) ? sqa::launch_attn_fwd_bf16(p, st) : sqa::launch_attn_fwd_f32(p, st);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
@@ -176,6 +207,8 @@ sqa_status check_layer(int64_t B, int64_t N, int64_t D, int64_t H, int64_t H_q, 
                 (long long)H);
   const int64_t d = D / H;
   if (dtype != SQA_BF16) return fail(SQA_ERR_UNSUPPORTED, "the layer supports bf16 only");
+  if (d != 16 && d != 64)
+    return fail(SQA_ERR_UNSUPPORTED, "the layer supports head dims 16 and 64 (got D/H=%lld)", (long long)d);
   sqa_status s = check_attn(B, H_q, H_kv, N, d, dtype, scale, causal);
   if (s != SQA_OK) return s;
   if (!std::isfinite(rope_base) || rope_base <= 0.f) return fail(SQA_ERR_ARG, "rope_base must be finite and > 0");

@@ -82,6 +82,7 @@ class Workload:
     d_ff: int = 0               # SwiGLU width of a block workload
     d_model: int = 0
     rope_base: float = 10000.0
+    varlen: int = 0             # > 0: a packed batch of this many sequences summing to N tokens
     description: str = ""
 
 
@@ -111,6 +112,24 @@ WORKLOADS = {
         variants=((8, 4), (16, 16), (16, 4), (16, 1)), dtype="bf16",
         causal=(0,), scale=0.125, sampled_rows=4096,
         description="B=1 N=32768 d=64 SQA(8,4) vs MHA/GQA-4/MQA bf16 non-causal"),
+    # Wider shape family: head dims 128 and 32, uneven head groups, and a
+    # packed batch of sequences of mixed lengths (32768 tokens in 8).
+    "long32k_d128_bf16": Workload(
+        name="long32k_d128_bf16", B=1, N=32768, H=16, d=128, variants=((8, 4), (16, 16)),
+        dtype="bf16", causal=(0, 1), scale=1.0 / 128 ** 0.5, sampled_rows=4096,
+        description="B=1 N=32768 d=128 SQA(8,4) vs MHA bf16"),
+    "long32k_d32_bf16": Workload(
+        name="long32k_d32_bf16", B=1, N=32768, H=16, d=32, variants=((8, 4), (16, 16)),
+        dtype="bf16", causal=(0,), scale=1.0 / 32 ** 0.5, sampled_rows=4096,
+        description="B=1 N=32768 d=32 SQA(8,4) vs MHA bf16 non-causal"),
+    "long32k_uneven_bf16": Workload(
+        name="long32k_uneven_bf16", B=1, N=32768, H=16, d=64, variants=((12, 8), (6, 4)),
+        dtype="bf16", causal=(0,), scale=0.125, sampled_rows=4096,
+        description="B=1 N=32768 d=64, H_kv not dividing H_q: (12,8), (6,4) bf16 non-causal"),
+    "varlen32k_bf16": Workload(
+        name="varlen32k_bf16", B=1, N=32768, H=16, d=64, variants=((8, 4), (16, 16)),
+        dtype="bf16", causal=(1, 0), scale=0.125, varlen=8,
+        description="packed batch of 8 sequences (mixed lengths, 32768 tokens) d=64 SQA(8,4) vs MHA bf16"),
     "long131k_bf16": Workload(
         name="long131k_bf16", B=1, N=131072, H=16, d=64,
         variants=((8, 8), (4, 4), (16, 16)), dtype="bf16", causal=(0, 1),

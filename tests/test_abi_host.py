@@ -30,8 +30,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ["sqa_attn_fwd", "sqa_layer_fwd", "sqa_layer_workspace_bytes", "sqa_status_str",
-              "sqa_last_error", "sqa_version"]:
+    for n in ["sqa_attn_fwd", "sqa_attn_fwd_varlen", "sqa_layer_fwd", "sqa_layer_workspace_bytes",
+              "sqa_status_str", "sqa_last_error", "sqa_version"]:
         assert n in names
 
 
@@ -75,9 +75,9 @@ def _attn(lib, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(o=None), 1),
-    (dict(Hkv=3), 2), (dict(Hkv=0), 2), (dict(Hkv=16), 2), (dict(Hq=0), 2), (dict(N=-1), 2),
+    (dict(Hkv=9), 2), (dict(Hkv=0), 2), (dict(Hkv=16), 2), (dict(Hq=0), 2), (dict(N=-1), 2),
     (dict(B=-2), 2), (dict(N=1 << 31), 2),
-    (dict(d=32), 3), (dict(d=128), 3), (dict(dtype=5), 3),
+    (dict(d=48), 3), (dict(d=256), 3), (dict(d=8), 3), (dict(dtype=5), 3),
     (dict(q=FAKE + 2), 4), (dict(o=FAKE + 0x300008), 4),
     (dict(scale=float("inf")), 7), (dict(scale=float("nan")), 7), (dict(causal=2), 7),
     (dict(o=FAKE), 7),                               # o aliases q
@@ -94,6 +94,36 @@ def test_attn_rejects_invalid_arguments(lib, kw, code):
 def test_zero_size_is_a_noop(lib):
     assert _attn(lib, q=None, k=None, v=None, o=None, B=0) == 0
     assert _attn(lib, q=None, k=None, v=None, o=None, N=0) == 0
+    assert lib.sqa_last_error().decode() == ""
+
+
+def _varlen(lib, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, cu=FAKE + 0x400000,
+            B=4, Hq=8, Hkv=4, T=4096, maxlen=2048, d=64, dtype=1, scale=0.125, causal=1, lse=None):
+    return lib.sqa_attn_fwd_varlen(q, k, v, o, cu, B, Hq, Hkv, T, maxlen, d, dtype, scale, causal, lse, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(cu=None), 1), (dict(o=None), 1),
+    (dict(B=-1), 2), (dict(T=-1), 2), (dict(maxlen=-1), 2), (dict(maxlen=5000), 2),
+    (dict(Hkv=9), 2), (dict(Hkv=0), 2), (dict(maxlen=1 << 31, T=1 << 31), 2),
+    (dict(d=48), 3), (dict(dtype=7), 3),
+    (dict(q=FAKE + 8), 4), (dict(cu=FAKE + 0x400002), 4), (dict(lse=FAKE + 0x500002), 4),
+    (dict(scale=float("inf")), 7), (dict(causal=3), 7),
+    (dict(o=FAKE + 0x200000), 7),                    # o aliases v
+    (dict(o=FAKE + 0x400000 - 0x80000), 7),          # o overlaps inputs and cu_seqlens
+    (dict(lse=FAKE + 0x400000), 7),                  # lse aliases cu_seqlens
+])
+@cpu_only
+def test_varlen_rejects_invalid_arguments(lib, kw, code):
+    assert _varlen(lib, **kw) == code
+    assert lib.sqa_last_error().decode() != ""
+
+
+@cpu_only
+def test_varlen_empty_is_a_noop(lib):
+    assert _varlen(lib, q=None, k=None, v=None, o=None, cu=None, B=0) == 0
+    assert _varlen(lib, q=None, k=None, v=None, o=None, cu=None, T=0, maxlen=0) == 0
+    assert _varlen(lib, q=None, k=None, v=None, o=None, cu=None, maxlen=0) == 0
     assert lib.sqa_last_error().decode() == ""
 
 
@@ -116,7 +146,8 @@ def _layer(lib, x=FAKE, ws=FAKE + 0x1000000, ws_bytes=1 << 26, B=16, N=1024, D=2
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), 1), (dict(ws=None), 5), (dict(ws_bytes=100), 5), (dict(dtype=0), 3),
-    (dict(D=250), 2), (dict(H=0), 2), (dict(Hkv=3), 2), (dict(D=512, H=16), 3),
+    (dict(D=250), 2), (dict(H=0), 2), (dict(Hkv=9), 2), (dict(D=512, H=16), 3),
+    (dict(D=512, H=4), 3),                           # d = 128: not a layer head dim
     (dict(base=0.0), 7), (dict(base=float("nan")), 7), (dict(ws=FAKE + 0x1000010), 4),
 ])
 @cpu_only
@@ -159,8 +190,8 @@ def _bwd(lib, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000,
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(lse=None), 1), (dict(dv=None), 1),
-    (dict(Hkv=3), 2), (dict(N=-1), 2),
-    (dict(d=16), 3), (dict(dtype=0), 3), (dict(d=128), 3),
+    (dict(Hkv=9), 2), (dict(N=-1), 2),
+    (dict(d=16), 3), (dict(dtype=0), 3), (dict(d=128), 3), (dict(d=32), 3),
     (dict(do=FAKE + 0x400008), 4), (dict(lse=FAKE + 0x500002), 4), (dict(ws=FAKE + 0x900008), 4),
     (dict(ws=None), 5), (dict(ws_bytes=65535), 5),
     (dict(scale=float("nan")), 7), (dict(causal=-1), 7),

@@ -230,11 +230,12 @@ def test_lse_bf16_matches_oracle():
 def test_error_paths_on_device():
     q = torch.zeros(1, 8, 64, 64, dtype=torch.bfloat16, device="cuda")
     k = torch.zeros(1, 4, 64, 64, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(sqa.SQAError) as e:
-        sqa.sqa_attn_fwd(q, k[:, :3].contiguous(), k[:, :3].contiguous())
+    kk = torch.zeros(1, 9, 64, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sqa.SQAError) as e:                 # H_kv > H_q
+        sqa.sqa_attn_fwd(q, kk, kk)
     assert e.value.status == 2
-    with pytest.raises(sqa.SQAError) as e:
-        sqa.sqa_attn_fwd(q[..., :32].contiguous(), k[..., :32].contiguous(), k[..., :32].contiguous())
+    with pytest.raises(sqa.SQAError) as e:                 # d = 48
+        sqa.sqa_attn_fwd(q[..., :48].contiguous(), k[..., :48].contiguous(), k[..., :48].contiguous())
     assert e.value.status == 3
     flat = torch.zeros(1 + 8 * 64 * 64, dtype=torch.bfloat16, device="cuda")
     mis = flat[1:].view(1, 8, 64, 64)           # 2-byte offset: misaligned

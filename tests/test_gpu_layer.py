@@ -41,6 +41,7 @@ def test_sqatm_layer_all_outputs():
 @pytest.mark.parametrize("B,N,D,H,Hq,Hkv,causal", [
     (1, 1, 256, 16, 8, 4, 1), (2, 70, 256, 16, 8, 4, 1), (1, 129, 256, 16, 16, 1, 0),
     (3, 65, 256, 16, 4, 4, 1), (1, 200, 512, 8, 4, 2, 1), (2, 33, 256, 4, 2, 1, 0),
+    (2, 100, 256, 16, 6, 4, 1), (1, 77, 512, 8, 5, 2, 0),     # H_kv not dividing H_q
 ])
 def test_layer_shapes(B, N, D, H, Hq, Hkv, causal):
     label = f"layer B={B} N={N} D={D} H={H} ({Hq},{Hkv}) causal={causal}"

@@ -1,0 +1,234 @@
+"""GPU parity of the wider shape family (through the C ABI) against the fp64
+oracle: head dims 32 and 128, query-head counts that H_kv does not divide,
+and packed variable-length batches (sqa_attn_fwd_varlen). Same bars as the
+other forward tests (tests/parity.py): bf16 max |O - O_ref| <= 1e-2 *
+max |O_ref| plus the per-row gate, fp32 <= 1e-4.
+"""
+import functools
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention as oracle_attention
+from oracle import attention_bwd as oracle_bwd
+from oracle import attention_varlen as oracle_varlen
+from synth import (WORKLOADS, boundary_rows, draw_attn_case, draw_qkv, draw_upstream, draw_varlen,
+                   sample_rows, select_variant, varlen_lengths)
+from tests.parity import ROW_FLOOR, check_global, check_rows, log, oracle_threads, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import sparse_query_attention_sqa_amd as sqa  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    sqa.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _fwd(q, k, v, dtype, scale, causal):
+    o, lse = sqa.sqa_attn_fwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), scale=scale,
+                              causal=bool(causal), return_lse=True)
+    torch.cuda.synchronize()
+    return to_host(o), lse.cpu().numpy().astype(np.float64)
+
+
+def _check_fwd(q, k, v, dtype, scale, causal, label):
+    o, lse = _fwd(q, k, v, dtype, scale, causal)
+    ref, ref_lse = oracle_attention(q, k, v, scale=scale, causal=bool(causal), return_lse=True,
+                                    threads=oracle_threads())
+    check_global(o, ref, dtype, label)
+    if dtype == "bf16":
+        check_rows(o, ref, label)
+    assert np.max(np.abs(lse - ref_lse)) <= (1e-4 if dtype == "f32" else 2e-3), f"{label}: lse"
+
+
+# ------------------------------------------------------------ head dims 32, 128
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 129, 1000])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 4), (6, 4), (3, 1)])
+def test_bf16_head_dims_small_all_rows(Hq, Hkv, N, causal, d):
+    label = f"bf16 d={d} Hq={Hq} Hkv={Hkv} N={N} causal={causal}"
+    log(f"[case] {label}")
+    B = 2 if N <= 129 else 1
+    q, k, v = draw_attn_case(B, Hq, Hkv, N, d, "bf16", seed=N * 7 + d + Hq)
+    _check_fwd(q, k, v, "bf16", 1.0 / math.sqrt(d), causal, label)
+
+
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("N,Hq,Hkv", [(1, 2, 1), (17, 8, 4), (257, 6, 4), (700, 5, 2)])
+def test_f32_head_dims_small_all_rows(N, Hq, Hkv, causal, d):
+    label = f"f32 d={d} Hq={Hq} Hkv={Hkv} N={N} causal={causal}"
+    log(f"[case] {label}")
+    q, k, v = draw_attn_case(1, Hq, Hkv, N, d, "f32", seed=N + d)
+    _check_fwd(q, k, v, "f32", 1.0 / math.sqrt(d), causal, label)
+
+
+# ------------------------------------------------------------- uneven groups
+@pytest.mark.parametrize("d", [64, 16])
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("N", [1, 65, 1000, 4096])
+@pytest.mark.parametrize("Hq,Hkv", [(6, 4), (5, 2), (7, 3), (12, 8)])
+def test_bf16_uneven_groups_all_rows(Hq, Hkv, N, causal, d):
+    label = f"bf16 uneven Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}"
+    log(f"[case] {label}")
+    B = 2 if N <= 65 else 1
+    q, k, v = draw_attn_case(B, Hq, Hkv, N, d, "bf16", seed=N * 3 + Hq * 11 + Hkv)
+    _check_fwd(q, k, v, "bf16", 1.0 / math.sqrt(d), causal, label)
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("N,Hq,Hkv", [(100, 6, 4), (1000, 5, 2), (333, 7, 3)])
+def test_bwd_uneven_groups(N, Hq, Hkv, causal):
+    label = f"bwd uneven Hq={Hq} Hkv={Hkv} N={N} causal={causal}"
+    log(f"[case] {label}")
+    q, k, v = draw_attn_case(1, Hq, Hkv, N, 64, "bf16", seed=N + Hq)
+    do = draw_upstream(q.shape, "bf16", seed=N + 9)
+    tq, tk, tv = (to_dev(a, "bf16") for a in (q, k, v))
+    o, lse = sqa.sqa_attn_fwd(tq, tk, tv, scale=0.125, causal=bool(causal), return_lse=True)
+    grads = sqa.sqa_attn_bwd(tq, tk, tv, o, to_dev(do, "bf16"), lse, scale=0.125, causal=bool(causal))
+    torch.cuda.synchronize()
+    refs = oracle_bwd(q, k, v, do, scale=0.125, causal=bool(causal), threads=oracle_threads())
+    for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
+        check_global(to_host(g), r, "bf16", f"{label} {name}", floor=ROW_FLOOR)
+
+
+# ----------------------------------------------------- packed variable length
+LEN_MIXES = {
+    "tiles": [1, 31, 32, 33, 0, 64, 65, 500, 7, 1000],
+    "one": [300],
+    "tiny": [5, 0, 0, 2],
+}
+
+
+def _varlen_run(q, k, v, cu, dtype, scale, causal, max_seqlen=None):
+    o, lse = sqa.sqa_attn_fwd_varlen(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype),
+                                     torch.from_numpy(cu).to("cuda"), max_seqlen, scale=scale,
+                                     causal=bool(causal), return_lse=True)
+    torch.cuda.synchronize()
+    return to_host(o), lse.cpu().numpy().astype(np.float64)
+
+
+def _check_varlen(q, k, v, cu, dtype, scale, causal, label):
+    o, lse = _varlen_run(q, k, v, cu, dtype, scale, causal)
+    ref, ref_lse = oracle_varlen(q, k, v, cu, scale=scale, causal=bool(causal), return_lse=True,
+                                 threads=oracle_threads())
+    check_global(o, ref, dtype, label)
+    if dtype == "bf16":
+        check_rows(o, ref, label)
+    assert np.max(np.abs(lse - ref_lse)) <= (1e-4 if dtype == "f32" else 2e-3), f"{label}: lse"
+
+
+@pytest.mark.parametrize("d", [64, 16, 32, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("mix", sorted(LEN_MIXES))
+@pytest.mark.parametrize("Hq,Hkv", [(8, 4), (6, 4)])
+def test_bf16_varlen_all_rows(Hq, Hkv, mix, causal, d):
+    label = f"bf16 varlen {mix} Hq={Hq} Hkv={Hkv} d={d} causal={causal}"
+    log(f"[case] {label}")
+    q, k, v, cu = draw_varlen(LEN_MIXES[mix], Hq, Hkv, d, "bf16", seed=len(mix) + d + Hq)
+    _check_varlen(q, k, v, cu, "bf16", 1.0 / math.sqrt(d), causal, label)
+
+
+@pytest.mark.parametrize("d", [16, 64, 32, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_f32_varlen_all_rows(causal, d):
+    label = f"f32 varlen d={d} causal={causal}"
+    log(f"[case] {label}")
+    q, k, v, cu = draw_varlen(LEN_MIXES["tiles"], 6, 4, d, "f32", seed=d)
+    _check_varlen(q, k, v, cu, "f32", 1.0 / math.sqrt(d), causal, label)
+
+
+@pytest.mark.parametrize("d", [64, 16, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_varlen_one_sequence_equals_dense_bitwise(causal, d):
+    """One sequence of N tokens through the packed entry point runs the same
+    arithmetic as the dense B = 1 call: identical bits."""
+    q, k, v, cu = draw_varlen([777], 8, 4, d, "bf16", seed=d + 1)
+    ov, lv = _varlen_run(q, k, v, cu, "bf16", 0.2, causal)
+    od, ld = _fwd(q[None], k[None], v[None], "bf16", 0.2, causal)
+    assert np.array_equal(ov, od[0]) and np.array_equal(lv, ld[0])
+
+
+def test_varlen_larger_max_seqlen_is_harmless():
+    """max_seqlen above the true longest length only adds workgroups that
+    find no rows."""
+    q, k, v, cu = draw_varlen([40, 90, 3], 4, 2, 64, "bf16", seed=4)
+    a, la = _varlen_run(q, k, v, cu, "bf16", 0.125, 1)
+    b, lb = _varlen_run(q, k, v, cu, "bf16", 0.125, 1, max_seqlen=133)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_varlen_error_paths():
+    q, k, v, cu = draw_varlen([10, 20], 8, 4, 64, "bf16", seed=2)
+    tq, tk, tv = (to_dev(a, "bf16") for a in (q, k, v))
+    tcu = torch.from_numpy(cu).to("cuda")
+    with pytest.raises(sqa.SQAError) as e:
+        sqa.sqa_attn_fwd_varlen(tq, tk, tv, tcu, 31)     # max_seqlen > T
+    assert e.value.status == 2
+    with pytest.raises(sqa.SQAError) as e:
+        sqa.sqa_attn_fwd_varlen(tq, tk, tv, tcu, 20, out=tq)  # o aliases q
+    assert e.value.status == 7
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------- 32k workloads, sampled rows
+@functools.lru_cache(maxsize=1)
+def _inputs(name):
+    w = WORKLOADS[name]
+    log(f"[gen] {name}")
+    return draw_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=0)
+
+
+def _long_sampled(name, Hq, Hkv, causal):
+    w = WORKLOADS[name]
+    label = f"{name} ({Hq},{Hkv}) causal={causal}"
+    log(f"[case] {label}")
+    q, k, v = select_variant(*_inputs(name), Hq, Hkv)
+    o, lse = sqa.sqa_attn_fwd(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), scale=w.scale,
+                              causal=bool(causal), return_lse=True)
+    torch.cuda.synchronize()
+    rows, brows = sample_rows(w.N, w.sampled_rows), boundary_rows(w.N)
+    got = o.index_select(2, torch.from_numpy(rows).to("cuda")).float().cpu().numpy().astype(np.float64)
+    got_b = o.index_select(2, torch.from_numpy(brows).to("cuda")).float().cpu().numpy().astype(np.float64)
+    got_lse = lse.index_select(2, torch.from_numpy(rows).to("cuda")).cpu().numpy()
+    th = oracle_threads()
+    ref, ref_lse = oracle_attention(q, k, v, scale=w.scale, causal=bool(causal), rows=rows, threads=th,
+                                    return_lse=True)
+    check_global(got, ref, "bf16", label + " sampled")
+    check_rows(got_b, oracle_attention(q, k, v, scale=w.scale, causal=bool(causal), rows=brows, threads=th),
+               label + " boundary rows")
+    assert np.max(np.abs(got_lse - ref_lse)) <= 2e-3
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_long32k_d128_sqa(causal):
+    _long_sampled("long32k_d128_bf16", 8, 4, causal)
+
+
+def test_long32k_d32_sqa():
+    _long_sampled("long32k_d32_bf16", 8, 4, 0)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(12, 8), (6, 4)])
+def test_long32k_uneven(Hq, Hkv):
+    _long_sampled("long32k_uneven_bf16", Hq, Hkv, 0)
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_varlen32k_all_rows(causal):
+    w = WORKLOADS["varlen32k_bf16"]
+    lens = varlen_lengths(w.N, w.varlen)
+    q, k, v, cu = draw_varlen(lens, w.H, w.H, w.d, "bf16", seed=0)
+    q, k, v = q[:8], k[:4], v[:4]
+    label = f"{w.name} (8,4) causal={causal} lens={lens.tolist()}"
+    log(f"[case] {label}")
+    _check_varlen(q, k, v, cu, "bf16", w.scale, causal, label)
