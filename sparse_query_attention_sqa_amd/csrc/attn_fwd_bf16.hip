@@ -494,7 +494,7 @@ hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream) {
   if (p.D == 64) return launch_attn_fwd_bf16_d64(p, stream);
   if (p.D == 16) return launch_d<16>(p, stream);
   if (p.D == 32) return launch_d<32>(p, stream);
-  if (p.D == 128) return launch_d<128>(p, stream);
+  if (p.D == 128) return launch_attn_fwd_bf16_d128(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -29,6 +29,8 @@ struct AttnProblem {
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream);
 // head dim 64, software-pipelined (attn_fwd_bf16_d64.hip)
 hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream);
+// head dim 128, software-pipelined (attn_fwd_bf16_d128.hip)
+hipError_t launch_attn_fwd_bf16_d128(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnProblem& p, hipStream_t stream);
 
 // SQA attention backward (bf16, head dim 64): dq [B,Hq,N,D], dk/dv
