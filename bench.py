@@ -47,8 +47,16 @@ def counted_flops(B, Hq, N, d, causal):
     return f / 2 if causal else f
 
 
+KERNELS = {64: ("attn_fwd_bf16_d64_kernel", "attn_fwd_bf16_d64.hip"),
+           128: ("attn_fwd_bf16_d128_kernel", "attn_fwd_bf16_d128.hip")}
+
+
+def kernel_name(d: int) -> str:
+    return KERNELS[d][0] if d in KERNELS else f"attn_fwd_bf16_kernel<{d}>"
+
+
 def kernel_source(d: int) -> str:
-    name = "attn_fwd_bf16_d64.hip" if d == 64 else "attn_fwd_bf16.hip"
+    name = KERNELS[d][1] if d in KERNELS else "attn_fwd_bf16.hip"
     return os.path.join(ROOT, "sparse_query_attention_sqa_amd", "csrc", name)
 
 
@@ -316,7 +324,7 @@ def bench_varlen(sqa, torch, w, args):
                                                     "tflops": round(flops(var[0]) / (cms * 1e-3) / 1e12, 2)}
         if "16,16" in comparison:
             comparison["speedup_vs_mha"] = round(comparison["16,16"]["ms"] / ms, 3)
-    kernel = "attn_fwd_bf16_d64_kernel" if w.d == 64 else f"attn_fwd_bf16_kernel<{w.d}>"
+    kernel = kernel_name(w.d)
     return _common(args, ms, w, {
         "value": round(tflops, 3), "unit": "TFLOP/s", "dtype": "bf16",
         "tokens_per_s": round(w.N / (ms * 1e-3), 1),
@@ -441,7 +449,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic,
-                "kernel": "attn_fwd_bf16_d64_kernel" if w.d == 64 else f"attn_fwd_bf16_kernel<{w.d}>",
+                "kernel": kernel_name(w.d),
                 "per_launch_flop": flops}
 
     cpu = None
