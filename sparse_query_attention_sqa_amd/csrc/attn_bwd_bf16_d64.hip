@@ -214,12 +214,11 @@ __device__ __forceinline__ void kv_step(const KvCtx& cx, KvState& w, int s, int 
     rt[2 * e] = make_float2(x.x, x.y);
     rt[2 * e + 1] = make_float2(x.z, x.w);
   }
-  const bool masked = cx.causal && qt == cx.kb;
   f32x16_t p, ds;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     float x = __builtin_fmaf(sc[e], cx.c, -rt[e].x);
-    if (masked && lg * 16 + e < l32) x = -INFINITY;  // query row before the key
+    if (cx.causal && qt == cx.kb && lg * 16 + e < l32) x = -INFINITY;  // query row before the key
     p[e] = __builtin_amdgcn_exp2f(x);
     ds[e] = p[e] * (dp[e] - rt[e].y);
   }
@@ -328,9 +327,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
 }
 
 // ------------------------------------------------------------------ dQ
-constexpr int kDqBuf = 4;
+// Software-pipelined over 32-key tiles j (one stage, as the forward):
+//   phase j: MFMA  dQ^T += K(j-1)^T dS(j-1)^T  and  S^T(j+1), dP^T(j+1)
+//            VALU  P(j) = 2^(s c - lse2), dS(j) = P (dP - D)
+// The fragments the next phase multiplies (K and V rows of tile j+2, the
+// transposed K of tile j) are read from LDS during this phase.
+constexpr int kDqBuf = 5;                // ring slots
 constexpr int kDqSlot = 3 * kTileBytes;  // K rows | V rows | K tr
-constexpr int kDqDma = 3;
+constexpr int kDqDma = 3;                // DMA instructions per wave per tile
 
 struct DqArgs {
   const uint16_t* q;
@@ -355,13 +359,18 @@ struct DqCtx {
   const uint16_t* vbase;
   int N, nlim, last, tb, causal, wave, t;
   float c;
+  float masked;  // score whose exponent s*c is -inf: -inf * sign(c)
   uint32_t off_rows, off_tr;
   ReadOffsets ro;
 };
 
 struct DqState {
   u32x4_t qf[4], df[4];  // Q and dO of this wave's 32 rows as B operands
-  f32x16_t acc[2];
+  f32x16_t acc[2];       // dQ^T
+  u32x4_t kr[4], vr[4];  // K and V row fragments of the next S^T, dP^T
+  u32x4_t kt[2][2];      // transposed K fragments of the next dQ product
+  f32x16_t sc[2], dp[2]; // S^T and dP^T of tiles j (index j & 1) and j+1
+  u32x4_t dsk[2][2];     // dS of tiles j-1 and j, packed as B operands
   float lse2, dd;
 };
 
@@ -374,39 +383,48 @@ __device__ __forceinline__ void dq_issue(const DqCtx& cx, int kt) {
   dma_tile_part(cx.kbase, row0, cx.nlim, slot + 2 * kTileBytes + cx.wave * 1024, cx.off_tr);
 }
 
-template <int SLOT>
-__device__ __forceinline__ void dq_step(const DqCtx& cx, DqState& w, int j) {
-  constexpr int AHEAD = (SLOT + kDqBuf - 1) % kDqBuf;
-  // this wave's DMA of tile j has landed; every wave is done with tile j-1
-  barrier_vm<(kDqBuf - 2) * kDqDma>();
-  dq_issue<AHEAD>(cx, j + kDqBuf - 1);
+// Scheduling hints: 12 MFMAs, each followed by 5 VALU instructions of the
+// independent softmax work.
+__device__ __forceinline__ void dq_interleave() {
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+  }
+}
+
+template <int SLOT, int P>
+__device__ __forceinline__ void dq_phase(const DqCtx& cx, DqState& w, int j) {
+  constexpr int AHEAD = (SLOT + 4) % kDqBuf;
+  constexpr int NEXT2 = (SLOT + 2) % kDqBuf;
+  // tile j+2 has landed (tile j+3 may still be in flight); every wave is done
+  // with tile j-1, whose slot receives tile j+4
+  barrier_vm<kDqDma>();
+  dq_issue<AHEAD>(cx, j + 4);
   if (j > cx.last) return;
-  const uint8_t* slot = cx.ring.p[SLOT];
-  const int lane = threadIdx.x & 63, lg = lane >> 5;
+  const int lg = (threadIdx.x & 63) >> 5;
+  // mask S^T(j) on diagonal and tail tiles only, before the phase's MFMAs so
+  // that the MFMA/softmax block below stays one basic block
+  if ((cx.causal && j == cx.tb) || (j * kTileRows + kTileRows > cx.N)) {
+    const int key0 = j * kTileRows + lg * 16;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (!(key0 + e < cx.N && (!cx.causal || key0 + e <= cx.t))) w.sc[P][e] = cx.masked;
+  }
 
-  u32x4_t a[4];
-  read_rows(slot, cx.ro, a);
-  const f32x16_t sc = mfma_k64(a, w.qf);  // entry e: key j*32 + lg*16 + e, query t
-  read_rows(slot + kTileBytes, cx.ro, a);
-  const f32x16_t dp = mfma_k64(a, w.df);
-  u32x4_t kt[2][2];
-  read_tr(slot + 2 * kTileBytes, cx.ro, kt);
+  mfma_tr(w.kt, w.dsk[P ^ 1], w.acc);                                  // dQ^T += K(j-1)^T dS(j-1)^T
+  read_tr(cx.ring.p[SLOT] + 2 * kTileBytes, cx.ro, w.kt);              // K(j)^T
+  w.sc[P ^ 1] = mfma_k64(w.kr, w.qf);                                  // S^T(j+1)
+  w.dp[P ^ 1] = mfma_k64(w.vr, w.df);                                  // dP^T(j+1)
+  read_rows(cx.ring.p[NEXT2], cx.ro, w.kr);                            // K(j+2)
+  read_rows(cx.ring.p[NEXT2] + kTileBytes, cx.ro, w.vr);               // V(j+2)
 
-  const int key0 = j * kTileRows + lg * 16;
-  const bool masked = (cx.causal && j == cx.tb) || (j * kTileRows + kTileRows > cx.N);
   f32x16_t ds;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    float x = __builtin_fmaf(sc[e], cx.c, -w.lse2);
-    if (masked) {
-      const int key = key0 + e;
-      if (!(key < cx.N && (!cx.causal || key <= cx.t))) x = -INFINITY;
-    }
-    ds[e] = __builtin_amdgcn_exp2f(x) * (dp[e] - w.dd);
-  }
-  u32x4_t dsk[2];
-  pack_pairs(ds, dsk);
-  mfma_tr(kt, dsk, w.acc);
+  for (int e = 0; e < 16; ++e)
+    ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(w.sc[P][e], cx.c, -w.lse2)) * (w.dp[P][e] - w.dd);
+  pack_pairs(ds, w.dsk[P]);
+  dq_interleave();
 }
 
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
@@ -414,6 +432,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring1[kDqSlot];
   __shared__ __attribute__((aligned(16))) uint8_t ring2[kDqSlot];
   __shared__ __attribute__((aligned(16))) uint8_t ring3[kDqSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring4[kDqSlot];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -438,6 +457,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
   cx.ring.p[1] = ring1;
   cx.ring.p[2] = ring2;
   cx.ring.p[3] = ring3;
+  cx.ring.p[4] = ring4;
   cx.kbase = a.k + (size_t)bkv * N * kD;
   cx.vbase = a.v + (size_t)bkv * N * kD;
   cx.N = N;
@@ -448,6 +468,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
   cx.wave = wave;
   cx.t = tb * kTileRows + l32;
   cx.c = a.c;
+  cx.masked = a.c > 0.f ? -INFINITY : INFINITY;
   cx.off_rows = dma_off_rows(wave, lane);
   cx.off_tr = dma_off_tr(wave, lane);
   cx.ro = read_offsets(lane);
@@ -470,32 +491,65 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
   }
   w.acc[0] = zero16();
   w.acc[1] = zero16();
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    w.kt[x][0] = u32x4_t{0u, 0u, 0u, 0u};  // K(-1) = 0 and dS(-1) = 0: the first dQ product is a no-op
+    w.kt[x][1] = u32x4_t{0u, 0u, 0u, 0u};
+    w.dsk[1][x] = u32x4_t{0u, 0u, 0u, 0u};
+  }
 
   for (int e = tid; e < kDqSlot / 16; e += kThreads) {
     reinterpret_cast<u32x4_t*>(ring0)[e] = u32x4_t{0u, 0u, 0u, 0u};
     reinterpret_cast<u32x4_t*>(ring1)[e] = u32x4_t{0u, 0u, 0u, 0u};
     reinterpret_cast<u32x4_t*>(ring2)[e] = u32x4_t{0u, 0u, 0u, 0u};
     reinterpret_cast<u32x4_t*>(ring3)[e] = u32x4_t{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4_t*>(ring4)[e] = u32x4_t{0u, 0u, 0u, 0u};
   }
-  barrier_vm<63>();
+  barrier_vm<0>();
 
+  // prologue: tiles 0..3 in flight, wait for tiles 0..2, S^T(0) and dP^T(0),
+  // then the row fragments of tile 1
   dq_issue<0>(cx, 0);
   dq_issue<1>(cx, 1);
   dq_issue<2>(cx, 2);
+  dq_issue<3>(cx, 3);
+  barrier_vm<kDqDma>();
+  read_rows(ring0, cx.ro, w.kr);
+  read_rows(ring0 + kTileBytes, cx.ro, w.vr);
+  w.sc[0] = mfma_k64(w.kr, w.qf);
+  w.dp[0] = mfma_k64(w.vr, w.df);
+  read_rows(ring1, cx.ro, w.kr);
+  read_rows(ring1 + kTileBytes, cx.ro, w.vr);
 
+  // whole ten-phase rounds first (ring slot period 5, register parity 2)
   int j = 0;
-  for (; j + kDqBuf <= nt; j += kDqBuf) {
-    dq_step<0>(cx, w, j);
-    dq_step<1>(cx, w, j + 1);
-    dq_step<2>(cx, w, j + 2);
-    dq_step<3>(cx, w, j + 3);
+  for (; j + 2 * kDqBuf <= nt; j += 2 * kDqBuf) {
+    dq_phase<0, 0>(cx, w, j);
+    dq_phase<1, 1>(cx, w, j + 1);
+    dq_phase<2, 0>(cx, w, j + 2);
+    dq_phase<3, 1>(cx, w, j + 3);
+    dq_phase<4, 0>(cx, w, j + 4);
+    dq_phase<0, 1>(cx, w, j + 5);
+    dq_phase<1, 0>(cx, w, j + 6);
+    dq_phase<2, 1>(cx, w, j + 7);
+    dq_phase<3, 0>(cx, w, j + 8);
+    dq_phase<4, 1>(cx, w, j + 9);
   }
-  if (j < nt) dq_step<0>(cx, w, j);
-  if (j + 1 < nt) dq_step<1>(cx, w, j + 1);
-  if (j + 2 < nt) dq_step<2>(cx, w, j + 2);
+  if (j < nt) dq_phase<0, 0>(cx, w, j);
+  if (j + 1 < nt) dq_phase<1, 1>(cx, w, j + 1);
+  if (j + 2 < nt) dq_phase<2, 0>(cx, w, j + 2);
+  if (j + 3 < nt) dq_phase<3, 1>(cx, w, j + 3);
+  if (j + 4 < nt) dq_phase<4, 0>(cx, w, j + 4);
+  if (j + 5 < nt) dq_phase<0, 1>(cx, w, j + 5);
+  if (j + 6 < nt) dq_phase<1, 0>(cx, w, j + 6);
+  if (j + 7 < nt) dq_phase<2, 1>(cx, w, j + 7);
+  if (j + 8 < nt) dq_phase<3, 0>(cx, w, j + 8);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
   if (!wave_valid || cx.t >= N) return;
+  // drain dQ^T += K(last)^T dS(last)^T
+  if (cx.last & 1) mfma_tr(w.kt, w.dsk[1], w.acc);
+  else mfma_tr(w.kt, w.dsk[0], w.acc);
   store_tr_row(a.dq + (((size_t)b * a.Hq + h) * N + cx.t) * kD, w.acc, a.scale, lg);
 }
 
@@ -511,7 +565,11 @@ hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream) {
   if (p.N * kRowBytes > 0x7fffffffLL) return hipErrorInvalidValue;  // buffer descriptor range
   const int N = (int)p.N;
   const int Np = (N + kTileRows - 1) / kTileRows * kTileRows;
-  const float c = p.scale * kLog2e;
+  // c = scale * log2(e), kept away from 0 so that a masked score (+-inf)
+  // times c is -inf; at scale 0 the scores s*c stay below 1e-22 in
+  // magnitude and round away exactly as 0 would
+  float c = p.scale * kLog2e;
+  if (fabsf(c) < 1e-30f) c = p.scale < 0.f ? -1e-30f : 1e-30f;
   float2* rt = static_cast<float2*>(p.rowterms);
 
   {
