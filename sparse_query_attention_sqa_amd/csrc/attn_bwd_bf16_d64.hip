@@ -124,10 +124,21 @@ __device__ __forceinline__ void wg_coords(int spread, int causal, bool reverse, 
 }
 
 // ------------------------------------------------------------------ dK, dV
-constexpr int kKvBuf = 4;                           // ring slots
-constexpr int kKvRt = 4 * kTileBytes;               // row-term area offset
-constexpr int kKvSlot = 4 * kTileBytes + 1024;      // Q rows | dO rows | Q tr | dO tr | row terms
-constexpr int kKvDma = 5;                           // DMA instructions per wave per step
+// A step s is one 32-row query tile of one query head of the group (steps
+// ordered by query tile, then head). Software-pipelined over steps:
+//   phase s: MFMA  dV^T += dO(s-1)^T P(s-1), dK^T += Q(s-1)^T dS(s-1),
+//                  interleaved with
+//            VALU  P(s) = 2^(s c - lse2), dS(s) = P (dP - D);
+//            then MFMA S(s+1) = Q K^T, dP(s+1) = dO V^T into the registers
+//            the softmax has just consumed (one score buffer keeps the wave
+//            at two waves per SIMD).
+// Q and dO of a step sit in LDS once each, in the shared layout of
+// bf16_tiles.h (row reads for S and dP, transposed reads for dK and dV), so a
+// ring slot is 9 KB and six slots give four steps of lookahead.
+constexpr int kKvBuf = 6;                       // ring slots
+constexpr int kKvRt = 2 * kTileBytes;           // row-term area offset
+constexpr int kKvSlot = 2 * kTileBytes + 1024;  // Q | dO | row terms
+constexpr int kKvDma = 3;                       // DMA instructions per wave per step
 
 struct KvArgs {
   const uint16_t* q;
@@ -152,16 +163,18 @@ struct KvCtx {
   const uint16_t* q;     // Q of batch b, head 0
   const uint16_t* dout;  // dO of batch b, head 0
   const float2* rt;      // row terms of batch b, head 0 (rows padded to Np)
-  int N, Np, g, h0, qt0, kb, causal, wave;
-  bool wave_valid;
+  int N, Np, g, h0, qt0, kb, causal, wave, first;  // first: the first step this wave computes
   float c;
-  uint32_t off_rows, off_tr;
+  float masked;  // score whose exponent s*c is -inf: -inf * sign(c)
+  uint32_t off;
   ReadOffsets ro;
 };
 
 struct KvState {
-  u32x4_t kb_f[4], vb_f[4];  // K and V rows of this wave's 32 keys as B operands
-  f32x16_t acc_k[2], acc_v[2];
+  u32x4_t kb_f[4], vb_f[4];     // K and V rows of this wave's 32 keys as B operands
+  f32x16_t acc_k[2], acc_v[2];  // dK^T, dV^T
+  f32x16_t sc, dp;              // S and dP of the current step
+  u32x4_t pk[2][2], dsk[2][2];  // P and dS of steps s-1 and s, packed as B operands
 };
 
 // DMA step s (query tile qt of query head h0 + i) into ring slot SLOT.
@@ -171,13 +184,9 @@ __device__ __forceinline__ void kv_issue(const KvCtx& cx, int s) {
   const size_t head = (size_t)(cx.h0 + i) * cx.N;
   const int row0 = qt * kTileRows;
   uint8_t* slot = cx.ring.p[SLOT];
-  const uint16_t* qb = cx.q + head * kD;
-  const uint16_t* db = cx.dout + head * kD;
   const float2* rb = cx.rt + (size_t)(cx.h0 + i) * cx.Np;
-  dma_tile_part(qb, row0, cx.N, slot + cx.wave * 1024, cx.off_rows);
-  dma_tile_part(db, row0, cx.N, slot + kTileBytes + cx.wave * 1024, cx.off_rows);
-  dma_tile_part(qb, row0, cx.N, slot + 2 * kTileBytes + cx.wave * 1024, cx.off_tr);
-  dma_tile_part(db, row0, cx.N, slot + 3 * kTileBytes + cx.wave * 1024, cx.off_tr);
+  dma_tile_part(cx.q + head * kD, row0, cx.N, slot + cx.wave * 1024, cx.off);
+  dma_tile_part(cx.dout + head * kD, row0, cx.N, slot + kTileBytes + cx.wave * 1024, cx.off);
   // row terms of the 32 rows (8 B each, whole tiles thanks to the padding)
   // land in the first 256 B of the area; every wave writes the same bytes
   // (lanes past 16 write zeros beyond them)
@@ -188,48 +197,87 @@ __device__ __forceinline__ void kv_issue(const KvCtx& cx, int s) {
                                            0, 0, 0);
 }
 
+// S and dP of the step in slot SLOT.
 template <int SLOT>
-__device__ __forceinline__ void kv_step(const KvCtx& cx, KvState& w, int s, int nsteps) {
-  constexpr int AHEAD = (SLOT + kKvBuf - 1) % kKvBuf;
-  // this wave's DMA of step s has landed; every wave is done with step s-1
-  barrier_vm<(kKvBuf - 2) * kKvDma>();
-  kv_issue<AHEAD>(cx, s + kKvBuf - 1);
-  const int qt = cx.qt0 + s / cx.g;
-  const bool active = cx.wave_valid && (!cx.causal || qt >= cx.kb);
-  if (!active) return;
-  const uint8_t* slot = cx.ring.p[SLOT];
-  const int lane = threadIdx.x & 63, lg = lane >> 5, l32 = lane & 31;
-
+__device__ __forceinline__ void kv_scores(const KvCtx& cx, KvState& w) {
   u32x4_t a[4];
-  read_rows(slot, cx.ro, a);
-  const f32x16_t sc = mfma_k64(a, w.kb_f);  // entry e: query qt*32 + lg*16 + e, key kb*32 + l32
-  read_rows(slot + kTileBytes, cx.ro, a);
-  const f32x16_t dp = mfma_k64(a, w.vb_f);
+  read_rows(cx.ring.p[SLOT], cx.ro, a);
+  w.sc = mfma_k64(a, w.kb_f);
+  read_rows(cx.ring.p[SLOT] + kTileBytes, cx.ro, a);
+  w.dp = mfma_k64(a, w.vb_f);
+}
 
+// Scheduling hints: 8 MFMAs, each followed by 8 VALU instructions of the
+// independent softmax work.
+__device__ __forceinline__ void kv_interleave() {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+  }
+}
+
+template <int SLOT, int P>
+__device__ __forceinline__ void kv_phase(const KvCtx& cx, KvState& w, int s) {
+  constexpr int AHEAD = (SLOT + 4) % kKvBuf;
+  constexpr int PREV = (SLOT + kKvBuf - 1) % kKvBuf;
+  constexpr int NEXT = (SLOT + 1) % kKvBuf;
+  // step s+1 has landed (steps s+2, s+3 may still be in flight); every wave
+  // is done with step s-2, whose slot receives step s+4
+  barrier_vm<2 * kKvDma>();
+  kv_issue<AHEAD>(cx, s + 4);
+  const int lane = threadIdx.x & 63, lg = lane >> 5, l32 = lane & 31;
+  // Masks of S(s). Steps before the wave's first (causal: query tiles that
+  // see none of its keys) run the same code fully masked (P = dS = 0), so
+  // every wave keeps one pipeline from step 0; on the causal diagonal step,
+  // query rows before the key (entry e <-> query lg*16 + e).
+  if (s < cx.first) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) w.sc[e] = cx.masked;
+  } else if (cx.causal && cx.qt0 + s / cx.g == cx.kb) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (lg * 16 + e < l32) w.sc[e] = cx.masked;
+  }
   float2 rt[16];
-  const float4* rtp = reinterpret_cast<const float4*>(slot + kKvRt + lg * 128);
+  const float4* rtp = reinterpret_cast<const float4*>(cx.ring.p[SLOT] + kKvRt + lg * 128);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float4 x = rtp[e];
     rt[2 * e] = make_float2(x.x, x.y);
     rt[2 * e + 1] = make_float2(x.z, x.w);
   }
+  u32x4_t qt_f[2][2], dt_f[2][2];
+  read_tr_shared(cx.ring.p[PREV], cx.ro, qt_f);               // Q(s-1)^T
+  read_tr_shared(cx.ring.p[PREV] + kTileBytes, cx.ro, dt_f);  // dO(s-1)^T
+  mfma_tr(dt_f, w.pk[P ^ 1], w.acc_v);                        // dV^T += dO(s-1)^T P(s-1)
+  mfma_tr(qt_f, w.dsk[P ^ 1], w.acc_k);                       // dK^T += Q(s-1)^T dS(s-1)
+
   f32x16_t p, ds;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    float x = __builtin_fmaf(sc[e], cx.c, -rt[e].x);
-    if (cx.causal && qt == cx.kb && lg * 16 + e < l32) x = -INFINITY;  // query row before the key
-    p[e] = __builtin_amdgcn_exp2f(x);
-    ds[e] = p[e] * (dp[e] - rt[e].y);
+    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(w.sc[e], cx.c, -rt[e].x));
+    ds[e] = p[e] * (w.dp[e] - rt[e].y);
   }
-  u32x4_t pk[2], dsk[2];
-  pack_pairs(p, pk);
-  pack_pairs(ds, dsk);
-  u32x4_t t[2][2];
-  read_tr(slot + 3 * kTileBytes, cx.ro, t);
-  mfma_tr(t, pk, w.acc_v);
-  read_tr(slot + 2 * kTileBytes, cx.ro, t);
-  mfma_tr(t, dsk, w.acc_k);
+  pack_pairs(p, w.pk[P]);
+  pack_pairs(ds, w.dsk[P]);
+  kv_interleave();
+  kv_scores<NEXT>(cx, w);  // S(s+1), dP(s+1)
+}
+
+// dV^T += dO(s)^T P(s), dK^T += Q(s)^T dS(s) for the last step, in slot SLOT.
+template <int SLOT>
+__device__ __forceinline__ void kv_drain(const KvCtx& cx, KvState& w, int par) {
+  u32x4_t qt_f[2][2], dt_f[2][2];
+  read_tr_shared(cx.ring.p[SLOT], cx.ro, qt_f);
+  read_tr_shared(cx.ring.p[SLOT] + kTileBytes, cx.ro, dt_f);
+  if (par) {
+    mfma_tr(dt_f, w.pk[1], w.acc_v);
+    mfma_tr(qt_f, w.dsk[1], w.acc_k);
+  } else {
+    mfma_tr(dt_f, w.pk[0], w.acc_v);
+    mfma_tr(qt_f, w.dsk[0], w.acc_k);
+  }
 }
 
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
@@ -237,6 +285,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring1[kKvSlot];
   __shared__ __attribute__((aligned(16))) uint8_t ring2[kKvSlot];
   __shared__ __attribute__((aligned(16))) uint8_t ring3[kKvSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring4[kKvSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring5[kKvSlot];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -251,6 +301,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
   cx.ring.p[1] = ring1;
   cx.ring.p[2] = ring2;
   cx.ring.p[3] = ring3;
+  cx.ring.p[4] = ring4;
+  cx.ring.p[5] = ring5;
   cx.q = a.q + (size_t)b * a.Hq * N * kD;
   cx.dout = a.dout + (size_t)b * a.Hq * N * kD;
   cx.rt = a.rt + (size_t)b * a.Hq * a.Np;
@@ -263,12 +315,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
   cx.kb = w_in * kWaves + wave;
   cx.causal = a.causal;
   cx.wave = wave;
-  cx.wave_valid = cx.kb < a.KB;
   cx.c = a.c;
-  cx.off_rows = dma_off_rows(wave, lane);
-  cx.off_tr = dma_off_tr(wave, lane);
-  cx.ro = read_offsets(lane);
+  cx.masked = a.c > 0.f ? -INFINITY : INFINITY;
+  cx.off = dma_off_shared(wave, lane);
+  cx.ro = read_offsets_shared(lane);
+  const bool wave_valid = cx.kb < a.KB;
   const int nsteps = max(a.NQT - cx.qt0, 0) * cx.g;
+  // causal: this wave's keys are first seen by query tile kb, i.e. step (kb - qt0) * g
+  cx.first = !wave_valid ? nsteps : (a.causal ? min((cx.kb - cx.qt0) * cx.g, nsteps) : 0);
 
   KvState w;
   {
@@ -279,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
       w.kb_f[ds] = u32x4_t{0u, 0u, 0u, 0u};
       w.vb_f[ds] = u32x4_t{0u, 0u, 0u, 0u};
     }
-    if (cx.wave_valid) {
+    if (wave_valid) {
       load_row_frags(a.k + kv_row, lg, w.kb_f);
       load_row_frags(a.v + kv_row, lg, w.vb_f);
     }
@@ -287,6 +341,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
     for (int x = 0; x < 2; ++x) {
       w.acc_k[x] = zero16();
       w.acc_v[x] = zero16();
+      // P and dS of the step before a wave's first are 0: its first dK/dV
+      // products add nothing
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        w.pk[par][x] = u32x4_t{0u, 0u, 0u, 0u};
+        w.dsk[par][x] = u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
   }
 
@@ -296,31 +357,51 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
     reinterpret_cast<u32x4_t*>(ring1)[e] = u32x4_t{0u, 0u, 0u, 0u};
     reinterpret_cast<u32x4_t*>(ring2)[e] = u32x4_t{0u, 0u, 0u, 0u};
     reinterpret_cast<u32x4_t*>(ring3)[e] = u32x4_t{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4_t*>(ring4)[e] = u32x4_t{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4_t*>(ring5)[e] = u32x4_t{0u, 0u, 0u, 0u};
   }
-  barrier_vm<63>();
+  barrier_vm<0>();
 
-  // prologue: steps 0 .. kKvBuf-2 in flight
+  // prologue: steps 0..3 in flight (empty ranges past the end), wait for
+  // steps 0..2, then S(0) and dP(0)
   kv_issue<0>(cx, 0);
   kv_issue<1>(cx, 1);
   kv_issue<2>(cx, 2);
+  kv_issue<3>(cx, 3);
+  barrier_vm<kKvDma>();
+  kv_scores<0>(cx, w);
 
-  // whole ring rounds first, so that every path to the loop back-edge has
-  // issued the same DMAs and the compiler's wait bookkeeping stays exact
+  // whole six-phase rounds first (ring slot period 6, register parity 2)
   int s = 0;
   for (; s + kKvBuf <= nsteps; s += kKvBuf) {
-    kv_step<0>(cx, w, s, nsteps);
-    kv_step<1>(cx, w, s + 1, nsteps);
-    kv_step<2>(cx, w, s + 2, nsteps);
-    kv_step<3>(cx, w, s + 3, nsteps);
+    kv_phase<0, 0>(cx, w, s);
+    kv_phase<1, 1>(cx, w, s + 1);
+    kv_phase<2, 0>(cx, w, s + 2);
+    kv_phase<3, 1>(cx, w, s + 3);
+    kv_phase<4, 0>(cx, w, s + 4);
+    kv_phase<5, 1>(cx, w, s + 5);
   }
-  if (s < nsteps) kv_step<0>(cx, w, s, nsteps);
-  if (s + 1 < nsteps) kv_step<1>(cx, w, s + 1, nsteps);
-  if (s + 2 < nsteps) kv_step<2>(cx, w, s + 2, nsteps);
+  if (s < nsteps) kv_phase<0, 0>(cx, w, s);
+  if (s + 1 < nsteps) kv_phase<1, 1>(cx, w, s + 1);
+  if (s + 2 < nsteps) kv_phase<2, 0>(cx, w, s + 2);
+  if (s + 3 < nsteps) kv_phase<3, 1>(cx, w, s + 3);
+  if (s + 4 < nsteps) kv_phase<4, 0>(cx, w, s + 4);
   // drain the DMAs still in flight before the wave ends
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
   const int u = cx.kb * kTileRows + l32;
-  if (!cx.wave_valid || u >= N) return;
+  if (cx.first >= nsteps) return;  // no step for this wave (all waves of it: uniform)
+  // dK/dV of the last step (its slot is still intact: later DMAs went elsewhere)
+  const int last = nsteps - 1;
+  switch (last % kKvBuf) {
+    case 0: kv_drain<0>(cx, w, last & 1); break;
+    case 1: kv_drain<1>(cx, w, last & 1); break;
+    case 2: kv_drain<2>(cx, w, last & 1); break;
+    case 3: kv_drain<3>(cx, w, last & 1); break;
+    case 4: kv_drain<4>(cx, w, last & 1); break;
+    default: kv_drain<5>(cx, w, last & 1); break;
+  }
+  if (u >= N) return;
   const size_t kv_row = ((size_t)bkv * N + u) * kD;
   store_tr_row(a.dk + kv_row, w.acc_k, a.scale, lg);
   store_tr_row(a.dv + kv_row, w.acc_v, 1.0f, lg);

@@ -93,6 +93,34 @@ __device__ __forceinline__ ReadOffsets read_offsets(int lane) {
   return o;
 }
 
+// "Shared layout": LDS row r holds tile row pi(r), as in the row layout, but
+// with the swizzle swz_s(r) = 2*(r&3) + ((r>>2)&1). Eight consecutive rows
+// then put one logical chunk in eight different bank groups (row reads), and
+// four consecutive rows put a pair of chunks in eight different bank groups
+// (transposed reads), so one copy of a tile serves both operand forms:
+// read_rows with read_offsets_shared().rows, and read_tr_shared, whose k
+// position (hh, lg, s) <-> tile row lg*16 + hh*8 + s sits at LDS row
+// hh*16 + lg*4 + s (s < 4) or hh*16 + 8 + lg*4 + s - 4 (s >= 4).
+__device__ __forceinline__ int swz_s(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+__device__ __forceinline__ uint32_t dma_off_shared(int part, int lane) {
+  const int r = part * 8 + (lane >> 3), s = lane & 7;
+  return (uint32_t)(pi_row(r) * kRowBytes + ((s ^ swz_s(r)) * 16));
+}
+__device__ __forceinline__ ReadOffsets read_offsets_shared(int lane) {
+  ReadOffsets o;
+  const int l32 = lane & 31, lg = lane >> 5;
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) o.rows[ds] = (uint32_t)(l32 * kRowBytes + (((ds * 2 + lg) ^ swz_s(l32)) * 16));
+  const int j16 = lane & 15, g1 = (lane >> 4) & 1;
+  const int row = lg * 4 + (j16 >> 2);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int c16 = x * 4 + 2 * g1 + ((j16 & 3) >> 1);
+    o.tr[x] = (uint32_t)(row * kRowBytes + ((c16 ^ swz_s(row)) * 16) + (j16 & 1) * 8);
+  }
+  return o;
+}
+
 // DMA one wave's 8 rows of a tile that starts at row `row0` of a [rows, 64]
 // bf16 array whose valid rows end at `nlim`; rows at or past nlim are
 // zero-filled by the descriptor range check without any memory access.
@@ -120,6 +148,22 @@ __device__ __forceinline__ void read_tr(const uint8_t* tile, const ReadOffsets& 
       const uint8_t* p = tile + ro.tr[x] + hh * 8 * kRowBytes;
       const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
       const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * kRowBytes));
+      const u32x2_t a = __builtin_bit_cast(u32x2_t, lo);
+      const u32x2_t b = __builtin_bit_cast(u32x2_t, hi);
+      f[x][hh] = u32x4_t{a[0], a[1], b[0], b[1]};
+    }
+}
+
+// Transposed A fragments [x][hh] of a shared-layout tile (see read_tr for
+// the operand; the k positions map to LDS rows as stated at swz_s).
+__device__ __forceinline__ void read_tr_shared(const uint8_t* tile, const ReadOffsets& ro, u32x4_t (&f)[2][2]) {
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint8_t* p = tile + ro.tr[x] + hh * 16 * kRowBytes;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 8 * kRowBytes));
       const u32x2_t a = __builtin_bit_cast(u32x2_t, lo);
       const u32x2_t b = __builtin_bit_cast(u32x2_t, hi);
       f[x][hh] = u32x4_t{a[0], a[1], b[0], b[1]};
