@@ -68,6 +68,7 @@ __all__ = [
     "attention",
     "attention_bwd",
     "attention_varlen",
+    "attention_bwd_varlen",
     "rope",
     "layer",
     "layer_weight_shapes",
@@ -333,6 +334,38 @@ def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
         for (b, j, sl, gk, gv) in sorted(results, key=lambda r: (r[0], r[1], r[2])):
             dk[b, j] += gk
             dv[b, j] += gv
+    return dq, dk, dv
+
+
+def attention_bwd_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                         cu_seqlens: Sequence[int], scale: Optional[float] = None, causal: bool = False,
+                         threads: int = 1):
+    """Backward of ``attention_varlen`` in float64: (dQ [H_q, T, d], dK, dV
+    [H_kv, T, d]). Sequences are independent, so each is the dense backward
+    above on its slice."""
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    dout = np.asarray(dout)
+    if q.ndim != 3 or k.ndim != 3 or v.ndim != 3 or dout.shape != q.shape:
+        raise ValueError("expected 3-D [heads, T, d] arrays, dout shaped like q")
+    H_q, T, d = q.shape
+    if k.shape[1:] != (T, d) or v.shape != k.shape:
+        raise ValueError("q/k/v shapes disagree")
+    cu = [int(x) for x in cu_seqlens]
+    if len(cu) < 1 or cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must rise from 0 to T")
+    dq = np.zeros((H_q, T, d), dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for a, b in zip(cu, cu[1:]):
+        if b == a:
+            continue
+        gq, gk, gv = attention_bwd(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], dout[None, :, a:b],
+                                   scale=scale, causal=causal, threads=threads)
+        dq[:, a:b] = gq[0]
+        dk[:, a:b] = gk[0]
+        dv[:, a:b] = gv[0]
     return dq, dk, dv
 
 

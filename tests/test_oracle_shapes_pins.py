@@ -185,3 +185,65 @@ def test_varlen_rejects_bad_offsets():
     for bad in ([0, 5, 4, 7], [1, 7], [0, 3, 8]):
         with pytest.raises(ValueError):
             attention_varlen(q, k, v, bad)
+
+
+# ----------------------------------------------------- packed-batch backward
+def _autograd_packed(q, k, v, g, cu, scale, causal):
+    """torch autograd through fp64 SDPA over the whole pack with the explicit
+    block-diagonal (causal-within-block) mask; K/V gathered by kv_head_index,
+    so autograd sums each K/V head's group."""
+    H_q, T, _ = q.shape
+    H_kv = k.shape[0]
+    seq = np.zeros(T, dtype=np.int64)
+    for n, (a, b) in enumerate(zip(cu, cu[1:])):
+        seq[a:b] = n
+    seq = torch.from_numpy(seq)
+    mask = seq[:, None] == seq[None, :]
+    if causal:
+        pos = torch.arange(T)
+        mask = mask & (pos[None, :] <= pos[:, None])
+    idx = torch.tensor([kv_head_index(i, H_q, H_kv) for i in range(H_q)])
+    tq = torch.from_numpy(q).double().requires_grad_(True)
+    tk = torch.from_numpy(k).double().requires_grad_(True)
+    tv = torch.from_numpy(v).double().requires_grad_(True)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq[None], tk.index_select(0, idx)[None], tv.index_select(0, idx)[None], attn_mask=mask, scale=scale)
+    o.backward(torch.from_numpy(g)[None])
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("lens,H_q,H_kv", [([9, 1, 20, 0, 7], 8, 4), ([12, 12], 6, 4), ([5, 16], 5, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_bwd_matches_torch_autograd(lens, H_q, H_kv, causal):
+    from oracle import attention_bwd_varlen
+    q, k, v, cu = draw_varlen(lens, H_q, H_kv, 8, "bf16", seed=sum(lens) + 3)
+    g = np.random.default_rng(7).standard_normal(q.shape)
+    got = attention_bwd_varlen(q, k, v, g, cu, scale=0.3, causal=causal)
+    ref = _autograd_packed(q, k, v, g, cu, 0.3, causal)
+    for a, b in zip(got, ref):
+        assert np.max(np.abs(a - b)) <= 1e-11
+
+
+def test_varlen_bwd_matches_finite_differences_of_forward():
+    """Central differences of the (separately pinned) packed forward oracle."""
+    from oracle import attention_bwd_varlen
+    lens = [3, 0, 4]
+    q, k, v, cu = draw_varlen(lens, 3, 2, 2, "f32", seed=9)
+    q, k, v = (x.astype(np.float64) for x in (q, k, v))
+    g = np.random.default_rng(10).standard_normal(q.shape)
+    got = attention_bwd_varlen(q, k, v, g, cu, scale=0.8, causal=True)
+    eps = 1e-6
+
+    def loss(qq, kk, vv):
+        return float(np.sum(attention_varlen(qq, kk, vv, cu, scale=0.8, causal=True) * g))
+
+    for which, arr in enumerate((q, k, v)):
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            args = [q, k, v]
+            up = arr.copy(); up[idx] += eps
+            dn = arr.copy(); dn[idx] -= eps
+            args[which] = up; lp = loss(*args)
+            args[which] = dn; lm = loss(*args)
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert np.max(np.abs(got[which] - fd)) <= 1e-7 * max(1.0, np.max(np.abs(fd)))
