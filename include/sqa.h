@@ -151,6 +151,35 @@ sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void*
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sqa_attn_bwd_varlen_workspace_bytes -- bytes of device workspace
+ * sqa_attn_bwd_varlen needs: one fp32 pair (lse * log2(e), D_t) per packed
+ * row plus 32 rows of padding per query head, 8 * H_q * (T + 32) bytes
+ * rounded up to 256. Returns 0 for invalid or zero sizes, or when d / dtype
+ * are not supported.
+ */
+size_t sqa_attn_bwd_varlen_workspace_bytes(int64_t B, int64_t H_q, int64_t T, int64_t d, int dtype);
+
+/*
+ * sqa_attn_bwd_varlen -- sqa_attn_bwd for a packed batch of variable-length
+ * sequences, the layout of sqa_attn_fwd_varlen: per sequence the result
+ * equals sqa_attn_bwd with B = 1 on that sequence's rows.
+ *
+ *   q, o, dout, dq [H_q,  T, d]  bf16 (dq output, overwritten)
+ *   k, v, dk, dv   [H_kv, T, d]  bf16 (dk, dv outputs, overwritten)
+ *   lse            [H_q, T]      fp32, sqa_attn_fwd_varlen's lse
+ *   cu_seqlens     [B + 1]       DEVICE int32 offsets, as in sqa_attn_fwd_varlen
+ *   workspace      at least sqa_attn_bwd_varlen_workspace_bytes(...) bytes
+ *   d = 64, dtype SQA_BF16; head counts, scale, causal as sqa_attn_bwd.
+ * Outputs must not overlap each other, an input (cu_seqlens included) or
+ * the workspace. Errors: as sqa_attn_bwd.
+ */
+sqa_status sqa_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                               const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
+                               int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t max_seqlen, int64_t d,
+                               int dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * sqa_layer_workspace_bytes -- bytes of device workspace sqa_layer_fwd needs
  * for these sizes: bf16 Q [B,H_q,N,d], K and V [B,H_kv,N,d], the attention
  * output [B,H_q,N,d] and an fp32 RoPE (cos, sin) table [N, d/2, 2], each

@@ -11,6 +11,9 @@ library is not built, importing the functions raises.
     sqa_attn_bwd(q, k, v, o, dout, lse, *, scale=None, causal=False, dq=None, dk=None,
                  dv=None, workspace=None)
     sqa_attn_bwd_workspace_bytes(B, H_q, N, d, dtype="bf16")
+    sqa_attn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen=None, *, scale=None, causal=False,
+                        dq=None, dk=None, dv=None, workspace=None)
+    sqa_attn_bwd_varlen_workspace_bytes(B, H_q, T, d, dtype="bf16")
     sqa_layer_fwd(x, w_q, w_k, w_v, w_o, *, H, H_q, H_kv, rope_base=10000.0,
                   scale=None, causal=True, out=None, workspace=None)
     sqa_layer_workspace_bytes(B, N, D, H, H_q, H_kv, dtype="bf16")
@@ -26,6 +29,7 @@ import os
 from typing import Optional
 
 __all__ = ["SQAError", "lib_path", "load_library", "sqa_attn_fwd", "sqa_attn_fwd_varlen", "sqa_attn_bwd",
+           "sqa_attn_bwd_varlen", "sqa_attn_bwd_varlen_workspace_bytes",
            "sqa_attn_bwd_workspace_bytes", "sqa_layer_fwd", "sqa_block_fwd",
            "sqa_block_workspace_bytes",
            "sqa_layer_workspace_bytes", "sqa_status_str", "sqa_version",
@@ -72,6 +76,11 @@ def load_library() -> ctypes.CDLL:
     lib.sqa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                  ctypes.c_int, f32, ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.sqa_attn_bwd.restype = ctypes.c_int
+    lib.sqa_attn_bwd_varlen_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.sqa_attn_bwd_varlen_workspace_bytes.restype = ctypes.c_size_t
+    lib.sqa_attn_bwd_varlen.argtypes = [vp] * 10 + [i64] * 6 + [ctypes.c_int, f32, ctypes.c_int, vp,
+                                                                ctypes.c_size_t, vp]
+    lib.sqa_attn_bwd_varlen.restype = ctypes.c_int
     lib.sqa_layer_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
     lib.sqa_layer_workspace_bytes.restype = ctypes.c_size_t
     lib.sqa_layer_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32,
@@ -265,6 +274,66 @@ def sqa_attn_bwd(q, k, v, o, dout, lse, *, scale: Optional[float] = None, causal
                           B, H_q, H_kv, N, d, code, float(scale), int(bool(causal)),
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           _stream_handle(q.device))
+    _check(st)
+    return outs[0], outs[1], outs[2]
+
+
+def sqa_attn_bwd_varlen_workspace_bytes(B: int, H_q: int, T: int, d: int, dtype: str = "bf16") -> int:
+    code = SQA_BF16 if dtype == "bf16" else SQA_F32
+    return int(load_library().sqa_attn_bwd_varlen_workspace_bytes(B, H_q, T, d, code))
+
+
+def sqa_attn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: Optional[int] = None, *,
+                        scale: Optional[float] = None, causal: bool = False, dq=None, dk=None, dv=None,
+                        workspace=None):
+    """Gradients of ``sqa_attn_fwd_varlen`` for the upstream gradient ``dout``.
+
+    q, o, dout [H_q, T, d]; k, v [H_kv, T, d] bf16 (d = 64); lse [H_q, T] fp32
+    from ``sqa_attn_fwd_varlen(..., return_lse=True)``; cu_seqlens the same
+    int32 GPU offsets. Returns (dq, dk, dv). ``max_seqlen`` as in the forward.
+    """
+    torch = _torch()
+    lib = load_library()
+    _require_device(q, k, v, o, dout, lse, cu_seqlens)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("expected 3-D [H, T, d] tensors")
+    if k.shape != v.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("k/v and q/o/dout shapes must match")
+    if len({q.dtype, k.dtype, v.dtype, o.dtype, dout.dtype}) != 1:
+        raise ValueError("q, k, v, o and dout must share a dtype")
+    if lse.dtype != torch.float32:
+        raise ValueError("lse must be float32")
+    H_q, T, d = q.shape
+    if k.shape[1] != T or k.shape[2] != d or tuple(lse.shape) != (H_q, T):
+        raise ValueError("q, k/v and lse shapes disagree")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of B + 1 offsets")
+    B = cu_seqlens.numel() - 1
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if B > 0 else 0
+    H_kv = k.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    outs = []
+    for t, like in ((dq, q), (dk, k), (dv, v)):
+        if t is None:
+            t = torch.empty_like(like)
+        else:
+            _require_device(t)
+            if t.shape != like.shape or t.dtype != like.dtype:
+                raise ValueError("gradient outputs must match their inputs in shape and dtype")
+        outs.append(t)
+    code = _dtype_code(q)
+    need = int(lib.sqa_attn_bwd_varlen_workspace_bytes(B, H_q, T, d, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _require_device(workspace)
+    st = lib.sqa_attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                 lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                                 cu_seqlens.data_ptr(), B, H_q, H_kv, T, int(max_seqlen), d, code, float(scale),
+                                 int(bool(causal)), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream_handle(q.device))
     _check(st)
     return outs[0], outs[1], outs[2]
 

@@ -148,8 +148,10 @@ struct KvArgs {
   const float2* rt;  // row terms, [B*H_q, Np]
   uint16_t* dk;
   uint16_t* dv;
-  int N, Np, Hq, Hkv, KB, NQT, wg_per_bkv, n_bkv, nwg;
-  int spread;  // uneven head groups: spread_coords order
+  const int* cu;  // packed sequence offsets (nullptr: dense)
+  int64_t T;      // packed: total tokens
+  int N, Np, Hq, Hkv, wg_per_bkv, n_bkv, nwg;  // N: the (longest) sequence; Np: row-term rows per head
+  int spread;  // uneven head groups or packed sequences: spread_coords order
   float c, scale;
   int causal;
 };
@@ -163,7 +165,8 @@ struct KvCtx {
   const uint16_t* q;     // Q of batch b, head 0
   const uint16_t* dout;  // dO of batch b, head 0
   const float2* rt;      // row terms of batch b, head 0 (rows padded to Np)
-  int N, Np, g, h0, qt0, kb, causal, wave, first;  // first: the first step this wave computes
+  int64_t stride, rt_stride;  // rows between heads of Q/dO and of the row terms
+  int N, g, h0, qt0, kb, causal, wave, first;  // N: this sequence; first: the first step this wave computes
   float c;
   float masked;  // score whose exponent s*c is -inf: -inf * sign(c)
   uint32_t off;
@@ -181,16 +184,16 @@ struct KvState {
 template <int SLOT>
 __device__ __forceinline__ void kv_issue(const KvCtx& cx, int s) {
   const int qt = cx.qt0 + s / cx.g, i = s % cx.g;
-  const size_t head = (size_t)(cx.h0 + i) * cx.N;
+  const size_t head = (size_t)(cx.h0 + i) * cx.stride;
   const int row0 = qt * kTileRows;
   uint8_t* slot = cx.ring.p[SLOT];
-  const float2* rb = cx.rt + (size_t)(cx.h0 + i) * cx.Np;
+  const float2* rb = cx.rt + (size_t)(cx.h0 + i) * cx.rt_stride;
   dma_tile_part(cx.q + head * kD, row0, cx.N, slot + cx.wave * 1024, cx.off);
   dma_tile_part(cx.dout + head * kD, row0, cx.N, slot + kTileBytes + cx.wave * 1024, cx.off);
-  // row terms of the 32 rows (8 B each, whole tiles thanks to the padding)
-  // land in the first 256 B of the area; every wave writes the same bytes
-  // (lanes past 16 write zeros beyond them)
-  const int rem = row0 < cx.Np ? kTileRows * 8 : 0;
+  // row terms of the 32 rows (8 B each; whole tiles stay inside the buffer
+  // thanks to its padding) land in the first 256 B of the area; every wave
+  // writes the same bytes (lanes past 16 write zeros beyond them)
+  const int rem = row0 < cx.N ? kTileRows * 8 : 0;
   __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void*)(rb + row0), (short)0, rem, kBufferWord3);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + kKvRt), 16, (uint32_t)(threadIdx.x & 63) * 16,
@@ -294,7 +297,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
   int bkv, w_in;
   wg_coords(a.spread, a.causal, false, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
-  const int N = a.N;
+  const SeqGeom sg = seq_geom(a.cu, a.T, a.N, b, a.Hq, a.Hkv);
+  const int N = sg.n;
+  const int KB = (N + kTileRows - 1) / kTileRows;  // key (and query) tiles of this sequence
+  if (w_in * kWaves >= KB) return;  // no keys for this workgroup (whole workgroup)
 
   KvCtx cx;
   cx.ring.p[0] = ring0;
@@ -303,11 +309,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
   cx.ring.p[3] = ring3;
   cx.ring.p[4] = ring4;
   cx.ring.p[5] = ring5;
-  cx.q = a.q + (size_t)b * a.Hq * N * kD;
-  cx.dout = a.dout + (size_t)b * a.Hq * N * kD;
-  cx.rt = a.rt + (size_t)b * a.Hq * a.Np;
+  cx.q = a.q + (size_t)sg.q_base * kD;
+  cx.dout = a.dout + (size_t)sg.q_base * kD;
+  cx.rt = a.rt + (a.cu != nullptr ? (size_t)sg.q_base : (size_t)b * a.Hq * a.Np);
+  cx.stride = sg.stride;
+  cx.rt_stride = a.Np;
   cx.N = N;
-  cx.Np = a.Np;
   const HeadGroup hg = head_group(kvh, a.Hq, a.Hkv);
   cx.g = hg.count;
   cx.h0 = hg.first;
@@ -319,15 +326,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
   cx.masked = a.c > 0.f ? -INFINITY : INFINITY;
   cx.off = dma_off_shared(wave, lane);
   cx.ro = read_offsets_shared(lane);
-  const bool wave_valid = cx.kb < a.KB;
-  const int nsteps = max(a.NQT - cx.qt0, 0) * cx.g;
+  const bool wave_valid = cx.kb < KB;
+  const int nsteps = max(KB - cx.qt0, 0) * cx.g;
   // causal: this wave's keys are first seen by query tile kb, i.e. step (kb - qt0) * g
   cx.first = !wave_valid ? nsteps : (a.causal ? min((cx.kb - cx.qt0) * cx.g, nsteps) : 0);
 
   KvState w;
   {
     const int u = min(cx.kb * kTileRows + l32, N - 1);
-    const size_t kv_row = ((size_t)bkv * N + u) * kD;
+    const size_t kv_row = ((size_t)(sg.kv_base + (int64_t)kvh * sg.stride) + u) * kD;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
       w.kb_f[ds] = u32x4_t{0u, 0u, 0u, 0u};
@@ -402,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
     default: kv_drain<5>(cx, w, last & 1); break;
   }
   if (u >= N) return;
-  const size_t kv_row = ((size_t)bkv * N + u) * kD;
+  const size_t kv_row = ((size_t)(sg.kv_base + (int64_t)kvh * sg.stride) + u) * kD;
   store_tr_row(a.dk + kv_row, w.acc_k, a.scale, lg);
   store_tr_row(a.dv + kv_row, w.acc_v, 1.0f, lg);
 }
@@ -424,8 +431,10 @@ struct DqArgs {
   const uint16_t* dout;
   const float2* rt;  // row terms, [B*H_q, Np]
   uint16_t* dq;
-  int N, Np, Hq, Hkv, TB, NT, wg_per_bkv, n_bkv, nwg;  // wg_per_bkv: for the largest group
-  int spread;  // uneven head groups: spread_coords order
+  const int* cu;  // packed sequence offsets (nullptr: dense)
+  int64_t T;      // packed: total tokens
+  int N, Np, Hq, Hkv, wg_per_bkv, n_bkv, nwg;  // sized for the longest sequence and the largest group
+  int spread;  // uneven head groups or packed sequences: spread_coords order
   float c, scale;
   int causal;
 };
@@ -523,15 +532,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
   const int slot = w_in * kWaves + wave;
   const HeadGroup hg = head_group(kvh, a.Hq, a.Hkv);
-  const int g = hg.count;
-  if (w_in * kWaves >= a.TB * g) return;  // past this group's rows (whole workgroup)
+  const SeqGeom sg = seq_geom(a.cu, a.T, a.N, b, a.Hq, a.Hkv);
+  const int N = sg.n, g = hg.count;
+  const int TB = (N + kTileRows - 1) / kTileRows;  // 32-row query (and key) tiles of this sequence
+  if (w_in * kWaves >= TB * g) return;  // past this group's rows (whole workgroup)
   const int tb = slot / g, jh = slot % g;
-  const bool wave_valid = tb < a.TB;
+  const bool wave_valid = tb < TB;
   const int h = hg.first + jh;
-  const int N = a.N;
   // key tiles the workgroup streams, and the last one this wave uses
-  const int maxtb = min((w_in * kWaves + kWaves - 1) / g, a.TB - 1);
-  const int nt = a.causal ? maxtb + 1 : a.NT;
+  const int maxtb = min((w_in * kWaves + kWaves - 1) / g, TB - 1);
+  const int nt = a.causal ? maxtb + 1 : TB;
 
   DqCtx cx;
   cx.ring.p[0] = ring0;
@@ -539,11 +549,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
   cx.ring.p[2] = ring2;
   cx.ring.p[3] = ring3;
   cx.ring.p[4] = ring4;
-  cx.kbase = a.k + (size_t)bkv * N * kD;
-  cx.vbase = a.v + (size_t)bkv * N * kD;
+  const int64_t kvrow0 = sg.kv_base + (int64_t)kvh * sg.stride;
+  const int64_t qrow0 = sg.q_base + (int64_t)h * sg.stride;
+  const int64_t rtrow0 = a.cu != nullptr ? sg.q_base + (int64_t)h * a.Np : ((int64_t)b * a.Hq + h) * a.Np;
+  cx.kbase = a.k + (size_t)kvrow0 * kD;
+  cx.vbase = a.v + (size_t)kvrow0 * kD;
   cx.N = N;
   cx.nlim = min(N, nt * kTileRows);
-  cx.last = !wave_valid ? -1 : (a.causal ? tb : a.NT - 1);
+  cx.last = !wave_valid ? -1 : (a.causal ? tb : TB - 1);
   cx.tb = tb;
   cx.causal = a.causal;
   cx.wave = wave;
@@ -554,7 +567,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
   cx.off_tr = dma_off_tr(wave, lane);
   cx.ro = read_offsets(lane);
 
-  const size_t row_q = ((size_t)b * a.Hq + h) * N + min(cx.t, N - 1);
+  const size_t row_q = (size_t)qrow0 + min(cx.t, N - 1);
   DqState w;
 #pragma unroll
   for (int ds = 0; ds < 4; ++ds) {
@@ -566,7 +579,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
   if (wave_valid) {
     load_row_frags(a.q + row_q * kD, lg, w.qf);
     load_row_frags(a.dout + row_q * kD, lg, w.df);
-    const float2 r = a.rt[((size_t)b * a.Hq + h) * a.Np + min(cx.t, N - 1)];
+    const float2 r = a.rt[(size_t)rtrow0 + min(cx.t, N - 1)];
     w.lse2 = r.x;
     w.dd = r.y;
   }
@@ -631,7 +644,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
   // drain dQ^T += K(last)^T dS(last)^T
   if (cx.last & 1) mfma_tr(w.kt, w.dsk[1], w.acc);
   else mfma_tr(w.kt, w.dsk[0], w.acc);
-  store_tr_row(a.dq + (((size_t)b * a.Hq + h) * N + cx.t) * kD, w.acc, a.scale, lg);
+  store_tr_row(a.dq + ((size_t)qrow0 + cx.t) * kD, w.acc, a.scale, lg);
 }
 
 }  // namespace
@@ -641,26 +654,37 @@ size_t attn_bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N) {
   return (size_t)(B * Hq * Np) * sizeof(float2);
 }
 
+// Packed sequences: row terms [H_q, T + 32]; a 32-row tile read from any
+// row of any sequence then stays inside the buffer.
+size_t attn_bwd_rowterm_bytes_packed(int64_t Hq, int64_t T) { return (size_t)(Hq * (T + kTileRows)) * sizeof(float2); }
+
 hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream) {
   if (p.D != kD) return hipErrorInvalidValue;
   if (p.N * kRowBytes > 0x7fffffffLL) return hipErrorInvalidValue;  // buffer descriptor range
-  const int N = (int)p.N;
-  const int Np = (N + kTileRows - 1) / kTileRows * kTileRows;
+  const bool packed = p.cu_seqlens != nullptr;
+  const int N = (int)p.N;  // the (longest) sequence
+  // row-term rows per head: dense, N padded to whole tiles; packed, T + 32
+  const int64_t Np64 = packed ? p.T + kTileRows : (p.N + kTileRows - 1) / kTileRows * kTileRows;
+  if (Np64 > 0x7fffffff) return hipErrorInvalidValue;
+  const int Np = (int)Np64;
   // c = scale * log2(e), kept away from 0 so that a masked score (+-inf)
   // times c is -inf; at scale 0 the scores s*c stay below 1e-22 in
   // magnitude and round away exactly as 0 would
   float c = p.scale * kLog2e;
   if (fabsf(c) < 1e-30f) c = p.scale < 0.f ? -1e-30f : 1e-30f;
   float2* rt = static_cast<float2*>(p.rowterms);
+  const int spread = (packed || p.Hq % p.Hkv != 0) ? 1 : 0;
+  const int n_bkv = (int)(p.B * p.Hkv);
 
   {
+    // a packed batch is, for the row terms, one sequence of T tokens
     RowArgs a;
     a.o = static_cast<const uint16_t*>(p.o);
     a.dout = static_cast<const uint16_t*>(p.dout);
     a.lse = p.lse;
     a.rt = rt;
-    a.nrows = p.B * p.Hq * Np;
-    a.N = N;
+    a.nrows = (packed ? 1 : p.B) * p.Hq * Np64;
+    a.N = packed ? (int)p.T : N;
     a.Np = Np;
     const int64_t nblk = (a.nrows + 31) / 32;
     if (nblk > 0x7fffffff) return hipErrorInvalidValue;
@@ -668,6 +692,7 @@ hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const int tiles = (N + kTileRows - 1) / kTileRows;  // of the longest sequence
   {
     KvArgs a;
     a.q = static_cast<const uint16_t*>(p.q);
@@ -677,15 +702,15 @@ hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream) {
     a.rt = rt;
     a.dk = static_cast<uint16_t*>(p.dk);
     a.dv = static_cast<uint16_t*>(p.dv);
+    a.cu = p.cu_seqlens;
+    a.T = p.T;
     a.N = N;
     a.Np = Np;
     a.Hq = (int)p.Hq;
     a.Hkv = (int)p.Hkv;
-    a.spread = p.Hq % p.Hkv != 0 ? 1 : 0;
-    a.KB = (N + kTileRows - 1) / kTileRows;
-    a.NQT = a.KB;
-    a.wg_per_bkv = (a.KB + kWaves - 1) / kWaves;
-    a.n_bkv = (int)(p.B * p.Hkv);
+    a.spread = spread;
+    a.wg_per_bkv = (tiles + kWaves - 1) / kWaves;
+    a.n_bkv = n_bkv;
     const int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     a.nwg = (int)nwg;
@@ -704,16 +729,16 @@ hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream) {
     a.dout = static_cast<const uint16_t*>(p.dout);
     a.rt = rt;
     a.dq = static_cast<uint16_t*>(p.dq);
+    a.cu = p.cu_seqlens;
+    a.T = p.T;
     a.N = N;
     a.Np = Np;
     a.Hq = (int)p.Hq;
     a.Hkv = (int)p.Hkv;
-    a.spread = p.Hq % p.Hkv != 0 ? 1 : 0;
-    a.TB = (N + kTileRows - 1) / kTileRows;
-    a.NT = a.TB;
-    const int64_t slots = (int64_t)a.TB * max_group(a.Hq, a.Hkv);
+    a.spread = spread;
+    const int64_t slots = (int64_t)tiles * max_group(a.Hq, a.Hkv);
     a.wg_per_bkv = (int)((slots + kWaves - 1) / kWaves);
-    a.n_bkv = (int)(p.B * p.Hkv);
+    a.n_bkv = n_bkv;
     const int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     a.nwg = (int)nwg;

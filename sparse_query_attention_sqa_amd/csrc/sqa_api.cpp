@@ -184,6 +184,60 @@ sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void*
   return SQA_OK;
 }
 
+size_t sqa_attn_bwd_varlen_workspace_bytes(int64_t B, int64_t H_q, int64_t T, int64_t d, int dtype) {
+  if (B <= 0 || H_q <= 0 || T <= 0 || d != 64 || dtype != SQA_BF16) return 0;
+  if (T > kMaxN || T * H_q * d > kMaxElems) return 0;
+  return round256(sqa::attn_bwd_rowterm_bytes_packed(H_q, T));
+}
+
+sqa_status sqa_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                               const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
+                               int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t max_seqlen, int64_t d,
+                               int dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  g_err.clear();
+  if (B < 0 || T < 0 || max_seqlen < 0) return fail(SQA_ERR_SHAPE, "negative size");
+  sqa_status s = check_attn(B > 0 ? 1 : 0, H_q, H_kv, max_seqlen, d, dtype, scale, causal);
+  if (s != SQA_OK) return s;
+  if (dtype != SQA_BF16 || d != 64)
+    return fail(SQA_ERR_UNSUPPORTED, "backward supports bf16 with d=64 only (got dtype %d, d=%lld)", dtype,
+                (long long)d);
+  if (max_seqlen > T) return fail(SQA_ERR_SHAPE, "max_seqlen=%lld exceeds T=%lld", (long long)max_seqlen,
+                                  (long long)T);
+  if (T > kMaxN || T * H_q * d > kMaxElems) return fail(SQA_ERR_SHAPE, "tensor too large");
+  if (B == 0 || T == 0 || max_seqlen == 0) return SQA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens)
+    return fail(SQA_ERR_NULL, "q, k, v, o, dout, lse, dq, dk, dv and cu_seqlens must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(SQA_ERR_ALIGN, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(cu_seqlens, 4)) return fail(SQA_ERR_ALIGN, "lse and cu_seqlens must be 4-byte aligned");
+  const size_t need = sqa_attn_bwd_varlen_workspace_bytes(B, H_q, T, d, dtype);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SQA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(SQA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  const size_t nq = (size_t)(H_q * T * d) * 2, nkv = (size_t)(H_kv * T * d) * 2;
+  const size_t nl = (size_t)(H_q * T) * 4, ncu = (size_t)(B + 1) * 4;
+  const void* ins[7] = {q, k, v, o, dout, lse, cu_seqlens};
+  const size_t in_n[7] = {nq, nkv, nkv, nq, nq, nl, ncu};
+  const void* outs[4] = {dq, dk, dv, workspace};
+  const size_t out_n[4] = {nq, nkv, nkv, need};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 7; ++b)
+      if (overlaps(outs[a], out_n[a], ins[b], in_n[b]))
+        return fail(SQA_ERR_ARG, "an output or the workspace overlaps an input");
+    for (int b = a + 1; b < 4; ++b)
+      if (overlaps(outs[a], out_n[a], outs[b], out_n[b]))
+        return fail(SQA_ERR_ARG, "outputs and workspace must not overlap each other");
+  }
+  sqa::BwdProblem p{q,  k,  v,  o,   dout, lse,       dq,    dk,     dv,         workspace,
+                    B,  H_q, H_kv, max_seqlen, d, scale, causal, cu_seqlens, T};
+  hipError_t e = sqa::launch_attn_bwd_bf16_d64(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
+  return SQA_OK;
+}
+
 size_t sqa_layer_workspace_bytes(int64_t B, int64_t N, int64_t D, int64_t H, int64_t H_q, int64_t H_kv,
                                  int dtype) {
   if (B <= 0 || N <= 0 || D <= 0 || H <= 0 || H_q <= 0 || H_kv <= 0) return 0;

@@ -211,6 +211,36 @@ def test_bwd_zero_size_is_a_noop(lib):
     assert _bwd(lib, N=0, ws=None) == 0
 
 
+def test_bwd_varlen_workspace_bytes(lib):
+    # 8 B per (query head, packed row), plus 32 padding rows per head
+    assert sqa.sqa_attn_bwd_varlen_workspace_bytes(3, 8, 1000, 64) == 8 * 8 * 1032
+    assert sqa.sqa_attn_bwd_varlen_workspace_bytes(1, 1, 1, 64) == 512   # 33 rows x 8 B, rounded up
+    assert sqa.sqa_attn_bwd_varlen_workspace_bytes(0, 8, 1000, 64) == 0
+    assert sqa.sqa_attn_bwd_varlen_workspace_bytes(2, 8, 1000, 128) == 0
+
+
+def _bwd_varlen(lib, q=FAKE, cu=FAKE + 0xa00000, dq=FAKE + 0x600000, B=2, Hq=8, Hkv=4, T=1024, maxlen=600,
+                d=64, dtype=1, ws=FAKE + 0x900000, ws_bytes=1 << 20):
+    return lib.sqa_attn_bwd_varlen(q, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
+                                   FAKE + 0x500000, dq, FAKE + 0x700000, FAKE + 0x800000, cu, B, Hq, Hkv, T,
+                                   maxlen, d, dtype, 0.125, 1, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(cu=None), 1), (dict(dq=None), 1),
+    (dict(B=-1), 2), (dict(maxlen=2000), 2), (dict(Hkv=9), 2),
+    (dict(d=32), 3), (dict(dtype=0), 3),
+    (dict(cu=FAKE + 0xa00002), 4), (dict(ws=FAKE + 0x900008), 4),
+    (dict(ws=None), 5), (dict(ws_bytes=100), 5),
+    (dict(dq=FAKE + 0x100000), 7),                   # dq overlaps k
+    (dict(ws=FAKE + 0xa00000), 7),                   # workspace overlaps cu_seqlens
+])
+@cpu_only
+def test_bwd_varlen_rejects_invalid_arguments(lib, kw, code):
+    assert _bwd_varlen(lib, **kw) == code
+    assert lib.sqa_last_error().decode() != ""
+
+
 # ------------------------------------------------------------------ block
 def test_block_workspace_bytes(lib):
     # SQAT-m block B=16 N=1024 D=256 (8,4) F=768: the layer's workspace plus the

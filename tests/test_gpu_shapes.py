@@ -232,3 +232,73 @@ def test_varlen32k_all_rows(causal):
     label = f"{w.name} (8,4) causal={causal} lens={lens.tolist()}"
     log(f"[case] {label}")
     _check_varlen(q, k, v, cu, "bf16", w.scale, causal, label)
+
+
+# ------------------------------------------------- packed-batch backward
+def _varlen_bwd_run(q, k, v, do, cu, scale, causal):
+    tq, tk, tv, tdo = (to_dev(a, "bf16") for a in (q, k, v, do))
+    tcu = torch.from_numpy(cu).to("cuda")
+    o, lse = sqa.sqa_attn_fwd_varlen(tq, tk, tv, tcu, scale=scale, causal=bool(causal), return_lse=True)
+    g = sqa.sqa_attn_bwd_varlen(tq, tk, tv, o, tdo, lse, tcu, scale=scale, causal=bool(causal))
+    torch.cuda.synchronize()
+    return tuple(to_host(x) for x in g)
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("mix", sorted(LEN_MIXES))
+@pytest.mark.parametrize("Hq,Hkv", [(8, 4), (6, 4)])
+def test_bwd_varlen_all_elements(Hq, Hkv, mix, causal):
+    from oracle import attention_bwd_varlen
+    label = f"bwd varlen {mix} Hq={Hq} Hkv={Hkv} causal={causal}"
+    log(f"[case] {label}")
+    q, k, v, cu = draw_varlen(LEN_MIXES[mix], Hq, Hkv, 64, "bf16", seed=len(mix) * 3 + Hq)
+    do = draw_upstream(q.shape, "bf16", seed=len(mix) + 41)
+    got = _varlen_bwd_run(q, k, v, do, cu, 0.125, causal)
+    ref = attention_bwd_varlen(q, k, v, do, cu, scale=0.125, causal=bool(causal), threads=oracle_threads())
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        check_global(g, r, "bf16", f"{label} {name}", floor=ROW_FLOOR)
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_bwd_varlen_one_sequence_equals_dense_bitwise(causal):
+    q, k, v, cu = draw_varlen([901], 8, 4, 64, "bf16", seed=77)
+    do = draw_upstream(q.shape, "bf16", seed=78)
+    gv = _varlen_bwd_run(q, k, v, do, cu, 0.125, causal)
+    tq, tk, tv, tdo = (to_dev(a[None], "bf16") for a in (q, k, v, do))
+    o, lse = sqa.sqa_attn_fwd(tq, tk, tv, scale=0.125, causal=bool(causal), return_lse=True)
+    gd = sqa.sqa_attn_bwd(tq, tk, tv, o, tdo, lse, scale=0.125, causal=bool(causal))
+    torch.cuda.synchronize()
+    for a, b in zip(gv, gd):
+        assert np.array_equal(a, to_host(b)[0])
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_bwd_varlen32k(causal):
+    from oracle import attention_bwd_varlen
+    w = WORKLOADS["varlen32k_bf16"]
+    lens = varlen_lengths(w.N, w.varlen)
+    q, k, v, cu = draw_varlen(lens, w.H, w.H, w.d, "bf16", seed=0)
+    q, k, v = q[:8], k[:4], v[:4]
+    do = draw_upstream(q.shape, "bf16", seed=56)
+    label = f"bwd {w.name} (8,4) causal={causal}"
+    log(f"[case] {label}")
+    got = _varlen_bwd_run(q, k, v, do, cu, w.scale, causal)
+    log(f"[oracle] {label}")
+    ref = attention_bwd_varlen(q, k, v, do, cu, scale=w.scale, causal=bool(causal), threads=oracle_threads())
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        check_global(g, r, "bf16", f"{label} {name}", floor=ROW_FLOOR)
+
+
+def test_bwd_varlen_error_paths():
+    q, k, v, cu = draw_varlen([10, 20], 8, 4, 64, "bf16", seed=3)
+    tq, tk, tv = (to_dev(a, "bf16") for a in (q, k, v))
+    tcu = torch.from_numpy(cu).to("cuda")
+    o, lse = sqa.sqa_attn_fwd_varlen(tq, tk, tv, tcu, 20, return_lse=True)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sqa.SQAError) as e:
+        sqa.sqa_attn_bwd_varlen(tq, tk, tv, o, o, lse, tcu, 20, workspace=small)
+    assert e.value.status == 5
+    with pytest.raises(sqa.SQAError) as e:
+        sqa.sqa_attn_bwd_varlen(tq, tk, tv, o, o, lse, tcu, 31)   # max_seqlen > T
+    assert e.value.status == 2
+    torch.cuda.synchronize()
