@@ -314,6 +314,25 @@ def bench_varlen(sqa, torch, w, args):
 
     ms = run(variant)
     tflops = flops(variant[0]) / (ms * 1e-3) / 1e12
+    backward = None
+    if not args.no_backward and w.d == 64:
+        from synth import draw_upstream
+        hq, hkv = variant
+        q, k, v = dev(q_all[:hq]), dev(k_all[:hkv]), dev(v_all[:hkv])
+        o, lse = sqa.sqa_attn_fwd_varlen(q, k, v, tcu, maxlen, scale=w.scale, causal=bool(causal), return_lse=True)
+        do = dev(draw_upstream(tuple(q.shape), "bf16", seed=55))
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(sqa.sqa_attn_bwd_varlen_workspace_bytes(w.varlen, hq, w.N, w.d), dtype=torch.uint8,
+                         device="cuda")
+        fn = lambda: sqa.sqa_attn_bwd_varlen(q, k, v, o, do, lse, tcu, maxlen, scale=w.scale, causal=bool(causal),
+                                             dq=dq, dk=dk, dv=dv, workspace=ws)
+        bms = _timed(torch, fn, args.steps, args.warmup)
+        counted = 2.5 * flops(hq)
+        backward = {"ms": round(bms, 4), "counted_flop": counted,
+                    "tflops_counted": round(counted / (bms * 1e-3) / 1e12, 2),
+                    "frac_of_peak_counted": round(counted / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del q, k, v, o, lse, do, dq, dk, dv, ws
+        torch.cuda.empty_cache()
     comparison = None
     if not args.no_compare:
         comparison = {}
@@ -333,7 +352,7 @@ def bench_varlen(sqa, torch, w, args):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": kernel, "per_launch_flop": flops(variant[0])},
-        "cpu_baseline": None, "comparison": comparison})
+        "cpu_baseline": None, "comparison": comparison, "backward": backward})
 
 
 def main():
