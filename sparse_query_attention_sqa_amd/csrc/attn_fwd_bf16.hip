@@ -1,5 +1,6 @@
 // SQA attention forward, bf16 in/out, fp32 softmax state, for gfx950: the
-// kernel for head dims 16, 32 and 128 (64 has its own pipelined kernel).
+// kernel for head dims 16 and 32 (64 and 128 have their own pipelined
+// kernels).
 //
 // What is computed: per query head i and position t, softmax attention over
 // the keys of K/V head floor(i*H_kv/H_q) (contiguous query-head groups as in
@@ -65,8 +66,7 @@ constexpr int kXcds = 8;
 
 template <int D>
 struct Cfg {
-  static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head dim");
-  static constexpr int MINB = D >= 128 ? 1 : 2;    // workgroups per CU the registers allow
+  static_assert(D == 16 || D == 32, "head dim");
   static constexpr int DSTEPS = D / 16;            // MFMA k-steps over d for S^T
   static constexpr int DSUB = (D + 31) / 32;       // 32-row O^T tiles over d
   static constexpr int KROW = D + 8;               // LDS pitch of a K row (bf16)
@@ -300,7 +300,7 @@ __device__ __forceinline__ void process_tile(const uint16_t* ks, const u32x4_t (
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_fwd_bf16_kernel(Args a) {
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Args a) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
 
