@@ -315,7 +315,7 @@ def bench_varlen(sqa, torch, w, args):
     ms = run(variant)
     tflops = flops(variant[0]) / (ms * 1e-3) / 1e12
     backward = None
-    if not args.no_backward and w.d == 64:
+    if not args.no_backward and w.d in (64, 128):
         from synth import draw_upstream
         hq, hkv = variant
         q, k, v = dev(q_all[:hq]), dev(k_all[:hkv]), dev(v_all[:hkv])
@@ -458,7 +458,7 @@ def main():
             comparison["expected_H_over_Hq"] = w.H / Hq
 
     backward = None
-    if not args.no_backward and w.d == 64:
+    if not args.no_backward and w.d in (64, 128):
         q, k, v = (dev(a) for a in select_variant(q_all, k_all, v_all, *variant))
         backward = bench_backward(sqa, torch, q, k, v, w, causal, args.steps, args.warmup)
         del q, k, v

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsqa.so")
 
-SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_bf16_d64.hip", "attn_fwd_bf16_d128.hip", "attn_fwd_f32.hip", "attn_bwd_bf16_d64.hip",
+SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_bf16_d64.hip", "attn_fwd_bf16_d128.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip",
            "gemm_bf16.hip", "norm_rope.hip", "sqa_api.cpp"]
 
 

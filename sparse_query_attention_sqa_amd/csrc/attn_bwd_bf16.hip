@@ -1,4 +1,4 @@
-// SQA attention backward for head dim 64, bf16 in/out, gfx950.
+// SQA attention backward for head dims 64 and 128, bf16 in/out, gfx950.
 //
 // Operation: the exact derivative of the forward (query head i attends K/V
 // head floor(i*H_kv/H_q), "GQA ..." page, "The idea"; fewer query heads than
@@ -23,12 +23,16 @@
 //      rows (Q, dO in registers) and streams K/V tiles: S^T = K Q^T,
 //      dP^T = V dO^T, dQ^T += K^T dS^T.
 // Both streamed operands are DMA'd HBM -> LDS (buffer_load ... lds) into a
-// ring, each tile in the two layouts of bf16_tiles.h (row layout for row
-// fragments, transposed layout for ds_read_b64_tr_b16), with one barrier per
-// tile. Every DMA is issued unconditionally -- tiles past the last one needed
-// get an empty descriptor range and cost no memory traffic -- so the explicit
+// ring of tiles in the layouts of bf16_tiles.h, with one barrier per tile.
+// Every DMA is issued unconditionally -- tiles past the last one needed get
+// an empty descriptor range and cost no memory traffic -- so the explicit
 // vmcnt waits are exact. P and dS are rounded to bf16 (nearest even) for the
 // MFMA products; everything else accumulates in fp32.
+//
+// Head dim 128 (DH = 2 halves of 64): every 32-row tile is stored as two
+// 64-wide half-tiles, products over the head dim add the two halves, and the
+// dK/dV and dQ accumulators hold four 32-dim tiles. The same code then needs
+// about twice the registers, so the d = 128 kernels run one wave per SIMD.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -60,6 +64,14 @@ __device__ __forceinline__ void barrier_vm() {
   asm volatile("" ::: "memory");
 }
 
+// Per head-dim width: DH halves of 64.
+template <int DH>
+struct Dims {
+  static constexpr int D = kD * DH;           // elements per row
+  static constexpr int RB = kRowBytes * DH;   // bytes per row in HBM
+  static constexpr int MINB = DH == 1 ? 2 : 1;  // workgroups per CU the registers allow
+};
+
 // ------------------------------------------------------------------ row terms
 struct RowArgs {
   const uint16_t* o;
@@ -70,10 +82,13 @@ struct RowArgs {
   int N, Np;
 };
 
-// Eight lanes per query row: each forms the products of 8 bf16 pairs exactly
-// (v_dot2_f32_bf16) and the eight partial sums are added with lane shuffles.
-// Padding rows (t >= N) get (0, 0), so row-term tiles are always whole.
+// Eight lanes per query row: each forms the products of 8*DH bf16 pairs
+// exactly (v_dot2_f32_bf16) and the eight partial sums are added with lane
+// shuffles. Padding rows (t >= N) get (0, 0), so row-term tiles are always
+// whole.
+template <int DH>
 __global__ __launch_bounds__(256) void bwd_rowterms_kernel(RowArgs a) {
+  constexpr int D = Dims<DH>::D;
   const int64_t prow = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int part = threadIdx.x & 7;
   const int64_t bh = prow / a.Np;
@@ -82,15 +97,18 @@ __global__ __launch_bounds__(256) void bwd_rowterms_kernel(RowArgs a) {
   const int64_t row = bh * a.N + t;
   float acc = 0.f;
   if (valid) {
-    const u32x4_t ov = *reinterpret_cast<const u32x4_t*>(a.o + row * kD + part * 8);
-    const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(a.dout + row * kD + part * 8);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // copy the elements out first: a bit cast of a vector-element
-      // expression reads element 0
-      const uint32_t ow = ov[w], dw = dv[w];
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ow), __builtin_bit_cast(bf16x2_t, dw), acc,
-                                            false);
+    for (int h = 0; h < DH; ++h) {
+      const u32x4_t ov = *reinterpret_cast<const u32x4_t*>(a.o + row * D + h * kD + part * 8);
+      const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(a.dout + row * D + h * kD + part * 8);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // copy the elements out first: a bit cast of a vector-element
+        // expression reads element 0
+        const uint32_t ow = ov[w], dw = dv[w];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ow), __builtin_bit_cast(bf16x2_t, dw),
+                                              acc, false);
+      }
     }
   }
   acc += __shfl_xor(acc, 1);
@@ -103,7 +121,8 @@ __global__ __launch_bounds__(256) void bwd_rowterms_kernel(RowArgs a) {
 // Encoder-style: consecutive logical workgroups on one XCD (they share the
 // streamed operand in L2). Causal: workgroups launch largest-work first,
 // which is ascending w_in, or descending with `reverse`. Uneven head groups
-// (`spread`): the spread_coords order, which deals every group over all XCDs.
+// or packed sequences (`spread`): the spread_coords order, which deals every
+// group and sequence over all XCDs.
 __device__ __forceinline__ void wg_coords(int spread, int causal, bool reverse, int nwg, int wg_per_bkv,
                                           int n_bkv, int& bkv, int& w_in) {
   if (spread) {
@@ -123,6 +142,20 @@ __device__ __forceinline__ void wg_coords(int spread, int causal, bool reverse, 
   }
 }
 
+// acc (+)= sum over the DH halves of A_rows(h) . B(h).
+template <int DH>
+__device__ __forceinline__ f32x16_t mfma_rows(const uint8_t* tile0, const ReadOffsets& ro, const u32x4_t (&b)[DH][4]) {
+  f32x16_t acc = zero16();
+#pragma unroll
+  for (int h = 0; h < DH; ++h) {
+    u32x4_t a[4];
+    read_rows(tile0 + h * kTileBytes, ro, a);
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) acc = mfma(a[ds], b[h][ds], acc);
+  }
+  return acc;
+}
+
 // ------------------------------------------------------------------ dK, dV
 // A step s is one 32-row query tile of one query head of the group (steps
 // ordered by query tile, then head). Software-pipelined over steps:
@@ -130,15 +163,21 @@ __device__ __forceinline__ void wg_coords(int spread, int causal, bool reverse, 
 //                  interleaved with
 //            VALU  P(s) = 2^(s c - lse2), dS(s) = P (dP - D);
 //            then MFMA S(s+1) = Q K^T, dP(s+1) = dO V^T into the registers
-//            the softmax has just consumed (one score buffer keeps the wave
-//            at two waves per SIMD).
+//            the softmax has just consumed (one score buffer keeps the d = 64
+//            wave at two waves per SIMD).
 // Q and dO of a step sit in LDS once each, in the shared layout of
-// bf16_tiles.h (row reads for S and dP, transposed reads for dK and dV), so a
-// ring slot is 9 KB and six slots give four steps of lookahead.
-constexpr int kKvBuf = 6;                       // ring slots
-constexpr int kKvRt = 2 * kTileBytes;           // row-term area offset
-constexpr int kKvSlot = 2 * kTileBytes + 1024;  // Q | dO | row terms
-constexpr int kKvDma = 3;                       // DMA instructions per wave per step
+// bf16_tiles.h (row reads for S and dP, transposed reads for dK and dV); six
+// ring slots give four steps of lookahead.
+constexpr int kKvBuf = 6;  // ring slots
+
+template <int DH>
+struct KvCfg {
+  static constexpr int kQ = 0;                            // Q half-tiles
+  static constexpr int kDo = DH * kTileBytes;             // dO half-tiles
+  static constexpr int kRt = 2 * DH * kTileBytes;         // row terms
+  static constexpr int kSlot = 2 * DH * kTileBytes + 1024;
+  static constexpr int kDma = 2 * DH + 1;                 // DMA instructions per wave per step
+};
 
 struct KvArgs {
   const uint16_t* q;
@@ -162,9 +201,9 @@ struct KvRing {
 
 struct KvCtx {
   KvRing ring;
-  const uint16_t* q;     // Q of batch b, head 0
-  const uint16_t* dout;  // dO of batch b, head 0
-  const float2* rt;      // row terms of batch b, head 0 (rows padded to Np)
+  const uint16_t* q;     // Q of sequence b, head 0
+  const uint16_t* dout;  // dO of sequence b, head 0
+  const float2* rt;      // row terms of sequence b, head 0
   int64_t stride, rt_stride;  // rows between heads of Q/dO and of the row terms
   int N, g, h0, qt0, kb, causal, wave, first;  // N: this sequence; first: the first step this wave computes
   float c;
@@ -173,62 +212,85 @@ struct KvCtx {
   ReadOffsets ro;
 };
 
+template <int DH>
 struct KvState {
-  u32x4_t kb_f[4], vb_f[4];     // K and V rows of this wave's 32 keys as B operands
-  f32x16_t acc_k[2], acc_v[2];  // dK^T, dV^T
-  f32x16_t sc, dp;              // S and dP of the current step
-  u32x4_t pk[2][2], dsk[2][2];  // P and dS of steps s-1 and s, packed as B operands
+  u32x4_t kb_f[DH][4], vb_f[DH][4];   // K and V rows of this wave's 32 keys as B operands
+  f32x16_t acc_k[DH][2], acc_v[DH][2];  // dK^T, dV^T
+  f32x16_t sc, dp;                      // S and dP of the current step
+  u32x4_t pk[2][2], dsk[2][2];          // P and dS of steps s-1 and s, packed as B operands
 };
 
 // DMA step s (query tile qt of query head h0 + i) into ring slot SLOT.
-template <int SLOT>
+template <int DH, int SLOT>
 __device__ __forceinline__ void kv_issue(const KvCtx& cx, int s) {
+  using C = KvCfg<DH>;
+  constexpr int RB = Dims<DH>::RB;
   const int qt = cx.qt0 + s / cx.g, i = s % cx.g;
   const size_t head = (size_t)(cx.h0 + i) * cx.stride;
   const int row0 = qt * kTileRows;
   uint8_t* slot = cx.ring.p[SLOT];
   const float2* rb = cx.rt + (size_t)(cx.h0 + i) * cx.rt_stride;
-  dma_tile_part(cx.q + head * kD, row0, cx.N, slot + cx.wave * 1024, cx.off);
-  dma_tile_part(cx.dout + head * kD, row0, cx.N, slot + kTileBytes + cx.wave * 1024, cx.off);
+#pragma unroll
+  for (int h = 0; h < DH; ++h) {
+    dma_tile_part<RB>(cx.q + head * Dims<DH>::D, row0, cx.N, slot + C::kQ + h * kTileBytes + cx.wave * 1024,
+                      cx.off + h * kRowBytes);
+    dma_tile_part<RB>(cx.dout + head * Dims<DH>::D, row0, cx.N, slot + C::kDo + h * kTileBytes + cx.wave * 1024,
+                      cx.off + h * kRowBytes);
+  }
   // row terms of the 32 rows (8 B each; whole tiles stay inside the buffer
   // thanks to its padding) land in the first 256 B of the area; every wave
   // writes the same bytes (lanes past 16 write zeros beyond them)
   const int rem = row0 < cx.N ? kTileRows * 8 : 0;
   __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void*)(rb + row0), (short)0, rem, kBufferWord3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + kKvRt), 16, (uint32_t)(threadIdx.x & 63) * 16,
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + C::kRt), 16, (uint32_t)(threadIdx.x & 63) * 16,
                                            0, 0, 0);
 }
 
 // S and dP of the step in slot SLOT.
-template <int SLOT>
-__device__ __forceinline__ void kv_scores(const KvCtx& cx, KvState& w) {
-  u32x4_t a[4];
-  read_rows(cx.ring.p[SLOT], cx.ro, a);
-  w.sc = mfma_k64(a, w.kb_f);
-  read_rows(cx.ring.p[SLOT] + kTileBytes, cx.ro, a);
-  w.dp = mfma_k64(a, w.vb_f);
+template <int DH, int SLOT>
+__device__ __forceinline__ void kv_scores(const KvCtx& cx, KvState<DH>& w) {
+  using C = KvCfg<DH>;
+  w.sc = mfma_rows<DH>(cx.ring.p[SLOT] + C::kQ, cx.ro, w.kb_f);
+  w.dp = mfma_rows<DH>(cx.ring.p[SLOT] + C::kDo, cx.ro, w.vb_f);
 }
 
-// Scheduling hints: 8 MFMAs, each followed by 8 VALU instructions of the
-// independent softmax work.
-__device__ __forceinline__ void kv_interleave() {
+// dV^T += dO^T P and dK^T += Q^T dS for the step in `slot`.
+template <int DH>
+__device__ __forceinline__ void kv_grads(const uint8_t* slot, const ReadOffsets& ro, const u32x4_t (&pk)[2],
+                                         const u32x4_t (&dsk)[2], KvState<DH>& w) {
+  using C = KvCfg<DH>;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+  for (int h = 0; h < DH; ++h) {
+    u32x4_t qt_f[2][2], dt_f[2][2];
+    read_tr_shared(slot + C::kQ + h * kTileBytes, ro, qt_f);
+    read_tr_shared(slot + C::kDo + h * kTileBytes, ro, dt_f);
+    mfma_tr(dt_f, pk, w.acc_v[h]);
+    mfma_tr(qt_f, dsk, w.acc_k[h]);
   }
 }
 
-template <int SLOT, int P>
-__device__ __forceinline__ void kv_phase(const KvCtx& cx, KvState& w, int s) {
+// Scheduling hints: 8*DH MFMAs, each followed by 8/DH VALU instructions of
+// the independent softmax work.
+template <int DH>
+__device__ __forceinline__ void kv_interleave() {
+#pragma unroll
+  for (int i = 0; i < 8 * DH; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 8 / DH, 0);  // VALU
+  }
+}
+
+template <int DH, int SLOT, int P>
+__device__ __forceinline__ void kv_phase(const KvCtx& cx, KvState<DH>& w, int s) {
+  using C = KvCfg<DH>;
   constexpr int AHEAD = (SLOT + 4) % kKvBuf;
   constexpr int PREV = (SLOT + kKvBuf - 1) % kKvBuf;
   constexpr int NEXT = (SLOT + 1) % kKvBuf;
   // step s+1 has landed (steps s+2, s+3 may still be in flight); every wave
   // is done with step s-2, whose slot receives step s+4
-  barrier_vm<2 * kKvDma>();
-  kv_issue<AHEAD>(cx, s + 4);
+  barrier_vm<2 * C::kDma>();
+  kv_issue<DH, AHEAD>(cx, s + 4);
   const int lane = threadIdx.x & 63, lg = lane >> 5, l32 = lane & 31;
   // Masks of S(s). Steps before the wave's first (causal: query tiles that
   // see none of its keys) run the same code fully masked (P = dS = 0), so
@@ -243,18 +305,14 @@ __device__ __forceinline__ void kv_phase(const KvCtx& cx, KvState& w, int s) {
       if (lg * 16 + e < l32) w.sc[e] = cx.masked;
   }
   float2 rt[16];
-  const float4* rtp = reinterpret_cast<const float4*>(cx.ring.p[SLOT] + kKvRt + lg * 128);
+  const float4* rtp = reinterpret_cast<const float4*>(cx.ring.p[SLOT] + C::kRt + lg * 128);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float4 x = rtp[e];
     rt[2 * e] = make_float2(x.x, x.y);
     rt[2 * e + 1] = make_float2(x.z, x.w);
   }
-  u32x4_t qt_f[2][2], dt_f[2][2];
-  read_tr_shared(cx.ring.p[PREV], cx.ro, qt_f);               // Q(s-1)^T
-  read_tr_shared(cx.ring.p[PREV] + kTileBytes, cx.ro, dt_f);  // dO(s-1)^T
-  mfma_tr(dt_f, w.pk[P ^ 1], w.acc_v);                        // dV^T += dO(s-1)^T P(s-1)
-  mfma_tr(qt_f, w.dsk[P ^ 1], w.acc_k);                       // dK^T += Q(s-1)^T dS(s-1)
+  kv_grads<DH>(cx.ring.p[PREV], cx.ro, w.pk[P ^ 1], w.dsk[P ^ 1], w);  // step s-1
 
   f32x16_t p, ds;
 #pragma unroll
@@ -264,32 +322,27 @@ __device__ __forceinline__ void kv_phase(const KvCtx& cx, KvState& w, int s) {
   }
   pack_pairs(p, w.pk[P]);
   pack_pairs(ds, w.dsk[P]);
-  kv_interleave();
-  kv_scores<NEXT>(cx, w);  // S(s+1), dP(s+1)
+  kv_interleave<DH>();
+  kv_scores<DH, NEXT>(cx, w);  // S(s+1), dP(s+1)
 }
 
-// dV^T += dO(s)^T P(s), dK^T += Q(s)^T dS(s) for the last step, in slot SLOT.
-template <int SLOT>
-__device__ __forceinline__ void kv_drain(const KvCtx& cx, KvState& w, int par) {
-  u32x4_t qt_f[2][2], dt_f[2][2];
-  read_tr_shared(cx.ring.p[SLOT], cx.ro, qt_f);
-  read_tr_shared(cx.ring.p[SLOT] + kTileBytes, cx.ro, dt_f);
-  if (par) {
-    mfma_tr(dt_f, w.pk[1], w.acc_v);
-    mfma_tr(qt_f, w.dsk[1], w.acc_k);
-  } else {
-    mfma_tr(dt_f, w.pk[0], w.acc_v);
-    mfma_tr(qt_f, w.dsk[0], w.acc_k);
-  }
+// dK/dV of the last step, in slot SLOT.
+template <int DH, int SLOT>
+__device__ __forceinline__ void kv_drain(const KvCtx& cx, KvState<DH>& w, int par) {
+  if (par) kv_grads<DH>(cx.ring.p[SLOT], cx.ro, w.pk[1], w.dsk[1], w);
+  else kv_grads<DH>(cx.ring.p[SLOT], cx.ro, w.pk[0], w.dsk[0], w);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring0[kKvSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t ring1[kKvSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t ring2[kKvSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t ring3[kKvSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t ring4[kKvSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t ring5[kKvSlot];
+template <int DH>
+__global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dkdv_kernel(KvArgs a) {
+  using C = KvCfg<DH>;
+  constexpr int D = Dims<DH>::D;
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[C::kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[C::kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[C::kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring3[C::kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring4[C::kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring5[C::kSlot];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -309,8 +362,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
   cx.ring.p[3] = ring3;
   cx.ring.p[4] = ring4;
   cx.ring.p[5] = ring5;
-  cx.q = a.q + (size_t)sg.q_base * kD;
-  cx.dout = a.dout + (size_t)sg.q_base * kD;
+  cx.q = a.q + (size_t)sg.q_base * D;
+  cx.dout = a.dout + (size_t)sg.q_base * D;
   cx.rt = a.rt + (a.cu != nullptr ? (size_t)sg.q_base : (size_t)b * a.Hq * a.Np);
   cx.stride = sg.stride;
   cx.rt_stride = a.Np;
@@ -324,42 +377,47 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
   cx.wave = wave;
   cx.c = a.c;
   cx.masked = a.c > 0.f ? -INFINITY : INFINITY;
-  cx.off = dma_off_shared(wave, lane);
+  cx.off = dma_off_shared<Dims<DH>::RB>(wave, lane);
   cx.ro = read_offsets_shared(lane);
   const bool wave_valid = cx.kb < KB;
   const int nsteps = max(KB - cx.qt0, 0) * cx.g;
   // causal: this wave's keys are first seen by query tile kb, i.e. step (kb - qt0) * g
   cx.first = !wave_valid ? nsteps : (a.causal ? min((cx.kb - cx.qt0) * cx.g, nsteps) : 0);
+  const size_t kv_row0 = (size_t)(sg.kv_base + (int64_t)kvh * sg.stride);
 
-  KvState w;
+  KvState<DH> w;
   {
     const int u = min(cx.kb * kTileRows + l32, N - 1);
-    const size_t kv_row = ((size_t)(sg.kv_base + (int64_t)kvh * sg.stride) + u) * kD;
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) {
-      w.kb_f[ds] = u32x4_t{0u, 0u, 0u, 0u};
-      w.vb_f[ds] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int h = 0; h < DH; ++h) {
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) {
+        w.kb_f[h][ds] = u32x4_t{0u, 0u, 0u, 0u};
+        w.vb_f[h][ds] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      if (wave_valid) {
+        load_row_frags(a.k + (kv_row0 + u) * D + h * kD, lg, w.kb_f[h]);
+        load_row_frags(a.v + (kv_row0 + u) * D + h * kD, lg, w.vb_f[h]);
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        w.acc_k[h][x] = zero16();
+        w.acc_v[h][x] = zero16();
+      }
     }
-    if (wave_valid) {
-      load_row_frags(a.k + kv_row, lg, w.kb_f);
-      load_row_frags(a.v + kv_row, lg, w.vb_f);
-    }
+    // P and dS of the step before a wave's first are 0: its first dK/dV
+    // products add nothing
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      w.acc_k[x] = zero16();
-      w.acc_v[x] = zero16();
-      // P and dS of the step before a wave's first are 0: its first dK/dV
-      // products add nothing
+    for (int par = 0; par < 2; ++par)
 #pragma unroll
-      for (int par = 0; par < 2; ++par) {
+      for (int x = 0; x < 2; ++x) {
         w.pk[par][x] = u32x4_t{0u, 0u, 0u, 0u};
         w.dsk[par][x] = u32x4_t{0u, 0u, 0u, 0u};
       }
-    }
   }
 
   // zero the ring once so that no LDS byte is ever uninitialised
-  for (int e = tid; e < kKvSlot / 16; e += kThreads) {
+  for (int e = tid; e < C::kSlot / 16; e += kThreads) {
     reinterpret_cast<u32x4_t*>(ring0)[e] = u32x4_t{0u, 0u, 0u, 0u};
     reinterpret_cast<u32x4_t*>(ring1)[e] = u32x4_t{0u, 0u, 0u, 0u};
     reinterpret_cast<u32x4_t*>(ring2)[e] = u32x4_t{0u, 0u, 0u, 0u};
@@ -371,47 +429,49 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
 
   // prologue: steps 0..3 in flight (empty ranges past the end), wait for
   // steps 0..2, then S(0) and dP(0)
-  kv_issue<0>(cx, 0);
-  kv_issue<1>(cx, 1);
-  kv_issue<2>(cx, 2);
-  kv_issue<3>(cx, 3);
-  barrier_vm<kKvDma>();
-  kv_scores<0>(cx, w);
+  kv_issue<DH, 0>(cx, 0);
+  kv_issue<DH, 1>(cx, 1);
+  kv_issue<DH, 2>(cx, 2);
+  kv_issue<DH, 3>(cx, 3);
+  barrier_vm<C::kDma>();
+  kv_scores<DH, 0>(cx, w);
 
   // whole six-phase rounds first (ring slot period 6, register parity 2)
   int s = 0;
   for (; s + kKvBuf <= nsteps; s += kKvBuf) {
-    kv_phase<0, 0>(cx, w, s);
-    kv_phase<1, 1>(cx, w, s + 1);
-    kv_phase<2, 0>(cx, w, s + 2);
-    kv_phase<3, 1>(cx, w, s + 3);
-    kv_phase<4, 0>(cx, w, s + 4);
-    kv_phase<5, 1>(cx, w, s + 5);
+    kv_phase<DH, 0, 0>(cx, w, s);
+    kv_phase<DH, 1, 1>(cx, w, s + 1);
+    kv_phase<DH, 2, 0>(cx, w, s + 2);
+    kv_phase<DH, 3, 1>(cx, w, s + 3);
+    kv_phase<DH, 4, 0>(cx, w, s + 4);
+    kv_phase<DH, 5, 1>(cx, w, s + 5);
   }
-  if (s < nsteps) kv_phase<0, 0>(cx, w, s);
-  if (s + 1 < nsteps) kv_phase<1, 1>(cx, w, s + 1);
-  if (s + 2 < nsteps) kv_phase<2, 0>(cx, w, s + 2);
-  if (s + 3 < nsteps) kv_phase<3, 1>(cx, w, s + 3);
-  if (s + 4 < nsteps) kv_phase<4, 0>(cx, w, s + 4);
+  if (s < nsteps) kv_phase<DH, 0, 0>(cx, w, s);
+  if (s + 1 < nsteps) kv_phase<DH, 1, 1>(cx, w, s + 1);
+  if (s + 2 < nsteps) kv_phase<DH, 2, 0>(cx, w, s + 2);
+  if (s + 3 < nsteps) kv_phase<DH, 3, 1>(cx, w, s + 3);
+  if (s + 4 < nsteps) kv_phase<DH, 4, 0>(cx, w, s + 4);
   // drain the DMAs still in flight before the wave ends
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
   const int u = cx.kb * kTileRows + l32;
-  if (cx.first >= nsteps) return;  // no step for this wave (all waves of it: uniform)
+  if (cx.first >= nsteps) return;  // no step for this wave (no barrier follows)
   // dK/dV of the last step (its slot is still intact: later DMAs went elsewhere)
   const int last = nsteps - 1;
   switch (last % kKvBuf) {
-    case 0: kv_drain<0>(cx, w, last & 1); break;
-    case 1: kv_drain<1>(cx, w, last & 1); break;
-    case 2: kv_drain<2>(cx, w, last & 1); break;
-    case 3: kv_drain<3>(cx, w, last & 1); break;
-    case 4: kv_drain<4>(cx, w, last & 1); break;
-    default: kv_drain<5>(cx, w, last & 1); break;
+    case 0: kv_drain<DH, 0>(cx, w, last & 1); break;
+    case 1: kv_drain<DH, 1>(cx, w, last & 1); break;
+    case 2: kv_drain<DH, 2>(cx, w, last & 1); break;
+    case 3: kv_drain<DH, 3>(cx, w, last & 1); break;
+    case 4: kv_drain<DH, 4>(cx, w, last & 1); break;
+    default: kv_drain<DH, 5>(cx, w, last & 1); break;
   }
   if (u >= N) return;
-  const size_t kv_row = ((size_t)(sg.kv_base + (int64_t)kvh * sg.stride) + u) * kD;
-  store_tr_row(a.dk + kv_row, w.acc_k, a.scale, lg);
-  store_tr_row(a.dv + kv_row, w.acc_v, 1.0f, lg);
+#pragma unroll
+  for (int h = 0; h < DH; ++h) {
+    store_tr_row(a.dk + (kv_row0 + u) * D + h * kD, w.acc_k[h], a.scale, lg);
+    store_tr_row(a.dv + (kv_row0 + u) * D + h * kD, w.acc_v[h], 1.0f, lg);
+  }
 }
 
 // ------------------------------------------------------------------ dQ
@@ -420,9 +480,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(KvArgs a) {
 //            VALU  P(j) = 2^(s c - lse2), dS(j) = P (dP - D)
 // The fragments the next phase multiplies (K and V rows of tile j+2, the
 // transposed K of tile j) are read from LDS during this phase.
-constexpr int kDqBuf = 5;                // ring slots
-constexpr int kDqSlot = 3 * kTileBytes;  // K rows | V rows | K tr
-constexpr int kDqDma = 3;                // DMA instructions per wave per tile
+constexpr int kDqBuf = 5;  // ring slots
+
+template <int DH>
+struct DqCfg {
+  static constexpr int kK = 0;                       // K half-tiles, row layout
+  static constexpr int kV = DH * kTileBytes;         // V half-tiles, row layout
+  static constexpr int kKt = 2 * DH * kTileBytes;    // K half-tiles, transposed layout
+  static constexpr int kSlot = 3 * DH * kTileBytes;
+  static constexpr int kDma = 3 * DH;                // DMA instructions per wave per tile
+};
 
 struct DqArgs {
   const uint16_t* q;
@@ -454,43 +521,72 @@ struct DqCtx {
   ReadOffsets ro;
 };
 
+template <int DH>
 struct DqState {
-  u32x4_t qf[4], df[4];  // Q and dO of this wave's 32 rows as B operands
-  f32x16_t acc[2];       // dQ^T
-  u32x4_t kr[4], vr[4];  // K and V row fragments of the next S^T, dP^T
-  u32x4_t kt[2][2];      // transposed K fragments of the next dQ product
-  f32x16_t sc[2], dp[2]; // S^T and dP^T of tiles j (index j & 1) and j+1
-  u32x4_t dsk[2][2];     // dS of tiles j-1 and j, packed as B operands
+  u32x4_t qf[DH][4], df[DH][4];  // Q and dO of this wave's 32 rows as B operands
+  f32x16_t acc[DH][2];           // dQ^T
+  u32x4_t kr[DH][4], vr[DH][4];  // K and V row fragments of the next S^T, dP^T
+  u32x4_t kt[DH][2][2];          // transposed K fragments of the next dQ product
+  f32x16_t sc[2], dp[2];         // S^T and dP^T of tiles j (index j & 1) and j+1
+  u32x4_t dsk[2][2];             // dS of tiles j-1 and j, packed as B operands
   float lse2, dd;
 };
 
-template <int SLOT>
+template <int DH, int SLOT>
 __device__ __forceinline__ void dq_issue(const DqCtx& cx, int kt) {
+  using C = DqCfg<DH>;
+  constexpr int RB = Dims<DH>::RB;
   const int row0 = kt * kTileRows;
   uint8_t* slot = cx.ring.p[SLOT];
-  dma_tile_part(cx.kbase, row0, cx.nlim, slot + cx.wave * 1024, cx.off_rows);
-  dma_tile_part(cx.vbase, row0, cx.nlim, slot + kTileBytes + cx.wave * 1024, cx.off_rows);
-  dma_tile_part(cx.kbase, row0, cx.nlim, slot + 2 * kTileBytes + cx.wave * 1024, cx.off_tr);
-}
-
-// Scheduling hints: 12 MFMAs, each followed by 5 VALU instructions of the
-// independent softmax work.
-__device__ __forceinline__ void dq_interleave() {
 #pragma unroll
-  for (int i = 0; i < 12; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+  for (int h = 0; h < DH; ++h) {
+    const uint32_t hb = h * kRowBytes;
+    dma_tile_part<RB>(cx.kbase, row0, cx.nlim, slot + C::kK + h * kTileBytes + cx.wave * 1024, cx.off_rows + hb);
+    dma_tile_part<RB>(cx.vbase, row0, cx.nlim, slot + C::kV + h * kTileBytes + cx.wave * 1024, cx.off_rows + hb);
+    dma_tile_part<RB>(cx.kbase, row0, cx.nlim, slot + C::kKt + h * kTileBytes + cx.wave * 1024, cx.off_tr + hb);
   }
 }
 
-template <int SLOT, int P>
-__device__ __forceinline__ void dq_phase(const DqCtx& cx, DqState& w, int j) {
+template <int DH>
+__device__ __forceinline__ void dq_read_rows(const uint8_t* slot, const ReadOffsets& ro, DqState<DH>& w) {
+  using C = DqCfg<DH>;
+#pragma unroll
+  for (int h = 0; h < DH; ++h) {
+    read_rows(slot + C::kK + h * kTileBytes, ro, w.kr[h]);
+    read_rows(slot + C::kV + h * kTileBytes, ro, w.vr[h]);
+  }
+}
+
+template <int DH>
+__device__ __forceinline__ f32x16_t mfma_regs(const u32x4_t (&a)[DH][4], const u32x4_t (&b)[DH][4]) {
+  f32x16_t acc = zero16();
+#pragma unroll
+  for (int h = 0; h < DH; ++h)
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) acc = mfma(a[h][ds], b[h][ds], acc);
+  return acc;
+}
+
+// Scheduling hints: 12*DH MFMAs, each followed by 5/DH (at least 2) VALU
+// instructions of the independent softmax work.
+template <int DH>
+__device__ __forceinline__ void dq_interleave() {
+#pragma unroll
+  for (int i = 0; i < 12 * DH; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, DH == 1 ? 5 : 2, 0);  // VALU
+  }
+}
+
+template <int DH, int SLOT, int P>
+__device__ __forceinline__ void dq_phase(const DqCtx& cx, DqState<DH>& w, int j) {
+  using C = DqCfg<DH>;
   constexpr int AHEAD = (SLOT + 4) % kDqBuf;
   constexpr int NEXT2 = (SLOT + 2) % kDqBuf;
   // tile j+2 has landed (tile j+3 may still be in flight); every wave is done
   // with tile j-1, whose slot receives tile j+4
-  barrier_vm<kDqDma>();
-  dq_issue<AHEAD>(cx, j + 4);
+  barrier_vm<C::kDma>();
+  dq_issue<DH, AHEAD>(cx, j + 4);
   if (j > cx.last) return;
   const int lg = (threadIdx.x & 63) >> 5;
   // mask S^T(j) on diagonal and tail tiles only, before the phase's MFMAs so
@@ -502,27 +598,31 @@ __device__ __forceinline__ void dq_phase(const DqCtx& cx, DqState& w, int j) {
       if (!(key0 + e < cx.N && (!cx.causal || key0 + e <= cx.t))) w.sc[P][e] = cx.masked;
   }
 
-  mfma_tr(w.kt, w.dsk[P ^ 1], w.acc);                                  // dQ^T += K(j-1)^T dS(j-1)^T
-  read_tr(cx.ring.p[SLOT] + 2 * kTileBytes, cx.ro, w.kt);              // K(j)^T
-  w.sc[P ^ 1] = mfma_k64(w.kr, w.qf);                                  // S^T(j+1)
-  w.dp[P ^ 1] = mfma_k64(w.vr, w.df);                                  // dP^T(j+1)
-  read_rows(cx.ring.p[NEXT2], cx.ro, w.kr);                            // K(j+2)
-  read_rows(cx.ring.p[NEXT2] + kTileBytes, cx.ro, w.vr);               // V(j+2)
+#pragma unroll
+  for (int h = 0; h < DH; ++h) mfma_tr(w.kt[h], w.dsk[P ^ 1], w.acc[h]);  // dQ^T += K(j-1)^T dS(j-1)^T
+#pragma unroll
+  for (int h = 0; h < DH; ++h) read_tr(cx.ring.p[SLOT] + C::kKt + h * kTileBytes, cx.ro, w.kt[h]);  // K(j)^T
+  w.sc[P ^ 1] = mfma_regs<DH>(w.kr, w.qf);  // S^T(j+1)
+  w.dp[P ^ 1] = mfma_regs<DH>(w.vr, w.df);  // dP^T(j+1)
+  dq_read_rows<DH>(cx.ring.p[NEXT2], cx.ro, w);  // K(j+2), V(j+2)
 
   f32x16_t ds;
 #pragma unroll
   for (int e = 0; e < 16; ++e)
     ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(w.sc[P][e], cx.c, -w.lse2)) * (w.dp[P][e] - w.dd);
   pack_pairs(ds, w.dsk[P]);
-  dq_interleave();
+  dq_interleave<DH>();
 }
 
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring0[kDqSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t ring1[kDqSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t ring2[kDqSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t ring3[kDqSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t ring4[kDqSlot];
+template <int DH>
+__global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dq_kernel(DqArgs a) {
+  using C = DqCfg<DH>;
+  constexpr int D = Dims<DH>::D;
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[C::kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[C::kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[C::kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring3[C::kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring4[C::kSlot];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -552,8 +652,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
   const int64_t kvrow0 = sg.kv_base + (int64_t)kvh * sg.stride;
   const int64_t qrow0 = sg.q_base + (int64_t)h * sg.stride;
   const int64_t rtrow0 = a.cu != nullptr ? sg.q_base + (int64_t)h * a.Np : ((int64_t)b * a.Hq + h) * a.Np;
-  cx.kbase = a.k + (size_t)kvrow0 * kD;
-  cx.vbase = a.v + (size_t)kvrow0 * kD;
+  cx.kbase = a.k + (size_t)kvrow0 * D;
+  cx.vbase = a.v + (size_t)kvrow0 * D;
   cx.N = N;
   cx.nlim = min(N, nt * kTileRows);
   cx.last = !wave_valid ? -1 : (a.causal ? tb : TB - 1);
@@ -563,36 +663,46 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
   cx.t = tb * kTileRows + l32;
   cx.c = a.c;
   cx.masked = a.c > 0.f ? -INFINITY : INFINITY;
-  cx.off_rows = dma_off_rows(wave, lane);
-  cx.off_tr = dma_off_tr(wave, lane);
+  cx.off_rows = dma_off_rows<Dims<DH>::RB>(wave, lane);
+  cx.off_tr = dma_off_tr<Dims<DH>::RB>(wave, lane);
   cx.ro = read_offsets(lane);
 
   const size_t row_q = (size_t)qrow0 + min(cx.t, N - 1);
-  DqState w;
+  DqState<DH> w;
 #pragma unroll
-  for (int ds = 0; ds < 4; ++ds) {
-    w.qf[ds] = u32x4_t{0u, 0u, 0u, 0u};
-    w.df[ds] = u32x4_t{0u, 0u, 0u, 0u};
+  for (int hh = 0; hh < DH; ++hh) {
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      w.qf[hh][ds] = u32x4_t{0u, 0u, 0u, 0u};
+      w.df[hh][ds] = u32x4_t{0u, 0u, 0u, 0u};
+    }
   }
   w.lse2 = 0.f;
   w.dd = 0.f;
   if (wave_valid) {
-    load_row_frags(a.q + row_q * kD, lg, w.qf);
-    load_row_frags(a.dout + row_q * kD, lg, w.df);
+#pragma unroll
+    for (int hh = 0; hh < DH; ++hh) {
+      load_row_frags(a.q + row_q * D + hh * kD, lg, w.qf[hh]);
+      load_row_frags(a.dout + row_q * D + hh * kD, lg, w.df[hh]);
+    }
     const float2 r = a.rt[(size_t)rtrow0 + min(cx.t, N - 1)];
     w.lse2 = r.x;
     w.dd = r.y;
   }
-  w.acc[0] = zero16();
-  w.acc[1] = zero16();
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    w.kt[x][0] = u32x4_t{0u, 0u, 0u, 0u};  // K(-1) = 0 and dS(-1) = 0: the first dQ product is a no-op
-    w.kt[x][1] = u32x4_t{0u, 0u, 0u, 0u};
-    w.dsk[1][x] = u32x4_t{0u, 0u, 0u, 0u};
+  for (int hh = 0; hh < DH; ++hh) {
+    w.acc[hh][0] = zero16();
+    w.acc[hh][1] = zero16();
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      w.kt[hh][x][0] = u32x4_t{0u, 0u, 0u, 0u};  // K(-1) = 0 and dS(-1) = 0: the first dQ product is a no-op
+      w.kt[hh][x][1] = u32x4_t{0u, 0u, 0u, 0u};
+    }
   }
+  w.dsk[1][0] = u32x4_t{0u, 0u, 0u, 0u};
+  w.dsk[1][1] = u32x4_t{0u, 0u, 0u, 0u};
 
-  for (int e = tid; e < kDqSlot / 16; e += kThreads) {
+  for (int e = tid; e < C::kSlot / 16; e += kThreads) {
     reinterpret_cast<u32x4_t*>(ring0)[e] = u32x4_t{0u, 0u, 0u, 0u};
     reinterpret_cast<u32x4_t*>(ring1)[e] = u32x4_t{0u, 0u, 0u, 0u};
     reinterpret_cast<u32x4_t*>(ring2)[e] = u32x4_t{0u, 0u, 0u, 0u};
@@ -603,64 +713,55 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqArgs a) {
 
   // prologue: tiles 0..3 in flight, wait for tiles 0..2, S^T(0) and dP^T(0),
   // then the row fragments of tile 1
-  dq_issue<0>(cx, 0);
-  dq_issue<1>(cx, 1);
-  dq_issue<2>(cx, 2);
-  dq_issue<3>(cx, 3);
-  barrier_vm<kDqDma>();
-  read_rows(ring0, cx.ro, w.kr);
-  read_rows(ring0 + kTileBytes, cx.ro, w.vr);
-  w.sc[0] = mfma_k64(w.kr, w.qf);
-  w.dp[0] = mfma_k64(w.vr, w.df);
-  read_rows(ring1, cx.ro, w.kr);
-  read_rows(ring1 + kTileBytes, cx.ro, w.vr);
+  dq_issue<DH, 0>(cx, 0);
+  dq_issue<DH, 1>(cx, 1);
+  dq_issue<DH, 2>(cx, 2);
+  dq_issue<DH, 3>(cx, 3);
+  barrier_vm<C::kDma>();
+  dq_read_rows<DH>(ring0, cx.ro, w);
+  w.sc[0] = mfma_regs<DH>(w.kr, w.qf);
+  w.dp[0] = mfma_regs<DH>(w.vr, w.df);
+  dq_read_rows<DH>(ring1, cx.ro, w);
 
   // whole ten-phase rounds first (ring slot period 5, register parity 2)
   int j = 0;
   for (; j + 2 * kDqBuf <= nt; j += 2 * kDqBuf) {
-    dq_phase<0, 0>(cx, w, j);
-    dq_phase<1, 1>(cx, w, j + 1);
-    dq_phase<2, 0>(cx, w, j + 2);
-    dq_phase<3, 1>(cx, w, j + 3);
-    dq_phase<4, 0>(cx, w, j + 4);
-    dq_phase<0, 1>(cx, w, j + 5);
-    dq_phase<1, 0>(cx, w, j + 6);
-    dq_phase<2, 1>(cx, w, j + 7);
-    dq_phase<3, 0>(cx, w, j + 8);
-    dq_phase<4, 1>(cx, w, j + 9);
+    dq_phase<DH, 0, 0>(cx, w, j);
+    dq_phase<DH, 1, 1>(cx, w, j + 1);
+    dq_phase<DH, 2, 0>(cx, w, j + 2);
+    dq_phase<DH, 3, 1>(cx, w, j + 3);
+    dq_phase<DH, 4, 0>(cx, w, j + 4);
+    dq_phase<DH, 0, 1>(cx, w, j + 5);
+    dq_phase<DH, 1, 0>(cx, w, j + 6);
+    dq_phase<DH, 2, 1>(cx, w, j + 7);
+    dq_phase<DH, 3, 0>(cx, w, j + 8);
+    dq_phase<DH, 4, 1>(cx, w, j + 9);
   }
-  if (j < nt) dq_phase<0, 0>(cx, w, j);
-  if (j + 1 < nt) dq_phase<1, 1>(cx, w, j + 1);
-  if (j + 2 < nt) dq_phase<2, 0>(cx, w, j + 2);
-  if (j + 3 < nt) dq_phase<3, 1>(cx, w, j + 3);
-  if (j + 4 < nt) dq_phase<4, 0>(cx, w, j + 4);
-  if (j + 5 < nt) dq_phase<0, 1>(cx, w, j + 5);
-  if (j + 6 < nt) dq_phase<1, 0>(cx, w, j + 6);
-  if (j + 7 < nt) dq_phase<2, 1>(cx, w, j + 7);
-  if (j + 8 < nt) dq_phase<3, 0>(cx, w, j + 8);
+  if (j < nt) dq_phase<DH, 0, 0>(cx, w, j);
+  if (j + 1 < nt) dq_phase<DH, 1, 1>(cx, w, j + 1);
+  if (j + 2 < nt) dq_phase<DH, 2, 0>(cx, w, j + 2);
+  if (j + 3 < nt) dq_phase<DH, 3, 1>(cx, w, j + 3);
+  if (j + 4 < nt) dq_phase<DH, 4, 0>(cx, w, j + 4);
+  if (j + 5 < nt) dq_phase<DH, 0, 1>(cx, w, j + 5);
+  if (j + 6 < nt) dq_phase<DH, 1, 0>(cx, w, j + 6);
+  if (j + 7 < nt) dq_phase<DH, 2, 1>(cx, w, j + 7);
+  if (j + 8 < nt) dq_phase<DH, 3, 0>(cx, w, j + 8);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
   if (!wave_valid || cx.t >= N) return;
   // drain dQ^T += K(last)^T dS(last)^T
-  if (cx.last & 1) mfma_tr(w.kt, w.dsk[1], w.acc);
-  else mfma_tr(w.kt, w.dsk[0], w.acc);
-  store_tr_row(a.dq + ((size_t)qrow0 + cx.t) * kD, w.acc, a.scale, lg);
+#pragma unroll
+  for (int hh = 0; hh < DH; ++hh) {
+    if (cx.last & 1) mfma_tr(w.kt[hh], w.dsk[1], w.acc[hh]);
+    else mfma_tr(w.kt[hh], w.dsk[0], w.acc[hh]);
+    store_tr_row(a.dq + ((size_t)qrow0 + cx.t) * D + hh * kD, w.acc[hh], a.scale, lg);
+  }
 }
 
-}  // namespace
-
-size_t attn_bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N) {
-  const int64_t Np = (N + kTileRows - 1) / kTileRows * kTileRows;
-  return (size_t)(B * Hq * Np) * sizeof(float2);
-}
-
-// Packed sequences: row terms [H_q, T + 32]; a 32-row tile read from any
-// row of any sequence then stays inside the buffer.
-size_t attn_bwd_rowterm_bytes_packed(int64_t Hq, int64_t T) { return (size_t)(Hq * (T + kTileRows)) * sizeof(float2); }
-
-hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream) {
-  if (p.D != kD) return hipErrorInvalidValue;
-  if (p.N * kRowBytes > 0x7fffffffLL) return hipErrorInvalidValue;  // buffer descriptor range
+template <int DH>
+hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
+  constexpr int RB = Dims<DH>::RB;
+  if (p.N * RB > 0x7fffffffLL) return hipErrorInvalidValue;  // buffer descriptor range
   const bool packed = p.cu_seqlens != nullptr;
   const int N = (int)p.N;  // the (longest) sequence
   // row-term rows per head: dense, N padded to whole tiles; packed, T + 32
@@ -688,7 +789,7 @@ hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream) {
     a.Np = Np;
     const int64_t nblk = (a.nrows + 31) / 32;
     if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(bwd_rowterms_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_rowterms_kernel<DH>, dim3((unsigned)nblk), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -717,7 +818,7 @@ hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream) {
     a.c = c;
     a.scale = p.scale;
     a.causal = p.causal;
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(a.nwg), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<DH>, dim3(a.nwg), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -745,9 +846,26 @@ hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream) {
     a.c = c;
     a.scale = p.scale;
     a.causal = p.causal;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(a.nwg), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dq_kernel<DH>, dim3(a.nwg), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
   }
+}
+
+}  // namespace
+
+size_t attn_bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N) {
+  const int64_t Np = (N + kTileRows - 1) / kTileRows * kTileRows;
+  return (size_t)(B * Hq * Np) * sizeof(float2);
+}
+
+// Packed sequences: row terms [H_q, T + 32]; a 32-row tile read from any
+// row of any sequence then stays inside the buffer.
+size_t attn_bwd_rowterm_bytes_packed(int64_t Hq, int64_t T) { return (size_t)(Hq * (T + kTileRows)) * sizeof(float2); }
+
+hipError_t launch_attn_bwd_bf16(const BwdProblem& p, hipStream_t stream) {
+  if (p.D == 64) return launch_bwd<1>(p, stream);
+  if (p.D == 128) return launch_bwd<2>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace sqa

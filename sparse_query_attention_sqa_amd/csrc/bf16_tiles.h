@@ -62,14 +62,18 @@ __device__ __forceinline__ f32x16_t zero16() {
 
 // Per-lane byte offsets. A wave DMAs 8 tile rows (rows 8*part .. 8*part+7)
 // of one tile, one 16-byte chunk per lane; these are the lane's source
-// offsets within the tile for the two layouts.
+// offsets within the tile for the two layouts. RB is the row pitch of the
+// array in HBM: 128 B for head dim 64; for head dim 128 a tile is two 64-wide
+// halves, and half h adds h*128 to the offset.
+template <int RB = kRowBytes>
 __device__ __forceinline__ uint32_t dma_off_rows(int part, int lane) {
   const int r = part * 8 + (lane >> 3), s = lane & 7;
-  return (uint32_t)(pi_row(r) * kRowBytes + ((s ^ swz_k(r)) * 16));
+  return (uint32_t)(pi_row(r) * RB + ((s ^ swz_k(r)) * 16));
 }
+template <int RB = kRowBytes>
 __device__ __forceinline__ uint32_t dma_off_tr(int part, int lane) {
   const int r = part * 8 + (lane >> 3), s = lane & 7;
-  return (uint32_t)(r * kRowBytes + ((s ^ swz_v(r)) * 16));
+  return (uint32_t)(r * RB + ((s ^ swz_v(r)) * 16));
 }
 
 // Read offsets within a tile: row-layout A fragments (k steps ds = 0..3) and
@@ -102,9 +106,10 @@ __device__ __forceinline__ ReadOffsets read_offsets(int lane) {
 // position (hh, lg, s) <-> tile row lg*16 + hh*8 + s sits at LDS row
 // hh*16 + lg*4 + s (s < 4) or hh*16 + 8 + lg*4 + s - 4 (s >= 4).
 __device__ __forceinline__ int swz_s(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+template <int RB = kRowBytes>
 __device__ __forceinline__ uint32_t dma_off_shared(int part, int lane) {
   const int r = part * 8 + (lane >> 3), s = lane & 7;
-  return (uint32_t)(pi_row(r) * kRowBytes + ((s ^ swz_s(r)) * 16));
+  return (uint32_t)(pi_row(r) * RB + ((s ^ swz_s(r)) * 16));
 }
 __device__ __forceinline__ ReadOffsets read_offsets_shared(int lane) {
   ReadOffsets o;
@@ -121,14 +126,16 @@ __device__ __forceinline__ ReadOffsets read_offsets_shared(int lane) {
   return o;
 }
 
-// DMA one wave's 8 rows of a tile that starts at row `row0` of a [rows, 64]
-// bf16 array whose valid rows end at `nlim`; rows at or past nlim are
-// zero-filled by the descriptor range check without any memory access.
+// DMA one wave's 8 rows of a tile that starts at row `row0` of a bf16
+// array with RB-byte rows whose valid rows end at `nlim`; rows at or past
+// nlim are zero-filled by the descriptor range check without any memory
+// access.
+template <int RB = kRowBytes>
 __device__ __forceinline__ void dma_tile_part(const uint16_t* base, int row0, int nlim, uint8_t* lds_part,
                                               uint32_t voff) {
-  const int rem = max(nlim - row0, 0) * kRowBytes;
+  const int rem = max(nlim - row0, 0) * RB;
   __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)row0 * kD), (short)0, rem, kBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)row0 * (RB / 2)), (short)0, rem, kBufferWord3);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_part, 16, voff, 0, 0, 0);
 }
 

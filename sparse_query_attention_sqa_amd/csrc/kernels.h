@@ -33,7 +33,7 @@ hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16_d128(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnProblem& p, hipStream_t stream);
 
-// SQA attention backward (bf16, head dim 64): dq [B,Hq,N,D], dk/dv
+// SQA attention backward (bf16, head dim 64 or 128): dq [B,Hq,N,D], dk/dv
 // [B,Hkv,N,D] from q, k, v, the forward's o and lse, and dout (or the packed
 // layouts with cu_seqlens, N the longest sequence). `rowterms` is device
 // scratch of attn_bwd_rowterm_bytes(B, Hq, N) bytes (packed:
@@ -57,7 +57,7 @@ struct BwdProblem {
 };
 size_t attn_bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N);
 size_t attn_bwd_rowterm_bytes_packed(int64_t Hq, int64_t T);
-hipError_t launch_attn_bwd_bf16_d64(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_attn_bwd_bf16(const BwdProblem& p, hipStream_t stream);
 
 // Projection + RoPE: x [M=B*N, Dm] bf16 times w_q [Dm,Hq*d] | w_k [Dm,Hkv*d] |
 // w_v [Dm,Hkv*d]; writes q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16 with RoPE applied

@@ -137,7 +137,7 @@ sqa_status sqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void
 }
 
 size_t sqa_attn_bwd_workspace_bytes(int64_t B, int64_t H_q, int64_t N, int64_t d, int dtype) {
-  if (B <= 0 || H_q <= 0 || N <= 0 || d != 64 || dtype != SQA_BF16) return 0;
+  if (B <= 0 || H_q <= 0 || N <= 0 || (d != 64 && d != 128) || dtype != SQA_BF16) return 0;
   if (N > kMaxN || B * H_q * N * d > kMaxElems) return 0;
   return round256(sqa::attn_bwd_rowterm_bytes(B, H_q, N));
 }
@@ -149,8 +149,8 @@ sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void*
   g_err.clear();
   sqa_status s = check_attn(B, H_q, H_kv, N, d, dtype, scale, causal);
   if (s != SQA_OK) return s;
-  if (dtype != SQA_BF16 || d != 64)
-    return fail(SQA_ERR_UNSUPPORTED, "backward supports bf16 with d=64 only (got dtype %d, d=%lld)", dtype,
+  if (dtype != SQA_BF16 || (d != 64 && d != 128))
+    return fail(SQA_ERR_UNSUPPORTED, "backward supports bf16 with d=64 or d=128 (got dtype %d, d=%lld)", dtype,
                 (long long)d);
   if (B == 0 || N == 0) return SQA_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
@@ -179,13 +179,13 @@ sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void*
         return fail(SQA_ERR_ARG, "outputs and workspace must not overlap each other");
   }
   sqa::BwdProblem p{q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H_q, H_kv, N, d, scale, causal};
-  hipError_t e = sqa::launch_attn_bwd_bf16_d64(p, static_cast<hipStream_t>(stream));
+  hipError_t e = sqa::launch_attn_bwd_bf16(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   return SQA_OK;
 }
 
 size_t sqa_attn_bwd_varlen_workspace_bytes(int64_t B, int64_t H_q, int64_t T, int64_t d, int dtype) {
-  if (B <= 0 || H_q <= 0 || T <= 0 || d != 64 || dtype != SQA_BF16) return 0;
+  if (B <= 0 || H_q <= 0 || T <= 0 || (d != 64 && d != 128) || dtype != SQA_BF16) return 0;
   if (T > kMaxN || T * H_q * d > kMaxElems) return 0;
   return round256(sqa::attn_bwd_rowterm_bytes_packed(H_q, T));
 }
@@ -199,8 +199,8 @@ sqa_status sqa_attn_bwd_varlen(const void* q, const void* k, const void* v, cons
   if (B < 0 || T < 0 || max_seqlen < 0) return fail(SQA_ERR_SHAPE, "negative size");
   sqa_status s = check_attn(B > 0 ? 1 : 0, H_q, H_kv, max_seqlen, d, dtype, scale, causal);
   if (s != SQA_OK) return s;
-  if (dtype != SQA_BF16 || d != 64)
-    return fail(SQA_ERR_UNSUPPORTED, "backward supports bf16 with d=64 only (got dtype %d, d=%lld)", dtype,
+  if (dtype != SQA_BF16 || (d != 64 && d != 128))
+    return fail(SQA_ERR_UNSUPPORTED, "backward supports bf16 with d=64 or d=128 (got dtype %d, d=%lld)", dtype,
                 (long long)d);
   if (max_seqlen > T) return fail(SQA_ERR_SHAPE, "max_seqlen=%lld exceeds T=%lld", (long long)max_seqlen,
                                   (long long)T);
@@ -233,7 +233,7 @@ sqa_status sqa_attn_bwd_varlen(const void* q, const void* k, const void* v, cons
   }
   sqa::BwdProblem p{q,  k,  v,  o,   dout, lse,       dq,    dk,     dv,         workspace,
                     B,  H_q, H_kv, max_seqlen, d, scale, causal, cu_seqlens, T};
-  hipError_t e = sqa::launch_attn_bwd_bf16_d64(p, static_cast<hipStream_t>(stream));
+  hipError_t e = sqa::launch_attn_bwd_bf16(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   return SQA_OK;
 }

@@ -177,6 +177,7 @@ def test_bwd_workspace_bytes(lib):
     assert sqa.sqa_attn_bwd_workspace_bytes(1, 1, 1, 64) == 256
     assert sqa.sqa_attn_bwd_workspace_bytes(0, 8, 1024, 64) == 0
     assert sqa.sqa_attn_bwd_workspace_bytes(1, 8, 1024, 16) == 0
+    assert sqa.sqa_attn_bwd_workspace_bytes(1, 8, 1024, 128) == 8 * 1024 * 8
     assert sqa.sqa_attn_bwd_workspace_bytes(1, 8, 1024, 64, dtype="f32") == 0
 
 
@@ -191,7 +192,7 @@ def _bwd(lib, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000,
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(lse=None), 1), (dict(dv=None), 1),
     (dict(Hkv=9), 2), (dict(N=-1), 2),
-    (dict(d=16), 3), (dict(dtype=0), 3), (dict(d=128), 3), (dict(d=32), 3),
+    (dict(d=16), 3), (dict(dtype=0), 3), (dict(d=256), 3), (dict(d=32), 3),
     (dict(do=FAKE + 0x400008), 4), (dict(lse=FAKE + 0x500002), 4), (dict(ws=FAKE + 0x900008), 4),
     (dict(ws=None), 5), (dict(ws_bytes=65535), 5),
     (dict(scale=float("nan")), 7), (dict(causal=-1), 7),
@@ -216,7 +217,8 @@ def test_bwd_varlen_workspace_bytes(lib):
     assert sqa.sqa_attn_bwd_varlen_workspace_bytes(3, 8, 1000, 64) == 8 * 8 * 1032
     assert sqa.sqa_attn_bwd_varlen_workspace_bytes(1, 1, 1, 64) == 512   # 33 rows x 8 B, rounded up
     assert sqa.sqa_attn_bwd_varlen_workspace_bytes(0, 8, 1000, 64) == 0
-    assert sqa.sqa_attn_bwd_varlen_workspace_bytes(2, 8, 1000, 128) == 0
+    assert sqa.sqa_attn_bwd_varlen_workspace_bytes(2, 8, 1000, 128) == 8 * 8 * 1032   # same for d = 128
+    assert sqa.sqa_attn_bwd_varlen_workspace_bytes(2, 8, 1000, 32) == 0
 
 
 def _bwd_varlen(lib, q=FAKE, cu=FAKE + 0xa00000, dq=FAKE + 0x600000, B=2, Hq=8, Hkv=4, T=1024, maxlen=600,
