@@ -138,7 +138,7 @@ size_t sqa_attn_bwd_workspace_bytes(int64_t B, int64_t H_q, int64_t N, int64_t d
  *   dk, dv     [B, H_kv, N, d] outputs, bf16, overwritten (group sums)
  *   workspace  device buffer of at least sqa_attn_bwd_workspace_bytes(...)
  *              bytes, owned by the caller; contents on return unspecified.
- *   d = 64 and dtype SQA_BF16 only (others: SQA_ERR_UNSUPPORTED).
+ *   d = 64 or 128 and dtype SQA_BF16 only (others: SQA_ERR_UNSUPPORTED).
  *   Arithmetic: P is recomputed from lse; scores and all sums are fp32, P and
  *   dS are rounded to bf16 (nearest even) for the matrix products, outputs
  *   are rounded to nearest-even bf16. Deterministic: no atomics.
@@ -169,7 +169,7 @@ size_t sqa_attn_bwd_varlen_workspace_bytes(int64_t B, int64_t H_q, int64_t T, in
  *   lse            [H_q, T]      fp32, sqa_attn_fwd_varlen's lse
  *   cu_seqlens     [B + 1]       DEVICE int32 offsets, as in sqa_attn_fwd_varlen
  *   workspace      at least sqa_attn_bwd_varlen_workspace_bytes(...) bytes
- *   d = 64, dtype SQA_BF16; head counts, scale, causal as sqa_attn_bwd.
+ *   d = 64 or 128, dtype SQA_BF16; head counts, scale, causal as sqa_attn_bwd.
  * Outputs must not overlap each other, an input (cu_seqlens included) or
  * the workspace. Errors: as sqa_attn_bwd.
  */

@@ -231,7 +231,7 @@ def sqa_attn_bwd(q, k, v, o, dout, lse, *, scale: Optional[float] = None, causal
                  dq=None, dk=None, dv=None, workspace=None):
     """Gradients of ``sqa_attn_fwd`` for the upstream gradient ``dout``.
 
-    q, o, dout [B, H_q, N, d]; k, v [B, H_kv, N, d] bf16 (d = 64); lse
+    q, o, dout [B, H_q, N, d]; k, v [B, H_kv, N, d] bf16 (d = 64 or 128); lse
     [B, H_q, N] fp32 from ``sqa_attn_fwd(..., return_lse=True)`` with the same
     scale and causal flag. Returns (dq, dk, dv); dk and dv sum over the query
     heads of each K/V head's group. ``workspace`` is an optional uint8 GPU
@@ -288,7 +288,7 @@ def sqa_attn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: Optional[
                         workspace=None):
     """Gradients of ``sqa_attn_fwd_varlen`` for the upstream gradient ``dout``.
 
-    q, o, dout [H_q, T, d]; k, v [H_kv, T, d] bf16 (d = 64); lse [H_q, T] fp32
+    q, o, dout [H_q, T, d]; k, v [H_kv, T, d] bf16 (d = 64 or 128); lse [H_q, T] fp32
     from ``sqa_attn_fwd_varlen(..., return_lse=True)``; cu_seqlens the same
     int32 GPU offsets. Returns (dq, dk, dv). ``max_seqlen`` as in the forward.
     """
