@@ -123,10 +123,10 @@ __global__ __launch_bounds__(256) void bwd_rowterms_kernel(RowArgs a) {
 // which is ascending w_in, or descending with `reverse`. Uneven head groups
 // or packed sequences (`spread`): the spread_coords order, which deals every
 // group and sequence over all XCDs.
-__device__ __forceinline__ void wg_coords(int spread, int causal, bool reverse, int nwg, int wg_per_bkv,
+__device__ __forceinline__ void wg_coords(int spread, int block, int causal, bool reverse, int nwg, int wg_per_bkv,
                                           int n_bkv, int& bkv, int& w_in) {
   if (spread) {
-    spread_coords(blockIdx.x, n_bkv, wg_per_bkv, causal && reverse, bkv, w_in);
+    spread_coords(blockIdx.x, n_bkv, wg_per_bkv, causal && reverse, block, bkv, w_in);
   } else if (!causal) {
     const int bid = blockIdx.x;
     const int per = nwg / kXcds, rem = nwg % kXcds;
@@ -191,6 +191,7 @@ struct KvArgs {
   int64_t T;      // packed: total tokens
   int N, Np, Hq, Hkv, wg_per_bkv, n_bkv, nwg;  // N: the (longest) sequence; Np: row-term rows per head
   int spread;  // uneven head groups or packed sequences: spread_coords order
+  int spread_block;  // its rotation block
   float c, scale;
   int causal;
 };
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dkdv_kernel(KvAr
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lg = lane >> 5, l32 = lane & 31;
   int bkv, w_in;
-  wg_coords(a.spread, a.causal, false, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
+  wg_coords(a.spread, a.spread_block, a.causal, false, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
   const SeqGeom sg = seq_geom(a.cu, a.T, a.N, b, a.Hq, a.Hkv);
   const int N = sg.n;
@@ -502,6 +503,7 @@ struct DqArgs {
   int64_t T;      // packed: total tokens
   int N, Np, Hq, Hkv, wg_per_bkv, n_bkv, nwg;  // sized for the longest sequence and the largest group
   int spread;  // uneven head groups or packed sequences: spread_coords order
+  int spread_block;  // its rotation block
   float c, scale;
   int causal;
 };
@@ -628,7 +630,7 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dq_kernel(DqArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lg = lane >> 5, l32 = lane & 31;
   int bkv, w_in;
-  wg_coords(a.spread, a.causal, true, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
+  wg_coords(a.spread, a.spread_block, a.causal, true, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
   const int slot = w_in * kWaves + wave;
   const HeadGroup hg = head_group(kvh, a.Hq, a.Hkv);
@@ -776,6 +778,7 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   float2* rt = static_cast<float2*>(p.rowterms);
   const int spread = (packed || p.Hq % p.Hkv != 0) ? 1 : 0;
   const int n_bkv = (int)(p.B * p.Hkv);
+  const int block = spread_block(packed, n_bkv);
 
   {
     // a packed batch is, for the row terms, one sequence of T tokens
@@ -810,6 +813,7 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
     a.Hq = (int)p.Hq;
     a.Hkv = (int)p.Hkv;
     a.spread = spread;
+    a.spread_block = block;
     a.wg_per_bkv = (tiles + kWaves - 1) / kWaves;
     a.n_bkv = n_bkv;
     const int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;
@@ -837,6 +841,7 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
     a.Hq = (int)p.Hq;
     a.Hkv = (int)p.Hkv;
     a.spread = spread;
+    a.spread_block = block;
     const int64_t slots = (int64_t)tiles * max_group(a.Hq, a.Hkv);
     a.wg_per_bkv = (int)((slots + kWaves - 1) / kWaves);
     a.n_bkv = n_bkv;

@@ -94,6 +94,7 @@ struct Args {
   int n_bkv;       // B * Hkv
   int nwg;
   int spread;      // 1: spread_coords order (packed sequences, causal uneven groups)
+  int spread_block;   // rotation block of the spread order
   int exact_per_batch;  // > 0: exact_coords order with this many workgroups per batch
   float c;         // |scale| * log2(e)
   uint32_t qsign;  // 0x80008000 flips both bf16 halves when scale < 0
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Args a) {
   // ---- workgroup -> (batch*Hkv, slot range)
   int bkv, w_in;
   if (a.spread) {  // packed sequences, or uneven groups under a causal mask
-    spread_coords(blockIdx.x, a.n_bkv, a.wg_per_bkv, a.causal != 0, bkv, w_in);
+    spread_coords(blockIdx.x, a.n_bkv, a.wg_per_bkv, a.causal != 0, a.spread_block, bkv, w_in);
   } else if (a.exact_per_batch > 0) {  // uneven groups, encoder-style: XCD-contiguous, exact counts
     const int bid = blockIdx.x;
     const int per = a.nwg / kXcds, rem = a.nwg % kXcds;
@@ -466,6 +467,7 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
   a.Hkv = (int)p.Hkv;
   const bool uneven = p.Hq % p.Hkv != 0;
   a.spread = (p.cu_seqlens != nullptr || (uneven && p.causal)) ? 1 : 0;
+  a.spread_block = spread_block(p.cu_seqlens != nullptr, p.B * p.Hkv);
   const int TB = (int)((p.N + kRowsPerWave - 1) / kRowsPerWave);
   const int64_t slots = (int64_t)TB * max_group(a.Hq, a.Hkv);
   a.wg_per_bkv = (int)((slots + kWaves - 1) / kWaves);
