@@ -81,6 +81,7 @@ __device__ __forceinline__ uint32_t dma_off_tr(int part, int lane) {
 struct ReadOffsets {
   uint32_t rows[4];
   uint32_t tr[2];
+  uint32_t tr_hi[2];  // shared layout only: the same reads 8 LDS rows further on
 };
 __device__ __forceinline__ ReadOffsets read_offsets(int lane) {
   ReadOffsets o;
@@ -98,14 +99,21 @@ __device__ __forceinline__ ReadOffsets read_offsets(int lane) {
 }
 
 // "Shared layout": LDS row r holds tile row pi(r), as in the row layout, but
-// with the swizzle swz_s(r) = 2*(r&3) + ((r>>2)&1). Eight consecutive rows
-// then put one logical chunk in eight different bank groups (row reads), and
-// four consecutive rows put a pair of chunks in eight different bank groups
-// (transposed reads), so one copy of a tile serves both operand forms:
-// read_rows with read_offsets_shared().rows, and read_tr_shared, whose k
-// position (hh, lg, s) <-> tile row lg*16 + hh*8 + s sits at LDS row
-// hh*16 + lg*4 + s (s < 4) or hh*16 + 8 + lg*4 + s - 4 (s >= 4).
-__device__ __forceinline__ int swz_s(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+// with the swizzle swz_s(r) = f((r>>1)&7), f(k) = 4*(k&1) + (k>>1). The LDS
+// has 64 four-byte banks (256 B); a 16-byte read serves 16 lanes per cycle
+// and a ds_read_b64_tr_b16 32 lanes. Rows of one parity in an aligned block
+// of 16 then take eight different chunk positions (row reads: 16 rows, one
+// logical chunk, conflict-free), and rows R and R+2 of an aligned block of 4
+// differ in bit 2 of the swizzle, so their 64-byte halves land in opposite
+// bank halves (transposed reads: 4 rows x 4 chunks, conflict-free). One copy
+// of a tile thus serves both operand forms: read_rows with
+// read_offsets_shared().rows, and read_tr_shared, whose k position
+// (hh, lg, s) <-> tile row lg*16 + hh*8 + s sits at LDS row hh*16 + lg*4 + s
+// (s < 4) or hh*16 + 8 + lg*4 + s - 4 (s >= 4).
+__device__ __forceinline__ int swz_s(int r) {
+  const int k = (r >> 1) & 7;
+  return ((k & 1) << 2) | (k >> 1);
+}
 template <int RB = kRowBytes>
 __device__ __forceinline__ uint32_t dma_off_shared(int part, int lane) {
   const int r = part * 8 + (lane >> 3), s = lane & 7;
@@ -121,7 +129,10 @@ __device__ __forceinline__ ReadOffsets read_offsets_shared(int lane) {
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int c16 = x * 4 + 2 * g1 + ((j16 & 3) >> 1);
+    // swz_s ignores bit 4 of the row (the hh * 16 rows read_tr_shared adds)
+    // but not bit 3, so the reads 8 rows on get their own offsets
     o.tr[x] = (uint32_t)(row * kRowBytes + ((c16 ^ swz_s(row)) * 16) + (j16 & 1) * 8);
+    o.tr_hi[x] = (uint32_t)((row + 8) * kRowBytes + ((c16 ^ swz_s(row + 8)) * 16) + (j16 & 1) * 8);
   }
   return o;
 }
@@ -168,9 +179,10 @@ __device__ __forceinline__ void read_tr_shared(const uint8_t* tile, const ReadOf
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const uint8_t* p = tile + ro.tr[x] + hh * 16 * kRowBytes;
-      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
-      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 8 * kRowBytes));
+      const s16x4_t lo =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + ro.tr[x] + hh * 16 * kRowBytes));
+      const s16x4_t hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + ro.tr_hi[x] + hh * 16 * kRowBytes));
       const u32x2_t a = __builtin_bit_cast(u32x2_t, lo);
       const u32x2_t b = __builtin_bit_cast(u32x2_t, hi);
       f[x][hh] = u32x4_t{a[0], a[1], b[0], b[1]};
