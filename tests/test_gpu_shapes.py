@@ -92,8 +92,10 @@ def test_bf16_uneven_groups_all_rows(Hq, Hkv, N, causal, d):
 
 
 @pytest.mark.parametrize("causal", [0, 1])
-@pytest.mark.parametrize("N,Hq,Hkv", [(100, 6, 4), (1000, 5, 2), (333, 7, 3)])
+@pytest.mark.parametrize("N,Hq,Hkv", [(100, 6, 4), (1000, 5, 2), (333, 7, 3), (4096, 6, 4)])
 def test_bwd_uneven_groups(N, Hq, Hkv, causal):
+    # (4096, 6, 4): four (batch, K/V head) pairs and more than 16 workgroups
+    # per pair in both kernels, so the spread order's rotation block advances
     label = f"bwd uneven Hq={Hq} Hkv={Hkv} N={N} causal={causal}"
     log(f"[case] {label}")
     q, k, v = draw_attn_case(1, Hq, Hkv, N, 64, "bf16", seed=N + Hq)
@@ -224,9 +226,10 @@ def test_long32k_d32_sqa():
     _long_sampled("long32k_d32_bf16", 8, 4, 0)
 
 
+@pytest.mark.parametrize("causal", [0, 1])
 @pytest.mark.parametrize("Hq,Hkv", [(12, 8), (6, 4)])
-def test_long32k_uneven(Hq, Hkv):
-    _long_sampled("long32k_uneven_bf16", Hq, Hkv, 0)
+def test_long32k_uneven(Hq, Hkv, causal):
+    _long_sampled("long32k_uneven_bf16", Hq, Hkv, causal)
 
 
 @pytest.mark.parametrize("causal", [1, 0])
