@@ -181,9 +181,9 @@ sqa_status sqa_attn_bwd_varlen(const void* q, const void* k, const void* v, cons
 
 /*
  * sqa_layer_workspace_bytes -- bytes of device workspace sqa_layer_fwd needs
- * for these sizes: bf16 Q [B,H_q,N,d], K and V [B,H_kv,N,d], the attention
- * output [B,H_q,N,d] and an fp32 RoPE (cos, sin) table [N, d/2, 2], each
- * rounded up to 256 bytes. Returns 0 for invalid or zero sizes.
+ * for these sizes: bf16 Q [B,H_q,N,d], K and V [B,H_kv,N,d] and the
+ * attention output [B,H_q,N,d], each rounded up to 256 bytes. Returns 0 for
+ * invalid or zero sizes.
  */
 size_t sqa_layer_workspace_bytes(int64_t B, int64_t N, int64_t D, int64_t H,
                                  int64_t H_q, int64_t H_kv, int dtype);

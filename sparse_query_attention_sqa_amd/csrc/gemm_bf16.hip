@@ -74,7 +74,7 @@ struct GemmArgs {
   uint16_t* y;            // [M, ncols] (SwiGLU: h [M, F])
   // QKV epilogue
   uint16_t* qkv[3];       // Q [B,Hq,N,d], K/V [B,Hkv,N,d]
-  const float* rope_cs;   // [N, d/2] (cos, sin)
+  double rope_theta[32];  // rope_base^(-2c/d) for pair c < d/2
   int64_t Nseq, Hq, Hkv, d;
 };
 
@@ -348,11 +348,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
       uint16_t* dst_bt = a.qkv[part] + ((int64_t)b * nheads * ns + t) * d;
       const uint32_t head_stride = ns * (uint32_t)d;
       const bool rope = part < 2;
-      // (cos, sin) of pair indices kp = 8*ab + 4*lg + e (mod half) of row t:
-      // four consecutive pairs (32 bytes) per ab; for d = 16 one group serves all
+      // (cos, sin) of the angle t * theta_kp for pair indices
+      // kp = 8*ab + 4*lg + e (mod half) of row t; for d = 16 one group of
+      // four serves all. The angle is formed and reduced modulo 2*pi in fp64,
+      // so that its rounding error does not grow with t, then taken in fp32.
       float2 cs[4][4];
       if (rope) {
-        const float* row = a.rope_cs + 2 * (t * half);
+        const double twopi = 6.283185307179586476925286766559;
 #pragma unroll
         for (int ab = 0; ab < 4; ++ab) {
           if (d == 16 && ab > 0) {
@@ -360,13 +362,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
             for (int e = 0; e < 4; ++e) cs[ab][e] = cs[0][e];
             continue;
           }
-          const int64_t kb = (8 * ab + 4 * lg) % half;
-          const float4* p4 = reinterpret_cast<const float4*>(row + 2 * kb);
-          const float4 u = p4[0], w = p4[1];
-          cs[ab][0] = make_float2(u.x, u.y);
-          cs[ab][1] = make_float2(u.z, u.w);
-          cs[ab][2] = make_float2(w.x, w.y);
-          cs[ab][3] = make_float2(w.z, w.w);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const double th = lg ? a.rope_theta[8 * ab + 4 + e] : a.rope_theta[8 * ab + e];
+            double ang = (double)t * th;
+            ang -= twopi * floor(ang / twopi);
+            float sn, cn;
+            sincosf((float)ang, &sn, &cn);
+            cs[ab][e] = make_float2(cn, sn);
+          }
         }
       }
 #pragma unroll
@@ -459,7 +463,8 @@ hipError_t launch_qkv_rope(const QkvProblem& p, hipStream_t stream) {
   a.qkv[0] = static_cast<uint16_t*>(p.q);
   a.qkv[1] = static_cast<uint16_t*>(p.k);
   a.qkv[2] = static_cast<uint16_t*>(p.v);
-  a.rope_cs = p.rope_cs;
+  for (int c = 0; c < 32; ++c)
+    a.rope_theta[c] = (c < p.d / 2) ? pow((double)p.rope_base, -2.0 * c / (double)p.d) : 0.0;
   a.Nseq = p.N;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;

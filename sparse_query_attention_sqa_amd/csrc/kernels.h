@@ -63,7 +63,6 @@ hipError_t launch_attn_bwd_bf16(const BwdProblem& p, hipStream_t stream);
 // w_v [Dm,Hkv*d]; writes q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16 with RoPE applied
 // to q and k.
 struct QkvProblem {
-  const float* rope_cs;  // [N, d/2] (cos, sin) pairs from launch_rope_table
   const void* x;
   const void* wq;
   const void* wk;
@@ -76,8 +75,6 @@ struct QkvProblem {
 };
 hipError_t launch_qkv_rope(const QkvProblem& p, hipStream_t stream);
 
-// RoPE table: cs[t][c] = (cos, sin)(t * base^(-2c/d)) for t < N, c < d/2.
-hipError_t launch_rope_table(float* cs, int64_t N, int64_t d, float rope_base, hipStream_t stream);
 
 // Output projection: y [B,N,Dm] = O_flat [B*N, Hq*d] times w_o [Hq*d, Dm],
 // reading O from its [B,Hq,N,d] layout.

@@ -1,9 +1,7 @@
-// Row-wise helpers of the SQA layer and the SQAT-m block (SQAT-m model card,
-// "Architecture details": RoPE, RMS Norm):
-//   rope_table : (cos, sin) of t*base^(-2c/d) for every position t and pair c,
-//                the angle formed and reduced modulo 2*pi in fp64.
-//   rms_norm   : y = x / sqrt(mean(x^2) + eps) * g per row, fp32 math.
-// The projection GEMMs live in gemm_bf16.hip.
+// Row-wise helper of the SQAT-m block (SQAT-m model card, "Architecture
+// details": RMS Norm):
+//   rms_norm : y = x / sqrt(mean(x^2) + eps) * g per row, fp32 math.
+// The projection GEMMs (with the RoPE epilogue) live in gemm_bf16.hip.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -18,16 +16,12 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kMaxHalf = 32;    // d/2 <= 32
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2_t f = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-struct Theta {
-  double v[kMaxHalf];
-};
 
 // ---------------------------------------------------------------- RMSNorm
 struct NormArgs {
@@ -75,41 +69,7 @@ __global__ __launch_bounds__(kThreads) void rms_norm_kernel(NormArgs a) {
   }
 }
 
-struct RopeArgs {
-  float* cs;
-  int64_t N, half;
-  Theta theta;
-};
-
-__global__ __launch_bounds__(kThreads) void rope_table_kernel(RopeArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= a.N * a.half) return;
-  const int64_t t = i / a.half, c = i % a.half;
-  const double twopi = 6.283185307179586476925286766559;
-  double ang = (double)t * a.theta.v[c];
-  ang -= twopi * floor(ang / twopi);  // reduce to [0, 2*pi) in fp64
-  float sn, cn;
-  sincosf((float)ang, &sn, &cn);
-  a.cs[2 * i] = cn;
-  a.cs[2 * i + 1] = sn;
-}
-
 }  // namespace
-
-hipError_t launch_rope_table(float* cs, int64_t N, int64_t d, float rope_base, hipStream_t stream) {
-  if (d % 2 != 0 || d / 2 > kMaxHalf) return hipErrorInvalidValue;
-  RopeArgs a;
-  a.cs = cs;
-  a.N = N;
-  a.half = d / 2;
-  for (int i = 0; i < kMaxHalf; ++i)
-    a.theta.v[i] = (i < d / 2) ? pow((double)rope_base, -2.0 * i / (double)d) : 0.0;
-  const int64_t n = N * a.half;
-  const int64_t nblk = (n + kThreads - 1) / kThreads;
-  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_rms_norm(const void* x, const void* g, void* y, int64_t M, int64_t D, float eps,
                            hipStream_t stream) {

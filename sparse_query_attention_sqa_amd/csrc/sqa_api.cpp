@@ -246,8 +246,7 @@ size_t sqa_layer_workspace_bytes(int64_t B, int64_t N, int64_t D, int64_t H, int
   if (B * N * (H_q > H_kv ? H_q : H_kv) * d > kMaxElems) return 0;
   const size_t esz = 2;
   const size_t nq = (size_t)(B * H_q * N * d) * esz, nkv = (size_t)(B * H_kv * N * d) * esz;
-  const size_t ncs = (size_t)(N * (d / 2)) * 2 * sizeof(float);  // RoPE (cos, sin) table
-  return 2 * round256(nq) + 2 * round256(nkv) + round256(ncs);
+  return 2 * round256(nq) + 2 * round256(nkv);
 }
 
 namespace {
@@ -282,11 +281,8 @@ sqa_status run_layer(const void* x, const void* w_q, const void* w_k, const void
   void* kb = ws + nq;
   void* vb = ws + nq + nkv;
   void* ob = ws + nq + 2 * nkv;
-  float* cs = reinterpret_cast<float*>(ws + 2 * nq + 2 * nkv);
-  hipError_t e = sqa::launch_rope_table(cs, N, d, rope_base, st);
-  if (e != hipSuccess) return hip_fail(e, "RoPE table launch");
-  sqa::QkvProblem qp{cs, x, w_q, w_k, w_v, qb, kb, vb, B, N, D, H_q, H_kv, d, rope_base};
-  e = sqa::launch_qkv_rope(qp, st);
+  sqa::QkvProblem qp{x, w_q, w_k, w_v, qb, kb, vb, B, N, D, H_q, H_kv, d, rope_base};
+  hipError_t e = sqa::launch_qkv_rope(qp, st);
   if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
   sqa::AttnProblem ap{qb, kb, vb, ob, nullptr, B, H_q, H_kv, N, d, scale, causal};
   e = sqa::launch_attn_fwd_bf16(ap, st);

@@ -129,10 +129,10 @@ def test_varlen_empty_is_a_noop(lib):
 
 def test_layer_workspace_bytes(lib):
     # SQAT-m layer: B=16 N=1024 D=256 H=16 (8,4): Q and O 4 MiB each, K and V
-    # 2 MiB each, RoPE table 1024 x 8 x (cos, sin) fp32 = 64 KiB
-    assert sqa.sqa_layer_workspace_bytes(16, 1024, 256, 16, 8, 4) == 2 * 4194304 + 2 * 2097152 + 65536
-    # B=1 N=3: Q 768 B, K 384 B, table 192 B -> rounded to 768, 512 and 256
-    assert sqa.sqa_layer_workspace_bytes(1, 3, 256, 16, 8, 4) == 2 * 768 + 2 * 512 + 256
+    # 2 MiB each
+    assert sqa.sqa_layer_workspace_bytes(16, 1024, 256, 16, 8, 4) == 2 * 4194304 + 2 * 2097152
+    # B=1 N=3: Q 768 B, K 384 B -> rounded to 768 and 512
+    assert sqa.sqa_layer_workspace_bytes(1, 3, 256, 16, 8, 4) == 2 * 768 + 2 * 512
     assert sqa.sqa_layer_workspace_bytes(0, 1024, 256, 16, 8, 4) == 0
     assert sqa.sqa_layer_workspace_bytes(1, 1024, 256, 16, 8, 4, dtype="f32") == 0
 
@@ -248,7 +248,7 @@ def test_block_workspace_bytes(lib):
     # SQAT-m block B=16 N=1024 D=256 (8,4) F=768: the layer's workspace plus the
     # normalised input and residual stream (8 MiB each) and the SwiGLU
     # activations (24 MiB)
-    layer = 2 * 4194304 + 2 * 2097152 + 65536
+    layer = 2 * 4194304 + 2 * 2097152
     assert sqa.sqa_block_workspace_bytes(16, 1024, 256, 16, 8, 4, 768) == layer + 2 * 8388608 + 25165824
     assert sqa.sqa_block_workspace_bytes(16, 1024, 256, 16, 8, 4, 0) == 0
     assert sqa.sqa_block_workspace_bytes(0, 1024, 256, 16, 8, 4, 768) == 0
