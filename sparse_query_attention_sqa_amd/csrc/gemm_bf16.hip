@@ -74,7 +74,7 @@ struct GemmArgs {
   uint16_t* y;            // [M, ncols] (SwiGLU: h [M, F])
   // QKV epilogue
   uint16_t* qkv[3];       // Q [B,Hq,N,d], K/V [B,Hkv,N,d]
-  double rope_theta[32];  // rope_base^(-2c/d) for pair c < d/2
+  double rope_theta[32];  // rope_base^(-2c/d) / (2 pi): revolutions per position, pair c < d/2
   int64_t Nseq, Hq, Hkv, d;
 };
 
@@ -350,11 +350,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
       const bool rope = part < 2;
       // (cos, sin) of the angle t * theta_kp for pair indices
       // kp = 8*ab + 4*lg + e (mod half) of row t; for d = 16 one group of
-      // four serves all. The angle is formed and reduced modulo 2*pi in fp64,
-      // so that its rounding error does not grow with t, then taken in fp32.
+      // four serves all. The angle is formed in revolutions and reduced to
+      // [0, 1) in fp64, so that its rounding error does not grow with t, and
+      // v_cos_f32 / v_sin_f32 take it in revolutions (measured on gfx950:
+      // at most 1.3e-7 absolute error over [0, 1)).
       float2 cs[4][4];
       if (rope) {
-        const double twopi = 6.283185307179586476925286766559;
 #pragma unroll
         for (int ab = 0; ab < 4; ++ab) {
           if (d == 16 && ab > 0) {
@@ -365,11 +366,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const double th = lg ? a.rope_theta[8 * ab + 4 + e] : a.rope_theta[8 * ab + e];
-            double ang = (double)t * th;
-            ang -= twopi * floor(ang / twopi);
-            float sn, cn;
-            sincosf((float)ang, &sn, &cn);
-            cs[ab][e] = make_float2(cn, sn);
+            const double rev = (double)t * th;
+            const float f = (float)(rev - floor(rev));
+            cs[ab][e] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
           }
         }
       }
@@ -464,7 +463,8 @@ hipError_t launch_qkv_rope(const QkvProblem& p, hipStream_t stream) {
   a.qkv[1] = static_cast<uint16_t*>(p.k);
   a.qkv[2] = static_cast<uint16_t*>(p.v);
   for (int c = 0; c < 32; ++c)
-    a.rope_theta[c] = (c < p.d / 2) ? pow((double)p.rope_base, -2.0 * c / (double)p.d) : 0.0;
+    a.rope_theta[c] =
+        (c < p.d / 2) ? pow((double)p.rope_base, -2.0 * c / (double)p.d) / 6.283185307179586476925286766559 : 0.0;
   a.Nseq = p.N;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
