@@ -376,7 +376,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the forward needs no collective; see the sharding notes in DESIGN.md)",
+              "(the library runs on one GPU; the forward needs no collective)",
               file=sys.stderr)
         sys.exit(2)
 
