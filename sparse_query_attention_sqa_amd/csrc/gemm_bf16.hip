@@ -16,12 +16,12 @@
 //
 // Tiling: the output columns are cut into 64-wide segments of the weight
 // parts (W_q | W_k | W_v for the QKV projection, one matrix otherwise); a
-// 4-wave workgroup computes 128 rows x two segments (SwiGLU: one segment of
-// both gate and up), and wave (wm, wn) owns 64 rows of segment wn as four
-// 32x32 accumulators. The reduction runs in 64-wide chunks, DMA'd HBM -> LDS
-// with buffer_load ... lds into a ring of S stages with S-1 chunks in
-// flight (S = 4 for small grids, where one workgroup per CU would otherwise
-// wait out one HBM round trip per chunk; S = 2 otherwise); rows past M,
+// 4-wave workgroup computes 64*MB rows x two segments (SwiGLU: one segment of
+// both gate and up), and wave (wm, wn) owns 32*MB rows of segment wn as 2*MB
+// 32x32 accumulators (MB = 2, or 1 for small grids, which then get twice the
+// workgroups). The reduction runs in 64-wide chunks, DMA'd HBM -> LDS with
+// buffer_load ... lds into a ring of S stages with S-1 chunks in flight
+// (S = 3 with MB = 1 for small grids, S = 2 otherwise); rows past M,
 // columns past the part's width and reduction indices past K -- including
 // whole chunks past the end, so every step issues the same DMAs and the
 // waits are exact -- are zero-filled by the descriptor's range check (their
@@ -39,11 +39,24 @@ namespace {
 using namespace tiles;
 
 constexpr int kThreads = 256;
-constexpr int TM = 128;                      // rows per workgroup
 constexpr int TK = 64;                       // reduction chunk
-constexpr int kATiles = TM / kTileRows;      // 4 row tiles of [32 m][64 k]
-constexpr int kStageBytes = 8 * kTileBytes;  // A 16 KB | W 16 KB (4 tiles of [32 k][64 n])
 constexpr uint32_t kOOB = 0x80000000u;       // an offset past every descriptor range
+
+// MB = 32-row blocks per wave: a workgroup (two waves along the rows) takes
+// TM = 64*MB rows; a stage holds the A tiles ([32 m][64 k], 2*MB of them)
+// and the 4 W tiles ([32 k][64 n]).
+template <int MB>
+struct Tiling {
+  static_assert(MB == 1 || MB == 2, "32 or 64 rows per wave");
+  static constexpr int TM = 64 * MB;
+  static constexpr int kATiles = 2 * MB;
+  static constexpr int kStageBytes = (kATiles + 4) * kTileBytes;
+  static constexpr int kAParts = 2 * MB;      // A DMAs (8 rows each) per wave per chunk
+  static constexpr int kDma = kAParts + 4;    // DMAs per wave per chunk
+};
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt vm, expcnt 7, lgkmcnt 0.
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
 
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_QKV = 2 };
 
@@ -116,11 +129,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kBufferWord3);
 }
 
-constexpr int kDmaPerChunk = 8;  // DMA instructions per wave per chunk
-
-template <int EPI, int S, bool GATHER>
+template <int EPI, int S, bool GATHER, int MB>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
   static_assert(S >= 2 && S <= 4, "2 to 4 stages");
+  using T = Tiling<MB>;
+  constexpr int TM = T::TM;
+  constexpr int kATiles = T::kATiles;
+  constexpr int kStageBytes = T::kStageBytes;
   __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st2[S > 2 ? kStageBytes : 16];
@@ -162,20 +177,24 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t rw0 = rsrc(wp0.w, K * wp0.ncols * 2);
   const __amdgpu_buffer_rsrc_t rw1 = rsrc(wp1.w, K * wp1.ncols * 2);
 
-  // This wave DMAs A tile `wave` (4 parts of 8 rows) and W tile `wave`
-  // (kh = wave / 2, c = wave % 2; 4 parts of 8 k-rows). Per-lane row terms
-  // are fixed across the reduction and computed once here.
+  // This wave DMAs parts (8 rows each) of A tile atile -- all four of tile
+  // `wave` for MB = 2, parts 2*(wave/2) + 0, 1 of tile wave % 2 for MB = 1 --
+  // and W tile `wave` (kh = wave / 2, c = wave % 2; 4 parts of 8 k-rows).
+  // Per-lane row terms are fixed across the reduction and computed once here.
   const int r8 = lane >> 3, s = lane & 7;
   const uint32_t dshift = GATHER ? (uint32_t)__builtin_ctzll((unsigned long long)A.d) : 0u;
-  uint32_t a_base[4], a_k[4];
-  bool a_ok[4];
+  constexpr int NQA = T::kAParts;
+  const int atile = (MB == 2) ? wave : (wave & 1);
+  const int aq0 = (MB == 2) ? 0 : 2 * (wave >> 1);
+  uint32_t a_base[NQA], a_k[NQA];
+  bool a_ok[NQA];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = q * 8 + r8;                         // row within the 32-row tile
-    const int64_t m = m0 + wave * kTileRows + r;
-    a_ok[q] = m < A.M;
-    a_base[q] = a_ok[q] ? a_row_base<GATHER>(A, (uint32_t)m) : 0u;
-    a_k[q] = 8u * (uint32_t)(s ^ swz_k(r));
+  for (int j = 0; j < NQA; ++j) {
+    const int r = (aq0 + j) * 8 + r8;                 // row within the 32-row tile
+    const int64_t m = m0 + atile * kTileRows + r;
+    a_ok[j] = m < A.M;
+    a_base[j] = a_ok[j] ? a_row_base<GATHER>(A, (uint32_t)m) : 0u;
+    a_k[j] = 8u * (uint32_t)(s ^ swz_k(r));
   }
   const int wkh = wave >> 1, wc = wave & 1;
   const WPart wq = wc ? wp1 : wp0;
@@ -194,10 +213,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
   auto issue = [&](uint8_t* stage, int64_t k0) {
     const uint32_t k32 = (uint32_t)k0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t off = a_offset<GATHER>(A, a_base[q], a_ok[q], k32 + a_k[q], dshift);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(stage + wave * kTileBytes + q * 1024), 16, off, 0,
-                                               0, 0);
+    for (int j = 0; j < NQA; ++j) {
+      const uint32_t off = a_offset<GATHER>(A, a_base[j], a_ok[j], k32 + a_k[j], dshift);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(stage + atile * kTileBytes + (aq0 + j) * 1024), 16,
+                                               off, 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -226,11 +245,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
   const uint32_t toff0 = (EPI == EPI_SWIGLU) ? (wn ? ro.tr[1] : ro.tr[0]) : ro.tr[0];
   const uint32_t toff1 = (EPI == EPI_SWIGLU) ? (wn ? ro.tr[1] : ro.tr[0]) : ro.tr[1];
 
-  f32x16_t acc[2][2];  // [slot x][row block mb]
+  f32x16_t acc[2][MB];  // [slot x][row block mb]
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) acc[x][mb] = zero16();
+    for (int mb = 0; mb < MB; ++mb) acc[x][mb] = zero16();
 
   // One reduction chunk from stage CUR while chunk kc+S-1 streams into the
   // stage freed by chunk kc-1. The stages are separate LDS objects and the
@@ -240,9 +259,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
     // chunk kc landed (later ones may not have); every wave is done with
     // chunk kc-1, whose stage receives chunk kc+S-1
     asm volatile("" ::: "memory");
-    if constexpr (S == 2) __builtin_amdgcn_s_waitcnt(0x0070);           // vmcnt(0) lgkmcnt(0)
-    else if constexpr (S == 3) __builtin_amdgcn_s_waitcnt(0x0078);      // vmcnt(8) lgkmcnt(0)
-    else __builtin_amdgcn_s_waitcnt(0x4070);                            // vmcnt(16) lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 2) * T::kDma));  // S-2 chunks may stay in flight
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     issue(ahead, (int64_t)(kc + S - 1) * TK);
@@ -264,8 +281,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const uint8_t* at = cur + (wm * 2 + mb) * kTileBytes;
+        for (int mb = 0; mb < MB; ++mb) {
+          const uint8_t* at = cur + (wm * MB + mb) * kTileBytes;
           const u32x4_t af = *reinterpret_cast<const u32x4_t*>(at + boff[kh][hh]);
 #pragma unroll
           for (int x = 0; x < 2; ++x) acc[x][mb] = mfma(wf[x][hh], af, acc[x][mb]);
@@ -290,10 +307,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0070);
 
   // ---------------- epilogues. Entry i of acc[x][mb] (lane l): row
-  // m0 + wm*64 + mb*32 + l32; column (within the slot's 32) 8*(i/4) + 4*lg + i%4.
+  // m0 + wm*32*MB + mb*32 + l32; column (within the slot's 32) 8*(i/4) + 4*lg + i%4.
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int64_t m = m0 + wm * 64 + mb * 32 + l32;
+  for (int mb = 0; mb < MB; ++mb) {
+    const int64_t m = m0 + wm * 32 * MB + mb * 32 + l32;
     if (m >= A.M) continue;
     if (EPI == EPI_SWIGLU) {
       const int64_t F = a.part[0].ncols;
@@ -403,26 +420,35 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
   }
 }
 
-template <int EPI, bool GATHER>
-hipError_t launch_stages(const GemmArgs& a, int64_t nblk, hipStream_t stream) {
-  // few workgroups (about one per CU or less): keep every chunk of a short
-  // reduction in flight at once; otherwise two stages and two workgroups/CU
-  if (nblk <= 384)
-    hipLaunchKernelGGL((gemm_kernel<EPI, 4, GATHER>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((gemm_kernel<EPI, 2, GATHER>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
+template <int EPI, int S, bool GATHER, int MB>
+hipError_t launch_grid(const GemmArgs& a, hipStream_t stream) {
+  const int64_t mtiles = (a.A.M + Tiling<MB>::TM - 1) / Tiling<MB>::TM;
+  const int64_t nblk = mtiles * a.tiles_total;
+  if (nblk > 0x7fffffff || nblk <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_kernel<EPI, S, GATHER, MB>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
+// Grids of at most 384 workgroups of 128 rows (about one per CU; the SQAT-m
+// QKV, output and down projections) run 64-row workgroups with three stages
+// instead: twice the workgroups, two per CU (72 KB of LDS each), two chunks
+// in flight. Measured on the SQAT-m block (B16 N1024): QKV 11.3 -> 8.9 us,
+// output projection 11.2 -> 10.0, down 17.2 -> 15.7 (128-row workgroups with
+// four stages before; 64-row with two or four stages were slower). Larger
+// grids (the gate/up projection) keep 128 rows and two stages.
+template <int EPI, bool GATHER>
+hipError_t launch_stages(const GemmArgs& a, hipStream_t stream) {
+  const int64_t nblk128 = ((a.A.M + 127) / 128) * a.tiles_total;
+  if (nblk128 <= 384) return launch_grid<EPI, 3, GATHER, 1>(a, stream);
+  return launch_grid<EPI, 2, GATHER, 2>(a, stream);
+}
+
 hipError_t launch(const GemmArgs& a, int epi, hipStream_t stream) {
-  const int64_t mtiles = (a.A.M + TM - 1) / TM;
-  const int64_t nblk = mtiles * a.tiles_total;
-  if (nblk > 0x7fffffff || nblk <= 0) return hipErrorInvalidValue;
+  if (a.tiles_total <= 0 || a.A.M <= 0) return hipErrorInvalidValue;
   if (epi == EPI_STORE)
-    return a.A.gather ? launch_stages<EPI_STORE, true>(a, nblk, stream)
-                      : launch_stages<EPI_STORE, false>(a, nblk, stream);
-  if (epi == EPI_SWIGLU) return launch_stages<EPI_SWIGLU, false>(a, nblk, stream);
-  return launch_stages<EPI_QKV, false>(a, nblk, stream);
+    return a.A.gather ? launch_stages<EPI_STORE, true>(a, stream) : launch_stages<EPI_STORE, false>(a, stream);
+  if (epi == EPI_SWIGLU) return launch_stages<EPI_SWIGLU, false>(a, stream);
+  return launch_stages<EPI_QKV, false>(a, stream);
 }
 
 GemmArgs base_args() {
