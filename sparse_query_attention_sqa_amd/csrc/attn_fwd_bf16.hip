@@ -30,10 +30,13 @@
 //     (built in registers with a 4x4 transpose) so the A operand of the P.V
 //     product is one 16-byte LDS read.
 //   * Online softmax in fp32 with base-2 exponentials (v_exp_f32) of
-//     s*c - m, c = |scale|*log2(e). The running maximum m is only raised when
-//     a tile's maximum exceeds it by more than kRescaleSlack (log2 units); the
-//     probabilities are then bounded by 2^kRescaleSlack, well inside the
-//     bf16/fp32 range, and the O rescale is skipped on most tiles.
+//     s*c - m, c = |scale|*log2(e). The running maximum m is raised lazily:
+//     probabilities are computed against m as it stands, and only when a
+//     lane's sum of its 32 probabilities of a tile exceeds kSumLimit (or is
+//     not finite, as on the first tile where m = -inf) is the tile's exact
+//     row maximum taken, O and l rescaled and the tile's probabilities
+//     recomputed. Between refreshes every probability is <= kSumLimit, far
+//     inside the bf16/fp32 range, and no tile pays for a row maximum.
 //   * Probabilities are rounded to bf16 (round to nearest even) for the P.V
 //     MFMA; the row sum l adds the same rounded values, so the weights that
 //     multiply V sum exactly to l.
@@ -62,7 +65,9 @@ constexpr int kThreads = 256;      // 4 waves of 64
 constexpr int kWaves = 4;
 constexpr int kMaxRowsPerWave = 64;  // query rows per wave: QS (1 or 2) 32-row MFMA tiles
 constexpr int kTileKeys = 64;      // keys per K/V tile
-constexpr float kRescaleSlack = 8.0f;
+constexpr float kSumLimit = 1048576.0f;  // 2^20
+constexpr float kMaskedScore = -3.0e38f;
+constexpr float kMinC = 1e-30f;          // |scale|*log2(e) is clamped up to this
 constexpr int kXcds = 8;
 
 template <int D>
@@ -196,6 +201,30 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* buf, 
   }
 }
 
+// Probabilities of query tile qs (both 32-key halves of a 64-key tile)
+// against the maximum m, rounded to bf16 and packed as the B operand of
+// O^T += V^T P^T; returns the lane's sum of its 32 rounded probabilities,
+// accumulated in two partial sums (two short dependency chains).
+template <int QS>
+__device__ __forceinline__ float exp_rows(const f32x16_t (&s)[2][QS], int qs, uint32_t (&pk)[2][QS][2][4],
+                                          float c, float m) {
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  const float mneg = -m;
+  float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+  for (int kx = 0; kx < 2; ++kx)
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kx][qs][2 * w], c, mneg));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kx][qs][2 * w + 1], c, mneg));
+      const uint32_t pp = pack_bf16x2(p0, p1);
+      pk[kx][qs][w >> 2][w & 3] = pp;
+      if (w & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, l1, false);
+      else l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, l0, false);
+    }
+  return l0 + l1;
+}
+
 // One K/V tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
 // MASKED adds the causal (key <= t) and tail (key < N) masks; it is used only
 // for a wave's diagonal tile and for the ragged last tile.
@@ -227,6 +256,9 @@ __device__ __forceinline__ void process_tile(const uint16_t* ks, const u32x4_t (
     }
   }
 
+  // invisible keys get kMaskedScore, whose probability underflows to exactly
+  // 0 for any c >= kMinC once m is finite; every row's first tile (tile 0)
+  // holds a visible key (key 0), so m is finite after it.
   if constexpr (MASKED) {
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
@@ -237,24 +269,27 @@ __device__ __forceinline__ void process_tile(const uint16_t* ks, const u32x4_t (
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + kx * 32 + lg * 16 + i;
           const bool ok = key < N && (!causal || key <= t);
-          if (!ok) s[kx][qs][i] = -INFINITY;
+          if (!ok) s[kx][qs][i] = kMaskedScore;
         }
     }
   }
 
-  // online softmax (fp32), lazily raised running maximum
-  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  // online softmax (fp32) against the running maximum as it stands; a
+  // query tile whose probabilities grew too large (or whose m was still
+  // -inf) takes the exact row maximum, rescales O and l and recomputes.
   uint32_t pk[2][QS][2][4];  // [kx][qs][half][word] bf16 pairs
+  float lsum[QS];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) lsum[qs] = exp_rows<QS>(s, qs, pk, c, m_run[qs]);
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs) {
-    float mx = s[0][qs][0];
+    if (__ballot(!(lsum[qs] <= kSumLimit))) {
+      float mx = s[0][qs][0];
 #pragma unroll
-    for (int kx = 0; kx < 2; ++kx)
+      for (int kx = 0; kx < 2; ++kx)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kx][qs][i]);
-    const float cand = (MASKED && mx == -INFINITY) ? -INFINITY : mx * c;
-    const bool need = cand > m_run[qs] + kRescaleSlack;
-    if (__ballot(need)) {
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kx][qs][i]);
+      const float cand = mx * c;
       const float other = __shfl_xor(cand, 32);
       const float mnew = fmaxf(m_run[qs], fmaxf(cand, other));
       const float alpha = (m_run[qs] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[qs] - mnew);
@@ -264,24 +299,9 @@ __device__ __forceinline__ void process_tile(const uint16_t* ks, const u32x4_t (
       for (int x = 0; x < C::DSUB; ++x)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc_o[x][qs][i] *= alpha;
+      lsum[qs] = exp_rows<QS>(s, qs, pk, c, m_run[qs]);
     }
-    const float mneg = -m_run[qs];
-    float lsum = 0.f;
-#pragma unroll
-    for (int kx = 0; kx < 2; ++kx)
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kx][qs][2 * w], c, mneg));
-        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kx][qs][2 * w + 1], c, mneg));
-        if constexpr (MASKED) {
-          if (s[kx][qs][2 * w] == -INFINITY) p0 = 0.f;
-          if (s[kx][qs][2 * w + 1] == -INFINITY) p1 = 0.f;
-        }
-        const uint32_t pp = pack_bf16x2(p0, p1);
-        pk[kx][qs][w >> 2][w & 3] = pp;
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, lsum, false);
-      }
-    l_run[qs] += lsum;
+    l_run[qs] += lsum[qs];
   }
 
   // O^T += V^T P^T
@@ -494,7 +514,7 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
   }
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
   a.nwg = (int)nwg;
-  a.c = fabsf(p.scale) * 1.4426950408889634f;
+  a.c = fmaxf(fabsf(p.scale) * 1.4426950408889634f, kMinC);
   a.qsign = (p.scale < 0.f) ? 0x80008000u : 0u;
   a.causal = p.causal;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QS>), dim3(a.nwg), dim3(kThreads), 0, stream, a);

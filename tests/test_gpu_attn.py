@@ -163,13 +163,33 @@ def test_identical_keys_give_mean(causal):
     check_global(o, ref, "bf16", f"identical keys causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 16, 32, 128])
 @pytest.mark.parametrize("scale", [0.0, -0.125, 0.5])
-def test_scale_values(scale):
-    q, k, v = draw_attn_case(1, 8, 4, 333, 64, "bf16", seed=5)
+def test_scale_values(scale, d):
+    q, k, v = draw_attn_case(1, 8, 4, 333, d, "bf16", seed=5)
     for causal in (0, 1):
         o = to_host(_run(q, k, v, "bf16", scale, causal))
         ref = oracle_attention(q, k, v, scale=scale, causal=bool(causal))
-        check_global(o, ref, "bf16", f"scale={scale} causal={causal}")
+        check_global(o, ref, "bf16", f"scale={scale} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_score_jumps_in_later_tiles(d, causal):
+    """Keys from position 600 on are scaled by 4 and keys 1100-1109 by 16
+    (powers of two: still exact in bf16), so the row maximum jumps by far more
+    than 2^20 in probability in tiles after the first one; every row is
+    compared with the oracle."""
+    N = 1500
+    label = f"score jumps d={d} causal={causal}"
+    log(f"[case] {label}")
+    q, k, v = draw_attn_case(1, 8, 4, N, d, "bf16", seed=23)
+    k[:, :, 600:] *= 4.0
+    k[:, :, 1100:1110] *= 4.0
+    o = to_host(_run(q, k, v, "bf16", 1.0 / math.sqrt(d), causal))
+    ref = oracle_attention(q, k, v, scale=1.0 / math.sqrt(d), causal=bool(causal))
+    check_global(o, ref, "bf16", label)
+    check_rows(o, ref, label)
 
 
 def test_permutation_equivariance_noncausal():
