@@ -225,86 +225,75 @@ __device__ __forceinline__ float exp_rows(const f32x16_t (&s)[2][QS], int qs, ui
   return l0 + l1;
 }
 
-// One K/V tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// MASKED adds the causal (key <= t) and tail (key < N) masks; it is used only
-// for a wave's diagonal tile and for the ragged last tile.
-template <int D, int QS, bool MASKED>
-__device__ __forceinline__ void process_tile(const uint16_t* ks, const u32x4_t (&qf)[QS][Cfg<D>::DSTEPS],
-                                             f32x16_t (&acc_o)[Cfg<D>::DSUB][QS], float (&m_run)[QS],
-                                             float (&l_run)[QS], float c, int key0, int N, int causal,
-                                             int trow0, int l32, int lg) {
-  using C = Cfg<D>;
-  const uint16_t* vs = ks + C::KBUF;
-
-  // S^T[key][query] for 2 key sub-tiles x 2 query sub-tiles
-  f32x16_t s[2][QS];
+// S^T = K Q^T of query tile qs against both 32-key halves of the tile.
+template <int D, int QS>
+__device__ __forceinline__ void tile_scores(const bf16x8_t (&kf)[2][Cfg<D>::DSTEPS],
+                                            const u32x4_t (&qf)[QS][Cfg<D>::DSTEPS], int qs,
+                                            f32x16_t (&s)[2][QS]) {
 #pragma unroll
   for (int kx = 0; kx < 2; ++kx) {
-    bf16x8_t kf[C::DSTEPS];
+    f32x16_t acc;
 #pragma unroll
-    for (int ds = 0; ds < C::DSTEPS; ++ds)
-      kf[ds] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(ks + (kx * 32 + l32) * C::KROW + (ds * 2 + lg) * 8));
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs) {
-      f32x16_t accs;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) accs[i] = 0.f;
-#pragma unroll
-      for (int ds = 0; ds < C::DSTEPS; ++ds)
-        accs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], as_bf16x8(qf[qs][ds]), accs, 0, 0, 0);
-      s[kx][qs] = accs;
-    }
+    for (int ds = 0; ds < Cfg<D>::DSTEPS; ++ds)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kx][ds], as_bf16x8(qf[qs][ds]), acc, 0, 0, 0);
+    s[kx][qs] = acc;
   }
+}
 
-  // invisible keys get kMaskedScore, whose probability underflows to exactly
-  // 0 for any c >= kMinC once m is finite; every row's first tile (tile 0)
-  // holds a visible key (key 0), so m is finite after it.
-  if constexpr (MASKED) {
+// Invisible keys (causal: key > t; tail: key >= N) get kMaskedScore, whose
+// probability underflows to exactly 0 for any c >= kMinC once m is finite;
+// every row's first tile (tile 0) holds a visible key (key 0), so m is finite
+// after it. Only a wave's diagonal tile and the ragged last tile need this.
+template <int QS>
+__device__ __forceinline__ void mask_tile(f32x16_t (&s)[2][QS], int qs, int key0, int N, int causal, int trow0,
+                                          int l32, int lg) {
+  const int t = trow0 + qs * 32 + l32;
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs) {
-      const int t = trow0 + qs * 32 + l32;
+  for (int kx = 0; kx < 2; ++kx)
 #pragma unroll
-      for (int kx = 0; kx < 2; ++kx)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + kx * 32 + lg * 16 + i;
-          const bool ok = key < N && (!causal || key <= t);
-          if (!ok) s[kx][qs][i] = kMaskedScore;
-        }
+    for (int i = 0; i < 16; ++i) {
+      const int key = key0 + kx * 32 + lg * 16 + i;
+      const bool ok = key < N && (!causal || key <= t);
+      if (!ok) s[kx][qs][i] = kMaskedScore;
     }
-  }
+}
 
-  // online softmax (fp32) against the running maximum as it stands; a
-  // query tile whose probabilities grew too large (or whose m was still
-  // -inf) takes the exact row maximum, rescales O and l and recomputes.
-  uint32_t pk[2][QS][2][4];  // [kx][qs][half][word] bf16 pairs
-  float lsum[QS];
+// Online softmax (fp32) of query tile qs against the running maximum as it
+// stands; if a lane's probabilities grew too large (or m was still -inf),
+// take the exact row maximum, rescale O and l and recompute.
+template <int D, int QS>
+__device__ __forceinline__ void tile_softmax(const f32x16_t (&s)[2][QS], int qs, uint32_t (&pk)[2][QS][2][4],
+                                             f32x16_t (&acc_o)[Cfg<D>::DSUB][QS], float (&m_run)[QS],
+                                             float (&l_run)[QS], float c) {
+  float lsum = exp_rows<QS>(s, qs, pk, c, m_run[qs]);
+  if (__ballot(!(lsum <= kSumLimit))) {
+    float mx = s[0][qs][0];
 #pragma unroll
-  for (int qs = 0; qs < QS; ++qs) lsum[qs] = exp_rows<QS>(s, qs, pk, c, m_run[qs]);
+    for (int kx = 0; kx < 2; ++kx)
 #pragma unroll
-  for (int qs = 0; qs < QS; ++qs) {
-    if (__ballot(!(lsum[qs] <= kSumLimit))) {
-      float mx = s[0][qs][0];
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kx][qs][i]);
+    const float cand = mx * c;
+    const float other = __shfl_xor(cand, 32);
+    const float mnew = fmaxf(m_run[qs], fmaxf(cand, other));
+    const float alpha = (m_run[qs] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[qs] - mnew);
+    m_run[qs] = mnew;
+    l_run[qs] *= alpha;
 #pragma unroll
-      for (int kx = 0; kx < 2; ++kx)
+    for (int x = 0; x < Cfg<D>::DSUB; ++x)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kx][qs][i]);
-      const float cand = mx * c;
-      const float other = __shfl_xor(cand, 32);
-      const float mnew = fmaxf(m_run[qs], fmaxf(cand, other));
-      const float alpha = (m_run[qs] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[qs] - mnew);
-      m_run[qs] = mnew;
-      l_run[qs] *= alpha;
-#pragma unroll
-      for (int x = 0; x < C::DSUB; ++x)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc_o[x][qs][i] *= alpha;
-      lsum[qs] = exp_rows<QS>(s, qs, pk, c, m_run[qs]);
-    }
-    l_run[qs] += lsum[qs];
+      for (int i = 0; i < 16; ++i) acc_o[x][qs][i] *= alpha;
+    lsum = exp_rows<QS>(s, qs, pk, c, m_run[qs]);
   }
+  l_run[qs] += lsum;
+}
 
-  // O^T += V^T P^T
+// O^T += V^T P^T for query tile qs.
+template <int D, int QS>
+__device__ __forceinline__ void tile_pv(const uint16_t* vs, const uint32_t (&pk)[2][QS][2][4], int qs,
+                                        f32x16_t (&acc_o)[Cfg<D>::DSUB][QS], int l32, int lg) {
+  using C = Cfg<D>;
 #pragma unroll
   for (int x = 0; x < C::DSUB; ++x)
 #pragma unroll
@@ -313,12 +302,41 @@ __device__ __forceinline__ void process_tile(const uint16_t* ks, const u32x4_t (
       for (int hh = 0; hh < 2; ++hh) {
         const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
             vs + (x * 32 + l32) * C::VROW + kx * 32 + lg * 16 + hh * 8));
-#pragma unroll
-        for (int qs = 0; qs < QS; ++qs) {
-          u32x4_t pw = {pk[kx][qs][hh][0], pk[kx][qs][hh][1], pk[kx][qs][hh][2], pk[kx][qs][hh][3]};
-          acc_o[x][qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pw), acc_o[x][qs], 0, 0, 0);
-        }
+        const u32x4_t pw = {pk[kx][qs][hh][0], pk[kx][qs][hh][1], pk[kx][qs][hh][2], pk[kx][qs][hh][3]};
+        acc_o[x][qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pw), acc_o[x][qs], 0, 0, 0);
       }
+}
+
+// One K/V tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// With two query tiles the MFMAs of one overlap the softmax of the other:
+// S(1) is issued next to the softmax of tile 0, P(0).V next to that of tile 1.
+// MASKED adds the causal and tail masks.
+template <int D, int QS, bool MASKED>
+__device__ __forceinline__ void process_tile(const uint16_t* ks, const u32x4_t (&qf)[QS][Cfg<D>::DSTEPS],
+                                             f32x16_t (&acc_o)[Cfg<D>::DSUB][QS], float (&m_run)[QS],
+                                             float (&l_run)[QS], float c, int key0, int N, int causal,
+                                             int trow0, int l32, int lg) {
+  using C = Cfg<D>;
+  const uint16_t* vs = ks + C::KBUF;
+  bf16x8_t kf[2][C::DSTEPS];
+#pragma unroll
+  for (int kx = 0; kx < 2; ++kx)
+#pragma unroll
+    for (int ds = 0; ds < C::DSTEPS; ++ds)
+      kf[kx][ds] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(ks + (kx * 32 + l32) * C::KROW + (ds * 2 + lg) * 8));
+
+  f32x16_t s[2][QS];
+  uint32_t pk[2][QS][2][4];  // [kx][qs][half][word] bf16 pairs
+  tile_scores<D, QS>(kf, qf, 0, s);
+  if constexpr (MASKED) mask_tile<QS>(s, 0, key0, N, causal, trow0, l32, lg);
+  if constexpr (QS == 2) tile_scores<D, QS>(kf, qf, 1, s);
+  tile_softmax<D, QS>(s, 0, pk, acc_o, m_run, l_run, c);
+  tile_pv<D, QS>(vs, pk, 0, acc_o, l32, lg);
+  if constexpr (QS == 2) {
+    if constexpr (MASKED) mask_tile<QS>(s, 1, key0, N, causal, trow0, l32, lg);
+    tile_softmax<D, QS>(s, 1, pk, acc_o, m_run, l_run, c);
+    tile_pv<D, QS>(vs, pk, 1, acc_o, l32, lg);
+  }
 }
 
 template <int D, int QS>
