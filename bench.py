@@ -80,18 +80,28 @@ def stored_traffic(workload: str, variant, causal: int, d: int):
     return e.get("hbm_bytes_per_launch")
 
 
+# --num-splits: key-range splits of the forward (None: the library's choice)
+NUM_SPLITS = None
+
+
+def resolved_splits(sqa, B, Hq, Hkv, N, d, causal):
+    if NUM_SPLITS is not None:
+        return NUM_SPLITS
+    return sqa.sqa_attn_fwd_num_splits(B, Hq, Hkv, N, d, causal=bool(causal))
+
+
 def time_variant(sqa, torch, q, k, v, scale, causal, steps, warmup):
     stream = torch.cuda.current_stream()
     out = torch.empty_like(q)
     for _ in range(warmup):
-        sqa.sqa_attn_fwd(q, k, v, scale=scale, causal=causal, out=out)
+        sqa.sqa_attn_fwd(q, k, v, scale=scale, causal=causal, out=out, num_splits=NUM_SPLITS)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     start.record(stream)
     for _ in range(steps):
-        sqa.sqa_attn_fwd(q, k, v, scale=scale, causal=causal, out=out)
+        sqa.sqa_attn_fwd(q, k, v, scale=scale, causal=causal, out=out, num_splits=NUM_SPLITS)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -306,7 +316,8 @@ def bench_varlen(sqa, torch, w, args):
         hq, hkv = var
         q, k, v = dev(q_all[:hq]), dev(k_all[:hkv]), dev(v_all[:hkv])
         out = torch.empty_like(q)
-        fn = lambda: sqa.sqa_attn_fwd_varlen(q, k, v, tcu, maxlen, scale=w.scale, causal=bool(causal), out=out)
+        fn = lambda: sqa.sqa_attn_fwd_varlen(q, k, v, tcu, maxlen, scale=w.scale, causal=bool(causal), out=out,
+                                             num_splits=NUM_SPLITS)
         ms = _timed(torch, fn, args.steps, args.warmup)
         del q, k, v, out
         torch.cuda.empty_cache()
@@ -348,7 +359,8 @@ def bench_varlen(sqa, torch, w, args):
         "value": round(tflops, 3), "unit": "TFLOP/s", "dtype": "bf16",
         "tokens_per_s": round(w.N / (ms * 1e-3), 1),
         "config": {"workload": w.name, "T": w.N, "sequences": lens.tolist(), "H": w.H,
-                   "H_q": variant[0], "H_kv": variant[1], "d": w.d, "causal": int(causal)},
+                   "H_q": variant[0], "H_kv": variant[1], "d": w.d, "causal": int(causal),
+                   "num_splits": resolved_splits(sqa, 1, variant[0], variant[1], maxlen, w.d, causal)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": kernel, "per_launch_flop": flops(variant[0])},
@@ -369,10 +381,14 @@ def main():
     ap.add_argument("--backward-only", action="store_true",
                     help="time only sqa_attn_bwd (for profiling) and print its object")
     ap.add_argument("--cpu-rows", type=int, default=65536)
+    ap.add_argument("--num-splits", type=int, default=None,
+                    help="key-range splits of the d=64 forward (default: the library's choice)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
                          "used to scale rocprofv3 FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
+    global NUM_SPLITS
+    NUM_SPLITS = args.num_splits
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -491,6 +507,7 @@ def main():
         "tokens_per_s": round(tokens, 1),
         "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "H_q": Hq, "H_kv": Hkv,
                    "d": w.d, "causal": int(causal), "scale": w.scale, "peaky_keys": w.peaky,
+                   "num_splits": resolved_splits(sqa, w.B, Hq, Hkv, w.N, w.d, causal),
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -109,6 +109,59 @@ sqa_status sqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void
                                int causal, float* lse, void* stream);
 
 /*
+ * sqa_attn_fwd_num_splits -- the number of key-range splits the library
+ * recommends for sqa_attn_fwd_split / sqa_attn_fwd_varlen_split on the
+ * current device (1: none). It models the launch as rounds of workgroups
+ * over the device's compute units: an encoder-style launch is split when
+ * its workgroups fill less than one round (up to 4 splits) or when two
+ * splits cut the rounds of whole-row workgroups by at least 10 % (for
+ * example one sequence much longer than the rest of a packed batch). Never
+ * under a causal mask (measured slower) and never for d != 64 or
+ * dtype != SQA_BF16. For a packed batch pass B = 1 and N = max_seqlen.
+ * Returns 1 for invalid sizes.
+ */
+int64_t sqa_attn_fwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
+                                int causal);
+
+/*
+ * sqa_attn_fwd_split_workspace_bytes -- bytes of device workspace a split
+ * forward with num_splits > 1 needs for `rows` query rows (B * H_q * N, or
+ * H_q * T packed): num_splits * rows * (d + 2) fp32 values (each range's
+ * unnormalised output, maximum and sum per row). Returns 0 when
+ * num_splits <= 1, for invalid sizes, and when d != 64 or dtype != SQA_BF16.
+ */
+size_t sqa_attn_fwd_split_workspace_bytes(int64_t rows, int64_t d, int dtype, int64_t num_splits);
+
+/*
+ * sqa_attn_fwd_split / sqa_attn_fwd_varlen_split -- sqa_attn_fwd and
+ * sqa_attn_fwd_varlen with the keys of each long sequence cut into
+ * num_splits contiguous ranges computed by separate workgroups, whose
+ * partial softmax states are merged afterwards (the streaming-softmax
+ * recurrence applied once more across the ranges; the pages do not
+ * describe a kernel, this is a scheduling choice). Same results as the
+ * unsplit calls up to fp32 rounding order. A range holds at least 1024 keys
+ * (an even number of 32-key tiles), so a sequence of at most 1024 keys is
+ * computed unsplit and a short one gets fewer than num_splits ranges.
+ *
+ *   num_splits 1..16; > 1 only for d = 64 and dtype SQA_BF16
+ *              (SQA_ERR_UNSUPPORTED otherwise). 1 behaves exactly as the
+ *              unsplit call and ignores the workspace.
+ *   workspace  device buffer of at least sqa_attn_fwd_split_workspace_bytes
+ *              bytes, 16-byte aligned, owned by the caller, not overlapping
+ *              any tensor argument; contents on return unspecified.
+ *   every other argument: as sqa_attn_fwd / sqa_attn_fwd_varlen.
+ * Errors: as those calls, plus SQA_ERR_WORKSPACE.
+ */
+sqa_status sqa_attn_fwd_split(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H_q,
+                              int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal, float* lse,
+                              int64_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+sqa_status sqa_attn_fwd_varlen_split(const void* q, const void* k, const void* v, void* o,
+                                     const int32_t* cu_seqlens, int64_t B, int64_t H_q, int64_t H_kv,
+                                     int64_t T, int64_t max_seqlen, int64_t d, int dtype, float scale,
+                                     int causal, float* lse, int64_t num_splits, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * sqa_attn_bwd_workspace_bytes -- bytes of device workspace sqa_attn_bwd
  * needs for these sizes: one fp32 pair (lse * log2(e), D_t) per query row,
  * with each (batch, query head)'s rows padded up to a multiple of 32, i.e.

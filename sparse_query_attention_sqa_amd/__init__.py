@@ -71,6 +71,16 @@ def load_library() -> ctypes.CDLL:
     lib.sqa_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
                                         f32, ctypes.c_int, vp, vp]
     lib.sqa_attn_fwd_varlen.restype = ctypes.c_int
+    lib.sqa_attn_fwd_split.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, f32,
+                                       ctypes.c_int, vp, i64, vp, ctypes.c_size_t, vp]
+    lib.sqa_attn_fwd_split.restype = ctypes.c_int
+    lib.sqa_attn_fwd_varlen_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                              f32, ctypes.c_int, vp, i64, vp, ctypes.c_size_t, vp]
+    lib.sqa_attn_fwd_varlen_split.restype = ctypes.c_int
+    lib.sqa_attn_fwd_num_splits.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.sqa_attn_fwd_num_splits.restype = i64
+    lib.sqa_attn_fwd_split_workspace_bytes.argtypes = [i64, i64, ctypes.c_int, i64]
+    lib.sqa_attn_fwd_split_workspace_bytes.restype = ctypes.c_size_t
     lib.sqa_attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.sqa_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.sqa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
@@ -143,13 +153,15 @@ def _require_device(*ts) -> None:
 
 
 def sqa_attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, out=None,
-                 return_lse: bool = False):
+                 return_lse: bool = False, num_splits: Optional[int] = None):
     """SQA attention forward on the GPU.
 
     q [B, H_q, N, d]; k, v [B, H_kv, N, d]; bf16 or fp32, contiguous, on the
     same GPU; d in {16, 32, 64, 128}. Query head i reads K/V head
     floor(i * H_kv / H_q). Returns o [B, H_q, N, d] (and lse [B, H_q, N] fp32
-    if ``return_lse``).
+    if ``return_lse``). ``num_splits``: key-range splits (bf16, d = 64 only;
+    None: the library's choice, sqa_attn_fwd_num_splits); with more than one
+    a workspace is allocated from torch's caching allocator.
     """
     torch = _torch()
     lib = load_library()
@@ -171,16 +183,41 @@ def sqa_attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False
         if out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("out must match q in shape and dtype")
     lse = torch.empty((B, H_q, N), dtype=torch.float32, device=q.device) if return_lse else None
-    st = lib.sqa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H_q, H_kv,
-                          N, d, _dtype_code(q), float(scale), int(bool(causal)),
-                          lse.data_ptr() if lse is not None else None, _stream_handle(q.device))
+    if num_splits is None:
+        num_splits = lib.sqa_attn_fwd_num_splits(B, H_q, H_kv, N, d, _dtype_code(q), int(bool(causal)))
+    if num_splits == 1:
+        st = lib.sqa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H_q, H_kv,
+                              N, d, _dtype_code(q), float(scale), int(bool(causal)),
+                              lse.data_ptr() if lse is not None else None, _stream_handle(q.device))
+    else:
+        ws, nbytes = _split_workspace(lib, B * H_q * N, d, q, num_splits)
+        st = lib.sqa_attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H_q, H_kv,
+                                    N, d, _dtype_code(q), float(scale), int(bool(causal)),
+                                    lse.data_ptr() if lse is not None else None, int(num_splits),
+                                    ws, nbytes, _stream_handle(q.device))
     _check(st)
     return (out, lse) if return_lse else out
 
 
+def _split_workspace(lib, rows: int, d: int, q, num_splits: int):
+    """Device workspace for a split forward (None, 0 when it needs none)."""
+    nbytes = lib.sqa_attn_fwd_split_workspace_bytes(rows, d, _dtype_code(q), int(num_splits))
+    if nbytes == 0:
+        return None, 0
+    buf = _torch().empty(nbytes, dtype=_torch().uint8, device=q.device)
+    return buf.data_ptr(), nbytes
+
+
+def sqa_attn_fwd_num_splits(B: int, H_q: int, H_kv: int, N: int, d: int, dtype: str = "bf16",
+                            causal: bool = False) -> int:
+    """The library's recommended key-range splits (packed batch: B = 1, N = max_seqlen)."""
+    code = SQA_BF16 if dtype == "bf16" else SQA_F32
+    return int(load_library().sqa_attn_fwd_num_splits(B, H_q, H_kv, N, d, code, int(bool(causal))))
+
+
 def sqa_attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: Optional[int] = None, *,
                         scale: Optional[float] = None, causal: bool = False, out=None,
-                        return_lse: bool = False):
+                        return_lse: bool = False, num_splits: Optional[int] = None):
     """SQA attention forward over a packed batch of variable-length sequences.
 
     q [H_q, T, d]; k, v [H_kv, T, d] (bf16 or fp32); cu_seqlens: int32 GPU
@@ -188,7 +225,8 @@ def sqa_attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: Optional[int] = None, *
     cu[b] .. cu[b+1]-1 and attends only within itself. ``max_seqlen`` (the
     longest sequence) sizes the launch; if None it is read from cu_seqlens,
     which synchronises with the device. Returns o [H_q, T, d] (and lse
-    [H_q, T] fp32 if ``return_lse``).
+    [H_q, T] fp32 if ``return_lse``). ``num_splits`` as in sqa_attn_fwd (the
+    library's choice is made for the longest sequence).
     """
     torch = _torch()
     lib = load_library()
@@ -214,10 +252,21 @@ def sqa_attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: Optional[int] = None, *
         if out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("out must match q in shape and dtype")
     lse = torch.empty((H_q, T), dtype=torch.float32, device=q.device) if return_lse else None
-    st = lib.sqa_attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                 cu_seqlens.data_ptr(), B, H_q, k.shape[0], T, int(max_seqlen), d,
-                                 _dtype_code(q), float(scale), int(bool(causal)),
-                                 lse.data_ptr() if lse is not None else None, _stream_handle(q.device))
+    if num_splits is None:
+        num_splits = lib.sqa_attn_fwd_num_splits(1 if B > 0 else 0, H_q, k.shape[0], int(max_seqlen), d,
+                                                 _dtype_code(q), int(bool(causal)))
+    if num_splits == 1:
+        st = lib.sqa_attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     cu_seqlens.data_ptr(), B, H_q, k.shape[0], T, int(max_seqlen), d,
+                                     _dtype_code(q), float(scale), int(bool(causal)),
+                                     lse.data_ptr() if lse is not None else None, _stream_handle(q.device))
+    else:
+        ws, nbytes = _split_workspace(lib, H_q * T, d, q, num_splits)
+        st = lib.sqa_attn_fwd_varlen_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                           cu_seqlens.data_ptr(), B, H_q, k.shape[0], T, int(max_seqlen), d,
+                                           _dtype_code(q), float(scale), int(bool(causal)),
+                                           lse.data_ptr() if lse is not None else None, int(num_splits),
+                                           ws, nbytes, _stream_handle(q.device))
     _check(st)
     return (out, lse) if return_lse else out
 

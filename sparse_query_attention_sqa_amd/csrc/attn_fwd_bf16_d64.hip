@@ -71,6 +71,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -108,6 +109,9 @@ struct Args {
   float c;
   uint32_t qsign;
   int causal;
+  int nsplit;    // key-range splits per workgroup's rows (1: none)
+  float* part;   // nsplit > 1: [nsplit][rows][64] unnormalised O, then [nsplit][rows][2] (m, l)
+  int64_t rows;  // query rows: B*Hq*N (packed: Hq*T)
 };
 
 // MFMA row r of a K tile holds key pi(r), so that S^T entry i of lane-half lg
@@ -282,7 +286,7 @@ struct Ctx {
   Ring ring;
   const uint16_t* kbase;
   const uint16_t* vbase;
-  int N, nt, last, tb, causal, wave;
+  int N, nt, last, diag0, causal, wave;
   int t0, t1;
   float c;
 };
@@ -294,7 +298,7 @@ __device__ __forceinline__ void step(const Ctx& cx, const Lane& ln, WaveState& w
   constexpr int AHEAD = (SLOT + 4) % NBUF;
   const int key0 = j * kTileKeys;
   const bool active = j <= cx.last;
-  const bool masked = (cx.causal && j >= 2 * cx.tb) || (key0 + kTileKeys > cx.N);
+  const bool masked = (cx.causal && j >= cx.diag0) || (key0 + kTileKeys > cx.N);
 
   // ---------------- phase A(j)
   if (active) {
@@ -341,25 +345,35 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- workgroup -> (batch*Hkv, slot range)
+  // ---- workgroup -> (key-range split, batch*Hkv, slot range)
+  // The hardware deals workgroups round-robin over the 8 XCDs. Runs of 8
+  // consecutive workgroups take one split index, cycling over the splits, so
+  // that the splits of logical workgroup wid all run on XCD wid % 8, close
+  // together in time (a split index tied to blockIdx % nsplit would put, for
+  // two splits, every first range -- under a causal mask most of the work --
+  // on the even XCDs). With one split wid = blockIdx.x.
+  const int g8 = (int)(blockIdx.x >> 3), x8 = (int)(blockIdx.x & 7);
+  const int split = g8 % a.nsplit;
+  const int wid = (g8 / a.nsplit) * 8 + x8;
+  if (wid >= a.nwg) return;
   int bkv, w_in;
   if (a.spread) {  // packed sequences, or uneven groups under a causal mask
-    spread_coords(blockIdx.x, a.n_bkv, a.wg_per_bkv, a.causal != 0, a.spread_block, bkv, w_in);
+    spread_coords(wid, a.n_bkv, a.wg_per_bkv, a.causal != 0, a.spread_block, bkv, w_in);
   } else if (a.exact_per_batch > 0) {  // uneven groups, encoder-style: XCD-contiguous, exact counts
-    const int bid = blockIdx.x;
+    const int bid = wid;
     const int per = a.nwg / kXcds, rem = a.nwg % kXcds;
     const int x = bid % kXcds, i = bid / kXcds;
     exact_coords(x * per + min(x, rem) + i, a.exact_per_batch, a.Hq, a.Hkv,
                  (a.N + kRowsPerWave - 1) / kRowsPerWave, kWaves, bkv, w_in);
   } else if (!a.causal) {  // consecutive logical workgroups on one XCD (shared L2)
-    const int bid = blockIdx.x;
+    const int bid = wid;
     const int per = a.nwg / kXcds, rem = a.nwg % kXcds;
     const int x = bid % kXcds, i = bid / kXcds;
     const int L = x * per + min(x, rem) + i;
     bkv = L / a.wg_per_bkv;
     w_in = L % a.wg_per_bkv;
   } else {  // longest (largest position block) first
-    const int L = blockIdx.x;
+    const int L = wid;
     const int wr = L / a.n_bkv;
     bkv = L % a.n_bkv;
     w_in = a.wg_per_bkv - 1 - wr;
@@ -379,8 +393,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   // key tiles the workgroup streams, and the last one this wave computes
   // (-1: none). A causal wave's rows end at key tile 2*tb+1.
   const int maxtb = min((w_in * kWaves + kWaves - 1) / g, TB - 1);
-  const int nt = a.causal ? min(2 * maxtb + 2, NT) : NT;
-  const int last = !wave_valid ? -1 : (a.causal ? min(2 * tb + 1, NT - 1) : NT - 1);
+  const int nt_all = a.causal ? min(2 * maxtb + 2, NT) : NT;
+  const int last_all = !wave_valid ? -1 : (a.causal ? min(2 * tb + 1, NT - 1) : NT - 1);
+  // Key-range split: this workgroup takes key tiles [kt0, kt0 + chunk) of
+  // its rows. Below, tiles, keys, N and the causal positions are counted
+  // from kt0, so the pipeline runs unchanged on the shifted range. With an
+  // even chunk a causal wave either has a visible key for all its rows in
+  // this range (kt0 <= 2*tb) or none (last = -1).
+  const int chunk = split_chunk(NT, a.nsplit);
+  const bool split_rows = NT > chunk;
+  const int kt0 = split * chunk;
+  if (kt0 >= nt_all) return;
+  const int nt = min(nt_all - kt0, chunk);
+  const int last = last_all < kt0 ? -1 : min(last_all - kt0, chunk - 1);
+  const int key_shift = kt0 * kTileKeys;
   const int trow0 = tb * kRowsPerWave;
 
   Lane ln;
@@ -404,8 +430,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
 
   const int64_t kvrow0 = sg.kv_base + (int64_t)kvh * sg.stride;
   const int64_t qrow0 = sg.q_base + (int64_t)h * sg.stride;
-  const uint16_t* kbase = a.k + (size_t)kvrow0 * D;
-  const uint16_t* vbase = a.v + (size_t)kvrow0 * D;
+  const uint16_t* kbase = a.k + (size_t)(kvrow0 + key_shift) * D;
+  const uint16_t* vbase = a.v + (size_t)(kvrow0 + key_shift) * D;
+  const int Nk = N - key_shift;  // keys of this sequence from the range start on
   const size_t qoff = (size_t)qrow0 * D;
 
   WaveState w;
@@ -443,24 +470,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   wait_vm_then_barrier(false);
 
   // prologue: tiles 0..3 in flight, wait for tiles 0..2, S(0,h0)
-  issue_tile<0>(ring, kbase, vbase, 0, N, wave, ln);
-  if (nt > 1) issue_tile<1>(ring, kbase, vbase, 1, N, wave, ln);
-  if (nt > 2) issue_tile<2>(ring, kbase, vbase, 2, N, wave, ln);
-  if (nt > 3) issue_tile<3>(ring, kbase, vbase, 3, N, wave, ln);
+  issue_tile<0>(ring, kbase, vbase, 0, Nk, wave, ln);
+  if (nt > 1) issue_tile<1>(ring, kbase, vbase, 1, Nk, wave, ln);
+  if (nt > 2) issue_tile<2>(ring, kbase, vbase, 2, Nk, wave, ln);
+  if (nt > 3) issue_tile<3>(ring, kbase, vbase, 3, Nk, wave, ln);
   wait_vm_then_barrier(nt > 3);
 
   Ctx cx;
   cx.ring = ring;
   cx.kbase = kbase;
   cx.vbase = vbase;
-  cx.N = N;
+  cx.N = Nk;
   cx.nt = nt;
   cx.last = last;
-  cx.tb = tb;
+  cx.diag0 = 2 * tb - kt0;
   cx.causal = a.causal;
   cx.wave = wave;
-  cx.t0 = trow0 + ln.l32;
-  cx.t1 = trow0 + 32 + ln.l32;
+  cx.t0 = trow0 + ln.l32 - key_shift;
+  cx.t1 = trow0 + 32 + ln.l32 - key_shift;
   cx.c = a.c;
 
   read_k<0>(ring, ln, w.kf);
@@ -476,6 +503,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   if (last >= 0) mfma_pv(w.vf, w.pk1, w.acc_o[1]);  // drain P(last,h1) V(last)
 
   if (!wave_valid) return;
+
+  if (split_rows) {
+    // ---- split epilogue: unnormalised O^T, m and l of this key range (fp32);
+    // the merge kernel combines the ranges. A wave with no key in this range
+    // writes nothing; the merge knows which ranges a row sees.
+    if (last < 0) return;
+    float* po = a.part + ((size_t)split * a.rows + qrow0) * D;
+    float* pml = a.part + (size_t)a.nsplit * a.rows * D + ((size_t)split * a.rows + qrow0) * 2;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const float ltot = w.l_run[qs] + __shfl_xor(w.l_run[qs], 32);
+      const int t = trow0 + qs * 32 + ln.l32;
+      if (t < N) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int ab = 0; ab < 4; ++ab) {
+            const f32x4_t v4 = {w.acc_o[qs][x][4 * ab], w.acc_o[qs][x][4 * ab + 1], w.acc_o[qs][x][4 * ab + 2],
+                                w.acc_o[qs][x][4 * ab + 3]};
+            *reinterpret_cast<f32x4_t*>(po + (size_t)t * D + x * 32 + 8 * ab + 4 * ln.lg) = v4;
+          }
+        if (ln.lg == 0) *reinterpret_cast<f32x2_t*>(pml + (size_t)t * 2) = f32x2_t{w.m_run[qs], ltot};
+      }
+    }
+    return;
+  }
 
   // ---- epilogue: O = O^T / l (bf16, nearest even); LSE = m ln2 + ln l
 #pragma unroll
@@ -499,6 +552,78 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
         a.lse[(size_t)qrow0 + t] = (w.m_run[qs] + log2f(ltot)) * 0.69314718055994531f;
     }
   }
+}
+
+// Combine the key-range splits of each query row (16 lanes per row, lane j
+// holding head dims 4j..4j+3): with the ranges' maxima m_s, sums l_s and
+// unnormalised outputs O_s, M = max m_s, O = sum 2^(m_s-M) O_s / sum 2^(m_s-M) l_s
+// (the streaming-softmax merge), written as bf16; LSE = (M + log2 L) ln 2.
+// Range s is part of row t when it holds a tile of the sequence and, under a
+// causal mask, starts at or before t; rows of sequences that were not split
+// were finished by the attention kernel.
+struct MergeArgs {
+  const float* part;
+  uint16_t* o;
+  float* lse;
+  const int* cu;  // packed sequence offsets (nullptr: dense)
+  int64_t T, rows;
+  int N, B, nsplit, causal;
+};
+
+__global__ __launch_bounds__(256) void attn_split_merge_kernel(MergeArgs a) {
+  const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int j = threadIdx.x & 15;
+  if (r >= a.rows) return;
+  int t, n;
+  if (a.cu == nullptr) {
+    t = (int)(r % a.N);
+    n = a.N;
+  } else {
+    // token p of some head; its sequence is the last b with start(b) <= p,
+    // offsets clamped into [0, T] as the attention kernel clamps them
+    const int64_t p = r % a.T;
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      int64_t st = a.cu[mid];
+      st = st < 0 ? 0 : (st > a.T ? a.T : st);
+      if (st <= p) lo = mid; else hi = mid - 1;
+    }
+    int64_t st = a.cu[lo], en = a.cu[lo + 1];
+    st = st < 0 ? 0 : (st > a.T ? a.T : st);
+    en = en < st ? st : (en > a.T ? a.T : en);
+    if (p < st || p >= en) return;
+    t = (int)(p - st);
+    n = (int)(en - st < (int64_t)a.N ? en - st : (int64_t)a.N);
+  }
+  if (t >= n) return;
+  const int NT = (n + kTileKeys - 1) / kTileKeys;
+  const int chunk = split_chunk(NT, a.nsplit);
+  if (NT <= chunk) return;
+  const float* pml = a.part + (size_t)a.nsplit * a.rows * D;
+  float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const int kt0 = s * chunk;
+    if (kt0 >= NT || (a.causal && kt0 * kTileKeys > t)) break;
+    M = fmaxf(M, pml[((size_t)s * a.rows + r) * 2]);
+  }
+  float L = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.nsplit; ++s) {
+    const int kt0 = s * chunk;
+    if (kt0 >= NT || (a.causal && kt0 * kTileKeys > t)) break;
+    const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(pml + ((size_t)s * a.rows + r) * 2);
+    const float wgt = __builtin_amdgcn_exp2f(ml[0] - M);
+    L += wgt * ml[1];
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.part + ((size_t)s * a.rows + r) * D + 4 * j);
+    acc += wgt * v;
+  }
+  const float inv = 1.0f / L;
+  u32x2_t out;
+  out[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  out[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2_t*>(a.o + (size_t)r * D + 4 * j) = out;
+  if (a.lse != nullptr && j == 0) a.lse[r] = (M + log2f(L)) * 0.69314718055994531f;
 }
 
 }  // namespace
@@ -538,8 +663,61 @@ hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream) {
   a.c = fmaxf(fabsf(p.scale) * 1.4426950408889634f, kMinC);
   a.qsign = (p.scale < 0.f) ? 0x80008000u : 0u;
   a.causal = p.causal;
-  hipLaunchKernelGGL(attn_fwd_bf16_d64_kernel, dim3(a.nwg), dim3(kThreads), 0, stream, a);
+  a.nsplit = p.nsplit < 1 ? 1 : p.nsplit;
+  a.part = p.split_ws;
+  a.rows = p.cu_seqlens != nullptr ? p.Hq * p.T : p.B * p.Hq * p.N;
+  if (a.nsplit > 1 && a.part == nullptr) return hipErrorInvalidValue;
+  // with splits the grid covers whole runs of 8 (see the kernel's decode)
+  const int64_t grid = a.nsplit == 1 ? a.nwg : ((int64_t)a.nwg + 7) / 8 * 8 * a.nsplit;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_fwd_bf16_d64_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  MergeArgs m;
+  m.part = a.part;
+  m.o = a.o;
+  m.lse = a.lse;
+  m.cu = a.cu;
+  m.T = a.T;
+  m.rows = a.rows;
+  m.N = a.N;
+  m.B = (int)p.B;
+  m.nsplit = a.nsplit;
+  m.causal = a.causal;
+  const int64_t blocks = (a.rows + 15) / 16;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_split_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, m);
   return hipGetLastError();
+}
+
+// Recommended key-range splits for this kernel, from measurements on MI355X
+// (B=1, N=32768 and a packed 32k batch whose longest sequence has 18496
+// tokens, d=64; TFLOP/s unsplit -> 2 / 3 / 4 splits):
+//  * encoder-style packed (8,4) 766 -> 845 / 834 / 825, (16,16) 740 -> 874 /
+//    803 / 830; dense (6,4) 1005 -> 1021;
+//  * causal packed (8,4) 788 -> 650 / 755 / 580, dense (6,4) 939 -> 764: the
+//    longest-first order already balances causal launches, and split
+//    workgroups ran slower per tile, so causal launches are never split.
+// Model: the workgroups of the longest sequence run in rounds of 2 * cus
+// (two per CU), r = workgroups / slots. When the whole launch fits in one
+// round, split as far as 4 ways while it still does; otherwise take two
+// splits when they cut the whole-row rounds, ceil(r) -> ceil(2r)/2, by at
+// least 10 %. Packed batch: B = 1, N = the longest sequence.
+int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, bool causal, int cus) {
+  if (causal) return 1;
+  const int64_t NT = (N + kTileKeys - 1) / kTileKeys, TB = (N + kRowsPerWave - 1) / kRowsPerWave;
+  int64_t wgs = 0;
+  for (int j = 0; j < Hkv; ++j) wgs += group_wgs(j, (int)Hq, (int)Hkv, (int)TB, kWaves);
+  const double r = (double)(wgs * B) / (2.0 * (cus > 0 ? cus : 256));
+  for (int S = 4; S >= 2; --S)
+    if (S * r <= 1.0 && NT >= (int64_t)S * kMinSplitTiles) return S;
+  if (NT >= 2 * kMinSplitTiles && ceil(2.0 * r) / 2.0 <= 0.9 * ceil(r)) return 2;
+  return 1;
+}
+
+size_t attn_split_workspace_bytes(int64_t rows, int nsplit) {
+  if (rows <= 0 || nsplit <= 1) return 0;
+  return (size_t)nsplit * (size_t)rows * (D + 2) * sizeof(float);
 }
 
 }  // namespace sqa

@@ -24,8 +24,16 @@ struct AttnProblem {
   int causal;
   const int* cu_seqlens;  // nullptr: dense
   int64_t T;              // packed: total tokens
+  // key-range splits (bf16, d = 64 only): nsplit > 1 needs split_ws of
+  // attn_split_workspace_bytes(rows, nsplit) bytes, rows = B*Hq*N (packed:
+  // Hq*T)
+  int nsplit = 1;
+  float* split_ws = nullptr;
 };
 
+size_t attn_split_workspace_bytes(int64_t rows, int nsplit);
+// recommended nsplit for the d = 64 bf16 forward on a device with `cus` CUs
+int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, bool causal, int cus);
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream);
 // head dim 64, software-pipelined (attn_fwd_bf16_d64.hip)
 hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream);

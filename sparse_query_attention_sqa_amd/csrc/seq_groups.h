@@ -111,4 +111,17 @@ __device__ __forceinline__ void exact_coords(int L, int per_batch, int Hq, int H
   w_in = r;
 }
 
+// Key-range split of the d = 64 forward: with S splits the key tiles of a
+// sequence with NT 32-key tiles are cut into chunks of split_chunk(NT, S)
+// tiles (split s takes tiles [s*chunk, (s+1)*chunk)). A chunk is even (so
+// a causal wave either sees a key of every one of its 64 rows in a split or
+// none of them) and at least kMinSplitTiles tiles; a sequence with
+// NT <= chunk is not split.
+constexpr int kMinSplitTiles = 32;
+__host__ __device__ __forceinline__ int split_chunk(int NT, int nsplit) {
+  int c = (NT + nsplit - 1) / nsplit;
+  c = (c + 1) & ~1;
+  return c < kMinSplitTiles ? kMinSplitTiles : c;
+}
+
 }  // namespace sqa

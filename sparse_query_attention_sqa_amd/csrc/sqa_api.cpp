@@ -6,6 +6,7 @@
 // synchronises: all work goes onto the caller's stream.
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -72,6 +73,48 @@ sqa_status check_attn(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d
   return SQA_OK;
 }
 
+constexpr int64_t kMaxSplits = 16;
+
+sqa_status check_splits(int64_t num_splits, int64_t d, int dtype) {
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(SQA_ERR_ARG, "num_splits must be in [1, %lld] (got %lld)", (long long)kMaxSplits,
+                (long long)num_splits);
+  if (num_splits > 1 && (d != 64 || dtype != SQA_BF16))
+    return fail(SQA_ERR_UNSUPPORTED, "key-range splits need d = 64 and bf16");
+  return SQA_OK;
+}
+
+// Workspace of a split forward: present, aligned, large enough and clear of
+// every tensor argument (tensors[i] spans sizes[i] bytes).
+sqa_status check_split_workspace(int64_t num_splits, int64_t rows, const void* ws, size_t ws_bytes,
+                                 const void* const* tensors, const size_t* sizes) {
+  if (num_splits <= 1) return SQA_OK;
+  const size_t need = sqa::attn_split_workspace_bytes(rows, (int)num_splits);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(SQA_ERR_WORKSPACE, "split workspace of %zu bytes needed (got %zu)", need, ws ? ws_bytes : (size_t)0);
+  if (!aligned(ws, 16)) return fail(SQA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(ws, need, tensors[i], sizes[i])) return fail(SQA_ERR_ARG, "workspace overlaps a tensor");
+  return SQA_OK;
+}
+
+// Compute units of the current device (256, MI355X's count, if the query
+// fails), cached per device ordinal; concurrent first calls store the same
+// value.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,8 +122,16 @@ extern "C" {
 sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H_q,
                         int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal,
                         float* lse, void* stream) {
+  return sqa_attn_fwd_split(q, k, v, o, B, H_q, H_kv, N, d, dtype, scale, causal, lse, 1, nullptr, 0, stream);
+}
+
+sqa_status sqa_attn_fwd_split(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H_q,
+                              int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal, float* lse,
+                              int64_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   sqa_status s = check_attn(B, H_q, H_kv, N, d, dtype, scale, causal);
+  if (s != SQA_OK) return s;
+  s = check_splits(num_splits, d, dtype);
   if (s != SQA_OK) return s;
   if (B == 0 || N == 0) return SQA_OK;
   if (!q || !k || !v || !o) return fail(SQA_ERR_NULL, "q, k, v and o must be non-NULL");
@@ -95,8 +146,14 @@ sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* o, in
   if (lse && (overlaps(lse, nl, o, nq) || overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) ||
               overlaps(lse, nl, v, nkv)))
     return fail(SQA_ERR_ARG, "lse overlaps another tensor");
+  const void* tensors[5] = {q, k, v, o, lse};
+  const size_t sizes[5] = {nq, nkv, nkv, nq, nl};
+  s = check_split_workspace(num_splits, B * H_q * N, workspace, workspace_bytes, tensors, sizes);
+  if (s != SQA_OK) return s;
 
   sqa::AttnProblem p{q, k, v, o, lse, B, H_q, H_kv, N, d, scale, causal};
+  p.nsplit = (int)num_splits;
+  p.split_ws = num_splits > 1 ? static_cast<float*>(workspace) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = (dtype == SQA_BF16) ? sqa::launch_attn_fwd_bf16(p, st) : sqa::launch_attn_fwd_f32(p, st);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
@@ -106,14 +163,26 @@ sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* o, in
 sqa_status sqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
                                int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t max_seqlen, int64_t d,
                                int dtype, float scale, int causal, float* lse, void* stream) {
+  return sqa_attn_fwd_varlen_split(q, k, v, o, cu_seqlens, B, H_q, H_kv, T, max_seqlen, d, dtype, scale, causal,
+                                   lse, 1, nullptr, 0, stream);
+}
+
+sqa_status sqa_attn_fwd_varlen_split(const void* q, const void* k, const void* v, void* o,
+                                     const int32_t* cu_seqlens, int64_t B, int64_t H_q, int64_t H_kv,
+                                     int64_t T, int64_t max_seqlen, int64_t d, int dtype, float scale,
+                                     int causal, float* lse, int64_t num_splits, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (B < 0 || T < 0 || max_seqlen < 0) return fail(SQA_ERR_SHAPE, "negative size");
   // shape rules of one sequence of the longest length; the total is checked below
   sqa_status s = check_attn(B > 0 ? 1 : 0, H_q, H_kv, max_seqlen, d, dtype, scale, causal);
   if (s != SQA_OK) return s;
+  s = check_splits(num_splits, d, dtype);
+  if (s != SQA_OK) return s;
   if (max_seqlen > T) return fail(SQA_ERR_SHAPE, "max_seqlen=%lld exceeds T=%lld", (long long)max_seqlen,
                                   (long long)T);
   if (T * H_q * d > kMaxElems) return fail(SQA_ERR_SHAPE, "tensor too large");
+  if (B > 0x7fffffffLL) return fail(SQA_ERR_SHAPE, "too many sequences");
   if (B == 0 || T == 0 || max_seqlen == 0) return SQA_OK;
   if (!q || !k || !v || !o || !cu_seqlens) return fail(SQA_ERR_NULL, "q, k, v, o and cu_seqlens must be non-NULL");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
@@ -128,12 +197,33 @@ sqa_status sqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void
   if (lse && (overlaps(lse, nl, o, nq) || overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) ||
               overlaps(lse, nl, v, nkv) || overlaps(lse, nl, cu_seqlens, ncu)))
     return fail(SQA_ERR_ARG, "lse overlaps another tensor");
+  if (num_splits > 1 && overlaps(workspace, workspace_bytes, cu_seqlens, ncu))
+    return fail(SQA_ERR_ARG, "workspace overlaps cu_seqlens");
+  const void* tensors[5] = {q, k, v, o, lse};
+  const size_t sizes[5] = {nq, nkv, nkv, nq, nl};
+  s = check_split_workspace(num_splits, H_q * T, workspace, workspace_bytes, tensors, sizes);
+  if (s != SQA_OK) return s;
 
   sqa::AttnProblem p{q, k, v, o, lse, B, H_q, H_kv, max_seqlen, d, scale, causal, cu_seqlens, T};
+  p.nsplit = (int)num_splits;
+  p.split_ws = num_splits > 1 ? static_cast<float*>(workspace) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = (dtype == SQA_BF16) ? sqa::launch_attn_fwd_bf16(p, st) : sqa::launch_attn_fwd_f32(p, st);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   return SQA_OK;
+}
+
+int64_t sqa_attn_fwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
+                                int causal) {
+  if (B <= 0 || N <= 0 || H_q < 1 || H_kv < 1 || H_kv > H_q || H_q > 4096 || N > kMaxN) return 1;
+  if (d != 64 || dtype != SQA_BF16) return 1;
+  return sqa::attn_fwd_auto_splits(B, H_q, H_kv, N, causal != 0, device_cus());
+}
+
+size_t sqa_attn_fwd_split_workspace_bytes(int64_t rows, int64_t d, int dtype, int64_t num_splits) {
+  if (rows <= 0 || rows > kMaxElems || num_splits <= 1 || num_splits > kMaxSplits) return 0;
+  if (d != 64 || dtype != SQA_BF16) return 0;
+  return round256(sqa::attn_split_workspace_bytes(rows, (int)num_splits));
 }
 
 size_t sqa_attn_bwd_workspace_bytes(int64_t B, int64_t H_q, int64_t N, int64_t d, int dtype) {

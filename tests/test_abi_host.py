@@ -127,6 +127,88 @@ def test_varlen_empty_is_a_noop(lib):
     assert lib.sqa_last_error().decode() == ""
 
 
+def _split(lib, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, B=1, Hq=8, Hkv=4, N=1024,
+           d=64, dtype=1, scale=0.125, causal=0, lse=None, ns=2, ws=FAKE + 0x1000000, ws_bytes=1 << 24):
+    return lib.sqa_attn_fwd_split(q, k, v, o, B, Hq, Hkv, N, d, dtype, scale, causal, lse, ns, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ns=0), 7), (dict(ns=17), 7), (dict(ns=-1), 7),
+    (dict(d=128), 3), (dict(d=32), 3), (dict(dtype=0), 3),
+    (dict(ws=None), 5), (dict(ws_bytes=100), 5),
+    (dict(ws=FAKE + 0x1000008), 4),
+    (dict(ws=FAKE + 0x200000), 7),                   # workspace over v
+    (dict(q=None), 1), (dict(Hkv=3, Hq=2), 2),
+])
+@cpu_only
+def test_split_rejects_invalid_arguments(lib, kw, code):
+    assert _split(lib, **kw) == code
+    assert lib.sqa_last_error().decode() != ""
+
+
+@cpu_only
+def test_split_varlen_rejects_invalid_arguments(lib):
+    f = lib.sqa_attn_fwd_varlen_split
+    M = 0x1000000  # 16 MiB apart: the fake tensors (4 MiB each) do not overlap
+    base = [FAKE, FAKE + M, FAKE + 2 * M, FAKE + 3 * M, FAKE + 4 * M, 4, 8, 4, 4096, 2048, 64, 1, 0.125, 1, None]
+    assert f(*base, 2, None, 0, None) == 5
+    assert f(*base, 2, FAKE + 5 * M, 1000, None) == 5               # too small
+    big = 1 << 26  # > 2 x 32768 rows x 66 x 4 B
+    assert f(*base, 2, FAKE + 4 * M, big, None) == 7                # workspace over cu_seqlens
+    assert f(*base, 2, FAKE + 3 * M, big, None) == 7                # workspace over o
+    assert f(*base, 20, FAKE + 5 * M, big, None) == 7
+    assert f(*(base[:10] + [32] + base[11:]), 2, FAKE + 5 * M, big, None) == 3
+    assert f(*(base[:5] + [0] + base[6:]), 2, None, 0, None) == 0  # B = 0: nothing to do
+
+
+@cpu_only
+def test_split_one_needs_no_workspace(lib):
+    # num_splits = 1 is the unsplit call: the workspace is not checked, so only
+    # the fake tensors' validation remains (q = NULL -> SQA_ERR_NULL)
+    assert _split(lib, q=None, ns=1, ws=None, ws_bytes=0) == 1
+
+
+def test_split_workspace_bytes(lib):
+    f = lib.sqa_attn_fwd_split_workspace_bytes
+    # 3 ranges x 100 rows x (64 + 2) fp32 = 79200 B, rounded up to 256
+    assert f(100, 64, 1, 3) == 79360
+    assert f(8 * 32768, 64, 1, 3) == 3 * 8 * 32768 * 66 * 4
+    assert f(100, 64, 1, 1) == 0
+    assert f(100, 128, 1, 2) == 0
+    assert f(100, 64, 0, 2) == 0
+    assert f(0, 64, 1, 2) == 0
+    assert f(100, 64, 1, 17) == 0
+
+
+def test_split_policy(lib):
+    """The library's split choice (round model; 256 CUs on MI355X and as the
+    fallback without a device)."""
+    f = sqa.sqa_attn_fwd_num_splits
+    # 1024 workgroups = exactly two rounds of 512: no split (the 32k headline)
+    assert f(1, 8, 4, 32768, 64) == 1
+    assert f(1, 16, 16, 32768, 64) == 1
+    assert f(1, 4, 4, 131072, 64, causal=True) == 1
+    # one 18496-token sequence of a packed batch: 580 workgroups, 1.13 rounds
+    # -> two ranges (1.5 rounds); (16,16): 2.28 rounds -> 2.5
+    assert f(1, 8, 4, 18496, 64) == 2
+    assert f(1, 16, 16, 18496, 64) == 2
+    # (6,4): 768 workgroups, 1.5 rounds -> 1.5 rounds of half-length ones
+    assert f(1, 6, 4, 32768, 64) == 2
+    # never under a causal mask
+    assert f(1, 8, 4, 18496, 64, causal=True) == 1
+    assert f(1, 8, 4, 4096, 64, causal=True) == 1
+    # a quarter of a round fills the chip with four ranges; half a round with two
+    assert f(1, 8, 4, 4096, 64) == 4
+    assert f(2, 8, 4, 4096, 64) == 2
+    # ranges keep at least 1024 keys: a 1000-key sequence is not split
+    assert f(1, 8, 4, 1000, 64) == 1
+    # only the bf16 d = 64 kernel splits
+    assert f(1, 8, 4, 18496, 128) == 1
+    assert f(1, 8, 4, 18496, 32) == 1
+    assert f(1, 8, 4, 18496, 64, dtype="f32") == 1
+    assert f(0, 8, 4, 18496, 64) == 1 and f(1, 4, 8, 18496, 64) == 1
+
+
 def test_layer_workspace_bytes(lib):
     # SQAT-m layer: B=16 N=1024 D=256 H=16 (8,4): Q and O 4 MiB each, K and V
     # 2 MiB each

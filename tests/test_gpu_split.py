@@ -1,0 +1,142 @@
+"""GPU parity of the key-range split forward (sqa_attn_fwd_split,
+sqa_attn_fwd_varlen_split) against the fp64 oracle.
+
+Each long sequence's keys are cut into ranges computed by separate
+workgroups and merged by their softmax states; the result must meet the
+same bf16 bar as the unsplit call, on every row, for forced split counts
+(2, 3, 4) over ragged lengths, both masks, uneven head groups and packed
+batches with one dominant sequence, plus the library's own choice at the
+packed 32k workload. Tolerances are in tests/parity.py.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+from oracle import attention as oracle_attention
+from oracle import attention_varlen as oracle_varlen
+from synth import draw_attn_case, draw_varlen
+from tests.parity import check_global, check_rows, log, oracle_threads, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import sparse_query_attention_sqa_amd as sqa  # noqa: E402
+
+# lse bar of the bf16 forward (natural log): the row sum adds probabilities
+# rounded to bf16 (relative error at most 2^-8 each), so |LSE - LSE_ref| <=
+# ln(1 + 2^-8) ~ 3.9e-3 plus fp32 rounding.
+LSE_TOL = 5e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    sqa.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+@functools.lru_cache(maxsize=None)
+def _dense_case(B, Hq, Hkv, N, causal):
+    q, k, v = draw_attn_case(B, Hq, Hkv, N, 64, "bf16", seed=N * 7 + Hq)
+    ref, ref_lse = oracle_attention(q, k, v, scale=0.125, causal=bool(causal), return_lse=True,
+                                    threads=oracle_threads())
+    return q, k, v, ref, ref_lse
+
+
+# N = 1100: 35 tiles, ranges of 32 and 3 tiles; N = 2113 and 4200: ragged
+# last tiles, up to four ranges; (6,4): groups of 2 and 1 heads.
+@pytest.mark.parametrize("splits", [2, 3, 4])
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 8, 4, 1100), (2, 6, 4, 2113), (1, 8, 4, 4200), (1, 3, 1, 3001)])
+def test_split_dense_all_rows(B, Hq, Hkv, N, causal, splits):
+    label = f"split dense B={B} ({Hq},{Hkv}) N={N} causal={causal} splits={splits}"
+    log(f"[case] {label}")
+    q, k, v, ref, ref_lse = _dense_case(B, Hq, Hkv, N, causal)
+    o, lse = sqa.sqa_attn_fwd(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), scale=0.125,
+                              causal=bool(causal), return_lse=True, num_splits=splits)
+    torch.cuda.synchronize()
+    o = to_host(o)
+    check_global(o, ref, "bf16", label)
+    check_rows(o, ref, label)
+    err = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse)))
+    assert err <= LSE_TOL, f"{label}: lse error {err:.3e}"
+
+
+def test_split_one_is_the_unsplit_call_bitwise():
+    q, k, v, _, _ = _dense_case(1, 8, 4, 4200, 1)
+    tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    a, la = sqa.sqa_attn_fwd(tq, tk, tv, scale=0.125, causal=True, return_lse=True, num_splits=1)
+    lib = sqa.load_library()
+    b = torch.empty_like(tq)
+    lb = torch.empty_like(la)
+    st = lib.sqa_attn_fwd_split(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), b.data_ptr(), 1, 8, 4, 4200, 64, 1,
+                                0.125, 1, lb.data_ptr(), 1, None, 0, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_split_is_deterministic_and_reuses_a_dirty_workspace():
+    q, k, v, ref, _ = _dense_case(1, 8, 4, 4200, 0)
+    tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    lib = sqa.load_library()
+    nbytes = lib.sqa_attn_fwd_split_workspace_bytes(8 * 4200, 64, 1, 3)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN bytes everywhere
+    outs = []
+    for _ in range(2):
+        o = torch.empty_like(tq)
+        st = lib.sqa_attn_fwd_split(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), 1, 8, 4, 4200, 64, 1,
+                                    0.125, 0, None, 3, ws.data_ptr(), nbytes, torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    check_global(to_host(outs[0]), ref, "bf16", "split=3 on a dirty workspace")
+
+
+# packed batches: one sequence far longer than the rest (the case the split
+# is for), empty and one-token sequences, ragged tiles
+SPLIT_MIXES = {
+    "dominant": [5000, 300, 0, 1, 1500, 64],
+    "two_long": [2113, 31, 3000],
+}
+
+
+@functools.lru_cache(maxsize=None)
+def _varlen_case(mix, Hq, Hkv, causal):
+    lens = SPLIT_MIXES[mix]
+    q, k, v, cu = draw_varlen(lens, Hq, Hkv, 64, "bf16", seed=len(lens) + Hq)
+    ref, ref_lse = oracle_varlen(q, k, v, cu, scale=0.125, causal=bool(causal), return_lse=True,
+                                 threads=oracle_threads())
+    return q, k, v, cu, ref, ref_lse
+
+
+@pytest.mark.parametrize("splits", [2, 3])
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("mix", sorted(SPLIT_MIXES))
+@pytest.mark.parametrize("Hq,Hkv", [(8, 4), (6, 4)])
+def test_split_varlen_all_rows(Hq, Hkv, mix, causal, splits):
+    label = f"split varlen {mix} ({Hq},{Hkv}) causal={causal} splits={splits}"
+    log(f"[case] {label}")
+    q, k, v, cu, ref, ref_lse = _varlen_case(mix, Hq, Hkv, causal)
+    o, lse = sqa.sqa_attn_fwd_varlen(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                                     torch.from_numpy(cu).to("cuda"), scale=0.125, causal=bool(causal),
+                                     return_lse=True, num_splits=splits)
+    torch.cuda.synchronize()
+    o = to_host(o)
+    check_global(o, ref, "bf16", label)
+    check_rows(o, ref, label)
+    err = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse)))
+    assert err <= LSE_TOL, f"{label}: lse error {err:.3e}"
+
+
+def test_split_errors_on_device():
+    q, k, v, _, _ = _dense_case(1, 8, 4, 1100, 0)
+    tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    with pytest.raises(sqa.SQAError):
+        sqa.sqa_attn_fwd(tq, tk, tv, num_splits=0)
+    with pytest.raises(sqa.SQAError):
+        sqa.sqa_attn_fwd(tq.float(), tk.float(), tv.float(), num_splits=2)  # fp32 path does not split
