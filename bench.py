@@ -84,10 +84,18 @@ def stored_traffic(workload: str, variant, causal: int, d: int):
 NUM_SPLITS = None
 
 
-def resolved_splits(sqa, B, Hq, Hkv, N, d, causal):
+def resolved_splits(sqa, B, Hq, Hkv, N, d, causal, T=0):
     if NUM_SPLITS is not None:
         return NUM_SPLITS
-    return sqa.sqa_attn_fwd_num_splits(B, Hq, Hkv, N, d, causal=bool(causal))
+    return sqa.sqa_attn_fwd_num_splits(B, Hq, Hkv, N, d, causal=bool(causal), T=T)
+
+
+def bwd_splits(sqa, B, Hq, Hkv, N, d, causal, T=0):
+    """Range splits of the timed backward: --num-splits where the backward
+    allows it (encoder-style), else the library's choice."""
+    if NUM_SPLITS is not None and not causal:
+        return NUM_SPLITS
+    return sqa.sqa_attn_bwd_num_splits(B, Hq, Hkv, N, d, causal=bool(causal), T=T)
 
 
 def time_variant(sqa, torch, q, k, v, scale, causal, steps, warmup):
@@ -141,11 +149,14 @@ def bench_backward(sqa, torch, q, k, v, w, causal, steps, warmup):
     do = torch.from_numpy(draw_upstream(tuple(q.shape), "bf16", seed=55)).to("cuda").to(torch.bfloat16)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     B, Hq, N, d = q.shape
-    ws = torch.empty(max(1, sqa.sqa_attn_bwd_workspace_bytes(B, Hq, N, d)), dtype=torch.uint8, device="cuda")
+    Hkv = k.shape[1]
+    ns = bwd_splits(sqa, B, Hq, Hkv, N, d, causal)
+    ws = torch.empty(max(1, sqa.sqa_attn_bwd_split_workspace_bytes(B, Hq, Hkv, N, d, ns)), dtype=torch.uint8,
+                     device="cuda")
 
     def fn():
         sqa.sqa_attn_bwd(q, k, v, o, do, lse, scale=w.scale, causal=bool(causal), dq=dq, dk=dk, dv=dv,
-                         workspace=ws)
+                         workspace=ws, num_splits=ns)
 
     ms = _timed(torch, fn, steps, warmup)
     fwd = counted_flops(B, Hq, N, d, causal)
@@ -156,6 +167,7 @@ def bench_backward(sqa, torch, q, k, v, w, causal, steps, warmup):
             "executed_flop": 3.5 * fwd,
             "tflops_executed": round(3.5 * fwd / (ms * 1e-3) / 1e12, 2),
             "kernels": ["bwd_rowterms_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"],
+            "num_splits": ns,
             "tokens_per_s": round(B * N / (ms * 1e-3), 1)}
 
 
@@ -333,13 +345,14 @@ def bench_varlen(sqa, torch, w, args):
         o, lse = sqa.sqa_attn_fwd_varlen(q, k, v, tcu, maxlen, scale=w.scale, causal=bool(causal), return_lse=True)
         do = dev(draw_upstream(tuple(q.shape), "bf16", seed=55))
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(sqa.sqa_attn_bwd_varlen_workspace_bytes(w.varlen, hq, w.N, w.d), dtype=torch.uint8,
-                         device="cuda")
+        ns = bwd_splits(sqa, w.varlen, hq, hkv, maxlen, w.d, causal, T=w.N)
+        ws = torch.empty(sqa.sqa_attn_bwd_varlen_split_workspace_bytes(w.varlen, hq, hkv, w.N, w.d, ns),
+                         dtype=torch.uint8, device="cuda")
         fn = lambda: sqa.sqa_attn_bwd_varlen(q, k, v, o, do, lse, tcu, maxlen, scale=w.scale, causal=bool(causal),
-                                             dq=dq, dk=dk, dv=dv, workspace=ws)
+                                             dq=dq, dk=dk, dv=dv, workspace=ws, num_splits=ns)
         bms = _timed(torch, fn, args.steps, args.warmup)
         counted = 2.5 * flops(hq)
-        backward = {"ms": round(bms, 4), "counted_flop": counted,
+        backward = {"ms": round(bms, 4), "counted_flop": counted, "num_splits": ns,
                     "tflops_counted": round(counted / (bms * 1e-3) / 1e12, 2),
                     "frac_of_peak_counted": round(counted / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del q, k, v, o, lse, do, dq, dk, dv, ws
@@ -360,7 +373,8 @@ def bench_varlen(sqa, torch, w, args):
         "tokens_per_s": round(w.N / (ms * 1e-3), 1),
         "config": {"workload": w.name, "T": w.N, "sequences": lens.tolist(), "H": w.H,
                    "H_q": variant[0], "H_kv": variant[1], "d": w.d, "causal": int(causal),
-                   "num_splits": resolved_splits(sqa, 1, variant[0], variant[1], maxlen, w.d, causal)},
+                   "num_splits": resolved_splits(sqa, w.varlen, variant[0], variant[1], maxlen, w.d, causal,
+                                                 T=w.N)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": kernel, "per_launch_flop": flops(variant[0])},

@@ -111,17 +111,19 @@ sqa_status sqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void
 /*
  * sqa_attn_fwd_num_splits -- the number of key-range splits the library
  * recommends for sqa_attn_fwd_split / sqa_attn_fwd_varlen_split on the
- * current device (1: none). It models the launch as rounds of workgroups
- * over the device's compute units: an encoder-style launch is split when
- * its workgroups fill less than one round (up to 4 splits) or when two
- * splits cut the rounds of whole-row workgroups by at least 10 % (for
- * example one sequence much longer than the rest of a packed batch). Never
- * under a causal mask (measured slower) and never for d != 64 or
- * dtype != SQA_BF16. For a packed batch pass B = 1 and N = max_seqlen.
- * Returns 1 for invalid sizes.
+ * current device (1: none). Dense (T = 0; B sequences of N tokens): it
+ * models the launch as rounds of workgroups over the device's compute
+ * units and splits an encoder-style launch when its workgroups fill less
+ * than one round (up to 4 splits) or when two splits cut the rounds of
+ * whole-row workgroups by at least 10 %. Packed (T > 0 tokens in B
+ * sequences, N = max_seqlen): 2 when the longest sequence has at least
+ * 2048 tokens and holds at least a quarter of the T (its workgroups then
+ * form the tail of the launch). Never under a causal mask (measured
+ * slower) and never for d != 64 or dtype != SQA_BF16. Returns 1 for
+ * invalid sizes.
  */
 int64_t sqa_attn_fwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
-                                int causal);
+                                int causal, int64_t T);
 
 /*
  * sqa_attn_fwd_split_workspace_bytes -- bytes of device workspace a split
@@ -231,6 +233,60 @@ sqa_status sqa_attn_bwd_varlen(const void* q, const void* k, const void* v, cons
                                int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t max_seqlen, int64_t d,
                                int dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * sqa_attn_bwd_split / sqa_attn_bwd_varlen_split -- sqa_attn_bwd and
+ * sqa_attn_bwd_varlen with the work of each long sequence cut into
+ * num_splits ranges computed by separate workgroups: dQ over ranges of keys,
+ * dK and dV over ranges of query rows. Each range leaves an fp32 partial
+ * gradient in the workspace and the partials are summed (dQ, dK and dV are
+ * plain sums over keys and queries; the pages do not describe a kernel, this
+ * is a scheduling choice). Same results as the unsplit calls up to fp32
+ * rounding order. Ranges hold at least 1024 rows (an even number of 32-row
+ * tiles), so a sequence of at most 1024 tokens is computed unsplit.
+ *
+ *   num_splits 1..16; > 1 only with causal == 0 (SQA_ERR_UNSUPPORTED
+ *              otherwise). 1 behaves exactly as the unsplit call.
+ *   workspace  device buffer of at least sqa_attn_bwd_split_workspace_bytes
+ *              (or the varlen variant) bytes, 16-byte aligned, owned by the
+ *              caller: the row terms of the unsplit call followed by the
+ *              partials; contents on return unspecified.
+ *   every other argument: as sqa_attn_bwd / sqa_attn_bwd_varlen.
+ * Errors: as those calls.
+ */
+sqa_status sqa_attn_bwd_split(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q,
+                              int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal,
+                              int64_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+sqa_status sqa_attn_bwd_varlen_split(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                     const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
+                                     int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t max_seqlen, int64_t d,
+                                     int dtype, float scale, int causal, int64_t num_splits, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
+ * sqa_attn_bwd_split_workspace_bytes / sqa_attn_bwd_varlen_split_workspace_bytes
+ * -- workspace of a split backward: the unsplit call's row terms plus, when
+ * num_splits > 1, num_splits * (rows_q + 2 * rows_kv) * d fp32 partials
+ * (rows_q = B * H_q * N, rows_kv = B * H_kv * N; packed: H_q * T and
+ * H_kv * T), each part rounded up to 256 bytes. Returns 0 for invalid sizes
+ * or unsupported d / dtype.
+ */
+size_t sqa_attn_bwd_split_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
+                                          int64_t num_splits);
+size_t sqa_attn_bwd_varlen_split_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t d,
+                                                 int dtype, int64_t num_splits);
+
+/*
+ * sqa_attn_bwd_num_splits -- the library's recommended num_splits for the
+ * split backward on the current device. Dense (T = 0): 2 for an
+ * encoder-style launch whose dK/dV or dQ workgroups fill under half a round
+ * of the device's compute units, or whose rounds two splits cut by at least
+ * 10 %. Packed (T > 0 tokens, N = max_seqlen): as sqa_attn_fwd_num_splits.
+ * Otherwise, and always under a causal mask, 1. Returns 1 for invalid sizes.
+ */
+int64_t sqa_attn_bwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
+                                int causal, int64_t T);
 
 /*
  * sqa_layer_workspace_bytes -- bytes of device workspace sqa_layer_fwd needs

@@ -28,7 +28,9 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["SQAError", "lib_path", "load_library", "sqa_attn_fwd", "sqa_attn_fwd_varlen", "sqa_attn_bwd",
+__all__ = ["SQAError", "lib_path", "load_library", "sqa_attn_fwd", "sqa_attn_fwd_varlen",
+           "sqa_attn_fwd_num_splits", "sqa_attn_bwd", "sqa_attn_bwd_num_splits",
+           "sqa_attn_bwd_split_workspace_bytes", "sqa_attn_bwd_varlen_split_workspace_bytes",
            "sqa_attn_bwd_varlen", "sqa_attn_bwd_varlen_workspace_bytes",
            "sqa_attn_bwd_workspace_bytes", "sqa_layer_fwd", "sqa_block_fwd",
            "sqa_block_workspace_bytes",
@@ -77,10 +79,22 @@ def load_library() -> ctypes.CDLL:
     lib.sqa_attn_fwd_varlen_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
                                               f32, ctypes.c_int, vp, i64, vp, ctypes.c_size_t, vp]
     lib.sqa_attn_fwd_varlen_split.restype = ctypes.c_int
-    lib.sqa_attn_fwd_num_splits.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.sqa_attn_fwd_num_splits.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, i64]
     lib.sqa_attn_fwd_num_splits.restype = i64
     lib.sqa_attn_fwd_split_workspace_bytes.argtypes = [i64, i64, ctypes.c_int, i64]
     lib.sqa_attn_fwd_split_workspace_bytes.restype = ctypes.c_size_t
+    lib.sqa_attn_bwd_split.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_int, f32, ctypes.c_int, i64, vp,
+                                                              ctypes.c_size_t, vp]
+    lib.sqa_attn_bwd_split.restype = ctypes.c_int
+    lib.sqa_attn_bwd_varlen_split.argtypes = [vp] * 10 + [i64] * 6 + [ctypes.c_int, f32, ctypes.c_int, i64, vp,
+                                                                      ctypes.c_size_t, vp]
+    lib.sqa_attn_bwd_varlen_split.restype = ctypes.c_int
+    lib.sqa_attn_bwd_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, i64]
+    lib.sqa_attn_bwd_split_workspace_bytes.restype = ctypes.c_size_t
+    lib.sqa_attn_bwd_varlen_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, i64]
+    lib.sqa_attn_bwd_varlen_split_workspace_bytes.restype = ctypes.c_size_t
+    lib.sqa_attn_bwd_num_splits.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, i64]
+    lib.sqa_attn_bwd_num_splits.restype = i64
     lib.sqa_attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.sqa_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.sqa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
@@ -184,7 +198,7 @@ def sqa_attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False
             raise ValueError("out must match q in shape and dtype")
     lse = torch.empty((B, H_q, N), dtype=torch.float32, device=q.device) if return_lse else None
     if num_splits is None:
-        num_splits = lib.sqa_attn_fwd_num_splits(B, H_q, H_kv, N, d, _dtype_code(q), int(bool(causal)))
+        num_splits = lib.sqa_attn_fwd_num_splits(B, H_q, H_kv, N, d, _dtype_code(q), int(bool(causal)), 0)
     if num_splits == 1:
         st = lib.sqa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H_q, H_kv,
                               N, d, _dtype_code(q), float(scale), int(bool(causal)),
@@ -209,10 +223,10 @@ def _split_workspace(lib, rows: int, d: int, q, num_splits: int):
 
 
 def sqa_attn_fwd_num_splits(B: int, H_q: int, H_kv: int, N: int, d: int, dtype: str = "bf16",
-                            causal: bool = False) -> int:
-    """The library's recommended key-range splits (packed batch: B = 1, N = max_seqlen)."""
+                            causal: bool = False, T: int = 0) -> int:
+    """The library's recommended key-range splits (packed batch: T tokens, N = max_seqlen)."""
     code = SQA_BF16 if dtype == "bf16" else SQA_F32
-    return int(load_library().sqa_attn_fwd_num_splits(B, H_q, H_kv, N, d, code, int(bool(causal))))
+    return int(load_library().sqa_attn_fwd_num_splits(B, H_q, H_kv, N, d, code, int(bool(causal)), T))
 
 
 def sqa_attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: Optional[int] = None, *,
@@ -253,8 +267,8 @@ def sqa_attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: Optional[int] = None, *
             raise ValueError("out must match q in shape and dtype")
     lse = torch.empty((H_q, T), dtype=torch.float32, device=q.device) if return_lse else None
     if num_splits is None:
-        num_splits = lib.sqa_attn_fwd_num_splits(1 if B > 0 else 0, H_q, k.shape[0], int(max_seqlen), d,
-                                                 _dtype_code(q), int(bool(causal)))
+        num_splits = lib.sqa_attn_fwd_num_splits(B, H_q, k.shape[0], int(max_seqlen), d, _dtype_code(q),
+                                                 int(bool(causal)), T)
     if num_splits == 1:
         st = lib.sqa_attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                      cu_seqlens.data_ptr(), B, H_q, k.shape[0], T, int(max_seqlen), d,
@@ -277,14 +291,17 @@ def sqa_attn_bwd_workspace_bytes(B: int, H_q: int, N: int, d: int, dtype: str = 
 
 
 def sqa_attn_bwd(q, k, v, o, dout, lse, *, scale: Optional[float] = None, causal: bool = False,
-                 dq=None, dk=None, dv=None, workspace=None):
+                 dq=None, dk=None, dv=None, workspace=None, num_splits: Optional[int] = None):
     """Gradients of ``sqa_attn_fwd`` for the upstream gradient ``dout``.
 
     q, o, dout [B, H_q, N, d]; k, v [B, H_kv, N, d] bf16 (d = 64 or 128); lse
     [B, H_q, N] fp32 from ``sqa_attn_fwd(..., return_lse=True)`` with the same
     scale and causal flag. Returns (dq, dk, dv); dk and dv sum over the query
     heads of each K/V head's group. ``workspace`` is an optional uint8 GPU
-    tensor of at least ``sqa_attn_bwd_workspace_bytes`` bytes.
+    tensor of at least ``sqa_attn_bwd_split_workspace_bytes`` bytes for the
+    split count used. ``num_splits``: range splits (encoder-style only; None:
+    the library's choice, sqa_attn_bwd_num_splits, reduced to 1 if a given
+    workspace is too small for it).
     """
     torch = _torch()
     lib = load_library()
@@ -313,18 +330,50 @@ def sqa_attn_bwd(q, k, v, o, dout, lse, *, scale: Optional[float] = None, causal
                 raise ValueError("gradient outputs must match their inputs in shape and dtype")
         outs.append(t)
     code = _dtype_code(q)
-    need = int(lib.sqa_attn_bwd_workspace_bytes(B, H_q, N, d, code))
+    need_of = lambda ns: int(lib.sqa_attn_bwd_split_workspace_bytes(B, H_q, H_kv, N, d, code, ns))
+    num_splits = _bwd_splits(lib, num_splits, workspace, need_of,
+                             lambda: lib.sqa_attn_bwd_num_splits(B, H_q, H_kv, N, d, code, int(bool(causal)), 0))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need_of(num_splits), 1), dtype=torch.uint8, device=q.device)
     else:
         _require_device(workspace)
-    st = lib.sqa_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                          lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
-                          B, H_q, H_kv, N, d, code, float(scale), int(bool(causal)),
-                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                          _stream_handle(q.device))
+    st = lib.sqa_attn_bwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                                B, H_q, H_kv, N, d, code, float(scale), int(bool(causal)), int(num_splits),
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                _stream_handle(q.device))
     _check(st)
     return outs[0], outs[1], outs[2]
+
+
+def _bwd_splits(lib, num_splits, workspace, need_of, auto) -> int:
+    """Range splits of a backward call: the requested count, or the library's
+    choice, reduced to 1 when the caller's workspace is too small for it."""
+    if num_splits is not None:
+        return int(num_splits)
+    ns = int(auto())
+    if ns > 1 and workspace is not None and workspace.numel() * workspace.element_size() < need_of(ns):
+        ns = 1
+    return ns
+
+
+def sqa_attn_bwd_num_splits(B: int, H_q: int, H_kv: int, N: int, d: int, dtype: str = "bf16",
+                            causal: bool = False, T: int = 0) -> int:
+    """The library's recommended range splits of the backward (packed batch: T tokens, N = max_seqlen)."""
+    code = SQA_BF16 if dtype == "bf16" else SQA_F32
+    return int(load_library().sqa_attn_bwd_num_splits(B, H_q, H_kv, N, d, code, int(bool(causal)), T))
+
+
+def sqa_attn_bwd_split_workspace_bytes(B: int, H_q: int, H_kv: int, N: int, d: int, num_splits: int,
+                                       dtype: str = "bf16") -> int:
+    code = SQA_BF16 if dtype == "bf16" else SQA_F32
+    return int(load_library().sqa_attn_bwd_split_workspace_bytes(B, H_q, H_kv, N, d, code, num_splits))
+
+
+def sqa_attn_bwd_varlen_split_workspace_bytes(B: int, H_q: int, H_kv: int, T: int, d: int, num_splits: int,
+                                              dtype: str = "bf16") -> int:
+    code = SQA_BF16 if dtype == "bf16" else SQA_F32
+    return int(load_library().sqa_attn_bwd_varlen_split_workspace_bytes(B, H_q, H_kv, T, d, code, num_splits))
 
 
 def sqa_attn_bwd_varlen_workspace_bytes(B: int, H_q: int, T: int, d: int, dtype: str = "bf16") -> int:
@@ -334,12 +383,14 @@ def sqa_attn_bwd_varlen_workspace_bytes(B: int, H_q: int, T: int, d: int, dtype:
 
 def sqa_attn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: Optional[int] = None, *,
                         scale: Optional[float] = None, causal: bool = False, dq=None, dk=None, dv=None,
-                        workspace=None):
+                        workspace=None, num_splits: Optional[int] = None):
     """Gradients of ``sqa_attn_fwd_varlen`` for the upstream gradient ``dout``.
 
     q, o, dout [H_q, T, d]; k, v [H_kv, T, d] bf16 (d = 64 or 128); lse [H_q, T] fp32
     from ``sqa_attn_fwd_varlen(..., return_lse=True)``; cu_seqlens the same
-    int32 GPU offsets. Returns (dq, dk, dv). ``max_seqlen`` as in the forward.
+    int32 GPU offsets. Returns (dq, dk, dv). ``max_seqlen`` as in the forward;
+    ``workspace`` and ``num_splits`` as in ``sqa_attn_bwd`` (the split choice
+    is made for the longest sequence).
     """
     torch = _torch()
     lib = load_library()
@@ -373,16 +424,19 @@ def sqa_attn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: Optional[
                 raise ValueError("gradient outputs must match their inputs in shape and dtype")
         outs.append(t)
     code = _dtype_code(q)
-    need = int(lib.sqa_attn_bwd_varlen_workspace_bytes(B, H_q, T, d, code))
+    need_of = lambda ns: int(lib.sqa_attn_bwd_varlen_split_workspace_bytes(B, H_q, H_kv, T, d, code, ns))
+    num_splits = _bwd_splits(lib, num_splits, workspace, need_of,
+                             lambda: lib.sqa_attn_bwd_num_splits(B, H_q, H_kv, int(max_seqlen), d, code,
+                                                                 int(bool(causal)), T))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need_of(num_splits), 1), dtype=torch.uint8, device=q.device)
     else:
         _require_device(workspace)
-    st = lib.sqa_attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                                 lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
-                                 cu_seqlens.data_ptr(), B, H_q, H_kv, T, int(max_seqlen), d, code, float(scale),
-                                 int(bool(causal)), workspace.data_ptr(),
-                                 workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+    st = lib.sqa_attn_bwd_varlen_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                       lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                                       cu_seqlens.data_ptr(), B, H_q, H_kv, T, int(max_seqlen), d, code,
+                                       float(scale), int(bool(causal)), int(num_splits), workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), _stream_handle(q.device))
     _check(st)
     return outs[0], outs[1], outs[2]
 

@@ -123,23 +123,43 @@ __global__ __launch_bounds__(256) void bwd_rowterms_kernel(RowArgs a) {
 // which is ascending w_in, or descending with `reverse`. Uneven head groups
 // or packed sequences (`spread`): the spread_coords order, which deals every
 // group and sequence over all XCDs.
-__device__ __forceinline__ void wg_coords(int spread, int block, int causal, bool reverse, int nwg, int wg_per_bkv,
-                                          int n_bkv, int& bkv, int& w_in) {
+__device__ __forceinline__ void wg_coords(int bid, int spread, int block, int causal, bool reverse, int nwg,
+                                          int wg_per_bkv, int n_bkv, int& bkv, int& w_in) {
   if (spread) {
-    spread_coords(blockIdx.x, n_bkv, wg_per_bkv, causal && reverse, block, bkv, w_in);
+    spread_coords(bid, n_bkv, wg_per_bkv, causal && reverse, block, bkv, w_in);
   } else if (!causal) {
-    const int bid = blockIdx.x;
     const int per = nwg / kXcds, rem = nwg % kXcds;
     const int x = bid % kXcds, i = bid / kXcds;
     const int L = x * per + min(x, rem) + i;
     bkv = L / wg_per_bkv;
     w_in = L % wg_per_bkv;
   } else {
-    const int L = blockIdx.x;
+    const int L = bid;
     const int wr = L / n_bkv;
     bkv = L % n_bkv;
     w_in = reverse ? wg_per_bkv - 1 - wr : wr;
   }
+}
+
+// Range splits (encoder-style only): runs of 8 consecutive workgroups take
+// one split index, cycling over the splits, so that the splits of logical
+// workgroup wid run on its XCD (wid % 8); with one split wid = blockIdx.x.
+__device__ __forceinline__ void split_decode(int nsplit, int& split, int& wid) {
+  const int g8 = (int)(blockIdx.x >> 3), x8 = (int)(blockIdx.x & 7);
+  split = g8 % nsplit;
+  wid = (g8 / nsplit) * 8 + x8;
+}
+
+// fp32 partial of one row from a transposed accumulator pair (layout of
+// store_tr_row), times mul.
+__device__ __forceinline__ void store_tr_row_f32(float* row, const f32x16_t (&o)[2], float mul, int lg) {
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int ab = 0; ab < 4; ++ab) {
+      const f32x4_t v = {o[x][4 * ab] * mul, o[x][4 * ab + 1] * mul, o[x][4 * ab + 2] * mul, o[x][4 * ab + 3] * mul};
+      *reinterpret_cast<f32x4_t*>(row + x * 32 + 8 * ab + 4 * lg) = v;
+    }
 }
 
 // acc (+)= sum over the DH halves of A_rows(h) . B(h).
@@ -194,6 +214,10 @@ struct KvArgs {
   int spread_block;  // its rotation block
   float c, scale;
   int causal;
+  int nsplit;        // query-range splits (encoder-style only; 1: none)
+  float* part_k;     // nsplit > 1: [nsplit][kv rows][D] fp32 partial dK (scaled), then dV
+  float* part_v;
+  int64_t kv_rows;   // B*Hkv*N (packed: Hkv*T)
 };
 
 struct KvRing {
@@ -348,13 +372,22 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dkdv_kernel(KvAr
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lg = lane >> 5, l32 = lane & 31;
-  int bkv, w_in;
-  wg_coords(a.spread, a.spread_block, a.causal, false, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
+  int split, wid, bkv, w_in;
+  split_decode(a.nsplit, split, wid);
+  if (wid >= a.nwg) return;
+  wg_coords(wid, a.spread, a.spread_block, a.causal, false, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
   const SeqGeom sg = seq_geom(a.cu, a.T, a.N, b, a.Hq, a.Hkv);
   const int N = sg.n;
   const int KB = (N + kTileRows - 1) / kTileRows;  // key (and query) tiles of this sequence
   if (w_in * kWaves >= KB) return;  // no keys for this workgroup (whole workgroup)
+  // query-range split (encoder-style): this workgroup streams query tiles
+  // [qa, qb) and leaves a partial dK/dV; one range (qa = 0, qb = KB) otherwise
+  const int qchunk = split_chunk(KB, a.nsplit);
+  const bool split_rows = KB > qchunk;
+  const int qa = split * qchunk;
+  if (qa >= KB) return;
+  const int qb = min(KB, qa + qchunk);
 
   KvCtx cx;
   cx.ring.p[0] = ring0;
@@ -372,7 +405,7 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dkdv_kernel(KvAr
   const HeadGroup hg = head_group(kvh, a.Hq, a.Hkv);
   cx.g = hg.count;
   cx.h0 = hg.first;
-  cx.qt0 = a.causal ? w_in * kWaves : 0;  // the first query tile any key of this workgroup sees
+  cx.qt0 = a.causal ? w_in * kWaves : qa;  // the first query tile any key of this workgroup sees
   cx.kb = w_in * kWaves + wave;
   cx.causal = a.causal;
   cx.wave = wave;
@@ -381,7 +414,7 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dkdv_kernel(KvAr
   cx.off = dma_off_shared<Dims<DH>::RB>(wave, lane);
   cx.ro = read_offsets_shared(lane);
   const bool wave_valid = cx.kb < KB;
-  const int nsteps = max(KB - cx.qt0, 0) * cx.g;
+  const int nsteps = max(qb - cx.qt0, 0) * cx.g;
   // causal: this wave's keys are first seen by query tile kb, i.e. step (kb - qt0) * g
   cx.first = !wave_valid ? nsteps : (a.causal ? min((cx.kb - cx.qt0) * cx.g, nsteps) : 0);
   const size_t kv_row0 = (size_t)(sg.kv_base + (int64_t)kvh * sg.stride);
@@ -468,6 +501,15 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dkdv_kernel(KvAr
     default: kv_drain<DH, 5>(cx, w, last & 1); break;
   }
   if (u >= N) return;
+  if (split_rows) {
+    const size_t prow = ((size_t)split * a.kv_rows + kv_row0 + u) * D;
+#pragma unroll
+    for (int h = 0; h < DH; ++h) {
+      store_tr_row_f32(a.part_k + prow + h * kD, w.acc_k[h], a.scale, lg);
+      store_tr_row_f32(a.part_v + prow + h * kD, w.acc_v[h], 1.0f, lg);
+    }
+    return;
+  }
 #pragma unroll
   for (int h = 0; h < DH; ++h) {
     store_tr_row(a.dk + (kv_row0 + u) * D + h * kD, w.acc_k[h], a.scale, lg);
@@ -506,6 +548,9 @@ struct DqArgs {
   int spread_block;  // its rotation block
   float c, scale;
   int causal;
+  int nsplit;       // key-range splits (encoder-style only; 1: none)
+  float* part_q;    // nsplit > 1: [nsplit][q rows][D] fp32 partial dQ (scaled)
+  int64_t q_rows;   // B*Hq*N (packed: Hq*T)
 };
 
 struct DqRing {
@@ -629,8 +674,10 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dq_kernel(DqArgs
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lg = lane >> 5, l32 = lane & 31;
-  int bkv, w_in;
-  wg_coords(a.spread, a.spread_block, a.causal, true, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
+  int split, wid, bkv, w_in;
+  split_decode(a.nsplit, split, wid);
+  if (wid >= a.nwg) return;
+  wg_coords(wid, a.spread, a.spread_block, a.causal, true, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
   const int slot = w_in * kWaves + wave;
   const HeadGroup hg = head_group(kvh, a.Hq, a.Hkv);
@@ -643,7 +690,15 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dq_kernel(DqArgs
   const int h = hg.first + jh;
   // key tiles the workgroup streams, and the last one this wave uses
   const int maxtb = min((w_in * kWaves + kWaves - 1) / g, TB - 1);
-  const int nt = a.causal ? maxtb + 1 : TB;
+  const int nt_all = a.causal ? maxtb + 1 : TB;
+  // key-range split (encoder-style): key tiles [ka, ka + nt) with K/V
+  // pointers, N and the tile index counted from ka; one range otherwise
+  const int kchunk = split_chunk(TB, a.nsplit);
+  const bool split_rows = TB > kchunk;
+  const int ka = split * kchunk;
+  if (ka >= nt_all) return;
+  const int nt = min(nt_all - ka, kchunk);
+  const int key_shift = ka * kTileRows;
 
   DqCtx cx;
   cx.ring.p[0] = ring0;
@@ -654,11 +709,11 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dq_kernel(DqArgs
   const int64_t kvrow0 = sg.kv_base + (int64_t)kvh * sg.stride;
   const int64_t qrow0 = sg.q_base + (int64_t)h * sg.stride;
   const int64_t rtrow0 = a.cu != nullptr ? sg.q_base + (int64_t)h * a.Np : ((int64_t)b * a.Hq + h) * a.Np;
-  cx.kbase = a.k + (size_t)kvrow0 * D;
-  cx.vbase = a.v + (size_t)kvrow0 * D;
-  cx.N = N;
-  cx.nlim = min(N, nt * kTileRows);
-  cx.last = !wave_valid ? -1 : (a.causal ? tb : TB - 1);
+  cx.kbase = a.k + (size_t)(kvrow0 + key_shift) * D;
+  cx.vbase = a.v + (size_t)(kvrow0 + key_shift) * D;
+  cx.N = N - key_shift;
+  cx.nlim = min(cx.N, nt * kTileRows);
+  cx.last = !wave_valid ? -1 : (a.causal ? tb : nt - 1);
   cx.tb = tb;
   cx.causal = a.causal;
   cx.wave = wave;
@@ -756,8 +811,79 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dq_kernel(DqArgs
   for (int hh = 0; hh < DH; ++hh) {
     if (cx.last & 1) mfma_tr(w.kt[hh], w.dsk[1], w.acc[hh]);
     else mfma_tr(w.kt[hh], w.dsk[0], w.acc[hh]);
-    store_tr_row(a.dq + ((size_t)qrow0 + cx.t) * D + hh * kD, w.acc[hh], a.scale, lg);
+    if (split_rows)
+      store_tr_row_f32(a.part_q + ((size_t)split * a.q_rows + qrow0 + cx.t) * D + hh * kD, w.acc[hh], a.scale, lg);
+    else
+      store_tr_row(a.dq + ((size_t)qrow0 + cx.t) * D + hh * kD, w.acc[hh], a.scale, lg);
   }
+}
+
+// out = sum of the range partials of each row (fp32, already scaled) as
+// bf16, one thread per 4 values. A row's ranges are those holding a 32-row
+// tile of its sequence; rows of sequences that were not split were written
+// by the gradient kernels. Rows are [B, H, N] (dense) or [H, T] (packed).
+struct SumArgs {
+  const float* part;
+  uint16_t* out;
+  const int* cu;
+  int64_t T, rows;
+  int N, B, D, nsplit;
+};
+
+__global__ __launch_bounds__(256) void bwd_split_sum_kernel(SumArgs a) {
+  const int per_row = a.D / 4;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= a.rows * per_row) return;
+  const int64_t r = e / per_row;
+  const int c4 = (int)(e % per_row);
+  int t, n;
+  if (a.cu == nullptr) {
+    t = (int)(r % a.N);
+    n = a.N;
+  } else {
+    const int64_t p = r % a.T;  // token; its sequence is the last b with start(b) <= p
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      int64_t st = a.cu[mid];
+      st = st < 0 ? 0 : (st > a.T ? a.T : st);
+      if (st <= p) lo = mid; else hi = mid - 1;
+    }
+    int64_t st = a.cu[lo], en = a.cu[lo + 1];
+    st = st < 0 ? 0 : (st > a.T ? a.T : st);
+    en = en < st ? st : (en > a.T ? a.T : en);
+    if (p < st || p >= en) return;
+    t = (int)(p - st);
+    n = (int)(en - st < (int64_t)a.N ? en - st : (int64_t)a.N);
+  }
+  if (t >= n) return;
+  const int NT = (n + kTileRows - 1) / kTileRows;
+  const int chunk = split_chunk(NT, a.nsplit);
+  if (NT <= chunk) return;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.nsplit && s * chunk < NT; ++s)
+    acc += *reinterpret_cast<const f32x4_t*>(a.part + ((size_t)s * a.rows + r) * a.D + 4 * c4);
+  u32x2_t o;
+  o[0] = pack_bf16x2(acc[0], acc[1]);
+  o[1] = pack_bf16x2(acc[2], acc[3]);
+  *reinterpret_cast<u32x2_t*>(a.out + (size_t)r * a.D + 4 * c4) = o;
+}
+
+hipError_t launch_split_sum(const float* part, void* out, const BwdProblem& p, int64_t rows, hipStream_t stream) {
+  SumArgs a;
+  a.part = part;
+  a.out = static_cast<uint16_t*>(out);
+  a.cu = p.cu_seqlens;
+  a.T = p.T;
+  a.rows = rows;
+  a.N = (int)p.N;
+  a.B = (int)p.B;
+  a.D = (int)p.D;
+  a.nsplit = p.nsplit;
+  const int64_t blocks = (rows * (p.D / 4) + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_split_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <int DH>
@@ -776,6 +902,15 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   float c = p.scale * kLog2e;
   if (fabsf(c) < 1e-30f) c = p.scale < 0.f ? -1e-30f : 1e-30f;
   float2* rt = static_cast<float2*>(p.rowterms);
+  const int nsplit = p.nsplit < 1 ? 1 : p.nsplit;
+  if (nsplit > 1 && (p.causal || p.split_ws == nullptr)) return hipErrorInvalidValue;
+  const int64_t q_rows = packed ? p.Hq * p.T : p.B * p.Hq * p.N;
+  const int64_t kv_rows = packed ? p.Hkv * p.T : p.B * p.Hkv * p.N;
+  float* part_q = p.split_ws;
+  float* part_k = part_q == nullptr ? nullptr : part_q + (size_t)nsplit * q_rows * p.D;
+  float* part_v = part_k == nullptr ? nullptr : part_k + (size_t)nsplit * kv_rows * p.D;
+  // with splits the grids cover whole runs of 8 (see split_decode)
+  auto grid_of = [&](int64_t nwg) { return nsplit == 1 ? nwg : (nwg + 7) / 8 * 8 * nsplit; };
   const int spread = (packed || p.Hq % p.Hkv != 0) ? 1 : 0;
   const int n_bkv = (int)(p.B * p.Hkv);
   const int block = spread_block(packed, n_bkv);
@@ -822,7 +957,13 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
     a.c = c;
     a.scale = p.scale;
     a.causal = p.causal;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<DH>, dim3(a.nwg), dim3(kThreads), 0, stream, a);
+    a.nsplit = nsplit;
+    a.part_k = part_k;
+    a.part_v = part_v;
+    a.kv_rows = kv_rows;
+    const int64_t grid = grid_of(a.nwg);
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<DH>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -851,12 +992,53 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
     a.c = c;
     a.scale = p.scale;
     a.causal = p.causal;
-    hipLaunchKernelGGL(bwd_dq_kernel<DH>, dim3(a.nwg), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+    a.nsplit = nsplit;
+    a.part_q = part_q;
+    a.q_rows = q_rows;
+    const int64_t grid = grid_of(a.nwg);
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bwd_dq_kernel<DH>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nsplit == 1) return e;
   }
+  hipError_t e = launch_split_sum(part_k, p.dk, p, kv_rows, stream);
+  if (e == hipSuccess) e = launch_split_sum(part_v, p.dv, p, kv_rows, stream);
+  if (e == hipSuccess) e = launch_split_sum(part_q, p.dq, p, q_rows, stream);
+  return e;
 }
 
 }  // namespace
+
+size_t attn_bwd_split_bytes(int64_t q_rows, int64_t kv_rows, int64_t D, int nsplit) {
+  if (nsplit <= 1 || q_rows <= 0 || kv_rows <= 0) return 0;
+  return (size_t)nsplit * (size_t)(q_rows + 2 * kv_rows) * (size_t)D * sizeof(float);
+}
+
+// Recommended range splits for the backward (encoder-style only), by the
+// round model of the d = 64 forward applied to both gradient kernels: the
+// dK/dV kernel's workgroups hold 128 keys of one K/V head, the dQ kernel's
+// four 32-row query slots; Dims<DH>::MINB workgroups fit per CU. Two splits
+// when they cut the rounds of the busier kernel by at least 10 %, or fill a
+// launch that is under half a round. Packed batches (T > 0 tokens, N the
+// longest sequence) as the forward's: two splits when packed_wants_split
+// (measured at 32k, longest sequence 18496 tokens, d = 64, counted TFLOP/s:
+// (8,4) 550 -> 608, (16,16) 525 -> 646). Causal launches are not split.
+int attn_bwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t T, int64_t D, bool causal,
+                         int cus) {
+  if (causal || (D != 64 && D != 128) || B <= 0 || N <= 0) return 1;
+  if (T > 0) return packed_wants_split(N, T) ? 2 : 1;
+  const int64_t tiles = (N + kTileRows - 1) / kTileRows;
+  if (tiles < 2 * kMinSplitTiles) return 1;
+  const int minb = D == 64 ? Dims<1>::MINB : Dims<2>::MINB;
+  const double slots = (double)(cus > 0 ? cus : 256) * minb;
+  int64_t wq = 0;
+  for (int j = 0; j < Hkv; ++j) wq += group_wgs(j, (int)Hq, (int)Hkv, (int)tiles, kWaves);
+  const double r_kv = (double)(B * Hkv * ((tiles + kWaves - 1) / kWaves)) / slots;
+  const double r_q = (double)(B * wq) / slots;
+  for (const double r : {r_kv, r_q})
+    if (2.0 * r <= 1.0 || ceil(2.0 * r) / 2.0 <= 0.9 * ceil(r)) return 2;
+  return 1;
+}
 
 size_t attn_bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N) {
   const int64_t Np = (N + kTileRows - 1) / kTileRows * kTileRows;

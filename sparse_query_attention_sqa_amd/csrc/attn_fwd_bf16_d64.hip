@@ -698,13 +698,16 @@ hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream) {
 //  * causal packed (8,4) 788 -> 650 / 755 / 580, dense (6,4) 939 -> 764: the
 //    longest-first order already balances causal launches, and split
 //    workgroups ran slower per tile, so causal launches are never split.
-// Model: the workgroups of the longest sequence run in rounds of 2 * cus
-// (two per CU), r = workgroups / slots. When the whole launch fits in one
-// round, split as far as 4 ways while it still does; otherwise take two
-// splits when they cut the whole-row rounds, ceil(r) -> ceil(2r)/2, by at
-// least 10 %. Packed batch: B = 1, N = the longest sequence.
-int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, bool causal, int cus) {
+// Dense: the workgroups run in rounds of 2 * cus (two per CU), r =
+// workgroups / slots. When the whole launch fits in one round, split as far
+// as 4 ways while it still does; otherwise take two splits when they cut
+// the whole-row rounds, ceil(r) -> ceil(2r)/2, by at least 10 %. Packed
+// batch (T > 0 tokens, N the longest sequence): the longest sequence's
+// workgroups reach the dispatcher late, behind the short sequences', and
+// form the tail, so two splits whenever packed_wants_split.
+int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t T, bool causal, int cus) {
   if (causal) return 1;
+  if (T > 0) return packed_wants_split(N, T) ? 2 : 1;
   const int64_t NT = (N + kTileKeys - 1) / kTileKeys, TB = (N + kRowsPerWave - 1) / kRowsPerWave;
   int64_t wgs = 0;
   for (int j = 0; j < Hkv; ++j) wgs += group_wgs(j, (int)Hq, (int)Hkv, (int)TB, kWaves);
@@ -713,6 +716,10 @@ int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, bool cau
     if (S * r <= 1.0 && NT >= (int64_t)S * kMinSplitTiles) return S;
   if (NT >= 2 * kMinSplitTiles && ceil(2.0 * r) / 2.0 <= 0.9 * ceil(r)) return 2;
   return 1;
+}
+
+bool packed_wants_split(int64_t N, int64_t T) {
+  return N >= 2 * kMinSplitTiles * kTileKeys && 4 * N >= T;
 }
 
 size_t attn_split_workspace_bytes(int64_t rows, int nsplit) {

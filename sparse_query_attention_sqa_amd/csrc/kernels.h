@@ -33,7 +33,7 @@ struct AttnProblem {
 
 size_t attn_split_workspace_bytes(int64_t rows, int nsplit);
 // recommended nsplit for the d = 64 bf16 forward on a device with `cus` CUs
-int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, bool causal, int cus);
+int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t T, bool causal, int cus);
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream);
 // head dim 64, software-pipelined (attn_fwd_bf16_d64.hip)
 hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream);
@@ -62,7 +62,16 @@ struct BwdProblem {
   int causal;
   const int* cu_seqlens;  // nullptr: dense; else packed as in AttnProblem
   int64_t T;              // packed: total tokens
+  // range splits (encoder-style only): nsplit > 1 needs split_ws of
+  // attn_bwd_split_bytes(q_rows, kv_rows, D, nsplit) bytes
+  int nsplit = 1;
+  float* split_ws = nullptr;
 };
+size_t attn_bwd_split_bytes(int64_t q_rows, int64_t kv_rows, int64_t D, int nsplit);
+// recommended nsplit for the backward on a device with `cus` CUs
+int attn_bwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t T, int64_t D, bool causal, int cus);
+// packed batches: two splits when the longest sequence (N tokens of T) is long and holds a quarter of them
+bool packed_wants_split(int64_t N, int64_t T);
 size_t attn_bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N);
 size_t attn_bwd_rowterm_bytes_packed(int64_t Hq, int64_t T);
 hipError_t launch_attn_bwd_bf16(const BwdProblem& p, hipStream_t stream);

@@ -84,6 +84,14 @@ sqa_status check_splits(int64_t num_splits, int64_t d, int dtype) {
   return SQA_OK;
 }
 
+sqa_status check_bwd_splits(int64_t num_splits, int causal) {
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(SQA_ERR_ARG, "num_splits must be in [1, %lld] (got %lld)", (long long)kMaxSplits,
+                (long long)num_splits);
+  if (num_splits > 1 && causal) return fail(SQA_ERR_UNSUPPORTED, "range splits of the backward are encoder-style only");
+  return SQA_OK;
+}
+
 // Workspace of a split forward: present, aligned, large enough and clear of
 // every tensor argument (tensors[i] spans sizes[i] bytes).
 sqa_status check_split_workspace(int64_t num_splits, int64_t rows, const void* ws, size_t ws_bytes,
@@ -214,10 +222,11 @@ sqa_status sqa_attn_fwd_varlen_split(const void* q, const void* k, const void* v
 }
 
 int64_t sqa_attn_fwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
-                                int causal) {
-  if (B <= 0 || N <= 0 || H_q < 1 || H_kv < 1 || H_kv > H_q || H_q > 4096 || N > kMaxN) return 1;
+                                int causal, int64_t T) {
+  if (B <= 0 || N <= 0 || H_q < 1 || H_kv < 1 || H_kv > H_q || H_q > 4096 || N > kMaxN || T < 0) return 1;
+  if (T > 0 && N > T) return 1;
   if (d != 64 || dtype != SQA_BF16) return 1;
-  return sqa::attn_fwd_auto_splits(B, H_q, H_kv, N, causal != 0, device_cus());
+  return sqa::attn_fwd_auto_splits(B, H_q, H_kv, N, T, causal != 0, device_cus());
 }
 
 size_t sqa_attn_fwd_split_workspace_bytes(int64_t rows, int64_t d, int dtype, int64_t num_splits) {
@@ -236,12 +245,22 @@ sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void*
                         const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q,
                         int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal,
                         void* workspace, size_t workspace_bytes, void* stream) {
+  return sqa_attn_bwd_split(q, k, v, o, dout, lse, dq, dk, dv, B, H_q, H_kv, N, d, dtype, scale, causal, 1,
+                            workspace, workspace_bytes, stream);
+}
+
+sqa_status sqa_attn_bwd_split(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q,
+                              int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal,
+                              int64_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   sqa_status s = check_attn(B, H_q, H_kv, N, d, dtype, scale, causal);
   if (s != SQA_OK) return s;
   if (dtype != SQA_BF16 || (d != 64 && d != 128))
     return fail(SQA_ERR_UNSUPPORTED, "backward supports bf16 with d=64 or d=128 (got dtype %d, d=%lld)", dtype,
                 (long long)d);
+  s = check_bwd_splits(num_splits, causal);
+  if (s != SQA_OK) return s;
   if (B == 0 || N == 0) return SQA_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
     return fail(SQA_ERR_NULL, "q, k, v, o, dout, lse, dq, dk and dv must be non-NULL");
@@ -249,7 +268,7 @@ sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void*
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return fail(SQA_ERR_ALIGN, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
   if (!aligned(lse, 4)) return fail(SQA_ERR_ALIGN, "lse must be 4-byte aligned");
-  const size_t need = sqa_attn_bwd_workspace_bytes(B, H_q, N, d, dtype);
+  const size_t need = sqa_attn_bwd_split_workspace_bytes(B, H_q, H_kv, N, d, dtype, num_splits);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(SQA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -269,6 +288,10 @@ sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void*
         return fail(SQA_ERR_ARG, "outputs and workspace must not overlap each other");
   }
   sqa::BwdProblem p{q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H_q, H_kv, N, d, scale, causal};
+  p.nsplit = (int)num_splits;
+  p.split_ws = num_splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                         sqa_attn_bwd_workspace_bytes(B, H_q, N, d, dtype))
+                              : nullptr;
   hipError_t e = sqa::launch_attn_bwd_bf16(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   return SQA_OK;
@@ -280,11 +303,42 @@ size_t sqa_attn_bwd_varlen_workspace_bytes(int64_t B, int64_t H_q, int64_t T, in
   return round256(sqa::attn_bwd_rowterm_bytes_packed(H_q, T));
 }
 
+size_t sqa_attn_bwd_split_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
+                                          int64_t num_splits) {
+  const size_t rt = sqa_attn_bwd_workspace_bytes(B, H_q, N, d, dtype);
+  if (rt == 0 || H_kv < 1 || H_kv > H_q || num_splits < 1 || num_splits > kMaxSplits) return 0;
+  return rt + round256(sqa::attn_bwd_split_bytes(B * H_q * N, B * H_kv * N, d, (int)num_splits));
+}
+
+size_t sqa_attn_bwd_varlen_split_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t d,
+                                                 int dtype, int64_t num_splits) {
+  const size_t rt = sqa_attn_bwd_varlen_workspace_bytes(B, H_q, T, d, dtype);
+  if (rt == 0 || H_kv < 1 || H_kv > H_q || num_splits < 1 || num_splits > kMaxSplits) return 0;
+  return rt + round256(sqa::attn_bwd_split_bytes(H_q * T, H_kv * T, d, (int)num_splits));
+}
+
+int64_t sqa_attn_bwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
+                                int causal, int64_t T) {
+  if (B <= 0 || N <= 0 || H_q < 1 || H_kv < 1 || H_kv > H_q || H_q > 4096 || N > kMaxN || T < 0) return 1;
+  if (T > 0 && N > T) return 1;
+  if ((d != 64 && d != 128) || dtype != SQA_BF16) return 1;
+  return sqa::attn_bwd_auto_splits(B, H_q, H_kv, N, T, d, causal != 0, device_cus());
+}
+
 sqa_status sqa_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
                                int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t max_seqlen, int64_t d,
                                int dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
                                void* stream) {
+  return sqa_attn_bwd_varlen_split(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, B, H_q, H_kv, T, max_seqlen, d,
+                                   dtype, scale, causal, 1, workspace, workspace_bytes, stream);
+}
+
+sqa_status sqa_attn_bwd_varlen_split(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                     const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
+                                     int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t max_seqlen, int64_t d,
+                                     int dtype, float scale, int causal, int64_t num_splits, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (B < 0 || T < 0 || max_seqlen < 0) return fail(SQA_ERR_SHAPE, "negative size");
   sqa_status s = check_attn(B > 0 ? 1 : 0, H_q, H_kv, max_seqlen, d, dtype, scale, causal);
@@ -295,6 +349,9 @@ sqa_status sqa_attn_bwd_varlen(const void* q, const void* k, const void* v, cons
   if (max_seqlen > T) return fail(SQA_ERR_SHAPE, "max_seqlen=%lld exceeds T=%lld", (long long)max_seqlen,
                                   (long long)T);
   if (T > kMaxN || T * H_q * d > kMaxElems) return fail(SQA_ERR_SHAPE, "tensor too large");
+  if (B > 0x7fffffffLL) return fail(SQA_ERR_SHAPE, "too many sequences");
+  s = check_bwd_splits(num_splits, causal);
+  if (s != SQA_OK) return s;
   if (B == 0 || T == 0 || max_seqlen == 0) return SQA_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens)
     return fail(SQA_ERR_NULL, "q, k, v, o, dout, lse, dq, dk, dv and cu_seqlens must be non-NULL");
@@ -302,7 +359,7 @@ sqa_status sqa_attn_bwd_varlen(const void* q, const void* k, const void* v, cons
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return fail(SQA_ERR_ALIGN, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
   if (!aligned(lse, 4) || !aligned(cu_seqlens, 4)) return fail(SQA_ERR_ALIGN, "lse and cu_seqlens must be 4-byte aligned");
-  const size_t need = sqa_attn_bwd_varlen_workspace_bytes(B, H_q, T, d, dtype);
+  const size_t need = sqa_attn_bwd_varlen_split_workspace_bytes(B, H_q, H_kv, T, d, dtype, num_splits);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(SQA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -323,6 +380,10 @@ sqa_status sqa_attn_bwd_varlen(const void* q, const void* k, const void* v, cons
   }
   sqa::BwdProblem p{q,  k,  v,  o,   dout, lse,       dq,    dk,     dv,         workspace,
                     B,  H_q, H_kv, max_seqlen, d, scale, causal, cu_seqlens, T};
+  p.nsplit = (int)num_splits;
+  p.split_ws = num_splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                         sqa_attn_bwd_varlen_workspace_bytes(B, H_q, T, d, dtype))
+                              : nullptr;
   hipError_t e = sqa::launch_attn_bwd_bf16(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   return SQA_OK;

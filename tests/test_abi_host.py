@@ -188,14 +188,19 @@ def test_split_policy(lib):
     assert f(1, 8, 4, 32768, 64) == 1
     assert f(1, 16, 16, 32768, 64) == 1
     assert f(1, 4, 4, 131072, 64, causal=True) == 1
-    # one 18496-token sequence of a packed batch: 580 workgroups, 1.13 rounds
-    # -> two ranges (1.5 rounds); (16,16): 2.28 rounds -> 2.5
+    # packed 32k batch whose longest sequence has 18496 tokens: two ranges
+    assert f(8, 8, 4, 18496, 64, T=32768) == 2
+    assert f(8, 16, 16, 18496, 64, T=32768) == 2
+    # ... but not when the longest holds under a quarter of the tokens, or is short
+    assert f(64, 8, 4, 8000, 64, T=65536) == 1
+    assert f(8, 8, 4, 2000, 64, T=4000) == 1
+    # one dense 18496-token sequence: 580 workgroups, 1.13 rounds -> 1.5
     assert f(1, 8, 4, 18496, 64) == 2
-    assert f(1, 16, 16, 18496, 64) == 2
     # (6,4): 768 workgroups, 1.5 rounds -> 1.5 rounds of half-length ones
     assert f(1, 6, 4, 32768, 64) == 2
     # never under a causal mask
     assert f(1, 8, 4, 18496, 64, causal=True) == 1
+    assert f(8, 8, 4, 18496, 64, causal=True, T=32768) == 1
     assert f(1, 8, 4, 4096, 64, causal=True) == 1
     # a quarter of a round fills the chip with four ranges; half a round with two
     assert f(1, 8, 4, 4096, 64) == 4
@@ -207,6 +212,37 @@ def test_split_policy(lib):
     assert f(1, 8, 4, 18496, 32) == 1
     assert f(1, 8, 4, 18496, 64, dtype="f32") == 1
     assert f(0, 8, 4, 18496, 64) == 1 and f(1, 4, 8, 18496, 64) == 1
+
+
+def test_bwd_split_workspace_and_policy(lib):
+    f = lib.sqa_attn_bwd_split_workspace_bytes
+    rt = lib.sqa_attn_bwd_workspace_bytes(1, 8, 1000, 64, 1)
+    assert f(1, 8, 4, 1000, 64, 1, 1) == rt
+    # 2 ranges x (8000 dQ rows + 2 x 4000 dK/dV rows) x 64 fp32
+    assert f(1, 8, 4, 1000, 64, 1, 2) == rt + 2 * 16000 * 64 * 4
+    assert f(1, 8, 4, 1000, 64, 1, 0) == 0 and f(1, 8, 4, 1000, 64, 1, 17) == 0
+    assert f(1, 4, 8, 1000, 64, 1, 2) == 0 and f(1, 8, 4, 1000, 32, 1, 2) == 0
+    g = lib.sqa_attn_bwd_varlen_split_workspace_bytes
+    assert g(3, 8, 4, 5000, 64, 1, 1) == lib.sqa_attn_bwd_varlen_workspace_bytes(3, 8, 5000, 64, 1)
+    assert g(3, 8, 4, 5000, 64, 1, 3) == g(3, 8, 4, 5000, 64, 1, 1) + 3 * (40000 + 40000) * 64 * 4
+    n = sqa.sqa_attn_bwd_num_splits
+    assert n(1, 8, 4, 32768, 64) == 1                  # 1024 / 512 dK/dV workgroups per slot: whole rounds
+    assert n(1, 8, 4, 18496, 64) == 2                  # 580 dK/dV workgroups: 1.13 rounds
+    assert n(8, 16, 16, 18496, 64, T=32768) == 2       # packed, longest sequence 56 % of the tokens
+    assert n(1, 8, 4, 18496, 64, causal=True) == 1     # never under a causal mask
+    assert n(1, 8, 4, 18496, 32) == 1 and n(1, 8, 4, 1000, 64) == 1
+
+
+@cpu_only
+def test_bwd_split_rejects_invalid_arguments(lib):
+    M = 0x1000000
+    args = [FAKE + i * M for i in range(9)] + [1, 8, 4, 1000, 64, 1, 0.125, 0]
+    f = lib.sqa_attn_bwd_split
+    assert f(*args, 0, FAKE + 9 * M, 1 << 24, None) == 7
+    assert f(*args, 17, FAKE + 9 * M, 1 << 24, None) == 7
+    assert f(*(args[:-1] + [1]), 2, FAKE + 9 * M, 1 << 24, None) == 3   # causal
+    assert f(*args, 2, FAKE + 9 * M, 1000, None) == 5                   # too small for the partials
+    assert f(*args, 2, FAKE + 9 * M + 8, 1 << 24, None) == 4
 
 
 def test_layer_workspace_bytes(lib):

@@ -140,3 +140,84 @@ def test_split_errors_on_device():
         sqa.sqa_attn_fwd(tq, tk, tv, num_splits=0)
     with pytest.raises(sqa.SQAError):
         sqa.sqa_attn_fwd(tq.float(), tk.float(), tv.float(), num_splits=2)  # fp32 path does not split
+
+
+# ------------------------------------------------------------- backward
+# dQ over key ranges, dK/dV over query ranges, summed in fp32: every element
+# against the fp64 oracle, the bf16 bar with the absolute floor for
+# gradients that can vanish (tests/parity.py).
+from oracle import attention_bwd as oracle_bwd  # noqa: E402
+from oracle import attention_bwd_varlen as oracle_bwd_varlen  # noqa: E402
+from synth import draw_upstream  # noqa: E402
+from tests.parity import ROW_FLOOR  # noqa: E402
+
+
+@functools.lru_cache(maxsize=None)
+def _bwd_dense_case(B, Hq, Hkv, N, d):
+    q, k, v = draw_attn_case(B, Hq, Hkv, N, d, "bf16", seed=N * 3 + Hq + d)
+    do = draw_upstream(q.shape, "bf16", seed=N + 5)
+    ref = oracle_bwd(q, k, v, do, scale=0.125, causal=False, threads=oracle_threads())
+    return q, k, v, do, ref
+
+
+@pytest.mark.parametrize("splits", [2, 3])
+@pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 8, 4, 2113, 64), (2, 6, 4, 1100, 64), (1, 4, 2, 3001, 128)])
+def test_split_bwd_dense_all_elements(B, Hq, Hkv, N, d, splits):
+    label = f"split bwd B={B} ({Hq},{Hkv}) N={N} d={d} splits={splits}"
+    log(f"[case] {label}")
+    q, k, v, do, ref = _bwd_dense_case(B, Hq, Hkv, N, d)
+    tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o, lse = sqa.sqa_attn_fwd(tq, tk, tv, scale=0.125, return_lse=True, num_splits=1)
+    got = sqa.sqa_attn_bwd(tq, tk, tv, o, to_dev(do, "bf16"), lse, scale=0.125, num_splits=splits)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        check_global(to_host(g), r, "bf16", f"{label} {name}", floor=ROW_FLOOR)
+
+
+@pytest.mark.parametrize("splits", [2, 3])
+@pytest.mark.parametrize("mix", sorted(SPLIT_MIXES))
+def test_split_bwd_varlen_all_elements(mix, splits):
+    label = f"split bwd varlen {mix} (8,4) splits={splits}"
+    log(f"[case] {label}")
+    q, k, v, cu = draw_varlen(SPLIT_MIXES[mix], 8, 4, 64, "bf16", seed=len(mix) + 11)
+    do = draw_upstream(q.shape, "bf16", seed=len(mix) + 12)
+    tq, tk, tv, tdo = (to_dev(a, "bf16") for a in (q, k, v, do))
+    tcu = torch.from_numpy(cu).to("cuda")
+    o, lse = sqa.sqa_attn_fwd_varlen(tq, tk, tv, tcu, scale=0.125, return_lse=True)
+    got = sqa.sqa_attn_bwd_varlen(tq, tk, tv, o, tdo, lse, tcu, scale=0.125, num_splits=splits)
+    torch.cuda.synchronize()
+    ref = oracle_bwd_varlen(q, k, v, do, cu, scale=0.125, causal=False, threads=oracle_threads())
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        check_global(to_host(g), r, "bf16", f"{label} {name}", floor=ROW_FLOOR)
+
+
+def test_split_bwd_one_is_the_unsplit_call_bitwise():
+    q, k, v, do, _ = _bwd_dense_case(1, 8, 4, 2113, 64)
+    tq, tk, tv, tdo = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(do, "bf16")
+    o, lse = sqa.sqa_attn_fwd(tq, tk, tv, scale=0.125, return_lse=True, num_splits=1)
+    a = sqa.sqa_attn_bwd(tq, tk, tv, o, tdo, lse, scale=0.125, num_splits=1)
+    lib = sqa.load_library()
+    need = lib.sqa_attn_bwd_workspace_bytes(1, 8, 2113, 64, 1)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    b = [torch.empty_like(t) for t in (tq, tk, tv)]
+    st = lib.sqa_attn_bwd(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), tdo.data_ptr(), lse.data_ptr(),
+                          b[0].data_ptr(), b[1].data_ptr(), b[2].data_ptr(), 1, 8, 4, 2113, 64, 1, 0.125, 0,
+                          ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_split_bwd_rejects_causal_and_small_workspace():
+    q, k, v, do, _ = _bwd_dense_case(1, 8, 4, 2113, 64)
+    tq, tk, tv, tdo = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(do, "bf16")
+    o, lse = sqa.sqa_attn_fwd(tq, tk, tv, scale=0.125, causal=True, return_lse=True)
+    with pytest.raises(sqa.SQAError):
+        sqa.sqa_attn_bwd(tq, tk, tv, o, tdo, lse, scale=0.125, causal=True, num_splits=2)
+    small = torch.empty(sqa.sqa_attn_bwd_workspace_bytes(1, 8, 2113, 64), dtype=torch.uint8, device="cuda")
+    with pytest.raises(sqa.SQAError):
+        sqa.sqa_attn_bwd(tq, tk, tv, o, tdo, lse, scale=0.125, workspace=small, num_splits=2)
+    # the library's choice falls back to one range when the given workspace is too small for more
+    sqa.sqa_attn_bwd(tq, tk, tv, o, tdo, lse, scale=0.125, workspace=small)
+    torch.cuda.synchronize()
