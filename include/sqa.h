@@ -130,7 +130,8 @@ int64_t sqa_attn_fwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N,
  * forward with num_splits > 1 needs for `rows` query rows (B * H_q * N, or
  * H_q * T packed): num_splits * rows * (d + 2) fp32 values (each range's
  * unnormalised output, maximum and sum per row). Returns 0 when
- * num_splits <= 1, for invalid sizes, and when d != 64 or dtype != SQA_BF16.
+ * num_splits <= 1, for invalid sizes, and when d is not 16, 32 or 64 or
+ * dtype != SQA_BF16.
  */
 size_t sqa_attn_fwd_split_workspace_bytes(int64_t rows, int64_t d, int dtype, int64_t num_splits);
 
@@ -141,11 +142,14 @@ size_t sqa_attn_fwd_split_workspace_bytes(int64_t rows, int64_t d, int dtype, in
  * partial softmax states are merged afterwards (the streaming-softmax
  * recurrence applied once more across the ranges; the pages do not
  * describe a kernel, this is a scheduling choice). Same results as the
- * unsplit calls up to fp32 rounding order. A range holds at least 1024 keys
- * (an even number of 32-key tiles), so a sequence of at most 1024 keys is
- * computed unsplit and a short one gets fewer than num_splits ranges.
+ * unsplit calls up to fp32 rounding order. At d = 64 a range holds at least
+ * 1024 keys (an even number of 32-key tiles), at d = 16 and 32 at least 256
+ * (64-key tiles), so a short sequence is computed unsplit or gets fewer
+ * than num_splits ranges. sqa_attn_fwd_num_splits only ever recommends
+ * splits at d = 64: at d = 16 under a causal mask (the SQAT-m layer's
+ * shape) split launches measured slower.
  *
- *   num_splits 1..16; > 1 only for d = 64 and dtype SQA_BF16
+ *   num_splits 1..16; > 1 only for d = 16, 32 or 64 and dtype SQA_BF16
  *              (SQA_ERR_UNSUPPORTED otherwise). 1 behaves exactly as the
  *              unsplit call and ignores the workspace.
  *   workspace  device buffer of at least sqa_attn_fwd_split_workspace_bytes

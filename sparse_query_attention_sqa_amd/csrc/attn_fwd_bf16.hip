@@ -50,6 +50,7 @@
 
 #include "kernels.h"
 #include "seq_groups.h"
+#include "split_merge.h"
 
 namespace sqa {
 namespace {
@@ -58,6 +59,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -105,6 +107,9 @@ struct Args {
   float c;         // |scale| * log2(e)
   uint32_t qsign;  // 0x80008000 flips both bf16 halves when scale < 0
   int causal;
+  int nsplit;      // key-range splits (1: none)
+  float* part;     // nsplit > 1: [nsplit][rows][D] unnormalised O, then [nsplit][rows][2] (m, l)
+  int64_t rows;    // query rows: B*Hq*N (packed: Hq*T)
 };
 
 // MFMA row r of a 32-key sub-tile holds key pi(r); the accumulator entry i
@@ -350,12 +355,18 @@ __global__ __launch_bounds__(kThreads, QS == 1 ? 4 : 2) void attn_fwd_bf16_kerne
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, lg = lane >> 5;
 
-  // ---- workgroup -> (batch*Hkv, slot range)
+  // ---- workgroup -> (key-range split, batch*Hkv, slot range); runs of 8
+  // consecutive workgroups take one split index, so that the splits of
+  // logical workgroup wid run on XCD wid % 8 (one split: wid = blockIdx.x)
+  const int g8 = (int)(blockIdx.x >> 3), x8 = (int)(blockIdx.x & 7);
+  const int split = g8 % a.nsplit;
+  const int wid = (g8 / a.nsplit) * 8 + x8;
+  if (wid >= a.nwg) return;
   int bkv, w_in;
   if (a.spread) {  // packed sequences, or uneven groups under a causal mask
-    spread_coords(blockIdx.x, a.n_bkv, a.wg_per_bkv, a.causal != 0, a.spread_block, bkv, w_in);
+    spread_coords(wid, a.n_bkv, a.wg_per_bkv, a.causal != 0, a.spread_block, bkv, w_in);
   } else if (a.exact_per_batch > 0) {  // uneven groups, encoder-style: XCD-contiguous, exact counts
-    const int bid = blockIdx.x;
+    const int bid = wid;
     const int per = a.nwg / kXcds, rem = a.nwg % kXcds;
     const int x = bid % kXcds, i = bid / kXcds;
     exact_coords(x * per + min(x, rem) + i, a.exact_per_batch, a.Hq, a.Hkv,
@@ -363,14 +374,14 @@ __global__ __launch_bounds__(kThreads, QS == 1 ? 4 : 2) void attn_fwd_bf16_kerne
   } else if (!a.causal) {
     // consecutive logical workgroups on one XCD (hardware deals blockIdx
     // round-robin over the XCDs)
-    const int bid = blockIdx.x;
+    const int bid = wid;
     const int per = a.nwg / kXcds, rem = a.nwg % kXcds;
     const int x = bid % kXcds, i = bid / kXcds;
     const int L = x * per + min(x, rem) + i;
     bkv = L / a.wg_per_bkv;
     w_in = L % a.wg_per_bkv;
   } else {  // longest (largest position block) first
-    const int L = blockIdx.x;
+    const int L = wid;
     const int wr = L / a.n_bkv;
     bkv = L % a.n_bkv;
     w_in = a.wg_per_bkv - 1 - wr;
@@ -398,7 +409,16 @@ __global__ __launch_bounds__(kThreads, QS == 1 ? 4 : 2) void attn_fwd_bf16_kerne
     nt = NT;
   }
   const int diag = min((tb * kRowsPerWave + kRowsPerWave - 1) / kTileKeys, NT - 1);
-  const int wave_last = a.causal ? diag : nt - 1;
+  // key-range split: this workgroup streams key tiles [kt0, kt_end) of its
+  // rows. A causal wave holds at most 64 rows, one tile's worth, so it sees
+  // a key of every row in a range that starts at or before its diagonal tile
+  // (kt0 * 64 <= its first row) and none in a later one.
+  const int chunk = split_chunk(NT, a.nsplit, kMinSplitTiles64, false);
+  const bool split_rows = NT > chunk;
+  const int kt0 = split * chunk;
+  if (kt0 >= nt) return;
+  const int kt_end = min(nt, kt0 + chunk);
+  const int wave_last = min(a.causal ? diag : nt - 1, kt_end - 1);
 
   const int64_t kvrow0 = sg.kv_base + (int64_t)kvh * sg.stride;
   const int64_t qrow0 = sg.q_base + (int64_t)h * sg.stride;
@@ -443,15 +463,15 @@ __global__ __launch_bounds__(kThreads, QS == 1 ? 4 : 2) void attn_fwd_bf16_kerne
   }
 
   TileRegs<D> regs;
-  load_tile<D>(regs, kbase, vbase, 0, N, tid);
+  load_tile<D>(regs, kbase, vbase, kt0, N, tid);
   __syncthreads();  // zero-fill above is complete before tile stores
   store_tile<D>(regs, smem, tid);
   __syncthreads();
 
   const float c = a.c;
-  for (int kt = 0; kt < nt; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nt) load_tile<D>(regs, kbase, vbase, kt + 1, N, tid);
+  for (int kt = kt0; kt < kt_end; ++kt) {
+    const int cur = (kt - kt0) & 1;
+    if (kt + 1 < kt_end) load_tile<D>(regs, kbase, vbase, kt + 1, N, tid);
 
     if (wave_valid && kt <= wave_last) {
       const uint16_t* ks = smem + cur * C::BUF;
@@ -465,11 +485,39 @@ __global__ __launch_bounds__(kThreads, QS == 1 ? 4 : 2) void attn_fwd_bf16_kerne
                                    tb * kRowsPerWave, l32, lg);
     }
 
-    if (kt + 1 < nt) store_tile<D>(regs, smem + (cur ^ 1) * C::BUF, tid);
+    if (kt + 1 < kt_end) store_tile<D>(regs, smem + (cur ^ 1) * C::BUF, tid);
     __syncthreads();
   }
 
   if (!wave_valid) return;
+
+  if (split_rows) {
+    // ---- split epilogue: unnormalised O^T, m and l of this key range (fp32)
+    if (wave_last < kt0) return;  // no key of this range for the wave's rows
+    float* po = a.part + ((size_t)split * a.rows + qrow0) * D;
+    float* pml = a.part + (size_t)a.nsplit * a.rows * D + ((size_t)split * a.rows + qrow0) * 2;
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      const float ltot = l_run[qs] + __shfl_xor(l_run[qs], 32);
+      const int t = tb * kRowsPerWave + qs * 32 + l32;
+      if (t < N) {
+#pragma unroll
+        for (int x = 0; x < C::DSUB; ++x) {
+          const int d0 = x * 32 + lg * 16;
+          if (d0 < D) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const f32x4_t v4 = {acc_o[x][qs][4 * e], acc_o[x][qs][4 * e + 1], acc_o[x][qs][4 * e + 2],
+                                  acc_o[x][qs][4 * e + 3]};
+              *reinterpret_cast<f32x4_t*>(po + (size_t)t * D + d0 + 4 * e) = v4;
+            }
+          }
+        }
+        if (lg == 0) *reinterpret_cast<f32x2_t*>(pml + (size_t)t * 2) = f32x2_t{m_run[qs], ltot};
+      }
+    }
+    return;
+  }
 
   // ---- epilogue: O = O^T / l (bf16, nearest even), LSE = m ln2 + ln l
 #pragma unroll
@@ -535,8 +583,31 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
   a.c = fmaxf(fabsf(p.scale) * 1.4426950408889634f, kMinC);
   a.qsign = (p.scale < 0.f) ? 0x80008000u : 0u;
   a.causal = p.causal;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QS>), dim3(a.nwg), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  a.nsplit = p.nsplit < 1 ? 1 : p.nsplit;
+  a.part = p.split_ws;
+  a.rows = p.cu_seqlens != nullptr ? p.Hq * p.T : p.B * p.Hq * p.N;
+  if (a.nsplit > 1 && a.part == nullptr) return hipErrorInvalidValue;
+  // with splits the grid covers whole runs of 8 (see the kernel's decode)
+  const int64_t grid = a.nsplit == 1 ? a.nwg : ((int64_t)a.nwg + 7) / 8 * 8 * a.nsplit;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QS>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  SplitMergeArgs m;
+  m.part = a.part;
+  m.o = a.o;
+  m.lse = a.lse;
+  m.cu = a.cu;
+  m.T = a.T;
+  m.rows = a.rows;
+  m.N = a.N;
+  m.B = (int)p.B;
+  m.nsplit = a.nsplit;
+  m.causal = a.causal;
+  m.tile_keys = kTileKeys;
+  m.min_tiles = kMinSplitTiles64;
+  m.even = 0;
+  return launch_split_merge<D>(m, stream);
 }
 
 }  // namespace

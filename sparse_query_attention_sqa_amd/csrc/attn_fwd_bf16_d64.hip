@@ -63,6 +63,7 @@
 
 #include "kernels.h"
 #include "seq_groups.h"
+#include "split_merge.h"
 
 namespace sqa {
 namespace {
@@ -554,78 +555,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   }
 }
 
-// Combine the key-range splits of each query row (16 lanes per row, lane j
-// holding head dims 4j..4j+3): with the ranges' maxima m_s, sums l_s and
-// unnormalised outputs O_s, M = max m_s, O = sum 2^(m_s-M) O_s / sum 2^(m_s-M) l_s
-// (the streaming-softmax merge), written as bf16; LSE = (M + log2 L) ln 2.
-// Range s is part of row t when it holds a tile of the sequence and, under a
-// causal mask, starts at or before t; rows of sequences that were not split
-// were finished by the attention kernel.
-struct MergeArgs {
-  const float* part;
-  uint16_t* o;
-  float* lse;
-  const int* cu;  // packed sequence offsets (nullptr: dense)
-  int64_t T, rows;
-  int N, B, nsplit, causal;
-};
-
-__global__ __launch_bounds__(256) void attn_split_merge_kernel(MergeArgs a) {
-  const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int j = threadIdx.x & 15;
-  if (r >= a.rows) return;
-  int t, n;
-  if (a.cu == nullptr) {
-    t = (int)(r % a.N);
-    n = a.N;
-  } else {
-    // token p of some head; its sequence is the last b with start(b) <= p,
-    // offsets clamped into [0, T] as the attention kernel clamps them
-    const int64_t p = r % a.T;
-    int lo = 0, hi = a.B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      int64_t st = a.cu[mid];
-      st = st < 0 ? 0 : (st > a.T ? a.T : st);
-      if (st <= p) lo = mid; else hi = mid - 1;
-    }
-    int64_t st = a.cu[lo], en = a.cu[lo + 1];
-    st = st < 0 ? 0 : (st > a.T ? a.T : st);
-    en = en < st ? st : (en > a.T ? a.T : en);
-    if (p < st || p >= en) return;
-    t = (int)(p - st);
-    n = (int)(en - st < (int64_t)a.N ? en - st : (int64_t)a.N);
-  }
-  if (t >= n) return;
-  const int NT = (n + kTileKeys - 1) / kTileKeys;
-  const int chunk = split_chunk(NT, a.nsplit);
-  if (NT <= chunk) return;
-  const float* pml = a.part + (size_t)a.nsplit * a.rows * D;
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const int kt0 = s * chunk;
-    if (kt0 >= NT || (a.causal && kt0 * kTileKeys > t)) break;
-    M = fmaxf(M, pml[((size_t)s * a.rows + r) * 2]);
-  }
-  float L = 0.f;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.nsplit; ++s) {
-    const int kt0 = s * chunk;
-    if (kt0 >= NT || (a.causal && kt0 * kTileKeys > t)) break;
-    const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(pml + ((size_t)s * a.rows + r) * 2);
-    const float wgt = __builtin_amdgcn_exp2f(ml[0] - M);
-    L += wgt * ml[1];
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.part + ((size_t)s * a.rows + r) * D + 4 * j);
-    acc += wgt * v;
-  }
-  const float inv = 1.0f / L;
-  u32x2_t out;
-  out[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  out[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  *reinterpret_cast<u32x2_t*>(a.o + (size_t)r * D + 4 * j) = out;
-  if (a.lse != nullptr && j == 0) a.lse[r] = (M + log2f(L)) * 0.69314718055994531f;
-}
-
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream) {
@@ -673,7 +602,7 @@ hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream) {
   hipLaunchKernelGGL(attn_fwd_bf16_d64_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  MergeArgs m;
+  SplitMergeArgs m;
   m.part = a.part;
   m.o = a.o;
   m.lse = a.lse;
@@ -684,10 +613,10 @@ hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream) {
   m.B = (int)p.B;
   m.nsplit = a.nsplit;
   m.causal = a.causal;
-  const int64_t blocks = (a.rows + 15) / 16;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_split_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, m);
-  return hipGetLastError();
+  m.tile_keys = kTileKeys;
+  m.min_tiles = kMinSplitTiles;
+  m.even = 1;
+  return launch_split_merge<D>(m, stream);
 }
 
 // Recommended key-range splits for this kernel, from measurements on MI355X
@@ -722,9 +651,9 @@ bool packed_wants_split(int64_t N, int64_t T) {
   return N >= 2 * kMinSplitTiles * kTileKeys && 4 * N >= T;
 }
 
-size_t attn_split_workspace_bytes(int64_t rows, int nsplit) {
+size_t attn_split_workspace_bytes(int64_t rows, int64_t d, int nsplit) {
   if (rows <= 0 || nsplit <= 1) return 0;
-  return (size_t)nsplit * (size_t)rows * (D + 2) * sizeof(float);
+  return (size_t)nsplit * (size_t)rows * (size_t)(d + 2) * sizeof(float);
 }
 
 }  // namespace sqa

@@ -24,14 +24,14 @@ struct AttnProblem {
   int causal;
   const int* cu_seqlens;  // nullptr: dense
   int64_t T;              // packed: total tokens
-  // key-range splits (bf16, d = 64 only): nsplit > 1 needs split_ws of
-  // attn_split_workspace_bytes(rows, nsplit) bytes, rows = B*Hq*N (packed:
-  // Hq*T)
+  // key-range splits (bf16, d = 16, 32, 64): nsplit > 1 needs split_ws of
+  // attn_split_workspace_bytes(rows, D, nsplit) bytes, rows = B*Hq*N
+  // (packed: Hq*T)
   int nsplit = 1;
   float* split_ws = nullptr;
 };
 
-size_t attn_split_workspace_bytes(int64_t rows, int nsplit);
+size_t attn_split_workspace_bytes(int64_t rows, int64_t d, int nsplit);
 // recommended nsplit for the d = 64 bf16 forward on a device with `cus` CUs
 int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t T, bool causal, int cus);
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream);

@@ -111,17 +111,22 @@ __device__ __forceinline__ void exact_coords(int L, int per_batch, int Hq, int H
   w_in = r;
 }
 
-// Key-range split of the d = 64 forward: with S splits the key tiles of a
-// sequence with NT 32-key tiles are cut into chunks of split_chunk(NT, S)
-// tiles (split s takes tiles [s*chunk, (s+1)*chunk)). A chunk is even (so
-// a causal wave either sees a key of every one of its 64 rows in a split or
-// none of them) and at least kMinSplitTiles tiles; a sequence with
-// NT <= chunk is not split.
-constexpr int kMinSplitTiles = 32;
-__host__ __device__ __forceinline__ int split_chunk(int NT, int nsplit) {
+// Range splits: with S splits the NT tiles of a sequence are cut into
+// chunks of split_chunk(NT, S, ...) tiles (split s takes tiles
+// [s*chunk, (s+1)*chunk)); a sequence with NT <= chunk is not split. A
+// chunk holds at least min_tiles tiles; `even` rounds it up to an even
+// count, which the 32-key-tile kernels need so that a causal wave of 64
+// rows either sees a key of every row in a range or none (the 64-key-tile
+// kernel needs no rounding: its waves hold at most 64 rows).
+constexpr int kMinSplitTiles = 32;   // 32-key (or 32-row) tiles: ranges of >= 1024
+constexpr int kMinSplitTiles64 = 4;  // 64-key tiles: ranges of >= 256 keys
+__host__ __device__ __forceinline__ int split_chunk(int NT, int nsplit, int min_tiles, bool even) {
   int c = (NT + nsplit - 1) / nsplit;
-  c = (c + 1) & ~1;
-  return c < kMinSplitTiles ? kMinSplitTiles : c;
+  if (even) c = (c + 1) & ~1;
+  return c < min_tiles ? min_tiles : c;
+}
+__host__ __device__ __forceinline__ int split_chunk(int NT, int nsplit) {
+  return split_chunk(NT, nsplit, kMinSplitTiles, true);
 }
 
 }  // namespace sqa

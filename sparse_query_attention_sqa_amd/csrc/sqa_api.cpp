@@ -79,8 +79,8 @@ sqa_status check_splits(int64_t num_splits, int64_t d, int dtype) {
   if (num_splits < 1 || num_splits > kMaxSplits)
     return fail(SQA_ERR_ARG, "num_splits must be in [1, %lld] (got %lld)", (long long)kMaxSplits,
                 (long long)num_splits);
-  if (num_splits > 1 && (d != 64 || dtype != SQA_BF16))
-    return fail(SQA_ERR_UNSUPPORTED, "key-range splits need d = 64 and bf16");
+  if (num_splits > 1 && (d > 64 || dtype != SQA_BF16))
+    return fail(SQA_ERR_UNSUPPORTED, "key-range splits need bf16 and d = 16, 32 or 64");
   return SQA_OK;
 }
 
@@ -94,10 +94,10 @@ sqa_status check_bwd_splits(int64_t num_splits, int causal) {
 
 // Workspace of a split forward: present, aligned, large enough and clear of
 // every tensor argument (tensors[i] spans sizes[i] bytes).
-sqa_status check_split_workspace(int64_t num_splits, int64_t rows, const void* ws, size_t ws_bytes,
+sqa_status check_split_workspace(int64_t num_splits, int64_t rows, int64_t d, const void* ws, size_t ws_bytes,
                                  const void* const* tensors, const size_t* sizes) {
   if (num_splits <= 1) return SQA_OK;
-  const size_t need = sqa::attn_split_workspace_bytes(rows, (int)num_splits);
+  const size_t need = sqa::attn_split_workspace_bytes(rows, d, (int)num_splits);
   if (ws == nullptr || ws_bytes < need)
     return fail(SQA_ERR_WORKSPACE, "split workspace of %zu bytes needed (got %zu)", need, ws ? ws_bytes : (size_t)0);
   if (!aligned(ws, 16)) return fail(SQA_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -156,7 +156,7 @@ sqa_status sqa_attn_fwd_split(const void* q, const void* k, const void* v, void*
     return fail(SQA_ERR_ARG, "lse overlaps another tensor");
   const void* tensors[5] = {q, k, v, o, lse};
   const size_t sizes[5] = {nq, nkv, nkv, nq, nl};
-  s = check_split_workspace(num_splits, B * H_q * N, workspace, workspace_bytes, tensors, sizes);
+  s = check_split_workspace(num_splits, B * H_q * N, d, workspace, workspace_bytes, tensors, sizes);
   if (s != SQA_OK) return s;
 
   sqa::AttnProblem p{q, k, v, o, lse, B, H_q, H_kv, N, d, scale, causal};
@@ -209,7 +209,7 @@ sqa_status sqa_attn_fwd_varlen_split(const void* q, const void* k, const void* v
     return fail(SQA_ERR_ARG, "workspace overlaps cu_seqlens");
   const void* tensors[5] = {q, k, v, o, lse};
   const size_t sizes[5] = {nq, nkv, nkv, nq, nl};
-  s = check_split_workspace(num_splits, H_q * T, workspace, workspace_bytes, tensors, sizes);
+  s = check_split_workspace(num_splits, H_q * T, d, workspace, workspace_bytes, tensors, sizes);
   if (s != SQA_OK) return s;
 
   sqa::AttnProblem p{q, k, v, o, lse, B, H_q, H_kv, max_seqlen, d, scale, causal, cu_seqlens, T};
@@ -231,8 +231,8 @@ int64_t sqa_attn_fwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N,
 
 size_t sqa_attn_fwd_split_workspace_bytes(int64_t rows, int64_t d, int dtype, int64_t num_splits) {
   if (rows <= 0 || rows > kMaxElems || num_splits <= 1 || num_splits > kMaxSplits) return 0;
-  if (d != 64 || dtype != SQA_BF16) return 0;
-  return round256(sqa::attn_split_workspace_bytes(rows, (int)num_splits));
+  if ((d != 16 && d != 32 && d != 64) || dtype != SQA_BF16) return 0;
+  return round256(sqa::attn_split_workspace_bytes(rows, d, (int)num_splits));
 }
 
 size_t sqa_attn_bwd_workspace_bytes(int64_t B, int64_t H_q, int64_t N, int64_t d, int dtype) {

@@ -134,7 +134,7 @@ def _split(lib, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000,
 
 @pytest.mark.parametrize("kw,code", [
     (dict(ns=0), 7), (dict(ns=17), 7), (dict(ns=-1), 7),
-    (dict(d=128), 3), (dict(d=32), 3), (dict(dtype=0), 3),
+    (dict(d=128), 3), (dict(dtype=0), 3),
     (dict(ws=None), 5), (dict(ws_bytes=100), 5),
     (dict(ws=FAKE + 0x1000008), 4),
     (dict(ws=FAKE + 0x200000), 7),                   # workspace over v
@@ -157,7 +157,7 @@ def test_split_varlen_rejects_invalid_arguments(lib):
     assert f(*base, 2, FAKE + 4 * M, big, None) == 7                # workspace over cu_seqlens
     assert f(*base, 2, FAKE + 3 * M, big, None) == 7                # workspace over o
     assert f(*base, 20, FAKE + 5 * M, big, None) == 7
-    assert f(*(base[:10] + [32] + base[11:]), 2, FAKE + 5 * M, big, None) == 3
+    assert f(*(base[:10] + [128] + base[11:]), 2, FAKE + 5 * M, big, None) == 3
     assert f(*(base[:5] + [0] + base[6:]), 2, None, 0, None) == 0  # B = 0: nothing to do
 
 
@@ -174,6 +174,8 @@ def test_split_workspace_bytes(lib):
     assert f(100, 64, 1, 3) == 79360
     assert f(8 * 32768, 64, 1, 3) == 3 * 8 * 32768 * 66 * 4
     assert f(100, 64, 1, 1) == 0
+    # d = 16: 2 x 100 x (16 + 2) x 4 = 14400 B -> 14592
+    assert f(100, 16, 1, 2) == 14592
     assert f(100, 128, 1, 2) == 0
     assert f(100, 64, 0, 2) == 0
     assert f(0, 64, 1, 2) == 0

@@ -65,6 +65,49 @@ def test_split_dense_all_rows(B, Hq, Hkv, N, causal, splits):
     assert err <= LSE_TOL, f"{label}: lse error {err:.3e}"
 
 
+@functools.lru_cache(maxsize=None)
+def _small_d_case(B, Hq, Hkv, N, d, causal):
+    q, k, v = draw_attn_case(B, Hq, Hkv, N, d, "bf16", seed=N + d)
+    ref, ref_lse = oracle_attention(q, k, v, scale=d ** -0.5, causal=bool(causal), return_lse=True,
+                                    threads=oracle_threads())
+    return q, k, v, ref, ref_lse
+
+
+# head dims 16 and 32 (64-key tiles, ranges of at least 4 tiles, 32-row
+# waves for d = 16 causal): only on request, the library never picks them
+@pytest.mark.parametrize("splits", [2, 3, 4])
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("d", [16, 32])
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(2, 8, 4, 1100), (1, 6, 4, 700)])
+def test_split_head_dims_16_32_all_rows(B, Hq, Hkv, N, d, causal, splits):
+    label = f"split d={d} B={B} ({Hq},{Hkv}) N={N} causal={causal} splits={splits}"
+    log(f"[case] {label}")
+    q, k, v, ref, ref_lse = _small_d_case(B, Hq, Hkv, N, d, causal)
+    o, lse = sqa.sqa_attn_fwd(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), scale=d ** -0.5,
+                              causal=bool(causal), return_lse=True, num_splits=splits)
+    torch.cuda.synchronize()
+    o = to_host(o)
+    check_global(o, ref, "bf16", label)
+    check_rows(o, ref, label)
+    err = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse)))
+    assert err <= LSE_TOL, f"{label}: lse error {err:.3e}"
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_split_varlen_d32(causal):
+    label = f"split varlen d=32 dominant causal={causal}"
+    log(f"[case] {label}")
+    q, k, v, cu = draw_varlen(SPLIT_MIXES["dominant"], 8, 4, 32, "bf16", seed=19)
+    ref = oracle_varlen(q, k, v, cu, scale=32 ** -0.5, causal=bool(causal), threads=oracle_threads())
+    o = sqa.sqa_attn_fwd_varlen(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                                torch.from_numpy(cu).to("cuda"), scale=32 ** -0.5, causal=bool(causal),
+                                num_splits=3)
+    torch.cuda.synchronize()
+    o = to_host(o)
+    check_global(o, ref, "bf16", label)
+    check_rows(o, ref, label)
+
+
 def test_split_one_is_the_unsplit_call_bitwise():
     q, k, v, _, _ = _dense_case(1, 8, 4, 4200, 1)
     tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
@@ -140,6 +183,9 @@ def test_split_errors_on_device():
         sqa.sqa_attn_fwd(tq, tk, tv, num_splits=0)
     with pytest.raises(sqa.SQAError):
         sqa.sqa_attn_fwd(tq.float(), tk.float(), tv.float(), num_splits=2)  # fp32 path does not split
+    q2, k2, v2 = draw_attn_case(1, 8, 4, 1100, 128, "bf16", seed=2)
+    with pytest.raises(sqa.SQAError):
+        sqa.sqa_attn_fwd(to_dev(q2, "bf16"), to_dev(k2, "bf16"), to_dev(v2, "bf16"), num_splits=2)  # nor d = 128
 
 
 # ------------------------------------------------------------- backward
