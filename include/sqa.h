@@ -119,8 +119,8 @@ sqa_status sqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void
  * sequences, N = max_seqlen): 2 when the longest sequence has at least
  * 2048 tokens and holds at least a quarter of the T (its workgroups then
  * form the tail of the launch). Never under a causal mask (measured
- * slower) and never for d != 64 or dtype != SQA_BF16. Returns 1 for
- * invalid sizes.
+ * slower), never at d = 16, 32 or 128 (measured slower or no gain) and
+ * never for dtype != SQA_BF16. Returns 1 for invalid sizes.
  */
 int64_t sqa_attn_fwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
                                 int causal, int64_t T);
@@ -130,8 +130,7 @@ int64_t sqa_attn_fwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N,
  * forward with num_splits > 1 needs for `rows` query rows (B * H_q * N, or
  * H_q * T packed): num_splits * rows * (d + 2) fp32 values (each range's
  * unnormalised output, maximum and sum per row). Returns 0 when
- * num_splits <= 1, for invalid sizes, and when d is not 16, 32 or 64 or
- * dtype != SQA_BF16.
+ * num_splits <= 1, for invalid sizes, and when dtype != SQA_BF16.
  */
 size_t sqa_attn_fwd_split_workspace_bytes(int64_t rows, int64_t d, int dtype, int64_t num_splits);
 
@@ -145,13 +144,14 @@ size_t sqa_attn_fwd_split_workspace_bytes(int64_t rows, int64_t d, int dtype, in
  * unsplit calls up to fp32 rounding order. At d = 64 a range holds at least
  * 1024 keys (an even number of 32-key tiles), at d = 16 and 32 at least 256
  * (64-key tiles), so a short sequence is computed unsplit or gets fewer
- * than num_splits ranges. sqa_attn_fwd_num_splits only ever recommends
- * splits at d = 64: at d = 16 under a causal mask (the SQAT-m layer's
- * shape) split launches measured slower.
+ * than num_splits ranges (d = 128: at least 1024 keys, 32-key tiles).
+ * sqa_attn_fwd_num_splits only ever recommends splits at d = 64: at d = 16
+ * under a causal mask (the SQAT-m layer's shape) and at d = 128 on a packed
+ * batch, split launches measured slower.
  *
- *   num_splits 1..16; > 1 only for d = 16, 32 or 64 and dtype SQA_BF16
- *              (SQA_ERR_UNSUPPORTED otherwise). 1 behaves exactly as the
- *              unsplit call and ignores the workspace.
+ *   num_splits 1..16; > 1 only for dtype SQA_BF16 (SQA_ERR_UNSUPPORTED
+ *              otherwise). 1 behaves exactly as the unsplit call and
+ *              ignores the workspace.
  *   workspace  device buffer of at least sqa_attn_fwd_split_workspace_bytes
  *              bytes, 16-byte aligned, owned by the caller, not overlapping
  *              any tensor argument; contents on return unspecified.

@@ -49,6 +49,7 @@
 
 #include "kernels.h"
 #include "seq_groups.h"
+#include "split_merge.h"
 
 namespace sqa {
 namespace {
@@ -57,6 +58,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -96,6 +98,9 @@ struct Args {
   float c;
   uint32_t qsign;
   int causal;
+  int nsplit;    // key-range splits (1: none)
+  float* part;   // nsplit > 1: [nsplit][rows][128] unnormalised O, then [nsplit][rows][2] (m, l)
+  int64_t rows;  // query rows: B*Hq*N (packed: Hq*T)
 };
 
 __device__ __forceinline__ int pi_row(int r) { return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3); }
@@ -319,11 +324,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d128_kernel(Args a)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- workgroup -> (batch*Hkv, slot range)
+  // key-range split: runs of 8 consecutive workgroups take one split index,
+  // so that the splits of logical workgroup wid run on XCD wid % 8
+  const int g8 = (int)(blockIdx.x >> 3), x8 = (int)(blockIdx.x & 7);
+  const int split = g8 % a.nsplit;
+  const int wid = (g8 / a.nsplit) * 8 + x8;
+  if (wid >= a.nwg) return;
   int bkv, w_in;
   if (a.spread) {
-    spread_coords(blockIdx.x, a.n_bkv, a.wg_per_bkv, a.causal != 0, a.spread_block, bkv, w_in);
+    spread_coords(wid, a.n_bkv, a.wg_per_bkv, a.causal != 0, a.spread_block, bkv, w_in);
   } else if (a.exact_per_batch > 0 || !a.causal) {  // XCD-contiguous (shared L2)
-    const int bid = blockIdx.x;
+    const int bid = wid;
     const int per = a.nwg / kXcds, rem = a.nwg % kXcds;
     const int x = bid % kXcds, i = bid / kXcds;
     const int L = x * per + min(x, rem) + i;
@@ -334,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d128_kernel(Args a)
       w_in = L % a.wg_per_bkv;
     }
   } else {  // causal: longest (largest position block) first
-    const int L = blockIdx.x;
+    const int L = wid;
     const int wr = L / a.n_bkv;
     bkv = L % a.n_bkv;
     w_in = a.wg_per_bkv - 1 - wr;
@@ -351,8 +362,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d128_kernel(Args a)
   const bool wave_valid = tb < TB;
   const int h = hg.first + jh;
   const int maxtb = min((w_in * kWaves + kWaves - 1) / g, TB - 1);
-  const int nt = a.causal ? min(maxtb + 1, NT) : NT;
-  const int last = !wave_valid ? -1 : (a.causal ? tb : NT - 1);
+  const int nt_all = a.causal ? min(maxtb + 1, NT) : NT;
+  const int last_all = !wave_valid ? -1 : (a.causal ? tb : NT - 1);
+  // Key-range split: key tiles [kt0, kt0 + chunk) of the workgroup's rows,
+  // with tiles, keys, n and the causal positions counted from kt0 below. A
+  // causal wave (32 rows, diagonal tile tb) sees a key of every row in a
+  // range starting at or before tb and none in a later one.
+  const int chunk = split_chunk(NT, a.nsplit, kMinSplitTiles, false);
+  const bool split_rows = NT > chunk;
+  const int kt0 = split * chunk;
+  if (kt0 >= nt_all) return;
+  const int nt = min(nt_all - kt0, chunk);
+  const int last = last_all < kt0 ? -1 : min(last_all - kt0, chunk - 1);
+  const int key_shift = kt0 * kTileKeys;
   const int trow0 = tb * kRowsPerWave;
 
   Lane ln;
@@ -376,8 +398,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d128_kernel(Args a)
 
   const int64_t kvrow0 = sg.kv_base + (int64_t)kvh * sg.stride;
   const int64_t qrow0 = sg.q_base + (int64_t)h * sg.stride;
-  const uint16_t* kbase = a.k + (size_t)kvrow0 * D;
-  const uint16_t* vbase = a.v + (size_t)kvrow0 * D;
+  const uint16_t* kbase = a.k + (size_t)(kvrow0 + key_shift) * D;
+  const uint16_t* vbase = a.v + (size_t)(kvrow0 + key_shift) * D;
+  const int nk = n - key_shift;  // keys of this sequence from the range start on
 
   WaveState w;
   {
@@ -412,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d128_kernel(Args a)
 
   // prologue: tiles 0..3 in flight (empty ranges past the end), wait for
   // tiles 0..2, S(0), then K(1) into kf
-  const int nlim = min(n, nt * kTileKeys);  // keys the workgroup streams
+  const int nlim = min(nk, nt * kTileKeys);  // keys the workgroup streams
   issue_tile<0>(ring, kbase, vbase, 0, nlim, wave, ln);
   issue_tile<1>(ring, kbase, vbase, 1, nlim, wave, ln);
   issue_tile<2>(ring, kbase, vbase, 2, nlim, wave, ln);
@@ -426,13 +449,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d128_kernel(Args a)
   cx.ring = ring;
   cx.kbase = kbase;
   cx.vbase = vbase;
-  cx.n = n;
+  cx.n = nk;
   cx.nlim = nlim;
   cx.last = last;
-  cx.tb = tb;
+  cx.tb = tb - kt0;
   cx.causal = a.causal;
   cx.wave = wave;
-  cx.t = trow0 + ln.l32;
+  cx.t = trow0 + ln.l32 - key_shift;
   cx.c = a.c;
 
   // ten phases per round (ring slots repeat every 5, register parity every
@@ -466,10 +489,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d128_kernel(Args a)
   if (last & 1) mfma_pv(w.vf, w.pk[1], w.acc_o);
   else mfma_pv(w.vf, w.pk[0], w.acc_o);
 
-  // ---- epilogue: O = O^T / l (bf16, nearest even); LSE = m ln2 + ln l
   const float ltot = w.l_run + __shfl_xor(w.l_run, 32);
-  const float inv = 1.0f / ltot;
   const int t = trow0 + ln.l32;
+  if (split_rows) {
+    // ---- split epilogue: unnormalised O^T, m and l of this key range (fp32)
+    if (t < n) {
+      float* po = a.part + ((size_t)split * a.rows + qrow0 + t) * D;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int ab = 0; ab < 4; ++ab) {
+          const f32x4_t v4 = {w.acc_o[x][4 * ab], w.acc_o[x][4 * ab + 1], w.acc_o[x][4 * ab + 2],
+                              w.acc_o[x][4 * ab + 3]};
+          *reinterpret_cast<f32x4_t*>(po + x * 32 + 8 * ab + 4 * ln.lg) = v4;
+        }
+      if (ln.lg == 0)
+        *reinterpret_cast<f32x2_t*>(a.part + (size_t)a.nsplit * a.rows * D + ((size_t)split * a.rows + qrow0 + t) * 2) =
+            f32x2_t{w.m_run, ltot};
+    }
+    return;
+  }
+
+  // ---- epilogue: O = O^T / l (bf16, nearest even); LSE = m ln2 + ln l
+  const float inv = 1.0f / ltot;
   if (t < n) {
     uint16_t* orow = a.o + ((size_t)qrow0 + t) * D;
 #pragma unroll
@@ -523,8 +565,31 @@ hipError_t launch_attn_fwd_bf16_d128(const AttnProblem& p, hipStream_t stream) {
   a.c = fmaxf(fabsf(p.scale) * 1.4426950408889634f, kMinC);
   a.qsign = (p.scale < 0.f) ? 0x80008000u : 0u;
   a.causal = p.causal;
-  hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel, dim3(a.nwg), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  a.nsplit = p.nsplit < 1 ? 1 : p.nsplit;
+  a.part = p.split_ws;
+  a.rows = p.cu_seqlens != nullptr ? p.Hq * p.T : p.B * p.Hq * p.N;
+  if (a.nsplit > 1 && a.part == nullptr) return hipErrorInvalidValue;
+  // with splits the grid covers whole runs of 8 (see the kernel's decode)
+  const int64_t grid = a.nsplit == 1 ? a.nwg : ((int64_t)a.nwg + 7) / 8 * 8 * a.nsplit;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  SplitMergeArgs m;
+  m.part = a.part;
+  m.o = a.o;
+  m.lse = a.lse;
+  m.cu = a.cu;
+  m.T = a.T;
+  m.rows = a.rows;
+  m.N = a.N;
+  m.B = (int)p.B;
+  m.nsplit = a.nsplit;
+  m.causal = a.causal;
+  m.tile_keys = kTileKeys;
+  m.min_tiles = kMinSplitTiles;
+  m.even = 0;
+  return launch_split_merge<D>(m, stream);
 }
 
 }  // namespace sqa

@@ -634,10 +634,11 @@ hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream) {
 // batch (T > 0 tokens, N the longest sequence): the longest sequence's
 // workgroups reach the dispatcher late, behind the short sequences', and
 // form the tail, so two splits whenever packed_wants_split.
-int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t T, bool causal, int cus) {
+int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t T, bool causal, int cus,
+                         int rows_per_wave) {
   if (causal) return 1;
   if (T > 0) return packed_wants_split(N, T) ? 2 : 1;
-  const int64_t NT = (N + kTileKeys - 1) / kTileKeys, TB = (N + kRowsPerWave - 1) / kRowsPerWave;
+  const int64_t NT = (N + kTileKeys - 1) / kTileKeys, TB = (N + rows_per_wave - 1) / rows_per_wave;
   int64_t wgs = 0;
   for (int j = 0; j < Hkv; ++j) wgs += group_wgs(j, (int)Hq, (int)Hkv, (int)TB, kWaves);
   const double r = (double)(wgs * B) / (2.0 * (cus > 0 ? cus : 256));

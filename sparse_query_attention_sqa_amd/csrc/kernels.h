@@ -24,7 +24,7 @@ struct AttnProblem {
   int causal;
   const int* cu_seqlens;  // nullptr: dense
   int64_t T;              // packed: total tokens
-  // key-range splits (bf16, d = 16, 32, 64): nsplit > 1 needs split_ws of
+  // key-range splits (bf16, any supported d): nsplit > 1 needs split_ws of
   // attn_split_workspace_bytes(rows, D, nsplit) bytes, rows = B*Hq*N
   // (packed: Hq*T)
   int nsplit = 1;
@@ -33,7 +33,10 @@ struct AttnProblem {
 
 size_t attn_split_workspace_bytes(int64_t rows, int64_t d, int nsplit);
 // recommended nsplit for the d = 64 bf16 forward on a device with `cus` CUs
-int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t T, bool causal, int cus);
+// (rows_per_wave: 64 for the d = 64 kernel, 32 for the d = 128 kernel; both
+// run two 4-wave workgroups per CU over 32-key tiles)
+int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t T, bool causal, int cus,
+                         int rows_per_wave);
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream);
 // head dim 64, software-pipelined (attn_fwd_bf16_d64.hip)
 hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream);

@@ -134,7 +134,7 @@ def _split(lib, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000,
 
 @pytest.mark.parametrize("kw,code", [
     (dict(ns=0), 7), (dict(ns=17), 7), (dict(ns=-1), 7),
-    (dict(d=128), 3), (dict(dtype=0), 3),
+    (dict(dtype=0), 3),
     (dict(ws=None), 5), (dict(ws_bytes=100), 5),
     (dict(ws=FAKE + 0x1000008), 4),
     (dict(ws=FAKE + 0x200000), 7),                   # workspace over v
@@ -157,7 +157,7 @@ def test_split_varlen_rejects_invalid_arguments(lib):
     assert f(*base, 2, FAKE + 4 * M, big, None) == 7                # workspace over cu_seqlens
     assert f(*base, 2, FAKE + 3 * M, big, None) == 7                # workspace over o
     assert f(*base, 20, FAKE + 5 * M, big, None) == 7
-    assert f(*(base[:10] + [128] + base[11:]), 2, FAKE + 5 * M, big, None) == 3
+    assert f(*(base[:11] + [0] + base[12:]), 2, FAKE + 5 * M, big, None) == 3   # fp32
     assert f(*(base[:5] + [0] + base[6:]), 2, None, 0, None) == 0  # B = 0: nothing to do
 
 
@@ -176,7 +176,7 @@ def test_split_workspace_bytes(lib):
     assert f(100, 64, 1, 1) == 0
     # d = 16: 2 x 100 x (16 + 2) x 4 = 14400 B -> 14592
     assert f(100, 16, 1, 2) == 14592
-    assert f(100, 128, 1, 2) == 0
+    assert f(100, 128, 1, 2) == round(2 * 100 * 130 * 4 / 256 + 0.4999) * 256
     assert f(100, 64, 0, 2) == 0
     assert f(0, 64, 1, 2) == 0
     assert f(100, 64, 1, 17) == 0
@@ -209,8 +209,9 @@ def test_split_policy(lib):
     assert f(2, 8, 4, 4096, 64) == 2
     # ranges keep at least 1024 keys: a 1000-key sequence is not split
     assert f(1, 8, 4, 1000, 64) == 1
-    # only the bf16 d = 64 kernel splits
+    # the library's choice: d = 64 only (d = 128 packed measured slower split)
     assert f(1, 8, 4, 18496, 128) == 1
+    assert f(8, 8, 4, 18496, 128, T=32768) == 1
     assert f(1, 8, 4, 18496, 32) == 1
     assert f(1, 8, 4, 18496, 64, dtype="f32") == 1
     assert f(0, 8, 4, 18496, 64) == 1 and f(1, 4, 8, 18496, 64) == 1
