@@ -28,6 +28,9 @@
 // an empty descriptor range and cost no memory traffic -- so the explicit
 // vmcnt waits are exact. P and dS are rounded to bf16 (nearest even) for the
 // MFMA products; everything else accumulates in fp32.
+// Encoder-style launches may split (nsplit > 1): the dK/dV kernel over
+// ranges of query tiles, the dQ kernel over ranges of key tiles; each range
+// leaves a scaled fp32 partial and bwd_split_sum_kernel adds them.
 //
 // Head dim 128 (DH = 2 halves of 64): every 32-row tile is stored as two
 // 64-wide half-tiles, products over the head dim add the two halves, and the

@@ -20,7 +20,10 @@
 //     the longest sequence, and workgroups with no rows leave at once.
 //   * K/V are streamed in 64-key tiles, HBM -> registers -> LDS, double
 //     buffered with one barrier per tile; each tile is read from HBM once per
-//     workgroup and consumed by 4 x 32*QS query rows.
+//     workgroup and consumed by 4 x 32*QS query rows. On request
+//     (nsplit > 1) each row block's key tiles are cut into ranges computed by
+//     separate workgroups, whose fp32 partial softmax states are merged
+//     afterwards (split_merge.h).
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (A = K tile from LDS, B = Q held in
 //     registers). The accumulator layout then already is the B operand of

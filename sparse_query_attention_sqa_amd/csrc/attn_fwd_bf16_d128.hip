@@ -8,7 +8,9 @@
 // Decomposition: a workgroup is 4 waves that share one (batch, K/V head);
 // each wave owns 32 query positions of one query head of the group (slots
 // ordered by position block, then head-in-group), so one K/V tile in LDS
-// feeds 128 query rows.
+// feeds 128 query rows. On request (nsplit > 1) each row block's keys are
+// cut into ranges computed by separate workgroups, merged afterwards
+// (split_merge.h).
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 // (A = K tile from LDS, B = Q in registers, 8 k-steps over d = 128); the

@@ -13,6 +13,11 @@
 // in size by one head (H_kv need not divide H_q) and packed batches have
 // sequences of different lengths: the grid is sized for the largest group
 // and the longest sequence, and workgroups with no rows leave at once.
+// With key-range splits (nsplit > 1) each row block's keys are cut into
+// ranges of an even number of tiles, one workgroup per range; a range's
+// workgroup runs the same pipeline on shifted pointers and leaves fp32
+// partial softmax states that attn_split_merge_kernel (split_merge.h)
+// combines.
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 // (A = K tile from LDS, B = Q in registers), so the score accumulator already
