@@ -112,6 +112,7 @@ struct Args {
   int spread;                  // 1: spread_coords order (packed sequences, causal uneven groups)
   int spread_block;   // rotation block of the spread order
   int exact_per_batch;         // > 0: exact_coords order with this many workgroups per batch
+  int pair_major;              // packed encoder-style: pair_major_coords order
   float c;
   uint32_t qsign;
   int causal;
@@ -363,7 +364,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   const int wid = (g8 / a.nsplit) * 8 + x8;
   if (wid >= a.nwg) return;
   int bkv, w_in;
-  if (a.spread) {  // packed sequences, or uneven groups under a causal mask
+  if (a.pair_major) {
+    if (!pair_major_coords(wid, a.n_bkv, a.wg_per_bkv, bkv, w_in)) return;
+  } else if (a.spread) {  // packed sequences, or uneven groups under a causal mask
     spread_coords(wid, a.n_bkv, a.wg_per_bkv, a.causal != 0, a.spread_block, bkv, w_in);
   } else if (a.exact_per_batch > 0) {  // uneven groups, encoder-style: XCD-contiguous, exact counts
     const int bid = wid;
@@ -592,6 +595,12 @@ hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream) {
     a.exact_per_batch = (int)per;
     nwg = per * p.B;
   }
+  // packed encoder-style: pair-major order (seq_groups.h). Measured on the
+  // packed 32k batch, unsplit: (8,4) 793 -> 862 TFLOP/s, (16,16) 746 -> 984
+  // against the rotating spread order, whose workgroups on one XCD came from
+  // many pairs (L2 hit rate 0.37).
+  a.pair_major = (p.cu_seqlens != nullptr && !p.causal) ? 1 : 0;
+  if (a.pair_major) nwg = pair_major_nwg(a.n_bkv, a.wg_per_bkv);
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
   a.nwg = (int)nwg;
   a.c = fmaxf(fabsf(p.scale) * 1.4426950408889634f, kMinC);
@@ -636,17 +645,24 @@ hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream) {
 // workgroups / slots. When the whole launch fits in one round, split as far
 // as 4 ways while it still does; otherwise take two splits when they cut
 // the whole-row rounds, ceil(r) -> ceil(2r)/2, by at least 10 %. Packed
-// batch (T > 0 tokens, N the longest sequence): the longest sequence's
-// workgroups reach the dispatcher late, behind the short sequences', and
-// form the tail, so two splits whenever packed_wants_split.
+// batch (T > 0 tokens, N the longest sequence), launched in pair-major
+// order: two splits when packed_wants_split and the longest sequence's own
+// workgroups fill between one and two rounds (r of B = 1), where its last
+// round is left mostly empty; with more rounds the other sequences fill the
+// tail (measured, pair-major, 2 ranges: (8,4) 845 -> 928 TFLOP/s at 1.13
+// rounds, (16,16) 971 -> 904 at 2.28).
 int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t T, bool causal, int cus,
                          int rows_per_wave) {
   if (causal) return 1;
-  if (T > 0) return packed_wants_split(N, T) ? 2 : 1;
   const int64_t NT = (N + kTileKeys - 1) / kTileKeys, TB = (N + rows_per_wave - 1) / rows_per_wave;
   int64_t wgs = 0;
   for (int j = 0; j < Hkv; ++j) wgs += group_wgs(j, (int)Hq, (int)Hkv, (int)TB, kWaves);
-  const double r = (double)(wgs * B) / (2.0 * (cus > 0 ? cus : 256));
+  const double slots = 2.0 * (cus > 0 ? cus : 256);
+  if (T > 0) {
+    const double r1 = (double)wgs / slots;
+    return (packed_wants_split(N, T) && r1 > 1.0 && r1 < 2.0 && ceil(2.0 * r1) / 2.0 <= 0.9 * ceil(r1)) ? 2 : 1;
+  }
+  const double r = (double)(wgs * B) / slots;
   for (int S = 4; S >= 2; --S)
     if (S * r <= 1.0 && NT >= (int64_t)S * kMinSplitTiles) return S;
   if (NT >= 2 * kMinSplitTiles && ceil(2.0 * r) / 2.0 <= 0.9 * ceil(r)) return 2;

@@ -77,6 +77,23 @@ __device__ __forceinline__ void spread_coords(int bid, int n_bkv, int wg_per_bkv
   w_in = descending ? wg_per_bkv - 1 - wr : wr;
 }
 
+// Pair-major order for packed encoder-style launches: XCD x (= wid % 8)
+// walks the (sequence, K/V head) pairs in turn and takes, of each, the
+// workgroup indices w_in = x, x + 8, x + 16, ...; every pair is dealt evenly
+// over the XCDs, and consecutive workgroups of an XCD share one pair's K/V
+// in its L2. The grid covers n_bkv * ceil(wg_per_bkv / 8) * 8 logical
+// workgroups (pair_major_nwg); indices past a pair's last workgroup exit.
+__device__ __forceinline__ bool pair_major_coords(int wid, int n_bkv, int wg_per_bkv, int& bkv, int& w_in) {
+  const int J = (wg_per_bkv + 7) / 8;
+  const int x = wid & 7, k = wid >> 3;
+  bkv = k / J;
+  w_in = (k % J) * 8 + x;
+  return bkv < n_bkv && w_in < wg_per_bkv;
+}
+__host__ __forceinline__ int64_t pair_major_nwg(int64_t n_bkv, int64_t wg_per_bkv) {
+  return n_bkv * ((wg_per_bkv + 7) / 8) * 8;
+}
+
 // Rotation block for spread_coords. Packed sequences: 1 (a block would put
 // the workgroups of the longest sequence on one XCD: 2-4x slower). Dense
 // batches with uneven head groups: 16 once there are at least four
