@@ -125,9 +125,13 @@ __global__ __launch_bounds__(256) void bwd_rowterms_kernel(RowArgs a) {
 // streamed operand in L2). Causal: workgroups launch largest-work first,
 // which is ascending w_in, or descending with `reverse`. Uneven head groups
 // or packed sequences (`spread`): the spread_coords order, which deals every
-// group and sequence over all XCDs.
-__device__ __forceinline__ void wg_coords(int bid, int spread, int block, int causal, bool reverse, int nwg,
-                                          int wg_per_bkv, int n_bkv, int& bkv, int& w_in) {
+// group and sequence over all XCDs; packed encoder-style (`pair_major`): the
+// pair_major_coords order (consecutive workgroups of an XCD share one pair's
+// streamed operand in L2). Returns false for a logical index past its pair's
+// last workgroup.
+__device__ __forceinline__ bool wg_coords(int bid, int pair_major, int spread, int block, int causal, bool reverse,
+                                          int nwg, int wg_per_bkv, int n_bkv, int& bkv, int& w_in) {
+  if (pair_major) return pair_major_coords(bid, n_bkv, wg_per_bkv, bkv, w_in);
   if (spread) {
     spread_coords(bid, n_bkv, wg_per_bkv, causal && reverse, block, bkv, w_in);
   } else if (!causal) {
@@ -142,6 +146,7 @@ __device__ __forceinline__ void wg_coords(int bid, int spread, int block, int ca
     bkv = L % n_bkv;
     w_in = reverse ? wg_per_bkv - 1 - wr : wr;
   }
+  return true;
 }
 
 // Range splits (encoder-style only): runs of 8 consecutive workgroups take
@@ -215,6 +220,7 @@ struct KvArgs {
   int N, Np, Hq, Hkv, wg_per_bkv, n_bkv, nwg;  // N: the (longest) sequence; Np: row-term rows per head
   int spread;  // uneven head groups or packed sequences: spread_coords order
   int spread_block;  // its rotation block
+  int pair_major;    // packed encoder-style: pair_major_coords order
   float c, scale;
   int causal;
   int nsplit;        // query-range splits (encoder-style only; 1: none)
@@ -378,7 +384,9 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dkdv_kernel(KvAr
   int split, wid, bkv, w_in;
   split_decode(a.nsplit, split, wid);
   if (wid >= a.nwg) return;
-  wg_coords(wid, a.spread, a.spread_block, a.causal, false, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
+  if (!wg_coords(wid, a.pair_major, a.spread, a.spread_block, a.causal, false, a.nwg, a.wg_per_bkv, a.n_bkv, bkv,
+                 w_in))
+    return;
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
   const SeqGeom sg = seq_geom(a.cu, a.T, a.N, b, a.Hq, a.Hkv);
   const int N = sg.n;
@@ -549,6 +557,7 @@ struct DqArgs {
   int N, Np, Hq, Hkv, wg_per_bkv, n_bkv, nwg;  // sized for the longest sequence and the largest group
   int spread;  // uneven head groups or packed sequences: spread_coords order
   int spread_block;  // its rotation block
+  int pair_major;   // packed encoder-style: pair_major_coords order
   float c, scale;
   int causal;
   int nsplit;       // key-range splits (encoder-style only; 1: none)
@@ -680,7 +689,9 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dq_kernel(DqArgs
   int split, wid, bkv, w_in;
   split_decode(a.nsplit, split, wid);
   if (wid >= a.nwg) return;
-  wg_coords(wid, a.spread, a.spread_block, a.causal, true, a.nwg, a.wg_per_bkv, a.n_bkv, bkv, w_in);
+  if (!wg_coords(wid, a.pair_major, a.spread, a.spread_block, a.causal, true, a.nwg, a.wg_per_bkv, a.n_bkv, bkv,
+                 w_in))
+    return;
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
   const int slot = w_in * kWaves + wave;
   const HeadGroup hg = head_group(kvh, a.Hq, a.Hkv);
@@ -915,6 +926,7 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   // with splits the grids cover whole runs of 8 (see split_decode)
   auto grid_of = [&](int64_t nwg) { return nsplit == 1 ? nwg : (nwg + 7) / 8 * 8 * nsplit; };
   const int spread = (packed || p.Hq % p.Hkv != 0) ? 1 : 0;
+  const int pair_major = (packed && !p.causal) ? 1 : 0;  // as the d = 64 forward
   const int n_bkv = (int)(p.B * p.Hkv);
   const int block = spread_block(packed, n_bkv);
 
@@ -954,7 +966,8 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
     a.spread_block = block;
     a.wg_per_bkv = (tiles + kWaves - 1) / kWaves;
     a.n_bkv = n_bkv;
-    const int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;
+    a.pair_major = pair_major;
+    const int64_t nwg = pair_major ? pair_major_nwg(a.n_bkv, a.wg_per_bkv) : (int64_t)a.wg_per_bkv * a.n_bkv;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     a.nwg = (int)nwg;
     a.c = c;
@@ -989,7 +1002,8 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
     const int64_t slots = (int64_t)tiles * max_group(a.Hq, a.Hkv);
     a.wg_per_bkv = (int)((slots + kWaves - 1) / kWaves);
     a.n_bkv = n_bkv;
-    const int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;
+    a.pair_major = pair_major;
+    const int64_t nwg = pair_major ? pair_major_nwg(a.n_bkv, a.wg_per_bkv) : (int64_t)a.wg_per_bkv * a.n_bkv;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     a.nwg = (int)nwg;
     a.c = c;
@@ -1023,14 +1037,23 @@ size_t attn_bwd_split_bytes(int64_t q_rows, int64_t kv_rows, int64_t D, int nspl
 // four 32-row query slots; Dims<DH>::MINB workgroups fit per CU. Two splits
 // when they cut the rounds of the busier kernel by at least 10 %, or fill a
 // launch that is under half a round. Packed batches (T > 0 tokens, N the
-// longest sequence) as the forward's: two splits when packed_wants_split
-// (measured at 32k, longest sequence 18496 tokens, d = 64, counted TFLOP/s:
-// (8,4) 550 -> 608, (16,16) 525 -> 646). Causal launches are not split.
+// longest sequence, pair-major order) as the forward's: two splits when
+// packed_wants_split and the longest sequence's own dK/dV workgroups fill
+// between one and two rounds (measured at 32k, longest sequence 18496
+// tokens, d = 64, counted TFLOP/s, unsplit -> 2 ranges: (8,4) 629 -> 688 at
+// 1.13 rounds, (16,16) 738 -> 699 at 4.5). Causal launches are not split.
 int attn_bwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t T, int64_t D, bool causal,
                          int cus) {
   if (causal || (D != 64 && D != 128) || B <= 0 || N <= 0) return 1;
-  if (T > 0) return packed_wants_split(N, T) ? 2 : 1;
   const int64_t tiles = (N + kTileRows - 1) / kTileRows;
+  if (T > 0) {
+    const int minb1 = D == 64 ? Dims<1>::MINB : Dims<2>::MINB;
+    const double r1 = (double)(Hkv * ((tiles + kWaves - 1) / kWaves)) / ((double)(cus > 0 ? cus : 256) * minb1);
+    return (tiles >= 2 * kMinSplitTiles && packed_wants_split(N, T) && r1 > 1.0 && r1 < 2.0 &&
+            ceil(2.0 * r1) / 2.0 <= 0.9 * ceil(r1))
+               ? 2
+               : 1;
+  }
   if (tiles < 2 * kMinSplitTiles) return 1;
   const int minb = D == 64 ? Dims<1>::MINB : Dims<2>::MINB;
   const double slots = (double)(cus > 0 ? cus : 256) * minb;

@@ -233,7 +233,8 @@ def test_bwd_split_workspace_and_policy(lib):
     n = sqa.sqa_attn_bwd_num_splits
     assert n(1, 8, 4, 32768, 64) == 1                  # 1024 / 512 dK/dV workgroups per slot: whole rounds
     assert n(1, 8, 4, 18496, 64) == 2                  # 580 dK/dV workgroups: 1.13 rounds
-    assert n(8, 16, 16, 18496, 64, T=32768) == 2       # packed, longest sequence 56 % of the tokens
+    assert n(8, 8, 4, 18496, 64, T=32768) == 2         # packed: 580 dK/dV workgroups of the longest, 1.13 rounds
+    assert n(8, 16, 16, 18496, 64, T=32768) == 1       # 2320 of them, 4.5 rounds: the others fill the tail
     assert n(1, 8, 4, 18496, 64, causal=True) == 1     # never under a causal mask
     assert n(1, 8, 4, 18496, 32) == 1 and n(1, 8, 4, 1000, 64) == 1
 
