@@ -97,6 +97,7 @@ struct Args {
   int spread;                  // 1: spread_coords order (packed sequences, causal uneven groups)
   int spread_block;   // rotation block of the spread order
   int exact_per_batch;         // > 0: exact_coords order with this many workgroups per batch
+  int pair_major;  // packed encoder-style: pair_major_coords order
   float c;
   uint32_t qsign;
   int causal;
@@ -333,7 +334,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d128_kernel(Args a)
   const int wid = (g8 / a.nsplit) * 8 + x8;
   if (wid >= a.nwg) return;
   int bkv, w_in;
-  if (a.spread) {
+  if (a.pair_major) {
+    if (!pair_major_coords(wid, a.n_bkv, a.wg_per_bkv, bkv, w_in)) return;
+  } else if (a.spread) {
     spread_coords(wid, a.n_bkv, a.wg_per_bkv, a.causal != 0, a.spread_block, bkv, w_in);
   } else if (a.exact_per_batch > 0 || !a.causal) {  // XCD-contiguous (shared L2)
     const int bid = wid;
@@ -562,6 +565,8 @@ hipError_t launch_attn_fwd_bf16_d128(const AttnProblem& p, hipStream_t stream) {
     a.exact_per_batch = (int)per;
     nwg = per * p.B;
   }
+  a.pair_major = (p.cu_seqlens != nullptr && !p.causal) ? 1 : 0;  // as the d = 64 kernel
+  if (a.pair_major) nwg = pair_major_nwg(a.n_bkv, a.wg_per_bkv);
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
   a.nwg = (int)nwg;
   a.c = fmaxf(fabsf(p.scale) * 1.4426950408889634f, kMinC);
