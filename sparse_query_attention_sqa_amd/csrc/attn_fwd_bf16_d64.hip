@@ -39,8 +39,13 @@
 // with sched_group_barrier hints alternating one MFMA with six VALU ops.
 //
 // Data movement. K and V tiles go straight from HBM to LDS with
-// buffer_load ... lds (no register staging), into a 5-slot ring with four
-// tiles of lookahead and one barrier per tile; the buffer descriptor's range
+// buffer_load ... lds (no register staging), into a 6-slot ring with one
+// barrier per two tiles: at the barrier of odd tile j every wave has read
+// tile j and everything before it, tiles up to j+3 have landed, and tiles
+// j+5 and j+6 are issued into the two slots just freed (tile j+4 is still in
+// flight). Measured against one barrier per tile (5 slots): 1045 -> 1065
+// TFLOP/s encoder-style and 946 -> 961 causal at N = 32768, (8,4), on one
+// box; packed batches unchanged. The buffer descriptor's range
 // check zero-fills keys past N. Both tiles are stored row-major (128 B rows)
 // with an XOR swizzle of their 16-byte chunks; K fragments are 16-byte
 // ds_read_b128, and V^T fragments come from ds_read_b64_tr_b16, whose
@@ -48,7 +53,7 @@
 // column. K(j+1) is already resident during phase A(j), so its fragments are
 // read there, ahead of the MFMAs of phase B(j) that use them. With the loop
 // unrolled over the ring slots every LDS address is a per-lane register plus
-// an immediate, so the per-tile barrier block has no VALU work.
+// an immediate, so the barrier block has no VALU work.
 //
 // Softmax. fp32, base-2 exponentials of s*c - m with c = |scale|*log2(e);
 // probabilities are rounded to bf16 (nearest even) for the P.V MFMA and the
@@ -92,7 +97,7 @@ constexpr int kTileKeys = 32;                      // keys per K/V tile
 constexpr int kRowBytes = D * 2;                   // 128 B per key row
 constexpr int kTileBytes = kTileKeys * kRowBytes;  // 4 KB (K or V)
 constexpr int kSlotBytes = 2 * kTileBytes;         // K then V
-constexpr int NBUF = 5;                            // ring slots
+constexpr int NBUF = 6;                            // ring slots
 constexpr int kXcds = 8;
 constexpr float kSumLimit = 1048576.0f;            // 2^20
 constexpr float kMaskedScore = -3.0e38f;
@@ -298,11 +303,13 @@ struct Ctx {
   float c;
 };
 
-// One pipeline step over tile j, whose K/V sit in ring slot SLOT = j % NBUF.
-template <int SLOT>
+// One pipeline step over tile j, whose K/V sit in ring slot SLOT = j % NBUF;
+// BAR (odd j) steps hold the workgroup barrier, the others a scheduling
+// barrier in its place so that both phases keep their own regions.
+template <int SLOT, bool BAR>
 __device__ __forceinline__ void step(const Ctx& cx, const Lane& ln, WaveState& w, int j) {
   constexpr int NEXT = (SLOT + 1) % NBUF;
-  constexpr int AHEAD = (SLOT + 4) % NBUF;
+  constexpr int PREV = (SLOT + NBUF - 1) % NBUF;
   const int key0 = j * kTileKeys;
   const bool active = j <= cx.last;
   const bool masked = (cx.causal && j >= cx.diag0) || (key0 + kTileKeys > cx.N);
@@ -319,10 +326,16 @@ __device__ __forceinline__ void step(const Ctx& cx, const Lane& ln, WaveState& w
     finish_half(ls, w.sB, w.pk0, w.m_run[0], w.l_run[0], w.acc_o[0], cx.c);
   }
 
-  // tiles j+1 and j+2 must have landed (tile j+3 may still be in flight);
-  // every wave is done with tile j-1, whose slot receives tile j+4.
-  wait_vm_then_barrier(j + 3 < cx.nt);
-  if (j + 4 < cx.nt) issue_tile<AHEAD>(cx.ring, cx.kbase, cx.vbase, j + 4, cx.N, cx.wave, ln);
+  // BAR: tiles up to j+3 must have landed (tile j+4 may still be in flight),
+  // for the reads of phases A(j+1) and A(j+2); every wave is done with tiles
+  // j-1 and j, whose slots receive tiles j+5 and j+6.
+  if (BAR) {
+    wait_vm_then_barrier(j + 4 < cx.nt);
+    if (j + 5 < cx.nt) issue_tile<PREV>(cx.ring, cx.kbase, cx.vbase, j + 5, cx.N, cx.wave, ln);
+    if (j + 6 < cx.nt) issue_tile<SLOT>(cx.ring, cx.kbase, cx.vbase, j + 6, cx.N, cx.wave, ln);
+  } else {
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // ---------------- phase B(j)
   if (active) {
@@ -341,12 +354,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   __shared__ __attribute__((aligned(16))) uint8_t ring2[kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ring3[kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ring4[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring5[kSlotBytes];
   Ring ring;
   ring.p[0] = ring0;
   ring.p[1] = ring1;
   ring.p[2] = ring2;
   ring.p[3] = ring3;
   ring.p[4] = ring4;
+  ring.p[5] = ring5;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -478,12 +493,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
       reinterpret_cast<u32x4_t*>(ring.p[sl])[e] = u32x4_t{0u, 0u, 0u, 0u};
   wait_vm_then_barrier(false);
 
-  // prologue: tiles 0..3 in flight, wait for tiles 0..2, S(0,h0)
+  // prologue: tiles 0..2 landed, then tiles 3..5 in flight, S(0,h0)
   issue_tile<0>(ring, kbase, vbase, 0, Nk, wave, ln);
   if (nt > 1) issue_tile<1>(ring, kbase, vbase, 1, Nk, wave, ln);
   if (nt > 2) issue_tile<2>(ring, kbase, vbase, 2, Nk, wave, ln);
+  wait_vm_then_barrier(false);
   if (nt > 3) issue_tile<3>(ring, kbase, vbase, 3, Nk, wave, ln);
-  wait_vm_then_barrier(nt > 3);
+  if (nt > 4) issue_tile<4>(ring, kbase, vbase, 4, Nk, wave, ln);
+  if (nt > 5) issue_tile<5>(ring, kbase, vbase, 5, Nk, wave, ln);
 
   Ctx cx;
   cx.ring = ring;
@@ -503,11 +520,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   mfma_s(w.kf, w.qf[0], w.sB);
 
   for (int j = 0; j < nt; j += NBUF) {
-    step<0>(cx, ln, w, j);
-    if (j + 1 < nt) step<1>(cx, ln, w, j + 1);
-    if (j + 2 < nt) step<2>(cx, ln, w, j + 2);
-    if (j + 3 < nt) step<3>(cx, ln, w, j + 3);
-    if (j + 4 < nt) step<4>(cx, ln, w, j + 4);
+    step<0, false>(cx, ln, w, j);
+    if (j + 1 < nt) step<1, true>(cx, ln, w, j + 1);
+    if (j + 2 < nt) step<2, false>(cx, ln, w, j + 2);
+    if (j + 3 < nt) step<3, true>(cx, ln, w, j + 3);
+    if (j + 4 < nt) step<4, false>(cx, ln, w, j + 4);
+    if (j + 5 < nt) step<5, true>(cx, ln, w, j + 5);
   }
   if (last >= 0) mfma_pv(w.vf, w.pk1, w.acc_o[1]);  // drain P(last,h1) V(last)
 
