@@ -210,6 +210,31 @@ sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void*
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sqa_attn_bwd_noalloc -- sqa_attn_bwd without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving or training loops, and harnesses that forbid allocation.
+ * Same arguments (minus workspace) and the same kernels, so the same
+ * results as sqa_attn_bwd bit for bit. The row terms go into a fixed
+ * 32 MiB device buffer that the library holds on each GPU it runs on, from
+ * the first call on that GPU until the process ends: the problem must
+ * satisfy sqa_attn_bwd_workspace_bytes(B, H_q, N, d, dtype) <= 33554432
+ * (8 B per query row, rows of each (batch, query head) padded to a multiple
+ * of 32: about 4.19M rows, e.g. B*H_q = 16 heads at N = 262144), else
+ * SQA_ERR_WORKSPACE and nothing is launched. Nothing in the buffer needs to
+ * start at zero: every call writes all of the entries it reads. The call
+ * allocates nothing and calls no allocating routine; its first call on a
+ * device looks up the buffer's address (hipGetSymbolAddress).
+ * Calls that overlap in time on one GPU (different streams, or different
+ * host threads) share the buffer and race: serialise them.
+ * Errors: as sqa_attn_bwd (SQA_ERR_WORKSPACE for problems over the limit;
+ * SQA_ERR_HIP if the address lookup fails).
+ */
+sqa_status sqa_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q,
+                                int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal,
+                                void* stream);
+
+/*
  * sqa_attn_bwd_varlen_workspace_bytes -- bytes of device workspace
  * sqa_attn_bwd_varlen needs: one fp32 pair (lse * log2(e), D_t) per packed
  * row plus 32 rows of padding per query head, 8 * H_q * (T + 32) bytes

@@ -11,6 +11,7 @@ library is not built, importing the functions raises.
     sqa_attn_bwd(q, k, v, o, dout, lse, *, scale=None, causal=False, dq=None, dk=None,
                  dv=None, workspace=None)
     sqa_attn_bwd_workspace_bytes(B, H_q, N, d, dtype="bf16")
+    sqa_attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, *, scale=None, causal=False)
     sqa_attn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen=None, *, scale=None, causal=False,
                         dq=None, dk=None, dv=None, workspace=None)
     sqa_attn_bwd_varlen_workspace_bytes(B, H_q, T, d, dtype="bf16")
@@ -29,7 +30,7 @@ import os
 from typing import Optional
 
 __all__ = ["SQAError", "lib_path", "load_library", "sqa_attn_fwd", "sqa_attn_fwd_varlen",
-           "sqa_attn_fwd_num_splits", "sqa_attn_bwd", "sqa_attn_bwd_num_splits",
+           "sqa_attn_fwd_num_splits", "sqa_attn_bwd", "sqa_attn_bwd_noalloc", "sqa_attn_bwd_num_splits",
            "sqa_attn_bwd_split_workspace_bytes", "sqa_attn_bwd_varlen_split_workspace_bytes",
            "sqa_attn_bwd_varlen", "sqa_attn_bwd_varlen_workspace_bytes",
            "sqa_attn_bwd_workspace_bytes", "sqa_layer_fwd", "sqa_block_fwd",
@@ -100,6 +101,8 @@ def load_library() -> ctypes.CDLL:
     lib.sqa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                  ctypes.c_int, f32, ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.sqa_attn_bwd.restype = ctypes.c_int
+    lib.sqa_attn_bwd_noalloc.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_int, f32, ctypes.c_int, vp]
+    lib.sqa_attn_bwd_noalloc.restype = ctypes.c_int
     lib.sqa_attn_bwd_varlen_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.sqa_attn_bwd_varlen_workspace_bytes.restype = ctypes.c_size_t
     lib.sqa_attn_bwd_varlen.argtypes = [vp] * 10 + [i64] * 6 + [ctypes.c_int, f32, ctypes.c_int, vp,
@@ -344,6 +347,36 @@ def sqa_attn_bwd(q, k, v, o, dout, lse, *, scale: Optional[float] = None, causal
                                 _stream_handle(q.device))
     _check(st)
     return outs[0], outs[1], outs[2]
+
+
+def sqa_attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, *, scale: Optional[float] = None,
+                         causal: bool = False) -> None:
+    """``sqa_attn_bwd`` into caller-provided dq, dk, dv with no allocation at
+    all (no workspace: the library's fixed per-GPU buffer holds the row
+    terms), for code under graph capture or loops that may not allocate.
+    Same results as ``sqa_attn_bwd``; raises SQAError (SQA_ERR_WORKSPACE)
+    for problems whose row terms exceed that buffer. Calls that overlap on
+    one GPU share the buffer and race."""
+    lib = load_library()
+    _require_device(q, k, v, o, dout, lse, dq, dk, dv)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected 4-D [B, H, N, d] tensors")
+    if k.shape != v.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("k/v and q/o/dout shapes must match")
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("dq, dk and dv must match q, k and v in shape")
+    if len({q.dtype, k.dtype, v.dtype, o.dtype, dout.dtype, dq.dtype, dk.dtype, dv.dtype}) != 1:
+        raise ValueError("q, k, v, o, dout and the gradients must share a dtype")
+    B, H_q, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d or tuple(lse.shape) != (B, H_q, N):
+        raise ValueError("q, k/v and lse shapes disagree")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.sqa_attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                  B, H_q, k.shape[1], N, d, _dtype_code(q), float(scale), int(bool(causal)),
+                                  _stream_handle(q.device))
+    _check(st)
 
 
 def _bwd_splits(lib, num_splits, workspace, need_of, auto) -> int:

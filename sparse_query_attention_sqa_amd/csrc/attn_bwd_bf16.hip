@@ -40,6 +40,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "bf16_tiles.h"
 #include "kernels.h"
 #include "seq_groups.h"
@@ -1079,6 +1081,38 @@ hipError_t launch_attn_bwd_bf16(const BwdProblem& p, hipStream_t stream) {
   if (p.D == 64) return launch_bwd<1>(p, stream);
   if (p.D == 128) return launch_bwd<2>(p, stream);
   return hipErrorInvalidValue;
+}
+
+}  // namespace sqa
+
+// Row-term buffer of the allocation-free backward (sqa_attn_bwd_noalloc):
+// one copy per GPU, loaded with the code object and held until the process
+// ends. Host code never passes this name to a kernel (on the host it is only
+// a stand-in for the device symbol); it passes the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[sqa::kNoAllocScratchBytes];
+
+namespace sqa {
+
+// Device address of `scratch` on the current device, looked up once per
+// device and cached (concurrent first calls on one device store the same
+// address).
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace sqa

@@ -78,6 +78,11 @@ bool packed_wants_split(int64_t N, int64_t T);
 size_t attn_bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N);
 size_t attn_bwd_rowterm_bytes_packed(int64_t Hq, int64_t T);
 hipError_t launch_attn_bwd_bf16(const BwdProblem& p, hipStream_t stream);
+// Fixed device buffer of the allocation-free backward: kNoAllocScratchBytes
+// per GPU (room for the row terms of 4M padded query rows). noalloc_scratch
+// returns its address on the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void** ptr);
 
 // Projection + RoPE: x [M=B*N, Dm] bf16 times w_q [Dm,Hq*d] | w_k [Dm,Hkv*d] |
 // w_v [Dm,Hkv*d]; writes q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16 with RoPE applied

@@ -252,11 +252,17 @@ sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void*
                             workspace, workspace_bytes, stream);
 }
 
-sqa_status sqa_attn_bwd_split(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                              const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q,
-                              int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal,
-                              int64_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// Every argument rule of the dense backward except the workspace's; `need`
+// receives the workspace bytes num_splits needs (0 for an empty problem,
+// which returns SQA_OK with nothing to launch).
+sqa_status check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q, int64_t H_kv,
+                     int64_t N, int64_t d, int dtype, float scale, int causal, int64_t num_splits, size_t* need) {
+  *need = 0;
   sqa_status s = check_attn(B, H_q, H_kv, N, d, dtype, scale, causal);
   if (s != SQA_OK) return s;
   if (dtype != SQA_BF16 || (d != 64 && d != 128))
@@ -271,25 +277,26 @@ sqa_status sqa_attn_bwd_split(const void* q, const void* k, const void* v, const
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return fail(SQA_ERR_ALIGN, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
   if (!aligned(lse, 4)) return fail(SQA_ERR_ALIGN, "lse must be 4-byte aligned");
-  const size_t need = sqa_attn_bwd_split_workspace_bytes(B, H_q, H_kv, N, d, dtype, num_splits);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(SQA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (!aligned(workspace, 16)) return fail(SQA_ERR_ALIGN, "workspace must be 16-byte aligned");
   const size_t nq = (size_t)(B * H_q * N * d) * 2, nkv = (size_t)(B * H_kv * N * d) * 2;
   const size_t nl = (size_t)(B * H_q * N) * 4;
   const void* ins[6] = {q, k, v, o, dout, lse};
   const size_t in_n[6] = {nq, nkv, nkv, nq, nq, nl};
-  const void* outs[4] = {dq, dk, dv, workspace};
-  const size_t out_n[4] = {nq, nkv, nkv, need};
-  for (int a = 0; a < 4; ++a) {
+  const void* outs[3] = {dq, dk, dv};
+  const size_t out_n[3] = {nq, nkv, nkv};
+  for (int a = 0; a < 3; ++a) {
     for (int b = 0; b < 6; ++b)
-      if (overlaps(outs[a], out_n[a], ins[b], in_n[b]))
-        return fail(SQA_ERR_ARG, "an output or the workspace overlaps an input");
-    for (int b = a + 1; b < 4; ++b)
-      if (overlaps(outs[a], out_n[a], outs[b], out_n[b]))
-        return fail(SQA_ERR_ARG, "outputs and workspace must not overlap each other");
+      if (overlaps(outs[a], out_n[a], ins[b], in_n[b])) return fail(SQA_ERR_ARG, "an output overlaps an input");
+    for (int b = a + 1; b < 3; ++b)
+      if (overlaps(outs[a], out_n[a], outs[b], out_n[b])) return fail(SQA_ERR_ARG, "outputs must not overlap");
   }
+  *need = sqa_attn_bwd_split_workspace_bytes(B, H_q, H_kv, N, d, dtype, num_splits);
+  return SQA_OK;
+}
+
+sqa_status launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q, int64_t H_kv,
+                      int64_t N, int64_t d, int dtype, float scale, int causal, int64_t num_splits, void* workspace,
+                      void* stream) {
   sqa::BwdProblem p{q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H_q, H_kv, N, d, scale, causal};
   p.nsplit = (int)num_splits;
   p.split_ws = num_splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
@@ -298,6 +305,52 @@ sqa_status sqa_attn_bwd_split(const void* q, const void* k, const void* v, const
   hipError_t e = sqa::launch_attn_bwd_bf16(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   return SQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sqa_status sqa_attn_bwd_split(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q,
+                              int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal,
+                              int64_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  size_t need = 0;
+  sqa_status s = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H_q, H_kv, N, d, dtype, scale, causal, num_splits,
+                           &need);
+  if (s != SQA_OK || need == 0) return s;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SQA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(SQA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  const size_t nq = (size_t)(B * H_q * N * d) * 2, nkv = (size_t)(B * H_kv * N * d) * 2;
+  const size_t nl = (size_t)(B * H_q * N) * 4;
+  const void* ts[9] = {q, k, v, o, dout, lse, dq, dk, dv};
+  const size_t tn[9] = {nq, nkv, nkv, nq, nq, nl, nq, nkv, nkv};
+  for (int i = 0; i < 9; ++i)
+    if (overlaps(workspace, need, ts[i], tn[i])) return fail(SQA_ERR_ARG, "the workspace overlaps a tensor");
+  return launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H_q, H_kv, N, d, dtype, scale, causal, num_splits,
+                    workspace, stream);
+}
+
+sqa_status sqa_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q,
+                                int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal,
+                                void* stream) {
+  g_err.clear();
+  size_t need = 0;
+  sqa_status s = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H_q, H_kv, N, d, dtype, scale, causal, 1, &need);
+  if (s != SQA_OK || need == 0) return s;
+  if (need > sqa::kNoAllocScratchBytes)
+    return fail(SQA_ERR_WORKSPACE,
+                "the row terms need %zu bytes, more than the %zu-byte buffer of the allocation-free backward",
+                need, sqa::kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = sqa::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "looking up the allocation-free backward's buffer");
+  return launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H_q, H_kv, N, d, dtype, scale, causal, 1, scratch,
+                    stream);
 }
 
 size_t sqa_attn_bwd_varlen_workspace_bytes(int64_t B, int64_t H_q, int64_t T, int64_t d, int dtype) {

@@ -336,6 +336,38 @@ def test_bwd_zero_size_is_a_noop(lib):
     assert _bwd(lib, N=0, ws=None) == 0
 
 
+def _bwd_noalloc(lib, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000,
+                 do=FAKE + 0x400000, lse=FAKE + 0x500000, dq=FAKE + 0x600000, dk=FAKE + 0x700000,
+                 dv=FAKE + 0x800000, B=1, Hq=8, Hkv=4, N=1024, d=64, dtype=1, scale=0.125, causal=0):
+    return lib.sqa_attn_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, B, Hq, Hkv, N, d, dtype, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(Hkv=9), 2), (dict(d=16), 3), (dict(lse=FAKE + 0x500002), 4),
+    (dict(scale=float("inf")), 7), (dict(dq=FAKE + 0x300000), 7),
+])
+@cpu_only
+def test_bwd_noalloc_rejects_invalid_arguments(lib, kw, code):
+    # every check runs before the buffer lookup, so no HIP call is made
+    assert _bwd_noalloc(lib, **kw) == code
+    assert lib.sqa_last_error().decode() != ""
+
+
+@cpu_only
+def test_bwd_noalloc_rejects_problems_over_its_buffer(lib):
+    # 32 query heads x 262144 rows x 8 B = 64 MiB of row terms > the 32 MiB
+    # buffer (16 heads x 262144 rows is exactly 32 MiB: accepted by the size
+    # rule, so it is not called here, where there is no device)
+    g = 1 << 32  # tensors of up to 1 GiB each, spaced apart so none overlap
+    ptrs = dict(q=FAKE, k=FAKE + g, v=FAKE + 2 * g, o=FAKE + 3 * g, do=FAKE + 4 * g, lse=FAKE + 5 * g,
+                dq=FAKE + 6 * g, dk=FAKE + 7 * g, dv=FAKE + 8 * g)
+    assert sqa.sqa_attn_bwd_workspace_bytes(1, 16, 262144, 64) == 32 << 20
+    assert _bwd_noalloc(lib, Hq=32, Hkv=8, N=262144, **ptrs) == 5
+    assert "buffer" in lib.sqa_last_error().decode()
+    assert _bwd_noalloc(lib, B=0, q=None) == 0     # empty problems return at once
+    assert _bwd_noalloc(lib, N=0) == 0
+
+
 def test_bwd_varlen_workspace_bytes(lib):
     # 8 B per (query head, packed row), plus 32 padding rows per head
     assert sqa.sqa_attn_bwd_varlen_workspace_bytes(3, 8, 1000, 64) == 8 * 8 * 1032
