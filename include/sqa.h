@@ -25,6 +25,20 @@
  *     surface at the caller's next synchronisation.
  *   - Zero-sized problems (B == 0 or N == 0) return SQA_OK and launch nothing.
  *   - No exceptions or output cross this interface.
+ *
+ * Size limits (SQA_ERR_SHAPE, checked before anything is launched):
+ *   - N (or max_seqlen) <= 2^30 and every tensor <= 2^40 elements.
+ *   - bf16 attention with d = 64: N <= 16777215 (one head's K or V rows,
+ *     N * 128 bytes, must stay below 2^31, the range of a buffer
+ *     descriptor); d = 128: N <= 8388607. The backward has the same limits.
+ *   - Grid sizes: B * H_kv, B * H_q and every kernel's workgroup count must
+ *     stay below 2^31.
+ *   - Layer and block: the activations [B*N, D] and every weight matrix
+ *     below 2^31 bytes (32-bit offsets of the projection kernels), and one
+ *     sequence's heads (H_q * N * d bf16 values) below 2^31 bytes.
+ *   A problem past these limits returns SQA_ERR_SHAPE with the kernel whose
+ *   limit it exceeds named in sqa_last_error(); SQA_ERR_HIP is reserved for
+ *   failures the HIP runtime reports.
  */
 #ifndef SQA_H_
 #define SQA_H_
@@ -39,7 +53,7 @@ extern "C" {
 typedef enum {
   SQA_OK = 0,
   SQA_ERR_NULL = 1,        /* a required pointer is NULL                         */
-  SQA_ERR_SHAPE = 2,       /* negative size, H_kv not in [1, H_q], too large      */
+  SQA_ERR_SHAPE = 2,       /* negative size, H_kv not in [1, H_q], past a limit   */
   SQA_ERR_UNSUPPORTED = 3, /* valid but not implemented: d, dtype, ...            */
   SQA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                     */
   SQA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required              */

@@ -19,9 +19,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsqa.so")
+PROBE_LIB = os.path.join(PKG, "libsqa_probe.so")
+PROBE_SOURCES = ["issue_probe.hip"]
 
 SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_bf16_d64.hip", "attn_fwd_bf16_d128.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip",
-           "gemm_bf16.hip", "norm_rope.hip", "sqa_api.cpp"]
+           "gemm_bf16.hip", "rms_norm.hip", "sqa_api.cpp"]
 
 
 def hipcc() -> str:
@@ -51,19 +53,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link LIB. Always rebuilds. Returns LIB."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking libsqa.so failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link LIB (the attention library) and
+    PROBE_LIB (the issue-rate probes). Always rebuilds. Returns LIB."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return LIB
 
 

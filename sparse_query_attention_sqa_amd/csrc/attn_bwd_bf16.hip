@@ -886,6 +886,7 @@ __global__ __launch_bounds__(256) void bwd_split_sum_kernel(SumArgs a) {
 }
 
 hipError_t launch_split_sum(const float* part, void* out, const BwdProblem& p, int64_t rows, hipStream_t stream) {
+  if (p.B > 0x7fffffff) return hipErrorInvalidValue;
   SumArgs a;
   a.part = part;
   a.out = static_cast<uint16_t*>(out);
@@ -898,6 +899,7 @@ hipError_t launch_split_sum(const float* part, void* out, const BwdProblem& p, i
   a.nsplit = p.nsplit;
   const int64_t blocks = (rows * (p.D / 4) + 255) / 256;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (p.dry_run) return hipSuccess;
   hipLaunchKernelGGL(bwd_split_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -929,6 +931,7 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   auto grid_of = [&](int64_t nwg) { return nsplit == 1 ? nwg : (nwg + 7) / 8 * 8 * nsplit; };
   const int spread = (packed || p.Hq % p.Hkv != 0) ? 1 : 0;
   const int pair_major = (packed && !p.causal) ? 1 : 0;  // as the d = 64 forward
+  if (p.B * p.Hkv > 0x7fffffff || p.B * p.Hq > 0x7fffffff) return hipErrorInvalidValue;
   const int n_bkv = (int)(p.B * p.Hkv);
   const int block = spread_block(packed, n_bkv);
 
@@ -944,9 +947,11 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
     a.Np = Np;
     const int64_t nblk = (a.nrows + 31) / 32;
     if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(bwd_rowterms_kernel<DH>, dim3((unsigned)nblk), dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (!p.dry_run) {
+      hipLaunchKernelGGL(bwd_rowterms_kernel<DH>, dim3((unsigned)nblk), dim3(256), 0, stream, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   const int tiles = (N + kTileRows - 1) / kTileRows;  // of the longest sequence
   {
@@ -981,9 +986,11 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
     a.kv_rows = kv_rows;
     const int64_t grid = grid_of(a.nwg);
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<DH>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (!p.dry_run) {
+      hipLaunchKernelGGL(bwd_dkdv_kernel<DH>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   {
     DqArgs a;
@@ -1002,6 +1009,7 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
     a.spread = spread;
     a.spread_block = block;
     const int64_t slots = (int64_t)tiles * max_group(a.Hq, a.Hkv);
+    if ((slots + kWaves - 1) / kWaves > 0x7fffffff || (int64_t)tiles * p.Hq > 0x7fffffff) return hipErrorInvalidValue;
     a.wg_per_bkv = (int)((slots + kWaves - 1) / kWaves);
     a.n_bkv = n_bkv;
     a.pair_major = pair_major;
@@ -1016,9 +1024,12 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
     a.q_rows = q_rows;
     const int64_t grid = grid_of(a.nwg);
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(bwd_dq_kernel<DH>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || nsplit == 1) return e;
+    if (!p.dry_run) {
+      hipLaunchKernelGGL(bwd_dq_kernel<DH>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (nsplit == 1) return hipSuccess;
   }
   hipError_t e = launch_split_sum(part_k, p.dk, p, kv_rows, stream);
   if (e == hipSuccess) e = launch_split_sum(part_v, p.dv, p, kv_rows, stream);

@@ -554,7 +554,10 @@ hipError_t launch_attn_fwd_bf16_d128(const AttnProblem& p, hipStream_t stream) {
   a.spread_block = spread_block(p.cu_seqlens != nullptr, p.B * p.Hkv);
   const int TB = (int)((p.N + kRowsPerWave - 1) / kRowsPerWave);
   const int64_t slots = (int64_t)TB * max_group(a.Hq, a.Hkv);
-  a.wg_per_bkv = (int)((slots + kWaves - 1) / kWaves);
+  const int64_t wg_per_bkv = (slots + kWaves - 1) / kWaves;
+  if (wg_per_bkv > 0x7fffffff || p.B * p.Hkv > 0x7fffffff || (int64_t)TB * p.Hq > 0x7fffffff)
+    return hipErrorInvalidValue;
+  a.wg_per_bkv = (int)wg_per_bkv;
   a.n_bkv = (int)(p.B * p.Hkv);
   int64_t nwg = (int64_t)a.wg_per_bkv * a.n_bkv;
   a.exact_per_batch = 0;
@@ -579,9 +582,12 @@ hipError_t launch_attn_fwd_bf16_d128(const AttnProblem& p, hipStream_t stream) {
   // with splits the grid covers whole runs of 8 (see the kernel's decode)
   const int64_t grid = a.nsplit == 1 ? a.nwg : ((int64_t)a.nwg + 7) / 8 * 8 * a.nsplit;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit == 1) return e;
+  if (!p.dry_run) {
+    hipLaunchKernelGGL(attn_fwd_bf16_d128_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.nsplit == 1) return hipSuccess;
   SplitMergeArgs m;
   m.part = a.part;
   m.o = a.o;
@@ -596,7 +602,7 @@ hipError_t launch_attn_fwd_bf16_d128(const AttnProblem& p, hipStream_t stream) {
   m.tile_keys = kTileKeys;
   m.min_tiles = kMinSplitTiles;
   m.even = 0;
-  return launch_split_merge<D>(m, stream);
+  return launch_split_merge<D>(m, stream, p.dry_run);
 }
 
 }  // namespace sqa

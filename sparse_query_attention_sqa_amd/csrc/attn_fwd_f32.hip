@@ -157,6 +157,7 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
   a.causal = p.causal;
   const int64_t nblk = (int64_t)a.blocks_per_head * p.B * p.Hq;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  if (p.dry_run) return hipSuccess;
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D, S>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

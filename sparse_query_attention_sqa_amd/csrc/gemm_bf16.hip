@@ -421,10 +421,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
 }
 
 template <int EPI, int S, bool GATHER, int MB>
-hipError_t launch_grid(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_grid(const GemmArgs& a, hipStream_t stream, bool dry_run) {
   const int64_t mtiles = (a.A.M + Tiling<MB>::TM - 1) / Tiling<MB>::TM;
   const int64_t nblk = mtiles * a.tiles_total;
   if (nblk > 0x7fffffff || nblk <= 0) return hipErrorInvalidValue;
+  if (dry_run) return hipSuccess;
   hipLaunchKernelGGL((gemm_kernel<EPI, S, GATHER, MB>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -437,18 +438,19 @@ hipError_t launch_grid(const GemmArgs& a, hipStream_t stream) {
 // four stages before; 64-row with two or four stages were slower). Larger
 // grids (the gate/up projection) keep 128 rows and two stages.
 template <int EPI, bool GATHER>
-hipError_t launch_stages(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_stages(const GemmArgs& a, hipStream_t stream, bool dry_run) {
   const int64_t nblk128 = ((a.A.M + 127) / 128) * a.tiles_total;
-  if (nblk128 <= 384) return launch_grid<EPI, 3, GATHER, 1>(a, stream);
-  return launch_grid<EPI, 2, GATHER, 2>(a, stream);
+  if (nblk128 <= 384) return launch_grid<EPI, 3, GATHER, 1>(a, stream, dry_run);
+  return launch_grid<EPI, 2, GATHER, 2>(a, stream, dry_run);
 }
 
-hipError_t launch(const GemmArgs& a, int epi, hipStream_t stream) {
+hipError_t launch(const GemmArgs& a, int epi, hipStream_t stream, bool dry_run) {
   if (a.tiles_total <= 0 || a.A.M <= 0) return hipErrorInvalidValue;
   if (epi == EPI_STORE)
-    return a.A.gather ? launch_stages<EPI_STORE, true>(a, stream) : launch_stages<EPI_STORE, false>(a, stream);
-  if (epi == EPI_SWIGLU) return launch_stages<EPI_SWIGLU, false>(a, stream);
-  return launch_stages<EPI_QKV, false>(a, stream);
+    return a.A.gather ? launch_stages<EPI_STORE, true>(a, stream, dry_run)
+                      : launch_stages<EPI_STORE, false>(a, stream, dry_run);
+  if (epi == EPI_SWIGLU) return launch_stages<EPI_SWIGLU, false>(a, stream, dry_run);
+  return launch_stages<EPI_QKV, false>(a, stream, dry_run);
 }
 
 GemmArgs base_args() {
@@ -475,6 +477,8 @@ hipError_t launch_qkv_rope(const QkvProblem& p, hipStream_t stream) {
   if (!fits(a.A.M * a.A.K * 2)) return hipErrorInvalidValue;
   const void* w[3] = {p.wq, p.wk, p.wv};
   const int64_t nc[3] = {p.Hq * p.d, p.Hkv * p.d, p.Hkv * p.d};
+  // 32-bit offsets: weights, and the heads of one sequence in the scatter
+  if (!fits(p.Dm * nc[0] * 2) || !fits(p.Dm * nc[1] * 2) || !fits(p.Hq * p.N * p.d * 2)) return hipErrorInvalidValue;
   a.nparts = 3;
   a.segs_total = 0;
   for (int i = 0; i < 3; ++i) {
@@ -495,7 +499,7 @@ hipError_t launch_qkv_rope(const QkvProblem& p, hipStream_t stream) {
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.d = p.d;
-  return launch(a, EPI_QKV, stream);
+  return launch(a, EPI_QKV, stream, p.dry_run);
 }
 
 hipError_t launch_out_proj(const OprojProblem& p, hipStream_t stream) {
@@ -508,7 +512,7 @@ hipError_t launch_out_proj(const OprojProblem& p, hipStream_t stream) {
   a.A.N = p.N;
   a.A.Hq = p.Hq;
   a.A.d = p.d;
-  if (!fits(a.A.M * a.A.K * 2)) return hipErrorInvalidValue;
+  if (!fits(a.A.M * a.A.K * 2) || !fits(a.A.K * p.Dm * 2) || !fits(a.A.M * p.Dm * 2)) return hipErrorInvalidValue;
   a.nparts = 1;
   a.part[0].w = static_cast<const uint16_t*>(p.wo);
   a.part[0].ncols = p.Dm;
@@ -518,7 +522,7 @@ hipError_t launch_out_proj(const OprojProblem& p, hipStream_t stream) {
   a.epi = EPI_STORE;
   a.resid = static_cast<const uint16_t*>(p.resid);
   a.y = static_cast<uint16_t*>(p.y);
-  return launch(a, EPI_STORE, stream);
+  return launch(a, EPI_STORE, stream, p.dry_run);
 }
 
 hipError_t launch_dense_residual(const DenseProblem& p, hipStream_t stream) {
@@ -527,7 +531,7 @@ hipError_t launch_dense_residual(const DenseProblem& p, hipStream_t stream) {
   a.A.p = static_cast<const uint16_t*>(p.a);
   a.A.M = p.M;
   a.A.K = p.K;
-  if (!fits(a.A.M * a.A.K * 2)) return hipErrorInvalidValue;
+  if (!fits(a.A.M * a.A.K * 2) || !fits(p.K * p.Ncols * 2) || !fits(p.M * p.Ncols * 2)) return hipErrorInvalidValue;
   a.nparts = 1;
   a.part[0].w = static_cast<const uint16_t*>(p.w);
   a.part[0].ncols = p.Ncols;
@@ -537,7 +541,7 @@ hipError_t launch_dense_residual(const DenseProblem& p, hipStream_t stream) {
   a.epi = EPI_STORE;
   a.resid = static_cast<const uint16_t*>(p.resid);
   a.y = static_cast<uint16_t*>(p.y);
-  return launch(a, EPI_STORE, stream);
+  return launch(a, EPI_STORE, stream, p.dry_run);
 }
 
 hipError_t launch_gate_up(const GateUpProblem& p, hipStream_t stream) {
@@ -546,7 +550,7 @@ hipError_t launch_gate_up(const GateUpProblem& p, hipStream_t stream) {
   a.A.p = static_cast<const uint16_t*>(p.z);
   a.A.M = p.M;
   a.A.K = p.K;
-  if (!fits(a.A.M * a.A.K * 2)) return hipErrorInvalidValue;
+  if (!fits(a.A.M * a.A.K * 2) || !fits(p.K * p.F * 2) || !fits(p.M * p.F * 2)) return hipErrorInvalidValue;
   a.nparts = 2;
   a.part[0].w = static_cast<const uint16_t*>(p.w_gate);
   a.part[0].ncols = p.F;
@@ -557,7 +561,7 @@ hipError_t launch_gate_up(const GateUpProblem& p, hipStream_t stream) {
   a.tiles_total = a.segs[0];
   a.epi = EPI_SWIGLU;
   a.y = static_cast<uint16_t*>(p.h);
-  return launch(a, EPI_SWIGLU, stream);
+  return launch(a, EPI_SWIGLU, stream, p.dry_run);
 }
 
 }  // namespace sqa

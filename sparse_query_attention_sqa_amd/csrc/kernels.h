@@ -29,6 +29,10 @@ struct AttnProblem {
   // (packed: Hq*T)
   int nsplit = 1;
   float* split_ws = nullptr;
+  // dry_run: run every check of the launcher (sizes against the 32-bit
+  // limits of grids, offsets and buffer descriptors) and launch nothing;
+  // hipErrorInvalidValue then means the problem exceeds a launch limit
+  bool dry_run = false;
 };
 
 size_t attn_split_workspace_bytes(int64_t rows, int64_t d, int nsplit);
@@ -69,6 +73,7 @@ struct BwdProblem {
   // attn_bwd_split_bytes(q_rows, kv_rows, D, nsplit) bytes
   int nsplit = 1;
   float* split_ws = nullptr;
+  bool dry_run = false;  // as in AttnProblem
 };
 size_t attn_bwd_split_bytes(int64_t q_rows, int64_t kv_rows, int64_t D, int nsplit);
 // recommended nsplit for the backward on a device with `cus` CUs
@@ -97,6 +102,7 @@ struct QkvProblem {
   void* v;
   int64_t B, N, Dm, Hq, Hkv, d;
   float rope_base;
+  bool dry_run = false;  // as in AttnProblem
 };
 hipError_t launch_qkv_rope(const QkvProblem& p, hipStream_t stream);
 
@@ -109,6 +115,7 @@ struct OprojProblem {
   void* y;
   int64_t B, N, Dm, Hq, d;
   const void* resid;  // optional [B*N, Dm] added in the epilogue (nullptr: none)
+  bool dry_run = false;  // as in AttnProblem
 };
 hipError_t launch_out_proj(const OprojProblem& p, hipStream_t stream);
 
@@ -119,12 +126,13 @@ struct DenseProblem {
   const void* resid;  // nullable
   void* y;
   int64_t M, K, Ncols;
+  bool dry_run = false;  // as in AttnProblem
 };
 hipError_t launch_dense_residual(const DenseProblem& p, hipStream_t stream);
 
 // y = x / sqrt(mean(x^2) + eps) * g over rows of D (bf16 in/out).
 hipError_t launch_rms_norm(const void* x, const void* g, void* y, int64_t M, int64_t D, float eps,
-                           hipStream_t stream);
+                           hipStream_t stream, bool dry_run = false);
 
 // h [M, F] = silu(z w_gate) * (z w_up); z [M, K], w_gate / w_up [K, F].
 struct GateUpProblem {
@@ -133,6 +141,7 @@ struct GateUpProblem {
   const void* w_up;
   void* h;
   int64_t M, K, F;
+  bool dry_run = false;  // as in AttnProblem
 };
 hipError_t launch_gate_up(const GateUpProblem& p, hipStream_t stream);
 

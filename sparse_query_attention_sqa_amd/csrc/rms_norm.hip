@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void rms_norm_kernel(NormArgs a) {
 }  // namespace
 
 hipError_t launch_rms_norm(const void* x, const void* g, void* y, int64_t M, int64_t D, float eps,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool dry_run) {
   if (D % 8 != 0 || D > (int64_t(1) << 20)) return hipErrorInvalidValue;
   NormArgs a;
   a.x = static_cast<const uint16_t*>(x);
@@ -83,6 +83,7 @@ hipError_t launch_rms_norm(const void* x, const void* g, void* y, int64_t M, int
   a.eps = eps;
   const int64_t nblk = (M + 7) / 8;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  if (dry_run) return hipSuccess;
   hipLaunchKernelGGL(rms_norm_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -89,10 +89,11 @@ __global__ __launch_bounds__(256) void attn_split_merge_kernel(SplitMergeArgs a)
 }
 
 template <int D>
-hipError_t launch_split_merge(const SplitMergeArgs& m, hipStream_t stream) {
+hipError_t launch_split_merge(const SplitMergeArgs& m, hipStream_t stream, bool dry_run) {
   constexpr int kRowsPerBlock = 256 / (D / 4);
   const int64_t blocks = (m.rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (dry_run) return hipSuccess;
   hipLaunchKernelGGL((attn_split_merge_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, m);
   return hipGetLastError();
 }

@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "kernels.h"
@@ -34,6 +35,23 @@ sqa_status hip_fail(hipError_t e, const char* what) {
   return fail(SQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// A launcher's dry run failed: the sizes pass the argument rules but exceed
+// a 32-bit limit of the kernels (grid size, offsets, buffer ranges).
+sqa_status limit_fail(const char* what) {
+  return fail(SQA_ERR_SHAPE, "%s: the sizes exceed a launch limit of the kernels (see include/sqa.h)", what);
+}
+
+// Dry-run the attention launch, then launch it.
+sqa_status launch_attn(sqa::AttnProblem p, int dtype, hipStream_t st) {
+  p.dry_run = true;
+  hipError_t e = (dtype == SQA_BF16) ? sqa::launch_attn_fwd_bf16(p, st) : sqa::launch_attn_fwd_f32(p, st);
+  if (e != hipSuccess) return limit_fail("attention");
+  p.dry_run = false;
+  e = (dtype == SQA_BF16) ? sqa::launch_attn_fwd_bf16(p, st) : sqa::launch_attn_fwd_f32(p, st);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return SQA_OK;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -46,6 +64,18 @@ constexpr int64_t kMaxN = (int64_t(1) << 30);          // positions per sequence
 constexpr int64_t kMaxElems = (int64_t(1) << 40);      // elements per tensor
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Product of non-negative factors <= lim, without overflowing int64_t.
+bool prod_le(std::initializer_list<int64_t> factors, int64_t lim) {
+  int64_t p = 1;
+  for (const int64_t f : factors) {
+    if (f < 0) return false;
+    if (f == 0) return true;
+    if (p > lim / f) return false;
+    p *= f;
+  }
+  return p <= lim;
+}
 
 // Shape rules shared by the attention and layer entry points.
 sqa_status check_heads(int64_t H_q, int64_t H_kv) {
@@ -68,7 +98,7 @@ sqa_status check_attn(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d
   if (!std::isfinite(scale)) return fail(SQA_ERR_ARG, "scale must be finite");
   if (causal != 0 && causal != 1) return fail(SQA_ERR_ARG, "causal must be 0 or 1 (got %d)", causal);
   if (N > kMaxN) return fail(SQA_ERR_SHAPE, "N=%lld exceeds the supported maximum", (long long)N);
-  if (B > 0 && N > 0 && B * H_q * N * d > kMaxElems)
+  if (B > 0 && N > 0 && !prod_le({B, H_q, N, d}, kMaxElems))
     return fail(SQA_ERR_SHAPE, "tensor too large");
   return SQA_OK;
 }
@@ -161,10 +191,7 @@ sqa_status sqa_attn_fwd_split(const void* q, const void* k, const void* v, void*
   sqa::AttnProblem p{q, k, v, o, lse, B, H_q, H_kv, N, d, scale, causal};
   p.nsplit = (int)num_splits;
   p.split_ws = num_splits > 1 ? static_cast<float*>(workspace) : nullptr;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = (dtype == SQA_BF16) ? sqa::launch_attn_fwd_bf16(p, st) : sqa::launch_attn_fwd_f32(p, st);
-  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-  return SQA_OK;
+  return launch_attn(p, dtype, static_cast<hipStream_t>(stream));
 }
 
 sqa_status sqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
@@ -188,7 +215,7 @@ sqa_status sqa_attn_fwd_varlen_split(const void* q, const void* k, const void* v
   if (s != SQA_OK) return s;
   if (max_seqlen > T) return fail(SQA_ERR_SHAPE, "max_seqlen=%lld exceeds T=%lld", (long long)max_seqlen,
                                   (long long)T);
-  if (T * H_q * d > kMaxElems) return fail(SQA_ERR_SHAPE, "tensor too large");
+  if (!prod_le({T, H_q, d}, kMaxElems)) return fail(SQA_ERR_SHAPE, "tensor too large");
   if (B > 0x7fffffffLL) return fail(SQA_ERR_SHAPE, "too many sequences");
   if (B == 0 || T == 0 || max_seqlen == 0) return SQA_OK;
   if (!q || !k || !v || !o || !cu_seqlens) return fail(SQA_ERR_NULL, "q, k, v, o and cu_seqlens must be non-NULL");
@@ -214,16 +241,14 @@ sqa_status sqa_attn_fwd_varlen_split(const void* q, const void* k, const void* v
   sqa::AttnProblem p{q, k, v, o, lse, B, H_q, H_kv, max_seqlen, d, scale, causal, cu_seqlens, T};
   p.nsplit = (int)num_splits;
   p.split_ws = num_splits > 1 ? static_cast<float*>(workspace) : nullptr;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = (dtype == SQA_BF16) ? sqa::launch_attn_fwd_bf16(p, st) : sqa::launch_attn_fwd_f32(p, st);
-  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-  return SQA_OK;
+  return launch_attn(p, dtype, static_cast<hipStream_t>(stream));
 }
 
 int64_t sqa_attn_fwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
                                 int causal, int64_t T) {
   if (B <= 0 || N <= 0 || H_q < 1 || H_kv < 1 || H_kv > H_q || H_q > 4096 || N > kMaxN || T < 0) return 1;
   if (T > 0 && N > T) return 1;
+  if (!prod_le({B, H_q, N, d > 0 ? d : 1}, kMaxElems) || !prod_le({T, H_q, d > 0 ? d : 1}, kMaxElems)) return 1;
   // d = 128: the packed 32k batch ran 903 TFLOP/s unsplit, 848 / 821 with 2 / 3
   // ranges (its 32-row waves already give the longest sequence 1156
   // workgroups); d = 16/32: slower under a causal mask. Splits there run on
@@ -240,7 +265,7 @@ size_t sqa_attn_fwd_split_workspace_bytes(int64_t rows, int64_t d, int dtype, in
 
 size_t sqa_attn_bwd_workspace_bytes(int64_t B, int64_t H_q, int64_t N, int64_t d, int dtype) {
   if (B <= 0 || H_q <= 0 || N <= 0 || (d != 64 && d != 128) || dtype != SQA_BF16) return 0;
-  if (N > kMaxN || B * H_q * N * d > kMaxElems) return 0;
+  if (N > kMaxN || !prod_le({B, H_q, N, d}, kMaxElems)) return 0;
   return round256(sqa::attn_bwd_rowterm_bytes(B, H_q, N));
 }
 
@@ -255,6 +280,16 @@ sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void*
 }  // extern "C"
 
 namespace {
+
+// Dry-run the backward's launches, then launch them.
+sqa_status run_bwd(sqa::BwdProblem p, hipStream_t st) {
+  p.dry_run = true;
+  if (sqa::launch_attn_bwd_bf16(p, st) != hipSuccess) return limit_fail("backward");
+  p.dry_run = false;
+  const hipError_t e = sqa::launch_attn_bwd_bf16(p, st);
+  if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
+  return SQA_OK;
+}
 
 // Every argument rule of the dense backward except the workspace's; `need`
 // receives the workspace bytes num_splits needs (0 for an empty problem,
@@ -302,9 +337,7 @@ sqa_status launch_bwd(const void* q, const void* k, const void* v, const void* o
   p.split_ws = num_splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                          sqa_attn_bwd_workspace_bytes(B, H_q, N, d, dtype))
                               : nullptr;
-  hipError_t e = sqa::launch_attn_bwd_bf16(p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
-  return SQA_OK;
+  return run_bwd(p, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -355,7 +388,7 @@ sqa_status sqa_attn_bwd_noalloc(const void* q, const void* k, const void* v, con
 
 size_t sqa_attn_bwd_varlen_workspace_bytes(int64_t B, int64_t H_q, int64_t T, int64_t d, int dtype) {
   if (B <= 0 || H_q <= 0 || T <= 0 || (d != 64 && d != 128) || dtype != SQA_BF16) return 0;
-  if (T > kMaxN || T * H_q * d > kMaxElems) return 0;
+  if (T > kMaxN || !prod_le({T, H_q, d}, kMaxElems)) return 0;
   return round256(sqa::attn_bwd_rowterm_bytes_packed(H_q, T));
 }
 
@@ -377,6 +410,7 @@ int64_t sqa_attn_bwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N,
                                 int causal, int64_t T) {
   if (B <= 0 || N <= 0 || H_q < 1 || H_kv < 1 || H_kv > H_q || H_q > 4096 || N > kMaxN || T < 0) return 1;
   if (T > 0 && N > T) return 1;
+  if (!prod_le({B, H_q, N, d > 0 ? d : 1}, kMaxElems) || !prod_le({T, H_q, d > 0 ? d : 1}, kMaxElems)) return 1;
   if ((d != 64 && d != 128) || dtype != SQA_BF16) return 1;
   return sqa::attn_bwd_auto_splits(B, H_q, H_kv, N, T, d, causal != 0, device_cus());
 }
@@ -404,7 +438,7 @@ sqa_status sqa_attn_bwd_varlen_split(const void* q, const void* k, const void* v
                 (long long)d);
   if (max_seqlen > T) return fail(SQA_ERR_SHAPE, "max_seqlen=%lld exceeds T=%lld", (long long)max_seqlen,
                                   (long long)T);
-  if (T > kMaxN || T * H_q * d > kMaxElems) return fail(SQA_ERR_SHAPE, "tensor too large");
+  if (T > kMaxN || !prod_le({T, H_q, d}, kMaxElems)) return fail(SQA_ERR_SHAPE, "tensor too large");
   if (B > 0x7fffffffLL) return fail(SQA_ERR_SHAPE, "too many sequences");
   s = check_bwd_splits(num_splits, causal);
   if (s != SQA_OK) return s;
@@ -440,9 +474,7 @@ sqa_status sqa_attn_bwd_varlen_split(const void* q, const void* k, const void* v
   p.split_ws = num_splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                          sqa_attn_bwd_varlen_workspace_bytes(B, H_q, T, d, dtype))
                               : nullptr;
-  hipError_t e = sqa::launch_attn_bwd_bf16(p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
-  return SQA_OK;
+  return run_bwd(p, static_cast<hipStream_t>(stream));
 }
 
 size_t sqa_layer_workspace_bytes(int64_t B, int64_t N, int64_t D, int64_t H, int64_t H_q, int64_t H_kv,
@@ -450,7 +482,7 @@ size_t sqa_layer_workspace_bytes(int64_t B, int64_t N, int64_t D, int64_t H, int
   if (B <= 0 || N <= 0 || D <= 0 || H <= 0 || H_q <= 0 || H_kv <= 0) return 0;
   if (dtype != SQA_BF16 || D % H != 0) return 0;
   const int64_t d = D / H;
-  if (B * N * (H_q > H_kv ? H_q : H_kv) * d > kMaxElems) return 0;
+  if (!prod_le({B, N, H_q > H_kv ? H_q : H_kv, d}, kMaxElems)) return 0;
   const size_t esz = 2;
   const size_t nq = (size_t)(B * H_q * N * d) * esz, nkv = (size_t)(B * H_kv * N * d) * esz;
   return 2 * round256(nq) + 2 * round256(nkv);
@@ -473,7 +505,7 @@ sqa_status check_layer(int64_t B, int64_t N, int64_t D, int64_t H, int64_t H_q, 
   if (s != SQA_OK) return s;
   if (!std::isfinite(rope_base) || rope_base <= 0.f) return fail(SQA_ERR_ARG, "rope_base must be finite and > 0");
   if (D % 16 != 0) return fail(SQA_ERR_UNSUPPORTED, "D must be a multiple of 16");
-  if (B * N * D > kMaxElems) return fail(SQA_ERR_SHAPE, "tensor too large");
+  if (!prod_le({B, N, D}, kMaxElems)) return fail(SQA_ERR_SHAPE, "tensor too large");
   *d_out = d;
   return SQA_OK;
 }
@@ -489,12 +521,17 @@ sqa_status run_layer(const void* x, const void* w_q, const void* w_k, const void
   void* vb = ws + nq + nkv;
   void* ob = ws + nq + 2 * nkv;
   sqa::QkvProblem qp{x, w_q, w_k, w_v, qb, kb, vb, B, N, D, H_q, H_kv, d, rope_base};
+  sqa::AttnProblem ap{qb, kb, vb, ob, nullptr, B, H_q, H_kv, N, d, scale, causal};
+  sqa::OprojProblem op{ob, w_o, y, B, N, D, H_q, d, resid};
+  qp.dry_run = ap.dry_run = op.dry_run = true;
+  if (sqa::launch_qkv_rope(qp, st) != hipSuccess) return limit_fail("qkv projection");
+  if (sqa::launch_attn_fwd_bf16(ap, st) != hipSuccess) return limit_fail("attention");
+  if (sqa::launch_out_proj(op, st) != hipSuccess) return limit_fail("output projection");
+  qp.dry_run = ap.dry_run = op.dry_run = false;
   hipError_t e = sqa::launch_qkv_rope(qp, st);
   if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
-  sqa::AttnProblem ap{qb, kb, vb, ob, nullptr, B, H_q, H_kv, N, d, scale, causal};
   e = sqa::launch_attn_fwd_bf16(ap, st);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-  sqa::OprojProblem op{ob, w_o, y, B, N, D, H_q, d, resid};
   e = sqa::launch_out_proj(op, st);
   if (e != hipSuccess) return hip_fail(e, "output projection launch");
   return SQA_OK;
@@ -535,7 +572,7 @@ sqa_status sqa_layer_fwd(const void* x, const void* w_q, const void* w_k, const 
 size_t sqa_block_workspace_bytes(int64_t B, int64_t N, int64_t D, int64_t H, int64_t H_q, int64_t H_kv,
                                  int64_t F, int dtype) {
   const size_t lw = sqa_layer_workspace_bytes(B, N, D, H, H_q, H_kv, dtype);
-  if (lw == 0 || F <= 0 || B * N * F > kMaxElems) return 0;
+  if (lw == 0 || F <= 0 || !prod_le({B, N, F}, kMaxElems)) return 0;
   return lw + 2 * round256((size_t)(B * N * D) * 2) + round256((size_t)(B * N * F) * 2);
 }
 
@@ -552,7 +589,7 @@ sqa_status sqa_block_fwd(const void* x, const void* norm1, const void* w_q, cons
                                         (long long)F);
   if (!std::isfinite(eps) || eps < 0.f) return fail(SQA_ERR_ARG, "eps must be finite and >= 0");
   if (B == 0 || N == 0) return SQA_OK;
-  if (B * N * F > kMaxElems) return fail(SQA_ERR_SHAPE, "tensor too large");
+  if (!prod_le({B, N, F}, kMaxElems)) return fail(SQA_ERR_SHAPE, "tensor too large");
   const void* ins[10] = {x, norm1, w_q, w_k, w_v, w_o, norm2, w_gate, w_up, w_down};
   for (const void* p : ins)
     if (!p) return fail(SQA_ERR_NULL, "inputs must be non-NULL");
@@ -581,16 +618,32 @@ sqa_status sqa_block_fwd(const void* x, const void* norm1, const void* w_q, cons
   void* gb = ws + lw + 2 * round256(nx);         // SwiGLU activations [M, F]
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t M = B * N;
+  sqa::GateUpProblem gp{xn, w_gate, w_up, gb, M, D, F};
+  sqa::DenseProblem dp{gb, w_down, hb, y, M, F, D};
+  gp.dry_run = dp.dry_run = true;
+  if (sqa::launch_rms_norm(x, norm1, xn, M, D, eps, st, true) != hipSuccess) return limit_fail("RMSNorm");
+  if (sqa::launch_gate_up(gp, st) != hipSuccess) return limit_fail("SwiGLU gate/up projection");
+  if (sqa::launch_dense_residual(dp, st) != hipSuccess) return limit_fail("down projection");
+  {
+    // the layer's own launches, dry (run_layer repeats this before launching)
+    const size_t nq = round256((size_t)(B * H_q * N * d) * 2), nkv = round256((size_t)(B * H_kv * N * d) * 2);
+    sqa::QkvProblem qp{xn, w_q, w_k, w_v, ws, ws + nq, ws + nq + nkv, B, N, D, H_q, H_kv, d, rope_base};
+    sqa::AttnProblem ap{ws, ws + nq, ws + nq + nkv, ws + nq + 2 * nkv, nullptr, B, H_q, H_kv, N, d, scale, causal};
+    sqa::OprojProblem op{ws + nq + 2 * nkv, w_o, hb, B, N, D, H_q, d, x};
+    qp.dry_run = ap.dry_run = op.dry_run = true;
+    if (sqa::launch_qkv_rope(qp, st) != hipSuccess) return limit_fail("qkv projection");
+    if (sqa::launch_attn_fwd_bf16(ap, st) != hipSuccess) return limit_fail("attention");
+    if (sqa::launch_out_proj(op, st) != hipSuccess) return limit_fail("output projection");
+  }
+  gp.dry_run = dp.dry_run = false;
   hipError_t e = sqa::launch_rms_norm(x, norm1, xn, M, D, eps, st);
   if (e != hipSuccess) return hip_fail(e, "RMSNorm launch");
   s = run_layer(xn, w_q, w_k, w_v, w_o, x, hb, B, N, D, d, H_q, H_kv, rope_base, scale, causal, ws, st);
   if (s != SQA_OK) return s;
   e = sqa::launch_rms_norm(hb, norm2, xn, M, D, eps, st);
   if (e != hipSuccess) return hip_fail(e, "RMSNorm launch");
-  sqa::GateUpProblem gp{xn, w_gate, w_up, gb, M, D, F};
   e = sqa::launch_gate_up(gp, st);
   if (e != hipSuccess) return hip_fail(e, "SwiGLU gate/up launch");
-  sqa::DenseProblem dp{gb, w_down, hb, y, M, F, D};
   e = sqa::launch_dense_residual(dp, st);
   if (e != hipSuccess) return hip_fail(e, "down projection launch");
   return SQA_OK;

@@ -427,3 +427,56 @@ def _block(lib, x=FAKE, ws=FAKE + 0x4000000, ws_bytes=1 << 27, B=16, N=1024, D=2
 @cpu_only
 def test_block_rejects_invalid_arguments(lib, kw, code):
     assert _block(lib, **kw) == code
+
+
+# ------------------------------------------------------ launch limits -> SHAPE
+SPACING = 1 << 40  # fake tensors this far apart never overlap, whatever their size
+
+
+def _spaced(n):
+    return [FAKE + i * SPACING for i in range(n)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,dtype", [
+    (1, 8, 4, 1 << 24, 64, 1),      # d = 64: N * 128 B reaches 2^31 (buffer descriptor range)
+    (1, 8, 4, 1 << 23, 128, 1),     # d = 128: N * 256 B reaches 2^31
+    (1 << 31, 1, 1, 1, 16, 1),      # B * H_kv reaches 2^31 (grid)
+    (1 << 31, 1, 1, 1, 32, 1),
+    (1 << 31, 2, 1, 1, 64, 1),
+    (1 << 31, 1, 1, 1, 16, 0),      # fp32: workgroup count reaches 2^31
+])
+@cpu_only
+def test_attn_launch_limits_are_shape_errors(lib, B, Hq, Hkv, N, d, dtype):
+    q, k, v, o = _spaced(4)
+    st = lib.sqa_attn_fwd(q, k, v, o, B, Hq, Hkv, N, d, dtype, 0.125, 0, None, None)
+    msg = lib.sqa_last_error().decode()
+    assert st == 2, (st, msg)
+    assert "launch limit" in msg
+
+
+@cpu_only
+def test_varlen_launch_limit_is_a_shape_error(lib):
+    q, k, v, o, cu = _spaced(5)
+    st = lib.sqa_attn_fwd_varlen(q, k, v, o, cu, 1, 8, 4, 1 << 24, 1 << 24, 64, 1, 0.125, 0, None, None)
+    assert st == 2 and "launch limit" in lib.sqa_last_error().decode()
+
+
+@pytest.mark.parametrize("N,d", [(1 << 24, 64), (1 << 23, 128)])
+@cpu_only
+def test_bwd_launch_limits_are_shape_errors(lib, N, d):
+    q, k, v, o, do, lse, dq, dk, dv, ws = _spaced(10)
+    st = lib.sqa_attn_bwd(q, k, v, o, do, lse, dq, dk, dv, 1, 8, 4, N, d, 1, 0.125, 0, ws, 1 << 36, None)
+    assert st == 2 and "launch limit" in lib.sqa_last_error().decode()
+    st = lib.sqa_attn_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, 1, 1, 1, N, d, 1, 0.125, 0, None)
+    # one query head: its row terms (N * 8 B, 64 or 128 MiB) exceed the
+    # no-alloc buffer's 32 MiB, which is checked before the dry run
+    assert st == 5
+
+
+@cpu_only
+def test_layer_launch_limit_is_a_shape_error(lib):
+    # X [1, 2^22, 256] bf16 is 2^31 bytes: past the projections' 32-bit offsets
+    x, wq, wk, wv, wo, y, ws = _spaced(7)
+    st = lib.sqa_layer_fwd(x, wq, wk, wv, wo, y, 1, 1 << 22, 256, 16, 8, 4, 10000.0, 0.25, 1, 1, ws, 1 << 36,
+                           None)
+    assert st == 2 and "launch limit" in lib.sqa_last_error().decode()
