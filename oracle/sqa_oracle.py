@@ -224,12 +224,16 @@ def attention_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens: Se
 
 
 def _attend_rows_bwd(q_rows: np.ndarray, t_rows: np.ndarray, kj: np.ndarray, vj: np.ndarray,
-                     do_rows: np.ndarray, scale: float, causal: bool):
+                     do_rows: np.ndarray, scale: float, causal: bool, absolute: bool = False,
+                     o_rows: Optional[np.ndarray] = None):
     """Gradients of one block of query rows against one K/V head (fp64).
 
     Returns dQ [R, d] for these rows and their contributions dK_part, dV_part
     [N, d] to the head's key and value gradients. The softmax is recomputed
-    exactly (two passes); nothing saved by a forward is used.
+    exactly (two passes). With ``o_rows`` (the forward output of these rows)
+    D_t = sum_c dO_tc O_tc; otherwise D_t = sum_u P_tu dP_tu, the same value
+    for the exact output. With ``absolute`` the same three sums are formed
+    from the absolute values of their terms instead (see ``attention_bwd``).
     """
     s = (q_rows @ kj.T) * scale                       # [R, N]
     if causal:
@@ -239,7 +243,11 @@ def _attend_rows_bwd(q_rows: np.ndarray, t_rows: np.ndarray, kj: np.ndarray, vj:
     e = np.exp(s - m)
     p = e / e.sum(axis=1, keepdims=True)              # masked entries are exactly 0
     dp = do_rows @ vj.T                               # dL/dP        [R, N]
-    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))   # dL/dS (softmax Jacobian)
+    D = (p * dp).sum(axis=1, keepdims=True) if o_rows is None else (do_rows * o_rows).sum(axis=1, keepdims=True)
+    ds = p * (dp - D)                                 # dL/dS (softmax Jacobian)
+    if absolute:
+        ads = np.abs(ds)
+        return ((ads @ np.abs(kj)) * abs(scale), (ads.T @ np.abs(q_rows)) * abs(scale), p.T @ np.abs(do_rows))
     dq = (ds @ kj) * scale
     dk_part = (ds.T @ q_rows) * scale
     dv_part = p.T @ do_rows
@@ -249,8 +257,21 @@ def _attend_rows_bwd(q_rows: np.ndarray, t_rows: np.ndarray, kj: np.ndarray, vj:
 def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
                   scale: Optional[float] = None, causal: bool = False,
                   rows: Optional[Sequence[int]] = None, threads: int = 1,
-                  chunk_elems: int = 1 << 22):
+                  chunk_elems: int = 1 << 22, absolute: bool = False, o: Optional[np.ndarray] = None):
     """Backward of ``attention`` in float64: returns (dQ, dK, dV).
+
+    ``o`` (optional, shaped like dout): a forward output to take
+    D_t = sum_c dout_tc o_tc from, as the library's backward does (it takes
+    the forward's output as an input); without it D_t = sum_u P_tu dP_tu,
+    which is the same for the exact output.
+
+    ``absolute=True`` returns instead the same sums with every term replaced
+    by its absolute value: |scale| sum_u |dS_tu| |K_u|,
+    |scale| sum_{i,t} |dS_tu| |Q_t| and sum_{i,t} P_tu |dO_t|. These are the
+    magnitudes that set the rounding error of any computation of the
+    gradients (for a sum of products, |fl(sum) - sum| is bounded by a
+    multiple of the sum of the products' absolute values); dS sums to zero
+    along each row, so |dQ| itself can be far smaller.
 
     dout is the upstream gradient dL/dO, shaped like O [B, H_q, N, d]. dK and
     dV [B, H_kv, N, d] sum the contributions of every query head of a K/V
@@ -309,7 +330,8 @@ def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
         for (i, r0, r1) in part:
             t_rows = t_all[r0:r1]
             gq, gk, gv = _attend_rows_bwd(q[b, i, t_rows].astype(np.float64), t_rows, kj, vj,
-                                          dout[b, i, t_rows].astype(np.float64), scale, causal)
+                                          dout[b, i, t_rows].astype(np.float64), scale, causal, absolute,
+                                          None if o is None else np.asarray(o)[b, i, t_rows].astype(np.float64))
             dq[b, i, r0:r1] = gq
             if want_kv:
                 dk_acc += gk

@@ -6,8 +6,19 @@ Acceptance (stated tolerance, per workload and variant):
   * bf16 inputs:  max |O - O_ref| <= 1e-2 * max |O_ref| over every checked
     element (all heads, all checked rows).
   * per-row gate (stricter in effect where rows differ in magnitude): for the
-    rows it is applied to, max_c |O - O_ref| <= 1e-2 * max_c |O_ref| + 2^-14
-    (the last term is the bf16 resolution floor near zero outputs).
+    rows it is applied to, max_c |O - O_ref| <= max(1e-2 * max_c |O_ref|, 2^-14)
+    (2^-14 is the bf16 resolution floor, which only takes over for rows whose
+    outputs all but vanish).
+  * per-row gate for gradients: a gradient row is a sum of products whose
+    terms cancel (each row of dS sums to zero), so its bar is set by the
+    sum of the terms' absolute values, the scale of the rounding error any
+    computation of it makes: max_c |g - g_ref| <= max(1e-2 * max_c A, 2^-14)
+    with A the oracle's absolute-term sums (attention_bwd(absolute=True)).
+    The kernels round dS and P to bf16 (relative error at most 2^-8 per
+    term), so their error stays below 2^-8 * A ~ 3.9e-3 * A.
+  * LSE of bf16 inputs: |LSE - LSE_ref| <= 5e-3. The kernels sum the
+    probabilities after rounding them to bf16 (relative error at most 2^-8
+    each), so |LSE - LSE_ref| <= ln(1 + 2^-8) ~ 3.9e-3 plus fp32 rounding.
 """
 from __future__ import annotations
 
@@ -19,6 +30,7 @@ import numpy as np
 FP32_TOL = 1e-4
 BF16_REL = 1e-2
 ROW_FLOOR = 2.0 ** -14
+LSE_BF16 = 5e-3
 
 
 def oracle_threads() -> int:
@@ -60,9 +72,19 @@ def check_global(got: np.ndarray, ref: np.ndarray, dtype: str, label: str = "", 
 
 
 def check_rows(got: np.ndarray, ref: np.ndarray, label: str = ""):
-    """Per-row gate; got/ref [..., R, d]."""
+    """Per-row gate; got/ref [..., R, d] (a row is the last axis)."""
     err = np.max(np.abs(got - ref), axis=-1)
-    lim = BF16_REL * np.max(np.abs(ref), axis=-1) + ROW_FLOOR
+    lim = np.maximum(BF16_REL * np.max(np.abs(ref), axis=-1), ROW_FLOOR)
+    worst = float(np.max(err / lim)) if err.size else 0.0
+    log(f"[parity] {label} per-row worst err/limit={worst:.3f}")
+    assert np.all(err <= lim), f"{label}: per-row gate failed (worst ratio {worst:.3f})"
+
+
+def check_rows_scaled(got: np.ndarray, ref: np.ndarray, mag: np.ndarray, label: str = ""):
+    """Per-row gate against a per-row magnitude: got/ref/mag [..., R, d];
+    limit max(1e-2 * max_c mag, 2^-14) per row."""
+    err = np.max(np.abs(got - ref), axis=-1)
+    lim = np.maximum(BF16_REL * np.max(mag, axis=-1), ROW_FLOOR)
     worst = float(np.max(err / lim)) if err.size else 0.0
     log(f"[parity] {label} per-row worst err/limit={worst:.3f}")
     assert np.all(err <= lim), f"{label}: per-row gate failed (worst ratio {worst:.3f})"

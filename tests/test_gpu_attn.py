@@ -12,7 +12,7 @@ import pytest
 
 from oracle import attention as oracle_attention
 from synth import WORKLOADS, boundary_rows, draw_attn_case, draw_qkv, sample_rows, select_variant
-from tests.parity import (check_global, check_rows, log, oracle_threads, to_dev, to_host)
+from tests.parity import (LSE_BF16, check_global, check_rows, log, oracle_threads, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,9 @@ def _run(q, k, v, dtype, scale, causal, return_lse=False):
 
 
 # --------------------------------------------------------- small, all rows
-SMALL_N = [1, 2, 15, 17, 63, 64, 65, 127, 129, 200, 1000]
+# 161 and 192 keys are six 32-key tiles: exactly one turn of the d = 64
+# kernel's six-slot ring, where no tile is issued at the pair barrier
+SMALL_N = [1, 2, 15, 17, 63, 64, 65, 127, 129, 161, 192, 200, 1000]
 SMALL_HEADS = [(1, 1), (2, 1), (8, 4), (4, 1), (16, 1), (3, 3), (6, 2)]
 
 
@@ -119,7 +121,7 @@ def _long_case(name, Hq, Hkv, causal):
     check_rows(got_b, ref_b, label + " boundary rows")
     lse_err = float(np.max(np.abs(got_lse - ref_lse)))
     log(f"[parity] {label} lse max_err={lse_err:.3e}")
-    assert lse_err <= 2e-2
+    assert lse_err <= LSE_BF16
 
 
 @pytest.mark.parametrize("Hq,Hkv", WORKLOADS["long32k_bf16"].variants)
@@ -243,7 +245,7 @@ def test_lse_bf16_matches_oracle():
         _, ref = oracle_attention(q, k, v, scale=0.125, causal=bool(causal), return_lse=True)
         err = float(np.max(np.abs(lse.cpu().numpy() - ref)))
         log(f"[parity] lse bf16 causal={causal} err={err:.3e}")
-        assert err <= 2e-2
+        assert err <= LSE_BF16
 
 
 # ------------------------------------------------------------- error paths

@@ -14,9 +14,10 @@ import math
 import numpy as np
 import pytest
 
+from oracle import attention as oracle_attention
 from oracle import attention_bwd as oracle_bwd
-from synth import WORKLOADS, draw_attn_case, draw_qkv, draw_upstream, select_variant
-from tests.parity import ROW_FLOOR, check_global, log, oracle_threads, to_dev, to_host
+from synth import WORKLOADS, bf16_round, draw_attn_case, draw_qkv, draw_upstream, select_variant
+from tests.parity import ROW_FLOOR, check_global, check_rows_scaled, log, oracle_threads, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +47,30 @@ def _check(got, ref, label):
     # (N = 1: dS = P (dP - D) = 0, computed as a difference of fp32 sums)
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
         check_global(g, r, "bf16", f"{label} {name}", floor=ROW_FLOOR)
+
+
+def _check_rows_given_forward(q, k, v, do, scale, causal, label):
+    """The backward alone, per row. Its inputs o and lse come from the
+    oracle's forward (o rounded to bf16, lse to fp32), and the oracle's
+    backward takes D_t = sum_c dout_tc o_tc from that same o, as the
+    library's backward is defined to. Every query row of dq and every key row
+    of dk and dv is then held to its own magnitude (its absolute-term sums,
+    tests/parity.py), so that an error confined to rows much smaller than
+    the tensor's largest (early query rows and late keys under a causal mask,
+    ordinary keys next to peaky ones) cannot hide under the global bar."""
+    th = oracle_threads()
+    o_ref, lse_ref = oracle_attention(q, k, v, scale=scale, causal=bool(causal), threads=th, return_lse=True)
+    o_in = bf16_round(o_ref.astype(np.float32))
+    tq, tk, tv, to, tdo = (to_dev(a, "bf16") for a in (q, k, v, o_in, do))
+    tl = torch.from_numpy(lse_ref.astype(np.float32)).to("cuda")
+    grads = sqa.sqa_attn_bwd(tq, tk, tv, to, tdo, tl, scale=scale, causal=bool(causal))
+    torch.cuda.synchronize()
+    got = [to_host(g) for g in grads]
+    ref = oracle_bwd(q, k, v, do, scale=scale, causal=bool(causal), threads=th, o=o_in)
+    mags = oracle_bwd(q, k, v, do, scale=scale, causal=bool(causal), threads=th, o=o_in, absolute=True)
+    for name, g, r, m in zip(("dq", "dk", "dv"), got, ref, mags):
+        check_global(g, r, "bf16", f"{label} {name}", floor=ROW_FLOOR)
+        check_rows_scaled(g, r, m, f"{label} {name}")
 
 
 # --------------------------------------------------------- small, all elements
@@ -115,6 +140,37 @@ def test_bwd_long32k_sqa(causal):
     log(f"[oracle] {label} (fp64 backward, all rows)")
     ref = oracle_bwd(q, k, v, do, scale=w.scale, causal=bool(causal), threads=oracle_threads())
     _check(got, ref, label)
+
+
+# ------------------------------------- per-row gates, forward outputs given
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("N,Hq,Hkv,d", [(4096, 8, 4, 64), (3000, 4, 4, 64), (2113, 8, 2, 128), (777, 6, 4, 64)])
+def test_bwd_rows_given_forward(N, Hq, Hkv, d, causal):
+    label = f"bwd rows Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}"
+    log(f"[case] {label}")
+    q, k, v = draw_attn_case(1, Hq, Hkv, N, d, "bf16", seed=N + 3)
+    do = draw_upstream(q.shape, "bf16", seed=N + 4)
+    _check_rows_given_forward(q, k, v, do, 1.0 / math.sqrt(d), causal, label)
+
+
+def test_bwd_rows_given_forward_peaky():
+    label = "bwd rows peaky N=4096 (4,4)"
+    log(f"[case] {label}")
+    qa, ka, va = draw_qkv(1, 16, 4096, 64, "bf16", seed=0, peaky=True)
+    q, k, v = select_variant(qa, ka, va, 4, 4)
+    do = draw_upstream(q.shape, "bf16", seed=12)
+    _check_rows_given_forward(q, k, v, do, 0.125, 0, label)
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_bwd_rows_given_forward_long32k(causal):
+    w = WORKLOADS["long32k_bf16"]
+    label = f"bwd rows {w.name} (8,4) causal={causal}"
+    log(f"[case] {label}")
+    qa, ka, va = draw_qkv(w.B, w.H, w.N, w.d, "bf16", seed=0)
+    q, k, v = select_variant(qa, ka, va, 8, 4)
+    do = draw_upstream(q.shape, "bf16", seed=55)
+    _check_rows_given_forward(q, k, v, do, w.scale, causal, label)
 
 
 # ------------------------------------------------------ closed forms on device

@@ -156,7 +156,7 @@ def test_bwd_linear_in_upstream_and_rows_and_threads():
 
 # ------------------------------------------------------- planted mistakes
 def _mutant(kind):
-    def f(q_rows, t_rows, kj, vj, do_rows, scale, causal):
+    def f(q_rows, t_rows, kj, vj, do_rows, scale, causal, absolute=False, o_rows=None):
         s = (q_rows @ kj.T) * scale
         if causal:
             u = np.arange(kj.shape[0])
@@ -185,3 +185,79 @@ def test_finite_differences_catch_planted_mistakes(kind, monkeypatch):
     monkeypatch.setattr(so, "_attend_rows_bwd", _mutant(kind))
     with pytest.raises(AssertionError):
         _check_against_fd(q, k, v, g, 0.7, True)
+
+
+# ---------------------------------------- absolute-term magnitudes (tolerances)
+def _abs_terms_brute(q, k, v, g, scale, causal):
+    """sum |dS_tu| |K_uc| etc. by explicit loops over every term (tiny N)."""
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    aq = np.zeros(q.shape)
+    ak = np.zeros(k.shape)
+    av = np.zeros(v.shape)
+    for b in range(B):
+        for i in range(Hq):
+            j = (i * Hkv) // Hq
+            for t in range(N):
+                us = [u for u in range(N) if (not causal or u <= t)]
+                s = [scale * sum(float(q[b, i, t, c]) * float(k[b, j, u, c]) for c in range(d)) for u in us]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                z = math.fsum(e)
+                p = [x / z for x in e]
+                dp = [sum(float(g[b, i, t, c]) * float(v[b, j, u, c]) for c in range(d)) for u in us]
+                D = math.fsum(pp * x for pp, x in zip(p, dp))
+                for n, u in enumerate(us):
+                    ds = p[n] * (dp[n] - D)
+                    for c in range(d):
+                        aq[b, i, t, c] += abs(scale) * abs(ds) * abs(float(k[b, j, u, c]))
+                        ak[b, j, u, c] += abs(scale) * abs(ds) * abs(float(q[b, i, t, c]))
+                        av[b, j, u, c] += p[n] * abs(float(g[b, i, t, c]))
+    return aq, ak, av
+
+
+@pytest.mark.parametrize("H_q,H_kv", [(2, 2), (4, 2), (3, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_absolute_terms_match_brute_force(H_q, H_kv, causal):
+    q, k, v = draw_attn_case(2, H_q, H_kv, 6, 4, "f32", seed=31)
+    g = np.random.default_rng(32).standard_normal(q.shape)
+    got = attention_bwd(q, k, v, g, scale=-0.6, causal=causal, absolute=True)
+    ref = _abs_terms_brute(q, k, v, g, -0.6, causal)
+    for a, r in zip(got, ref):
+        assert np.max(np.abs(a - r)) <= 1e-12 * max(1.0, np.max(np.abs(r)))
+
+
+def test_bwd_absolute_terms_bound_the_gradients():
+    q, k, v = draw_attn_case(1, 8, 4, 200, 16, "f32", seed=33)
+    g = np.random.default_rng(34).standard_normal(q.shape)
+    for causal in (False, True):
+        grads = attention_bwd(q, k, v, g, scale=0.25, causal=causal)
+        mags = attention_bwd(q, k, v, g, scale=0.25, causal=causal, absolute=True)
+        for gr, mg in zip(grads, mags):
+            assert np.all(np.abs(gr) <= mg * (1 + 1e-12) + 1e-15)
+        # a non-negative upstream gradient makes every dV term non-negative
+        gp = np.abs(g)
+        dv = attention_bwd(q, k, v, gp, scale=0.25, causal=causal)[2]
+        dv_abs = attention_bwd(q, k, v, gp, scale=0.25, causal=causal, absolute=True)[2]
+        assert np.allclose(dv, dv_abs, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_given_exact_forward_output_is_the_gradient(causal):
+    """D from a given forward output equals D = rowsum(P * dP) when that
+    output is the exact one; a perturbed output moves every dQ row along
+    scale * sum_u P_tu K_u by exactly -delta(D_t) (dS gains -P delta(D))."""
+    q, k, v = draw_attn_case(1, 4, 2, 40, 8, "f32", seed=41)
+    g = np.random.default_rng(42).standard_normal(q.shape)
+    o = attention(q, k, v, scale=0.3, causal=causal)
+    a = attention_bwd(q, k, v, g, scale=0.3, causal=causal)
+    b = attention_bwd(q, k, v, g, scale=0.3, causal=causal, o=o)
+    for x, y in zip(a, b):
+        assert np.max(np.abs(x - y)) <= 1e-12 * max(1.0, np.max(np.abs(x)))
+    delta = np.random.default_rng(43).standard_normal(o.shape) * 1e-3
+    c = attention_bwd(q, k, v, g, scale=0.3, causal=causal, o=o + delta)
+    dD = (g * delta).sum(-1)                                   # [B, H, N]
+    kr = np.repeat(k, 2, axis=1)                               # K of each query head's group
+    pk = attention(q, kr, kr, scale=0.3, causal=causal)        # sum_u P_tu K_u per row
+    expect = a[0] - 0.3 * dD[..., None] * pk
+    assert np.max(np.abs(c[0] - expect)) <= 1e-10
