@@ -3,15 +3,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--variant HQ,HKV] [--causal 0|1] [--no-cpu-baseline]
-                    [--no-compare]
+                    [--no-compare] [--no-backward] [--no-configs]
 
 A step is one sqa_attn_fwd call over the whole workload (default: B=1,
 N=32768, d=64, SQA H_q=8 / H_kv=4, bf16, encoder-style), with inputs already
 resident in HBM. FLOPs are counted as 4*B*N^2*H_q*d, halved for causal.
+Warm-up is at least W calls and at least 0.5 s of GPU time; the K timed calls
+are bracketed by device synchronisations, with a HIP event between
+consecutive calls on the launch stream, so the line carries the mean (the
+headline, = total / K), the median and the minimum of the per-call times.
+While the timed calls run, a thread samples the GPU's graphics clock
+(amdsmi GPU metrics), and the roofline is also stated against the peak at
+that measured clock (256 CUs x 4096 bf16 FLOP per clock).
 Prints ONE JSON line. The line also carries:
   * roofline: the attention kernel's achieved TFLOP/s against the MI355X
-    dense bf16 MFMA peak (2516.6 TFLOP/s = 256 CU x 4096 FLOP/clk x 2.4 GHz),
-    timed with HIP events on the stream the kernel runs on;
+    dense bf16 MFMA peak (2516.6 TFLOP/s = 256 CU x 4096 FLOP/clk x 2.4 GHz);
   * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
     sample of the same workload (sampled query rows, every head);
   * comparison: MHA / GQA-4 / MQA at the same shape (H_q = 16) and the
@@ -20,7 +26,14 @@ Prints ONE JSON line. The line also carries:
     forward's o and lse, a seeded N(0,1) upstream gradient), with FLOPs
     counted as 2.5x the forward's (the five matrix products of the textbook
     backward) and, separately, the FLOPs the kernels execute (3.5x: the dK/dV
-    and dQ kernels both recompute S and dP).
+    and dQ kernels both recompute S and dP);
+  * configs: every workload the target names, each variant timed the same
+    way (median and minimum over its calls, TFLOP/s, tokens/s, fraction of
+    the nominal and of the clock-adjusted peak, speedup over the (16,16)
+    baseline of the same shape next to H/H_q): the SQAT-m attention core
+    (fp32, N=1024), the SQAT-m layer (B=16, N=1024), 32k (8,4) / MHA /
+    GQA-4 / MQA, 131k (8,8) / (4,4) / (16,16) under both masks, and 200k
+    (4,4) / (16,16) with 1 % of the keys scaled by 8.
 """
 from __future__ import annotations
 
@@ -98,22 +111,132 @@ def bwd_splits(sqa, B, Hq, Hkv, N, d, causal, T=0):
     return sqa.sqa_attn_bwd_num_splits(B, Hq, Hkv, N, d, causal=bool(causal), T=T)
 
 
-def time_variant(sqa, torch, q, k, v, scale, causal, steps, warmup):
+class ClockSampler:
+    """Reads the graphics clock (MHz, mean over the XCDs) from amdsmi's GPU
+    metrics in a thread while a kernel runs back to back. The firmware
+    refreshes that table about once per second, so a clock reading needs a
+    window of a few seconds: only refreshes that arrive more than
+    SETTLE_S after the window opened (and so describe a loaded interval)
+    count. Reports None where amdsmi is unavailable."""
+
+    SETTLE_S = 1.1
+
+    def __init__(self, period_s: float = 0.02):
+        self.period = period_s
+        self.samples = []
+        self._stop = None
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self._amdsmi = amdsmi
+            self._handle = handles[0] if handles else None
+            if self._handle is not None and self._read() is None:
+                self._handle = None
+        except Exception:
+            self._handle = None
+
+    def _read(self):
+        """(refresh stamp, MHz) or None."""
+        try:
+            m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+            stamp = m.get("system_clock_counter", m.get("firmware_timestamp"))
+            xs = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+            if xs:
+                return stamp, sum(xs) / len(xs)
+            c = m.get("current_gfxclk")
+            if isinstance(c, (int, float)) and 0 < c < 10000:
+                return stamp, float(c)
+            return None
+        except Exception:
+            return None
+
+    def start(self):
+        import threading
+        self.samples = []
+        if self._handle is None:
+            return
+        self._stop = threading.Event()
+        t0 = time.perf_counter()
+
+        def run():
+            seen = set()
+            while not self._stop.is_set():
+                r = self._read()
+                if r is not None and r[0] not in seen:
+                    seen.add(r[0])
+                    self.samples.append((time.perf_counter() - t0, r[1]))
+                self._stop.wait(self.period)
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+        xs = [c for t, c in self.samples if t >= self.SETTLE_S]
+        if not xs:
+            return None
+        return {"mean_mhz": round(sum(xs) / len(xs), 1), "min_mhz": round(min(xs), 1),
+                "max_mhz": round(max(xs), 1), "refreshes": len(xs)}
+
+
+CLOCK = None  # ClockSampler, created in main()
+MIN_WARMUP_S = 0.5
+CLOCK_WINDOW_S = 2.6
+
+
+def measure(torch, fn, steps, warmup, min_warmup_s=MIN_WARMUP_S, clock_window_s=CLOCK_WINDOW_S):
+    """Warm up (at least ``warmup`` calls and ``min_warmup_s`` of GPU time,
+    each call synchronised so the queue never runs ahead; with a clock
+    window, the warm-up lasts at least that long and the graphics clock is
+    sampled meanwhile: the clock of this kernel under sustained load), then
+    time exactly ``steps`` calls bracketed by synchronisations, with a HIP
+    event on the launch stream between consecutive calls. Returns the mean
+    (total / steps), median and minimum per-call times in ms, the wall
+    time of the timed calls and the clock."""
     stream = torch.cuda.current_stream()
-    out = torch.empty_like(q)
-    for _ in range(warmup):
-        sqa.sqa_attn_fwd(q, k, v, scale=scale, causal=causal, out=out, num_splits=NUM_SPLITS)
+    window = clock_window_s if (clock_window_s and CLOCK is not None and CLOCK._handle is not None) else 0.0
+    if window:
+        CLOCK.start()
+    done, t0 = 0, time.perf_counter()
+    while done < warmup or time.perf_counter() - t0 < max(min_warmup_s, window):
+        fn()
+        torch.cuda.synchronize()
+        done += 1
+    clk = CLOCK.stop() if window else None
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(steps):
-        sqa.sqa_attn_fwd(q, k, v, scale=scale, causal=causal, out=out, num_splits=NUM_SPLITS)
-    end.record(stream)
+    evs[0].record(stream)
+    for i in range(steps):
+        fn()
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    return start.elapsed_time(end) / steps, wall, out
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    total = evs[0].elapsed_time(evs[steps])
+    n = len(per)
+    median = per[n // 2] if n % 2 else 0.5 * (per[n // 2 - 1] + per[n // 2])
+    return {"mean_ms": total / steps, "median_ms": median, "min_ms": per[0], "wall_s": wall,
+            "warmup_calls": done, "clock": clk}
+
+
+def clock_peak_tflops(clk):
+    """bf16 dense MFMA peak at the measured mean graphics clock."""
+    if not clk:
+        return None
+    return 256 * 4096 * clk["mean_mhz"] * 1e6 / 1e12
+
+
+def time_variant(sqa, torch, q, k, v, scale, causal, steps, warmup):
+    out = torch.empty_like(q)
+    fn = lambda: sqa.sqa_attn_fwd(q, k, v, scale=scale, causal=causal, out=out, num_splits=NUM_SPLITS)
+    m = measure(torch, fn, steps, warmup)
+    return m, out
 
 
 def cpu_baseline(w, variant, causal, rows_count, arrays):
@@ -125,10 +248,10 @@ def cpu_baseline(w, variant, causal, rows_count, arrays):
     q, k, v = select_variant(*arrays, Hq, Hkv)
     rows = sample_rows(w.N, rows_count)
     try:
-        cores = len(os.sched_getaffinity(0))
+        host_cores = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    threads = max(1, min(16, cores))
+        host_cores = os.cpu_count() or 1
+    threads = max(1, min(16, host_cores))
     t0 = time.perf_counter()
     oracle_attention(q, k, v, scale=w.scale, causal=bool(causal), rows=rows, threads=threads)
     dt = time.perf_counter() - t0
@@ -136,7 +259,8 @@ def cpu_baseline(w, variant, causal, rows_count, arrays):
         flops = float(np.sum(4.0 * (rows + 1) * w.d)) * w.B * Hq
     else:
         flops = 4.0 * len(rows) * w.N * w.d * w.B * Hq
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "host_cores": host_cores,
+            "kind": "oracle",
             "sample": f"{len(rows)} seeded query rows x {w.B * Hq} heads of {w.name} "
                       f"({Hq},{Hkv}) causal={causal}, full key range; fp64 numpy, "
                       f"{dt:.2f} s wall"}
@@ -171,23 +295,40 @@ def bench_backward(sqa, torch, q, k, v, w, causal, steps, warmup):
             "tokens_per_s": round(B * N / (ms * 1e-3), 1)}
 
 
-# v_exp_f32 issues at half rate: 64 lanes / 8 cycles per SIMD, 1024 SIMDs, 2.4 GHz
+# v_exp_f32: one wave64 instruction per 8 cycles per SIMD (64 exps), 1024
+# SIMDs, 2.4 GHz -- the rate the issue probe measures (bench.py --probe)
 PEAK_EXP_PER_S = 1024 * 8 * 2.4e9
+HBM_BYTES_PER_S = 8.0e12
+
+
+def layer_bound(B, N, D, Hq, Hkv, d, measured_ms):
+    """Lower bound on the SQA layer's time as the sum, over its three
+    kernels, of each kernel's largest single-resource time: the QKV+RoPE and
+    output-projection GEMMs by their HBM bytes (inputs read once, outputs
+    written once) or bf16 MFMA FLOPs, the causal d = 16 attention by its HBM
+    bytes, its MFMA FLOPs or its exponentials at the v_exp_f32 rate."""
+    e = 2  # bf16
+    x = B * N * D * e
+    qkv = B * N * (Hq + 2 * Hkv) * d * e
+    o = B * N * Hq * d * e
+    wts = (D * (Hq + 2 * Hkv) * d + Hq * d * D) * e
+    gemm1_flop = 2.0 * B * N * D * (Hq + 2 * Hkv) * d
+    gemm2_flop = 2.0 * B * N * Hq * d * D
+    attn_flop = counted_flops(B, Hq, N, d, True)
+    exps = B * Hq * N * (N + 1) / 2.0
+    t1 = max((x + qkv + D * (Hq + 2 * Hkv) * d * e) / HBM_BYTES_PER_S, gemm1_flop / (PEAK_BF16_TFLOPS * 1e12))
+    t2 = max((qkv + o) / HBM_BYTES_PER_S, attn_flop / (PEAK_BF16_TFLOPS * 1e12), exps / PEAK_EXP_PER_S)
+    t3 = max((o + x + Hq * d * D * e) / HBM_BYTES_PER_S, gemm2_flop / (PEAK_BF16_TFLOPS * 1e12))
+    bound_us = (t1 + t2 + t3) * 1e6
+    return {"bound": "hbm+exp (sum over kernels)", "bound_us": round(bound_us, 2),
+            "bound_parts_us": {"qkv_rope_gemm": round(t1 * 1e6, 2), "attention": round(t2 * 1e6, 2),
+                               "out_proj_gemm": round(t3 * 1e6, 2)},
+            "algorithmic_bytes": x + 2 * qkv + 2 * o + x + wts,
+            "frac_of_bound": round(bound_us / (measured_ms * 1e3), 4)}
 
 
 def _timed(torch, fn, steps, warmup):
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        fn()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    return measure(torch, fn, steps, warmup, clock_window_s=0)["mean_ms"]
 
 
 def _common(args, ms, w, extra):
@@ -211,21 +352,21 @@ def bench_layer(sqa, torch, w, args):
                      dtype=torch.uint8, device="cuda")
     fn = lambda: sqa.sqa_layer_fwd(tx, tq, tk, tv, to, H=w.H, H_q=Hq, H_kv=Hkv, rope_base=w.rope_base,
                                    scale=w.scale, causal=True, out=out, workspace=ws)
-    ms = _timed(torch, fn, args.steps, args.warmup)
+    m = measure(torch, fn, args.steps, args.warmup)
+    ms = m["mean_ms"]
     attn = counted_flops(w.B, Hq, w.N, d, True)
     gemm = 2.0 * w.B * w.N * w.d_model * (Hq + 2 * Hkv) * d + 2.0 * w.B * w.N * Hq * d * w.d_model
-    exps = w.B * Hq * w.N * (w.N + 1) / 2.0
     tflops = (attn + gemm) / (ms * 1e-3) / 1e12
-    achieved = exps / (ms * 1e-3) / 1e12
+    lb = layer_bound(w.B, w.N, w.d_model, Hq, Hkv, d, ms)
     return _common(args, ms, w, {
         "value": round(tflops, 3), "unit": "TFLOP/s", "dtype": "bf16",
         "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1),
         "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.d_model, "H": w.H, "H_q": Hq,
                    "H_kv": Hkv, "d": d, "causal": 1, "flop_attention": attn, "flop_gemm": gemm},
-        "roofline": {"bound": "alu", "achieved": round(achieved, 3),
-                     "peak": round(PEAK_EXP_PER_S / 1e12, 3), "unit": "Texp/s",
-                     "frac": round(achieved * 1e12 / PEAK_EXP_PER_S, 4), "traffic": None,
-                     "kernel": "whole layer (attention at d=16 is v_exp-bound)"},
+        "roofline": {"bound": "hbm+exp", "achieved": round(ms * 1e3, 3), "peak": lb["bound_us"], "unit": "us",
+                     "frac": lb["frac_of_bound"], "traffic": None, "parts_us": lb["bound_parts_us"],
+                     "median_ms": round(m["median_ms"], 5), "min_ms": round(m["min_ms"], 5),
+                     "kernel": "whole layer: time against the sum of each kernel's single-resource bound"},
         "cpu_baseline": None, "comparison": None})
 
 
@@ -392,6 +533,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--probe", action="store_true",
+                    help="only run the issue-rate probes (libsqa_probe.so) and the 32k (8,4) forward; "
+                         "print their JSON object")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the sweep over every target workload (the configs object)")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only sqa_attn_bwd (for profiling) and print its object")
     ap.add_argument("--cpu-rows", type=int, default=65536)
@@ -401,7 +547,7 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
                          "used to scale rocprofv3 FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
-    global NUM_SPLITS
+    global NUM_SPLITS, CLOCK
     NUM_SPLITS = args.num_splits
 
     if args.gpus != 1:
@@ -422,6 +568,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    CLOCK = ClockSampler()
+
+    if args.probe:
+        print(json.dumps({"probes": run_probes(torch, sqa)}), flush=True)
+        return
 
     if args.copy_calib:
         n = args.copy_calib * (1 << 20)
@@ -455,12 +606,12 @@ def main():
     def dev(a):
         return torch.from_numpy(a).to("cuda").to(torch.bfloat16).contiguous()
 
-    def run(var):
+    def run(var, steps, warmup):
         q, k, v = (dev(a) for a in select_variant(q_all, k_all, v_all, *var))
-        ms, wall, _ = time_variant(sqa, torch, q, k, v, w.scale, bool(causal), args.steps, args.warmup)
+        m, _ = time_variant(sqa, torch, q, k, v, w.scale, bool(causal), steps, warmup)
         del q, k, v
         torch.cuda.empty_cache()
-        return ms, wall
+        return m
 
     if args.backward_only:
         q, k, v = (dev(a) for a in select_variant(q_all, k_all, v_all, *variant))
@@ -468,7 +619,9 @@ def main():
                                                      args.warmup)}), flush=True)
         return
 
-    ms, wall = run(variant)
+    # the headline: exactly --steps timed calls after the warm-up
+    m = run(variant, args.steps, args.warmup)
+    ms = m["mean_ms"]
     flops = counted_flops(w.B, Hq, w.N, w.d, causal)
     tflops = flops / (ms * 1e-3) / 1e12
     tokens = w.B * w.N / (ms * 1e-3)
@@ -480,8 +633,9 @@ def main():
             key = f"{var[0]},{var[1]}"
             if key in comparison or var == variant or var[0] > w.H:
                 continue
-            cms, _ = run(var)
-            comparison[key] = {"ms": round(cms, 4),
+            cm = run(var, args.steps, args.warmup)
+            cms = cm["mean_ms"]
+            comparison[key] = {"ms": round(cms, 4), "median_ms": round(cm["median_ms"], 4),
                                "tflops": round(counted_flops(w.B, var[0], w.N, w.d, causal) / (cms * 1e-3) / 1e12, 2)}
         if "16,16" in comparison:
             comparison["speedup_vs_mha"] = round(comparison["16,16"]["ms"] / ms, 3)
@@ -493,17 +647,32 @@ def main():
         backward = bench_backward(sqa, torch, q, k, v, w, causal, args.steps, args.warmup)
         del q, k, v
         torch.cuda.empty_cache()
+    del q_all, k_all, v_all
 
     traffic = stored_traffic(w.name, variant, causal, w.d)
+    cpk = clock_peak_tflops(m["clock"])
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic,
+                "traffic_source": "profiles/attn_fwd_bf16_traffic.json (rocprofv3 FETCH_SIZE/WRITE_SIZE of this "
+                                  "kernel source, scaled by a 1 GiB copy); null if the source changed since",
                 "kernel": kernel_name(w.d),
-                "per_launch_flop": flops}
+                "per_launch_flop": flops,
+                "median_ms": round(m["median_ms"], 5), "min_ms": round(m["min_ms"], 5),
+                "tflops_median": round(flops / (m["median_ms"] * 1e-3) / 1e12, 2),
+                "tflops_min_time": round(flops / (m["min_ms"] * 1e-3) / 1e12, 2),
+                "clock": m["clock"],
+                "peak_at_clock": round(cpk, 1) if cpk else None,
+                "frac_at_clock": round(tflops / cpk, 4) if cpk else None}
+
+    configs = None
+    if not args.no_configs and w.name == "long32k_bf16":
+        configs = run_configs(sqa, torch, args)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, variant, causal, args.cpu_rows, (q_all, k_all, v_all))
+        qa, ka, va = draw_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=0, peaky=w.peaky)
+        cpu = cpu_baseline(w, variant, causal, args.cpu_rows, (qa, ka, va))
 
     line = {
         "metric": METRIC,
@@ -527,9 +696,184 @@ def main():
         "cpu_baseline": cpu,
         "comparison": comparison,
         "backward": backward,
-        "wall_s_timed_region": round(wall, 4),
+        "configs": configs,
+        "warmup_calls": m["warmup_calls"],
+        "wall_s_timed_region": round(m["wall_s"], 4),
     }
     print(json.dumps(line), flush=True)
+
+
+# ------------------------------------------------------------ issue probes
+PROBE_KINDS = {0: "mfma_only", 1: "forward_mix_registers", 2: "forward_mix_with_lds_reads", 3: "exp_only",
+               4: "fma_only"}
+
+
+def run_probes(torch, sqa):
+    """Time the issue-rate probes of libsqa_probe.so (two 4-wave workgroups
+    per CU) and the d = 64 forward on the 32k (8,4) workload in the same
+    process; rates per launch from HIP events, clock sampled meanwhile."""
+    import ctypes
+    path = os.path.join(ROOT, "sparse_query_attention_sqa_amd", "libsqa_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.sqa_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sqa_probe_run.restype = ctypes.c_int
+    lib.sqa_probe_threads.argtypes = [ctypes.c_int]
+    lib.sqa_probe_threads.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = 2 * cus
+    out = torch.empty(lib.sqa_probe_threads(wgs), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    res = {"workgroups": wgs, "threads_per_workgroup": 256, "cus": cus}
+    iters = {0: 4000, 1: 2000, 2: 2000, 3: 40000, 4: 40000}
+    for kind, name in PROBE_KINDS.items():
+        n = iters[kind]
+        fn = lambda: _check_probe(lib.sqa_probe_run(kind, wgs, n, ctypes.c_void_p(out.data_ptr()),
+                                                    ctypes.c_void_p(st.cuda_stream)))
+        m = measure(torch, fn, 7, 2, min_warmup_s=0.3)
+        t = m["median_ms"] * 1e-3
+        e = {"iters": n, "median_ms": round(m["median_ms"], 4), "min_ms": round(m["min_ms"], 4),
+             "clock_mhz": m["clock"]["mean_mhz"] if m["clock"] else None}
+        waves = wgs * 4
+        if kind in (0, 1, 2):
+            fl = waves * n * 16 * 32768.0
+            e["mfma_tflops"] = round(fl / t / 1e12, 2)
+            e["frac_of_nominal"] = round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)
+            cpk = clock_peak_tflops(m["clock"])
+            e["frac_at_clock"] = round(fl / t / 1e12 / cpk, 4) if cpk else None
+        else:
+            ops = waves * n * 16.0  # wave64 instructions
+            e["wave_instructions_per_s"] = round(ops / t, 1)
+            e["lane_ops_per_s"] = round(ops * 64 / t, 1)
+            if m["clock"]:
+                e["cycles_per_wave_instruction_per_simd"] = round(t * m["clock"]["mean_mhz"] * 1e6 / (ops / (cus * 4)), 3)
+        res[name] = e
+    base = res["mfma_only"]["mfma_tflops"]
+    for name in ("forward_mix_registers", "forward_mix_with_lds_reads"):
+        res[name]["frac_of_mfma_only"] = round(res[name]["mfma_tflops"] / base, 4)
+    # the forward itself on the 32k (8,4) workload, same process
+    from synth import draw_qkv, select_variant
+    q, k, v = (torch.from_numpy(a).to("cuda").to(torch.bfloat16).contiguous()
+               for a in select_variant(*draw_qkv(1, 16, 32768, 64, "bf16", seed=0), 8, 4))
+    o = torch.empty_like(q)
+    fn = lambda: sqa.sqa_attn_fwd(q, k, v, scale=0.125, causal=False, out=o, num_splits=1)
+    m = measure(torch, fn, 20, 5)
+    fl = counted_flops(1, 8, 32768, 64, False)
+    tf = fl / (m["median_ms"] * 1e-3) / 1e12
+    cpk = clock_peak_tflops(m["clock"])
+    mix = res["forward_mix_with_lds_reads"]
+    e = {"median_ms": round(m["median_ms"], 4), "tflops": round(tf, 2),
+         "frac_of_nominal": round(tf / PEAK_BF16_TFLOPS, 4), "frac_of_mfma_only": round(tf / base, 4),
+         "frac_of_forward_mix_with_lds_reads": round(tf / mix["mfma_tflops"], 4),
+         "clock_mhz": m["clock"]["mean_mhz"] if m["clock"] else None,
+         "frac_at_clock": round(tf / cpk, 4) if cpk else None}
+    if cpk and mix.get("frac_at_clock"):
+        # per clock cycle: the kernel's MFMA fraction against the probe's
+        e["per_clock_vs_forward_mix_with_lds_reads"] = round(e["frac_at_clock"] / mix["frac_at_clock"], 4)
+    res["attn_fwd_bf16_d64_kernel_long32k_8_4"] = e
+    return res
+
+
+def _check_probe(code):
+    if code != 0:
+        raise RuntimeError(f"sqa_probe_run failed with HIP error {code}")
+
+
+# ------------------------------------------------------------ every config
+CONFIG_MIN_TIMED_S = 0.25
+CONFIG_MIN_CALLS = 3
+CONFIG_MAX_CALLS = 20
+
+
+def _calls_for(ms_estimate):
+    return int(max(CONFIG_MIN_CALLS, min(CONFIG_MAX_CALLS, math.ceil(CONFIG_MIN_TIMED_S * 1e3 / max(ms_estimate, 1e-3)))))
+
+
+def _entry(m, flops, tokens, peak, calls):
+    cpk = clock_peak_tflops(m["clock"])
+    med = m["median_ms"]
+    tf = flops / (med * 1e-3) / 1e12
+    e = {"calls": calls, "median_ms": round(med, 5), "min_ms": round(m["min_ms"], 5),
+         "mean_ms": round(m["mean_ms"], 5), "tflops": round(tf, 2),
+         "tflops_min_time": round(flops / (m["min_ms"] * 1e-3) / 1e12, 2),
+         "tokens_per_s": round(tokens / (med * 1e-3), 1), "frac": round(tf / peak, 4),
+         "clock_mhz": m["clock"]["mean_mhz"] if m["clock"] else None}
+    if cpk and peak == PEAK_BF16_TFLOPS:
+        e["frac_at_clock"] = round(tf / cpk, 4)
+    return e
+
+
+def _attn_config(sqa, torch, wname, variants, causals):
+    """Time every (variant, causal) of a long-sequence workload; speedups are
+    t(16,16) / t(variant) of the same mask, next to H / H_q."""
+    from synth import WORKLOADS, draw_qkv, select_variant
+    w = WORKLOADS[wname]
+    qa, ka, va = draw_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=0, peaky=w.peaky)
+    out = {}
+    for var in variants:
+        q, k, v = (torch.from_numpy(a).to("cuda").to(torch.bfloat16).contiguous()
+                   for a in select_variant(qa, ka, va, *var))
+        o = torch.empty_like(q)
+        for causal in causals:
+            fn = lambda: sqa.sqa_attn_fwd(q, k, v, scale=w.scale, causal=bool(causal), out=o)
+            fl = counted_flops(w.B, var[0], w.N, w.d, causal)
+            est = fl / (1.0e15) * 1e3  # ms at 1 PFLOP/s, to size the timed calls
+            calls = _calls_for(est)
+            m = measure(torch, fn, calls, 2)
+            out[f"{var[0]},{var[1]}" + (":causal" if causal else "")] = _entry(m, fl, w.B * w.N, PEAK_BF16_TFLOPS,
+                                                                                 calls)
+            print(f"[bench] {wname} {var} causal={causal}: {m['median_ms']:.4f} ms", file=sys.stderr, flush=True)
+        del q, k, v, o
+        torch.cuda.empty_cache()
+    del qa, ka, va
+    for key, e in out.items():
+        causal = key.endswith(":causal")
+        base = out.get("16,16" + (":causal" if causal else ""))
+        hq = int(key.split(",")[0])
+        if base and hq != 16:
+            e["speedup_vs_16_16"] = round(base["median_ms"] / e["median_ms"], 3)
+            e["H_over_Hq"] = round(w.H / hq, 3)
+    return {"workload": wname, "B": w.B, "N": w.N, "d": w.d, "peaky_keys": w.peaky, "variants": out}
+
+
+def run_configs(sqa, torch, args):
+    from synth import WORKLOADS, draw_layer, draw_qkv, select_variant
+    res = {}
+    # SQAT-m attention core, fp32 (a correctness workload; fp32 vector bound)
+    w = WORKLOADS["sqatm_core_f32"]
+    q, k, v = (torch.from_numpy(a).to("cuda").contiguous()
+               for a in select_variant(*draw_qkv(w.B, w.H, w.N, w.d, "f32", seed=0), 8, 4))
+    o = torch.empty_like(q)
+    core = {}
+    for causal in (0, 1):
+        fn = lambda: sqa.sqa_attn_fwd(q, k, v, scale=w.scale, causal=bool(causal), out=o)
+        m = measure(torch, fn, 50, 5, min_warmup_s=0.2)
+        core["8,4" + (":causal" if causal else "")] = _entry(m, counted_flops(w.B, 8, w.N, w.d, causal), w.B * w.N,
+                                                              PEAK_F32_TFLOPS, 50)
+    res["C1_sqatm_core_f32"] = {"workload": w.name, "B": w.B, "N": w.N, "d": w.d, "dtype": "f32",
+                                "peak": "fp32 vector 157.3 TFLOP/s", "variants": core}
+    del q, k, v, o
+    # SQAT-m layer: projections + RoPE + causal SQA + output projection
+    w = WORKLOADS["sqatm_layer_bf16"]
+    d = w.d_model // w.H
+    arrs = [torch.from_numpy(a).to("cuda").to(torch.bfloat16).contiguous()
+            for a in draw_layer(w.B, w.N, w.d_model, w.H, 8, 4, seed=0)]
+    y = torch.empty_like(arrs[0])
+    ws = torch.empty(sqa.sqa_layer_workspace_bytes(w.B, w.N, w.d_model, w.H, 8, 4), dtype=torch.uint8, device="cuda")
+    fn = lambda: sqa.sqa_layer_fwd(*arrs, H=w.H, H_q=8, H_kv=4, rope_base=w.rope_base, scale=w.scale, causal=True,
+                                   out=y, workspace=ws)
+    m = measure(torch, fn, 100, 10, min_warmup_s=0.2)
+    attn = counted_flops(w.B, 8, w.N, d, True)
+    gemm = 2.0 * w.B * w.N * w.d_model * (8 + 2 * 4) * d + 2.0 * w.B * w.N * 8 * d * w.d_model
+    e = _entry(m, attn + gemm, w.B * w.N, PEAK_BF16_TFLOPS, 100)
+    e.update(layer_bound(w.B, w.N, w.d_model, 8, 4, d, m["median_ms"]))
+    res["C2_sqatm_layer_bf16"] = {"workload": w.name, "B": w.B, "N": w.N, "D": w.d_model, "d": d, "causal": 1,
+                                  "variants": {"8,4:causal": e}}
+    del arrs, y, ws
+    torch.cuda.empty_cache()
+    res["C3_long32k"] = _attn_config(sqa, torch, "long32k_bf16", [(8, 4), (16, 16), (16, 4), (16, 1)], (0,))
+    res["C4_long131k"] = _attn_config(sqa, torch, "long131k_bf16", [(8, 8), (4, 4), (16, 16)], (0, 1))
+    res["C5_long200k_peaky"] = _attn_config(sqa, torch, "long200k_peaky_bf16", [(4, 4), (16, 16)], (0,))
+    return res
 
 
 if __name__ == "__main__":
