@@ -182,6 +182,40 @@ sqa_status sqa_attn_fwd_varlen_split(const void* q, const void* k, const void* v
                                      size_t workspace_bytes, void* stream);
 
 /*
+ * sqa_attn_fwd_tail_splits / sqa_attn_fwd_tail_workspace_bytes /
+ * sqa_attn_fwd_tail -- sqa_attn_fwd with a schedule for launches whose last
+ * round of workgroups is mostly empty (a scheduling choice; the pages do
+ * not describe a kernel). The forward's workgroups run in rounds of two per
+ * compute unit. When the workgroups past the last whole round fill at most
+ * half a round, each of them runs as S workgroups over S contiguous key
+ * ranges (S = floor(slots / those workgroups), at most 16, each range at
+ * least 1024 keys), whose partial softmax states are merged afterwards; so
+ * the last round takes about 1/S of a workgroup's time instead of a whole
+ * one. Same results as sqa_attn_fwd up to fp32 rounding order.
+ * Planned only for dtype SQA_BF16, d = 64, causal == 0 and H_kv dividing
+ * H_q; the plan depends on the current device's compute-unit count.
+ *
+ *   sqa_attn_fwd_tail_splits        S for these sizes (1: no tail split)
+ *   sqa_attn_fwd_tail_workspace_bytes  device workspace sqa_attn_fwd_tail
+ *                                   needs: S * units * 256 rows * (64 + 2)
+ *                                   fp32 values (0 when S = 1)
+ *   sqa_attn_fwd_tail               arguments as sqa_attn_fwd, plus the
+ *                                   workspace (16-byte aligned, owned by the
+ *                                   caller, not overlapping any tensor;
+ *                                   contents on return unspecified). With
+ *                                   S = 1 it is sqa_attn_fwd and ignores the
+ *                                   workspace.
+ * Errors: as sqa_attn_fwd, plus SQA_ERR_WORKSPACE.
+ */
+int64_t sqa_attn_fwd_tail_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
+                                 int causal);
+size_t sqa_attn_fwd_tail_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
+                                         int causal);
+sqa_status sqa_attn_fwd_tail(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H_q,
+                             int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * sqa_attn_bwd_workspace_bytes -- bytes of device workspace sqa_attn_bwd
  * needs for these sizes: one fp32 pair (lse * log2(e), D_t) per query row,
  * with each (batch, query head)'s rows padded up to a multiple of 32, i.e.

@@ -30,7 +30,7 @@ import os
 from typing import Optional
 
 __all__ = ["SQAError", "lib_path", "load_library", "sqa_attn_fwd", "sqa_attn_fwd_varlen",
-           "sqa_attn_fwd_num_splits", "sqa_attn_bwd", "sqa_attn_bwd_noalloc", "sqa_attn_bwd_num_splits",
+           "sqa_attn_fwd_num_splits", "sqa_attn_fwd_tail_splits", "sqa_attn_bwd", "sqa_attn_bwd_noalloc", "sqa_attn_bwd_num_splits",
            "sqa_attn_bwd_split_workspace_bytes", "sqa_attn_bwd_varlen_split_workspace_bytes",
            "sqa_attn_bwd_varlen", "sqa_attn_bwd_varlen_workspace_bytes",
            "sqa_attn_bwd_workspace_bytes", "sqa_layer_fwd", "sqa_block_fwd",
@@ -82,6 +82,13 @@ def load_library() -> ctypes.CDLL:
     lib.sqa_attn_fwd_varlen_split.restype = ctypes.c_int
     lib.sqa_attn_fwd_num_splits.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, i64]
     lib.sqa_attn_fwd_num_splits.restype = i64
+    lib.sqa_attn_fwd_tail_splits.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.sqa_attn_fwd_tail_splits.restype = i64
+    lib.sqa_attn_fwd_tail_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.sqa_attn_fwd_tail_workspace_bytes.restype = ctypes.c_size_t
+    lib.sqa_attn_fwd_tail.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, f32, ctypes.c_int,
+                                      vp, vp, ctypes.c_size_t, vp]
+    lib.sqa_attn_fwd_tail.restype = ctypes.c_int
     lib.sqa_attn_fwd_split_workspace_bytes.argtypes = [i64, i64, ctypes.c_int, i64]
     lib.sqa_attn_fwd_split_workspace_bytes.restype = ctypes.c_size_t
     lib.sqa_attn_bwd_split.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_int, f32, ctypes.c_int, i64, vp,
@@ -170,7 +177,7 @@ def _require_device(*ts) -> None:
 
 
 def sqa_attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, out=None,
-                 return_lse: bool = False, num_splits: Optional[int] = None):
+                 return_lse: bool = False, num_splits: Optional[int] = None, tail: Optional[bool] = None):
     """SQA attention forward on the GPU.
 
     q [B, H_q, N, d]; k, v [B, H_kv, N, d]; bf16 or fp32, contiguous, on the
@@ -178,7 +185,9 @@ def sqa_attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False
     floor(i * H_kv / H_q). Returns o [B, H_q, N, d] (and lse [B, H_q, N] fp32
     if ``return_lse``). ``num_splits``: key-range splits (bf16, d = 64 only;
     None: the library's choice, sqa_attn_fwd_num_splits); with more than one
-    a workspace is allocated from torch's caching allocator.
+    a workspace is allocated from torch's caching allocator. ``tail``: the
+    tail-split schedule (sqa_attn_fwd_tail) where the library plans one;
+    None uses it when num_splits is also left to the library, False never.
     """
     torch = _torch()
     lib = load_library()
@@ -200,9 +209,21 @@ def sqa_attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False
         if out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("out must match q in shape and dtype")
     lse = torch.empty((B, H_q, N), dtype=torch.float32, device=q.device) if return_lse else None
+    if tail is None:
+        tail = num_splits is None
     if num_splits is None:
         num_splits = lib.sqa_attn_fwd_num_splits(B, H_q, H_kv, N, d, _dtype_code(q), int(bool(causal)), 0)
-    if num_splits == 1:
+    tail_bytes = 0
+    if num_splits == 1 and tail:
+        tail_bytes = int(lib.sqa_attn_fwd_tail_workspace_bytes(B, H_q, H_kv, N, d, _dtype_code(q),
+                                                               int(bool(causal))))
+    if tail_bytes > 0:
+        ws = torch.empty(tail_bytes, dtype=torch.uint8, device=q.device)
+        st = lib.sqa_attn_fwd_tail(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H_q, H_kv,
+                                   N, d, _dtype_code(q), float(scale), int(bool(causal)),
+                                   lse.data_ptr() if lse is not None else None, ws.data_ptr(), tail_bytes,
+                                   _stream_handle(q.device))
+    elif num_splits == 1:
         st = lib.sqa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H_q, H_kv,
                               N, d, _dtype_code(q), float(scale), int(bool(causal)),
                               lse.data_ptr() if lse is not None else None, _stream_handle(q.device))
@@ -223,6 +244,13 @@ def _split_workspace(lib, rows: int, d: int, q, num_splits: int):
         return None, 0
     buf = _torch().empty(nbytes, dtype=_torch().uint8, device=q.device)
     return buf.data_ptr(), nbytes
+
+
+def sqa_attn_fwd_tail_splits(B: int, H_q: int, H_kv: int, N: int, d: int, dtype: str = "bf16",
+                             causal: bool = False) -> int:
+    """Key ranges per tail workgroup the library plans (1: no tail split)."""
+    code = SQA_BF16 if dtype == "bf16" else SQA_F32
+    return int(load_library().sqa_attn_fwd_tail_splits(B, H_q, H_kv, N, d, code, int(bool(causal))))
 
 
 def sqa_attn_fwd_num_splits(B: int, H_q: int, H_kv: int, N: int, d: int, dtype: str = "bf16",

@@ -628,6 +628,7 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
 
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream) {
   if (p.D == 64) return launch_attn_fwd_bf16_d64(p, stream);
+  if (p.tail_split > 1) return hipErrorInvalidValue;  // the tail split is a d = 64 schedule
   // d = 16 under a causal mask: 32-row waves (112 VGPRs, four waves per
   // SIMD), whose extra waves hide the latency of the short causal tile chains
   // (B16 N1024 (8,4): 27.7 -> 23.1 us; N = 4096: +20 %; N = 32768: +9 %).

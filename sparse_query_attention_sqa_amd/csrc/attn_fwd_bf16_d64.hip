@@ -124,6 +124,12 @@ struct Args {
   int nsplit;    // key-range splits per workgroup's rows (1: none)
   float* part;   // nsplit > 1: [nsplit][rows][64] unnormalised O, then [nsplit][rows][2] (m, l)
   int64_t rows;  // query rows: B*Hq*N (packed: Hq*T)
+  // tail split (dense encoder-style, nsplit == 1): logical workgroups from
+  // tail_start on run as tail_split workgroups each, one per key range,
+  // leaving partial states in tail_part ([tail_split][units*256][64], then
+  // [tail_split][units*256][2]) for attn_tail_merge_kernel
+  int tail_start, tail_split;
+  float* tail_part;
 };
 
 // MFMA row r of a K tile holds key pi(r), so that S^T entry i of lane-half lg
@@ -374,12 +380,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   // together in time (a split index tied to blockIdx % nsplit would put, for
   // two splits, every first range -- under a causal mask most of the work --
   // on the even XCDs). With one split wid = blockIdx.x.
+  // Tail split: blocks from tail_start on are the key ranges of the
+  // logical workgroups past the last full round; the blocks before it map
+  // the whole workgroups below tail_start as an unsplit launch would.
+  const bool tail = a.tail_split > 1 && (int)blockIdx.x >= a.tail_start;
+  const int nsplit = tail ? a.tail_split : a.nsplit;
+  const int nwg_map = a.tail_split > 1 ? a.tail_start : a.nwg;
   const int g8 = (int)(blockIdx.x >> 3), x8 = (int)(blockIdx.x & 7);
-  const int split = g8 % a.nsplit;
-  const int wid = (g8 / a.nsplit) * 8 + x8;
+  const int split = tail ? ((int)blockIdx.x - a.tail_start) % a.tail_split : g8 % a.nsplit;
+  const int wid = tail ? a.tail_start + ((int)blockIdx.x - a.tail_start) / a.tail_split : (g8 / a.nsplit) * 8 + x8;
   if (wid >= a.nwg) return;
   int bkv, w_in;
-  if (a.pair_major) {
+  if (tail) {  // one logical workgroup per tail unit, in (batch*Hkv, index) order
+    bkv = wid / a.wg_per_bkv;
+    w_in = wid % a.wg_per_bkv;
+  } else if (a.pair_major) {
     if (!pair_major_coords(wid, a.n_bkv, a.wg_per_bkv, bkv, w_in)) return;
   } else if (a.spread) {  // packed sequences, or uneven groups under a causal mask
     spread_coords(wid, a.n_bkv, a.wg_per_bkv, a.causal != 0, a.spread_block, bkv, w_in);
@@ -391,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
                  (a.N + kRowsPerWave - 1) / kRowsPerWave, kWaves, bkv, w_in);
   } else if (!a.causal) {  // consecutive logical workgroups on one XCD (shared L2)
     const int bid = wid;
-    const int per = a.nwg / kXcds, rem = a.nwg % kXcds;
+    const int per = nwg_map / kXcds, rem = nwg_map % kXcds;
     const int x = bid % kXcds, i = bid / kXcds;
     const int L = x * per + min(x, rem) + i;
     bkv = L / a.wg_per_bkv;
@@ -424,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
   // from kt0, so the pipeline runs unchanged on the shifted range. With an
   // even chunk a causal wave either has a visible key for all its rows in
   // this range (kt0 <= 2*tb) or none (last = -1).
-  const int chunk = split_chunk(NT, a.nsplit);
+  const int chunk = split_chunk(NT, nsplit);
   const bool split_rows = NT > chunk;
   const int kt0 = split * chunk;
   if (kt0 >= nt_all) return;
@@ -536,22 +551,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
     // the merge kernel combines the ranges. A wave with no key in this range
     // writes nothing; the merge knows which ranges a row sees.
     if (last < 0) return;
-    float* po = a.part + ((size_t)split * a.rows + qrow0) * D;
-    float* pml = a.part + (size_t)a.nsplit * a.rows * D + ((size_t)split * a.rows + qrow0) * 2;
+    // partial rows: the global query rows, or (tail) the compact rows of
+    // the tail units, 256 per unit: row trow0 + r of this wave is compact
+    // row (unit * 4 + wave) * 64 + r
+    const int64_t prows = tail ? (int64_t)(a.nwg - a.tail_start) * (kWaves * kRowsPerWave) : a.rows;
+    const int64_t prow0 = tail ? ((int64_t)(wid - a.tail_start) * kWaves + wave) * kRowsPerWave : qrow0 + trow0;
+    float* const part = tail ? a.tail_part : a.part;
+    float* po = part + ((size_t)split * prows + prow0) * D;
+    float* pml = part + (size_t)nsplit * prows * D + ((size_t)split * prows + prow0) * 2;
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const float ltot = w.l_run[qs] + __shfl_xor(w.l_run[qs], 32);
-      const int t = trow0 + qs * 32 + ln.l32;
-      if (t < N) {
+      const int r = qs * 32 + ln.l32;
+      if (trow0 + r < N) {
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
           for (int ab = 0; ab < 4; ++ab) {
             const f32x4_t v4 = {w.acc_o[qs][x][4 * ab], w.acc_o[qs][x][4 * ab + 1], w.acc_o[qs][x][4 * ab + 2],
                                 w.acc_o[qs][x][4 * ab + 3]};
-            *reinterpret_cast<f32x4_t*>(po + (size_t)t * D + x * 32 + 8 * ab + 4 * ln.lg) = v4;
+            *reinterpret_cast<f32x4_t*>(po + (size_t)r * D + x * 32 + 8 * ab + 4 * ln.lg) = v4;
           }
-        if (ln.lg == 0) *reinterpret_cast<f32x2_t*>(pml + (size_t)t * 2) = f32x2_t{w.m_run[qs], ltot};
+        if (ln.lg == 0) *reinterpret_cast<f32x2_t*>(pml + (size_t)r * 2) = f32x2_t{w.m_run[qs], ltot};
       }
     }
     return;
@@ -579,6 +600,55 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_d64_kernel(Args a) 
         a.lse[(size_t)qrow0 + t] = (w.m_run[qs] + log2f(ltot)) * 0.69314718055994531f;
     }
   }
+}
+
+// Merge of the tail split: the key ranges of every compact row of the tail
+// units (256 per unit, unit u = logical workgroup tail_start + u, row
+// (u * 4 + wave) * 64 + r is query row trow0 + r of that wave's slot), with
+// the streaming-softmax merge of split_merge.h. Dense encoder-style
+// launches with equal head groups only, so every range holds keys of every
+// row. 16 lanes per row, lane j holding head dims 4j..4j+3.
+struct TailMergeArgs {
+  const float* part;  // [S][rows][64] O, then [S][rows][2] (m, l)
+  uint16_t* o;
+  float* lse;
+  int64_t rows;  // compact rows: (nwg - tail_start) * 256
+  int tail_start, S, N, Hq, Hkv, wg_per_bkv;
+};
+
+__global__ __launch_bounds__(256) void attn_tail_merge_kernel(TailMergeArgs a) {
+  typedef float f4_t __attribute__((ext_vector_type(4)));
+  const int64_t cr = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
+  const int j = threadIdx.x % 16;
+  if (cr >= a.rows) return;
+  const int unit = (int)(cr / (kWaves * kRowsPerWave)), wave = (int)(cr / kRowsPerWave) % kWaves;
+  const int r = (int)(cr % kRowsPerWave);
+  const int L = a.tail_start + unit;
+  const int bkv = L / a.wg_per_bkv, w_in = L % a.wg_per_bkv;
+  const int b = bkv / a.Hkv, kvh = bkv % a.Hkv, g = a.Hq / a.Hkv;
+  const int slot = w_in * kWaves + wave, tb = slot / g, jh = slot % g;
+  const int t = tb * kRowsPerWave + r;
+  if (t >= a.N) return;  // also every slot past the last position block
+  const int64_t orow = ((int64_t)b * a.Hq + kvh * g + jh) * a.N + t;
+  const int NT = (a.N + kTileKeys - 1) / kTileKeys;
+  const int chunk = split_chunk(NT, a.S);
+  const float* pml = a.part + (size_t)a.S * a.rows * D;
+  float M = -INFINITY;
+  for (int s = 0; s < a.S && s * chunk < NT; ++s) M = fmaxf(M, pml[((size_t)s * a.rows + cr) * 2]);
+  float Lsum = 0.f;
+  f4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.S && s * chunk < NT; ++s) {
+    const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(pml + ((size_t)s * a.rows + cr) * 2);
+    const float wgt = __builtin_amdgcn_exp2f(ml[0] - M);
+    Lsum += wgt * ml[1];
+    acc += wgt * *reinterpret_cast<const f4_t*>(a.part + ((size_t)s * a.rows + cr) * D + 4 * j);
+  }
+  const float inv = 1.0f / Lsum;
+  u32x2_t wv;
+  wv[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  wv[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2_t*>(a.o + (size_t)orow * D + 4 * j) = wv;
+  if (a.lse != nullptr && j == 0) a.lse[orow] = (M + log2f(Lsum)) * 0.69314718055994531f;
 }
 
 }  // namespace
@@ -631,13 +701,46 @@ hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream) {
   a.part = p.split_ws;
   a.rows = p.cu_seqlens != nullptr ? p.Hq * p.T : p.B * p.Hq * p.N;
   if (a.nsplit > 1 && a.part == nullptr) return hipErrorInvalidValue;
+  a.tail_start = 0;
+  a.tail_split = 0;
+  a.tail_part = nullptr;
+  if (p.tail_split > 1) {
+    // only where attn_fwd_tail_plan would plan one: dense, encoder-style,
+    // equal head groups, unsplit
+    if (p.cu_seqlens != nullptr || p.causal || uneven || a.nsplit != 1 || p.tail_ws == nullptr ||
+        p.tail_units <= 0 || p.tail_units > a.nwg || p.tail_split > kMaxTailSplit)
+      return hipErrorInvalidValue;
+    a.tail_start = a.nwg - (int)p.tail_units;
+    a.tail_split = p.tail_split;
+    a.tail_part = p.tail_ws;
+  }
   // with splits the grid covers whole runs of 8 (see the kernel's decode)
-  const int64_t grid = a.nsplit == 1 ? a.nwg : ((int64_t)a.nwg + 7) / 8 * 8 * a.nsplit;
+  const int64_t grid = a.tail_split > 1 ? (int64_t)a.tail_start + p.tail_units * p.tail_split
+                       : a.nsplit == 1  ? a.nwg
+                                        : ((int64_t)a.nwg + 7) / 8 * 8 * a.nsplit;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (!p.dry_run) {
     hipLaunchKernelGGL(attn_fwd_bf16_d64_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (a.tail_split > 1) {
+    TailMergeArgs t;
+    t.part = a.tail_part;
+    t.o = a.o;
+    t.lse = a.lse;
+    t.rows = p.tail_units * (kWaves * kRowsPerWave);
+    t.tail_start = a.tail_start;
+    t.S = a.tail_split;
+    t.N = a.N;
+    t.Hq = a.Hq;
+    t.Hkv = a.Hkv;
+    t.wg_per_bkv = a.wg_per_bkv;
+    const int64_t blocks = (t.rows + 15) / 16;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (p.dry_run) return hipSuccess;
+    hipLaunchKernelGGL(attn_tail_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, t);
+    return hipGetLastError();
   }
   if (a.nsplit == 1) return hipSuccess;
   SplitMergeArgs m;
@@ -695,6 +798,36 @@ int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t 
 
 bool packed_wants_split(int64_t N, int64_t T) {
   return N >= 2 * kMinSplitTiles * kTileKeys && 4 * N >= T;
+}
+
+// Tail split of dense encoder-style launches (measured at N = 200000,
+// (4,4): 3128 workgroups over 512 slots, a last round of 56). The
+// workgroups fill rounds of 2 * cus slots; the R whole rounds run unsplit
+// and the r workgroups past them, when they fill at most half a round,
+// run as r * S workgroups of one key range each, S = floor(2 * cus / r)
+// (at most kMaxTailSplit, each range at least kMinSplitTiles tiles):
+// their last round then takes about 1/S of a whole workgroup's time.
+// Equal head groups, bf16, d = 64 only. Returns S (0: no tail split) and
+// the number of tail workgroups.
+int attn_fwd_tail_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, bool causal, int cus, int64_t* units) {
+  *units = 0;
+  if (causal || B <= 0 || N <= 0 || Hkv <= 0 || Hq % Hkv != 0) return 0;
+  const int64_t TB = (N + kRowsPerWave - 1) / kRowsPerWave, NT = (N + kTileKeys - 1) / kTileKeys;
+  const int64_t nwg = (TB * (Hq / Hkv) + kWaves - 1) / kWaves * B * Hkv;
+  const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 256);
+  const int64_t r = nwg % slots;
+  if (nwg < slots || r == 0 || 2 * r > slots) return 0;
+  int64_t S = slots / r;
+  if (S > kMaxTailSplit) S = kMaxTailSplit;
+  while (S > 1 && NT < S * kMinSplitTiles) --S;
+  if (S < 2) return 0;
+  *units = r;
+  return (int)S;
+}
+
+size_t attn_tail_workspace_bytes(int64_t units, int S) {
+  if (units <= 0 || S <= 1) return 0;
+  return (size_t)S * (size_t)units * (kWaves * kRowsPerWave) * (size_t)(D + 2) * sizeof(float);
 }
 
 size_t attn_split_workspace_bytes(int64_t rows, int64_t d, int nsplit) {

@@ -165,6 +165,7 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn_fwd_f32(const AttnProblem& p, hipStream_t stream) {
+  if (p.tail_split > 1 || p.nsplit > 1) return hipErrorInvalidValue;
   // d = 16 (the SQAT-m core: N = 1024, 8 query heads): 16 splits per row put
   // four waves on each SIMD instead of one (40 -> 36 us; 8 and 32: slower)
   if (p.D == 16) return launch_d<16, 16>(p, stream);

@@ -29,6 +29,12 @@ struct AttnProblem {
   // (packed: Hq*T)
   int nsplit = 1;
   float* split_ws = nullptr;
+  // tail split (d = 64, dense encoder-style, equal head groups, nsplit 1):
+  // the last tail_units logical workgroups run as tail_split key ranges
+  // each; tail_ws holds attn_tail_workspace_bytes(tail_units, tail_split)
+  int tail_split = 0;
+  int64_t tail_units = 0;
+  float* tail_ws = nullptr;
   // dry_run: run every check of the launcher (sizes against the 32-bit
   // limits of grids, offsets and buffer descriptors) and launch nothing;
   // hipErrorInvalidValue then means the problem exceeds a launch limit
@@ -42,6 +48,11 @@ size_t attn_split_workspace_bytes(int64_t rows, int64_t d, int nsplit);
 int attn_fwd_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t T, bool causal, int cus,
                          int rows_per_wave);
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream);
+// tail split plan of the d = 64 forward on a device with `cus` CUs: returns
+// the key ranges per tail workgroup (0: none) and the tail workgroups
+constexpr int kMaxTailSplit = 16;
+int attn_fwd_tail_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, bool causal, int cus, int64_t* units);
+size_t attn_tail_workspace_bytes(int64_t units, int S);
 // head dim 64, software-pipelined (attn_fwd_bf16_d64.hip)
 hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream);
 // head dim 128, software-pipelined (attn_fwd_bf16_d128.hip)

@@ -257,6 +257,69 @@ int64_t sqa_attn_fwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N,
   return sqa::attn_fwd_auto_splits(B, H_q, H_kv, N, T, causal != 0, device_cus(), 64);
 }
 
+namespace {
+
+// The tail-split plan for these sizes on the current device (0: none).
+int tail_plan(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype, int causal, int64_t* units) {
+  *units = 0;
+  if (B <= 0 || N <= 0 || H_q < 1 || H_kv < 1 || H_kv > H_q || H_q > 4096 || N > kMaxN) return 0;
+  if (d != 64 || dtype != SQA_BF16 || causal != 0 || !prod_le({B, H_q, N, d}, kMaxElems)) return 0;
+  return sqa::attn_fwd_tail_plan(B, H_q, H_kv, N, false, device_cus(), units);
+}
+
+}  // namespace
+
+int64_t sqa_attn_fwd_tail_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
+                                 int causal) {
+  int64_t units = 0;
+  const int S = tail_plan(B, H_q, H_kv, N, d, dtype, causal, &units);
+  return S > 1 ? S : 1;
+}
+
+size_t sqa_attn_fwd_tail_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dtype,
+                                         int causal) {
+  int64_t units = 0;
+  const int S = tail_plan(B, H_q, H_kv, N, d, dtype, causal, &units);
+  return S > 1 ? round256(sqa::attn_tail_workspace_bytes(units, S)) : 0;
+}
+
+sqa_status sqa_attn_fwd_tail(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H_q,
+                             int64_t H_kv, int64_t N, int64_t d, int dtype, float scale, int causal, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int64_t units = 0;
+  const int S = tail_plan(B, H_q, H_kv, N, d, dtype, causal, &units);
+  if (S <= 1)  // no tail to split: the plain forward (validates everything)
+    return sqa_attn_fwd_split(q, k, v, o, B, H_q, H_kv, N, d, dtype, scale, causal, lse, 1, nullptr, 0, stream);
+  sqa_status s = check_attn(B, H_q, H_kv, N, d, dtype, scale, causal);
+  if (s != SQA_OK) return s;
+  if (!q || !k || !v || !o) return fail(SQA_ERR_NULL, "q, k, v and o must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(SQA_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(SQA_ERR_ALIGN, "lse must be 4-byte aligned");
+  const size_t nq = (size_t)(B * H_q * N * d) * 2, nkv = (size_t)(B * H_kv * N * d) * 2;
+  const size_t nl = lse ? (size_t)(B * H_q * N) * 4 : 0;
+  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
+    return fail(SQA_ERR_ARG, "o overlaps an input");
+  if (lse && (overlaps(lse, nl, o, nq) || overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) ||
+              overlaps(lse, nl, v, nkv)))
+    return fail(SQA_ERR_ARG, "lse overlaps another tensor");
+  const size_t need = sqa::attn_tail_workspace_bytes(units, S);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SQA_ERR_WORKSPACE, "tail workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(SQA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  const void* ts[5] = {q, k, v, o, lse};
+  const size_t tn[5] = {nq, nkv, nkv, nq, nl};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(workspace, need, ts[i], tn[i])) return fail(SQA_ERR_ARG, "workspace overlaps a tensor");
+  sqa::AttnProblem p{q, k, v, o, lse, B, H_q, H_kv, N, d, scale, causal};
+  p.tail_split = S;
+  p.tail_units = units;
+  p.tail_ws = static_cast<float*>(workspace);
+  return launch_attn(p, dtype, static_cast<hipStream_t>(stream));
+}
+
 size_t sqa_attn_fwd_split_workspace_bytes(int64_t rows, int64_t d, int dtype, int64_t num_splits) {
   if (rows <= 0 || rows > kMaxElems || num_splits <= 1 || num_splits > kMaxSplits) return 0;
   if ((d != 16 && d != 32 && d != 64 && d != 128) || dtype != SQA_BF16) return 0;

@@ -104,6 +104,16 @@ void attn_forward() {
   expect(sqa_attn_fwd_varlen(fake(0), fake(1), fake(2), fake(3), ifake(4), 1, 8, 4, int64_t(1) << 24, int64_t(1) << 24,
                              64, SQA_BF16, 0.125f, 0, nullptr, nullptr),
          SQA_ERR_SHAPE, "varlen d=64 launch limit");
+  // tail split (the plan assumes 256 CUs without a device)
+  expect(sqa_attn_fwd_tail(fake(0), fake(1), fake(2), fake(3), 1, 4, 4, 200000, 64, SQA_BF16, 0.125f, 0, nullptr,
+                           nullptr, 0, nullptr),
+         SQA_ERR_WORKSPACE, "tail without workspace");
+  expect(sqa_attn_fwd_tail(fake(0), fake(1), fake(2), fake(3), 1, 4, 4, 200000, 64, SQA_BF16, 0.125f, 0, nullptr,
+                           fake(2), size_t(1) << 30, nullptr),
+         SQA_ERR_ARG, "tail workspace aliases v");
+  expect(sqa_attn_fwd_tail(fake(0), fake(1), fake(2), fake(3), 1, 4, 0, 200000, 64, SQA_BF16, 0.125f, 0, nullptr,
+                           fake(4), size_t(1) << 30, nullptr),
+         SQA_ERR_SHAPE, "tail H_kv = 0");
   expect(sqa_attn_fwd_varlen_split(fake(0), fake(1), fake(2), fake(3), ifake(4), 4, 8, 4, 4096, 2048, 64, SQA_BF16,
                                    0.125f, 0, nullptr, 2, fake(4), size_t(1) << 30, nullptr),
          SQA_ERR_ARG, "varlen split workspace aliases cu");
@@ -191,6 +201,8 @@ void size_queries() {
       acc += sqa_layer_workspace_bytes(a, b, 256, 16, 8, 4, SQA_BF16);
       acc += sqa_block_workspace_bytes(a, b, 256, 16, 8, 4, 768, SQA_BF16);
       acc += (size_t)sqa_attn_fwd_num_splits(a, 8, 4, b, 64, SQA_BF16, 0, 0);
+      acc += (size_t)sqa_attn_fwd_tail_splits(a, 4, 4, b, 64, SQA_BF16, 0);
+      acc += sqa_attn_fwd_tail_workspace_bytes(b, 8, 4, a, 64, SQA_BF16, 0);
       acc += (size_t)sqa_attn_bwd_num_splits(a, 8, 4, b, 64, SQA_BF16, 0, 0);
     }
   std::printf("size queries done (%zu)\n", acc);

@@ -480,3 +480,33 @@ def test_layer_launch_limit_is_a_shape_error(lib):
     st = lib.sqa_layer_fwd(x, wq, wk, wv, wo, y, 1, 1 << 22, 256, 16, 8, 4, 10000.0, 0.25, 1, 1, ws, 1 << 36,
                            None)
     assert st == 2 and "launch limit" in lib.sqa_last_error().decode()
+
+
+# ------------------------------------------------------------- tail split
+@cpu_only
+def test_tail_plan_on_256_cus(lib):
+    # without a device the plan assumes MI355X's 256 CUs: 512 slots
+    assert sqa.sqa_attn_fwd_tail_splits(1, 4, 4, 200000, 64) == 9      # 3128 workgroups: 6 rounds + 56
+    need = lib.sqa_attn_fwd_tail_workspace_bytes(1, 4, 4, 200000, 64, 1, 0)
+    assert need == (9 * 56 * 256 * 66 * 4 + 255) // 256 * 256
+    assert sqa.sqa_attn_fwd_tail_splits(1, 8, 4, 17900, 64) == 10      # 560 workgroups: 1 round + 48
+    assert sqa.sqa_attn_fwd_tail_splits(1, 8, 4, 32768, 64) == 1       # 1024: whole rounds
+    assert sqa.sqa_attn_fwd_tail_splits(1, 16, 16, 200000, 64) == 2    # 12512: 24 rounds + 224
+    assert sqa.sqa_attn_fwd_tail_splits(1, 4, 4, 200000, 64, causal=True) == 1
+    assert sqa.sqa_attn_fwd_tail_splits(1, 4, 4, 200000, 128) == 1
+    assert sqa.sqa_attn_fwd_tail_splits(1, 6, 4, 200000, 64) == 1      # uneven groups
+    assert sqa.sqa_attn_fwd_tail_splits(1, 4, 4, 1000, 64) == 1        # under one round
+    assert lib.sqa_attn_fwd_tail_workspace_bytes(1, 8, 4, 32768, 64, 1, 0) == 0
+
+
+@cpu_only
+def test_tail_rejects_invalid_arguments(lib):
+    q, k, v, o, ws = _spaced(5)
+    f = lib.sqa_attn_fwd_tail
+    assert f(q, k, v, o, 1, 4, 4, 200000, 64, 1, 0.125, 0, None, None, 0, None) == 5        # no workspace
+    assert f(q, k, v, o, 1, 4, 4, 200000, 64, 1, 0.125, 0, None, ws, 1000, None) == 5       # too small
+    assert f(q, k, v, o, 1, 4, 4, 200000, 64, 1, 0.125, 0, None, FAKE + 8, 1 << 30, None) == 4
+    assert f(q, k, v, o, 1, 4, 4, 200000, 64, 1, 0.125, 0, None, k, 1 << 30, None) == 7     # overlaps k
+    assert f(None, k, v, o, 1, 4, 4, 200000, 64, 1, 0.125, 0, None, ws, 1 << 30, None) == 1
+    assert f(q, k, v, o, 1, 4, 0, 200000, 64, 1, 0.125, 0, None, ws, 1 << 30, None) == 2    # no plan: plain checks
+    assert f(q, k, v, o, 1, 4, 4, 200000, 64, 1, float("nan"), 0, None, ws, 1 << 30, None) == 7

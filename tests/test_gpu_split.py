@@ -266,3 +266,55 @@ def test_split_bwd_rejects_causal_and_small_workspace():
     # the library's choice falls back to one range when the given workspace is too small for more
     sqa.sqa_attn_bwd(tq, tk, tv, o, tdo, lse, scale=0.125, workspace=small)
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- tail split
+# Shapes whose workgroups overrun whole rounds of 2 per CU by a small tail
+# on MI355X (256 CUs, 512 slots): N = 36300 (4,4): 568 workgroups, 56 past
+# one round, 9 key ranges each; N = 17900 (8,4): 560, 48 past, 10 ranges;
+# B = 3, N = 11000 (4,2): 516, 4 past, 10 ranges (344 tiles). Ragged last tiles.
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 4, 4, 36300), (1, 8, 4, 17900), (3, 4, 2, 11000)])
+def test_tail_split_all_rows(B, Hq, Hkv, N):
+    S = sqa.sqa_attn_fwd_tail_splits(B, Hq, Hkv, N, 64)
+    if S <= 1:
+        pytest.skip(f"no tail split planned for this shape on this device ({torch.cuda.get_device_name()})")
+    label = f"tail split B={B} ({Hq},{Hkv}) N={N} S={S}"
+    log(f"[case] {label}")
+    q, k, v = draw_attn_case(B, Hq, Hkv, N, 64, "bf16", seed=N + 11)
+    ref, ref_lse = oracle_attention(q, k, v, scale=0.125, causal=False, return_lse=True, threads=oracle_threads())
+    tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o, lse = sqa.sqa_attn_fwd(tq, tk, tv, scale=0.125, return_lse=True, num_splits=1, tail=True)
+    plain = sqa.sqa_attn_fwd(tq, tk, tv, scale=0.125, num_splits=1, tail=False)
+    torch.cuda.synchronize()
+    o = to_host(o)
+    check_global(o, ref, "bf16", label)
+    check_rows(o, ref, label)
+    err = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse)))
+    log(f"[parity] {label} lse max_err={err:.3e}")
+    assert err <= LSE_TOL, f"{label}: lse error {err:.3e}"
+    # the whole units agree with the unsplit call exactly; the tail units up
+    # to the fp32 order of the merge
+    diff = np.abs(o - to_host(plain))
+    log(f"[parity] {label} vs unsplit max diff={float(diff.max()):.3e}")
+    check_global(to_host(plain), ref, "bf16", label + " unsplit")
+
+
+def test_tail_split_is_deterministic_and_reuses_a_dirty_workspace():
+    B, Hq, Hkv, N = 1, 8, 4, 17900
+    if sqa.sqa_attn_fwd_tail_splits(B, Hq, Hkv, N, 64) <= 1:
+        pytest.skip("no tail split planned for this shape on this device")
+    q, k, v = (to_dev(a, "bf16") for a in draw_attn_case(B, Hq, Hkv, N, 64, "bf16", seed=5))
+    lib = sqa.load_library()
+    nbytes = lib.sqa_attn_fwd_tail_workspace_bytes(B, Hq, Hkv, N, 64, sqa.SQA_BF16, 0)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")   # NaN-patterned garbage
+    outs = []
+    for _ in range(3):
+        o = torch.empty_like(q)
+        st = lib.sqa_attn_fwd_tail(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, Hq, Hkv, N, 64,
+                                   sqa.SQA_BF16, 0.125, 0, None, ws.data_ptr(), nbytes,
+                                   torch.cuda.current_stream().cuda_stream)
+        assert st == 0, lib.sqa_last_error()
+        torch.cuda.synchronize()
+        outs.append(o)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+    assert not torch.isnan(outs[0].float()).any().item()
