@@ -189,7 +189,7 @@ MIN_WARMUP_S = 0.5
 CLOCK_WINDOW_S = 2.6
 
 
-def measure(torch, fn, steps, warmup, min_warmup_s=MIN_WARMUP_S, clock_window_s=CLOCK_WINDOW_S):
+def measure(torch, fn, steps, warmup, min_warmup_s=None, clock_window_s=None):
     """Warm up (at least ``warmup`` calls and ``min_warmup_s`` of GPU time,
     each call synchronised so the queue never runs ahead; with a clock
     window, the warm-up lasts at least that long and the graphics clock is
@@ -199,6 +199,10 @@ def measure(torch, fn, steps, warmup, min_warmup_s=MIN_WARMUP_S, clock_window_s=
     (total / steps), median and minimum per-call times in ms, the wall
     time of the timed calls and the clock."""
     stream = torch.cuda.current_stream()
+    if min_warmup_s is None or MIN_WARMUP_S == 0.0:
+        min_warmup_s = MIN_WARMUP_S
+    if clock_window_s is None:
+        clock_window_s = CLOCK_WINDOW_S
     window = clock_window_s if (clock_window_s and CLOCK is not None and CLOCK._handle is not None) else 0.0
     if window:
         CLOCK.start()
@@ -295,9 +299,10 @@ def bench_backward(sqa, torch, q, k, v, w, causal, steps, warmup):
             "tokens_per_s": round(B * N / (ms * 1e-3), 1)}
 
 
-# v_exp_f32: one wave64 instruction per 8 cycles per SIMD (64 exps), 1024
-# SIMDs, 2.4 GHz -- the rate the issue probe measures (bench.py --probe)
-PEAK_EXP_PER_S = 1024 * 8 * 2.4e9
+# v_exp_f32: one wave64 instruction (64 exps) per 10.85 cycles per SIMD --
+# the rate the issue probe measures (bench.py --probe,
+# profiles/issue_probe_forward_mix_d64.md) -- on 1024 SIMDs at 2.4 GHz
+PEAK_EXP_PER_S = 1024 * 64 / 10.85 * 2.4e9
 HBM_BYTES_PER_S = 8.0e12
 
 
@@ -306,7 +311,7 @@ def layer_bound(B, N, D, Hq, Hkv, d, measured_ms):
     kernels, of each kernel's largest single-resource time: the QKV+RoPE and
     output-projection GEMMs by their HBM bytes (inputs read once, outputs
     written once) or bf16 MFMA FLOPs, the causal d = 16 attention by its HBM
-    bytes, its MFMA FLOPs or its exponentials at the v_exp_f32 rate."""
+    bytes, its MFMA FLOPs or its exponentials at the measured v_exp_f32 rate."""
     e = 2  # bf16
     x = B * N * D * e
     qkv = B * N * (Hq + 2 * Hkv) * d * e
@@ -533,6 +538,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="for runs under a profiler: warm up with exactly --warmup calls (no minimum time, no "
+                         "clock window), so that the trace holds only the calls asked for")
     ap.add_argument("--probe", action="store_true",
                     help="only run the issue-rate probes (libsqa_probe.so) and the 32k (8,4) forward; "
                          "print their JSON object")
@@ -568,7 +576,13 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    CLOCK = ClockSampler()
+    if args.profile:
+        global MIN_WARMUP_S, CLOCK_WINDOW_S
+        MIN_WARMUP_S = 0.0
+        CLOCK_WINDOW_S = 0.0
+        CLOCK = None
+    else:
+        CLOCK = ClockSampler()
 
     if args.probe:
         print(json.dumps({"probes": run_probes(torch, sqa)}), flush=True)
