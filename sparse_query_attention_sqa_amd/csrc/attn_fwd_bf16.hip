@@ -108,6 +108,7 @@ struct Args {
   int spread_block;   // rotation block of the spread order
   int exact_per_batch;  // > 0: exact_coords order with this many workgroups per batch
   int pair_major;  // packed encoder-style: pair_major_coords order
+  int snake;       // dense causal: the CU count; dispatch order reversed in every other round of that many
   float c;         // |scale| * log2(e)
   uint32_t qsign;  // 0x80008000 flips both bf16 halves when scale < 0
   int causal;
@@ -386,8 +387,17 @@ __global__ __launch_bounds__(kThreads, QS == 1 ? 4 : 2) void attn_fwd_bf16_kerne
     const int L = x * per + min(x, rem) + i;
     bkv = L / a.wg_per_bkv;
     w_in = L % a.wg_per_bkv;
-  } else {  // longest (largest position block) first
-    const int L = wid;
+  } else {
+    // longest (largest position block) first; within every other full
+    // round of `snake` workgroups the order runs backwards, so that the
+    // CUs that took the longest blocks of one round take the shortest of
+    // the next (measured on the SQAT-m attention, B16 N1024 (8,4) d = 16
+    // causal: 24.1 -> 22.7 us)
+    int L = wid;
+    if (a.snake > 0) {
+      const int r = L / a.snake, c = L % a.snake;
+      if ((r & 1) && (int64_t)(r + 1) * a.snake <= a.nwg) L = r * a.snake + (a.snake - 1 - c);
+    }
     const int wr = L / a.n_bkv;
     bkv = L % a.n_bkv;
     w_in = a.wg_per_bkv - 1 - wr;
@@ -543,8 +553,10 @@ __global__ __launch_bounds__(kThreads, QS == 1 ? 4 : 2) void attn_fwd_bf16_kerne
             w1[e] = pack_bf16x2(acc_o[x][qs][8 + 2 * e] * inv, acc_o[x][qs][8 + 2 * e + 1] * inv);
           }
           uint16_t* dst = a.o + qoff + (size_t)t * D + d0;
-          *reinterpret_cast<u32x4_t*>(dst) = w0;
-          *reinterpret_cast<u32x4_t*>(dst + 8) = w1;
+          // non-temporal: no dirty L2 line left to write back at the end
+          // (SQAT-m attention: 22.8 -> 22.1 us)
+          __builtin_nontemporal_store(w0, reinterpret_cast<u32x4_t*>(dst));
+          __builtin_nontemporal_store(w1, reinterpret_cast<u32x4_t*>(dst + 8));
         }
       }
       if (a.lse != nullptr && lg == 0) {
@@ -588,6 +600,7 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
     nwg = per * p.B;
   }
   a.pair_major = (p.cu_seqlens != nullptr && !p.causal) ? 1 : 0;  // as the d = 64 kernel
+  a.snake = (!p.dry_run && p.causal && !a.spread && a.exact_per_batch == 0 && !a.pair_major) ? device_cus() : 0;
   if (a.pair_major) nwg = pair_major_nwg(a.n_bkv, a.wg_per_bkv);
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
   a.nwg = (int)nwg;

@@ -129,6 +129,124 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kBufferWord3);
 }
 
+// QKV epilogue values of one 32-row block mb of a wave's accumulators
+// (lane row at position t of its sequence, part `part`): wv[x][ab] holds
+// the bf16 pairs of columns x*32 + 8*ab + 4*lg + 0..3 of the segment, with
+// RoPE (rotate-half pairs (c, c + d/2)) applied to Q and K.
+template <int MB>
+__device__ __forceinline__ void qkv_rows(const GemmArgs& a, const f32x16_t (&acc)[2][MB], int mb, uint32_t t,
+                                         int part, int lg, u32x2_t (&wv)[2][4]) {
+  const int64_t d = a.d, half = d / 2;
+  const bool rope = part < 2;
+  // (cos, sin) of the angle t * theta_kp for pair indices
+  // kp = 8*ab + 4*lg + e (mod half) of row t; for d = 16 one group of
+  // four serves all. The angle is formed in revolutions and reduced to
+  // [0, 1) in fp64, so that its rounding error does not grow with t, and
+  // v_cos_f32 / v_sin_f32 take it in revolutions (measured on gfx950:
+  // at most 1.3e-7 absolute error over [0, 1)).
+  float2 cs[4][4];
+  if (rope) {
+#pragma unroll
+    for (int ab = 0; ab < 4; ++ab) {
+      if (d == 16 && ab > 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cs[ab][e] = cs[0][e];
+        continue;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double th = lg ? a.rope_theta[8 * ab + 4 + e] : a.rope_theta[8 * ab + e];
+        const double rev = (double)t * th;
+        const float f = (float)(rev - floor(rev));
+        cs[ab][e] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+      }
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int ab = 0; ab < 4; ++ab) {
+      // column within the head: segments start on a head boundary
+      const int64_t c0 = (x * 32 + 8 * ab + 4 * lg) & (d - 1);
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float xv = acc[x][mb][4 * ab + e];
+        if (!rope) {
+          v[e] = xv;
+          continue;
+        }
+        // the partner column c0 + e -+ d/2 of the same head sits in this
+        // lane: d = 16 -> entry 4*(ab^1) + e of the same slot; d = 64 ->
+        // the same entry of the other slot
+        const float xp = (d == 16) ? acc[x][mb][4 * (ab ^ 1) + e] : acc[x ^ 1][mb][4 * ab + e];
+        const float2 c2 = cs[ab][e];
+        v[e] = (c0 + e < half) ? xv * c2.x - xp * c2.y : xp * c2.y + xv * c2.x;
+      }
+      wv[x][ab][0] = pack_bf16x2(v[0], v[1]);
+      wv[x][ab][1] = pack_bf16x2(v[2], v[3]);
+    }
+}
+
+// Epilogue of one 32-row block mb of a wave's accumulators: lane row m,
+// columns nb + x*32 + 8*(i/4) + 4*lg + i%4 of weight part `part`. EPI_STORE:
+// y [M, ncols] (+ the residual); EPI_QKV: RoPE on Q and K, scatter to
+// [B, H, N, d].
+template <int EPI, int MB>
+__device__ __forceinline__ void store_rows(const GemmArgs& a, const f32x16_t (&acc)[2][MB], int mb, int64_t m, int part,
+                                          int64_t nb, int lg) {
+  if (EPI == EPI_STORE) {
+    const int64_t ncols = a.part[0].ncols;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int ab = 0; ab < 4; ++ab) {
+        const int64_t n = nb + x * 32 + 8 * ab + 4 * lg;
+        if (n >= ncols) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[x][mb][4 * ab + e];
+        if (a.resid != nullptr) {
+          const u32x2_t rv = *reinterpret_cast<const u32x2_t*>(a.resid + m * ncols + n);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t pr = rv[e];
+            v[2 * e] += __builtin_bit_cast(float, pr << 16);
+            v[2 * e + 1] += __builtin_bit_cast(float, pr & 0xffff0000u);
+          }
+        }
+        u32x2_t wv;
+        wv[0] = pack_bf16x2(v[0], v[1]);
+        wv[1] = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<u32x2_t*>(a.y + m * ncols + n) = wv;
+      }
+  } else {  // EPI_QKV: scatter to [B, H, N, d]
+    const int64_t ncols = a.part[part].ncols;
+    const int64_t d = a.d;
+    const uint32_t dsh = (d == 16) ? 4u : 6u;
+    const uint32_t ns = (uint32_t)a.Nseq;
+    const uint32_t b = (uint32_t)m / ns, t = (uint32_t)m - b * ns;
+    const int64_t nheads = (part == 0) ? a.Hq : a.Hkv;
+    // element offset of (b, head 0, t, 0); a head adds N*d
+    uint16_t* dst_bt = a.qkv[part] + ((int64_t)b * nheads * ns + t) * d;
+    const uint32_t head_stride = ns * (uint32_t)d;
+    u32x2_t wv[2][4];
+    qkv_rows<MB>(a, acc, mb, t, part, lg, wv);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int ab = 0; ab < 4; ++ab) {
+        const int64_t n = nb + x * 32 + 8 * ab + 4 * lg;
+        if (n >= ncols) continue;
+        const int64_t head = n >> dsh, c0 = n & (d - 1);
+        // non-temporal: the projections end by writing back every dirty L2
+        // line, which this skips (SQAT-m layer QKV projection: 11.0 -> 9.4
+        // us; staging through LDS for whole-line stores measured 10.8)
+        __builtin_nontemporal_store(wv[x][ab], reinterpret_cast<u32x2_t*>(dst_bt + (uint32_t)head * head_stride + (uint32_t)c0));
+      }
+  }
+}
+
 template <int EPI, int S, bool GATHER, int MB>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
   static_assert(S >= 2 && S <= 4, "2 to 4 stages");
@@ -326,96 +444,181 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
         wv[1] = pack_bf16x2(h[2], h[3]);
         *reinterpret_cast<u32x2_t*>(a.y + m * F + n) = wv;
       }
-    } else if (EPI == EPI_STORE) {
-      const int64_t ncols = a.part[0].ncols;
-      const int64_t nb = wn ? wc1 : wc0;
+    } else {
+      const int part = (EPI == EPI_QKV) ? (wn ? sp1 : sp0) : 0;
+      store_rows<EPI, MB>(a, acc, mb, m, part, wn ? wc1 : wc0, lg);
+    }
+  }
+}
+
+// Short reductions (K <= 256) over at most four 64-column segments with the
+// store epilogue -- the SQAT-m output projection: a workgroup takes 64 rows
+// and every segment, so A is read once, and holds the whole reduction in LDS
+// (up to four 40 KB chunks), so every DMA is issued at the start and waited
+// for once instead of chunk after chunk; one workgroup per CU. Wave w owns
+// segment w: 64 rows (two 32-row blocks) x 64 columns (two 32-column slots).
+// (The QKV projection ran slower this way, 11.2 against 10.2 us, and keeps
+// the staged kernel.)
+constexpr int kWideChunkBytes = 10 * kTileBytes;  // A [2][32 m][64 k], W [kh 2][seg 4][32 k][64 n]
+constexpr int kWideMaxChunks = 4;
+
+template <int EPI, bool GATHER>
+__global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWideMaxChunks * kWideChunkBytes];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lg = lane >> 5, l32 = lane & 31;
+  const int64_t m0 = (int64_t)blockIdx.x * 64;
+  const ARows& A = a.A;
+  const int64_t K = A.K;
+  const int nk = (int)((K + TK - 1) / TK);
+
+  // segment `wave`: weight part and first column (past the part's width
+  // when the parts have fewer than four segments: all masked)
+  int part = 0;
+  int64_t col0;
+  {
+    int g = wave;
+    while (part < a.nparts - 1 && g >= a.segs[part]) g -= a.segs[part++];
+    col0 = (int64_t)g * 64;
+  }
+  const WPart wp = a.part[part];
+  const __amdgpu_buffer_rsrc_t ra = rsrc(A.p, A.M * A.K * 2);
+  const __amdgpu_buffer_rsrc_t rw = rsrc(wp.w, K * wp.ncols * 2);
+
+  // DMA lanes: A parts 2*(wave&1)+j (8 rows each) of A tile wave>>1, and the
+  // four 8-row parts of W tiles (kh, segment wave), kh = 0, 1
+  const int r8 = lane >> 3, s = lane & 7;
+  const uint32_t dshift = GATHER ? (uint32_t)__builtin_ctzll((unsigned long long)A.d) : 0u;
+  const int atile = wave >> 1;
+  uint32_t a_base[2], a_k[2];
+  bool a_ok[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = (2 * (wave & 1) + j) * 8 + r8;
+    const int64_t m = m0 + atile * kTileRows + r;
+    a_ok[j] = m < A.M;
+    a_base[j] = a_ok[j] ? a_row_base<GATHER>(A, (uint32_t)m) : 0u;
+    a_k[j] = 8u * (uint32_t)(s ^ swz_k(r));
+  }
+  const uint32_t wncols = (uint32_t)wp.ncols;
+  uint32_t w_col[4];
+  bool w_ok[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = q * 8 + r8;
+    const int64_t col = col0 + 8 * (s ^ swz_v(r));
+    w_ok[q] = col < wp.ncols;
+    w_col[q] = (uint32_t)col;
+  }
+  for (int kc = 0; kc < nk; ++kc) {
+    uint8_t* stage = lds + kc * kWideChunkBytes;
+    const uint32_t k32 = (uint32_t)(kc * TK);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t off = a_offset<GATHER>(A, a_base[j], a_ok[j], k32 + a_k[j], dshift);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(stage + atile * kTileBytes + (2 * (wave & 1) + j) * 1024),
+                                               16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t k = k32 + (uint32_t)(kh * kTileRows + q * 8 + r8);
+        const uint32_t off = (w_ok[q] && k < (uint32_t)K) ? (k * wncols + w_col[q]) * 2u : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rw, (lds_void_t*)(stage + (2 + kh * 4 + wave) * kTileBytes + q * 1024), 16, off, 0, 0, 0);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): every chunk landed
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  uint32_t boff[2][2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      boff[kh][hh] = (uint32_t)(l32 * kRowBytes + (((kh * 4 + lg * 2 + hh) ^ swz_k(l32)) * 16));
+  const ReadOffsets ro = read_offsets(lane);
+  f32x16_t acc[2][2];  // [slot x][row block mb]
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) acc[x][mb] = zero16();
+  for (int kc = 0; kc < nk; ++kc) {
+    const uint8_t* stage = lds + kc * kWideChunkBytes;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const uint8_t* wt = stage + (2 + kh * 4 + wave) * kTileBytes;
+      u32x4_t wf[2][2];  // [slot][hh]
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint8_t* q = wt + ro.tr[x] + hh * 8 * kRowBytes;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)q);
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(q + 4 * kRowBytes));
+          const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+          wf[x][hh] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+        }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const u32x4_t af = *reinterpret_cast<const u32x4_t*>(stage + mb * kTileBytes + boff[kh][hh]);
+#pragma unroll
+          for (int x = 0; x < 2; ++x) acc[x][mb] = mfma(wf[x][hh], af, acc[x][mb]);
+        }
+    }
+  }
+  if constexpr (EPI == EPI_STORE) {
+    // Coalesced store: every wave writes its 64 x 64 block to LDS as bf16
+    // (rows of 128 B, 16-byte chunks XOR-swizzled by the row), then the
+    // workgroup writes whole 512-byte rows of y, 16 bytes per lane, adding
+    // the residual there, with non-temporal stores. SQAT-m output
+    // projection: 7.3 us with 8-byte stores, one row per lane; 6.2 staged;
+    // 5.7 staged and non-temporal (8-byte non-temporal stores: 14.4).
+    const int64_t ncols = a.part[0].ncols;
+    __syncthreads();  // every wave is done reading the reduction chunks
+    uint8_t* blk = lds + wave * 8192;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int ab = 0; ab < 4; ++ab) {
-          const int64_t n = nb + x * 32 + 8 * ab + 4 * lg;
-          if (n >= ncols) continue;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[x][mb][4 * ab + e];
-          if (a.resid != nullptr) {
-            const u32x2_t rv = *reinterpret_cast<const u32x2_t*>(a.resid + m * ncols + n);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const uint32_t pr = rv[e];
-              v[2 * e] += __builtin_bit_cast(float, pr << 16);
-              v[2 * e + 1] += __builtin_bit_cast(float, pr & 0xffff0000u);
-            }
-          }
+          const int r = mb * 32 + l32, c = x * 32 + 8 * ab + 4 * lg;  // 4 columns c..c+3
           u32x2_t wv;
-          wv[0] = pack_bf16x2(v[0], v[1]);
-          wv[1] = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2_t*>(a.y + m * ncols + n) = wv;
+          wv[0] = pack_bf16x2(acc[x][mb][4 * ab], acc[x][mb][4 * ab + 1]);
+          wv[1] = pack_bf16x2(acc[x][mb][4 * ab + 2], acc[x][mb][4 * ab + 3]);
+          *reinterpret_cast<u32x2_t*>(blk + r * 128 + (((c >> 3) ^ (r & 7)) << 4) + (c & 7) * 2) = wv;
         }
-    } else {  // EPI_QKV: RoPE on Q and K (rotate-half pairs (c, c + d/2)), scatter to [B, H, N, d]
-      const int part = wn ? sp1 : sp0;
-      const int64_t nb = wn ? wc1 : wc0;
-      const int64_t ncols = a.part[part].ncols;
-      const int64_t d = a.d, half = d / 2;
-      const uint32_t dsh = (d == 16) ? 4u : 6u;
-      const uint32_t ns = (uint32_t)a.Nseq;
-      const uint32_t b = (uint32_t)m / ns, t = (uint32_t)m - b * ns;
-      const int64_t nheads = (part == 0) ? a.Hq : a.Hkv;
-      // element offset of (b, head 0, t, 0); a head adds N*d
-      uint16_t* dst_bt = a.qkv[part] + ((int64_t)b * nheads * ns + t) * d;
-      const uint32_t head_stride = ns * (uint32_t)d;
-      const bool rope = part < 2;
-      // (cos, sin) of the angle t * theta_kp for pair indices
-      // kp = 8*ab + 4*lg + e (mod half) of row t; for d = 16 one group of
-      // four serves all. The angle is formed in revolutions and reduced to
-      // [0, 1) in fp64, so that its rounding error does not grow with t, and
-      // v_cos_f32 / v_sin_f32 take it in revolutions (measured on gfx950:
-      // at most 1.3e-7 absolute error over [0, 1)).
-      float2 cs[4][4];
-      if (rope) {
+    __syncthreads();
+    // 64 rows x (4 waves x 8 chunks): thread -> (row, chunk), 8 rows per pass
 #pragma unroll
-        for (int ab = 0; ab < 4; ++ab) {
-          if (d == 16 && ab > 0) {
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 8 + (tid >> 5), cg = tid & 31;  // cg: 16-byte chunk of the 256-column row
+      const int w = cg >> 3, ch = cg & 7;
+      const int64_t m = m0 + r, n = (int64_t)cg * 8;
+      if (m >= A.M || n >= ncols) continue;
+      u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + w * 8192 + r * 128 + ((ch ^ (r & 7)) << 4));
+      if (a.resid != nullptr) {
+        const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(a.resid + m * ncols + n);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) cs[ab][e] = cs[0][e];
-            continue;
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const double th = lg ? a.rope_theta[8 * ab + 4 + e] : a.rope_theta[8 * ab + e];
-            const double rev = (double)t * th;
-            const float f = (float)(rev - floor(rev));
-            cs[ab][e] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
-          }
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __builtin_bit_cast(float, v[e] << 16) + __builtin_bit_cast(float, rv[e] << 16);
+          const float hi = __builtin_bit_cast(float, v[e] & 0xffff0000u) + __builtin_bit_cast(float, rv[e] & 0xffff0000u);
+          v[e] = pack_bf16x2(lo, hi);
         }
       }
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(a.y + m * ncols + n));
+    }
+  } else {
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int ab = 0; ab < 4; ++ab) {
-          const int64_t n = nb + x * 32 + 8 * ab + 4 * lg;
-          if (n >= ncols) continue;
-          const int64_t head = n >> dsh, c0 = n & (d - 1);
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float xv = acc[x][mb][4 * ab + e];
-            if (!rope) {
-              v[e] = xv;
-              continue;
-            }
-            // the partner column c0 + e -+ d/2 of the same head sits in this
-            // lane: d = 16 -> entry 4*(ab^1) + e of the same slot; d = 64 ->
-            // the same entry of the other slot
-            const float xp = (d == 16) ? acc[x][mb][4 * (ab ^ 1) + e] : acc[x ^ 1][mb][4 * ab + e];
-            const float2 c2 = cs[ab][e];
-            v[e] = (c0 + e < half) ? xv * c2.x - xp * c2.y : xp * c2.y + xv * c2.x;
-          }
-          u32x2_t wv;
-          wv[0] = pack_bf16x2(v[0], v[1]);
-          wv[1] = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2_t*>(dst_bt + (uint32_t)head * head_stride + (uint32_t)c0) = wv;
-        }
+    for (int mb = 0; mb < 2; ++mb) {
+      const int64_t m = m0 + mb * 32 + l32;
+      if (m < A.M) store_rows<EPI, 2>(a, acc, mb, m, part, col0, lg);
     }
   }
 }
@@ -444,8 +647,21 @@ hipError_t launch_stages(const GemmArgs& a, hipStream_t stream, bool dry_run) {
   return launch_grid<EPI, 2, GATHER, 2>(a, stream, dry_run);
 }
 
+template <int EPI, bool GATHER>
+hipError_t launch_wide(const GemmArgs& a, hipStream_t stream, bool dry_run) {
+  const int64_t nblk = (a.A.M + 63) / 64;
+  if (nblk > 0x7fffffff || nblk <= 0) return hipErrorInvalidValue;
+  if (dry_run) return hipSuccess;
+  hipLaunchKernelGGL((gemm_wide_kernel<EPI, GATHER>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch(const GemmArgs& a, int epi, hipStream_t stream, bool dry_run) {
   if (a.tiles_total <= 0 || a.A.M <= 0) return hipErrorInvalidValue;
+  // short reductions over at most four segments, store epilogue: the wide
+  // kernel (SQAT-m output projection, B16 N1024 D256: 7.3 -> 5.7 us)
+  if (epi == EPI_STORE && a.A.K <= (int64_t)kWideMaxChunks * TK && a.segs_total <= 4)
+    return a.A.gather ? launch_wide<EPI_STORE, true>(a, stream, dry_run) : launch_wide<EPI_STORE, false>(a, stream, dry_run);
   if (epi == EPI_STORE)
     return a.A.gather ? launch_stages<EPI_STORE, true>(a, stream, dry_run)
                       : launch_stages<EPI_STORE, false>(a, stream, dry_run);

@@ -100,6 +100,10 @@ hipError_t launch_attn_bwd_bf16(const BwdProblem& p, hipStream_t stream);
 constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
 hipError_t noalloc_scratch(void** ptr);
 
+// Compute units of the current device (256 if the query fails), cached per
+// device ordinal.
+int device_cus();
+
 // Projection + RoPE: x [M=B*N, Dm] bf16 times w_q [Dm,Hq*d] | w_k [Dm,Hkv*d] |
 // w_v [Dm,Hkv*d]; writes q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16 with RoPE applied
 // to q and k.

@@ -135,6 +135,10 @@ sqa_status check_split_workspace(int64_t num_splits, int64_t rows, int64_t d, co
   return SQA_OK;
 }
 
+}  // namespace
+
+namespace sqa {
+
 // Compute units of the current device (256, MI355X's count, if the query
 // fails), cached per device ordinal; concurrent first calls store the same
 // value.
@@ -152,7 +156,7 @@ int device_cus() {
   return cus;
 }
 
-}  // namespace
+}  // namespace sqa
 
 extern "C" {
 
@@ -254,7 +258,7 @@ int64_t sqa_attn_fwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N,
   // workgroups); d = 16/32: slower under a causal mask. Splits there run on
   // request only.
   if (d != 64 || dtype != SQA_BF16) return 1;
-  return sqa::attn_fwd_auto_splits(B, H_q, H_kv, N, T, causal != 0, device_cus(), 64);
+  return sqa::attn_fwd_auto_splits(B, H_q, H_kv, N, T, causal != 0, sqa::device_cus(), 64);
 }
 
 namespace {
@@ -264,7 +268,7 @@ int tail_plan(int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t d, int dt
   *units = 0;
   if (B <= 0 || N <= 0 || H_q < 1 || H_kv < 1 || H_kv > H_q || H_q > 4096 || N > kMaxN) return 0;
   if (d != 64 || dtype != SQA_BF16 || causal != 0 || !prod_le({B, H_q, N, d}, kMaxElems)) return 0;
-  return sqa::attn_fwd_tail_plan(B, H_q, H_kv, N, false, device_cus(), units);
+  return sqa::attn_fwd_tail_plan(B, H_q, H_kv, N, false, sqa::device_cus(), units);
 }
 
 }  // namespace
@@ -475,7 +479,7 @@ int64_t sqa_attn_bwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N,
   if (T > 0 && N > T) return 1;
   if (!prod_le({B, H_q, N, d > 0 ? d : 1}, kMaxElems) || !prod_le({T, H_q, d > 0 ? d : 1}, kMaxElems)) return 1;
   if ((d != 64 && d != 128) || dtype != SQA_BF16) return 1;
-  return sqa::attn_bwd_auto_splits(B, H_q, H_kv, N, T, d, causal != 0, device_cus());
+  return sqa::attn_bwd_auto_splits(B, H_q, H_kv, N, T, d, causal != 0, sqa::device_cus());
 }
 
 sqa_status sqa_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
