@@ -532,8 +532,10 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dkdv_kernel(KvAr
 
 // ------------------------------------------------------------------ dQ
 // Software-pipelined over 32-key tiles j (one stage, as the forward):
-//   phase j: MFMA  dQ^T += K(j-1)^T dS(j-1)^T  and  S^T(j+1), dP^T(j+1)
+//   phase j: MFMA  dQ^T += K(j-1)^T dS(j-1)^T  and  S^T(j+1), dP^T(j+1) - D
 //            VALU  P(j) = 2^(s c - lse2), dS(j) = P (dP - D)
+// (the dP^T accumulator starts from -D, the row's D in every entry, which
+// saves the subtraction per score)
 // The fragments the next phase multiplies (K and V rows of tile j+2, the
 // transposed K of tile j) are read from LDS during this phase.
 constexpr int kDqBuf = 5;  // ring slots
@@ -591,6 +593,7 @@ struct DqState {
   f32x16_t sc[2], dp[2];         // S^T and dP^T of tiles j (index j & 1) and j+1
   u32x4_t dsk[2][2];             // dS of tiles j-1 and j, packed as B operands
   float lse2, dd;
+  f32x16_t ndd;                  // -D in every entry: dP^T starts from it, so dS = P dP^T
 };
 
 template <int DH, int SLOT>
@@ -619,8 +622,9 @@ __device__ __forceinline__ void dq_read_rows(const uint8_t* slot, const ReadOffs
 }
 
 template <int DH>
-__device__ __forceinline__ f32x16_t mfma_regs(const u32x4_t (&a)[DH][4], const u32x4_t (&b)[DH][4]) {
-  f32x16_t acc = zero16();
+__device__ __forceinline__ f32x16_t mfma_regs(const u32x4_t (&a)[DH][4], const u32x4_t (&b)[DH][4],
+                                             const f32x16_t& init) {
+  f32x16_t acc = init;
 #pragma unroll
   for (int h = 0; h < DH; ++h)
 #pragma unroll
@@ -663,14 +667,14 @@ __device__ __forceinline__ void dq_phase(const DqCtx& cx, DqState<DH>& w, int j)
   for (int h = 0; h < DH; ++h) mfma_tr(w.kt[h], w.dsk[P ^ 1], w.acc[h]);  // dQ^T += K(j-1)^T dS(j-1)^T
 #pragma unroll
   for (int h = 0; h < DH; ++h) read_tr(cx.ring.p[SLOT] + C::kKt + h * kTileBytes, cx.ro, w.kt[h]);  // K(j)^T
-  w.sc[P ^ 1] = mfma_regs<DH>(w.kr, w.qf);  // S^T(j+1)
-  w.dp[P ^ 1] = mfma_regs<DH>(w.vr, w.df);  // dP^T(j+1)
+  w.sc[P ^ 1] = mfma_regs<DH>(w.kr, w.qf, zero16());  // S^T(j+1)
+  w.dp[P ^ 1] = mfma_regs<DH>(w.vr, w.df, w.ndd);  // dP^T(j+1) - D
   dq_read_rows<DH>(cx.ring.p[NEXT2], cx.ro, w);  // K(j+2), V(j+2)
 
   f32x16_t ds;
 #pragma unroll
   for (int e = 0; e < 16; ++e)
-    ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(w.sc[P][e], cx.c, -w.lse2)) * (w.dp[P][e] - w.dd);
+    ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(w.sc[P][e], cx.c, -w.lse2)) * w.dp[P][e];
   pack_pairs(ds, w.dsk[P]);
   dq_interleave<DH>();
 }
@@ -763,6 +767,8 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dq_kernel(DqArgs
     w.dd = r.y;
   }
 #pragma unroll
+  for (int e = 0; e < 16; ++e) w.ndd[e] = -w.dd;
+#pragma unroll
   for (int hh = 0; hh < DH; ++hh) {
     w.acc[hh][0] = zero16();
     w.acc[hh][1] = zero16();
@@ -792,8 +798,8 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dq_kernel(DqArgs
   dq_issue<DH, 3>(cx, 3);
   barrier_vm<C::kDma>();
   dq_read_rows<DH>(ring0, cx.ro, w);
-  w.sc[0] = mfma_regs<DH>(w.kr, w.qf);
-  w.dp[0] = mfma_regs<DH>(w.vr, w.df);
+  w.sc[0] = mfma_regs<DH>(w.kr, w.qf, zero16());
+  w.dp[0] = mfma_regs<DH>(w.vr, w.df, w.ndd);
   dq_read_rows<DH>(ring1, cx.ro, w);
 
   // whole ten-phase rounds first (ring slot period 5, register parity 2)
