@@ -30,7 +30,9 @@
  *   - N (or max_seqlen) <= 2^30 and every tensor <= 2^40 elements.
  *   - bf16 attention with d = 64: N <= 16777215 (one head's K or V rows,
  *     N * 128 bytes, must stay below 2^31, the range of a buffer
- *     descriptor); d = 128: N <= 8388607. The backward has the same limits.
+ *     descriptor); d = 128: N <= 8388607. The backward has the same limits,
+ *     and its row terms (B * H_q * N rounded up to whole 32-row tiles per
+ *     head; packed: H_q * (T + 32)) must stay below 2^29 - 64 rows.
  *   - Grid sizes: B * H_kv, B * H_q and every kernel's workgroup count must
  *     stay below 2^31.
  *   - Layer and block: the activations [B*N, D] and every weight matrix

@@ -12,7 +12,10 @@
 // with c = scale*log2 e.
 //
 // Three kernels, all on the caller's stream:
-//   1. bwd_rowterms_kernel: (lse*log2 e, D) per query row into the workspace.
+//   1. bwd_rowterms_kernel: per query row, -lse*log2(e)/c and -D into two
+//      planes of the workspace; the other kernels start their S and dP
+//      MFMA chains from them (S' = S - lse log2(e)/c, dP' = dP - D), so that
+//      P = 2^(c S') and dS = P dP' take one VALU operation per score fewer.
 //   2. bwd_dkdv_kernel (K/V-stationary): a wave holds 32 keys of one K/V head
 //      (K and V as MFMA B operands in registers) and streams every query tile
 //      of every query head of the group through LDS: S = Q K^T and
@@ -82,15 +85,17 @@ struct RowArgs {
   const uint16_t* o;
   const uint16_t* dout;
   const float* lse;
-  float2* rt;   // [B*H_q, Np]: every head's rows padded to Np, a multiple of 32
+  float* rt;    // plane 0 [B*H_q, Np]: -lse log2(e)/c; plane 1 (nrows floats later): -D.
+                // Every head's rows are padded to Np, a multiple of 32
   int64_t nrows;  // B*H_q*Np
   int N, Np;
+  float inv_c;    // 1/c
 };
 
 // Eight lanes per query row: each forms the products of 8*DH bf16 pairs
 // exactly (v_dot2_f32_bf16) and the eight partial sums are added with lane
-// shuffles. Padding rows (t >= N) get (0, 0), so row-term tiles are always
-// whole.
+// shuffles. Padding rows (t >= N) get 0 in both planes, so row-term tiles
+// are always whole.
 template <int DH>
 __global__ __launch_bounds__(256) void bwd_rowterms_kernel(RowArgs a) {
   constexpr int D = Dims<DH>::D;
@@ -119,7 +124,10 @@ __global__ __launch_bounds__(256) void bwd_rowterms_kernel(RowArgs a) {
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 4);
-  if (prow < a.nrows && part == 0) a.rt[prow] = valid ? make_float2(a.lse[row] * kLog2e, acc) : make_float2(0.f, 0.f);
+  if (prow < a.nrows && part == 0) {
+    a.rt[prow] = valid ? -(a.lse[row] * kLog2e) * a.inv_c : 0.f;
+    a.rt[a.nrows + prow] = valid ? -acc : 0.f;
+  }
 }
 
 // Workgroup -> (b*H_kv + K/V head, index w_in within that head).
@@ -172,10 +180,11 @@ __device__ __forceinline__ void store_tr_row_f32(float* row, const f32x16_t (&o)
     }
 }
 
-// acc (+)= sum over the DH halves of A_rows(h) . B(h).
+// init + sum over the DH halves of A_rows(h) . B(h).
 template <int DH>
-__device__ __forceinline__ f32x16_t mfma_rows(const uint8_t* tile0, const ReadOffsets& ro, const u32x4_t (&b)[DH][4]) {
-  f32x16_t acc = zero16();
+__device__ __forceinline__ f32x16_t mfma_rows(const uint8_t* tile0, const ReadOffsets& ro, const u32x4_t (&b)[DH][4],
+                                              const f32x16_t& init) {
+  f32x16_t acc = init;
 #pragma unroll
   for (int h = 0; h < DH; ++h) {
     u32x4_t a[4];
@@ -189,12 +198,15 @@ __device__ __forceinline__ f32x16_t mfma_rows(const uint8_t* tile0, const ReadOf
 // ------------------------------------------------------------------ dK, dV
 // A step s is one 32-row query tile of one query head of the group (steps
 // ordered by query tile, then head). Software-pipelined over steps:
-//   phase s: MFMA  dV^T += dO(s-1)^T P(s-1), dK^T += Q(s-1)^T dS(s-1),
+//   phase s: MFMA  dV^T += dO(s-1)^T P(s-1), dK^T += Q(s-1)^T dS(s-1), from
+//                  transposed fragments read into registers in phase s-1,
 //                  interleaved with
-//            VALU  P(s) = 2^(s c - lse2), dS(s) = P (dP - D);
-//            then MFMA S(s+1) = Q K^T, dP(s+1) = dO V^T into the registers
-//            the softmax has just consumed (one score buffer keeps the d = 64
-//            wave at two waves per SIMD).
+//            VALU  P(s) = 2^(c S'), dS(s) = P dP' (S' and dP' started from
+//                  the row terms);
+//            LDS   the transposed Q and dO fragments of step s for phase s+1;
+//            then MFMA S'(s+1), dP'(s+1) into the registers the softmax has
+//            just consumed (one score buffer keeps the d = 64 wave at two
+//            waves per SIMD: 249 VGPRs).
 // Q and dO of a step sit in LDS once each, in the shared layout of
 // bf16_tiles.h (row reads for S and dP, transposed reads for dK and dV); six
 // ring slots give four steps of lookahead.
@@ -214,7 +226,8 @@ struct KvArgs {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float2* rt;  // row terms, [B*H_q, Np]
+  const float* rt;   // row terms, plane 0 [B*H_q, Np] (-lse log2(e)/c), plane 1 rt_plane floats later (-D)
+  int64_t rt_plane;
   uint16_t* dk;
   uint16_t* dv;
   const int* cu;  // packed sequence offsets (nullptr: dense)
@@ -239,8 +252,9 @@ struct KvCtx {
   KvRing ring;
   const uint16_t* q;     // Q of sequence b, head 0
   const uint16_t* dout;  // dO of sequence b, head 0
-  const float2* rt;      // row terms of sequence b, head 0
+  const float* rt;       // row terms of sequence b, head 0 (plane 0)
   int64_t stride, rt_stride;  // rows between heads of Q/dO and of the row terms
+  uint32_t rt_plane_bytes;    // from plane 0 to plane 1
   int N, g, h0, qt0, kb, causal, wave, first;  // N: this sequence; first: the first step this wave computes
   float c;
   float masked;  // score whose exponent s*c is -inf: -inf * sign(c)
@@ -254,6 +268,7 @@ struct KvState {
   f32x16_t acc_k[DH][2], acc_v[DH][2];  // dK^T, dV^T
   f32x16_t sc, dp;                      // S and dP of the current step
   u32x4_t pk[2][2], dsk[2][2];          // P and dS of steps s-1 and s, packed as B operands
+  u32x4_t qt_f[DH][2][2], dt_f[DH][2][2];  // transposed Q and dO fragments of the step whose dK/dV come next
 };
 
 // DMA step s (query tile qt of query head h0 + i) into ring slot SLOT.
@@ -265,7 +280,7 @@ __device__ __forceinline__ void kv_issue(const KvCtx& cx, int s) {
   const size_t head = (size_t)(cx.h0 + i) * cx.stride;
   const int row0 = qt * kTileRows;
   uint8_t* slot = cx.ring.p[SLOT];
-  const float2* rb = cx.rt + (size_t)(cx.h0 + i) * cx.rt_stride;
+  const float* rb = cx.rt + (size_t)(cx.h0 + i) * cx.rt_stride;
 #pragma unroll
   for (int h = 0; h < DH; ++h) {
     dma_tile_part<RB>(cx.q + head * Dims<DH>::D, row0, cx.N, slot + C::kQ + h * kTileBytes + cx.wave * 1024,
@@ -273,36 +288,59 @@ __device__ __forceinline__ void kv_issue(const KvCtx& cx, int s) {
     dma_tile_part<RB>(cx.dout + head * Dims<DH>::D, row0, cx.N, slot + C::kDo + h * kTileBytes + cx.wave * 1024,
                       cx.off + h * kRowBytes);
   }
-  // row terms of the 32 rows (8 B each; whole tiles stay inside the buffer
-  // thanks to its padding) land in the first 256 B of the area; every wave
-  // writes the same bytes (lanes past 16 write zeros beyond them)
-  const int rem = row0 < cx.N ? kTileRows * 8 : 0;
+  // row terms of the 32 rows (whole tiles stay inside the planes thanks to
+  // their padding) land in the first 256 B of the area: lanes 0-7 bring
+  // plane 0's 128 B, lanes 8-15 plane 1's; every wave writes the same bytes
+  // (lanes past 16 are out of range and write zeros beyond them)
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t roff = lane < 8 ? lane * 16u : (lane < 16 ? cx.rt_plane_bytes + (lane - 8) * 16u : 0x80000000u);
+  const int rem = row0 < cx.N ? (int)cx.rt_plane_bytes + kTileRows * 4 : 0;
   __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void*)(rb + row0), (short)0, rem, kBufferWord3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + C::kRt), 16, (uint32_t)(threadIdx.x & 63) * 16,
-                                           0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + C::kRt), 16, roff, 0, 0, 0);
 }
 
-// S and dP of the step in slot SLOT.
+// S' = S - lse log2(e)/c and dP' = dP - D of the step in slot SLOT: the
+// chains start from the step's row terms (entry e <-> query row lg*16 + e).
 template <int DH, int SLOT>
 __device__ __forceinline__ void kv_scores(const KvCtx& cx, KvState<DH>& w) {
   using C = KvCfg<DH>;
-  w.sc = mfma_rows<DH>(cx.ring.p[SLOT] + C::kQ, cx.ro, w.kb_f);
-  w.dp = mfma_rows<DH>(cx.ring.p[SLOT] + C::kDo, cx.ro, w.vb_f);
+  const int lg = (threadIdx.x & 63) >> 5;
+  const f32x4_t* r0 = reinterpret_cast<const f32x4_t*>(cx.ring.p[SLOT] + C::kRt + lg * 64);
+  const f32x4_t* r1 = reinterpret_cast<const f32x4_t*>(cx.ring.p[SLOT] + C::kRt + 128 + lg * 64);
+  f32x16_t i0, i1;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4_t a = r0[q], b = r1[q];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      i0[4 * q + e] = a[e];
+      i1[4 * q + e] = b[e];
+    }
+  }
+  w.sc = mfma_rows<DH>(cx.ring.p[SLOT] + C::kQ, cx.ro, w.kb_f, i0);
+  w.dp = mfma_rows<DH>(cx.ring.p[SLOT] + C::kDo, cx.ro, w.vb_f, i1);
 }
 
-// dV^T += dO^T P and dK^T += Q^T dS for the step in `slot`.
+// dV^T += dO^T P and dK^T += Q^T dS of the step whose transposed fragments
+// sit in w.qt_f / w.dt_f.
 template <int DH>
-__device__ __forceinline__ void kv_grads(const uint8_t* slot, const ReadOffsets& ro, const u32x4_t (&pk)[2],
-                                         const u32x4_t (&dsk)[2], KvState<DH>& w) {
+__device__ __forceinline__ void kv_grads(const u32x4_t (&pk)[2], const u32x4_t (&dsk)[2], KvState<DH>& w) {
+#pragma unroll
+  for (int h = 0; h < DH; ++h) {
+    mfma_tr(w.dt_f[h], pk, w.acc_v[h]);
+    mfma_tr(w.qt_f[h], dsk, w.acc_k[h]);
+  }
+}
+
+// Transposed Q and dO fragments of the step in `slot`, for the next phase.
+template <int DH>
+__device__ __forceinline__ void kv_read_tr(const uint8_t* slot, const ReadOffsets& ro, KvState<DH>& w) {
   using C = KvCfg<DH>;
 #pragma unroll
   for (int h = 0; h < DH; ++h) {
-    u32x4_t qt_f[2][2], dt_f[2][2];
-    read_tr_shared(slot + C::kQ + h * kTileBytes, ro, qt_f);
-    read_tr_shared(slot + C::kDo + h * kTileBytes, ro, dt_f);
-    mfma_tr(dt_f, pk, w.acc_v[h]);
-    mfma_tr(qt_f, dsk, w.acc_k[h]);
+    read_tr_shared(slot + C::kQ + h * kTileBytes, ro, w.qt_f[h]);
+    read_tr_shared(slot + C::kDo + h * kTileBytes, ro, w.dt_f[h]);
   }
 }
 
@@ -340,21 +378,14 @@ __device__ __forceinline__ void kv_phase(const KvCtx& cx, KvState<DH>& w, int s)
     for (int e = 0; e < 16; ++e)
       if (lg * 16 + e < l32) w.sc[e] = cx.masked;
   }
-  float2 rt[16];
-  const float4* rtp = reinterpret_cast<const float4*>(cx.ring.p[SLOT] + C::kRt + lg * 128);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float4 x = rtp[e];
-    rt[2 * e] = make_float2(x.x, x.y);
-    rt[2 * e + 1] = make_float2(x.z, x.w);
-  }
-  kv_grads<DH>(cx.ring.p[PREV], cx.ro, w.pk[P ^ 1], w.dsk[P ^ 1], w);  // step s-1
+  kv_grads<DH>(w.pk[P ^ 1], w.dsk[P ^ 1], w);   // step s-1
+  kv_read_tr<DH>(cx.ring.p[SLOT], cx.ro, w);     // step s, for the next phase
 
   f32x16_t p, ds;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(w.sc[e], cx.c, -rt[e].x));
-    ds[e] = p[e] * (w.dp[e] - rt[e].y);
+    p[e] = __builtin_amdgcn_exp2f(w.sc[e] * cx.c);
+    ds[e] = p[e] * w.dp[e];
   }
   pack_pairs(p, w.pk[P]);
   pack_pairs(ds, w.dsk[P]);
@@ -362,11 +393,11 @@ __device__ __forceinline__ void kv_phase(const KvCtx& cx, KvState<DH>& w, int s)
   kv_scores<DH, NEXT>(cx, w);  // S(s+1), dP(s+1)
 }
 
-// dK/dV of the last step, in slot SLOT.
-template <int DH, int SLOT>
-__device__ __forceinline__ void kv_drain(const KvCtx& cx, KvState<DH>& w, int par) {
-  if (par) kv_grads<DH>(cx.ring.p[SLOT], cx.ro, w.pk[1], w.dsk[1], w);
-  else kv_grads<DH>(cx.ring.p[SLOT], cx.ro, w.pk[0], w.dsk[0], w);
+// dK/dV of the last step (its transposed fragments were read in its phase).
+template <int DH>
+__device__ __forceinline__ void kv_drain(KvState<DH>& w, int par) {
+  if (par) kv_grads<DH>(w.pk[1], w.dsk[1], w);
+  else kv_grads<DH>(w.pk[0], w.dsk[0], w);
 }
 
 template <int DH>
@@ -412,6 +443,7 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dkdv_kernel(KvAr
   cx.q = a.q + (size_t)sg.q_base * D;
   cx.dout = a.dout + (size_t)sg.q_base * D;
   cx.rt = a.rt + (a.cu != nullptr ? (size_t)sg.q_base : (size_t)b * a.Hq * a.Np);
+  cx.rt_plane_bytes = (uint32_t)(a.rt_plane * 4);
   cx.stride = sg.stride;
   cx.rt_stride = a.Np;
   cx.N = N;
@@ -452,8 +484,17 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dkdv_kernel(KvAr
         w.acc_v[h][x] = zero16();
       }
     }
-    // P and dS of the step before a wave's first are 0: its first dK/dV
-    // products add nothing
+    // P and dS of the step before a wave's first are 0 (and its transposed
+    // fragments finite zeros): its first dK/dV products add nothing
+#pragma unroll
+    for (int h = 0; h < DH; ++h)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          w.qt_f[h][x][hh] = u32x4_t{0u, 0u, 0u, 0u};
+          w.dt_f[h][x][hh] = u32x4_t{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
     for (int par = 0; par < 2; ++par)
 #pragma unroll
@@ -505,14 +546,7 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dkdv_kernel(KvAr
   if (cx.first >= nsteps) return;  // no step for this wave (no barrier follows)
   // dK/dV of the last step (its slot is still intact: later DMAs went elsewhere)
   const int last = nsteps - 1;
-  switch (last % kKvBuf) {
-    case 0: kv_drain<DH, 0>(cx, w, last & 1); break;
-    case 1: kv_drain<DH, 1>(cx, w, last & 1); break;
-    case 2: kv_drain<DH, 2>(cx, w, last & 1); break;
-    case 3: kv_drain<DH, 3>(cx, w, last & 1); break;
-    case 4: kv_drain<DH, 4>(cx, w, last & 1); break;
-    default: kv_drain<DH, 5>(cx, w, last & 1); break;
-  }
+  kv_drain<DH>(w, last & 1);
   if (u >= N) return;
   if (split_rows) {
     const size_t prow = ((size_t)split * a.kv_rows + kv_row0 + u) * D;
@@ -554,7 +588,8 @@ struct DqArgs {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float2* rt;  // row terms, [B*H_q, Np]
+  const float* rt;   // row terms, plane 0 [B*H_q, Np] (-lse log2(e)/c), plane 1 rt_plane floats later (-D)
+  int64_t rt_plane;
   uint16_t* dq;
   const int* cu;  // packed sequence offsets (nullptr: dense)
   int64_t T;      // packed: total tokens
@@ -762,9 +797,9 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dq_kernel(DqArgs
       load_row_frags(a.q + row_q * D + hh * kD, lg, w.qf[hh]);
       load_row_frags(a.dout + row_q * D + hh * kD, lg, w.df[hh]);
     }
-    const float2 r = a.rt[(size_t)rtrow0 + min(cx.t, N - 1)];
-    w.lse2 = r.x;
-    w.dd = r.y;
+    const size_t rr = (size_t)rtrow0 + min(cx.t, N - 1);
+    w.lse2 = -a.rt[rr] * a.c;  // lse log2(e)
+    w.dd = -a.rt[a.rt_plane + rr];
   }
 #pragma unroll
   for (int e = 0; e < 16; ++e) w.ndd[e] = -w.dd;
@@ -925,7 +960,11 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   // magnitude and round away exactly as 0 would
   float c = p.scale * kLog2e;
   if (fabsf(c) < 1e-30f) c = p.scale < 0.f ? -1e-30f : 1e-30f;
-  float2* rt = static_cast<float2*>(p.rowterms);
+  float* rt = static_cast<float*>(p.rowterms);
+  // two planes of row terms, 4 bytes per row each; a row-term DMA spans
+  // from a row of plane 0 to 128 bytes into plane 1 (32-bit range)
+  const int64_t rt_rows = (packed ? 1 : p.B) * p.Hq * Np64;
+  if (rt_rows > (0x7fffffffLL - 256) / 4) return hipErrorInvalidValue;
   const int nsplit = p.nsplit < 1 ? 1 : p.nsplit;
   if (nsplit > 1 && (p.causal || p.split_ws == nullptr)) return hipErrorInvalidValue;
   const int64_t q_rows = packed ? p.Hq * p.T : p.B * p.Hq * p.N;
@@ -948,9 +987,10 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
     a.dout = static_cast<const uint16_t*>(p.dout);
     a.lse = p.lse;
     a.rt = rt;
-    a.nrows = (packed ? 1 : p.B) * p.Hq * Np64;
+    a.nrows = rt_rows;
     a.N = packed ? (int)p.T : N;
     a.Np = Np;
+    a.inv_c = 1.0f / c;
     const int64_t nblk = (a.nrows + 31) / 32;
     if (nblk > 0x7fffffff) return hipErrorInvalidValue;
     if (!p.dry_run) {
@@ -967,6 +1007,7 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
     a.v = static_cast<const uint16_t*>(p.v);
     a.dout = static_cast<const uint16_t*>(p.dout);
     a.rt = rt;
+    a.rt_plane = rt_rows;
     a.dk = static_cast<uint16_t*>(p.dk);
     a.dv = static_cast<uint16_t*>(p.dv);
     a.cu = p.cu_seqlens;
@@ -1005,6 +1046,7 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
     a.v = static_cast<const uint16_t*>(p.v);
     a.dout = static_cast<const uint16_t*>(p.dout);
     a.rt = rt;
+    a.rt_plane = rt_rows;
     a.dq = static_cast<uint16_t*>(p.dq);
     a.cu = p.cu_seqlens;
     a.T = p.T;

@@ -474,6 +474,15 @@ def test_bwd_launch_limits_are_shape_errors(lib, N, d):
 
 
 @cpu_only
+def test_bwd_row_term_limit_is_a_shape_error(lib):
+    # 64 query heads of 2^23 rows: within the per-head limit, but the row
+    # terms (two planes of 4 bytes per row, one DMA spanning both) pass 2^31 bytes
+    q, k, v, o, do, lse, dq, dk, dv, ws = _spaced(10)
+    st = lib.sqa_attn_bwd(q, k, v, o, do, lse, dq, dk, dv, 1, 64, 64, 1 << 23, 64, 1, 0.125, 0, ws, 1 << 36, None)
+    assert st == 2 and "launch limit" in lib.sqa_last_error().decode()
+
+
+@cpu_only
 def test_layer_launch_limit_is_a_shape_error(lib):
     # X [1, 2^22, 256] bf16 is 2^31 bytes: past the projections' 32-bit offsets
     x, wq, wk, wv, wo, y, ws = _spaced(7)
