@@ -58,6 +58,8 @@ hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream);
 // head dim 128, software-pipelined (attn_fwd_bf16_d128.hip)
 hipError_t launch_attn_fwd_bf16_d128(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnProblem& p, hipStream_t stream);
+// fp32, d = 16, dense (cu_seqlens == nullptr) on the fp32 matrix pipe
+hipError_t launch_attn_fwd_f32_mfma16(const AttnProblem& p, hipStream_t stream);
 
 // SQA attention backward (bf16, head dim 64 or 128): dq [B,Hq,N,D], dk/dv
 // [B,Hkv,N,D] from q, k, v, the forward's o and lse, and dout (or the packed

@@ -15,8 +15,19 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "sparse_query_attention_sqa_amd", "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_bf16_d64.hip", "attn_fwd_bf16_d128.hip", "attn_fwd_f32.hip",
-           "attn_bwd_bf16.hip", "gemm_bf16.hip", "rms_norm.hip", "sqa_api.cpp"]
+
+def _library_sources():
+    """The library's source list, read from its build script (loaded from
+    its file, so that importing the package is not needed)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_sqa_build", os.path.join(ROOT, "sparse_query_attention_sqa_amd",
+                                                                          "_build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return list(mod.SOURCES)
+
+
+SOURCES = _library_sources()
 HIPCC = "/opt/rocm/bin/hipcc"
 CLANG = "/opt/rocm/lib/llvm/bin/clang++"
 # sanitizers for the host code of each HIP source (each flag after -Xarch_host)
