@@ -66,6 +66,17 @@ def test_bf16_head_dims_small_all_rows(Hq, Hkv, N, causal, d):
     _check_fwd(q, k, v, "bf16", 1.0 / math.sqrt(d), causal, label)
 
 
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("B,N,Hq,Hkv,scale", [(3, 333, 6, 4, 0.25), (2, 64, 5, 2, -0.3), (2, 1100, 8, 4, 0.25)])
+def test_f32_d16_batched_uneven_all_rows(B, N, Hq, Hkv, scale, causal):
+    """fp32 d = 16 dense (the matrix-pipe kernel): several batches, uneven
+    head groups, a negative scale and more key tiles than key splits."""
+    label = f"f32 d=16 B={B} Hq={Hq} Hkv={Hkv} N={N} scale={scale} causal={causal}"
+    log(f"[case] {label}")
+    q, k, v = draw_attn_case(B, Hq, Hkv, N, 16, "f32", seed=B * 31 + N)
+    _check_fwd(q, k, v, "f32", scale, causal, label)
+
+
 @pytest.mark.parametrize("d", [32, 128])
 @pytest.mark.parametrize("causal", [0, 1])
 @pytest.mark.parametrize("N,Hq,Hkv", [(1, 2, 1), (17, 8, 4), (257, 6, 4), (700, 5, 2)])
