@@ -109,16 +109,11 @@ __device__ __forceinline__ f32x16_t mfma(const u32x4_t& a, const u32x4_t& b, con
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// Wait for this wave's LDS reads and for its DMAs of every tile but the
-// `pending` newest, then synchronise the workgroup.
-__device__ __forceinline__ void wait_vm_then_barrier(int pending) {
+// Wait for this wave's LDS reads and for its DMAs of every tile but the two
+// newest, then synchronise the workgroup.
+__device__ __forceinline__ void wait_vm_then_barrier() {
   asm volatile("" ::: "memory");
-  if (pending >= 2)
-    __builtin_amdgcn_s_waitcnt(0x0072);  // vmcnt(2) lgkmcnt(0)
-  else if (pending == 1)
-    __builtin_amdgcn_s_waitcnt(0x0071);  // vmcnt(1) lgkmcnt(0)
-  else
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt(0x0072);  // vmcnt(2) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -151,7 +146,12 @@ struct WaveState {
 };
 
 // DMA wave `wave`'s 1 KB part of tile kt into ring slot SLOT; keys at or past
-// N are zero-filled by the descriptor's range check.
+// N are zero-filled by the descriptor's range check, without any memory
+// access (a tile past the last is all zeros). Every wave issues one DMA per
+// tile step, also past the last tile, so that the count of VMEM operations
+// in flight is the same on every path: the compiler's own waits before LDS
+// reads of a slot are then exact instead of a wait for every DMA (measured
+// as an s_waitcnt vmcnt(0) before the reads of one slot in four).
 template <int SLOT>
 __device__ __forceinline__ void issue_tile(const Ctx& cx, const Lane& ln, int kt) {
   const int key0 = kt * kTileKeys;
@@ -231,8 +231,8 @@ __device__ __forceinline__ void pv(const Ctx& cx, const Lane& ln, const u32x4_t 
 // wave has rows that see it, scores, softmax and P.V.
 template <int SLOT, bool FIRST>
 __device__ __forceinline__ void step(const Ctx& cx, const Lane& ln, WaveState& w, int kt) {
-  wait_vm_then_barrier(min(cx.nt - 1 - kt, NBUF - 2));
-  if (kt + NBUF - 1 < cx.nt) issue_tile<(SLOT + NBUF - 1) % NBUF>(cx, ln, kt + NBUF - 1);
+  wait_vm_then_barrier();
+  issue_tile<(SLOT + NBUF - 1) % NBUF>(cx, ln, kt + NBUF - 1);
   if (kt > cx.last) return;
 
   const int key0 = kt * kTileKeys;
@@ -395,16 +395,20 @@ __global__ __launch_bounds__(kThreads, 4) void attn_fwd_bf16_d16_kernel(Args16 a
 
   // ---- prologue: tiles 0..2 in flight, then one tile per step
   issue_tile<0>(cx, ln, 0);
-  if (cx.nt > 1) issue_tile<1>(cx, ln, 1);
-  if (cx.nt > 2) issue_tile<2>(cx, ln, 2);
+  issue_tile<1>(cx, ln, 1);
+  issue_tile<2>(cx, ln, 2);
+  // whole turns of the ring: steps past the last tile only wait, barrier and
+  // issue their (empty) DMA, so that every path issues the same VMEM sequence
   step<0, true>(cx, ln, w, 0);
   for (int kt = 1; kt < cx.nt; kt += NBUF) {
     step<1, false>(cx, ln, w, kt);
-    if (kt + 1 < cx.nt) step<2, false>(cx, ln, w, kt + 1);
-    if (kt + 2 < cx.nt) step<3, false>(cx, ln, w, kt + 2);
-    if (kt + 3 < cx.nt) step<0, false>(cx, ln, w, kt + 3);
+    step<2, false>(cx, ln, w, kt + 1);
+    step<3, false>(cx, ln, w, kt + 2);
+    step<0, false>(cx, ln, w, kt + 3);
   }
 
+  // no DMA may still write this workgroup's LDS once its waves have ended
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   if (!wave_valid) return;
   // ---- epilogue: O = O^T / l (bf16, nearest even), LSE = m ln2 + ln l.
   // Lane-half 0 holds dims 0-3 in entries 0-3 and 4-7 in entries 8-11;
