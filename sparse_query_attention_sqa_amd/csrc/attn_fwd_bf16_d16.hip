@@ -6,19 +6,18 @@
 // query-head groups, "GQA ..." page, "The idea") with fewer query heads than
 // the baseline (SQA paper abstract); encoder-style or causal.
 //
-// At d = 16 each score costs one MFMA k-step but the softmax spends a
-// v_exp_f32 and a handful of other VALU instructions on it, so this kernel
-// is bound by VALU issue, not by the matrix pipe. It trades matrix work for
-// VALU work wherever it can:
+// At d = 16 each score costs half an MFMA k-step but the softmax spends a
+// v_exp_f32 and a few other VALU instructions on it, so this kernel is bound
+// by VALU issue, not by the matrix pipe. It trades matrix work for VALU work:
 //   * The scale and the running maximum are folded into the score MFMAs.
 //     Each query row is multiplied by c = scale*log2(e) in fp32 and split
-//     into two bf16 parts, x = hi + lo (|x - hi - lo| <= 2^-18 |x|), and the
-//     score chain S'^T = K.hi^T + K.lo^T starts from the C operand -m (m the
-//     row's running maximum, in every accumulator entry). The accumulator then
-//     holds s*c - m, and a probability is one v_exp_f32 of it.
-//   * V^T rows 16..31 of the 32-row P.V MFMA (which d = 16 leaves over) read
-//     the same V rows with the head dims rotated by 4, so each lane-half ends
-//     with all 16 dims of its row and stores 8 of them as one 16-byte write.
+//     into two bf16 parts, x = hi + lo (|x - hi - lo| <= 2^-18 |x|), which
+//     fill the 32-deep k of v_mfma_f32_16x16x32_bf16 (K rows twice against
+//     hi then lo), and the chain starts from the C operand -m (m the row's
+//     running maximum). The accumulator then holds s*c - m, and a probability
+//     is one v_exp_f32 of it.
+//   * 16x16 tiles fit d = 16 exactly: O^T (16 dims x 16 queries) += V^T P^T
+//     over 32 keys is one MFMA with no padded rows.
 // What is left per score: v_exp_f32, half a v_cvt_pk_bf16_f32 and half a
 // v_dot2c_f32_bf16 (the row sum of the rounded probabilities).
 //
@@ -26,18 +25,23 @@
 // wave owns 32 query rows of one query head (slots ordered by position block,
 // then head-in-group, as the other forward kernels; groups may differ in size
 // by one head and packed sequences in length, and workgroups with no rows
-// leave at once). K/V stream in 64-key
-// tiles straight from HBM to LDS (buffer_load ... lds, one 1 KB DMA per wave
-// and tile: K keys 0-31, K keys 32-63, V keys 0-31, V keys 32-63) through a
-// 4-slot ring with one barrier per tile. K rows sit in LDS under the
-// permutation pi (accumulator entry i of lane-half lg is then key lg*16 + i,
-// the B-operand order of P^T) with their two 16-byte chunks swapped on rows
-// 8-15 and 24-31 (conflict-free fragment reads); V rows are in key order and
-// reach the P.V MFMA through ds_read_b64_tr_b16.
+// leave at once). K/V stream in 64-key tiles straight from HBM to LDS
+// (buffer_load ... lds, one 1 KB DMA per wave and tile: K keys 0-31, K keys
+// 32-63, V keys 0-31, V keys 32-63) through a 4-slot ring, one barrier per
+// tile. K and V rows are in key order (32 B), the K rows' two 16-byte chunks
+// swapped on rows 8-15 of every 16 (conflict-free fragment reads); V reaches
+// the P.V MFMA through ds_read_b64_tr_b16.
+//
+// Schedule: a wave's 32 rows are two 16-row halves in a two-phase pipeline
+// over the tiles kt (as the d = 64 kernel's):
+//   phase A(kt): MFMA P(kt-1,h1).V(kt-1), S(kt,h1)    VALU softmax S(kt,h0)
+//   phase B(kt): MFMA P(kt,h0).V(kt),   S(kt+1,h0)    VALU softmax S(kt,h1)
+// so the MFMAs of one half run under the exponentials of the other and a
+// wave's chain of tiles is not a sequence of MFMA and VALU latencies.
 //
 // Softmax: probabilities against the running maximum as it stands; a wave's
 // first tile takes its exact row maximum, later tiles raise it only when a
-// lane's sum of its 32 rounded probabilities exceeds 2^20 (or is not finite),
+// lane's sum of its 16 rounded probabilities exceeds 2^20 (or is not finite),
 // then rescale O and l and recompute the tile. Masked scores (causal key > t,
 // key >= N) become -inf, on the causal diagonal tile and the ragged last tile
 // only.
@@ -53,7 +57,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -95,8 +99,6 @@ struct Args16 {
   int causal;
 };
 
-__device__ __forceinline__ int pi_row(int r) { return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3); }
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2_t f = {a, b};
@@ -105,15 +107,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ f32x16_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+// MFMA lane layout (v_mfma_f32_16x16x32_bf16): A lane l -> row l%16,
+// k = (l/16)*8 + 0..7; B lane l -> column l%16, same k; accumulator entry i
+// of lane l -> row (l/16)*4 + i, column l%16.
+__device__ __forceinline__ f32x4_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// Wait for this wave's LDS reads and for its DMAs of every tile but the two
-// newest, then synchronise the workgroup.
+// Wait for this wave's LDS reads and for its DMAs of every tile but the
+// `pending` newest, then synchronise the workgroup.
+template <int PENDING>
 __device__ __forceinline__ void wait_vm_then_barrier() {
+  static_assert(PENDING == 1 || PENDING == 2, "pending DMAs");
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x0072);  // vmcnt(2) lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt(PENDING == 2 ? 0x0072 : 0x0071);  // vmcnt(PENDING) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -126,32 +133,34 @@ struct Ring {
 
 struct Lane {
   uint32_t dma_src;  // source byte offset within the tile of this lane's 16-byte DMA chunk
-  uint32_t kro[2];   // K fragment offsets (32-key block 0, 1) within a slot
-  uint32_t vro;      // V transposed-read offset within a slot (+ block*1 KB + hh*256 + hi*128)
+  uint32_t kro;      // K fragment offset within a slot (+ 16-key block * 512 B)
+  uint32_t vro;      // V transposed-read offset within a slot (+ 32-key range * 1 KB + half * 512 B)
 };
 
 struct Ctx {
   Ring ring;
   const uint16_t* kvbase;  // K (waves 0, 1) or V (waves 2, 3) of this (batch, K/V head)
   int N, nt, last, causal, wave;
-  int vis;                 // last key this lane's row may see
-  int lg;
+  int lim[2];              // per half: last visible key minus this lane's first key of a block, at tile 0
 };
 
 struct WaveState {
-  u32x4_t qh, ql;   // c*q split into two bf16 parts (B operand, k = head dims)
-  f32x16_t negm;    // -m in every entry: the C operand of each score chain
-  f32x16_t o;       // O^T (rows 0-15: dims 0-15; rows 16-31: dims rotated by 4)
-  float l;          // this lane's share of the row sum
+  u32x4_t qf[2];     // per half: c*q as the B operand, k-group G: hi dims 8G.. (G < 2), lo dims 8(G-2).. (G >= 2)
+  f32x4_t negm[2];   // per half: -m in every entry, the C operand of each score chain
+  f32x4_t o[2];      // per half: O^T entries, dims 4G .. 4G+3 of query l%16
+  float l[2];        // per half: this lane's share of the row sum
+  u32x4_t kf[4];     // K fragments of the tile whose scores come next, per 16-key block
+  u32x4_t vf[2];     // V^T fragments of the tile whose P.V comes next, per 32-key range
+  f32x4_t s[2][4];   // per half, per 16-key block: scores (keys 16*blk + 4G + i)
+  u32x4_t pk[2][2];  // per half, per 32-key range: P^T as the B operand
 };
 
 // DMA wave `wave`'s 1 KB part of tile kt into ring slot SLOT; keys at or past
 // N are zero-filled by the descriptor's range check, without any memory
 // access (a tile past the last is all zeros). Every wave issues one DMA per
-// tile step, also past the last tile, so that the count of VMEM operations
-// in flight is the same on every path: the compiler's own waits before LDS
-// reads of a slot are then exact instead of a wait for every DMA (measured
-// as an s_waitcnt vmcnt(0) before the reads of one slot in four).
+// tile, also past the last tile, so that the count of VMEM operations in
+// flight is the same on every path: the compiler's own waits before LDS reads
+// of a slot are then exact instead of a wait for every DMA in flight.
 template <int SLOT>
 __device__ __forceinline__ void issue_tile(const Ctx& cx, const Lane& ln, int kt) {
   const int key0 = kt * kTileKeys;
@@ -162,123 +171,156 @@ __device__ __forceinline__ void issue_tile(const Ctx& cx, const Lane& ln, int kt
                                            0, 0, 0);
 }
 
-// S'^T = K.hi^T + K.lo^T + C for both 32-key blocks of the tile in slot SLOT.
 template <int SLOT>
-__device__ __forceinline__ void scores(const Ctx& cx, const Lane& ln, const WaveState& w, const f32x16_t& cinit,
-                                       f32x16_t (&s)[2]) {
+__device__ __forceinline__ void read_k(const Ctx& cx, const Lane& ln, u32x4_t (&kf)[4]) {
 #pragma unroll
-  for (int kx = 0; kx < 2; ++kx) {
-    const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(cx.ring.p[SLOT] + ln.kro[kx]);
-    s[kx] = mfma(kf, w.qh, cinit);
-    s[kx] = mfma(kf, w.ql, s[kx]);
+  for (int kb = 0; kb < 4; ++kb)
+    kf[kb] = *reinterpret_cast<const u32x4_t*>(cx.ring.p[SLOT] + ln.kro + kb * 16 * kRowBytes);
+}
+
+// V^T fragments per 32-key range j: dims l%16 against keys 32j + 4G + 0..3
+// (k positions 8G + 0..3) and 32j + 16 + 4G + 0..3 (8G + 4..7).
+template <int SLOT>
+__device__ __forceinline__ void read_v(const Ctx& cx, const Lane& ln, u32x4_t (&vf)[2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint8_t* p = cx.ring.p[SLOT] + ln.vro + j * kBlockBytes;
+    const u32x2_t a = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
+    const u32x2_t b =
+        __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 16 * kRowBytes)));
+    vf[j] = u32x4_t{a[0], a[1], b[0], b[1]};
   }
 }
 
-// Keys past `lim` (relative to the block's first key of this lane-half)
-// become -inf.
-__device__ __forceinline__ void mask_tile(f32x16_t (&s)[2], int lim) {
+// S'^T = [K K].[hi lo]^T - m of half h for the four 16-key blocks in kf.
+__device__ __forceinline__ void mfma_s(WaveState& w, int h) {
 #pragma unroll
-  for (int kx = 0; kx < 2; ++kx)
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (i > lim - kx * 32) s[kx][i] = -INFINITY;
+  for (int kb = 0; kb < 4; ++kb) w.s[h][kb] = mfma(w.kf[kb], w.qf[h], w.negm[h]);
 }
 
-// Probabilities 2^s, rounded to bf16 and packed as the P^T B operand
-// [block][hh]; returns the lane's sum of its 32 rounded probabilities.
-__device__ __forceinline__ float exp_pack(const f32x16_t (&s)[2], u32x4_t (&pk)[2][2]) {
+// O^T(h) += V^T P^T(h) over the 64 keys of the tile in vf.
+__device__ __forceinline__ void mfma_pv(WaveState& w, int h) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) w.o[h] = mfma(w.vf[j], w.pk[h][j], w.o[h]);
+}
+
+// Keys past `lim` (relative to this lane's first key of each block) become -inf.
+__device__ __forceinline__ void mask_half(f32x4_t (&s)[4], int lim) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (kb * 16 + i > lim) s[kb][i] = -INFINITY;
+}
+
+// Probabilities 2^s of one half, rounded to bf16 and packed as the P^T B
+// operand of each 32-key range; returns the lane's sum of its 16 rounded
+// probabilities.
+__device__ __forceinline__ float exp_pack(const f32x4_t (&s)[4], u32x4_t (&pk)[2]) {
   const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
   float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-  for (int kx = 0; kx < 2; ++kx)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
+    for (int w = 0; w < 4; ++w) {
+      const f32x4_t& b = s[2 * j + (w >> 1)];
       const uint32_t pp =
-          pack_bf16x2(__builtin_amdgcn_exp2f(s[kx][2 * w]), __builtin_amdgcn_exp2f(s[kx][2 * w + 1]));
-      pk[kx][w >> 2][w & 3] = pp;
+          pack_bf16x2(__builtin_amdgcn_exp2f(b[2 * (w & 1)]), __builtin_amdgcn_exp2f(b[2 * (w & 1) + 1]));
+      pk[j][w] = pp;
       if (w & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, l1, false);
       else l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, l0, false);
     }
   return l0 + l1;
 }
 
-// Largest of the row's scores in this tile (both lane-halves).
-__device__ __forceinline__ float row_max(const f32x16_t (&s)[2]) {
+// Largest of a half's row scores in this tile (all four lane groups).
+__device__ __forceinline__ float row_max(const f32x4_t (&s)[4]) {
   float mx = s[0][0];
 #pragma unroll
-  for (int kx = 0; kx < 2; ++kx)
+  for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kx][i]);
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
   return fmaxf(mx, __shfl_xor(mx, 32));
 }
 
-// O^T += V^T P^T over the tile in slot SLOT.
-template <int SLOT>
-__device__ __forceinline__ void pv(const Ctx& cx, const Lane& ln, const u32x4_t (&pk)[2][2], f32x16_t& o) {
-#pragma unroll
-  for (int kx = 0; kx < 2; ++kx)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const uint8_t* p = cx.ring.p[SLOT] + ln.vro + kx * kBlockBytes + hh * 8 * kRowBytes;
-      const u32x2_t a = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
-      const u32x2_t b =
-          __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * kRowBytes)));
-      o = mfma(u32x4_t{a[0], a[1], b[0], b[1]}, pk[kx][hh], o);
-    }
-}
-
-// One tile: wait for it (and free the slot three tiles on), then, if the
-// wave has rows that see it, scores, softmax and P.V.
-template <int SLOT, bool FIRST>
-__device__ __forceinline__ void step(const Ctx& cx, const Lane& ln, WaveState& w, int kt) {
-  wait_vm_then_barrier();
-  issue_tile<(SLOT + NBUF - 1) % NBUF>(cx, ln, kt + NBUF - 1);
-  if (kt > cx.last) return;
-
-  const int key0 = kt * kTileKeys;
-  const bool masked = (cx.causal && kt == cx.last) || (key0 + kTileKeys > cx.N);
-  const int lim = cx.vis - key0 - cx.lg * 16;
-  f32x16_t s[2];
-  u32x4_t pk[2][2];
+// Softmax of half h's scores: the first tile takes the exact row maximum
+// (every row sees key 0); later tiles raise m only when a probability grew
+// past the safe range, rescaling O and l and recomputing.
+template <bool FIRST>
+__device__ __forceinline__ void softmax_half(WaveState& w, int h) {
   if constexpr (FIRST) {
-    // the wave's first tile: its exact row maximum (every row sees key 0)
-    f32x16_t zero;
+    const float mx = row_max(w.s[h]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) zero[i] = 0.f;
-    scores<SLOT>(cx, ln, w, zero, s);
-    if (masked) mask_tile(s, lim);
-    const float mx = row_max(s);
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int kx = 0; kx < 2; ++kx)
+      for (int i = 0; i < 4; ++i) w.s[h][kb][i] -= mx;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kx][i] -= mx;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) w.negm[i] = -mx;
-    w.l = exp_pack(s, pk);
+    for (int i = 0; i < 4; ++i) w.negm[h][i] = -mx;
+    w.l[h] = exp_pack(w.s[h], w.pk[h]);
   } else {
-    scores<SLOT>(cx, ln, w, w.negm, s);
-    if (masked) mask_tile(s, lim);
-    float ls = exp_pack(s, pk);
+    float ls = exp_pack(w.s[h], w.pk[h]);
     if (__ballot(!(ls <= kSumLimit))) {
-      // a probability grew past the safe range: raise m by the tile's
-      // maximum over it (never lower it), rescale O and l, recompute
-      const float dm = fmaxf(row_max(s), 0.f);
+      const float dm = fmaxf(row_max(w.s[h]), 0.f);  // never lower m
       const float alpha = __builtin_amdgcn_exp2f(-dm);
-      w.l *= alpha;
+      w.l[h] *= alpha;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        w.o[i] *= alpha;
-        w.negm[i] -= dm;
+      for (int i = 0; i < 4; ++i) {
+        w.o[h][i] *= alpha;
+        w.negm[h][i] -= dm;
       }
 #pragma unroll
-      for (int kx = 0; kx < 2; ++kx)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kx][i] -= dm;
-      ls = exp_pack(s, pk);
+        for (int i = 0; i < 4; ++i) w.s[h][kb][i] -= dm;
+      ls = exp_pack(w.s[h], w.pk[h]);
     }
-    w.l += ls;
+    w.l[h] += ls;
   }
-  pv<SLOT>(cx, ln, pk, w.o);
+}
+
+// Scheduling hints for a phase: each of its 6 MFMAs followed by 5 VALU
+// instructions of the other half's softmax.
+__device__ __forceinline__ void interleave_phase() {
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+  }
+}
+
+// One tile kt in ring slot SLOT: phase A(kt), the barrier that makes tile
+// kt+1 resident and frees tile kt-1's slot for tile kt+3, phase B(kt).
+template <int SLOT, bool FIRST>
+__device__ __forceinline__ void step(const Ctx& cx, const Lane& ln, WaveState& w, int kt) {
+  constexpr int NEXT = (SLOT + 1) % NBUF;
+  constexpr int ISSUE = (SLOT + NBUF - 1) % NBUF;
+  const bool active = kt <= cx.last;
+  const int key0 = kt * kTileKeys;
+  const bool masked = (cx.causal && kt == cx.last) || (key0 + kTileKeys > cx.N);
+
+  // ---- phase A(kt): P(kt-1,h1).V(kt-1), S(kt,h1) || softmax S(kt,h0)
+  if (active) {
+    if (masked) mask_half(w.s[0], cx.lim[0] - key0);
+    mfma_pv(w, 1);
+    mfma_s(w, 1);
+    softmax_half<FIRST>(w, 0);
+    interleave_phase();
+  }
+
+  wait_vm_then_barrier<1>();
+  issue_tile<ISSUE>(cx, ln, kt + NBUF - 1);
+
+  // ---- phase B(kt): P(kt,h0).V(kt), S(kt+1,h0) || softmax S(kt,h1)
+  if (active) {
+    read_v<SLOT>(cx, ln, w.vf);
+    read_k<NEXT>(cx, ln, w.kf);
+    if (masked) mask_half(w.s[1], cx.lim[1] - key0);
+    mfma_pv(w, 0);
+    mfma_s(w, 0);
+    softmax_half<FIRST>(w, 1);
+    interleave_phase();
+  }
 }
 
 __global__ __launch_bounds__(kThreads, 4) void attn_fwd_bf16_d16_kernel(Args16 a) {
@@ -290,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_fwd_bf16_d16_kernel(Args16 a
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, lg = lane >> 5;
+  const int c16 = lane & 15, G = lane >> 4;
 
   // ---- workgroup -> (batch*Hkv, workgroup index within it)
   const int wid = (int)blockIdx.x;
@@ -346,59 +388,69 @@ __global__ __launch_bounds__(kThreads, 4) void attn_fwd_bf16_d16_kernel(Args16 a
   cx.N = N;
   cx.causal = a.causal;
   cx.wave = wave;
-  cx.lg = lg;
   const int maxtb = min((w_in * kWaves + kWaves - 1) / g, TB - 1);
   cx.nt = a.causal ? min((maxtb * kRowsPerWave + kRowsPerWave - 1) / kTileKeys + 1, NT) : NT;
   cx.last = !wave_valid ? -1 : (a.causal ? min((tb * kRowsPerWave + kRowsPerWave - 1) / kTileKeys, NT - 1) : NT - 1);
-  const int t = tb * kRowsPerWave + l32;
-  cx.vis = a.causal ? min(t, N - 1) : N - 1;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int t = tb * kRowsPerWave + hf * 16 + c16;
+    cx.lim[hf] = (a.causal ? min(t, N - 1) : N - 1) - 4 * G;
+  }
   const int64_t kvrow0 = sg.kv_base + (int64_t)kvh * sg.stride;
   const int64_t qrow0 = sg.q_base + (int64_t)h * sg.stride;
   cx.kvbase = (wave < 2 ? a.k : a.v) + (size_t)kvrow0 * D;
 
   Lane ln;
-  if (wave < 2) {  // K keys 32*wave + pi(r), 16-byte chunk c at position c ^ ((r >> 3) & 1)
+  if (wave < 2) {  // K keys 32*wave + r, 16-byte chunk c at position c ^ ((r >> 3) & 1)
     const int r = lane >> 1, cp = lane & 1;
-    ln.dma_src = (uint32_t)((wave * 32 + pi_row(r)) * kRowBytes + ((cp ^ ((r >> 3) & 1)) * 16));
-  } else {         // V keys 32*(wave-2) .. +31 in order
+    ln.dma_src = (uint32_t)((wave * 32 + r) * kRowBytes + ((cp ^ ((r >> 3) & 1)) * 16));
+  } else {         // V keys 32*(wave-2) .. +31
     ln.dma_src = (uint32_t)((wave - 2) * kBlockBytes + lane * 16);
   }
+  ln.kro = (uint32_t)(c16 * kRowBytes + (((G & 1) ^ (c16 >> 3)) * 16));
+  ln.vro = (uint32_t)(kVOffset + (4 * G + (c16 >> 2)) * kRowBytes + (c16 & 3) * 8);
+
+  // ---- Q loads (the split into hi/lo waits until tile 0 has landed)
+  u32x4_t qraw[2];
 #pragma unroll
-  for (int kx = 0; kx < 2; ++kx)
-    ln.kro[kx] = (uint32_t)(kx * kBlockBytes + l32 * kRowBytes + ((lg ^ ((l32 >> 3) & 1)) * 16));
-  {
-    // lanes 16-31 of each half read dims 4.. with a rotation by 4, so that
-    // accumulator rows 16-31 hold dims (r - 12) mod 16
-    const int j16 = lane & 15, g1 = (lane >> 4) & 1;
-    ln.vro = (uint32_t)(kVOffset + (lg * 16 + (j16 >> 2)) * kRowBytes + ((((j16 & 3) + g1) & 3) * 8));
+  for (int hf = 0; hf < 2; ++hf) {
+    const int t = min(tb * kRowsPerWave + hf * 16 + c16, N - 1);
+    qraw[hf] = u32x4_t{0u, 0u, 0u, 0u};
+    if (wave_valid) qraw[hf] = *reinterpret_cast<const u32x4_t*>(a.q + ((size_t)qrow0 + t) * D + (G & 1) * 8);
   }
 
-  // ---- Q: c*q in fp32, split into bf16 hi + lo (B operand, dims lg*8 .. +8)
-  WaveState w;
-  {
-    u32x4_t x = {0u, 0u, 0u, 0u};
-    if (wave_valid) x = *reinterpret_cast<const u32x4_t*>(a.q + ((size_t)qrow0 + min(t, N - 1)) * D + lg * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x0 = bf16_lo(x[e]) * a.c, x1 = bf16_hi(x[e]) * a.c;
-      const uint32_t hi = pack_bf16x2(x0, x1);
-      w.qh[e] = hi;
-      w.ql[e] = pack_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi));
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    w.o[i] = 0.f;
-    w.negm[i] = 0.f;
-  }
-  w.l = 0.f;
-
-  // ---- prologue: tiles 0..2 in flight, then one tile per step
+  // ---- prologue: tiles 0..2 in flight; tile 0 landed; S(0,h0)
   issue_tile<0>(cx, ln, 0);
   issue_tile<1>(cx, ln, 1);
   issue_tile<2>(cx, ln, 2);
-  // whole turns of the ring: steps past the last tile only wait, barrier and
-  // issue their (empty) DMA, so that every path issues the same VMEM sequence
+
+  WaveState w;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = bf16_lo(qraw[hf][e]) * a.c, x1 = bf16_hi(qraw[hf][e]) * a.c;
+      const uint32_t hi = pack_bf16x2(x0, x1);
+      w.qf[hf][e] = G < 2 ? hi : pack_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w.o[hf][i] = 0.f;
+      w.negm[hf][i] = 0.f;
+    }
+    w.l[hf] = 0.f;
+    w.pk[hf][0] = w.pk[hf][1] = u32x4_t{0u, 0u, 0u, 0u};  // P(-1,h1) = 0: the first P.V is a no-op
+  }
+  w.vf[0] = w.vf[1] = u32x4_t{0u, 0u, 0u, 0u};
+
+  wait_vm_then_barrier<2>();
+  if (cx.last >= 0) {
+    read_k<0>(cx, ln, w.kf);
+    mfma_s(w, 0);
+  }
+
+  // whole turns of the ring: steps past the last tile only barrier and issue
+  // their (empty) DMA, so that every path issues the same VMEM sequence
   step<0, true>(cx, ln, w, 0);
   for (int kt = 1; kt < cx.nt; kt += NBUF) {
     step<1, false>(cx, ln, w, kt);
@@ -406,29 +458,27 @@ __global__ __launch_bounds__(kThreads, 4) void attn_fwd_bf16_d16_kernel(Args16 a
     step<3, false>(cx, ln, w, kt + 2);
     step<0, false>(cx, ln, w, kt + 3);
   }
+  if (cx.last >= 0) mfma_pv(w, 1);  // drain P(last,h1) V(last)
 
   // no DMA may still write this workgroup's LDS once its waves have ended
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   if (!wave_valid) return;
-  // ---- epilogue: O = O^T / l (bf16, nearest even), LSE = m ln2 + ln l.
-  // Lane-half 0 holds dims 0-3 in entries 0-3 and 4-7 in entries 8-11;
-  // lane-half 1 holds dims 8-11 in entries 8-11 and 12-15 in entries 4-7.
-  const float ltot = w.l + __shfl_xor(w.l, 32);
-  if (t < N) {
-    const float inv = 1.0f / ltot;
-    u32x4_t out;
+  // ---- epilogue: O = O^T / l (bf16, nearest even), LSE = m ln2 + ln l;
+  // lane group G holds dims 4G .. 4G+3 of query l%16 of each half
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float a0 = lg ? w.o[8 + 2 * e] : w.o[2 * e];
-      const float a1 = lg ? w.o[9 + 2 * e] : w.o[2 * e + 1];
-      const float b0 = lg ? w.o[4 + 2 * e] : w.o[8 + 2 * e];
-      const float b1 = lg ? w.o[5 + 2 * e] : w.o[9 + 2 * e];
-      out[e] = pack_bf16x2(a0 * inv, a1 * inv);
-      out[2 + e] = pack_bf16x2(b0 * inv, b1 * inv);
+  for (int hf = 0; hf < 2; ++hf) {
+    float ltot = w.l[hf] + __shfl_xor(w.l[hf], 16);
+    ltot += __shfl_xor(ltot, 32);
+    const int t = tb * kRowsPerWave + hf * 16 + c16;
+    if (t < N) {
+      const float inv = 1.0f / ltot;
+      const u32x2_t out = {pack_bf16x2(w.o[hf][0] * inv, w.o[hf][1] * inv),
+                           pack_bf16x2(w.o[hf][2] * inv, w.o[hf][3] * inv)};
+      // non-temporal: no dirty L2 line left to write back at the end
+      __builtin_nontemporal_store(out, reinterpret_cast<u32x2_t*>(a.o + ((size_t)qrow0 + t) * D + 4 * G));
+      if (a.lse != nullptr && G == 0)
+        a.lse[(size_t)qrow0 + t] = (log2f(ltot) - w.negm[hf][0]) * 0.69314718055994531f;
     }
-    // non-temporal: no dirty L2 line left to write back at the end
-    __builtin_nontemporal_store(out, reinterpret_cast<u32x4_t*>(a.o + ((size_t)qrow0 + t) * D + lg * 8));
-    if (a.lse != nullptr && lg == 0) a.lse[(size_t)qrow0 + t] = (log2f(ltot) - w.negm[0]) * 0.69314718055994531f;
   }
 }
 
