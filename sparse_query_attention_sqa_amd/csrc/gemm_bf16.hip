@@ -155,7 +155,11 @@ __device__ __forceinline__ void qkv_rows(const GemmArgs& a, const f32x16_t (&acc
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const double th = lg ? a.rope_theta[8 * ab + 4 + e] : a.rope_theta[8 * ab + e];
+        // both candidates are lane-uniform (scalar loads from the kernel
+      // arguments); a lane-indexed read became a global load whose
+      // latency the epilogue waited out
+      const double th0 = a.rope_theta[8 * ab + e], th1 = a.rope_theta[8 * ab + 4 + e];
+      const double th = lg ? th1 : th0;
         const double rev = (double)t * th;
         const float f = (float)(rev - floor(rev));
         cs[ab][e] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
@@ -197,6 +201,19 @@ __device__ __forceinline__ void store_rows(const GemmArgs& a, const f32x16_t (&a
                                           int64_t nb, int lg) {
   if (EPI == EPI_STORE) {
     const int64_t ncols = a.part[0].ncols;
+    // every residual load first: y may alias the residual, so a load placed
+    // after a store of the row cannot move above it, and interleaved they
+    // would pay one memory latency each
+    u32x2_t rv[2][4];
+    if (a.resid != nullptr) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int ab = 0; ab < 4; ++ab) {
+          const int64_t n = nb + x * 32 + 8 * ab + 4 * lg;
+          rv[x][ab] = (n < ncols) ? *reinterpret_cast<const u32x2_t*>(a.resid + m * ncols + n) : u32x2_t{0u, 0u};
+        }
+    }
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -207,10 +224,9 @@ __device__ __forceinline__ void store_rows(const GemmArgs& a, const f32x16_t (&a
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[x][mb][4 * ab + e];
         if (a.resid != nullptr) {
-          const u32x2_t rv = *reinterpret_cast<const u32x2_t*>(a.resid + m * ncols + n);
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const uint32_t pr = rv[e];
+            const uint32_t pr = rv[x][ab][e];
             v[2 * e] += __builtin_bit_cast(float, pr << 16);
             v[2 * e + 1] += __builtin_bit_cast(float, pr & 0xffff0000u);
           }
@@ -247,7 +263,13 @@ __device__ __forceinline__ void store_rows(const GemmArgs& a, const f32x16_t (&a
   }
 }
 
-template <int EPI, int S, bool GATHER, int MB>
+// KFULL (K a multiple of the 64-wide chunk): every lane's DMA offset is fixed
+// for the whole reduction and each chunk moves the descriptors' base instead.
+// With per-chunk offsets in VGPRs that the register allocator then reuses for
+// LDS read results, the compiler waits for the DMA just issued before those
+// reads (it treats the DMA's offset operand like a load destination), and no
+// chunk overlaps the next one's DMA.
+template <int EPI, int S, bool GATHER, int MB, bool KFULL>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
   static_assert(S >= 2 && S <= 4, "2 to 4 stages");
   using T = Tiling<MB>;
@@ -328,21 +350,54 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
     w_r[q] = (uint32_t)(wkh * kTileRows + r);
   }
 
+  // KFULL: the lanes' offsets at k = 0 (rows past M, columns past the part's
+  // width: kOOB)
+  // (a_off0 has the largest NQA as its size: sized NQA, clang left the host
+  // stub of the KFULL kernels undefined)
+  uint32_t a_off0[4], w_off0[4];
+#pragma unroll
+  for (int j = 0; j < NQA; ++j) a_off0[j] = a_offset<GATHER>(A, a_base[j], a_ok[j], a_k[j], dshift);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w_off0[q] = w_ok[q] ? (w_r[q] * wncols + w_col[q]) * 2u : kOOB;
+  const int64_t a_bytes = A.M * A.K * 2;
+  const int64_t w_bytes = K * (int64_t)wncols * 2;
+  const uint16_t* wbase = wc ? wp1.w : wp0.w;
+
   auto issue = [&](uint8_t* stage, int64_t k0) {
-    const uint32_t k32 = (uint32_t)k0;
+    if constexpr (KFULL) {
+      // chunk k0: A from element adv on (row-major: k0; gathered: head
+      // k0 / d, column k0 % d), W from row k0 on; the range checks count
+      // from the moved bases, so chunks past K read nothing
+      const int64_t adv = GATHER ? (((k0 >> dshift) * A.N) << dshift) + (k0 & ((1 << dshift) - 1)) : k0;
+      const int64_t arem = a_bytes - adv * 2;
+      const __amdgpu_buffer_rsrc_t rak = rsrc(A.p + adv, (k0 < K && arem > 0) ? arem : (int64_t)0);
+      const int64_t wadv = k0 * (int64_t)wncols;
+      const int64_t wrem = w_bytes - wadv * 2;
+      const __amdgpu_buffer_rsrc_t rwk = rsrc(wbase + wadv, wrem > 0 ? wrem : (int64_t)0);
 #pragma unroll
-    for (int j = 0; j < NQA; ++j) {
-      const uint32_t off = a_offset<GATHER>(A, a_base[j], a_ok[j], k32 + a_k[j], dshift);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(stage + atile * kTileBytes + (aq0 + j) * 1024), 16,
-                                               off, 0, 0, 0);
-    }
+      for (int j = 0; j < NQA; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rak, (lds_void_t*)(stage + atile * kTileBytes + (aq0 + j) * 1024), 16,
+                                                 a_off0[j], 0, 0, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t k = k32 + w_r[q];
-      const uint32_t off = (w_ok[q] && k < (uint32_t)K) ? (k * wncols + w_col[q]) * 2u : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wc ? rw1 : rw0,
-                                               (lds_void_t*)(stage + (kATiles + wave) * kTileBytes + q * 1024), 16,
-                                               off, 0, 0, 0);
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rwk, (lds_void_t*)(stage + (kATiles + wave) * kTileBytes + q * 1024),
+                                                 16, w_off0[q], 0, 0, 0);
+    } else {
+      const uint32_t k32 = (uint32_t)k0;
+#pragma unroll
+      for (int j = 0; j < NQA; ++j) {
+        const uint32_t off = a_offset<GATHER>(A, a_base[j], a_ok[j], k32 + a_k[j], dshift);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(stage + atile * kTileBytes + (aq0 + j) * 1024), 16,
+                                                 off, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t k = k32 + w_r[q];
+        const uint32_t off = (w_ok[q] && k < (uint32_t)K) ? (k * wncols + w_col[q]) * 2u : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wc ? rw1 : rw0,
+                                                 (lds_void_t*)(stage + (kATiles + wave) * kTileBytes + q * 1024), 16,
+                                                 off, 0, 0, 0);
+      }
     }
   };
 
@@ -580,6 +635,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(GemmArgs a) {
     // projection: 7.3 us with 8-byte stores, one row per lane; 6.2 staged;
     // 5.7 staged and non-temporal (8-byte non-temporal stores: 14.4).
     const int64_t ncols = a.part[0].ncols;
+    // the residual chunks of this thread's 8 row passes, loaded before the
+    // staging so that their latency overlaps it (y may alias the residual:
+    // each element is read before it is written)
+    u32x4_t rvs[8];
+    if (a.resid != nullptr) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = it * 8 + (tid >> 5), cg = tid & 31;
+        const int64_t m = m0 + r, n = (int64_t)cg * 8;
+        rvs[it] = (m < A.M && n < ncols) ? *reinterpret_cast<const u32x4_t*>(a.resid + m * ncols + n)
+                                         : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
     __syncthreads();  // every wave is done reading the reduction chunks
     uint8_t* blk = lds + wave * 8192;
 #pragma unroll
@@ -595,24 +663,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(GemmArgs a) {
           *reinterpret_cast<u32x2_t*>(blk + r * 128 + (((c >> 3) ^ (r & 7)) << 4) + (c & 7) * 2) = wv;
         }
     __syncthreads();
-    // 64 rows x (4 waves x 8 chunks): thread -> (row, chunk), 8 rows per pass
+    // 64 rows x (4 waves x 8 chunks): thread -> (row, chunk), 8 rows per
+    // pass. All eight chunks are read and finished before the first store:
+    // a register that still feeds a store in flight is rewritten only after
+    // that store completes, so reads into one register per pass would
+    // serialise the stores.
+    u32x4_t vals[8];
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int r = it * 8 + (tid >> 5), cg = tid & 31;  // cg: 16-byte chunk of the 256-column row
       const int w = cg >> 3, ch = cg & 7;
-      const int64_t m = m0 + r, n = (int64_t)cg * 8;
-      if (m >= A.M || n >= ncols) continue;
-      u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + w * 8192 + r * 128 + ((ch ^ (r & 7)) << 4));
+      vals[it] = *reinterpret_cast<const u32x4_t*>(lds + w * 8192 + r * 128 + ((ch ^ (r & 7)) << 4));
       if (a.resid != nullptr) {
-        const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(a.resid + m * ncols + n);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float lo = __builtin_bit_cast(float, v[e] << 16) + __builtin_bit_cast(float, rv[e] << 16);
-          const float hi = __builtin_bit_cast(float, v[e] & 0xffff0000u) + __builtin_bit_cast(float, rv[e] & 0xffff0000u);
-          v[e] = pack_bf16x2(lo, hi);
+          const uint32_t v = vals[it][e], rv = rvs[it][e];
+          const float lo = __builtin_bit_cast(float, v << 16) + __builtin_bit_cast(float, rv << 16);
+          const float hi = __builtin_bit_cast(float, v & 0xffff0000u) + __builtin_bit_cast(float, rv & 0xffff0000u);
+          vals[it][e] = pack_bf16x2(lo, hi);
         }
       }
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(a.y + m * ncols + n));
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 8 + (tid >> 5), cg = tid & 31;
+      const int64_t m = m0 + r, n = (int64_t)cg * 8;
+      if (m < A.M && n < ncols)
+        __builtin_nontemporal_store(vals[it], reinterpret_cast<u32x4_t*>(a.y + m * ncols + n));
     }
   } else {
 #pragma unroll
@@ -623,14 +700,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(GemmArgs a) {
   }
 }
 
+template <int EPI, int S, bool GATHER, int MB, bool KFULL>
+hipError_t launch_kernel(const GemmArgs& a, int64_t nblk, hipStream_t stream) {
+  gemm_kernel<EPI, S, GATHER, MB, KFULL><<<dim3((unsigned)nblk), dim3(kThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int EPI, int S, bool GATHER, int MB>
 hipError_t launch_grid(const GemmArgs& a, hipStream_t stream, bool dry_run) {
   const int64_t mtiles = (a.A.M + Tiling<MB>::TM - 1) / Tiling<MB>::TM;
   const int64_t nblk = mtiles * a.tiles_total;
   if (nblk > 0x7fffffff || nblk <= 0) return hipErrorInvalidValue;
   if (dry_run) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<EPI, S, GATHER, MB>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return a.A.K % TK == 0 ? launch_kernel<EPI, S, GATHER, MB, true>(a, nblk, stream)
+                         : launch_kernel<EPI, S, GATHER, MB, false>(a, nblk, stream);
 }
 
 // Grids of at most 384 workgroups of 128 rows (about one per CU; the SQAT-m
