@@ -21,11 +21,16 @@
 // What is left per score: v_exp_f32, half a v_cvt_pk_bf16_f32 and half a
 // v_dot2c_f32_bf16 (the row sum of the rounded probabilities).
 //
-// Decomposition: a workgroup is 4 waves sharing one (batch, K/V head); each
-// wave owns 32 query rows of one query head (slots ordered by position block,
+// Decomposition: a workgroup is 4 row waves sharing one (batch, K/V head);
+// each owns 32 query rows of one query head (slots ordered by position block,
 // then head-in-group, as the other forward kernels; groups may differ in size
 // by one head and packed sequences in length, and workgroups with no rows
-// leave at once). K/V stream in 64-key tiles straight from HBM to LDS
+// leave at once). On grids too small to fill the device the workgroup has 8
+// waves: the row waves twice, over two key ranges (the first ceil(nt/2) of
+// its nt tiles and the rest) in lockstep on one ring with two tiles a slot,
+// the two partial softmax results (O, l, m) combined through LDS at the end
+// (the rescaling of partial results by exp(m_part - m), as in the online
+// softmax itself). K/V stream in 64-key tiles straight from HBM to LDS
 // (buffer_load ... lds, one 1 KB DMA per wave and tile: K keys 0-31, K keys
 // 32-63, V keys 0-31, V keys 32-63) through a 4-slot ring, one barrier per
 // tile. K and V rows are in key order (32 B), the K rows' two 16-byte chunks
@@ -66,8 +71,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int D = 16;
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                          // row waves per key-range part
 constexpr int kRowsPerWave = 32;
 constexpr int kTileKeys = 64;
 constexpr int kRowBytes = D * 2;                   // 32 B per key row
@@ -139,8 +143,12 @@ struct Lane {
 
 struct Ctx {
   Ring ring;
-  const uint16_t* kvbase;  // K (waves 0, 1) or V (waves 2, 3) of this (batch, K/V head)
-  int N, nt, last, causal, wave;
+  const uint16_t* kvbase;  // K (row waves 0, 1) or V (row waves 2, 3) of this (batch, K/V head)
+  int N, causal;
+  int kbase, kend;         // this wave's key-range part: step j takes tile kbase + j, tiles below kend
+  int last;                // last tile this wave computes (below kbase: none)
+  int diag;                // causal: the tile that holds the diagonal of this wave's rows
+  uint32_t dst;            // LDS offset of this wave's DMA part within a slot
   int lim[2];              // per half: last visible key minus this lane's first key of a block, at tile 0
 };
 
@@ -162,13 +170,14 @@ struct WaveState {
 // flight is the same on every path: the compiler's own waits before LDS reads
 // of a slot are then exact instead of a wait for every DMA in flight.
 template <int SLOT>
-__device__ __forceinline__ void issue_tile(const Ctx& cx, const Lane& ln, int kt) {
-  const int key0 = kt * kTileKeys;
-  const int rem = max(cx.N - key0, 0) * kRowBytes;
+__device__ __forceinline__ void issue_tile(const Ctx& cx, const Lane& ln, int j) {
+  const int kt = cx.kbase + j;
+  const bool live = kt < cx.kend;
+  const int key0 = live ? kt * kTileKeys : 0;
+  const int rem = live ? max(cx.N - key0, 0) * kRowBytes : 0;
   __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void*)(cx.kvbase + (size_t)key0 * D), (short)0, rem, kBufferWord3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(cx.ring.p[SLOT] + cx.wave * kBlockBytes), 16, ln.dma_src,
-                                           0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(cx.ring.p[SLOT] + cx.dst), 16, ln.dma_src, 0, 0, 0);
 }
 
 template <int SLOT>
@@ -289,15 +298,17 @@ __device__ __forceinline__ void interleave_phase() {
   }
 }
 
-// One tile kt in ring slot SLOT: phase A(kt), the barrier that makes tile
-// kt+1 resident and frees tile kt-1's slot for tile kt+3, phase B(kt).
+// Step j (tile kt = kbase + j) in ring slot SLOT: phase A(kt), the barrier
+// that makes step j+1's tile resident and frees step j-1's slot for step
+// j+3's, phase B(kt).
 template <int SLOT, bool FIRST>
-__device__ __forceinline__ void step(const Ctx& cx, const Lane& ln, WaveState& w, int kt) {
+__device__ __forceinline__ void step(const Ctx& cx, const Lane& ln, WaveState& w, int j) {
   constexpr int NEXT = (SLOT + 1) % NBUF;
   constexpr int ISSUE = (SLOT + NBUF - 1) % NBUF;
+  const int kt = cx.kbase + j;
   const bool active = kt <= cx.last;
   const int key0 = kt * kTileKeys;
-  const bool masked = (cx.causal && kt == cx.last) || (key0 + kTileKeys > cx.N);
+  const bool masked = (cx.causal && kt == cx.diag) || (key0 + kTileKeys > cx.N);
 
   // ---- phase A(kt): P(kt-1,h1).V(kt-1), S(kt,h1) || softmax S(kt,h0)
   if (active) {
@@ -309,7 +320,7 @@ __device__ __forceinline__ void step(const Ctx& cx, const Lane& ln, WaveState& w
   }
 
   wait_vm_then_barrier<1>();
-  issue_tile<ISSUE>(cx, ln, kt + NBUF - 1);
+  issue_tile<ISSUE>(cx, ln, j + NBUF - 1);
 
   // ---- phase B(kt): P(kt,h0).V(kt), S(kt+1,h0) || softmax S(kt,h1)
   if (active) {
@@ -323,15 +334,22 @@ __device__ __forceinline__ void step(const Ctx& cx, const Lane& ln, WaveState& w
   }
 }
 
-__global__ __launch_bounds__(kThreads, 4) void attn_fwd_bf16_d16_kernel(Args16 a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring0[kSlotBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t ring1[kSlotBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t ring2[kSlotBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t ring3[kSlotBytes];
+// KSPLIT: eight waves, the workgroup's tiles split in two key-range parts
+// (row waves 0-3 the first ceil(nt/2) tiles, 4-7 the rest) run side by side
+// over the same rows, their partial results combined through LDS at the end.
+template <bool KSPLIT>
+__global__ __launch_bounds__(KSPLIT ? 512 : 256, 4) void attn_fwd_bf16_d16_kernel(Args16 a) {
+  constexpr int kParts = KSPLIT ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[kParts * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[kParts * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[kParts * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring3[kParts * kSlotBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rw = wave & (kWaves - 1);         // row wave
+  const int kh = KSPLIT ? wave / kWaves : 0;  // key-range part
   const int c16 = lane & 15, G = lane >> 4;
 
   // ---- workgroup -> (batch*Hkv, workgroup index within it)
@@ -375,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_fwd_bf16_d16_kernel(Args16 a
   const int TB = (N + kRowsPerWave - 1) / kRowsPerWave;
   const int NT = (N + kTileKeys - 1) / kTileKeys;
   if (w_in * kWaves >= TB * g) return;  // past this group's rows
-  const int slot = w_in * kWaves + wave;
+  const int slot = w_in * kWaves + rw;
   const int tb = slot / g, jh = slot % g;
   const bool wave_valid = tb < TB;
   const int h = hg.first + jh;
@@ -387,10 +405,18 @@ __global__ __launch_bounds__(kThreads, 4) void attn_fwd_bf16_d16_kernel(Args16 a
   cx.ring.p[3] = ring3;
   cx.N = N;
   cx.causal = a.causal;
-  cx.wave = wave;
   const int maxtb = min((w_in * kWaves + kWaves - 1) / g, TB - 1);
-  cx.nt = a.causal ? min((maxtb * kRowsPerWave + kRowsPerWave - 1) / kTileKeys + 1, NT) : NT;
-  cx.last = !wave_valid ? -1 : (a.causal ? min((tb * kRowsPerWave + kRowsPerWave - 1) / kTileKeys, NT - 1) : NT - 1);
+  const int nt = a.causal ? min((maxtb * kRowsPerWave + kRowsPerWave - 1) / kTileKeys + 1, NT) : NT;
+  // steps of the ring; the second key-range part starts at tile ns, where
+  // every row of a wave that computes any of its tiles sees the tile's first
+  // key (a wave's 32 rows lie in one 64-key window), as the first part's
+  // rows all see key 0: the first tile's exact row maximum is defined
+  const int ns = KSPLIT ? (nt + 1) / 2 : nt;
+  cx.kbase = kh * ns;
+  cx.kend = (KSPLIT && kh == 0) ? ns : nt;
+  cx.diag = !wave_valid ? -1 : (a.causal ? min((tb * kRowsPerWave + kRowsPerWave - 1) / kTileKeys, NT - 1) : NT - 1);
+  cx.last = min(cx.diag, cx.kend - 1);
+  cx.dst = (uint32_t)(kh * kSlotBytes + rw * kBlockBytes);
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const int t = tb * kRowsPerWave + hf * 16 + c16;
@@ -398,31 +424,33 @@ __global__ __launch_bounds__(kThreads, 4) void attn_fwd_bf16_d16_kernel(Args16 a
   }
   const int64_t kvrow0 = sg.kv_base + (int64_t)kvh * sg.stride;
   const int64_t qrow0 = sg.q_base + (int64_t)h * sg.stride;
-  cx.kvbase = (wave < 2 ? a.k : a.v) + (size_t)kvrow0 * D;
+  cx.kvbase = (rw < 2 ? a.k : a.v) + (size_t)kvrow0 * D;
 
   Lane ln;
-  if (wave < 2) {  // K keys 32*wave + r, 16-byte chunk c at position c ^ ((r >> 3) & 1)
+  if (rw < 2) {  // K keys 32*rw + r, 16-byte chunk c at position c ^ ((r >> 3) & 1)
     const int r = lane >> 1, cp = lane & 1;
-    ln.dma_src = (uint32_t)((wave * 32 + r) * kRowBytes + ((cp ^ ((r >> 3) & 1)) * 16));
-  } else {         // V keys 32*(wave-2) .. +31
-    ln.dma_src = (uint32_t)((wave - 2) * kBlockBytes + lane * 16);
+    ln.dma_src = (uint32_t)((rw * 32 + r) * kRowBytes + ((cp ^ ((r >> 3) & 1)) * 16));
+  } else {       // V keys 32*(rw-2) .. +31
+    ln.dma_src = (uint32_t)((rw - 2) * kBlockBytes + lane * 16);
   }
-  ln.kro = (uint32_t)(c16 * kRowBytes + (((G & 1) ^ (c16 >> 3)) * 16));
-  ln.vro = (uint32_t)(kVOffset + (4 * G + (c16 >> 2)) * kRowBytes + (c16 & 3) * 8);
+  ln.kro = (uint32_t)(kh * kSlotBytes + c16 * kRowBytes + (((G & 1) ^ (c16 >> 3)) * 16));
+  ln.vro = (uint32_t)(kh * kSlotBytes + kVOffset + (4 * G + (c16 >> 2)) * kRowBytes + (c16 & 3) * 8);
 
-  // ---- Q loads (the split into hi/lo waits until tile 0 has landed)
+  // ---- Q loads, on every wave (one past the last row block reads row N-1 of
+  // its head): a load under a branch would be waited for inside it, before
+  // the first DMA is issued. The split into hi/lo follows the DMA issue.
   u32x4_t qraw[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const int t = min(tb * kRowsPerWave + hf * 16 + c16, N - 1);
-    qraw[hf] = u32x4_t{0u, 0u, 0u, 0u};
-    if (wave_valid) qraw[hf] = *reinterpret_cast<const u32x4_t*>(a.q + ((size_t)qrow0 + t) * D + (G & 1) * 8);
+    qraw[hf] = *reinterpret_cast<const u32x4_t*>(a.q + ((size_t)qrow0 + t) * D + (G & 1) * 8);
   }
 
   // ---- prologue: tiles 0..2 in flight; tile 0 landed; S(0,h0)
   issue_tile<0>(cx, ln, 0);
   issue_tile<1>(cx, ln, 1);
   issue_tile<2>(cx, ln, 2);
+  __builtin_amdgcn_sched_barrier(0);
 
   WaveState w;
 #pragma unroll
@@ -444,7 +472,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_fwd_bf16_d16_kernel(Args16 a
   w.vf[0] = w.vf[1] = u32x4_t{0u, 0u, 0u, 0u};
 
   wait_vm_then_barrier<2>();
-  if (cx.last >= 0) {
+  if (cx.last >= cx.kbase) {
     read_k<0>(cx, ln, w.kf);
     mfma_s(w, 0);
   }
@@ -452,32 +480,66 @@ __global__ __launch_bounds__(kThreads, 4) void attn_fwd_bf16_d16_kernel(Args16 a
   // whole turns of the ring: steps past the last tile only barrier and issue
   // their (empty) DMA, so that every path issues the same VMEM sequence
   step<0, true>(cx, ln, w, 0);
-  for (int kt = 1; kt < cx.nt; kt += NBUF) {
-    step<1, false>(cx, ln, w, kt);
-    step<2, false>(cx, ln, w, kt + 1);
-    step<3, false>(cx, ln, w, kt + 2);
-    step<0, false>(cx, ln, w, kt + 3);
+  for (int j = 1; j < ns; j += NBUF) {
+    step<1, false>(cx, ln, w, j);
+    step<2, false>(cx, ln, w, j + 1);
+    step<3, false>(cx, ln, w, j + 2);
+    step<0, false>(cx, ln, w, j + 3);
   }
-  if (cx.last >= 0) mfma_pv(w, 1);  // drain P(last,h1) V(last)
+  if (cx.last >= cx.kbase) mfma_pv(w, 1);  // drain P(last,h1) V(last)
 
   // no DMA may still write this workgroup's LDS once its waves have ended
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  float ltot[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    ltot[hf] = w.l[hf] + __shfl_xor(w.l[hf], 16);
+    ltot[hf] += __shfl_xor(ltot[hf], 32);
+  }
+  if constexpr (KSPLIT) {
+    // the second part hands O^T, l and m (per lane, as held) to the row wave
+    // of the first part through the ring's first two slots; a part that
+    // computed no tile has l = 0 and adds nothing. Both parts' m are finite.
+    f32x4_t* ob = reinterpret_cast<f32x4_t*>(ring0);
+    f32x2_t* lb = reinterpret_cast<f32x2_t*>(ring1);
+    __syncthreads();  // every wave is past its last read of the ring
+    if (kh == 1) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        ob[(rw * 2 + hf) * 64 + lane] = w.o[hf];
+        lb[(rw * 2 + hf) * 64 + lane] = f32x2_t{ltot[hf], w.negm[hf][0]};
+      }
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4_t o1 = ob[(rw * 2 + hf) * 64 + lane];
+      const f32x2_t lm = lb[(rw * 2 + hf) * 64 + lane];
+      if (lm[0] > 0.f) {
+        const float m = fmaxf(-w.negm[hf][0], -lm[1]);
+        const float a0 = __builtin_amdgcn_exp2f(-w.negm[hf][0] - m), a1 = __builtin_amdgcn_exp2f(-lm[1] - m);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w.o[hf][i] = w.o[hf][i] * a0 + o1[i] * a1;
+        ltot[hf] = ltot[hf] * a0 + lm[0] * a1;
+        w.negm[hf][0] = -m;
+      }
+    }
+  }
   if (!wave_valid) return;
   // ---- epilogue: O = O^T / l (bf16, nearest even), LSE = m ln2 + ln l;
   // lane group G holds dims 4G .. 4G+3 of query l%16 of each half
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    float ltot = w.l[hf] + __shfl_xor(w.l[hf], 16);
-    ltot += __shfl_xor(ltot, 32);
     const int t = tb * kRowsPerWave + hf * 16 + c16;
     if (t < N) {
-      const float inv = 1.0f / ltot;
+      const float inv = 1.0f / ltot[hf];
       const u32x2_t out = {pack_bf16x2(w.o[hf][0] * inv, w.o[hf][1] * inv),
                            pack_bf16x2(w.o[hf][2] * inv, w.o[hf][3] * inv)};
       // non-temporal: no dirty L2 line left to write back at the end
       __builtin_nontemporal_store(out, reinterpret_cast<u32x2_t*>(a.o + ((size_t)qrow0 + t) * D + 4 * G));
       if (a.lse != nullptr && G == 0)
-        a.lse[(size_t)qrow0 + t] = (log2f(ltot) - w.negm[hf][0]) * 0.69314718055994531f;
+        a.lse[(size_t)qrow0 + t] = (log2f(ltot[hf]) - w.negm[hf][0]) * 0.69314718055994531f;
     }
   }
 }
@@ -526,7 +588,14 @@ hipError_t launch_attn_fwd_bf16_d16(const AttnProblem& p, hipStream_t stream) {
   a.c = p.scale < 0.f ? -cabs : cabs;
   a.causal = p.causal;
   if (p.dry_run) return hipSuccess;
-  hipLaunchKernelGGL(attn_fwd_bf16_d16_kernel, dim3((unsigned)a.nwg), dim3(kThreads), 0, stream, a);
+  // key-range parts when the eight-wave workgroups all fit on the device at
+  // once (two per CU at four waves per SIMD): the waves' tile chains halve
+  // and twice the waves hide each other's latency. With more workgroups
+  // they would run in two rounds, slower than the four-wave kernel in one.
+  if ((int64_t)a.nwg <= 2LL * device_cus())
+    hipLaunchKernelGGL(attn_fwd_bf16_d16_kernel<true>, dim3((unsigned)a.nwg), dim3(2 * kWaves * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_bf16_d16_kernel<false>, dim3((unsigned)a.nwg), dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
