@@ -256,6 +256,9 @@ struct KvCtx {
   int64_t stride, rt_stride;  // rows between heads of Q/dO and of the row terms
   uint32_t rt_plane_bytes;    // from plane 0 to plane 1
   int N, g, h0, qt0, kb, causal, wave, first;  // N: this sequence; first: the first step this wave computes
+  int diag0;                  // causal: the first step of query tile kb (its g steps hold the diagonal)
+  int64_t d_head, d_wrap;     // cursor moves (elements) to the next head / to head 0 of the next tile
+  int64_t rt_wrap;            // the same in the row terms (to the next head: rt_stride)
   float c;
   float masked;  // score whose exponent s*c is -inf: -inf * sign(c)
   uint32_t off;
@@ -271,22 +274,42 @@ struct KvState {
   u32x4_t qt_f[DH][2][2], dt_f[DH][2][2];  // transposed Q and dO fragments of the step whose dK/dV come next
 };
 
-// DMA step s (query tile qt of query head h0 + i) into ring slot SLOT.
+// The source of the next step's DMA: step s is query tile qt0 + s / g of
+// query head h0 + s % g, so the cursor walks the group's heads and then the
+// next tile, by fixed moves (no division by g and no 64-bit product per step).
+struct KvCursor {
+  int64_t off;     // elements into Q and dO: head h0 + i, row row0
+  int64_t rt_off;  // floats into the row terms: the same head and row
+  int row0, i;
+};
+
+__device__ __forceinline__ void kv_advance(const KvCtx& cx, KvCursor& u) {
+  const bool wrap = u.i + 1 == cx.g;
+  u.i = wrap ? 0 : u.i + 1;
+  u.row0 += wrap ? kTileRows : 0;
+  u.off += wrap ? cx.d_wrap : cx.d_head;
+  u.rt_off += wrap ? cx.rt_wrap : cx.rt_stride;
+}
+
+// DMA the step at cursor u into ring slot SLOT, then move u to the next step.
 template <int DH, int SLOT>
-__device__ __forceinline__ void kv_issue(const KvCtx& cx, int s) {
+__device__ __forceinline__ void kv_issue(const KvCtx& cx, KvCursor& u) {
   using C = KvCfg<DH>;
   constexpr int RB = Dims<DH>::RB;
-  const int qt = cx.qt0 + s / cx.g, i = s % cx.g;
-  const size_t head = (size_t)(cx.h0 + i) * cx.stride;
-  const int row0 = qt * kTileRows;
+  const int row0 = u.row0;
   uint8_t* slot = cx.ring.p[SLOT];
-  const float* rb = cx.rt + (size_t)(cx.h0 + i) * cx.rt_stride;
+  const float* rb = cx.rt + u.rt_off - row0;
+  const int trem = max(cx.N - row0, 0) * RB;
 #pragma unroll
   for (int h = 0; h < DH; ++h) {
-    dma_tile_part<RB>(cx.q + head * Dims<DH>::D, row0, cx.N, slot + C::kQ + h * kTileBytes + cx.wave * 1024,
-                      cx.off + h * kRowBytes);
-    dma_tile_part<RB>(cx.dout + head * Dims<DH>::D, row0, cx.N, slot + C::kDo + h * kTileBytes + cx.wave * 1024,
-                      cx.off + h * kRowBytes);
+    __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cx.q + u.off), (short)0, trem, kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t*)(slot + C::kQ + h * kTileBytes + cx.wave * 1024), 16,
+                                             cx.off + h * kRowBytes, 0, 0, 0);
+    __amdgpu_buffer_rsrc_t rd =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cx.dout + u.off), (short)0, trem, kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void_t*)(slot + C::kDo + h * kTileBytes + cx.wave * 1024), 16,
+                                             cx.off + h * kRowBytes, 0, 0, 0);
   }
   // row terms of the 32 rows (whole tiles stay inside the planes thanks to
   // their padding) land in the first 256 B of the area: lanes 0-7 bring
@@ -298,6 +321,7 @@ __device__ __forceinline__ void kv_issue(const KvCtx& cx, int s) {
   __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void*)(rb + row0), (short)0, rem, kBufferWord3);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + C::kRt), 16, roff, 0, 0, 0);
+  kv_advance(cx, u);
 }
 
 // S' = S - lse log2(e)/c and dP' = dP - D of the step in slot SLOT: the
@@ -356,7 +380,7 @@ __device__ __forceinline__ void kv_interleave() {
 }
 
 template <int DH, int SLOT, int P>
-__device__ __forceinline__ void kv_phase(const KvCtx& cx, KvState<DH>& w, int s) {
+__device__ __forceinline__ void kv_phase(const KvCtx& cx, KvState<DH>& w, KvCursor& u, int s) {
   using C = KvCfg<DH>;
   constexpr int AHEAD = (SLOT + 4) % kKvBuf;
   constexpr int PREV = (SLOT + kKvBuf - 1) % kKvBuf;
@@ -364,7 +388,7 @@ __device__ __forceinline__ void kv_phase(const KvCtx& cx, KvState<DH>& w, int s)
   // step s+1 has landed (steps s+2, s+3 may still be in flight); every wave
   // is done with step s-2, whose slot receives step s+4
   barrier_vm<2 * C::kDma>();
-  kv_issue<DH, AHEAD>(cx, s + 4);
+  kv_issue<DH, AHEAD>(cx, u);  // step s + 4
   const int lane = threadIdx.x & 63, lg = lane >> 5, l32 = lane & 31;
   // Masks of S(s). Steps before the wave's first (causal: query tiles that
   // see none of its keys) run the same code fully masked (P = dS = 0), so
@@ -373,7 +397,7 @@ __device__ __forceinline__ void kv_phase(const KvCtx& cx, KvState<DH>& w, int s)
   if (s < cx.first) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) w.sc[e] = cx.masked;
-  } else if (cx.causal && cx.qt0 + s / cx.g == cx.kb) {
+  } else if (cx.causal && (unsigned)(s - cx.diag0) < (unsigned)cx.g) {  // query tile kb
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       if (lg * 16 + e < l32) w.sc[e] = cx.masked;
@@ -462,6 +486,10 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dkdv_kernel(KvAr
   const int nsteps = max(qb - cx.qt0, 0) * cx.g;
   // causal: this wave's keys are first seen by query tile kb, i.e. step (kb - qt0) * g
   cx.first = !wave_valid ? nsteps : (a.causal ? min((cx.kb - cx.qt0) * cx.g, nsteps) : 0);
+  cx.diag0 = (cx.kb - cx.qt0) * cx.g;
+  cx.d_head = cx.stride * D;
+  cx.d_wrap = (int64_t)kTileRows * D - (int64_t)(cx.g - 1) * cx.stride * D;
+  cx.rt_wrap = (int64_t)kTileRows - (int64_t)(cx.g - 1) * cx.rt_stride;
   const size_t kv_row0 = (size_t)(sg.kv_base + (int64_t)kvh * sg.stride);
 
   KvState<DH> w;
@@ -517,28 +545,33 @@ __global__ __launch_bounds__(kThreads, Dims<DH>::MINB) void bwd_dkdv_kernel(KvAr
 
   // prologue: steps 0..3 in flight (empty ranges past the end), wait for
   // steps 0..2, then S(0) and dP(0)
-  kv_issue<DH, 0>(cx, 0);
-  kv_issue<DH, 1>(cx, 1);
-  kv_issue<DH, 2>(cx, 2);
-  kv_issue<DH, 3>(cx, 3);
+  KvCursor cur;
+  cur.i = 0;
+  cur.row0 = cx.qt0 * kTileRows;
+  cur.off = (int64_t)cx.h0 * cx.stride * D + (int64_t)cur.row0 * D;
+  cur.rt_off = (int64_t)cx.h0 * cx.rt_stride + cur.row0;
+  kv_issue<DH, 0>(cx, cur);
+  kv_issue<DH, 1>(cx, cur);
+  kv_issue<DH, 2>(cx, cur);
+  kv_issue<DH, 3>(cx, cur);
   barrier_vm<C::kDma>();
   kv_scores<DH, 0>(cx, w);
 
   // whole six-phase rounds first (ring slot period 6, register parity 2)
   int s = 0;
   for (; s + kKvBuf <= nsteps; s += kKvBuf) {
-    kv_phase<DH, 0, 0>(cx, w, s);
-    kv_phase<DH, 1, 1>(cx, w, s + 1);
-    kv_phase<DH, 2, 0>(cx, w, s + 2);
-    kv_phase<DH, 3, 1>(cx, w, s + 3);
-    kv_phase<DH, 4, 0>(cx, w, s + 4);
-    kv_phase<DH, 5, 1>(cx, w, s + 5);
+    kv_phase<DH, 0, 0>(cx, w, cur, s);
+    kv_phase<DH, 1, 1>(cx, w, cur, s + 1);
+    kv_phase<DH, 2, 0>(cx, w, cur, s + 2);
+    kv_phase<DH, 3, 1>(cx, w, cur, s + 3);
+    kv_phase<DH, 4, 0>(cx, w, cur, s + 4);
+    kv_phase<DH, 5, 1>(cx, w, cur, s + 5);
   }
-  if (s < nsteps) kv_phase<DH, 0, 0>(cx, w, s);
-  if (s + 1 < nsteps) kv_phase<DH, 1, 1>(cx, w, s + 1);
-  if (s + 2 < nsteps) kv_phase<DH, 2, 0>(cx, w, s + 2);
-  if (s + 3 < nsteps) kv_phase<DH, 3, 1>(cx, w, s + 3);
-  if (s + 4 < nsteps) kv_phase<DH, 4, 0>(cx, w, s + 4);
+  if (s < nsteps) kv_phase<DH, 0, 0>(cx, w, cur, s);
+  if (s + 1 < nsteps) kv_phase<DH, 1, 1>(cx, w, cur, s + 1);
+  if (s + 2 < nsteps) kv_phase<DH, 2, 0>(cx, w, cur, s + 2);
+  if (s + 3 < nsteps) kv_phase<DH, 3, 1>(cx, w, cur, s + 3);
+  if (s + 4 < nsteps) kv_phase<DH, 4, 0>(cx, w, cur, s + 4);
   // drain the DMAs still in flight before the wave ends
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
