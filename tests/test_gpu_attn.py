@@ -59,6 +59,26 @@ def test_bf16_small_all_rows(Hq, Hkv, N, causal, d):
     check_rows(o, ref, label)
 
 
+# d = 16 grids of at most two workgroups per CU run eight-wave workgroups
+# whose two key-range parts are merged through LDS; larger grids the
+# four-wave workgroups. On 256 CUs, N = 1024 (8,4) has 512 workgroups at B = 8
+# (the last grid with parts) and 576 at B = 9 (the first without); N = 960
+# gives odd tile counts per workgroup (the second part one tile short).
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("B,N", [(8, 1024), (9, 1024), (8, 960)])
+def test_bf16_d16_grid_bound_all_rows(B, N, causal):
+    label = f"bf16 d=16 B={B} N={N} (8,4) causal={causal}"
+    log(f"[case] {label}")
+    q, k, v = draw_attn_case(B, 8, 4, N, 16, "bf16", seed=B * 1000 + N)
+    o, lse = _run(q, k, v, "bf16", 0.25, causal, return_lse=True)
+    ref, ref_lse = oracle_attention(q, k, v, scale=0.25, causal=bool(causal), return_lse=True,
+                                    threads=oracle_threads())
+    o = to_host(o)
+    check_global(o, ref, "bf16", label)
+    check_rows(o, ref, label)
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= LSE_BF16
+
+
 @pytest.mark.parametrize("d", [16, 64])
 @pytest.mark.parametrize("causal", [0, 1])
 @pytest.mark.parametrize("N,Hq,Hkv", [(1, 2, 1), (17, 8, 4), (255, 4, 4), (256, 2, 2),
