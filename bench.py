@@ -187,6 +187,11 @@ class ClockSampler:
 CLOCK = None  # ClockSampler, created in main()
 MIN_WARMUP_S = 0.5
 CLOCK_WINDOW_S = 2.6
+# A HIP event recorded between two calls adds about 2.5 us to the interval
+# it closes (measured on the SQAT-m layer: 32.2 us per call with an event
+# after every call, 29.6 with one after every ten, 29.6 around 100 calls).
+# Calls shorter than this are therefore timed in groups between events.
+MIN_INTERVAL_MS = 0.25
 
 
 def measure(torch, fn, steps, warmup, min_warmup_s=None, clock_window_s=None):
@@ -195,9 +200,12 @@ def measure(torch, fn, steps, warmup, min_warmup_s=None, clock_window_s=None):
     window, the warm-up lasts at least that long and the graphics clock is
     sampled meanwhile: the clock of this kernel under sustained load), then
     time exactly ``steps`` calls bracketed by synchronisations, with a HIP
-    event on the launch stream between consecutive calls. Returns the mean
-    (total / steps), median and minimum per-call times in ms, the wall
-    time of the timed calls and the clock."""
+    event on the launch stream between consecutive calls -- or, for calls
+    shorter than MIN_INTERVAL_MS (estimated from 5 calls between two events;
+    not under --profile), between consecutive groups of about MIN_INTERVAL_MS
+    of calls, each group's time divided by its number of calls. Returns the mean (total /
+    steps), median and minimum per-call times in ms, the calls per timed
+    interval, the wall time of the timed calls and the clock."""
     stream = torch.cuda.current_stream()
     if min_warmup_s is None or MIN_WARMUP_S == 0.0:
         min_warmup_s = MIN_WARMUP_S
@@ -212,21 +220,35 @@ def measure(torch, fn, steps, warmup, min_warmup_s=None, clock_window_s=None):
         torch.cuda.synchronize()
         done += 1
     clk = CLOCK.stop() if window else None
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    group = 1
+    if MIN_WARMUP_S > 0.0:  # --profile: exactly warmup + steps calls, one event after each
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(5):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        est = e0.elapsed_time(e1) / 5
+        group = max(1, min(steps, math.ceil(MIN_INTERVAL_MS / max(est, 1e-6))))
+    nint = max(1, steps // group)
+    sizes = [steps // nint + (1 if i < steps % nint else 0) for i in range(nint)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nint + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     evs[0].record(stream)
-    for i in range(steps):
-        fn()
+    for i, sz in enumerate(sizes):
+        for _ in range(sz):
+            fn()
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
-    total = evs[0].elapsed_time(evs[steps])
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) / sizes[i] for i in range(nint))
+    total = evs[0].elapsed_time(evs[nint])
     n = len(per)
     median = per[n // 2] if n % 2 else 0.5 * (per[n // 2 - 1] + per[n // 2])
-    return {"mean_ms": total / steps, "median_ms": median, "min_ms": per[0], "wall_s": wall,
-            "warmup_calls": done, "clock": clk}
+    return {"mean_ms": total / steps, "median_ms": median, "min_ms": per[0], "calls_per_interval": group,
+            "wall_s": wall, "warmup_calls": done, "clock": clk}
 
 
 def clock_peak_tflops(clk):
@@ -806,7 +828,8 @@ def _entry(m, flops, tokens, peak, calls):
     cpk = clock_peak_tflops(m["clock"])
     med = m["median_ms"]
     tf = flops / (med * 1e-3) / 1e12
-    e = {"calls": calls, "median_ms": round(med, 5), "min_ms": round(m["min_ms"], 5),
+    e = {"calls": calls, "calls_per_interval": m["calls_per_interval"], "median_ms": round(med, 5),
+         "min_ms": round(m["min_ms"], 5),
          "mean_ms": round(m["mean_ms"], 5), "tflops": round(tf, 2),
          "tflops_min_time": round(flops / (m["min_ms"] * 1e-3) / 1e12, 2),
          "tokens_per_s": round(tokens / (med * 1e-3), 1), "frac": round(tf / peak, 4),
