@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libsqa.so")
 PROBE_LIB = os.path.join(PKG, "libsqa_probe.so")
 PROBE_SOURCES = ["issue_probe.hip"]
 
-SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_bf16_d16.hip", "attn_fwd_bf16_d64.hip", "attn_fwd_bf16_d128.hip", "attn_fwd_f32.hip",
+SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_bf16_d16.hip", "attn_fwd_bf16_d32.hip", "attn_fwd_bf16_d64.hip", "attn_fwd_bf16_d128.hip", "attn_fwd_f32.hip",
            "attn_fwd_f32_mfma.hip", "attn_bwd_bf16.hip",
            "gemm_bf16.hip", "rms_norm.hip", "sqa_api.cpp"]
 

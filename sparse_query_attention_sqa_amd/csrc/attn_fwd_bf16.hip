@@ -671,16 +671,16 @@ hipError_t launch_d(const AttnProblem& p, hipStream_t stream) {
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, hipStream_t stream) {
   if (p.D == 64) return launch_attn_fwd_bf16_d64(p, stream);
   if (p.tail_split > 1) return hipErrorInvalidValue;  // the tail split is a d = 64 schedule
-  // Unsplit d = 16: the kernel that folds the scale and the running maximum
-  // into the score MFMAs (attn_fwd_bf16_d16.hip). This one serves d = 16
-  // key-range splits (and N of 2^26 and more): under a causal mask with
-  // 32-row waves (112 VGPRs, four waves per SIMD), whose extra waves hide the
-  // latency of the short causal tile chains (B16 N1024 (8,4): 27.7 -> 23.1 us;
-  // N = 4096: +20 %; N = 32768: +9 %). Encoder-style and d = 32 keep 64-row
-  // waves (32-row waves re-read every K/V fragment per 32 rows: d = 32 at 32k
-  // ran 7 % slower).
+  // Unsplit d = 16 and d = 32: the kernels that fold the scale and the
+  // running maximum into the score MFMAs (attn_fwd_bf16_d16.hip,
+  // attn_fwd_bf16_d32.hip). This one serves their key-range splits (and the
+  // longest N): under a causal mask with 32-row waves (112 VGPRs, four waves
+  // per SIMD), whose extra waves hide the latency of the short causal tile
+  // chains (B16 N1024 (8,4): 27.7 -> 23.1 us; N = 4096: +20 %; N = 32768:
+  // +9 %); encoder-style d = 16 and d = 32 with 64-row waves.
   if (p.D == 16 && p.nsplit <= 1 && p.N * 32 < 0x7fffffffLL) return launch_attn_fwd_bf16_d16(p, stream);
   if (p.D == 16) return p.causal ? launch_d<16, 1>(p, stream) : launch_d<16, 2>(p, stream);
+  if (p.D == 32 && p.nsplit <= 1 && p.N * 64 < 0x7fffffffLL) return launch_attn_fwd_bf16_d32(p, stream);
   if (p.D == 32) return launch_d<32, 2>(p, stream);
   if (p.D == 128) return launch_attn_fwd_bf16_d128(p, stream);
   return hipErrorInvalidValue;

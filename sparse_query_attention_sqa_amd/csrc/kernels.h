@@ -55,6 +55,8 @@ int attn_fwd_tail_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, bool causa
 size_t attn_tail_workspace_bytes(int64_t units, int S);
 // head dim 16, unsplit, N*32 < 2^31 (attn_fwd_bf16_d16.hip)
 hipError_t launch_attn_fwd_bf16_d16(const AttnProblem& p, hipStream_t stream);
+// head dim 32, unsplit, N*64 < 2^31 (attn_fwd_bf16_d32.hip)
+hipError_t launch_attn_fwd_bf16_d32(const AttnProblem& p, hipStream_t stream);
 // head dim 64, software-pipelined (attn_fwd_bf16_d64.hip)
 hipError_t launch_attn_fwd_bf16_d64(const AttnProblem& p, hipStream_t stream);
 // head dim 128, software-pipelined (attn_fwd_bf16_d128.hip)
