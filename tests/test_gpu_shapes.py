@@ -88,7 +88,7 @@ def test_f32_head_dims_small_all_rows(N, Hq, Hkv, causal, d):
 
 
 # ------------------------------------------------------------- uneven groups
-@pytest.mark.parametrize("d", [64, 16])
+@pytest.mark.parametrize("d", [64, 16, 32])
 @pytest.mark.parametrize("causal", [0, 1])
 @pytest.mark.parametrize("N", [1, 65, 1000, 4096])
 @pytest.mark.parametrize("Hq,Hkv", [(6, 4), (5, 2), (7, 3), (12, 8)])
@@ -164,7 +164,7 @@ def test_f32_varlen_all_rows(causal, d):
     _check_varlen(q, k, v, cu, "f32", 1.0 / math.sqrt(d), causal, label)
 
 
-@pytest.mark.parametrize("d", [64, 16, 128])
+@pytest.mark.parametrize("d", [64, 16, 32, 128])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_varlen_one_sequence_equals_dense_bitwise(causal, d):
     """One sequence of N tokens through the packed entry point runs the same
