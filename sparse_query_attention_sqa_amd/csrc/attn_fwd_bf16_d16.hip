@@ -34,8 +34,12 @@
 // (buffer_load ... lds, one 1 KB DMA per wave and tile: K keys 0-31, K keys
 // 32-63, V keys 0-31, V keys 32-63) through a 4-slot ring, one barrier per
 // tile. K and V rows are in key order (32 B), the K rows' two 16-byte chunks
-// swapped on rows 8-15 of every 16 (conflict-free fragment reads); V reaches
-// the P.V MFMA through ds_read_b64_tr_b16.
+// swapped on rows 8-15 of every 16; V reaches the P.V MFMA through
+// ds_read_b64_tr_b16. The score MFMA's k-groups run hi and lo of one chunk
+// before the other chunk's (G = 2*chunk + part), so that lanes 0-31 of a K
+// fragment read share 16 chunks: a 16-byte LDS read is served in passes of
+// 32 lanes x 8 bytes, and two chunks per row in one pass met in the same
+// banks (SQ_LDS_BANK_CONFLICT about 2 per LDS instruction before, 0 after).
 //
 // Schedule: a wave's 32 rows are two 16-row halves in a two-phase pipeline
 // over the tiles kt (as the d = 64 kernel's):
@@ -153,7 +157,7 @@ struct Ctx {
 };
 
 struct WaveState {
-  u32x4_t qf[2];     // per half: c*q as the B operand, k-group G: hi dims 8G.. (G < 2), lo dims 8(G-2).. (G >= 2)
+  u32x4_t qf[2];     // per half: c*q as the B operand, k-group G: hi (G even) or lo (G odd) of dims 8(G>>1)..
   f32x4_t negm[2];   // per half: -m in every entry, the C operand of each score chain
   f32x4_t o[2];      // per half: O^T entries, dims 4G .. 4G+3 of query l%16
   float l[2];        // per half: this lane's share of the row sum
@@ -433,7 +437,7 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, 4) void attn_fwd_bf16_d16_kerne
   } else {       // V keys 32*(rw-2) .. +31
     ln.dma_src = (uint32_t)((rw - 2) * kBlockBytes + lane * 16);
   }
-  ln.kro = (uint32_t)(kh * kSlotBytes + c16 * kRowBytes + (((G & 1) ^ (c16 >> 3)) * 16));
+  ln.kro = (uint32_t)(kh * kSlotBytes + c16 * kRowBytes + (((G >> 1) ^ (c16 >> 3)) * 16));
   ln.vro = (uint32_t)(kh * kSlotBytes + kVOffset + (4 * G + (c16 >> 2)) * kRowBytes + (c16 & 3) * 8);
 
   // ---- Q loads, on every wave (one past the last row block reads row N-1 of
@@ -443,7 +447,7 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, 4) void attn_fwd_bf16_d16_kerne
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const int t = min(tb * kRowsPerWave + hf * 16 + c16, N - 1);
-    qraw[hf] = *reinterpret_cast<const u32x4_t*>(a.q + ((size_t)qrow0 + t) * D + (G & 1) * 8);
+    qraw[hf] = *reinterpret_cast<const u32x4_t*>(a.q + ((size_t)qrow0 + t) * D + (G >> 1) * 8);
   }
 
   // ---- prologue: tiles 0..2 in flight; tile 0 landed; S(0,h0)
@@ -459,7 +463,7 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, 4) void attn_fwd_bf16_d16_kerne
     for (int e = 0; e < 4; ++e) {
       const float x0 = bf16_lo(qraw[hf][e]) * a.c, x1 = bf16_hi(qraw[hf][e]) * a.c;
       const uint32_t hi = pack_bf16x2(x0, x1);
-      w.qf[hf][e] = G < 2 ? hi : pack_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi));
+      w.qf[hf][e] = (G & 1) ? pack_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi)) : hi;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -29,7 +29,11 @@
 // V rows their two 32-byte halves swapped when (key >> 2) & 1, so the
 // fragment reads (16-byte reads of 16 rows, transposed 8-byte reads of 8
 // rows) spread over all LDS banks; V reaches the P.V MFMA through
-// ds_read_b64_tr_b16.
+// ds_read_b64_tr_b16. The score MFMA's k-groups run hi and lo of one
+// 16-byte chunk before the other chunk's (G = 2*chunk + part): a 16-byte LDS
+// read is served in passes of 32 lanes x 8 bytes, so lanes 0-31 must not
+// touch two chunks of one row (SQ_LDS_BANK_CONFLICT 2 per LDS instruction
+// with hi/lo as the high k-group bit, 0 with this order).
 //
 // Schedule: a wave's 32 rows are two 16-row halves in the two-phase pipeline
 // of the d = 16 kernel:
@@ -143,7 +147,7 @@ struct Ctx {
 };
 
 struct WaveState {
-  u32x4_t qf[2][2];  // [half][dim half]: c*q as the B operand, k-group G: hi (G < 2) or lo (G >= 2) of dims 8(G&1)..
+  u32x4_t qf[2][2];  // [half][dim half]: c*q as the B operand, k-group G: hi (G even) or lo (G odd) of dims 8(G>>1)..
   f32x4_t negm[2];   // per half: -m in every entry, the C operand of each score chain
   f32x4_t o[2][2];   // [half][dim half]: O^T entries, dims 16*dh + 4G .. +3 of query l%16
   float l[2];        // per half: this lane's share of the row sum
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_d32_kernel(Args32 a
   }
 #pragma unroll
   for (int dh = 0; dh < 2; ++dh) {
-    ln.kro[dh] = (uint32_t)(c16 * kRowBytes + (((2 * dh + (G & 1)) ^ ((c16 >> 2) & 3)) * 16));
+    ln.kro[dh] = (uint32_t)(c16 * kRowBytes + (((2 * dh + (G >> 1)) ^ ((c16 >> 2) & 3)) * 16));
     ln.vro[dh] = (uint32_t)(kVOffset + (4 * G + (c16 >> 2)) * kRowBytes + ((dh ^ (G & 1)) * 32) + (c16 & 3) * 8);
   }
 
@@ -432,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_d32_kernel(Args32 a
     const int t = min(tb * kRowsPerWave + hf * 16 + c16, N - 1);
 #pragma unroll
     for (int dh = 0; dh < 2; ++dh)
-      qraw[hf][dh] = *reinterpret_cast<const u32x4_t*>(a.q + ((size_t)qrow0 + t) * D + dh * 16 + (G & 1) * 8);
+      qraw[hf][dh] = *reinterpret_cast<const u32x4_t*>(a.q + ((size_t)qrow0 + t) * D + dh * 16 + (G >> 1) * 8);
   }
 
   // ---- prologue: tiles 0..2 in flight; tile 0 landed; S(0,h0)
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_d32_kernel(Args32 a
       for (int e = 0; e < 4; ++e) {
         const float x0 = bf16_lo(qraw[hf][dh][e]) * a.c, x1 = bf16_hi(qraw[hf][dh][e]) * a.c;
         const uint32_t hi = pack_bf16x2(x0, x1);
-        w.qf[hf][dh][e] = G < 2 ? hi : pack_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi));
+        w.qf[hf][dh][e] = (G & 1) ? pack_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi)) : hi;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) w.o[hf][dh][i] = 0.f;
